@@ -1,0 +1,148 @@
+"""Seeded synthetic workloads for the KDN mixer recurrence.
+
+This module only draws inputs.  It holds none of the recurrence's arithmetic,
+so the GPU library, the fp64 oracle, the tests and the benchmark can all use
+the same inputs without sharing any part of the computation.
+
+Recipe (every tensor is drawn in float32 from ``numpy.random.default_rng``,
+in the fixed order q, k, v, alpha, omega, r, c0; ``N(m, s)`` means mean m and
+standard deviation s):
+
+* q, k ~ N(0, 1), each (b, t, h) row L2-normalised over its d_k channels;
+* v ~ N(0, 1);
+* alpha = sigmoid(N(alpha_loc, 0.5)) per channel (isotropic: per head-token);
+* omega = softplus(N(omega_loc, 1)) with the same shape as alpha;
+* r = 0.01 + softplus(N(0, 1)) per head-token (the pages' r_min = 0.01);
+* c0 = 1.0 per head, or U(0.5, 2) per head;
+* decode state: S0 ~ N(0, 0.1), p0 ~ U(0.1, 1) (isotropic: one p0 per head).
+
+For bf16 workloads every tensor above except c0, S0 and p0 is then rounded
+to bf16 (round to nearest, ties to even) and returned as float32 arrays that
+hold exactly the bf16 values, so both sides of a comparison see identical
+numbers.  The shapes are those of the 750M and 1.3B mixer layers of the
+"Kalman Delta Networks" pages (d_k = d_v = 128, 16 heads).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    variant: str          # "diagonal" or "isotropic"
+    dtype: str            # "f32" or "bf16": dtype of q, k, v, alpha, omega, r and o
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    mu: float
+    c0: str               # "one" or "uniform"
+    seed: int
+    alpha_loc: float = 2.0
+    omega_loc: float = -4.0
+    decode_steps: int = 0  # > 0: a decode workload with B sequences and T = 1 per step
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "diag_f32_b1_t256_h2_d64": Workload(
+        "diag_f32_b1_t256_h2_d64", "diagonal", "f32", 1, 256, 2, 64, 64, 64.0, "one", 1000),
+    "diag_bf16_b8_t4096_h16_d128": Workload(
+        "diag_bf16_b8_t4096_h16_d128", "diagonal", "bf16", 8, 4096, 16, 128, 128, 128.0,
+        "uniform", 1001),
+    "iso_bf16_b8_t4096_h16_d128": Workload(
+        "iso_bf16_b8_t4096_h16_d128", "isotropic", "bf16", 8, 4096, 16, 128, 128, 128.0,
+        "uniform", 1002),
+    "diag_bf16_b1_t65536_h16_d128": Workload(
+        "diag_bf16_b1_t65536_h16_d128", "diagonal", "bf16", 1, 65536, 16, 128, 128, 128.0,
+        "one", 1003, alpha_loc=4.0),
+    "decode_diag_bf16_n256_h16_d128_s1024": Workload(
+        "decode_diag_bf16_n256_h16_d128_s1024", "diagonal", "bf16", 256, 1, 16, 128, 128, 128.0,
+        "one", 1004, decode_steps=1024),
+}
+# the five workloads in the order they are listed in the benchmark table
+WORKLOAD_ORDER = list(WORKLOADS)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 value (ties to even), returned as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+
+
+def _softplus(x):
+    return np.log1p(np.exp(x)).astype(np.float32)
+
+
+def _l2norm(x):
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n).astype(np.float32)
+
+
+def _normal(rng, shape, loc=0.0, scale=1.0):
+    z = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        z *= np.float32(scale)
+    if loc != 0.0:
+        z += np.float32(loc)
+    return z
+
+
+def _draw_tokens(rng, w: Workload, lead: tuple) -> dict:
+    """Draw q, k, v, alpha, omega, r with leading shape ``lead`` (e.g. (B,T,H))."""
+    gate_shape = lead + (w.dk,) if w.variant == "diagonal" else lead
+    out = {
+        "q": _l2norm(_normal(rng, lead + (w.dk,))),
+        "k": _l2norm(_normal(rng, lead + (w.dk,))),
+        "v": _normal(rng, lead + (w.dv,)),
+        "alpha": _sigmoid(_normal(rng, gate_shape, w.alpha_loc, 0.5)),
+        "omega": _softplus(_normal(rng, gate_shape, w.omega_loc, 1.0)),
+        "r": (np.float32(0.01) + _softplus(_normal(rng, lead))).astype(np.float32),
+    }
+    if w.dtype == "bf16":
+        out = {key: round_bf16(val) for key, val in out.items()}
+    return out
+
+
+def _draw_c0(rng, w: Workload) -> np.ndarray:
+    if w.c0 == "uniform":
+        return rng.uniform(0.5, 2.0, size=w.H).astype(np.float32)
+    return np.ones(w.H, dtype=np.float32)
+
+
+def forward_inputs(w: Workload) -> dict:
+    """All inputs of one forward call: q,k,v,alpha,omega,r (float32 arrays that
+    hold the exact values of ``w.dtype``) and c0 [H] float32."""
+    rng = np.random.default_rng(w.seed)
+    out = _draw_tokens(rng, w, (w.B, w.T, w.H))
+    out["c0"] = _draw_c0(rng, w)
+    return out
+
+
+def decode_state(w: Workload) -> dict:
+    """Initial carried state of a decode workload: S0 [N,H,dk,dv], p0 [N,H,dk]
+    (isotropic: [N,H]) float32, N = w.B."""
+    rng = np.random.default_rng([w.seed, 0xD0])
+    S0 = _normal(rng, (w.B, w.H, w.dk, w.dv), 0.0, 0.1)
+    pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)
+    p0 = rng.uniform(0.1, 1.0, size=pshape).astype(np.float32)
+    return {"S0": S0, "p0": p0}
+
+
+def decode_tokens(w: Workload, step: int) -> dict:
+    """The token of decode step ``step`` for all N = w.B sequences:
+    q,k,alpha,omega [N,H,dk] (isotropic alpha, omega [N,H]), v [N,H,dv], r [N,H]."""
+    rng = np.random.default_rng([w.seed, 0x70, step])
+    return _draw_tokens(rng, w, (w.B, w.H))

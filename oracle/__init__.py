@@ -1,0 +1,139 @@
+"""fp64 CPU oracle for the Kalman Delta Network recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  It shares no code
+with the HIP library (kalman_delta_network_amd) and the library never calls
+it.
+
+* ``forward_diag`` / ``forward_iso`` / ``step_diag`` / ``step_iso`` wrap the
+  sequential fp64 recurrence in ``kdn_oracle.c`` ("Kalman Delta Networks:
+  Uncertainty-aware Associative Memory", summary page, section on the
+  method steps, steps 2-5, and its closing sentence for the isotropic
+  variant).
+* ``dense`` holds the brute-force dense-covariance filter (Bayesian Layer
+  page, section 2.2, Proposition 1) used to pin the oracle.
+
+Every function here is pinned by CPU tests in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kdn_oracle.c")
+_LIB = os.path.join(_HERE, "libkdn_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP over independent heads)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        fwd = [I, I, I, I, I, P, P, P, P, P, P, P, D, P, P, P, P, P, P, P, P]
+        for name in ("kdn_oracle_forward_diag", "kdn_oracle_forward_iso"):
+            fn = getattr(lib, name)
+            fn.argtypes = fwd
+            fn.restype = I
+        stp = [I, I, I, I, P, P, P, P, P, P, D, P, P, P]
+        for name in ("kdn_oracle_step_diag", "kdn_oracle_step_iso"):
+            fn = getattr(lib, name)
+            fn.argtypes = stp
+            fn.restype = I
+        _lib = lib
+    return _lib
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _forward(name, q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
+    q, k, v, alpha, omega, r = (_f32(x) for x in (q, k, v, alpha, omega, r))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    iso = name.endswith("iso")
+    c0 = _f32(np.broadcast_to(np.asarray(c0, np.float32), (H,)))
+    S0, p0 = _f64(S0), _f64(p0)
+    o = np.zeros((B, T, H, dv))
+    S_T = np.zeros((B, H, dk, dv))
+    p_T = np.zeros((B, H) if iso else (B, H, dk))
+    tr = None
+    if trace:
+        tshape = (B, T, H) if iso else (B, T, H, dk)
+        tr = {"p_hat": np.zeros(tshape), "kappa": np.zeros((B, T, H, dk)), "p": np.zeros(tshape)}
+    rc = getattr(_load(), name)(
+        B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0),
+        float(mu), _ptr(S0), _ptr(p0), _ptr(o), _ptr(S_T), _ptr(p_T),
+        _ptr(tr["p_hat"]) if tr else None, _ptr(tr["kappa"]) if tr else None,
+        _ptr(tr["p"]) if tr else None)
+    if rc != 0:
+        raise ValueError(f"{name}: bad arguments (rc={rc})")
+    out = {"o": o, "S": S_T, "p": p_T}
+    if tr:
+        out.update({"trace_" + key: val for key, val in tr.items()})
+    return out
+
+
+def forward_diag(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
+    """Diagonal KDN forward.  Shapes: q,k,alpha,omega [B,T,H,dk]; v [B,T,H,dv];
+    r [B,T,H]; c0 [H] (or scalar); S0 [B,H,dk,dv]; p0 [B,H,dk].
+    Returns dict o [B,T,H,dv], S [B,H,dk,dv], p [B,H,dk] (+ traces)."""
+    return _forward("kdn_oracle_forward_diag", q, k, v, alpha, omega, r, c0, mu, S0, p0, trace)
+
+
+def forward_iso(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
+    """Isotropic KDN forward.  alpha, omega, r [B,T,H]; p0 / returned p [B,H]."""
+    return _forward("kdn_oracle_forward_iso", q, k, v, alpha, omega, r, c0, mu, S0, p0, trace)
+
+
+def _step(name, q, k, v, alpha, omega, r, mu, S, p):
+    q, k, v, alpha, omega, r = (_f32(x) for x in (q, k, v, alpha, omega, r))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.array(S, dtype=np.float64, order="C", copy=True)
+    p = np.array(p, dtype=np.float64, order="C", copy=True)
+    o = np.zeros((N, H, dv))
+    rc = getattr(_load(), name)(N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                _ptr(omega), _ptr(r), float(mu), _ptr(S), _ptr(p), _ptr(o))
+    if rc != 0:
+        raise ValueError(f"{name}: bad arguments (rc={rc})")
+    return {"o": o, "S": S, "p": p}
+
+
+def step_diag(q, k, v, alpha, omega, r, mu, S, p):
+    """One decode step.  q,k,alpha,omega [N,H,dk]; v [N,H,dv]; r [N,H];
+    S [N,H,dk,dv]; p [N,H,dk].  Returns new (o, S, p); inputs untouched."""
+    return _step("kdn_oracle_step_diag", q, k, v, alpha, omega, r, mu, S, p)
+
+
+def step_iso(q, k, v, alpha, omega, r, mu, S, p):
+    """Isotropic decode step: alpha, omega, r [N,H]; p [N,H]."""
+    return _step("kdn_oracle_step_iso", q, k, v, alpha, omega, r, mu, S, p)

@@ -1,0 +1,256 @@
+/*
+ * kdn_oracle.c -- plain, sequential fp64 CPU oracle for the Kalman Delta
+ * Network (KDN) mixer recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent reference that the
+ * GPU library is checked against.  It shares no code, header, table or helper
+ * with the HIP library under kalman_delta_network_amd/, and nothing in the
+ * product path may load it: only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark do.
+ *
+ * Source of the equations: "Kalman Delta Networks: Uncertainty-aware
+ * Associative Memory" (arXiv 2609.07816), summary page, section "方法步骤详情"
+ * (method steps 1-5) and the English page, section 3 (Kalman view and its
+ * diagonal restriction).  Every step below is the page's equation written out
+ * one token at a time, in fp64, with no blocking, chunking or reordering:
+ *
+ *   predict    p_hat   = alpha^2 (.) p + omega                    (step 2)
+ *   gain       kappa_i = p_hat_i k_i / (r + sum_j p_hat_j k_j^2)   (step 3)
+ *   write      S       = diag(alpha) S + kappa (v - (diag(alpha) S)^T k)^T
+ *                                                                 (step 4)
+ *   read       o       = S^T q   (the post-write memory)          (step 4)
+ *   posterior  u = (mu/r) k (.) k ;  p = p_hat / (1 + u (.) p_hat) (step 5)
+ *
+ * Isotropic variant (same section, last sentence): one uncertainty scalar b
+ * per head, trace-projected prediction b_hat = a b + omega/d_k with
+ * a = mean_i alpha_i^2 (alpha is a scalar per head-token here, so a =
+ * alpha^2), scalar gain beta = b_hat/(r + b_hat |k|^2), kappa = beta k, and
+ * the posterior precision increment averaged over the d_k channels:
+ * b = b_hat / (1 + (mu/(d_k r)) |k|^2 b_hat).  That last formula is a reading
+ * (the page does not print it); see the readings list of the repository.
+ *
+ * Inputs arrive as float arrays holding exactly the values the GPU receives
+ * (bf16 values widen to float without loss); all arithmetic is double.
+ * Layouts (row-major, contiguous):
+ *   q, k, alpha, omega : [B,T,H,dk]   (isotropic alpha, omega: [B,T,H])
+ *   v, o               : [B,T,H,dv]
+ *   r                  : [B,T,H]
+ *   c0                 : [H]
+ *   S0, S_T            : [B,H,dk,dv]
+ *   p0, p_T            : [B,H,dk]     (isotropic: [B,H])
+ * Optional per-token traces (NULL to skip), layout [B,T,H,dk]
+ * (isotropic p_hat / p traces: [B,T,H]):
+ *   tr_phat = predicted p_hat_t, tr_kappa = gain kappa_t, tr_p = posterior p_t.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <stddef.h>
+
+#define IDX_TOK(b, t, h, B, T, H) ((((size_t)(b) * (size_t)(T) + (size_t)(t)) * (size_t)(H)) + (size_t)(h))
+
+/* One (b,h) recurrence of the Diagonal KDN, token by token. */
+static void diag_head(int b, int h, int T, int H, int dk, int dv,
+                      const float* q, const float* k, const float* v,
+                      const float* alpha, const float* omega, const float* r,
+                      const float* c0, double mu, const double* S0,
+                      const double* p0, double* o, double* S_T, double* p_T,
+                      double* tr_phat, double* tr_kappa, double* tr_p) {
+    (void)T;
+    const size_t state = ((size_t)b * H + h);
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* Sh = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* p = (double*)malloc(sizeof(double) * dk);
+    double* ph = (double*)malloc(sizeof(double) * dk);
+    double* kap = (double*)malloc(sizeof(double) * dk);
+    double* delta = (double*)malloc(sizeof(double) * dv);
+
+    /* initial state: S_0 = 0 and p_0 = c0[h] * 1 unless given */
+    for (int i = 0; i < dk; ++i) {
+        p[i] = p0 ? p0[state * dk + i] : (double)c0[h];
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] = S0 ? S0[state * (size_t)dk * dv + (size_t)i * dv + j] : 0.0;
+    }
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = IDX_TOK(b, t, h, 0, T, H);
+        const float* kt = k + tok * dk;
+        const float* qt = q + tok * dk;
+        const float* vt = v + tok * dv;
+        const float* at = alpha + tok * dk;
+        const float* wt = omega + tok * dk;
+        const double rt = (double)r[tok];
+
+        /* predict: p_hat = alpha^2 p + omega */
+        for (int i = 0; i < dk; ++i) {
+            const double a = at[i];
+            ph[i] = a * a * p[i] + (double)wt[i];
+        }
+        /* gain: kappa = p_hat k / (r + k^T (p_hat k)) */
+        double s = 0.0;
+        for (int i = 0; i < dk; ++i) s += ph[i] * (double)kt[i] * (double)kt[i];
+        for (int i = 0; i < dk; ++i) kap[i] = ph[i] * (double)kt[i] / (rt + s);
+
+        /* predicted mean S_hat = diag(alpha) S and innovation v - S_hat^T k */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) Sh[(size_t)i * dv + j] = (double)at[i] * S[(size_t)i * dv + j];
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += Sh[(size_t)i * dv + j] * (double)kt[i];
+            delta[j] = (double)vt[j] - pred;
+        }
+        /* residual write S = S_hat + kappa delta^T */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = Sh[(size_t)i * dv + j] + kap[i] * delta[j];
+        /* readout from the written memory: o = S^T q */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * (double)qt[i];
+            o[tok * dv + j] = acc;
+        }
+        /* mean-field posterior with information scale mu */
+        for (int i = 0; i < dk; ++i) {
+            const double u = (mu / rt) * (double)kt[i] * (double)kt[i];
+            p[i] = ph[i] / (1.0 + u * ph[i]);
+        }
+        if (tr_phat) for (int i = 0; i < dk; ++i) tr_phat[tok * dk + i] = ph[i];
+        if (tr_kappa) for (int i = 0; i < dk; ++i) tr_kappa[tok * dk + i] = kap[i];
+        if (tr_p) for (int i = 0; i < dk; ++i) tr_p[tok * dk + i] = p[i];
+    }
+
+    for (int i = 0; i < dk; ++i) {
+        if (p_T) p_T[state * dk + i] = p[i];
+        if (S_T)
+            for (int j = 0; j < dv; ++j)
+                S_T[state * (size_t)dk * dv + (size_t)i * dv + j] = S[(size_t)i * dv + j];
+    }
+    free(S); free(Sh); free(p); free(ph); free(kap); free(delta);
+}
+
+/* One (b,h) recurrence of the Isotropic KDN (alpha, omega scalar per head-token). */
+static void iso_head(int b, int h, int T, int H, int dk, int dv,
+                     const float* q, const float* k, const float* v,
+                     const float* alpha, const float* omega, const float* r,
+                     const float* c0, double mu, const double* S0,
+                     const double* p0, double* o, double* S_T, double* p_T,
+                     double* tr_phat, double* tr_kappa, double* tr_p) {
+    const size_t state = ((size_t)b * H + h);
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* delta = (double*)malloc(sizeof(double) * dv);
+    double bcov = p0 ? p0[state] : (double)c0[h];
+    for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] = S0 ? S0[state * (size_t)dk * dv + e] : 0.0;
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = IDX_TOK(b, t, h, 0, T, H);
+        const float* kt = k + tok * dk;
+        const float* qt = q + tok * dk;
+        const float* vt = v + tok * dv;
+        const double a = alpha[tok];
+        const double w = omega[tok];
+        const double rt = r[tok];
+
+        /* trace-projected predict: b_hat = a b + omega/d_k, a = alpha^2 */
+        const double bh = a * a * bcov + w / (double)dk;
+        double n = 0.0;
+        for (int i = 0; i < dk; ++i) n += (double)kt[i] * (double)kt[i];
+        /* scalar gain beta = b_hat / (r + b_hat |k|^2), kappa = beta k */
+        const double beta = bh / (rt + bh * n);
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += a * S[(size_t)i * dv + j] * (double)kt[i];
+            delta[j] = (double)vt[j] - pred;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + beta * (double)kt[i] * delta[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * (double)qt[i];
+            o[tok * dv + j] = acc;
+        }
+        /* posterior: precision increment (mu/r)|k|^2 averaged over d_k channels */
+        bcov = bh / (1.0 + (mu / ((double)dk * rt)) * n * bh);
+        if (tr_phat) tr_phat[tok] = bh;
+        if (tr_kappa) for (int i = 0; i < dk; ++i) tr_kappa[tok * dk + i] = beta * (double)kt[i];
+        if (tr_p) tr_p[tok] = bcov;
+    }
+    if (p_T) p_T[state] = bcov;
+    if (S_T)
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) S_T[state * (size_t)dk * dv + e] = S[e];
+    free(S); free(delta);
+}
+
+typedef void (*head_fn)(int, int, int, int, int, int, const float*, const float*, const float*,
+                        const float*, const float*, const float*, const float*, double,
+                        const double*, const double*, double*, double*, double*, double*,
+                        double*, double*);
+
+static int run_heads(head_fn fn, int B, int T, int H, int dk, int dv,
+                     const float* q, const float* k, const float* v, const float* alpha,
+                     const float* omega, const float* r, const float* c0, double mu,
+                     const double* S0, const double* p0, double* o, double* S_T, double* p_T,
+                     double* tr_phat, double* tr_kappa, double* tr_p) {
+    if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return 1;
+    if (!q || !k || !v || !alpha || !omega || !r || !o) return 1;
+    if (!c0 && !p0) return 1;
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u)
+        fn((int)(u / H), (int)(u % H), T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
+           o, S_T, p_T, tr_phat, tr_kappa, tr_p);
+    return 0;
+}
+
+int kdn_oracle_forward_diag(int B, int T, int H, int dk, int dv,
+                            const float* q, const float* k, const float* v,
+                            const float* alpha, const float* omega, const float* r,
+                            const float* c0, double mu, const double* S0, const double* p0,
+                            double* o, double* S_T, double* p_T,
+                            double* tr_phat, double* tr_kappa, double* tr_p) {
+    return run_heads(diag_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
+                     o, S_T, p_T, tr_phat, tr_kappa, tr_p);
+}
+
+int kdn_oracle_forward_iso(int B, int T, int H, int dk, int dv,
+                           const float* q, const float* k, const float* v,
+                           const float* alpha, const float* omega, const float* r,
+                           const float* c0, double mu, const double* S0, const double* p0,
+                           double* o, double* S_T, double* p_T,
+                           double* tr_phat, double* tr_kappa, double* tr_p) {
+    return run_heads(iso_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
+                     o, S_T, p_T, tr_phat, tr_kappa, tr_p);
+}
+
+/*
+ * Single-token decode step: exactly one iteration of the recurrence on the
+ * carried state (S, p), for N independent sequences.  S [N,H,dk,dv] and
+ * p [N,H,dk] (isotropic [N,H]) are read and overwritten in place; token
+ * inputs use the forward layouts with T = 1.
+ */
+static int step_common(head_fn fn, int pdim, int N, int H, int dk, int dv,
+                       const float* q, const float* k, const float* v, const float* alpha,
+                       const float* omega, const float* r, double mu, double* S, double* p,
+                       double* o) {
+    if (!S || !p) return 1;
+    const size_t ns = (size_t)N * H * dk * dv, np_ = (size_t)N * H * pdim;
+    double* S_in = (double*)malloc(sizeof(double) * (ns ? ns : 1));
+    double* p_in = (double*)malloc(sizeof(double) * (np_ ? np_ : 1));
+    memcpy(S_in, S, sizeof(double) * ns);
+    memcpy(p_in, p, sizeof(double) * np_);
+    const int rc = run_heads(fn, N, 1, H, dk, dv, q, k, v, alpha, omega, r, NULL, mu, S_in, p_in,
+                             o, S, p, NULL, NULL, NULL);
+    free(S_in); free(p_in);
+    return rc;
+}
+
+int kdn_oracle_step_diag(int N, int H, int dk, int dv, const float* q, const float* k,
+                         const float* v, const float* alpha, const float* omega, const float* r,
+                         double mu, double* S, double* p, double* o) {
+    return step_common(diag_head, dk, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
+}
+
+int kdn_oracle_step_iso(int N, int H, int dk, int dv, const float* q, const float* k,
+                        const float* v, const float* alpha, const float* omega, const float* r,
+                        double mu, double* S, double* p, double* o) {
+    return step_common(iso_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
+}

@@ -1,0 +1,395 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics
+fix, independent of the oracle's own code.
+
+Sources: "Kalman Delta Networks: Uncertainty-aware Associative Memory"
+(summary page, method steps 1-5; English page, section 3) and "Memory by
+Design: Probabilistic Sequence Layers" (section 2.2 Proposition 1;
+appendices E.1, E.2, E.4).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dense
+from kalman_delta_network_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "bayesian_layer_collision_e4.txt")
+
+
+def small(variant="diagonal", B=2, T=40, H=3, dk=8, dv=5, seed=7, dtype="f32", **kw):
+    w = wl.Workload("t", variant, dtype, B, T, H, dk, dv, float(kw.pop("mu", dk)), "uniform", seed, **kw)
+    return w, wl.forward_inputs(w)
+
+
+# --------------------------------------------------------------------------
+# The dense helper itself: Bayesian Layer page, appendix E.4 (exact experiment)
+# --------------------------------------------------------------------------
+
+def _collision(rho, reset):
+    D, m = 16, 6
+    e = np.eye(D)
+    keys = {0: e[0], 1: rho * e[0] + math.sqrt(1 - rho * rho) * e[1], 2: e[2], 3: e[3], 4: e[4], 5: e[5]}
+    seq = [0, 1, 2, 3, 4, 5] * 2 + [1] * 40 + [0] * 60
+    M, P = np.zeros((D, m)), 3.0 * np.eye(D)
+    l2, r2 = 0.05, 0.05
+    margins, gains = [], []
+    for ident in seq:
+        k = keys[ident]
+        v = np.eye(m)[ident]
+        override = l2 * np.eye(D) if reset else None
+        M, P, y, u, beta = dense.dense_step(M, P, k, v, np.eye(D), l2 * np.eye(D), r2, q=keys[1],
+                                            P_bar_override=override)
+        margins.append(math.tanh((y[1] - y[0]) / 2.0))
+        gains.append(np.linalg.norm(beta * u))
+    return np.array(margins), np.array(gains)
+
+
+def _golden():
+    rows = {"overlap": [], "gain": [], "margin": [], "steady_gain": []}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                rows[line[0]].append([float(x) for x in line[1:]])
+    return rows
+
+
+def test_dense_helper_reproduces_overlap_sweep():
+    g = _golden()
+    assert len(g["overlap"]) == 9
+    for rho, bayes, reset in g["overlap"]:
+        mb, _ = _collision(rho, False)
+        mr, _ = _collision(rho, True)
+        assert abs(mb[111] - bayes) <= 0.0051, (rho, mb[111], bayes)
+        assert abs(mr[111] - reset) <= 0.0051, (rho, mr[111], reset)
+
+
+def test_dense_helper_reproduces_key_values():
+    g = _golden()
+    mb, gb = _collision(0.92, False)
+    mr, gr = _collision(0.92, True)
+    for t, bayes, reset in g["gain"]:
+        # printed as approximate values ("~1.0", "~2.0", "~0.6"); reset exactly 0.50
+        assert abs(gb[int(t) - 1] - bayes) < 0.05
+        assert abs(gr[int(t) - 1] - reset) < 0.005
+    for t, bayes, reset in g["margin"]:
+        assert abs(mb[int(t) - 1] - bayes) <= 0.0051
+        assert abs(mr[int(t) - 1] - reset) <= 0.0051
+
+
+# --------------------------------------------------------------------------
+# Möbius form of the uncertainty recurrence (KDN summary page, step 5)
+# --------------------------------------------------------------------------
+
+def test_mobius_product_equals_step_recurrence_diag():
+    w, x = small(T=64, mu=8.0)
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")},
+                              mu=w.mu, trace=True)
+    B, T, H, dk = x["k"].shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(dk):
+                Mp = np.eye(2)
+                for t in range(T):
+                    a2 = float(x["alpha"][b, t, h, i]) ** 2
+                    om = float(x["omega"][b, t, h, i])
+                    u = w.mu / float(x["r"][b, t, h]) * float(x["k"][b, t, h, i]) ** 2
+                    Mt = np.array([[a2, om], [u * a2, 1.0 + u * om]])
+                    assert np.linalg.det(Mt) > 0
+                    Mp = Mt @ Mp
+                    p0 = float(x["c0"][h])
+                    num, den = Mp @ np.array([p0, 1.0])
+                    np.testing.assert_allclose(num / den, ref["trace_p"][b, t, h, i], rtol=1e-13)
+
+
+def test_mobius_product_equals_step_recurrence_iso():
+    w, x = small("isotropic", T=64, mu=8.0)
+    ref = oracle.forward_iso(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")},
+                             mu=w.mu, trace=True)
+    B, T, H, dk = x["k"].shape
+    for b in range(B):
+        for h in range(H):
+            Mp = np.eye(2)
+            for t in range(T):
+                a2 = float(x["alpha"][b, t, h]) ** 2
+                om = float(x["omega"][b, t, h]) / dk
+                n = float(np.sum(x["k"][b, t, h].astype(np.float64) ** 2))
+                c = w.mu / (dk * float(x["r"][b, t, h])) * n
+                Mp = np.array([[a2, om], [c * a2, 1.0 + c * om]]) @ Mp
+                num, den = Mp @ np.array([float(x["c0"][h]), 1.0])
+                np.testing.assert_allclose(num / den, ref["trace_p"][b, t, h], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Invariants and closed forms of the posterior
+# --------------------------------------------------------------------------
+
+def test_posterior_and_gain_invariants():
+    w, x = small(T=200, dk=16, dv=4, mu=16.0)
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")},
+                              mu=w.mu, trace=True)
+    p, ph, kap = ref["trace_p"], ref["trace_p_hat"], ref["trace_kappa"]
+    assert np.all(p > 0) and np.all(p <= ph)
+    g = np.sum(kap * x["k"], axis=-1)  # k^T kappa = s / (r + s)
+    assert np.all(g > 0) and np.all(g < 1)
+
+
+def test_precision_additivity_without_dynamics():
+    # alpha = 1, omega = 0: 1/p_T = 1/c0 + sum_t (mu/r_t) k_t^2
+    w, x = small(T=50, mu=3.0)
+    x["alpha"][:] = 1.0
+    x["omega"][:] = 0.0
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=w.mu)
+    k64 = x["k"].astype(np.float64)
+    prec = 1.0 / x["c0"].astype(np.float64)[None, :, None] + np.sum(
+        w.mu / x["r"].astype(np.float64)[..., None] * k64 ** 2, axis=1)
+    np.testing.assert_allclose(1.0 / ref["p"], prec, rtol=1e-12)
+
+
+def test_mobius_fixed_point_under_constant_inputs():
+    # constant alpha, omega, r, k: p converges to the positive root of
+    # c a^2 p^2 + (1 + c w - a^2) p - w = 0 with c = mu k^2 / r
+    T, dk = 3000, 4
+    a, om, r, mu = 0.9, 0.02, 0.3, 4.0
+    k = np.array([0.5, -0.5, 0.5, 0.5], np.float32)
+    x = {"q": np.tile(k, (1, T, 1, 1)), "k": np.tile(k, (1, T, 1, 1)),
+         "v": np.ones((1, T, 1, 2), np.float32), "alpha": np.full((1, T, 1, dk), a, np.float32),
+         "omega": np.full((1, T, 1, dk), om, np.float32), "r": np.full((1, T, 1), r, np.float32)}
+    ref = oracle.forward_diag(**x, c0=[1.7], mu=mu)
+    a, om, r = float(np.float32(a)), float(np.float32(om)), float(np.float32(r))
+    c = mu * 0.25 / r
+    A2 = a * a
+    root = (-(1 + c * om - A2) + math.sqrt((1 + c * om - A2) ** 2 + 4 * c * A2 * om)) / (2 * c * A2)
+    np.testing.assert_allclose(ref["p"][0, 0], root, rtol=1e-12)
+
+
+def test_steady_state_gain_is_printed_golden_ratio():
+    # one-hot repeated key, alpha=1, mu=1, omega=r=0.05: predicted variance ->
+    # root of x^2 - w x - w r = 0 (Bayesian Layer page, appendix E.1) and the
+    # gain -> (sqrt 5 - 1)/2, printed as 0.62 in appendix E.2.
+    T, dk = 400, 3
+    e = np.zeros(dk, np.float32)
+    e[0] = 1.0
+    x = {"q": np.tile(e, (1, T, 1, 1)), "k": np.tile(e, (1, T, 1, 1)),
+         "v": np.ones((1, T, 1, 2), np.float32), "alpha": np.ones((1, T, 1, dk), np.float32),
+         "omega": np.full((1, T, 1, dk), 0.05, np.float32), "r": np.full((1, T, 1), 0.05, np.float32)}
+    ref = oracle.forward_diag(**x, c0=[3.0], mu=1.0, trace=True)
+    gain = ref["trace_kappa"][0, -1, 0, 0]
+    w = r = float(np.float32(0.05))
+    xr = (w + math.sqrt(w * w + 4 * w * r)) / 2
+    np.testing.assert_allclose(ref["trace_p_hat"][0, -1, 0, 0], xr, rtol=1e-12)
+    np.testing.assert_allclose(gain, xr / (r + xr), rtol=1e-12)
+    assert abs(gain - _golden()["steady_gain"][0][0]) < 0.005
+    assert abs(gain - (math.sqrt(5) - 1) / 2) < 1e-6
+
+
+@pytest.mark.parametrize("w_over_r,expect", [(1e-4, "small"), (1e4, "large")])
+def test_steady_gain_asymptotics(w_over_r, expect):
+    # appendix E.2: small state noise g ~ sqrt(w/r); large g ~ 1 - r/(2w)
+    T, dk = 20000 if expect == "small" else 50, 2
+    r = 1.0
+    w = w_over_r * r
+    e = np.array([1.0, 0.0], np.float32)
+    x = {"q": np.tile(e, (1, T, 1, 1)), "k": np.tile(e, (1, T, 1, 1)),
+         "v": np.ones((1, T, 1, 1), np.float32), "alpha": np.ones((1, T, 1, dk), np.float32),
+         "omega": np.full((1, T, 1, dk), w, np.float32), "r": np.full((1, T, 1), r, np.float32)}
+    ref = oracle.forward_diag(**x, c0=[1.0], mu=1.0, trace=True)
+    g = ref["trace_kappa"][0, -1, 0, 0]
+    w = float(np.float32(w))
+    if expect == "small":
+        assert abs(g - math.sqrt(w / r)) < 2 * (w / r)  # next order is O(w/r)
+    else:
+        # The page prints 1 - r/(2w) for this limit; the exact root of its own
+        # fixed-point quadratic (appendix E.1) gives g = 1 - r/w + O((r/w)^2).
+        # Pinned: g -> 1 with 1 - g of order r/w, between the two constants.
+        assert r / (2 * w) <= 1 - g <= r / w * (1 + 1e-3)
+        assert abs((1 - g) - r / w) < 3 * (r / w) ** 2
+
+
+# --------------------------------------------------------------------------
+# Diagonal projection against the brute-force dense Kalman filter (d_k <= 8)
+# --------------------------------------------------------------------------
+
+def test_diag_mean_is_exact_dense_posterior_mean_and_mu1_precision_is_its_diagonal():
+    dk, dv, N, H = 6, 4, 2, 2
+    w = wl.Workload("t", "diagonal", "f32", N, 1, H, dk, dv, 1.0, "one", 11)
+    st = wl.decode_state(w)
+    S, p = st["S0"].astype(np.float64), st["p0"].astype(np.float64)
+    for step in range(30):
+        x = wl.decode_tokens(w, step)
+        new = oracle.step_diag(**x, mu=1.0, S=S, p=p)
+        for n in range(N):
+            for h in range(H):
+                a = x["alpha"][n, h].astype(np.float64)
+                Mn, Pn, y, _, _ = dense.dense_step(
+                    S[n, h], np.diag(p[n, h]), x["k"][n, h], x["v"][n, h], np.diag(a),
+                    np.diag(x["omega"][n, h].astype(np.float64)), float(x["r"][n, h]), q=x["q"][n, h])
+                np.testing.assert_allclose(new["S"][n, h], Mn, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(new["o"][n, h], y, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(1.0 / new["p"][n, h], np.diag(np.linalg.inv(Pn)), rtol=1e-10)
+        S, p = new["S"], new["p"]
+
+
+def test_axis_aligned_keys_match_dense_filter_exactly():
+    # one-hot keys, mu = 1, diagonal P0: the exact posterior stays diagonal,
+    # so Diagonal KDN is the exact Kalman filter (KDN English page, section 3)
+    w, x = small(B=1, H=1, T=60, dk=5, dv=3, mu=1.0)
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 5, size=60)
+    x["k"][0, :, 0, :] = np.eye(5, dtype=np.float32)[idx] * rng.choice([-1, 1], size=(60, 1))
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=1.0)
+    A = [np.diag(x["alpha"][0, t, 0].astype(np.float64)) for t in range(60)]
+    Q = [np.diag(x["omega"][0, t, 0].astype(np.float64)) for t in range(60)]
+    out = dense.dense_filter(x["k"][0, :, 0], x["v"][0, :, 0], A, Q, x["r"][0, :, 0].astype(np.float64),
+                             float(x["c0"][0]) * np.eye(5), queries=x["q"][0, :, 0])
+    np.testing.assert_allclose(ref["S"][0, 0], out["M"][-1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["p"][0, 0], np.diag(out["P"][-1]), rtol=1e-12)
+    np.testing.assert_allclose(ref["o"][0, :, 0], np.array(out["y"]), rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Isotropic variant
+# --------------------------------------------------------------------------
+
+def test_isotropic_covariance_reset_is_gated_delta_rule():
+    # with b_hat forced to a given value each step, the KDN write is the shared
+    # fixed-gain residual form S = (I - beta k k^T) alpha S + beta k v^T with
+    # beta = b_hat / (r + b_hat |k|^2) (KDN summary page, core-method section)
+    N, H, dk, dv = 2, 2, 8, 6
+    w = wl.Workload("t", "isotropic", "f32", N, 1, H, dk, dv, 8.0, "one", 21, omega_loc=0.0)
+    st = wl.decode_state(w)
+    S_kdn = st["S0"].astype(np.float64)
+    S_gdn = S_kdn.copy()
+    rng = np.random.default_rng(5)
+    for step in range(25):
+        x = wl.decode_tokens(w, step)
+        bhat = rng.uniform(0.05, 3.0, size=(N, H))
+        a = x["alpha"].astype(np.float64)
+        # choose the carried b so that the trace-projected prediction equals bhat
+        b_prev = (bhat - x["omega"].astype(np.float64) / dk) / (a * a)
+        new = oracle.step_iso(**x, mu=w.mu, S=S_kdn, p=b_prev)
+        for n in range(N):
+            for h in range(H):
+                k = x["k"][n, h].astype(np.float64)
+                beta = bhat[n, h] / (float(x["r"][n, h]) + bhat[n, h] * (k @ k))
+                S_gdn[n, h] = (np.eye(dk) - beta * np.outer(k, k)) @ (a[n, h] * S_gdn[n, h]) + \
+                    beta * np.outer(k, x["v"][n, h].astype(np.float64))
+        np.testing.assert_allclose(new["S"], S_gdn, rtol=1e-12, atol=1e-12)
+        S_kdn = new["S"]
+
+
+def test_isotropic_posterior_at_mu_dk_is_dense_variance_along_unit_key():
+    dk, dv = 8, 3
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal(dk)
+    k /= np.linalg.norm(k)
+    k = k.astype(np.float32)
+    k64 = k.astype(np.float64)
+    x = {"q": k.reshape(1, 1, dk), "k": k.reshape(1, 1, dk), "v": np.ones((1, 1, dv), np.float32),
+         "alpha": np.array([[0.8]], np.float32), "omega": np.array([[0.3]], np.float32),
+         "r": np.array([[0.2]], np.float32)}
+    b0 = 0.7
+    new = oracle.step_iso(**x, mu=float(dk), S=np.zeros((1, 1, dk, dv)), p=np.array([[b0]]))
+    bhat = float(np.float32(0.8)) ** 2 * b0 + float(np.float32(0.3)) / dk
+    _, P, _, _, _ = dense.dense_step(np.zeros((dk, dv)), bhat * np.eye(dk), k64, np.ones(dv),
+                                     np.eye(dk), np.zeros((dk, dk)), float(np.float32(0.2)),
+                                     P_bar_override=bhat * np.eye(dk))
+    along = k64 @ P @ k64 / (k64 @ k64)
+    np.testing.assert_allclose(new["p"][0, 0], along, rtol=2e-7)  # |k| = 1 up to float32 rounding
+
+
+# --------------------------------------------------------------------------
+# Write invariant, degenerate cases
+# --------------------------------------------------------------------------
+
+def test_write_moves_prediction_toward_value_by_gain():
+    N, H, dk, dv = 3, 2, 8, 5
+    w = wl.Workload("t", "diagonal", "f32", N, 1, H, dk, dv, 8.0, "one", 31)
+    st = wl.decode_state(w)
+    x = wl.decode_tokens(w, 0)
+    S, p = st["S0"].astype(np.float64), st["p0"].astype(np.float64)
+    new = oracle.step_diag(**x, mu=w.mu, S=S, p=p)
+    for n in range(N):
+        for h in range(H):
+            k = x["k"][n, h].astype(np.float64)
+            a = x["alpha"][n, h].astype(np.float64)
+            ph = a * a * p[n, h] + x["omega"][n, h]
+            s = np.sum(ph * k * k)
+            g = s / (float(x["r"][n, h]) + s)
+            pred = (a[:, None] * S[n, h]).T @ k
+            np.testing.assert_allclose(new["S"][n, h].T @ k, (1 - g) * pred + g * x["v"][n, h],
+                                       rtol=1e-12, atol=1e-12)
+
+
+def test_exact_overwrite_when_noise_vanishes():
+    # r -> 0 with an isotropic predictive uncertainty: S^T k = v after the write
+    dk, dv = 8, 4
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal(dk).astype(np.float32)
+    x = {"q": k.reshape(1, 1, dk), "k": k.reshape(1, 1, dk), "v": rng.standard_normal((1, 1, dv)).astype(np.float32),
+         "alpha": np.full((1, 1, dk), 0.9, np.float32), "omega": np.full((1, 1, dk), 0.1, np.float32),
+         "r": np.array([[1e-30]], np.float32)}
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    new = oracle.step_diag(**x, mu=float(dk), S=S0, p=np.full((1, 1, dk), 0.5))
+    np.testing.assert_allclose(new["S"][0, 0].T @ k.astype(np.float64), x["v"][0, 0], rtol=1e-12)
+
+
+def test_infinite_observation_noise_is_pure_decay():
+    w, x = small(T=30, mu=8.0)
+    x["r"][:] = np.float32(1e30)
+    B, T, H, dk = x["k"].shape
+    S0 = np.random.default_rng(4).standard_normal((B, H, dk, x["v"].shape[-1]))
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")},
+                              mu=w.mu, S0=S0)
+    gamma = np.cumprod(x["alpha"].astype(np.float64), axis=1)  # [B,T,H,dk]
+    S_t = gamma[..., None] * S0[:, None]                      # [B,T,H,dk,dv]
+    np.testing.assert_allclose(ref["S"], S_t[:, -1], rtol=1e-12, atol=1e-30)
+    o = np.einsum("bthij,bthi->bthj", S_t, x["q"].astype(np.float64))
+    np.testing.assert_allclose(ref["o"], o, rtol=1e-11, atol=1e-14)
+
+
+def test_zero_information_scale_is_linear_scan():
+    w, x = small(T=30)
+    ref = oracle.forward_diag(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=0.0)
+    p = np.broadcast_to(x["c0"].astype(np.float64)[None, :, None], ref["p"].shape).copy()
+    for t in range(x["k"].shape[1]):
+        p = x["alpha"][:, t].astype(np.float64) ** 2 * p + x["omega"][:, t]
+    np.testing.assert_allclose(ref["p"], p, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Plumbing of the oracle: decode step == forward, split continuation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_oracle_step_and_split_continuation_match_forward(variant):
+    w, x = small(variant, T=33)
+    fwd = oracle.forward_iso if variant == "isotropic" else oracle.forward_diag
+    stp = oracle.step_iso if variant == "isotropic" else oracle.step_diag
+    args = {k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r")}
+    ref = fwd(**args, c0=x["c0"], mu=w.mu)
+    a = fwd(**{k: v[:, :20] for k, v in args.items()}, c0=x["c0"], mu=w.mu)
+    b = fwd(**{k: v[:, 20:] for k, v in args.items()}, c0=x["c0"], mu=w.mu, S0=a["S"], p0=a["p"])
+    np.testing.assert_allclose(b["S"], ref["S"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(b["p"], ref["p"], rtol=1e-13)
+    np.testing.assert_allclose(np.concatenate([a["o"], b["o"]], 1), ref["o"], rtol=1e-13, atol=1e-15)
+    B, H, dk, dv = x["k"].shape[0], w.H, w.dk, w.dv
+    S = np.zeros((B, H, dk, dv))
+    p = np.broadcast_to(x["c0"].astype(np.float64)[None, :] if variant == "isotropic"
+                        else x["c0"].astype(np.float64)[None, :, None], ref["p"].shape).copy()
+    for t in range(w.T):
+        s = stp(**{k: v[:, t] for k, v in args.items()}, mu=w.mu, S=S, p=p)
+        np.testing.assert_allclose(s["o"], ref["o"][:, t], rtol=1e-12, atol=1e-14)
+        S, p = s["S"], s["p"]
+    np.testing.assert_allclose(S, ref["S"], rtol=1e-13, atol=1e-15)
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    ours = wl.round_bf16(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours, theirs)
