@@ -1,0 +1,212 @@
+"""Benchmark of the KDN forward recurrence on one MI355X.
+
+One step = one kdn_forward call over the diagonal bf16 mixer-layer workload
+(B=8, T=4096, H=16, d_k=d_v=128, fp32 state), inputs resident in HBM.
+Prints ONE JSON line with the throughput in tokens/s (B*T per call), the
+HBM roofline of the forward kernel measured with HIP events on the stream it
+runs on, and the fp64 CPU oracle's rate on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--algo auto|recurrent|chunked]
+                    [--no-cpu-baseline] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MAIN = "diag_bf16_b8_t4096_h16_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def forward_bytes(w) -> int:
+    """Algorithmic HBM bytes of one forward call: every input read once, o
+    written once in the input dtype, final state written, c0 read."""
+    es = 2 if w.dtype == "bf16" else 4
+    toks = w.B * w.T * w.H
+    gate = w.dk if w.variant == "diagonal" else 1
+    per_tok = es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv
+    pdim = w.dk if w.variant == "diagonal" else 1
+    return toks * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4
+
+
+def step_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode step: state read and written once,
+    one token of inputs read, o written."""
+    es = 2 if w.dtype == "bf16" else 4
+    units = w.B * w.H
+    gate = w.dk if w.variant == "diagonal" else 1
+    pdim = w.dk if w.variant == "diagonal" else 1
+    return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kalman_delta_network_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def upload(x, dtype, dev):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {n: torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v", "alpha", "omega", "r")}
+    out["c0"] = torch.from_numpy(x["c0"]).to(dev)
+    return out
+
+
+def time_forward(kdn, w, t, steps, warmup, algo):
+    """Returns (ms per step over the timed loop, mean single-launch ms)."""
+    import torch
+    out = (torch.empty((w.B, w.T, w.H, w.dv), dtype=t["q"].dtype, device=t["q"].device),
+           torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=t["q"].device),
+           torch.empty((w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H),
+                       dtype=torch.float32, device=t["q"].device))
+    for _ in range(warmup):
+        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+    torch.cuda.synchronize()
+    # whole timed loop
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    # per-launch durations (events on the same stream the kernel runs on)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return ms_step, ms_launch
+
+
+def bench_decode(kdn, w, dev, steps_cap=None):
+    """Time w.decode_steps consecutive kdn_step calls (tokens pre-uploaded)."""
+    import torch
+    from kalman_delta_network_amd import workloads as wl
+    nsteps = w.decode_steps if steps_cap is None else min(steps_cap, w.decode_steps)
+    st = wl.decode_state(w)
+    S = torch.from_numpy(st["S0"]).to(dev)
+    p = torch.from_numpy(st["p0"]).to(dev)
+    toks = []
+    for s in range(nsteps):
+        toks.append(upload(dict(wl.decode_tokens(w, s), c0=np.ones(1, np.float32)), w.dtype, dev))
+    o = torch.empty((w.B, w.H, w.dv), dtype=toks[0]["q"].dtype, device=dev)
+    names = ("q", "k", "v", "alpha", "omega", "r")
+    for s in range(min(3, nsteps)):  # warm-up on a scratch copy of the state
+        S2, p2 = S.clone(), p.clone()
+        kdn.step(**{n: toks[s][n] for n in names}, mu=w.mu, S=S2, p=p2, variant=w.variant, o=o)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(nsteps):
+        kdn.step(**{n: toks[s][n] for n in names}, mu=w.mu, S=S, p=p, variant=w.variant, o=o)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    return {"workload": w.name, "steps": nsteps, "ms_per_step": ms / nsteps,
+            "tokens_per_s": w.B * nsteps / (ms / 1e3),
+            "hbm_gbs_algorithmic": step_bytes(w) / (ms / nsteps / 1e3) / 1e9,
+            "hbm_frac": step_bytes(w) / (ms / nsteps / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(w, x):
+    import oracle
+    t0 = time.perf_counter()
+    fn = oracle.forward_diag if w.variant == "diagonal" else oracle.forward_iso
+    fn(**{n: x[n] for n in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=w.mu)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full {w.name} workload (B={w.B}, T={w.T}, H={w.H}), fp64, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the isotropic and decode lines")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(each (batch, head) pair is independent; see the sharding notes). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kalman_delta_network_amd as kdn
+    from kalman_delta_network_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    kdn.load_library()
+    w = wl.WORKLOADS[MAIN]
+    x = wl.forward_inputs(w)
+    t = upload(x, w.dtype, dev)
+    ms_step, ms_launch = time_forward(kdn, w, t, args.steps, args.warmup, args.algo)
+    nbytes = forward_bytes(w)
+    achieved = nbytes / (ms_launch / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(MAIN + "/" + args.algo) or tr.get(MAIN)
+        if ent and ent.get("kernel_hash") == kernel_source_hash():
+            traffic = ent["bytes_per_launch"]
+    extra = {}
+    if not args.no_extra:
+        wi = wl.WORKLOADS["iso_bf16_b8_t4096_h16_d128"]
+        ti = upload(wl.forward_inputs(wi), wi.dtype, dev)
+        mi, li = time_forward(kdn, wi, ti, max(3, args.steps // 2), 2, args.algo)
+        extra["isotropic"] = {"workload": wi.name, "tokens_per_s": wi.B * wi.T / (mi / 1e3),
+                              "ms_per_step": mi, "hbm_frac": forward_bytes(wi) / (li / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del ti
+        extra["decode"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
+                                       args.decode_steps)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x)
+    line = {
+        "metric": "KDN forward tokens/sec at H=16,d_k=d_v=128 on 1 GPU; % of HBM/MFMA roofline",
+        "value": w.B * w.T / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "T": w.T, "H": w.H, "d_k": w.dk,
+                   "d_v": w.dv, "mu": w.mu, "state": "fp32", "algo": args.algo},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": nbytes, "launch_ms": ms_launch},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * kdn.h -- C ABI of the MI355X (gfx950) Kalman Delta Network mixer library.
+ *
+ * The library computes the forward recurrence of the scan-compatible Kalman
+ * Delta Network (KDN) mixer and its single-token decode step, as defined in
+ * "Kalman Delta Networks: Uncertainty-aware Associative Memory" (summary
+ * page, method steps 1-5 and the closing isotropic sentence; English page,
+ * section 3).  Per (batch, head) pair and token t, with fp32 state:
+ *
+ *   Diagonal variant (uncertainty p has one entry per key channel):
+ *     p_hat = alpha_t^2 * p + omega_t                       predict
+ *     kappa = p_hat * k_t / (r_t + sum_i p_hat_i k_t,i^2)    Kalman gain
+ *     S     = diag(alpha_t) S
+ *             + kappa (v_t - (diag(alpha_t) S)^T k_t)^T      residual write
+ *     o_t   = S^T q_t                                        readout (after the write)
+ *     p     = p_hat / (1 + (mu / r_t) k_t^2 * p_hat)         mean-field posterior
+ *
+ *   Isotropic variant (one uncertainty scalar b per head; alpha_t, omega_t
+ *   are scalars per head-token):
+ *     b_hat = alpha_t^2 b + omega_t / d_k
+ *     kappa = k_t * b_hat / (r_t + b_hat |k_t|^2)
+ *     S, o_t as above with the scalar decay alpha_t
+ *     b     = b_hat / (1 + (mu / (d_k r_t)) |k_t|^2 b_hat)
+ *
+ * Initial state: S_0 = S0 (or zero when S0 is NULL); p_0 = p0 (or c0[h] on
+ * every channel when p0 is NULL).  No 1/sqrt(d_k) scaling is applied to q.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP device memory of the
+ *    current device), row-major and contiguous.  The caller owns every buffer;
+ *    the library allocates no device memory and keeps no state between calls
+ *    apart from a thread-local error message.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream).  KDN_OK means the work was enqueued.
+ *  - Arguments are validated on the host before any launch.  On any error
+ *    nothing is launched and nothing is written; kdn_last_error() describes
+ *    the problem.  No C++ exception crosses the ABI.
+ *  - Value preconditions are documented, not checked on the device:
+ *    r > 0, c0 > 0 (or p0 > 0), 0 < alpha <= 1, omega >= 0.  Violations give
+ *    NaN/Inf results, not errors.  mu must be finite and >= 0 (checked).
+ *  - Results are deterministic: repeated calls with the same inputs give
+ *    bit-identical outputs.
+ *  - dtype KDN_BF16: q, k, v, alpha, omega, r are bfloat16 and o is written
+ *    as bfloat16 (round to nearest even).  KDN_F32: all of them are float.
+ *    c0, S0, p0, S_T, p_T and the decode state are always float.
+ *  - Supported sizes: d_k and d_v in {64, 128}; B, T, H, N >= 0 (zero sizes
+ *    are valid: with T = 0 the forward only writes S_T = S_0, p_T = p_0).
+ *    Anything else returns KDN_ERR_UNSUPPORTED or KDN_ERR_SHAPE.
+ */
+#ifndef KDN_H
+#define KDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kdn_variant { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1 };
+enum kdn_dtype { KDN_F32 = 0, KDN_BF16 = 1 };
+enum kdn_status {
+    KDN_OK = 0,
+    KDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDN_ERR_SHAPE = 2,       /* a size is negative or the element count overflows */
+    KDN_ERR_UNSUPPORTED = 3, /* unsupported variant, dtype, d_k, d_v or algorithm */
+    KDN_ERR_VALUE = 4,       /* mu is negative or not finite */
+    KDN_ERR_HIP = 5,         /* the HIP runtime refused a launch */
+    KDN_ERR_ALIAS = 6        /* an output overlaps an input it may not overlap */
+};
+/* forward algorithms (kdn_forward_algo) */
+enum kdn_algo {
+    KDN_ALGO_AUTO = 0,      /* the library picks (chunked when available) */
+    KDN_ALGO_RECURRENT = 1, /* token-by-token recurrence, state in registers */
+    KDN_ALGO_CHUNKED = 2    /* chunkwise WY/UT form on matrix cores */
+};
+
+/*
+ * kdn_forward -- the KDN layer recurrence over a whole sequence batch
+ * (summary page, method steps 2-5; isotropic variant per its last sentence).
+ *
+ *   q, k        [B,T,H,dk]   dtype
+ *   v           [B,T,H,dv]   dtype
+ *   alpha,omega [B,T,H,dk]   dtype (KDN_ISOTROPIC: [B,T,H])
+ *   r           [B,T,H]      dtype
+ *   c0          [H]          float, per-head initial uncertainty; may be NULL
+ *                            only when p0 is given
+ *   mu                       information scale of the posterior update
+ *   S0          [B,H,dk,dv]  float or NULL (zero initial memory)
+ *   p0          [B,H,dk]     float or NULL (KDN_ISOTROPIC: [B,H])
+ *   o           [B,T,H,dv]   dtype, output
+ *   S_T         [B,H,dk,dv]  float, output: memory after the last token
+ *   p_T         [B,H,dk]     float, output (KDN_ISOTROPIC: [B,H])
+ * S_T may be the same buffer as S0 (the memory is continued in place).  No
+ * other output may overlap an input or another output (KDN_ERR_ALIAS); in
+ * particular p_T needs its own buffer.
+ */
+int kdn_forward(const void* q, const void* k, const void* v, const void* alpha,
+                const void* omega, const void* r, const float* c0, float mu, int variant,
+                int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                const float* p0, void* o, float* S_T, float* p_T, void* stream);
+
+/* kdn_forward with an explicit algorithm (enum kdn_algo); same arguments and
+ * results up to floating-point rounding. */
+int kdn_forward_algo(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* omega, const void* r, const float* c0, float mu, int variant,
+                     int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                     const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
+
+/*
+ * kdn_step -- one decode step for N independent sequences: exactly one
+ * token of the recurrence applied to the carried state (constant-memory
+ * decoding; summary page, prerequisites on linear attention, and English
+ * page, introduction).
+ *
+ *   q, k        [N,H,dk]     dtype
+ *   v           [N,H,dv]     dtype
+ *   alpha,omega [N,H,dk]     dtype (KDN_ISOTROPIC: [N,H])
+ *   r           [N,H]        dtype
+ *   S           [N,H,dk,dv]  float, read and overwritten in place
+ *   p           [N,H,dk]     float, read and overwritten (KDN_ISOTROPIC: [N,H])
+ *   o           [N,H,dv]     dtype, output
+ */
+int kdn_step(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+             const void* r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
+             float* S, float* p, void* o, void* stream);
+
+/* Host-only argument checks of kdn_forward / kdn_step: the same checks the
+ * entry points run, with no device access and no launch.  Return a status. */
+int kdn_validate_forward(const void* q, const void* k, const void* v, const void* alpha,
+                         const void* omega, const void* r, const float* c0, float mu,
+                         int variant, int dtype, int B, int T, int H, int dk, int dv,
+                         const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                         int algo);
+int kdn_validate_step(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* omega, const void* r, float mu, int variant, int dtype, int N,
+                      int H, int dk, int dv, float* S, float* p, void* o);
+
+/* Static description of a status code (never NULL). */
+const char* kdn_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* kdn_last_error(void);
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int kdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDN_H */

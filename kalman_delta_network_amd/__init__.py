@@ -1,1 +1,170 @@
-"""MI355X (gfx950) implementation of the Kalman Delta Network mixer recurrence."""
+"""MI355X (gfx950) implementation of the Kalman Delta Network mixer recurrence.
+
+Thin Python binding of the C ABI in ``include/kdn.h`` (``libkdn.so``, built by
+``kalman_delta_network_amd.build``).  This module only marshals arguments:
+it checks tensor dtypes, shapes and devices, allocates outputs with PyTorch
+and passes raw device pointers plus the current HIP stream to the library.
+Every step of the recurrence runs in the library's kernels; there is no
+fallback of any kind, and calling into a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkdn.so")
+
+KDN_DIAGONAL, KDN_ISOTROPIC = 0, 1
+KDN_F32, KDN_BF16 = 0, 1
+KDN_OK, KDN_ERR_NULL, KDN_ERR_SHAPE, KDN_ERR_UNSUPPORTED, KDN_ERR_VALUE, KDN_ERR_HIP, KDN_ERR_ALIAS = range(7)
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
+VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC}
+
+# exported symbols of include/kdn.h
+SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_step", "kdn_validate_forward",
+           "kdn_validate_step", "kdn_status_string", "kdn_last_error", "kdn_version")
+
+_lib = None
+
+
+class KDNError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkdn.so and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m kalman_delta_network_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd = [P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
+    lib.kdn_forward.argtypes = fwd + [P]
+    lib.kdn_forward_algo.argtypes = fwd + [P, I]
+    lib.kdn_validate_forward.argtypes = fwd + [I]
+    step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
+    lib.kdn_step.argtypes = step + [P]
+    lib.kdn_validate_step.argtypes = step
+    for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
+               lib.kdn_validate_step, lib.kdn_version):
+        fn.restype = I
+    lib.kdn_status_string.argtypes = [I]
+    lib.kdn_status_string.restype = ctypes.c_char_p
+    lib.kdn_last_error.argtypes = []
+    lib.kdn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != KDN_OK:
+        lib = load_library()
+        detail = (lib.kdn_last_error() or lib.kdn_status_string(status)).decode()
+        raise KDNError(status, where, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDN_BF16
+    if t.dtype == torch.float32:
+        return KDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=None,
+            algo="auto", out=None):
+    """KDN forward over [B,T,H,*] tensors on one GPU.
+
+    q, k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk] (isotropic [B,T,H]);
+    r [B,T,H] -- all float32 or all bfloat16.  c0 [H] float32 (may be None if
+    p0 is given); S0 [B,H,dk,dv] / p0 [B,H,dk] (isotropic [B,H]) float32 or None.
+    Returns (o, S_T, p_T); ``out`` may supply preallocated (o, S_T, p_T).
+    """
+    torch = _torch()
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    gshape = (B, T, H, dk) if var == KDN_DIAGONAL else (B, T, H)
+    pshape = (B, H, dk) if var == KDN_DIAGONAL else (B, H)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if c0 is not None:
+        _need(c0, "c0", (H,), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if p0 is not None:
+        _need(p0, "p0", pshape, torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        p_T = torch.empty(pshape, dtype=torch.float32, device=dev)
+    else:
+        o, S_T, p_T = out
+        _need(o, "o", (B, T, H, dv), dt, dev)
+        _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+        _need(p_T, "p_T", pshape, torch.float32, dev)
+    st = lib.kdn_forward_algo(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0),
+                              float(mu), var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
+                              _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
+    _check(st, "kdn_forward")
+    return o, S_T, p_T
+
+
+def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
+    """One decode step for N sequences; S [N,H,dk,dv] and p [N,H,dk]
+    (isotropic [N,H]) float32 are updated in place.  Returns o [N,H,dv]."""
+    torch = _torch()
+    lib = load_library()
+    var = VARIANTS[variant]
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    gshape = (N, H, dk) if var == KDN_DIAGONAL else (N, H)
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
+                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (N, H))):
+        _need(t, name, shp, dt, dev)
+    _need(S, "S", (N, H, dk, dv), torch.float32, dev)
+    _need(p, "p", (N, H, dk) if var == KDN_DIAGONAL else (N, H), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _need(o, "o", (N, H, dv), dt, dev)
+    st = lib.kdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), float(mu), var,
+                      _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
+    _check(st, "kdn_step")
+    return o

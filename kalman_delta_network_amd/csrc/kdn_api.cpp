@@ -1,0 +1,219 @@
+// kdn_api.cpp -- the C ABI declared in include/kdn.h: host-side argument
+// validation, algorithm dispatch and error reporting.  All device work is in
+// the launchers of kdn_internal.h.
+#include "kdn.h"
+#include "kdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return KDN_OK;
+}
+
+// Test hook: KDN_FAULT=launch makes every entry point report KDN_ERR_HIP
+// after validation, without launching, so the error path can be exercised
+// on a machine without a GPU.
+bool fault_launch() {
+    const char* f = std::getenv("KDN_FAULT");
+    return f && std::strcmp(f, "launch") == 0;
+}
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, size_t elems, size_t esize) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + elems * esize};
+}
+
+bool overlap(Span a, Span b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from overflow
+
+int validate_common(int variant, int dtype, float mu, int dk, int dv) {
+    if (variant != KDN_DIAGONAL && variant != KDN_ISOTROPIC)
+        return fail(KDN_ERR_UNSUPPORTED, "unknown variant %d", variant);
+    if (dtype != KDN_F32 && dtype != KDN_BF16) return fail(KDN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (!std::isfinite(mu) || mu < 0.f) return fail(KDN_ERR_VALUE, "mu must be finite and >= 0 (got %g)", double(mu));
+    if (dk < 0 || dv < 0) return fail(KDN_ERR_SHAPE, "negative head dimension (dk=%d, dv=%d)", dk, dv);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(KDN_ERR_UNSUPPORTED, "dk and dv must be 64 or 128 (got dk=%d, dv=%d)", dk, dv);
+    return KDN_OK;
+}
+
+int validate_forward(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* omega, const void* r, const float* c0, float mu, int variant,
+                     int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                     const float* p0, void* o, float* S_T, float* p_T, int algo) {
+    int st = validate_common(variant, dtype, mu, dk, dv);
+    if (st != KDN_OK) return st;
+    if (algo != KDN_ALGO_AUTO && algo != KDN_ALGO_RECURRENT && algo != KDN_ALGO_CHUNKED)
+        return fail(KDN_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
+    if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
+    const int64_t units = int64_t(B) * H;
+    const int64_t toks = units * T;
+    if (units > INT32_MAX || toks > kMaxElems / 128)
+        return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
+    if (units == 0) return ok();  // nothing to read or write
+    const bool iso = variant == KDN_ISOTROPIC;
+    if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r || !o))
+        return fail(KDN_ERR_NULL, "q, k, v, alpha, omega, r and o must be non-NULL");
+    if (!S_T || !p_T) return fail(KDN_ERR_NULL, "S_T and p_T must be non-NULL");
+    if (!c0 && !p0) return fail(KDN_ERR_NULL, "c0 may be NULL only when p0 is given");
+
+    const size_t es = dtype == KDN_BF16 ? 2 : 4;
+    const size_t nk = size_t(toks) * dk, nv = size_t(toks) * dv, ng = iso ? size_t(toks) : nk;
+    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * dk;
+    const Span in[] = {span(q, nk, es),      span(k, nk, es),       span(v, nv, es),
+                       span(alpha, ng, es),  span(omega, ng, es),   span(r, size_t(toks), es),
+                       span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4)};
+    const Span so = span(o, nv, es), sS = span(S_T, ns, 4), sp = span(p_T, np, 4);
+    for (const Span& x : in) {
+        if (overlap(so, x) || overlap(sp, x)) return fail(KDN_ERR_ALIAS, "an output overlaps an input");
+        // S_T may be exactly S0 (continuation in place), nothing else
+        if (overlap(sS, x) && !(x.lo == sS.lo && x.hi == sS.hi && S0 && x.lo == reinterpret_cast<uintptr_t>(S0)))
+            return fail(KDN_ERR_ALIAS, "S_T overlaps an input other than S0 itself");
+    }
+    if (overlap(so, sS) || overlap(so, sp) || overlap(sS, sp))
+        return fail(KDN_ERR_ALIAS, "outputs o, S_T, p_T overlap each other");
+    return KDN_OK;
+}
+
+int validate_step(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                  const void* r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
+                  float* S, float* p, void* o) {
+    int st = validate_common(variant, dtype, mu, dk, dv);
+    if (st != KDN_OK) return st;
+    if (N < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (N=%d, H=%d)", N, H);
+    const int64_t units = int64_t(N) * H;
+    if (units > INT32_MAX || units > kMaxElems / (128 * 128))
+        return fail(KDN_ERR_SHAPE, "problem too large (N=%d, H=%d)", N, H);
+    if (units == 0) return ok();
+    if (!q || !k || !v || !alpha || !omega || !r || !o || !S || !p)
+        return fail(KDN_ERR_NULL, "every pointer of kdn_step must be non-NULL");
+    const bool iso = variant == KDN_ISOTROPIC;
+    const size_t es = dtype == KDN_BF16 ? 2 : 4;
+    const size_t nk = size_t(units) * dk, nv = size_t(units) * dv, ng = iso ? size_t(units) : nk;
+    const Span in[] = {span(q, nk, es), span(k, nk, es), span(v, nv, es),
+                       span(alpha, ng, es), span(omega, ng, es), span(r, size_t(units), es)};
+    const Span so = span(o, nv, es), sS = span(S, size_t(units) * dk * dv, 4),
+               sp = span(p, iso ? size_t(units) : nk, 4);
+    for (const Span& x : in)
+        if (overlap(so, x) || overlap(sS, x) || overlap(sp, x))
+            return fail(KDN_ERR_ALIAS, "the state or o overlaps a token input");
+    if (overlap(so, sS) || overlap(so, sp) || overlap(sS, sp))
+        return fail(KDN_ERR_ALIAS, "o, S and p overlap each other");
+    return KDN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    if (e == hipErrorNotSupported) return fail(KDN_ERR_UNSUPPORTED, "%s: shape not supported by this algorithm", what);
+    return fail(KDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kdn_version(void) { return 100; }  // 0.1.0
+
+const char* kdn_status_string(int status) {
+    switch (status) {
+        case KDN_OK: return "ok";
+        case KDN_ERR_NULL: return "a required pointer is NULL";
+        case KDN_ERR_SHAPE: return "invalid size";
+        case KDN_ERR_UNSUPPORTED: return "unsupported variant, dtype, head size or algorithm";
+        case KDN_ERR_VALUE: return "invalid scalar argument";
+        case KDN_ERR_HIP: return "HIP runtime error";
+        case KDN_ERR_ALIAS: return "an output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+const char* kdn_last_error(void) { return g_last_error; }
+
+int kdn_validate_forward(const void* q, const void* k, const void* v, const void* alpha,
+                         const void* omega, const void* r, const float* c0, float mu, int variant,
+                         int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                         const float* p0, void* o, float* S_T, float* p_T, int algo) {
+    const int st = validate_forward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv,
+                                    S0, p0, o, S_T, p_T, algo);
+    return st == KDN_OK ? ok() : st;
+}
+
+int kdn_validate_step(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* omega, const void* r, float mu, int variant, int dtype, int N,
+                      int H, int dk, int dv, float* S, float* p, void* o) {
+    const int st = validate_step(q, k, v, alpha, omega, r, mu, variant, dtype, N, H, dk, dv, S, p, o);
+    return st == KDN_OK ? ok() : st;
+}
+
+int kdn_forward_algo(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* omega, const void* r, const float* c0, float mu, int variant,
+                     int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                     const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo) {
+    const int st = validate_forward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk,
+                                    dv, S0, p0, o, S_T, p_T, algo);
+    if (st != KDN_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv,
+                   S0, p0, o, S_T, p_T};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (algo == KDN_ALGO_CHUNKED) {
+        if (!kdn::chunked_supports(a))
+            return fail(KDN_ERR_UNSUPPORTED, "the chunked algorithm does not support this shape");
+        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
+    }
+    if (algo == KDN_ALGO_AUTO && kdn::chunked_supports(a))
+        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
+    return hip_status(kdn::launch_recurrent(a, s), "recurrent forward");
+}
+
+int kdn_forward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                int H, int dk, int dv, const float* S0, const float* p0, void* o, float* S_T,
+                float* p_T, void* stream) {
+    return kdn_forward_algo(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0,
+                            p0, o, S_T, p_T, stream, KDN_ALGO_AUTO);
+}
+
+int kdn_step(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+             const void* r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
+             float* S, float* p, void* o, void* stream) {
+    const int st = validate_step(q, k, v, alpha, omega, r, mu, variant, dtype, N, H, dk, dv, S, p, o);
+    if (st != KDN_OK) return st;
+    if (int64_t(N) * H == 0) return ok();
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    // one token per sequence: the forward layouts with B = N, T = 1, state in place
+    kdn::FwdArgs a{q, k, v, alpha, omega, r, nullptr, mu, variant, dtype, N, 1, H, dk, dv,
+                   S, p, o, S, p};
+    return hip_status(kdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "decode step");
+}
+
+}  // extern "C"

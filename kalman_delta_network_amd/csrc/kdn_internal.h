@@ -1,0 +1,41 @@
+// kdn_internal.h -- launcher interface between the C ABI (kdn_api.cpp) and the
+// gfx950 kernels.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kdn {
+
+// One forward call, after host validation.  Pointers are device pointers.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* alpha;
+    const void* omega;
+    const void* r;
+    const float* c0;
+    float mu;
+    int variant;  // 0 diagonal, 1 isotropic
+    int dtype;    // 0 f32, 1 bf16
+    int B, T, H, dk, dv;
+    const float* S0;
+    const float* p0;
+    void* o;
+    float* S_T;
+    float* p_T;
+};
+
+// Token-by-token recurrence; one workgroup per (b, h) covering all d_v
+// columns.  Also the decode step (T = 1, S_T == S0, p_T == p0 in place).
+hipError_t launch_recurrent(const FwdArgs& a, hipStream_t stream);
+
+// Chunkwise WY/UT forward on matrix cores.  Returns hipErrorNotSupported
+// for shapes it does not handle (the caller then reports KDN_ERR_UNSUPPORTED).
+bool chunked_supports(const FwdArgs& a);
+hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace kdn

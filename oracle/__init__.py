@@ -59,8 +59,14 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = stp
             fn.restype = I
+        lib.kdn_oracle_num_threads.restype = I
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().kdn_oracle_num_threads())
 
 
 def _f32(x):

@@ -254,3 +254,15 @@ int kdn_oracle_step_iso(int N, int H, int dk, int dv, const float* q, const floa
                         double mu, double* S, double* p, double* o) {
     return step_common(iso_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int kdn_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

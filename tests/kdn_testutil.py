@@ -1,0 +1,59 @@
+"""Shared helpers of the GPU parity tests (inputs to the device, error metric,
+oracle on a sample of heads)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from kalman_delta_network_amd import workloads as wl
+
+TOKEN_INPUTS = ("q", "k", "v", "alpha", "omega", "r")
+
+
+def tol(dtype: str) -> float:
+    """Max relative error allowed against the fp64 oracle: 1e-4 for fp32
+    inputs, 2e-2 for bf16 inputs with fp32 state."""
+    return 1e-4 if dtype == "f32" else 2e-2
+
+
+def rel_err(x, ref) -> float:
+    """max |x - ref| / max |ref| over one output tensor."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    scale = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / (scale if scale > 0 else 1.0))
+
+
+def to_dev(x: dict, dtype: str, device):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(tdt).to(device) for n in TOKEN_INPUTS if n in x}
+    if "c0" in x:
+        out["c0"] = torch.from_numpy(np.ascontiguousarray(x["c0"], np.float32)).to(device)
+    return out
+
+
+def oracle_forward(w: wl.Workload, x: dict, S0=None, p0=None, trace=False):
+    fn = oracle.forward_iso if w.variant == "isotropic" else oracle.forward_diag
+    return fn(**{n: x[n] for n in TOKEN_INPUTS}, c0=x["c0"], mu=w.mu, S0=S0, p0=p0, trace=trace)
+
+
+def oracle_forward_heads(w: wl.Workload, x: dict, pairs):
+    """Oracle on selected (b, h) pairs only; returns {(b,h): result}."""
+    res = {}
+    for b, h in pairs:
+        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in TOKEN_INPUTS}
+        sub["c0"] = x["c0"][h:h + 1]
+        res[(b, h)] = oracle_forward(w, sub)
+    return res
+
+
+def sample_pairs(B: int, H: int, n: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    allp = [(b, h) for b in range(B) for h in range(H)]
+    idx = rng.choice(len(allp), size=min(n, len(allp)), replace=False)
+    picked = {allp[i] for i in idx} | {(0, 0), (B - 1, H - 1)}
+    return sorted(picked)

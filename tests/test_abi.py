@@ -1,0 +1,194 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every symbol
+that include/kdn.h declares, and its host-side validation returns the right
+status for each kind of bad argument.  No call here touches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kalman_delta_network_amd as kdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdn.h")
+
+MiB = 1 << 20
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kdn.LIB_PATH):
+        import __graft_entry__  # noqa: F401  (build() compiles the library)
+        __graft_entry__.build()
+    return kdn.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(kdn.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kdn_version() == 100
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.kdn_status_string(s)
+    assert lib.kdn_status_string(99) == b"unknown status"
+
+
+class Fake:
+    """Distinct fake device addresses, far apart, never dereferenced."""
+
+    def __init__(self):
+        self.base = 1 << 40
+
+    def __call__(self):
+        self.base += 1 << 36
+        return ctypes.c_void_p(self.base)
+
+
+def fwd_args(fake, B=2, T=8, H=2, dk=64, dv=64, variant=0, dtype=1, mu=64.0, algo=0, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), c0=fake(), mu=mu,
+             variant=variant, dtype=dtype, B=B, T=T, H=H, dk=dk, dv=dv, S0=None, p0=None, o=fake(),
+             S_T=fake(), p_T=fake(), algo=algo)
+    a.update(over)
+    return a
+
+
+def call_validate(lib, a):
+    return lib.kdn_validate_forward(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["c0"],
+                                    a["mu"], a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"],
+                                    a["dv"], a["S0"], a["p0"], a["o"], a["S_T"], a["p_T"], a["algo"])
+
+
+def test_validate_forward_accepts_good_arguments(lib):
+    f = Fake()
+    for variant in (0, 1):
+        for dtype in (0, 1):
+            for dk in (64, 128):
+                for dv in (64, 128):
+                    assert call_validate(lib, fwd_args(f, variant=variant, dtype=dtype, dk=dk, dv=dv)) == 0
+    assert call_validate(lib, fwd_args(f, B=0, q=None, o=None, S_T=None)) == 0  # empty batch
+    assert call_validate(lib, fwd_args(f, T=0, q=None, k=None, v=None, o=None)) == 0  # empty sequence
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), kdn.KDN_ERR_NULL),
+    (dict(o=None), kdn.KDN_ERR_NULL),
+    (dict(S_T=None), kdn.KDN_ERR_NULL),
+    (dict(p_T=None), kdn.KDN_ERR_NULL),
+    (dict(c0=None), kdn.KDN_ERR_NULL),
+    (dict(B=-1), kdn.KDN_ERR_SHAPE),
+    (dict(T=-3), kdn.KDN_ERR_SHAPE),
+    (dict(H=-1), kdn.KDN_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12), kdn.KDN_ERR_SHAPE),
+    (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(dv=32), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(dk=-64), kdn.KDN_ERR_SHAPE),
+    (dict(variant=2), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(dtype=7), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(algo=9), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
+    (dict(mu=float("nan")), kdn.KDN_ERR_VALUE),
+    (dict(mu=float("inf")), kdn.KDN_ERR_VALUE),
+])
+def test_validate_forward_rejects(lib, over, status):
+    f = Fake()
+    assert call_validate(lib, fwd_args(f, **over)) == status
+    assert lib.kdn_last_error()
+
+
+def test_validate_forward_c0_optional_with_p0(lib):
+    f = Fake()
+    assert call_validate(lib, fwd_args(f, c0=None, p0=f())) == 0
+
+
+def test_validate_forward_aliasing(lib):
+    f = Fake()
+    a = fwd_args(f)
+    # S_T == S0 is allowed (continuation in place)
+    s = f()
+    assert call_validate(lib, dict(a, S0=s, S_T=s)) == 0
+    # p_T == p0 is not
+    p = f()
+    assert call_validate(lib, dict(a, p0=p, p_T=p)) == kdn.KDN_ERR_ALIAS
+    # o overlapping q
+    assert call_validate(lib, dict(a, o=a["q"])) == kdn.KDN_ERR_ALIAS
+    # S_T partially overlapping S0
+    assert call_validate(lib, dict(a, S0=s, S_T=ctypes.c_void_p(s.value + 256))) == kdn.KDN_ERR_ALIAS
+    # outputs overlapping each other
+    assert call_validate(lib, dict(a, p_T=a["S_T"])) == kdn.KDN_ERR_ALIAS
+
+
+def step_args(fake, N=4, H=2, dk=128, dv=128, variant=0, dtype=1, mu=128.0, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), mu=mu, variant=variant,
+             dtype=dtype, N=N, H=H, dk=dk, dv=dv, S=fake(), p=fake(), o=fake())
+    a.update(over)
+    return a
+
+
+def call_validate_step(lib, a):
+    return lib.kdn_validate_step(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["mu"],
+                                 a["variant"], a["dtype"], a["N"], a["H"], a["dk"], a["dv"], a["S"],
+                                 a["p"], a["o"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), kdn.KDN_OK),
+    (dict(N=0, q=None), kdn.KDN_OK),
+    (dict(S=None), kdn.KDN_ERR_NULL),
+    (dict(p=None), kdn.KDN_ERR_NULL),
+    (dict(N=-1), kdn.KDN_ERR_SHAPE),
+    (dict(dk=32), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(mu=-2.0), kdn.KDN_ERR_VALUE),
+    (dict(variant=5), kdn.KDN_ERR_UNSUPPORTED),
+])
+def test_validate_step(lib, over, status):
+    f = Fake()
+    assert call_validate_step(lib, step_args(f, **over)) == status
+
+
+def test_validate_step_aliasing(lib):
+    f = Fake()
+    a = step_args(f)
+    assert call_validate_step(lib, dict(a, o=a["S"])) == kdn.KDN_ERR_ALIAS
+    assert call_validate_step(lib, dict(a, p=a["k"])) == kdn.KDN_ERR_ALIAS
+
+
+def test_launch_error_path_without_gpu(lib, monkeypatch):
+    # KDN_FAULT=launch: validation passes, then the entry point reports a HIP
+    # error instead of launching
+    monkeypatch.setenv("KDN_FAULT", "launch")
+    f = Fake()
+    a = fwd_args(f)
+    st = lib.kdn_forward(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["c0"], a["mu"],
+                         a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["S0"],
+                         a["p0"], a["o"], a["S_T"], a["p_T"], None)
+    assert st == kdn.KDN_ERR_HIP
+    assert b"KDN_FAULT" in lib.kdn_last_error()
+    s = step_args(f)
+    st = lib.kdn_step(s["q"], s["k"], s["v"], s["alpha"], s["omega"], s["r"], s["mu"], s["variant"],
+                      s["dtype"], s["N"], s["H"], s["dk"], s["dv"], s["S"], s["p"], s["o"], None)
+    assert st == kdn.KDN_ERR_HIP
+    # bad arguments are still reported as such, before the launch stage
+    st = lib.kdn_forward(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["c0"], -1.0,
+                         a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["S0"],
+                         a["p0"], a["o"], a["S_T"], a["p_T"], None)
+    assert st == kdn.KDN_ERR_VALUE
+
+
+def test_binding_raises_when_library_missing(tmp_path):
+    saved = kdn._lib
+    kdn._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            kdn.load_library(str(tmp_path / "nope.so"))
+    finally:
+        kdn._lib = saved
