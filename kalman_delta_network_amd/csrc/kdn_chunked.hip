@@ -1,35 +1,52 @@
-// kdn_chunked.hip -- chunkwise forward of the KDN recurrence on gfx950
-// matrix cores (MFMA).
+// kdn_chunked.hip -- chunkwise forward of the KDN recurrence on gfx950: a
+// pipelined, wave-specialised kernel with the token-to-token coupling on
+// matrix cores (MFMA) and the fp32 memory carried in registers.
 //
-// The sequence of each (batch, head) pair is cut into chunks of L = 64
-// tokens.  The memory S (d_k x d_v, fp32) is carried from chunk to chunk in
-// registers; inside a chunk all 64 writes are applied at once.
+// Method ("Kalman Delta Networks: Uncertainty-aware Associative Memory",
+// summary page, method steps 2-5 and the isotropic closing sentence).  Per
+// (batch, head) and token t, with fp32 state:
+//   p_hat = alpha^2 * p + omega;  kappa = p_hat * k / (r + sum_i p_hat_i k_i^2)
+//   S = diag(alpha) S + kappa (v - (diag(alpha) S)^T k)^T;  o = S^T q
+//   p = p_hat / (1 + (mu / r) k^2 p_hat)
 //
-// Derivation (our own, from the per-token recurrence of the KDN summary
-// page, method steps 2-5).  Inside a chunk write g_t for the cumulative
-// decay prod_{s<=t} alpha_s (per key channel), kappa'_t = p_hat_t * k_t (the
-// gain numerator) and d_t = r_t + sum_i p_hat_t,i k_t,i^2 (the gain
-// denominator), so kappa_t = kappa'_t / d_t.  With
-//   Kt_t = k_t * g_t,   Qt_t = q_t * g_t,   Kh_t = kappa'_t / g_t,
-//   Kb_t = kappa'_t * g_L / g_t                (g_L: decay over the chunk)
-// the innovations delta_t = v_t - (diag(alpha_t) S_{t-1})^T k_t satisfy,
-// for Dn_t = delta_t / d_t,
-//   M Dn = V - Kt S_c,   M = diag(r) + tril(Kt Kh^T)   (diagonal included:
-//                                                     its diagonal is d_t)
+// Chunk form (our derivation from those steps).  The sequence is cut into
+// chunks of L = 32 tokens.  Inside a chunk let g_t be the cumulative decay
+// prod_{s<=t} alpha_s (per key channel), kappa'_t = p_hat_t * k_t the gain
+// numerator and d_t = r_t + sum_i p_hat_t,i k_t,i^2 its denominator.  With
+//   Kt_t = k_t g_t,  Qt_t = q_t g_t,  Kh_t = kappa'_t / g_t
+// and Dn_t = (v_t - (diag(alpha_t) S_{t-1})^T k_t) / d_t, the chunk's writes
+// satisfy
+//   M Dn = V - Kt S_c,        M = diag(r) + tril(Kt Kh^T)  (diagonal included:
+//                                                        M_tt = d_t)
 //   O    = Qt S_c + tril(Qt Kh^T) Dn
-//   S_{c+1} = diag(g_L) S_c + Kb^T Dn
-// which reproduces the token recurrence exactly (up to rounding).  The
-// gain denominator therefore never needs a separate reduction: it is the
-// diagonal of the same matrix product that couples the tokens.  M is lower
-// triangular; it is solved by 16 x 16 blocks: the four diagonal blocks are
-// inverted in fp32 (forward substitution), the block substitution runs on
-// MFMA.
+//   S_{c+1} = diag(g_L) (S_c + Kh^T Dn)
+// which is the token recurrence rewritten exactly.  M is lower triangular;
+// its two 16 x 16 diagonal blocks are inverted in fp32 and the solve is a
+// two-step block substitution on MFMA.  Operands are bf16 with fp32
+// accumulation; S, p and every scalar recurrence stay fp32.
 //
-// Work decomposition: one workgroup per (batch, head, 64-column tile of
-// d_v); 4 waves.  The per-channel part (uncertainty predict / posterior,
-// decay products, MFMA operands) is computed by every tile of a head; the
-// column part is split across waves, 16 value columns each.  Operands are
-// bf16 with fp32 accumulation; the state and the uncertainty stay fp32.
+// The uncertainty recurrence is a Mobius map of p (summary page, step 5):
+// p_t = (a p + w) / (u a p + 1 + u w) with a = alpha^2, w = omega, u = mu k^2 / r.
+//  - Diagonal variant: 128 independent channels per head fill a wave's lanes,
+//    so each lane runs its channel's map sequentially (one fma, one fma, one
+//    reciprocal, one multiply per token); this is the cheapest form in issued
+//    instructions, several times cheaper than a cross-lane scan over tokens.
+//  - Isotropic variant: one scalar per head, so the maps of a chunk's 32
+//    tokens (one per lane) are composed as 2 x 2 matrix products by an
+//    inclusive cross-lane scan (5 shuffle levels, renormalised each level).
+//
+// Workgroup = one (batch, head) pair and 64 value columns, 8 waves in roles:
+//   waves 0,1      "chain":     uncertainty recurrence of chunk c+2 -> gain
+//                               numerators kappa' and decays g (LDS)
+//   waves 2,3,6,7  "formation": MFMA operands Kt, Qt, Kh, Kh^T of chunk c+1,
+//                               then M, tril(Qt Kh^T) and the diagonal-block
+//                               inverses of M
+//   waves 4,5      "state":     memory pass of chunk c: 32 value columns each,
+//                               S (d_k x 32 fp32) in registers
+// Two workgroup barriers per iteration; every LDS buffer that crosses an
+// iteration is double buffered, and global inputs are prefetched into
+// registers one iteration ahead.  Roles run on all four SIMDs so the chain's
+// VALU work overlaps the MFMA work of the other roles.
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -39,319 +56,744 @@
 namespace kdn {
 namespace {
 
-constexpr int L = 64;     // chunk length
-constexpr int NWAVE = 4;  // waves per workgroup
-constexpr int DVT = 64;   // value columns per workgroup
+constexpr int L = 32;            // tokens per chunk
+constexpr int NT = L / 16;       // 16-token tiles per chunk
+constexpr int DVT = 64;          // value columns per workgroup
+constexpr int NTHREADS = 512;    // 8 waves
+constexpr int PT = L + 8;        // pitch (elements) of [rows][L] bf16 tiles
+constexpr int CHAIN_SPLIT = 22;  // chain tokens run before the mid-iteration barrier
+static_assert(L == 32 && NT == 2, "the kernel is written for 32-token chunks");
 
 typedef uint16_t bf16_t;
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
-typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float ld_f32(const bf16_t* p, size_t i) {
-    return __uint_as_float(uint32_t(p[i]) << 16);
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float bf1(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// float -> bf16, round to nearest even (hardware conversion on gfx950)
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    b2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
-
+__device__ __forceinline__ bf16_t to_bf(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(bf16_t, b);
+}
 __device__ __forceinline__ s4 pack4(f4 x) {
-    b4 b;
-    b[0] = (__bf16)x[0];
-    b[1] = (__bf16)x[1];
-    b[2] = (__bf16)x[2];
-    b[3] = (__bf16)x[3];
-    return __builtin_bit_cast(s4, b);
+    u2 u;
+    u[0] = pack2(x[0], x[1]);
+    u[1] = pack2(x[2], x[3]);
+    return __builtin_bit_cast(s4, u);
+}
+__device__ __forceinline__ b8 pack8(f4 x, f4 y) {
+    u4 u;
+    u[0] = pack2(x[0], x[1]);
+    u[1] = pack2(x[2], x[3]);
+    u[2] = pack2(y[0], y[1]);
+    u[3] = pack2(y[2], y[3]);
+    return __builtin_bit_cast(b8, u);
 }
 
-__device__ __forceinline__ s4 lds4(const __bf16* p) { return *reinterpret_cast<const s4*>(p); }
-
+// D = A B + C on one 16 x 16 tile.  16x16x32: lane l holds A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16] and C[4(l/16)..+3][l%16].  16x16x16: the same with
+// 4 K values per lane.
+__device__ __forceinline__ f4 mfma32(b8 a, b8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void st_out(bf16_t* p, float x) {
-    __bf16 b = (__bf16)x;
-    *p = __builtin_bit_cast(bf16_t, b);
+// K-slot order of 16x16x32 operands.  A register operand built from two
+// 16-row C tiles (rows 4g..4g+3 of each, lane group g) carries the K indices
+// {32kk + 4g + j, 32kk + 16 + 4g + j}; LDS operands are stored with column i
+// at position perm32(i) so that lane group g's 8 consecutive elements are
+// the same K indices.
+__device__ __forceinline__ int perm32(int i) {
+    return (i & ~31) | ((i & 12) << 1) | ((i & 16) >> 2) | (i & 3);
+}
+
+// [rows][DK] bf16 tiles: 16-byte chunk c of row r sits at chunk c ^ r so that
+// the 16 rows an MFMA operand read touches hit distinct banks.
+template <int DK>
+__device__ __forceinline__ int sw(int row, int col) {
+    constexpr int NCH = DK / 8;
+    return row * DK + ((((col >> 3) ^ row) & (NCH - 1)) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int DK>
 struct Smem {
-    static constexpr int PK = DK + 8;   // pitch of [L][DK] tiles (bf16)
-    static constexpr int PL = L + 8;    // pitch of [*][L] tiles (bf16)
-    static constexpr int PV = DVT + 8;  // pitch of the v tile (bf16)
-    __bf16 Kn[L * PK];      // -k_t * g_t
-    __bf16 Qt[L * PK];      // q_t * g_t
-    __bf16 Kh[L * PK];      // kappa'_t / g_t
-    __bf16 KbT[DK * PL];    // (kappa'_t * g_L / g_t)^T, [channel][token]
-    __bf16 Mn[L * PL];      // -M below the diagonal blocks
-    __bf16 QK[L * PL];      // tril(Qt Kh^T)
-    __bf16 Td[4 * 16 * 16]; // inverses of M's diagonal 16x16 blocks [block][t][s]
-    __bf16 Vt[L * PV];      // v tile of this workgroup's columns
-    float Md[4 * 16 * 17];  // M's diagonal blocks, fp32 [block][t][s]
-    float cr[L];            // mu / r_t (diagonal) or mu / (d_k r_t) (isotropic)
-    float rr[L];            // r_t (1 for padding tokens)
-    float nn[L];            // |k_t|^2 (isotropic)
-    float bh[L];            // b_hat_t (isotropic)
-    float gs[L];            // scalar decay products (isotropic)
-    float gL[DK];           // g_L per channel
+    bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
+    bf16_t Qt[2][L * DK];    //  q_t g_t
+    bf16_t Kh[2][L * DK];    // kappa'_t (chain), then kappa'_t / g_t (formation)
+    bf16_t KhT[2][DK * PT];  // (kappa'_t / g_t)^T  [i][perm32(t)]
+    bf16_t QK[2][L * PT];    // tril(Qt Kh^T)      [t][perm32(s)]
+    bf16_t Td[2][NT * 256];  // inverses of M's diagonal blocks [a][t][s]
+    bf16_t Mo[2][256];       // -M's block (1,0)   [t][s]
+    bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
+    bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
+    bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
+    bf16_t RW[2][L * DK];
+    float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
+    float rr[2][L];          // r_t
+    float bh[2][L];          // b_hat_t (isotropic)
+    float gs[2][L];          // g_t (isotropic, scalar)
+    float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
 };
 
-template <int DK, bool ISO>
-__global__ void __launch_bounds__(NWAVE * 64)
-kdn_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                 const bf16_t* __restrict__ v, const bf16_t* __restrict__ alpha,
-                 const bf16_t* __restrict__ omega, const bf16_t* __restrict__ r,
-                 const float* __restrict__ c0, float mu, int T, int H, int DV, int units,
-                 const float* S0, const float* __restrict__ p0, bf16_t* __restrict__ o,
-                 float* S_T, float* __restrict__ p_T) {
-    using SM = Smem<DK>;
-    constexpr int PK = SM::PK, PL = SM::PL, PV = SM::PV;
-    constexpr int KT = DK / 16;  // 16-row tiles of the key dimension
-    __shared__ SM sm;
+struct Args {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const bf16_t* alpha;
+    const bf16_t* omega;
+    const bf16_t* r;
+    const float* c0;
+    float mu;
+    int T, H, DV, units;
+    const float* S0;
+    const float* p0;
+    bf16_t* o;
+    float* S_T;
+    float* p_T;
+};
 
-    // block -> (unit, column tile); the tiles of one unit share an XCD
-    const int ntile = DV / DVT;
+// position of token t of the sequence of (b, h) in the [B,T,H] token grid
+__device__ __forceinline__ size_t tokidx(const Args& a, size_t b, int h, int t) {
+    return (b * size_t(a.T) + size_t(t)) * size_t(a.H) + size_t(h);
+}
+
+constexpr uint32_t BF_ONE = 0x3f80u;  // bf16 1.0
+
+// ---------------------------------------------------------------------------
+// chain role, diagonal variant: lane = key channel
+// ---------------------------------------------------------------------------
+// Loaders below issue unconditional loads from clamped addresses and never
+// touch the loaded registers: any use inside a loader would make the compiler
+// wait for each load in turn.  Tokens past the end of the sequence read the
+// last token and are masked where the values are used (tail chunk only).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes from `src`
+// land at dst + 16 l (dst uniform across the wave).  (The sub-dword forms of
+// this load place one dword per lane, so they are not used for bf16 data.)
+__device__ __forceinline__ void g2lds16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// Issue the raw k, alpha, omega tiles of chunk c into LDS buffer c & 1.
+// The chain waves split the 16-byte pieces; rows past the end of the
+// sequence repeat the last token (masked where used).
+template <int DK>
+__device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, size_t b, int h, int c,
+                                                 int nchunks, int w) {
+    if (c < 0 || c >= nchunks) return;
+    constexpr int NW = DK / 64;           // chain waves
+    constexpr int PR = DK / 8;            // 16-byte pieces per row
+    constexpr int PER = L * PR / 64 / NW; // instructions per tile per wave
+    const int lane = threadIdx.x & 63;
+    const int buf = c & 1;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int blk = w + NW * m;  // 64-piece block of the tile
+        const int pc = lane + 64 * blk;
+        const size_t off = tokidx(a, b, h, min(c * L + pc / PR, a.T - 1)) * DK + (pc % PR) * 8;
+        g2lds16(a.k + off, &sm.RK[buf][blk * 512]);
+        g2lds16(a.alpha + off, &sm.RA[buf][blk * 512]);
+        g2lds16(a.omega + off, &sm.RW[buf][blk * 512]);
+    }
+}
+
+// r_t of chunk c for lane t (lanes >= L repeat the chunk's last token)
+__device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h, int c, int nchunks) {
+    if (c < 0 || c >= nchunks) return BF_ONE;
+    const int lane = threadIdx.x & 63;
+    return a.r[tokidx(a, b, h, min(c * L + min(lane, L - 1), a.T - 1))];
+}
+
+// tokens [T0, T1) of chunk buffer buf with nvalid real tokens; p carries
+// across chunks, g restarts at every chunk.  Padding tokens (t >= nvalid) act
+// as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
+// gain.
+template <int DK, int T0, int T1, bool MASK>
+__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float cr, float& p, float& g,
+                                               int nvalid, int gring) {
+#pragma unroll
+    for (int t = T0; t < T1; ++t) {
+        float kk = bf1(sm.RK[buf][t * DK + i]);
+        float al = bf1(sm.RA[buf][t * DK + i]);
+        float w = bf1(sm.RW[buf][t * DK + i]);
+        if (MASK) {
+            const bool ok = t < nvalid;
+            kk = ok ? kk : 0.f;
+            al = ok ? al : 1.f;
+            w = ok ? w : 0.f;
+        }
+        const float ct = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), t));
+        const float asq = al * al;
+        const float u = ct * kk * kk;
+        const float ph = fmaf(asq, p, w);
+        p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
+        g *= al;
+        sm.Kh[buf][sw<DK>(t, perm32(i))] = to_bf(ph * kk);
+        sm.G[buf][t * DK + i] = to_bf(g);
+        if (t == L - 1) sm.gL[gring][i] = g;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chain role, isotropic variant: lane = token (lanes 32..63 help with |k|^2)
+// ---------------------------------------------------------------------------
+struct ChainIsoRegs {
+    u4 kr[8];            // half a k row (DK/2 channels) of token lane & 31
+    uint32_t al, w, rv;  // alpha, omega, r of token lane & 31
+};
+
+template <int DK>
+__device__ __forceinline__ void chain_iso_load(ChainIsoRegs& X, const Args& a, size_t b, int h, int c,
+                                               int nchunks) {
+    if (c < 0 || c >= nchunks) return;
+    const int lane = threadIdx.x & 63;
+    const size_t e = tokidx(a, b, h, min(c * L + (lane & 31), a.T - 1));
+    constexpr int NQ = DK / 16;  // 16-byte pieces per half row
+    const u4* src = reinterpret_cast<const u4*>(a.k + e * DK + (lane >> 5) * (DK / 2));
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) X.kr[m] = src[m];
+    X.al = a.alpha[e];
+    X.w = a.omega[e];
+    X.rv = a.r[e];
+}
+
+template <int DK>
+__device__ __forceinline__ void chain_iso_run(const ChainIsoRegs& X, Smem<DK>& sm, int buf, float mu,
+                                              float& bprev, int nvalid, int gring) {
+    const int lane = threadIdx.x & 63;
+    const bool ok = (lane & 31) < nvalid;
+    constexpr int NQ = DK / 16;
+    float n = 0.f;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = bf_lo(X.kr[m][e]), x1 = bf_hi(X.kr[m][e]);
+            n = fmaf(x0, x0, n);
+            n = fmaf(x1, x1, n);
+        }
+    n += __shfl_xor(n, 32, 64);
+    const float al = ok ? bf1(bf16_t(X.al)) : 1.f;
+    const float w = ok ? bf1(bf16_t(X.w)) * (1.f / float(DK)) : 0.f;
+    const float rt = ok ? bf1(bf16_t(X.rv)) : 1.f;
+    const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
+    const float asq = al * al;
+    // this token's Mobius matrix [[m00, m01], [m10, m11]] and decay
+    float m00 = asq, m01 = w, m10 = cn * asq, m11 = fmaf(cn, w, 1.f);
+    float g = al;
+#pragma unroll
+    for (int d = 1; d < L; d <<= 1) {
+        const float x00 = __shfl_up(m00, d, 32), x01 = __shfl_up(m01, d, 32);
+        const float x10 = __shfl_up(m10, d, 32), x11 = __shfl_up(m11, d, 32);
+        const float gg = __shfl_up(g, d, 32);
+        if ((lane & 31) >= d) {
+            // (this block) x (earlier block)
+            const float y00 = fmaf(m00, x00, m01 * x10), y01 = fmaf(m00, x01, m01 * x11);
+            const float y10 = fmaf(m10, x00, m11 * x10), y11 = fmaf(m10, x01, m11 * x11);
+            const float s = __builtin_amdgcn_rcpf(y11);
+            m00 = y00 * s;
+            m01 = y01 * s;
+            m10 = y10 * s;
+            m11 = 1.f;
+            g *= gg;
+        }
+    }
+    const float bt = (m00 * bprev + m01) / (m10 * bprev + m11);  // b after token t
+    float bbefore = __shfl_up(bt, 1, 32);
+    if ((lane & 31) == 0) bbefore = bprev;
+    if (lane < L) {
+        sm.bh[buf][lane] = fmaf(asq, bbefore, w);
+        sm.gs[buf][lane] = g;
+        sm.rr[buf][lane] = rt;
+    }
+    bprev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt), L - 1));
+    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
+    for (int i = lane; i < DK; i += 64) sm.gL[gring][i] = gl;
+}
+
+// ---------------------------------------------------------------------------
+// formation role: wave f in 0..3 owns tokens [8f, 8f + 8) of a chunk
+// ---------------------------------------------------------------------------
+template <int DK>
+struct FormRegs {
+    uint32_t kp[8];  // DK = 128: channels 2l, 2l+1; DK = 64: channel l (low half)
+    uint32_t qp[8];
+};
+
+template <int DK>
+__device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t b, int h, int f, int c,
+                                          int nchunks) {
+    if (c < 0 || c >= nchunks) return;
+    const unsigned lane = threadIdx.x & 63;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const size_t e = tokidx(a, b, h, min(c * L + 8 * f + tt, a.T - 1)) * DK;
+        if (DK == 128) {
+            X.kp[tt] = reinterpret_cast<const uint32_t*>(a.k + e)[lane];
+            X.qp[tt] = reinterpret_cast<const uint32_t*>(a.q + e)[lane];
+        } else {
+            X.kp[tt] = (a.k + e)[lane];
+            X.qp[tt] = (a.q + e)[lane];
+        }
+    }
+}
+
+template <int DK, bool ISO>
+__device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int f, int nvalid) {
+    const int lane = threadIdx.x & 63;
+    if (DK == 128) {
+        const int i0 = 2 * lane;
+        const int pos = perm32(i0);  // perm32(i0 + 1) == pos + 1
+        uint32_t t0w[4], t1w[4];     // Kh^T staging: 4 tokens of channels i0, i0+1
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const int t = 8 * f + tt;
+            const int off = sw<DK>(t, pos);
+            float g0, g1, kh0, kh1;
+            const uint32_t kp = t < nvalid ? X.kp[tt] : 0u, qp = t < nvalid ? X.qp[tt] : 0u;
+            const float k0 = bf_lo(kp), k1 = bf_hi(kp);
+            const float q0 = bf_lo(qp), q1 = bf_hi(qp);
+            if (ISO) {
+                g0 = g1 = sm.gs[nb][t];
+                const float s = sm.bh[nb][t] * __builtin_amdgcn_rcpf(g0);
+                kh0 = k0 * s;
+                kh1 = k1 * s;
+            } else {
+                const uint32_t gg = *reinterpret_cast<const uint32_t*>(&sm.G[nb][t * DK + i0]);
+                g0 = bf_lo(gg);
+                g1 = bf_hi(gg);
+                const uint32_t kap = *reinterpret_cast<const uint32_t*>(&sm.Kh[nb][off]);
+                kh0 = bf_lo(kap) * __builtin_amdgcn_rcpf(g0);
+                kh1 = bf_hi(kap) * __builtin_amdgcn_rcpf(g1);
+            }
+            const uint32_t khp = pack2(kh0, kh1);
+            *reinterpret_cast<uint32_t*>(&sm.Kn[nb][off]) = pack2(-k0 * g0, -k1 * g1);
+            *reinterpret_cast<uint32_t*>(&sm.Qt[nb][off]) = pack2(q0 * g0, q1 * g1);
+            *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khp;
+            const int j = tt & 3;
+            if (j == 0) {
+                t0w[0] = t0w[1] = t1w[0] = t1w[1] = 0;
+            }
+            // pair (token j, token j+1) per 32-bit word
+            if (j & 1) {
+                t0w[j >> 1] |= (khp & 0xffffu) << 16;
+                t1w[j >> 1] |= khp & 0xffff0000u;
+            } else {
+                t0w[j >> 1] = khp & 0xffffu;
+                t1w[j >> 1] = khp >> 16;
+            }
+            if (j == 3) {
+                const int tp = perm32(t - 3);
+                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) = u2{t0w[0], t0w[1]};
+                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + 1) * PT + tp]) = u2{t1w[0], t1w[1]};
+            }
+        }
+    } else {
+        const int i = lane;
+        const int pos = perm32(i);
+        uint32_t tw[2];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const int t = 8 * f + tt;
+            const int off = sw<DK>(t, pos);
+            const float kk = t < nvalid ? bf_lo(X.kp[tt]) : 0.f, qq = t < nvalid ? bf_lo(X.qp[tt]) : 0.f;
+            float g, kh;
+            if (ISO) {
+                g = sm.gs[nb][t];
+                kh = kk * sm.bh[nb][t] * __builtin_amdgcn_rcpf(g);
+            } else {
+                g = bf1(sm.G[nb][t * DK + i]);
+                kh = bf1(sm.Kh[nb][off]) * __builtin_amdgcn_rcpf(g);
+            }
+            const bf16_t khb = to_bf(kh);
+            sm.Kn[nb][off] = to_bf(-kk * g);
+            sm.Qt[nb][off] = to_bf(qq * g);
+            sm.Kh[nb][off] = khb;
+            const int j = tt & 3;
+            if (j & 1) tw[j >> 1] |= uint32_t(khb) << 16;
+            else tw[j >> 1] = khb;
+            if (j == 3) *reinterpret_cast<u2*>(&sm.KhT[nb][i * PT + perm32(t - 3)]) = u2{tw[0], tw[1]};
+        }
+    }
+}
+
+// M, tril(Qt Kh^T) and the diagonal-block inverses of chunk buffer nb
+template <int DK>
+__device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g4 = (lane >> 4) * 4;
+    const int kg8 = (lane >> 4) * 8;
+    constexpr int KS = DK / 32;
+    auto tile = [&](const bf16_t* A, int ra, int rb) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const b8 av = *reinterpret_cast<const b8*>(A + sw<DK>(ra + n, 32 * kk + kg8));
+            const b8 bv = *reinterpret_cast<const b8*>(sm.Kh[nb] + sw<DK>(rb + n, 32 * kk + kg8));
+            acc = mfma32(av, bv, acc);
+        }
+        return acc;  // acc[e] = row ra + g4 + e, column rb + n
+    };
+    if (f == 0) {
+        // diagonal blocks of M = diag(r) + tril(Kt Kh^T); Kn holds -Kt
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+            const f4 acc = tile(sm.Kn[nb], 16 * a, 16 * a);
+            f4 mv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tl = g4 + e;
+                mv[e] = tl > n ? -acc[e] : (tl == n ? sm.rr[nb][16 * a + tl] - acc[e] : 0.f);
+            }
+            *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;
+        }
+        wave_lds_sync();
+        // forward substitution, lane = (block a, column s): fp32 inverse
+        if (lane < NT * 16) {
+            const int a = lane >> 4, s = lane & 15;
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[t] = (t == s) ? 1.f : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float* col = &sm.Md[a * 256 + u * 16];
+                x[u] *= __builtin_amdgcn_rcpf(col[u]);
+#pragma unroll
+                for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-col[t], x[u], x[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) sm.Td[nb][a * 256 + t * 16 + s] = to_bf(x[t]);
+        }
+    } else if (f == 1) {
+        // block (1,0) of M is -acc; store -M_10 = acc for the substitution
+        const f4 acc = tile(sm.Kn[nb], 16, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Mo[nb][(g4 + e) * 16 + n] = to_bf(acc[e]);
+    } else if (f == 2) {
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+            const f4 acc = tile(sm.Qt[nb], 16 * a, 16 * a);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sm.QK[nb][(16 * a + g4 + e) * PT + perm32(16 * a + n)] = to_bf(g4 + e >= n ? acc[e] : 0.f);
+        }
+    } else {
+        const f4 acc = tile(sm.Qt[nb], 16, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.QK[nb][(16 + g4 + e) * PT + perm32(n)] = to_bf(acc[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// state role: wave cw in {0,1} owns 32 value columns, S in registers
+// ---------------------------------------------------------------------------
+struct StateRegs {
+    uint32_t vv[NT][2][4];  // bf16 bits of v at rows 16a + 4g + e, column tile ct
+};
+
+__device__ __forceinline__ void state_load(StateRegs& X, const Args& a, size_t b, int h, int colb, int c,
+                                           int nchunks) {
+    if (c < 0 || c >= nchunks) return;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    // rows differ per lane group: one 64-bit base per row, 32-bit column offsets
+#pragma unroll
+    for (int at = 0; at < NT; ++at)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16_t* row = a.v + tokidx(a, b, h, min(c * L + 16 * at + g4 + e, a.T - 1)) * a.DV;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) X.vv[at][ct][e] = row[unsigned(colb + 16 * ct + n)];
+        }
+}
+
+template <int DK>
+struct StateAcc {
+    f4 S[DK / 16][2];
+    f4 R[NT][2];
+    f4 O[NT][2];
+};
+
+template <int DK>
+__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, const StateRegs& X, Smem<DK>& sm, int b,
+                                           int nvalid) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
+    constexpr int KS = DK / 32;
+    b8 Sb[KS][2];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = 16 * at + g4 + e < nvalid ? bf1(bf16_t(X.vv[at][ct][e])) : 0.f;
+            f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const b8 ak = *reinterpret_cast<const b8*>(sm.Kn[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
+                const b8 aq = *reinterpret_cast<const b8*>(sm.Qt[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
+                r = mfma32(ak, Sb[kk][ct], r);  // V - Kt S
+                o = mfma32(aq, Sb[kk][ct], o);  // Qt S
+            }
+            st.R[at][ct] = r;
+            st.O[at][ct] = o;
+        }
+    }
+}
+
+template <int DK>
+__device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
+                                           int h, int colb, int c) {
+    const int gring = c % 3;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
+    const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
+    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
+    b8 Db[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const f4 d0 = mfma16(t0, pack4(st.R[0][ct]), zero);
+        const f4 r1 = mfma16(mo, pack4(d0), st.R[1][ct]);
+        const f4 d1 = mfma16(t1, pack4(r1), zero);
+        Db[ct] = pack8(d0, d1);
+    }
+    // outputs
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+        const b8 aqk = *reinterpret_cast<const b8*>(&sm.QK[b][(16 * at + n) * PT + kg8]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f4 o = mfma32(aqk, Db[ct], st.O[at][ct]);
+            const int col = colb + 16 * ct + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = c * L + 16 * at + g4 + e;
+                if (t < a.T) a.o[tokidx(a, bb, h, t) * a.DV + col] = to_bf(o[e]);
+            }
+        }
+    }
+    // S <- diag(g_L) (S + Kh^T Dn)
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+        const b8 ak = *reinterpret_cast<const b8*>(&sm.KhT[b][(16 * it + n) * PT + kg8]);
+        const f4 gl = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f4 s = mfma32(ak, Db[ct], st.S[it][ct]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] *= gl[e];
+            st.S[it][ct] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int DK, bool ISO>
+__global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
+    __shared__ Smem<DK> sm;
+    const int ntile = a.DV / DVT;
     const int bid = blockIdx.x;
+    // the column tiles of one (batch, head) pair share an XCD (and its L2)
     const int unit = (bid / (8 * ntile)) * 8 + (bid % 8);
     const int tile = (bid / 8) % ntile;
-    if (unit >= units) return;
-    const int h = unit % H;
-    const size_t b = size_t(unit / H);
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int n = lane & 15;  // MFMA column / A-operand row within a 16-tile
-    const int g4 = (lane >> 4) * 4;
-    const int col = tile * DVT + wave * 16 + n;  // this lane's value column
+    if (unit >= a.units) return;
+    const int h = unit % a.H;
+    const size_t b = size_t(unit / a.H);
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    const int nchunks = (a.T + L - 1) / L;
+    const int nit = ((nchunks + 2) + 1) & ~1;  // even number of pipeline iterations
 
-    // ---- initial state ----
-    f4 S[KT];
-    const size_t sbase = size_t(unit) * DK * DV;
-#pragma unroll
-    for (int it = 0; it < KT; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[it][e] = S0 ? S0[sbase + size_t(16 * it + g4 + e) * DV + col] : 0.f;
-    float p = 0.f;  // diagonal: channel `tid` (tid < DK); isotropic: thread 0
-    if (ISO) {
-        if (tid == 0) p = p0 ? p0[unit] : c0[h];
-    } else if (tid < DK) {
-        p = p0 ? p0[size_t(unit) * DK + tid] : c0[h];
+    // the chain's first input tiles
+    if (!ISO && wave < DK / 64) chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, wave);
+    // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31: zero them once
+    for (int e = threadIdx.x; e < 2 * 16 * 16; e += NTHREADS) {
+        const int bb = e >> 8, t = (e >> 4) & 15, s = 16 + (e & 15);
+        sm.QK[bb][t * PT + perm32(s)] = 0;
     }
+    __builtin_amdgcn_s_waitcnt(0);  // direct LDS loads complete before the barrier
+    __syncthreads();
 
-    const int nchunks = (T + L - 1) / L;
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * L;
-        const int nvalid = min(L, T - t0);
-        auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t0 + t)) * size_t(H) + size_t(h); };
-
-        // ---- phase 1: per-token scalars and the v tile ----
-        if (tid < L) {
-            const int t = tid;
-            float rt = 1.f, cc = 0.f, nk = 0.f;
-            if (t < nvalid) {
-                rt = ld_f32(r, tokidx(t));
-                cc = ISO ? mu / (float(DK) * rt) : mu / rt;
-                if (ISO) {
-                    const bf16_t* kr = k + tokidx(t) * DK;
-                    for (int i = 0; i < DK; ++i) {
-                        const float x = ld_f32(kr, i);
-                        nk += x * x;
+    if (wave == 0 || wave == 1) {
+        // ---------------- chain ----------------
+        if (!ISO) {
+            const bool active = wave < DK / 64;
+            const int i = wave * 64 + lane;
+            float p = 0.f;
+            if (active) p = a.p0 ? a.p0[size_t(unit) * DK + i] : a.c0[h];
+            uint32_t rnext = chain_r_load(a, b, h, 0, nchunks);
+            for (int c = 0; c < nit; ++c) {
+                // chunk c's tiles are in LDS buffer c & 1; chunk c + 1's are fetched meanwhile
+                const int buf = c & 1;
+                const int nvalid = min(L, a.T - c * L);
+                float cr = 0.f, g = 1.f;
+                const uint32_t rcur = rnext;  // loaded before the previous barrier
+                if (active) {
+                    chain_diag_issue<DK>(sm, a, b, h, c + 1, nchunks, wave);
+                    rnext = chain_r_load(a, b, h, c + 1, nchunks);
+                    if (c < nchunks) {
+                        const float rt = lane < nvalid ? bf1(bf16_t(rcur)) : 1.f;
+                        cr = lane < nvalid ? a.mu / rt : 0.f;
+                        if (wave == 0 && lane < L) sm.rr[buf][lane] = rt;
+                        if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, cr, p, g, L, c % 3);
+                        else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
                     }
                 }
-            }
-            sm.rr[t] = rt;
-            sm.cr[t] = cc;
-            sm.nn[t] = nk;
-        }
-        for (int e = tid; e < L * DVT; e += NWAVE * 64) {
-            const int t = e / DVT, j = e % DVT;
-            const float x = t < nvalid ? ld_f32(v, tokidx(t) * size_t(DV) + tile * DVT + j) : 0.f;
-            sm.Vt[t * PV + j] = (__bf16)x;
-        }
-        __syncthreads();
-        if (ISO && tid == 0) {
-            // scalar uncertainty chain of the chunk (trace-projected predict,
-            // averaged precision increment)
-            float g = 1.f;
-            for (int t = 0; t < L; ++t) {
-                float a = 1.f, w = 0.f;
-                if (t < nvalid) {
-                    a = ld_f32(alpha, tokidx(t));
-                    w = ld_f32(omega, tokidx(t));
+                __syncthreads();
+                if (active && c < nchunks) {
+                    if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, cr, p, g, L, c % 3);
+                    else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
                 }
-                const float ph = a * a * p + w * (1.f / float(DK));
-                p = ph / (1.f + sm.cr[t] * sm.nn[t] * ph);
-                g *= a;
-                sm.bh[t] = ph;
-                sm.gs[t] = g;
+                __builtin_amdgcn_s_waitcnt(0);  // chunk c + 1's tiles have landed
+                __syncthreads();
             }
-        }
-        if (ISO) __syncthreads();
-
-        // ---- phase 2: per-channel recurrence and MFMA operands ----
-        if (tid < DK) {
-            const int i = tid;
-            float g = 1.f;
-            float kh[L];
+            if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
+        } else {
+            float bprev = a.p0 ? a.p0[unit] : a.c0[h];
+            ChainIsoRegs A, B;
+            if (wave == 0) chain_iso_load<DK>(A, a, b, h, 0, nchunks);
+            for (int it = 0; it < nit; it += 2) {
 #pragma unroll
-            for (int t = 0; t < L; ++t) {
-                float a = 1.f, w = 0.f, kk = 0.f, qq = 0.f;
-                if (t < nvalid) {
-                    const size_t base = tokidx(t) * DK + i;
-                    kk = ld_f32(k, base);
-                    qq = ld_f32(q, base);
-                    if (!ISO) {
-                        a = ld_f32(alpha, base);
-                        w = ld_f32(omega, base);
+                for (int half = 0; half < 2; ++half) {
+                    ChainIsoRegs& X = half ? B : A;
+                    ChainIsoRegs& Y = half ? A : B;
+                    const int c = it + half;
+                    if (wave == 0) {
+                        chain_iso_load<DK>(Y, a, b, h, c + 1, nchunks);
+                        if (c < nchunks) chain_iso_run<DK>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
                     }
-                }
-                float ph;
-                if (ISO) {
-                    ph = sm.bh[t];
-                    g = sm.gs[t];
-                } else {
-                    ph = a * a * p + w;
-                    p = ph / (1.f + sm.cr[t] * kk * kk * ph);
-                    g *= a;
-                }
-                sm.Kn[t * PK + i] = (__bf16)(-kk * g);
-                sm.Qt[t * PK + i] = (__bf16)(qq * g);
-                kh[t] = ph * kk / g;
-            }
-            sm.gL[i] = g;
-#pragma unroll
-            for (int t = 0; t < L; ++t) {
-                sm.Kh[t * PK + i] = (__bf16)kh[t];
-                sm.KbT[i * PL + t] = (__bf16)(kh[t] * g);
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 3: M = diag(r) + tril(Kt Kh^T) and tril(Qt Kh^T) ----
-        for (int job = wave; job < 20; job += NWAVE) {
-            const bool isM = job < 10;
-            int jt = isM ? job : job - 10;
-            int a = 0;
-            while (jt > a) { jt -= a + 1; ++a; }
-            const int bb = jt;  // tile (a, bb), bb <= a
-            const __bf16* A = isM ? sm.Kn : sm.Qt;
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KT; ++kb)
-                acc = mfma16(lds4(A + (16 * a + n) * PK + 16 * kb + g4),
-                             lds4(sm.Kh + (16 * bb + n) * PK + 16 * kb + g4), acc);
-            // acc[e] holds row t = 16a + g4 + e, column s = 16bb + n
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tl = g4 + e, sl = n;
-                const int t = 16 * a + tl, s = 16 * bb + sl;
-                if (isM) {
-                    if (a == bb) {
-                        float mv = 0.f;
-                        if (sl < tl) mv = -acc[e];
-                        if (sl == tl) mv = sm.rr[t] - acc[e];
-                        sm.Md[(a * 16 + tl) * 17 + sl] = mv;
-                    } else {
-                        sm.Mn[t * PL + s] = (__bf16)acc[e];
-                    }
-                } else {
-                    sm.QK[t * PL + s] = (__bf16)((a != bb || sl <= tl) ? acc[e] : 0.f);
+                    __syncthreads();
+                    __syncthreads();
                 }
             }
+            if (wave == 0 && lane == 0 && tile == 0) a.p_T[unit] = bprev;
         }
-        __syncthreads();
-
-        // ---- phase 4: inverses of M's diagonal blocks (fp32) ----
-        if (wave == 0) {
-            const int a = lane >> 4, s = lane & 15;
-            const float* Mb = sm.Md + a * 16 * 17;
-            float X[16];
+    } else if (wave == 4 || wave == 5) {
+        // ---------------- state ----------------
+        const int cw = wave - 4;
+        const int colb = tile * DVT + cw * 32;
+        const int n = lane & 15, g4 = (lane >> 4) * 4;
+        StateAcc<DK> st;
+        const size_t sbase = size_t(unit) * DK * a.DV;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == s) ? 1.f : 0.f;
+        for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-                for (int u = 0; u < t; ++u) acc -= Mb[t * 17 + u] * X[u];
-                X[t] = acc / Mb[t * 17 + t];
-                sm.Td[(a * 16 + t) * 16 + s] = (__bf16)X[t];
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    st.S[it][ct][e] = a.S0 ? a.S0[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] : 0.f;
+        StateRegs A, B;
+        // chunk c is consumed at iteration c + 2; its v is loaded one iteration earlier
+        for (int it = 0; it < nit; it += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                StateRegs& X = half ? B : A;
+                StateRegs& Y = half ? A : B;
+                const int c = it + half - 2;
+                state_load(Y, a, b, h, colb, c + 1, nchunks);
+                if (c >= 0 && c < nchunks) state_seg1<DK>(st, X, sm, c & 1, min(L, a.T - c * L));
+                __syncthreads();
+                if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
+                __syncthreads();
             }
         }
-        __syncthreads();
-
-        // ---- phase 5: column part (wave = 16 value columns) ----
-        f4 Dl[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f4 acc;
+        for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = (float)sm.Vt[(16 * a + g4 + e) * PV + wave * 16 + n];
-            // R_a = V_a - Kt_a S_c
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int kb = 0; kb < KT; ++kb) acc = mfma16(lds4(sm.Kn + (16 * a + n) * PK + 16 * kb + g4), pack4(S[kb]), acc);
-            // subtract the coupling to earlier blocks: - M_ab Dn_b
+                for (int e = 0; e < 4; ++e)
+                    a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
+    } else {
+        // ---------------- formation ----------------
+        const int f = wave < 4 ? wave - 2 : wave - 4;  // 2,3,6,7 -> 0,1,2,3
+        FormRegs<DK> A, B;
+        // chunk c is formed at iteration c + 1; its q, k are loaded one iteration earlier
+        for (int it = 0; it < nit; it += 2) {
 #pragma unroll
-            for (int bb = 0; bb < a; ++bb) acc = mfma16(lds4(sm.Mn + (16 * a + n) * PL + 16 * bb + g4), pack4(Dl[bb]), acc);
-            const f4 zero = {0.f, 0.f, 0.f, 0.f};
-            Dl[a] = mfma16(lds4(sm.Td + (a * 16 + n) * 16 + g4), pack4(acc), zero);
-        }
-        // O = Qt S_c + tril(Qt Kh^T) Dn
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KT; ++kb) acc = mfma16(lds4(sm.Qt + (16 * a + n) * PK + 16 * kb + g4), pack4(S[kb]), acc);
-#pragma unroll
-            for (int bb = 0; bb <= a; ++bb) acc = mfma16(lds4(sm.QK + (16 * a + n) * PL + 16 * bb + g4), pack4(Dl[bb]), acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * a + g4 + e;
-                if (t < nvalid) st_out(o + tokidx(t) * size_t(DV) + col, acc[e]);
+            for (int half = 0; half < 2; ++half) {
+                FormRegs<DK>& X = half ? B : A;
+                FormRegs<DK>& Y = half ? A : B;
+                const int c = it + half - 1;
+                form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
+                if (c >= 0 && c < nchunks) form_run<DK, ISO>(X, sm, c & 1, f, min(L, a.T - c * L));
+                __syncthreads();
+                if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, f);
+                __syncthreads();
             }
-        }
-        // S_{c+1} = diag(g_L) S_c + Kb^T Dn
-#pragma unroll
-        for (int it = 0; it < KT; ++it) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[it][e] *= sm.gL[16 * it + g4 + e];
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-                S[it] = mfma16(lds4(sm.KbT + (16 * it + n) * PL + 16 * bb + g4), pack4(Dl[bb]), S[it]);
-        }
-        __syncthreads();
-    }
-
-    // ---- final state ----
-#pragma unroll
-    for (int it = 0; it < KT; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S_T[sbase + size_t(16 * it + g4 + e) * DV + col] = S[it][e];
-    if (tile == 0) {
-        if (ISO) {
-            if (tid == 0) p_T[unit] = p;
-        } else if (tid < DK) {
-            p_T[size_t(unit) * DK + tid] = p;
         }
     }
 }
 
 template <int DK, bool ISO>
-hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-    const int units = a.B * a.H;
+hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
+    const int units = f.B * f.H;
     if (units == 0) return hipSuccess;
-    const int ntile = a.dv / DVT;
+    Args a;
+    a.q = static_cast<const bf16_t*>(f.q);
+    a.k = static_cast<const bf16_t*>(f.k);
+    a.v = static_cast<const bf16_t*>(f.v);
+    a.alpha = static_cast<const bf16_t*>(f.alpha);
+    a.omega = static_cast<const bf16_t*>(f.omega);
+    a.r = static_cast<const bf16_t*>(f.r);
+    a.c0 = f.c0;
+    a.mu = f.mu;
+    a.T = f.T;
+    a.H = f.H;
+    a.DV = f.dv;
+    a.units = units;
+    a.S0 = f.S0;
+    a.p0 = f.p0;
+    a.o = static_cast<bf16_t*>(f.o);
+    a.S_T = f.S_T;
+    a.p_T = f.p_T;
+    const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, ISO>), dim3(grid), dim3(NWAVE * 64), 0, stream,
-                       static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.alpha),
-                       static_cast<const bf16_t*>(a.omega), static_cast<const bf16_t*>(a.r), a.c0,
-                       a.mu, a.T, a.H, a.dv, units, a.S0, a.p0, static_cast<bf16_t*>(a.o), a.S_T,
-                       a.p_T);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, ISO>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
 bool chunked_supports(const FwdArgs& a) {
-    return a.dtype == 1 && (a.dk == 64 || a.dk == 128) && (a.dv % DVT) == 0 && a.dv >= DVT;
+    if (a.dtype != 1 || (a.dk != 64 && a.dk != 128) || a.dv % DVT != 0 || a.dv < DVT) return false;
+    // 16-byte vector loads of k rows (isotropic) and 4-byte loads of q, k pairs
+    return aligned16(a.q) && aligned16(a.k);
 }
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
