@@ -148,6 +148,8 @@ struct Smem {
     bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
     bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
     bf16_t RW[2][L * DK];
+    bf16_t RR[2][64];        // raw r_t of the chain's chunks (lane t; lanes >= L repeat)
+    bf16_t RV[3][2][L * 32]; // v tiles of the two state waves, [t][32 columns], ring of 3
     float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
     float rr[2][L];          // r_t
     float bh[2][L];          // b_hat_t (isotropic)
@@ -182,18 +184,45 @@ constexpr uint32_t BF_ONE = 0x3f80u;  // bf16 1.0
 // ---------------------------------------------------------------------------
 // chain role, diagonal variant: lane = key channel
 // ---------------------------------------------------------------------------
-// Loaders below issue unconditional loads from clamped addresses and never
-// touch the loaded registers: any use inside a loader would make the compiler
-// wait for each load in turn.  Tokens past the end of the sequence read the
-// last token and are masked where the values are used (tail chunk only).
+// Register prefetch rules.  Loaders issue unconditional loads from clamped
+// addresses and never touch the loaded registers: a use inside a loader would
+// make the compiler wait for each load in turn, and a load skipped on some
+// path (a chunk index out of range) would make it wait for the newest loads
+// before using older ones.  Chunk indices are clamped into [0, nchunks) (the
+// kernel is never launched with T = 0) and tokens past the end of the
+// sequence read the last token; both are masked where the values are used.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes from `src`
-// land at dst + 16 l (dst uniform across the wave).  (The sub-dword forms of
-// this load place one dword per lane, so they are not used for bf16 data.)
+// Asynchronous copies and synchronisation.
+//
+// g2lds16: direct global -> LDS copy of 16 bytes per lane (lane l's bytes from
+// `src` land at dst + 16 l, dst uniform across the wave).  It is issued from
+// inline assembly so that the compiler does not track it: the compiler
+// otherwise waits for every such copy before the next LDS read, which would
+// serialise the prefetch.  Untracked copies only make the compiler's own
+// counter waits stricter (memory counters drain in order), never weaker.  The
+// issuing wave waits for its copies with vm_wait<N>() before the barrier that
+// precedes their use.  (The sub-dword forms of this load place one dword per
+// lane, so they are not used for bf16 data.)
+//
+// bar(): workgroup barrier that waits for this wave's LDS traffic only.
+// Global loads in flight (prefetches) and global stores (outputs nobody in
+// the workgroup reads) may stay outstanding across it.
 __device__ __forceinline__ void g2lds16(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)dst));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Make the compiler wait for the load that produced x here, before any copy
+// is issued: a wait it placed later would also drain the untracked copies.
+template <class T>
+__device__ __forceinline__ void settle(const T& x) {
+    asm volatile("" ::"v"(x));
 }
 
 // Issue the raw k, alpha, omega tiles of chunk c into LDS buffer c & 1.
@@ -221,7 +250,7 @@ __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, si
 
 // r_t of chunk c for lane t (lanes >= L repeat the chunk's last token)
 __device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h, int c, int nchunks) {
-    if (c < 0 || c >= nchunks) return BF_ONE;
+    c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
     return a.r[tokidx(a, b, h, min(c * L + min(lane, L - 1), a.T - 1))];
 }
@@ -233,24 +262,33 @@ __device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h,
 template <int DK, int T0, int T1, bool MASK>
 __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float cr, float& p, float& g,
                                                int nvalid, int gring) {
+    constexpr int NTOK = T1 - T0;
+    // read phase: every LDS read of the token range is issued before the
+    // recurrence starts (two waves per SIMD cannot hide LDS latency)
+    float kk[NTOK], al[NTOK], w[NTOK];
 #pragma unroll
-    for (int t = T0; t < T1; ++t) {
-        float kk = bf1(sm.RK[buf][t * DK + i]);
-        float al = bf1(sm.RA[buf][t * DK + i]);
-        float w = bf1(sm.RW[buf][t * DK + i]);
+    for (int j = 0; j < NTOK; ++j) {
+        const int t = T0 + j;
+        kk[j] = bf1(sm.RK[buf][t * DK + i]);
+        al[j] = bf1(sm.RA[buf][t * DK + i]);
+        w[j] = bf1(sm.RW[buf][t * DK + i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        const int t = T0 + j;
         if (MASK) {
             const bool ok = t < nvalid;
-            kk = ok ? kk : 0.f;
-            al = ok ? al : 1.f;
-            w = ok ? w : 0.f;
+            kk[j] = ok ? kk[j] : 0.f;
+            al[j] = ok ? al[j] : 1.f;
+            w[j] = ok ? w[j] : 0.f;
         }
         const float ct = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), t));
-        const float asq = al * al;
-        const float u = ct * kk * kk;
-        const float ph = fmaf(asq, p, w);
+        const float asq = al[j] * al[j];
+        const float u = ct * kk[j] * kk[j];
+        const float ph = fmaf(asq, p, w[j]);  // the only loop-carried chain: ph -> p
         p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
-        g *= al;
-        sm.Kh[buf][sw<DK>(t, perm32(i))] = to_bf(ph * kk);
+        g *= al[j];
+        sm.Kh[buf][sw<DK>(t, perm32(i))] = to_bf(ph * kk[j]);
         sm.G[buf][t * DK + i] = to_bf(g);
         if (t == L - 1) sm.gL[gring][i] = g;
     }
@@ -267,7 +305,7 @@ struct ChainIsoRegs {
 template <int DK>
 __device__ __forceinline__ void chain_iso_load(ChainIsoRegs& X, const Args& a, size_t b, int h, int c,
                                                int nchunks) {
-    if (c < 0 || c >= nchunks) return;
+    c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
     const size_t e = tokidx(a, b, h, min(c * L + (lane & 31), a.T - 1));
     constexpr int NQ = DK / 16;  // 16-byte pieces per half row
@@ -345,7 +383,7 @@ struct FormRegs {
 template <int DK>
 __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t b, int h, int f, int c,
                                           int nchunks) {
-    if (c < 0 || c >= nchunks) return;
+    c = min(max(c, 0), nchunks - 1);  // always issue: see the loader note above
     const unsigned lane = threadIdx.x & 63;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -363,78 +401,75 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
 template <int DK, bool ISO>
 __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int f, int nvalid) {
     const int lane = threadIdx.x & 63;
-    if (DK == 128) {
-        const int i0 = 2 * lane;
-        const int pos = perm32(i0);  // perm32(i0 + 1) == pos + 1
-        uint32_t t0w[4], t1w[4];     // Kh^T staging: 4 tokens of channels i0, i0+1
+    constexpr int CPL = DK / 64;           // channels per lane
+    const int i0 = CPL * lane;             // first channel of this lane
+    const int pos = perm32(i0);            // perm32(i0 + 1) == pos + 1
+    // read phase: the chain's outputs for the wave's 8 tokens
+    uint32_t gw[8], kw[8];  // DK = 128: bf16 pairs of g and kappa'; DK = 64: low halves
+    float gsv[8], bhv[8];   // isotropic scalars
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const int t = 8 * f + tt;
-            const int off = sw<DK>(t, pos);
-            float g0, g1, kh0, kh1;
-            const uint32_t kp = t < nvalid ? X.kp[tt] : 0u, qp = t < nvalid ? X.qp[tt] : 0u;
-            const float k0 = bf_lo(kp), k1 = bf_hi(kp);
-            const float q0 = bf_lo(qp), q1 = bf_hi(qp);
-            if (ISO) {
-                g0 = g1 = sm.gs[nb][t];
-                const float s = sm.bh[nb][t] * __builtin_amdgcn_rcpf(g0);
-                kh0 = k0 * s;
-                kh1 = k1 * s;
-            } else {
-                const uint32_t gg = *reinterpret_cast<const uint32_t*>(&sm.G[nb][t * DK + i0]);
-                g0 = bf_lo(gg);
-                g1 = bf_hi(gg);
-                const uint32_t kap = *reinterpret_cast<const uint32_t*>(&sm.Kh[nb][off]);
-                kh0 = bf_lo(kap) * __builtin_amdgcn_rcpf(g0);
-                kh1 = bf_hi(kap) * __builtin_amdgcn_rcpf(g1);
+    for (int tt = 0; tt < 8; ++tt) {
+        const int t = 8 * f + tt;
+        if (ISO) {
+            gsv[tt] = sm.gs[nb][t];
+            bhv[tt] = sm.bh[nb][t];
+        } else if (CPL == 2) {
+            gw[tt] = *reinterpret_cast<const uint32_t*>(&sm.G[nb][t * DK + i0]);
+            kw[tt] = *reinterpret_cast<const uint32_t*>(&sm.Kh[nb][sw<DK>(t, pos)]);
+        } else {
+            gw[tt] = sm.G[nb][t * DK + i0];
+            kw[tt] = sm.Kh[nb][sw<DK>(t, pos)];
+        }
+    }
+    uint32_t kt[4][CPL];  // Kh^T staging: 4 tokens of each of this lane's channels
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const int t = 8 * f + tt;
+        const int off = sw<DK>(t, pos);
+        const bool ok = t < nvalid;
+        const uint32_t kp = ok ? X.kp[tt] : 0u, qp = ok ? X.qp[tt] : 0u;
+        float kk[CPL], qq[CPL], g[CPL], kh[CPL];
+        kk[0] = bf_lo(kp);
+        qq[0] = bf_lo(qp);
+        if (CPL == 2) {
+            kk[CPL - 1] = bf_hi(kp);
+            qq[CPL - 1] = bf_hi(qp);
+        }
+        if (ISO) {
+            const float sc = bhv[tt] * __builtin_amdgcn_rcpf(gsv[tt]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                g[c] = gsv[tt];
+                kh[c] = kk[c] * sc;
             }
-            const uint32_t khp = pack2(kh0, kh1);
-            *reinterpret_cast<uint32_t*>(&sm.Kn[nb][off]) = pack2(-k0 * g0, -k1 * g1);
-            *reinterpret_cast<uint32_t*>(&sm.Qt[nb][off]) = pack2(q0 * g0, q1 * g1);
-            *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khp;
-            const int j = tt & 3;
-            if (j == 0) {
-                t0w[0] = t0w[1] = t1w[0] = t1w[1] = 0;
-            }
-            // pair (token j, token j+1) per 32-bit word
-            if (j & 1) {
-                t0w[j >> 1] |= (khp & 0xffffu) << 16;
-                t1w[j >> 1] |= khp & 0xffff0000u;
-            } else {
-                t0w[j >> 1] = khp & 0xffffu;
-                t1w[j >> 1] = khp >> 16;
-            }
-            if (j == 3) {
-                const int tp = perm32(t - 3);
-                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) = u2{t0w[0], t0w[1]};
-                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + 1) * PT + tp]) = u2{t1w[0], t1w[1]};
+        } else {
+            g[0] = bf_lo(gw[tt]);
+            kh[0] = bf_lo(kw[tt]) * __builtin_amdgcn_rcpf(g[0]);
+            if (CPL == 2) {
+                g[CPL - 1] = bf_hi(gw[tt]);
+                kh[CPL - 1] = bf_hi(kw[tt]) * __builtin_amdgcn_rcpf(g[CPL - 1]);
             }
         }
-    } else {
-        const int i = lane;
-        const int pos = perm32(i);
-        uint32_t tw[2];
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const int t = 8 * f + tt;
-            const int off = sw<DK>(t, pos);
-            const float kk = t < nvalid ? bf_lo(X.kp[tt]) : 0.f, qq = t < nvalid ? bf_lo(X.qp[tt]) : 0.f;
-            float g, kh;
-            if (ISO) {
-                g = sm.gs[nb][t];
-                kh = kk * sm.bh[nb][t] * __builtin_amdgcn_rcpf(g);
-            } else {
-                g = bf1(sm.G[nb][t * DK + i]);
-                kh = bf1(sm.Kh[nb][off]) * __builtin_amdgcn_rcpf(g);
-            }
-            const bf16_t khb = to_bf(kh);
-            sm.Kn[nb][off] = to_bf(-kk * g);
-            sm.Qt[nb][off] = to_bf(qq * g);
+        if (CPL == 2) {
+            const uint32_t khp = pack2(kh[0], kh[CPL - 1]);
+            *reinterpret_cast<uint32_t*>(&sm.Kn[nb][off]) = pack2(-kk[0] * g[0], -kk[CPL - 1] * g[CPL - 1]);
+            *reinterpret_cast<uint32_t*>(&sm.Qt[nb][off]) = pack2(qq[0] * g[0], qq[CPL - 1] * g[CPL - 1]);
+            *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khp;
+            kt[tt & 3][0] = khp & 0xffffu;
+            kt[tt & 3][CPL - 1] = khp >> 16;
+        } else {
+            const bf16_t khb = to_bf(kh[0]);
+            sm.Kn[nb][off] = to_bf(-kk[0] * g[0]);
+            sm.Qt[nb][off] = to_bf(qq[0] * g[0]);
             sm.Kh[nb][off] = khb;
-            const int j = tt & 3;
-            if (j & 1) tw[j >> 1] |= uint32_t(khb) << 16;
-            else tw[j >> 1] = khb;
-            if (j == 3) *reinterpret_cast<u2*>(&sm.KhT[nb][i * PT + perm32(t - 3)]) = u2{tw[0], tw[1]};
+            kt[tt & 3][0] = khb;
+        }
+        if ((tt & 3) == 3) {
+            const int tp = perm32(t - 3);  // 4 consecutive positions
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + c) * PT + tp]) =
+                    u2{kt[0][c] | (kt[1][c] << 16), kt[2][c] | (kt[3][c] << 16)};
         }
     }
 }
@@ -448,13 +483,15 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
     const int kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
     auto tile = [&](const bf16_t* A, int ra, int rb) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        b8 av[KS], bv[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            const b8 av = *reinterpret_cast<const b8*>(A + sw<DK>(ra + n, 32 * kk + kg8));
-            const b8 bv = *reinterpret_cast<const b8*>(sm.Kh[nb] + sw<DK>(rb + n, 32 * kk + kg8));
-            acc = mfma32(av, bv, acc);
+            av[kk] = *reinterpret_cast<const b8*>(A + sw<DK>(ra + n, 32 * kk + kg8));
+            bv[kk] = *reinterpret_cast<const b8*>(sm.Kh[nb] + sw<DK>(rb + n, 32 * kk + kg8));
         }
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma32(av[kk], bv[kk], acc);
         return acc;  // acc[e] = row ra + g4 + e, column rb + n
     };
     if (f == 0) {
@@ -474,15 +511,21 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
         // forward substitution, lane = (block a, column s): fp32 inverse
         if (lane < NT * 16) {
             const int a = lane >> 4, s = lane & 15;
+            // read phase: the lower triangle of the block, column by column
+            // (4-float groups that hold a row >= the column index)
+            f4 colv[16][4];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int q = u / 4; q < 4; ++q) colv[u][q] = *reinterpret_cast<const f4*>(&sm.Md[a * 256 + u * 16 + 4 * q]);
             float x[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) x[t] = (t == s) ? 1.f : 0.f;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                const float* col = &sm.Md[a * 256 + u * 16];
-                x[u] *= __builtin_amdgcn_rcpf(col[u]);
+                x[u] *= __builtin_amdgcn_rcpf(colv[u][u / 4][u % 4]);
 #pragma unroll
-                for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-col[t], x[u], x[t]);
+                for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-colv[u][t / 4][t % 4], x[u], x[t]);
             }
 #pragma unroll
             for (int t = 0; t < 16; ++t) sm.Td[nb][a * 256 + t * 16 + s] = to_bf(x[t]);
@@ -510,24 +553,20 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
 // ---------------------------------------------------------------------------
 // state role: wave cw in {0,1} owns 32 value columns, S in registers
 // ---------------------------------------------------------------------------
-struct StateRegs {
-    uint32_t vv[NT][2][4];  // bf16 bits of v at rows 16a + 4g + e, column tile ct
-};
-
-__device__ __forceinline__ void state_load(StateRegs& X, const Args& a, size_t b, int h, int colb, int c,
-                                           int nchunks) {
-    if (c < 0 || c >= nchunks) return;
+// The state wave's v tile (L tokens x its 32 columns) of chunk c goes to LDS
+// ring slot c % 3 by direct loads, two chunks ahead: 128 16-byte pieces, two
+// instructions per wave.
+template <int DK>
+__device__ __forceinline__ void state_issue_t(Smem<DK>& sm, const Args& a, size_t b, int h, int colb, int cw,
+                                              int c, int nchunks) {
+    c = min(max(c, 0), nchunks - 1);  // always exactly two instructions (the wait below counts them)
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15, g4 = (lane >> 4) * 4;
-    // rows differ per lane group: one 64-bit base per row, 32-bit column offsets
 #pragma unroll
-    for (int at = 0; at < NT; ++at)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16_t* row = a.v + tokidx(a, b, h, min(c * L + 16 * at + g4 + e, a.T - 1)) * a.DV;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) X.vv[at][ct][e] = row[unsigned(colb + 16 * ct + n)];
-        }
+    for (int m = 0; m < 2; ++m) {
+        const int pc = lane + 64 * m;  // piece: token pc / 4, columns 8 (pc % 4) ..
+        const size_t off = tokidx(a, b, h, min(c * L + pc / 4, a.T - 1)) * a.DV + colb + 8 * (pc % 4);
+        g2lds16(a.v + off, &sm.RV[c % 3][cw][m * 512]);
+    }
 }
 
 template <int DK>
@@ -538,11 +577,26 @@ struct StateAcc {
 };
 
 template <int DK>
-__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, const StateRegs& X, Smem<DK>& sm, int b,
+__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b, int cw, int vslot,
                                            int nvalid) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
+    // read phase: v and every A operand of the segment
+    uint32_t vr[NT][2][4];
+    b8 ak[NT][KS], aq[NT][KS];
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[at][ct][e] = sm.RV[vslot][cw][(16 * at + g4 + e) * 32 + 16 * ct + n];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            ak[at][kk] = *reinterpret_cast<const b8*>(sm.Kn[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
+            aq[at][kk] = *reinterpret_cast<const b8*>(sm.Qt[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
+        }
+    }
     b8 Sb[KS][2];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
@@ -554,14 +608,15 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, const StateRegs& X,
         for (int ct = 0; ct < 2; ++ct) {
             f4 r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = 16 * at + g4 + e < nvalid ? bf1(bf16_t(X.vv[at][ct][e])) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t vb = 16 * at + g4 + e < nvalid ? vr[at][ct][e] : 0u;
+                r[e] = bf1(bf16_t(vb));
+            }
             f4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const b8 ak = *reinterpret_cast<const b8*>(sm.Kn[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
-                const b8 aq = *reinterpret_cast<const b8*>(sm.Qt[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
-                r = mfma32(ak, Sb[kk][ct], r);  // V - Kt S
-                o = mfma32(aq, Sb[kk][ct], o);  // Qt S
+                r = mfma32(ak[at][kk], Sb[kk][ct], r);  // V - Kt S
+                o = mfma32(aq[at][kk], Sb[kk][ct], o);  // Qt S
             }
             st.R[at][ct] = r;
             st.O[at][ct] = o;
@@ -576,9 +631,19 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    // read phase: every LDS operand of the segment
     const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
     const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
     const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
+    b8 aqk[NT], akh[DK / 16];
+    f4 glv[DK / 16];
+#pragma unroll
+    for (int at = 0; at < NT; ++at) aqk[at] = *reinterpret_cast<const b8*>(&sm.QK[b][(16 * at + n) * PT + kg8]);
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+        akh[it] = *reinterpret_cast<const b8*>(&sm.KhT[b][(16 * it + n) * PT + kg8]);
+        glv[it] = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
+    }
     b8 Db[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -590,10 +655,9 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     // outputs
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
-        const b8 aqk = *reinterpret_cast<const b8*>(&sm.QK[b][(16 * at + n) * PT + kg8]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            const f4 o = mfma32(aqk, Db[ct], st.O[at][ct]);
+            const f4 o = mfma32(aqk[at], Db[ct], st.O[at][ct]);
             const int col = colb + 16 * ct + n;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -605,13 +669,11 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     // S <- diag(g_L) (S + Kh^T Dn)
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
-        const b8 ak = *reinterpret_cast<const b8*>(&sm.KhT[b][(16 * it + n) * PT + kg8]);
-        const f4 gl = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            f4 s = mfma32(ak, Db[ct], st.S[it][ct]);
+            f4 s = mfma32(akh[it], Db[ct], st.S[it][ct]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] *= gl[e];
+            for (int e = 0; e < 4; ++e) s[e] *= glv[it][e];
             st.S[it][ct] = s;
         }
     }
@@ -637,14 +699,19 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int nit = ((nchunks + 2) + 1) & ~1;  // even number of pipeline iterations
 
     // the chain's first input tiles
-    if (!ISO && wave < DK / 64) chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, wave);
+    uint32_t r0 = 0;
+    if (!ISO && wave < DK / 64) {
+        chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, wave);
+        r0 = chain_r_load(a, b, h, 0, nchunks);
+    }
     // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31: zero them once
     for (int e = threadIdx.x; e < 2 * 16 * 16; e += NTHREADS) {
         const int bb = e >> 8, t = (e >> 4) & 15, s = 16 + (e & 15);
         sm.QK[bb][t * PT + perm32(s)] = 0;
     }
-    __builtin_amdgcn_s_waitcnt(0);  // direct LDS loads complete before the barrier
-    __syncthreads();
+    vm_wait<0>();  // chunk 0's tiles and r have landed
+    if (!ISO && wave == 0) sm.RR[0][lane] = bf16_t(r0);
+    bar();
 
     if (wave == 0 || wave == 1) {
         // ---------------- chain ----------------
@@ -653,35 +720,38 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const int i = wave * 64 + lane;
             float p = 0.f;
             if (active) p = a.p0 ? a.p0[size_t(unit) * DK + i] : a.c0[h];
-            uint32_t rnext = chain_r_load(a, b, h, 0, nchunks);
+            settle(p);  // p is ready before the pipelined loop
             for (int c = 0; c < nit; ++c) {
                 // chunk c's tiles are in LDS buffer c & 1; chunk c + 1's are fetched meanwhile
                 const int buf = c & 1;
                 const int nvalid = min(L, a.T - c * L);
                 float cr = 0.f, g = 1.f;
-                const uint32_t rcur = rnext;  // loaded before the previous barrier
+                uint32_t rnext = 0;
                 if (active) {
                     chain_diag_issue<DK>(sm, a, b, h, c + 1, nchunks, wave);
                     rnext = chain_r_load(a, b, h, c + 1, nchunks);
                     if (c < nchunks) {
-                        const float rt = lane < nvalid ? bf1(bf16_t(rcur)) : 1.f;
+                        const float rt = lane < nvalid ? bf1(sm.RR[buf][lane]) : 1.f;
                         cr = lane < nvalid ? a.mu / rt : 0.f;
                         if (wave == 0 && lane < L) sm.rr[buf][lane] = rt;
                         if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, cr, p, g, L, c % 3);
                         else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
                     }
                 }
-                __syncthreads();
+                bar();
                 if (active && c < nchunks) {
                     if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, cr, p, g, L, c % 3);
                     else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
                 }
-                __builtin_amdgcn_s_waitcnt(0);  // chunk c + 1's tiles have landed
-                __syncthreads();
+                vm_wait<0>();  // chunk c + 1's tiles and r have landed
+                settle(rnext);
+                if (wave == 0) sm.RR[(c + 1) & 1][lane] = bf16_t(rnext);
+                bar();
             }
             if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
         } else {
             float bprev = a.p0 ? a.p0[unit] : a.c0[h];
+            settle(bprev);
             ChainIsoRegs A, B;
             if (wave == 0) chain_iso_load<DK>(A, a, b, h, 0, nchunks);
             for (int it = 0; it < nit; it += 2) {
@@ -694,8 +764,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                         chain_iso_load<DK>(Y, a, b, h, c + 1, nchunks);
                         if (c < nchunks) chain_iso_run<DK>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
                     }
-                    __syncthreads();
-                    __syncthreads();
+                    bar();
+                    bar();
                 }
             }
             if (wave == 0 && lane == 0 && tile == 0) a.p_T[unit] = bprev;
@@ -714,20 +784,22 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     st.S[it][ct][e] = a.S0 ? a.S0[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] : 0.f;
-        StateRegs A, B;
-        // chunk c is consumed at iteration c + 2; its v is loaded one iteration earlier
-        for (int it = 0; it < nit; it += 2) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                StateRegs& X = half ? B : A;
-                StateRegs& Y = half ? A : B;
-                const int c = it + half - 2;
-                state_load(Y, a, b, h, colb, c + 1, nchunks);
-                if (c >= 0 && c < nchunks) state_seg1<DK>(st, X, sm, c & 1, min(L, a.T - c * L));
-                __syncthreads();
-                if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
-                __syncthreads();
-            }
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) settle(st.S[it][ct]);  // S0 is ready before the loop
+        for (int it = 0; it < nit; ++it) {
+            // chunk it's v is issued at iteration it, waited for at iteration
+            // it + 1 and consumed at iteration it + 2 (ring slot it % 3)
+            const int c = it - 2;  // chunk consumed at this iteration
+            state_issue_t<DK>(sm, a, b, h, colb, cw, it, nchunks);
+            if (c >= 0 && c < nchunks) state_seg1<DK>(st, sm, c & 1, cw, c % 3, min(L, a.T - c * L));
+            // everything but the two loads just issued has landed: the v of
+            // chunk it - 1 and the previous iteration's stores
+            vm_wait<2>();
+            bar();
+            if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
+            bar();
         }
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
@@ -749,9 +821,9 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 const int c = it + half - 1;
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
                 if (c >= 0 && c < nchunks) form_run<DK, ISO>(X, sm, c & 1, f, min(L, a.T - c * L));
-                __syncthreads();
+                bar();
                 if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, f);
-                __syncthreads();
+                bar();
             }
         }
     }
@@ -798,6 +870,7 @@ bool chunked_supports(const FwdArgs& a) {
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
+    if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
     if (a.dk == 128) return a.variant == 1 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
     return a.variant == 1 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
 }
