@@ -126,6 +126,71 @@ def bench_decode(kdn, w, dev, steps_cap=None):
             "hbm_frac": step_bytes(w) / (ms / nsteps / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
+COPY_BYTES = 512 << 20  # calibration copy for the HBM byte counters
+
+
+def counters_pass(args):
+    """Workload for the rocprofv3 counter runs: one device-to-device copy of
+    COPY_BYTES (the calibration kernel), then a few forward calls."""
+    import torch
+    import kalman_delta_network_amd as kdn
+    from kalman_delta_network_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    kdn.load_library()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    w = wl.WORKLOADS[MAIN]
+    t = upload(wl.forward_inputs(w), w.dtype, dev)
+    for _ in range(3):
+        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=args.algo)
+    torch.cuda.synchronize()
+    print("counters pass done", flush=True)
+
+
+def _read_counter_csv(run_dir, counter):
+    """{dispatch id: (kernel name, value)} from a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    rows = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+                rows[d] = (r.get("Kernel_Name", ""), rows.get(d, ("", 0.0))[1] + float(r["Counter_Value"]))
+    return rows
+
+
+def traffic_from(fetch_dir, write_dir, out_path, algo):
+    """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the same counter of the calibration copy."""
+    res = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter_csv(run_dir, counter)
+        copies = [v for n, v in rows.values() if "kdn" not in n and v > 0]
+        fwd = [v for n, v in rows.values() if "kdn_chunk_kernel" in n]
+        if not copies or not fwd:
+            raise SystemExit(f"{counter}: no calibration copy or forward dispatch in {run_dir}")
+        scale = COPY_BYTES / (max(copies) * 1024.0)  # bytes per counted byte
+        res[counter] = {"kib_per_launch": float(np.mean(fwd)), "copy_kib": max(copies), "scale": scale,
+                        "bytes_per_launch": float(np.mean(fwd)) * 1024.0 * scale}
+    entry = {"kernel_hash": kernel_source_hash(), "algo": algo,
+             "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
+             "counters": res}
+    data = {}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            data = json.load(f)
+    data[MAIN + "/" + algo] = entry
+    with open(out_path, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(entry))
+
+
 def cpu_baseline(w, x):
     import oracle
     t0 = time.perf_counter()
@@ -145,12 +210,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the isotropic and decode lines")
     ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--counters-pass", action="store_true",
+                    help="run the workload of the rocprofv3 counter runs and exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc CSV runs into a traffic entry and exit")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.traffic_out, args.algo)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(each (batch, head) pair is independent; see the sharding notes). "
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.counters_pass:
+        counters_pass(args)
+        return
 
     import torch
     import kalman_delta_network_amd as kdn
