@@ -137,24 +137,24 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int DK>
 struct Smem {
-    bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
-    bf16_t Qt[2][L * DK];    //  q_t g_t
-    bf16_t Kh[2][L * DK];    // kappa'_t (chain), then kappa'_t / g_t (formation)
-    bf16_t KhT[2][DK * PT];  // (kappa'_t / g_t)^T  [i][perm32(t)]
-    bf16_t QK[2][L * PT];    // tril(Qt Kh^T)      [t][perm32(s)]
-    bf16_t Td[2][NT * 256];  // inverses of M's diagonal blocks [a][t][s]
-    bf16_t Mo[2][256];       // -M's block (1,0)   [t][s]
-    bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
-    bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
-    bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
-    bf16_t RW[2][L * DK];
-    bf16_t RR[2][64];        // raw r_t of the chain's chunks (lane t; lanes >= L repeat)
-    bf16_t RV[3][2][L * 32]; // v tiles of the two state waves, [t][32 columns], ring of 3
-    float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
-    float rr[2][L];          // r_t
-    float bh[2][L];          // b_hat_t (isotropic)
-    float gs[2][L];          // g_t (isotropic, scalar)
-    float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
+    alignas(16) bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
+    alignas(16) bf16_t Qt[2][L * DK];    //  q_t g_t
+    alignas(16) bf16_t Kh[2][L * DK];    // kappa'_t (chain), then kappa'_t / g_t (formation)
+    alignas(16) bf16_t KhT[2][DK * PT];  // (kappa'_t / g_t)^T  [i][perm32(t)]
+    alignas(16) bf16_t QK[2][L * PT];    // tril(Qt Kh^T)      [t][perm32(s)]
+    alignas(16) bf16_t Td[2][NT * 256];  // inverses of M's diagonal blocks [a][t][s]
+    alignas(16) bf16_t Mo[2][256];       // -M's block (1,0)   [t][s]
+    alignas(16) bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
+    alignas(16) bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
+    alignas(16) bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
+    alignas(16) bf16_t RW[2][L * DK];
+    alignas(16) bf16_t RV[3][2][L * 32]; // v tiles of the two state waves, [t][32 columns], ring of 3
+    alignas(16) float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
+    alignas(16) float rr[3][L];          // r_t (ring of three chunks: written a chunk ahead)
+    alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
+    alignas(16) float bh[2][L];          // b_hat_t (isotropic)
+    alignas(16) float gs[2][L];          // g_t (isotropic, scalar)
+    alignas(16) float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
 };
 
 struct Args {
@@ -248,6 +248,17 @@ __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, si
     }
 }
 
+// lane t: r_t and mu / r_t of a chunk with nvalid real tokens into LDS
+// (padding tokens: r = 1, no precision increment)
+template <int DK>
+__device__ __forceinline__ void chain_r_store(Smem<DK>& sm, int c, uint32_t rbits, int nvalid, float mu) {
+    const int lane = threadIdx.x & 63;
+    const bool ok = lane < nvalid;
+    const float rt = ok ? bf1(bf16_t(rbits)) : 1.f;
+    sm.cr[c & 1][lane] = ok ? mu / rt : 0.f;
+    if (lane < L) sm.rr[c % 3][lane] = rt;
+}
+
 // r_t of chunk c for lane t (lanes >= L repeat the chunk's last token)
 __device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h, int c, int nchunks) {
     c = min(max(c, 0), nchunks - 1);
@@ -260,18 +271,19 @@ __device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h,
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
 template <int DK, int T0, int T1, bool MASK>
-__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float cr, float& p, float& g,
-                                               int nvalid, int gring) {
+__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float& p, float& g, int nvalid,
+                                               int gring) {
     constexpr int NTOK = T1 - T0;
     // read phase: every LDS read of the token range is issued before the
     // recurrence starts (two waves per SIMD cannot hide LDS latency)
-    float kk[NTOK], al[NTOK], w[NTOK];
+    float kk[NTOK], al[NTOK], w[NTOK], cv[NTOK];
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
         const int t = T0 + j;
         kk[j] = bf1(sm.RK[buf][t * DK + i]);
         al[j] = bf1(sm.RA[buf][t * DK + i]);
         w[j] = bf1(sm.RW[buf][t * DK + i]);
+        cv[j] = sm.cr[buf][t];  // same address on every lane: broadcast
     }
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
@@ -282,9 +294,8 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, flo
             al[j] = ok ? al[j] : 1.f;
             w[j] = ok ? w[j] : 0.f;
         }
-        const float ct = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), t));
         const float asq = al[j] * al[j];
-        const float u = ct * kk[j] * kk[j];
+        const float u = cv[j] * kk[j] * kk[j];
         const float ph = fmaf(asq, p, w[j]);  // the only loop-carried chain: ph -> p
         p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
         g *= al[j];
@@ -364,7 +375,7 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs& X, Smem<DK>& s
     if (lane < L) {
         sm.bh[buf][lane] = fmaf(asq, bbefore, w);
         sm.gs[buf][lane] = g;
-        sm.rr[buf][lane] = rt;
+        sm.rr[gring][lane] = rt;
     }
     bprev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt), L - 1));
     const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
@@ -398,7 +409,7 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
     }
 }
 
-template <int DK, bool ISO>
+template <int DK, bool ISO, bool MASK>
 __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int f, int nvalid) {
     const int lane = threadIdx.x & 63;
     constexpr int CPL = DK / 64;           // channels per lane
@@ -426,7 +437,7 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     for (int tt = 0; tt < 8; ++tt) {
         const int t = 8 * f + tt;
         const int off = sw<DK>(t, pos);
-        const bool ok = t < nvalid;
+        const bool ok = !MASK || t < nvalid;  // tail chunk only: tokens past T read as zero
         const uint32_t kp = ok ? X.kp[tt] : 0u, qp = ok ? X.qp[tt] : 0u;
         float kk[CPL], qq[CPL], g[CPL], kh[CPL];
         kk[0] = bf_lo(kp);
@@ -474,9 +485,30 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     }
 }
 
+// Four steps u = 4 GRP .. 4 GRP + 3 of the column-oriented forward
+// substitution for M_aa x = e_s (Mb: the block, column-major; rd: reciprocals
+// of its diagonal).  The unit right-hand side enters as a select at step u
+// (an initial one-hot would be stored with the lane's index, through scratch).
+// Only the 4-float groups of each column at or below the diagonal are read.
+template <int GRP>
+__device__ __forceinline__ void inv_group(const float* Mb, float (&x)[16], const float (&rd)[16], int s) {
+    f4 col[4][4];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+        for (int q = GRP; q < 4; ++q) col[uu][q] = *reinterpret_cast<const f4*>(&Mb[(4 * GRP + uu) * 16 + 4 * q]);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+        const int u = 4 * GRP + uu;
+        x[u] = (x[u] + (u == s ? 1.f : 0.f)) * rd[u];
+#pragma unroll
+        for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-col[uu][t / 4][t % 4], x[u], x[t]);
+    }
+}
+
 // M, tril(Qt Kh^T) and the diagonal-block inverses of chunk buffer nb
 template <int DK>
-__device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
+__device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g4 = (lane >> 4) * 4;
@@ -494,59 +526,58 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int f) {
         for (int kk = 0; kk < KS; ++kk) acc = mfma32(av[kk], bv[kk], acc);
         return acc;  // acc[e] = row ra + g4 + e, column rb + n
     };
-    if (f == 0) {
-        // diagonal blocks of M = diag(r) + tril(Kt Kh^T); Kn holds -Kt
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
+    if (f < NT) {
+        // diagonal block a = f of M = diag(r) + tril(Kt Kh^T) (Kn holds -Kt),
+        // then its fp32 inverse by forward substitution, lane = column s
+        const int a = f;
+        {
             const f4 acc = tile(sm.Kn[nb], 16 * a, 16 * a);
             f4 mv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tl = g4 + e;
-                mv[e] = tl > n ? -acc[e] : (tl == n ? sm.rr[nb][16 * a + tl] - acc[e] : 0.f);
+                mv[e] = tl > n ? -acc[e] : (tl == n ? sm.rr[rslot][16 * a + tl] - acc[e] : 0.f);
             }
-            *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;
+            *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;  // column-major
         }
         wave_lds_sync();
-        // forward substitution, lane = (block a, column s): fp32 inverse
-        if (lane < NT * 16) {
-            const int a = lane >> 4, s = lane & 15;
-            // read phase: the lower triangle of the block, column by column
-            // (4-float groups that hold a row >= the column index)
-            f4 colv[16][4];
+        if (lane < 16) {
+            const int s = lane;
+            const float* Mb = &sm.Md[a * 256];
+            // reciprocals of the diagonal, off the substitution's dependency chain
+            float rd[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-#pragma unroll
-                for (int q = u / 4; q < 4; ++q) colv[u][q] = *reinterpret_cast<const f4*>(&sm.Md[a * 256 + u * 16 + 4 * q]);
+            for (int u = 0; u < 16; ++u) rd[u] = __builtin_amdgcn_rcpf(Mb[u * 16 + u]);
+            // x solves M_aa x = e_s, four columns per step group (every index
+            // static: see inv_group)
             float x[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = (t == s) ? 1.f : 0.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                x[u] *= __builtin_amdgcn_rcpf(colv[u][u / 4][u % 4]);
-#pragma unroll
-                for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-colv[u][t / 4][t % 4], x[u], x[t]);
-            }
+            for (int t = 0; t < 16; ++t) x[t] = 0.f;
+            inv_group<0>(Mb, x, rd, s);
+            inv_group<1>(Mb, x, rd, s);
+            inv_group<2>(Mb, x, rd, s);
+            inv_group<3>(Mb, x, rd, s);
 #pragma unroll
             for (int t = 0; t < 16; ++t) sm.Td[nb][a * 256 + t * 16 + s] = to_bf(x[t]);
         }
-    } else if (f == 1) {
-        // block (1,0) of M is -acc; store -M_10 = acc for the substitution
+    } else if (f == 2) {
+        // block (1,0) of M is -acc: store -M_10 = acc for the substitution;
+        // diagonal block (0,0) of tril(Qt Kh^T)
         const f4 acc = tile(sm.Kn[nb], 16, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sm.Mo[nb][(g4 + e) * 16 + n] = to_bf(acc[e]);
-    } else if (f == 2) {
+        const f4 q0 = tile(sm.Qt[nb], 0, 0);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) {
-            const f4 acc = tile(sm.Qt[nb], 16 * a, 16 * a);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sm.QK[nb][(16 * a + g4 + e) * PT + perm32(16 * a + n)] = to_bf(g4 + e >= n ? acc[e] : 0.f);
-        }
+        for (int e = 0; e < 4; ++e) sm.QK[nb][(g4 + e) * PT + perm32(n)] = to_bf(g4 + e >= n ? q0[e] : 0.f);
     } else {
-        const f4 acc = tile(sm.Qt[nb], 16, 0);
+        // blocks (1,0) and (1,1) of tril(Qt Kh^T)
+        const f4 q10 = tile(sm.Qt[nb], 16, 0);
+        const f4 q11 = tile(sm.Qt[nb], 16, 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.QK[nb][(16 + g4 + e) * PT + perm32(n)] = to_bf(acc[e]);
+        for (int e = 0; e < 4; ++e) {
+            sm.QK[nb][(16 + g4 + e) * PT + perm32(n)] = to_bf(q10[e]);
+            sm.QK[nb][(16 + g4 + e) * PT + perm32(16 + n)] = to_bf(g4 + e >= n ? q11[e] : 0.f);
+        }
     }
 }
 
@@ -628,6 +659,7 @@ template <int DK>
 __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
                                            int h, int colb, int c) {
     const int gring = c % 3;
+    const bool full = (c + 1) * L <= a.T;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -658,11 +690,16 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const f4 o = mfma32(aqk[at], Db[ct], st.O[at][ct]);
-            const int col = colb + 16 * ct + n;
+            const unsigned col = unsigned(colb + 16 * ct + n);
+            if (full) {  // uniform: no per-element exec masking
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = c * L + 16 * at + g4 + e;
-                if (t < a.T) a.o[tokidx(a, bb, h, t) * a.DV + col] = to_bf(o[e]);
+                for (int e = 0; e < 4; ++e) (a.o + tokidx(a, bb, h, c * L + 16 * at + g4 + e) * a.DV)[col] = to_bf(o[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = c * L + 16 * at + g4 + e;
+                    if (t < a.T) a.o[tokidx(a, bb, h, t) * a.DV + col] = to_bf(o[e]);
+                }
             }
         }
     }
@@ -710,7 +747,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         sm.QK[bb][t * PT + perm32(s)] = 0;
     }
     vm_wait<0>();  // chunk 0's tiles and r have landed
-    if (!ISO && wave == 0) sm.RR[0][lane] = bf16_t(r0);
+    if (!ISO && wave == 0) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
     if (wave == 0 || wave == 1) {
@@ -725,27 +762,24 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 // chunk c's tiles are in LDS buffer c & 1; chunk c + 1's are fetched meanwhile
                 const int buf = c & 1;
                 const int nvalid = min(L, a.T - c * L);
-                float cr = 0.f, g = 1.f;
+                float g = 1.f;
                 uint32_t rnext = 0;
                 if (active) {
                     chain_diag_issue<DK>(sm, a, b, h, c + 1, nchunks, wave);
                     rnext = chain_r_load(a, b, h, c + 1, nchunks);
                     if (c < nchunks) {
-                        const float rt = lane < nvalid ? bf1(sm.RR[buf][lane]) : 1.f;
-                        cr = lane < nvalid ? a.mu / rt : 0.f;
-                        if (wave == 0 && lane < L) sm.rr[buf][lane] = rt;
-                        if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, cr, p, g, L, c % 3);
-                        else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
+                        if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, p, g, L, c % 3);
+                        else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, p, g, nvalid, c % 3);
                     }
                 }
                 bar();
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, cr, p, g, L, c % 3);
-                    else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, cr, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, p, g, L, c % 3);
+                    else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, p, g, nvalid, c % 3);
                 }
                 vm_wait<0>();  // chunk c + 1's tiles and r have landed
                 settle(rnext);
-                if (wave == 0) sm.RR[(c + 1) & 1][lane] = bf16_t(rnext);
+                if (wave == 0) chain_r_store<DK>(sm, c + 1, rnext, min(L, a.T - (c + 1) * L), a.mu);
                 bar();
             }
             if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
@@ -820,9 +854,13 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 FormRegs<DK>& Y = half ? A : B;
                 const int c = it + half - 1;
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
-                if (c >= 0 && c < nchunks) form_run<DK, ISO>(X, sm, c & 1, f, min(L, a.T - c * L));
+                if (c >= 0 && c < nchunks) {
+                    const int nvalid = min(L, a.T - c * L);
+                    if (nvalid == L) form_run<DK, ISO, false>(X, sm, c & 1, f, L);
+                    else form_run<DK, ISO, true>(X, sm, c & 1, f, nvalid);
+                }
                 bar();
-                if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, f);
+                if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, c % 3, f);
                 bar();
             }
         }
