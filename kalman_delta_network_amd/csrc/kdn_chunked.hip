@@ -61,7 +61,7 @@ constexpr int NT = L / 16;       // 16-token tiles per chunk
 constexpr int DVT = 64;          // value columns per workgroup
 constexpr int NTHREADS = 512;    // 8 waves
 constexpr int PT = L + 8;        // pitch (elements) of [rows][L] bf16 tiles
-constexpr int CHAIN_SPLIT = 22;  // chain tokens run before the mid-iteration barrier
+constexpr int CHAIN_SPLIT = 18;  // chain tokens run before the mid-iteration barrier
 static_assert(L == 32 && NT == 2, "the kernel is written for 32-token chunks");
 
 typedef uint16_t bf16_t;
@@ -155,6 +155,7 @@ struct Smem {
     alignas(16) float bh[2][L];          // b_hat_t (isotropic)
     alignas(16) float gs[2][L];          // g_t (isotropic, scalar)
     alignas(16) float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
+    alignas(16) float Wi[NT][2][64];     // inverses of their 8x8 diagonal sub-blocks, column-major
 };
 
 struct Args {
@@ -225,16 +226,18 @@ __device__ __forceinline__ void settle(const T& x) {
     asm volatile("" ::"v"(x));
 }
 
-// Issue the raw k, alpha, omega tiles of chunk c into LDS buffer c & 1.
-// The chain waves split the 16-byte pieces; rows past the end of the
-// sequence repeat the last token (masked where used).
+// Issue the raw k, alpha, omega tiles of chunk c (the chain's input) into
+// LDS buffer c & 1.  The four formation waves (w = 0..3) split the 16-byte
+// pieces, so the chain waves spend their issue slots on the recurrence only;
+// rows past the end of the sequence repeat the last token (masked where used).
 template <int DK>
 __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, size_t b, int h, int c,
                                                  int nchunks, int w) {
     if (c < 0 || c >= nchunks) return;
-    constexpr int NW = DK / 64;           // chain waves
+    constexpr int NW = 4;                 // issuing waves
     constexpr int PR = DK / 8;            // 16-byte pieces per row
     constexpr int PER = L * PR / 64 / NW; // instructions per tile per wave
+    static_assert(PER * 64 * NW == L * PR, "pieces must split evenly over the issuing waves");
     const int lane = threadIdx.x & 63;
     const int buf = c & 1;
 #pragma unroll
@@ -274,6 +277,12 @@ template <int DK, int T0, int T1, bool MASK>
 __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float& p, float& g, int nvalid,
                                                int gring) {
     constexpr int NTOK = T1 - T0;
+    // swizzled LDS offsets of this lane's gain column for rows 0..15; rows
+    // 16..31 repeat the pattern 16 rows further (the swizzle period divides 16)
+    const int pos = perm32(i);
+    int khoff[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) khoff[t] = sw<DK>(t, pos);
     // read phase: every LDS read of the token range is issued before the
     // recurrence starts (two waves per SIMD cannot hide LDS latency)
     float kk[NTOK], al[NTOK], w[NTOK], cv[NTOK];
@@ -299,7 +308,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, flo
         const float ph = fmaf(asq, p, w[j]);  // the only loop-carried chain: ph -> p
         p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
         g *= al[j];
-        sm.Kh[buf][sw<DK>(t, perm32(i))] = to_bf(ph * kk[j]);
+        sm.Kh[buf][khoff[t & 15] + (t >> 4) * 16 * DK] = to_bf(ph * kk[j]);
         sm.G[buf][t * DK + i] = to_bf(g);
         if (t == L - 1) sm.gL[gring][i] = g;
     }
@@ -485,28 +494,77 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     }
 }
 
-// Four steps u = 4 GRP .. 4 GRP + 3 of the column-oriented forward
-// substitution for M_aa x = e_s (Mb: the block, column-major; rd: reciprocals
-// of its diagonal).  The unit right-hand side enters as a select at step u
-// (an initial one-hot would be stored with the lane's index, through scratch).
-// Only the 4-float groups of each column at or below the diagonal are read.
-template <int GRP>
-__device__ __forceinline__ void inv_group(const float* Mb, float (&x)[16], const float (&rd)[16], int s) {
-    f4 col[4][4];
+// Inverses of the two 16x16 diagonal blocks of M (in Md, fp32) into Td as
+// bf16.  Each block is split into 8x8 sub-blocks,
+//     [[P, 0], [C, Q]]^-1 = [[P^-1, 0], [-Q^-1 C P^-1, Q^-1]],
+// so the sequential part is an 8-step substitution that runs for all four
+// sub-blocks of the chunk at once (lanes 0..31), and the corner blocks are
+// two small fp32 matrix-core products.  Td's block (0,1) of each diagonal
+// block is zero and is written once, at kernel start.  One wave.
+template <int DK>
+__device__ __forceinline__ void block_inverse(Smem<DK>& sm, int nb, int lane) {
+    if (lane < 32) {
+        // lane = (block a, sub-block w, column s): x solves P x = e_s (w = 0)
+        // or Q x = e_s (w = 1) by forward substitution over the columns
+        const int a = lane >> 4, w = (lane >> 3) & 1, s = lane & 7, o = 8 * w;
+        const float* Mb = &sm.Md[a * 256 + o * 16 + o];  // sub-block entry (t, u) at Mb[16 u + t]
+        f4 col[8][2];
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu)
+        for (int u = 0; u < 8; ++u) {
+            col[u][0] = *reinterpret_cast<const f4*>(&Mb[16 * u]);
+            col[u][1] = *reinterpret_cast<const f4*>(&Mb[16 * u + 4]);
+        }
+        float x[8];
 #pragma unroll
-        for (int q = GRP; q < 4; ++q) col[uu][q] = *reinterpret_cast<const f4*>(&Mb[(4 * GRP + uu) * 16 + 4 * q]);
+        for (int t = 0; t < 8; ++t) x[t] = 0.f;
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-        const int u = 4 * GRP + uu;
-        x[u] = (x[u] + (u == s ? 1.f : 0.f)) * rd[u];
+        for (int u = 0; u < 8; ++u) {
+            // the unit right-hand side enters as a select (an indexed store
+            // of a one-hot vector would go through scratch memory)
+            x[u] = (x[u] + (u == s ? 1.f : 0.f)) * __builtin_amdgcn_rcpf(col[u][u / 4][u % 4]);
 #pragma unroll
-        for (int t = u + 1; t < 16; ++t) x[t] = fmaf(-col[uu][t / 4][t % 4], x[u], x[t]);
+            for (int t = u + 1; t < 8; ++t) x[t] = fmaf(-col[u][t / 4][t % 4], x[u], x[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sm.Td[nb][a * 256 + (o + t) * 16 + o + s] = to_bf(x[t]);
+        *reinterpret_cast<f4*>(&sm.Wi[a][w][8 * s]) = f4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f4*>(&sm.Wi[a][w][8 * s + 4]) = f4{x[4], x[5], x[6], x[7]};
+    }
+    wave_lds_sync();
+    // corner blocks -Q^-1 (C P^-1) of both diagonal blocks together, as two
+    // products of block-diagonal 16x16 fp32 matrices on the matrix cores
+    // (index 8 a + t of those matrices is index t of block a).  Lane (j, n)
+    // supplies row or column n and k-slot j; the second product takes its k
+    // slots permuted (k = 4 j + i in step i) so that its right operand is
+    // exactly the lane's accumulator of the first.
+    const int n = lane & 15, j = lane >> 4;
+    const int an = n >> 3, tn = n & 7;
+    f4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = 4 * i + j, ak = k >> 3, tk = k & 7;
+        const float cv = sm.Md[an * 256 + 16 * tk + 8 + tn];  // C of block an, [tn][tk]
+        const float pv = sm.Wi[ak][0][8 * tn + tk];           // P^-1 of block ak, [tk][tn]
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(an == ak ? cv : 0.f, an == ak ? pv : 0.f, y, 0, 0, 0);
+    }
+    // y[e] = (C P^-1)[4 j + e][n] (block-diagonal)
+    f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = 4 * j + i, ak = k >> 3, tk = k & 7;
+        const float qv = sm.Wi[ak][1][8 * tk + tn];  // Q^-1 of block ak, [tn][tk]
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(an == ak ? qv : 0.f, y[i], z, 0, 0, 0);
+    }
+    // z[e] = (Q^-1 C P^-1)[4 j + e][n]: rows and column in the same block form
+    // row 4 (j & 1) + e, column tn of block an's corner
+    if ((j >> 1) == an) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Td[nb][an * 256 + (8 + 4 * (j & 1) + e) * 16 + tn] = to_bf(-z[e]);
     }
 }
 
-// M, tril(Qt Kh^T) and the diagonal-block inverses of chunk buffer nb
+// M, tril(Qt Kh^T) and the diagonal-block inverses of chunk buffer nb; the
+// work is split over the four formation waves f
 template <int DK>
 __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
     const int lane = threadIdx.x & 63;
@@ -526,41 +584,26 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
         for (int kk = 0; kk < KS; ++kk) acc = mfma32(av[kk], bv[kk], acc);
         return acc;  // acc[e] = row ra + g4 + e, column rb + n
     };
-    if (f < NT) {
-        // diagonal block a = f of M = diag(r) + tril(Kt Kh^T) (Kn holds -Kt),
-        // then its fp32 inverse by forward substitution, lane = column s
-        const int a = f;
-        {
+    if (f == 0) {
+        // the diagonal blocks of M = diag(r) + tril(Kt Kh^T) (Kn holds -Kt),
+        // column-major fp32, then their inverses
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
             const f4 acc = tile(sm.Kn[nb], 16 * a, 16 * a);
+            // r of rows g4 .. g4 + 3, read by every lane (a read under the
+            // diagonal's select would become a branch and a wait per element)
+            const f4 rv = *reinterpret_cast<const f4*>(&sm.rr[rslot][16 * a + g4]);
             f4 mv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tl = g4 + e;
-                mv[e] = tl > n ? -acc[e] : (tl == n ? sm.rr[rslot][16 * a + tl] - acc[e] : 0.f);
+                mv[e] = tl > n ? -acc[e] : (tl == n ? rv[e] - acc[e] : 0.f);
             }
             *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;  // column-major
         }
         wave_lds_sync();
-        if (lane < 16) {
-            const int s = lane;
-            const float* Mb = &sm.Md[a * 256];
-            // reciprocals of the diagonal, off the substitution's dependency chain
-            float rd[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) rd[u] = __builtin_amdgcn_rcpf(Mb[u * 16 + u]);
-            // x solves M_aa x = e_s, four columns per step group (every index
-            // static: see inv_group)
-            float x[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = 0.f;
-            inv_group<0>(Mb, x, rd, s);
-            inv_group<1>(Mb, x, rd, s);
-            inv_group<2>(Mb, x, rd, s);
-            inv_group<3>(Mb, x, rd, s);
-#pragma unroll
-            for (int t = 0; t < 16; ++t) sm.Td[nb][a * 256 + t * 16 + s] = to_bf(x[t]);
-        }
-    } else if (f == 2) {
+        block_inverse<DK>(sm, nb, lane);
+    } else if (f == 1) {
         // block (1,0) of M is -acc: store -M_10 = acc for the substitution;
         // diagonal block (0,0) of tril(Qt Kh^T)
         const f4 acc = tile(sm.Kn[nb], 16, 0);
@@ -569,7 +612,7 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
         const f4 q0 = tile(sm.Qt[nb], 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sm.QK[nb][(g4 + e) * PT + perm32(n)] = to_bf(g4 + e >= n ? q0[e] : 0.f);
-    } else {
+    } else if (f == 2) {
         // blocks (1,0) and (1,1) of tril(Qt Kh^T)
         const f4 q10 = tile(sm.Qt[nb], 16, 0);
         const f4 q11 = tile(sm.Qt[nb], 16, 16);
@@ -647,7 +690,7 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 r = mfma32(ak[at][kk], Sb[kk][ct], r);  // V - Kt S
-                o = mfma32(aq[at][kk], Sb[kk][ct], o);  // Qt S
+                o = mfma32(Sb[kk][ct], aq[at][kk], o);  // (Qt S)^T: value column x token
             }
             st.R[at][ct] = r;
             st.O[at][ct] = o;
@@ -684,24 +727,19 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
         const f4 d1 = mfma16(t1, pack4(r1), zero);
         Db[ct] = pack8(d0, d1);
     }
-    // outputs
+    // outputs, transposed: lane (n, g4) holds value columns g4 .. g4 + 3 of
+    // token 16 at + n, written as one 8-byte store per tile
+    bf16_t* orow = a.o + tokidx(a, bb, h, c * L + n) * a.DV + colb + g4;
+    const size_t ostep = size_t(16) * a.H * a.DV;  // 16 tokens
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
+        const bool ok = full || c * L + 16 * at + n < a.T;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            const f4 o = mfma32(aqk[at], Db[ct], st.O[at][ct]);
-            const unsigned col = unsigned(colb + 16 * ct + n);
-            if (full) {  // uniform: no per-element exec masking
-#pragma unroll
-                for (int e = 0; e < 4; ++e) (a.o + tokidx(a, bb, h, c * L + 16 * at + g4 + e) * a.DV)[col] = to_bf(o[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = c * L + 16 * at + g4 + e;
-                    if (t < a.T) a.o[tokidx(a, bb, h, t) * a.DV + col] = to_bf(o[e]);
-                }
-            }
+            const f4 o = mfma32(Db[ct], aqk[at], st.O[at][ct]);  // (tril(Qt Kh^T) Dn)^T
+            if (ok) *reinterpret_cast<u2*>(orow + 16 * ct) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
         }
+        orow += ostep;
     }
     // S <- diag(g_L) (S + Kh^T Dn)
 #pragma unroll
@@ -735,19 +773,24 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int nchunks = (a.T + L - 1) / L;
     const int nit = ((nchunks + 2) + 1) & ~1;  // even number of pipeline iterations
 
-    // the chain's first input tiles
+    // the chain's first input tiles (issued by the formation waves)
+    const int fwave = wave < 4 ? wave - 2 : wave - 4;  // formation index of waves 2,3,6,7
+    const bool is_form = wave == 2 || wave == 3 || wave == 6 || wave == 7;
     uint32_t r0 = 0;
-    if (!ISO && wave < DK / 64) {
-        chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, wave);
-        r0 = chain_r_load(a, b, h, 0, nchunks);
+    if (!ISO && is_form) {
+        chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, fwave);
+        if (wave == 7) r0 = chain_r_load(a, b, h, 0, nchunks);
     }
-    // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31: zero them once
+    // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31, and the block
+    // (0,1) of each diagonal-block inverse is zero: write both once
     for (int e = threadIdx.x; e < 2 * 16 * 16; e += NTHREADS) {
         const int bb = e >> 8, t = (e >> 4) & 15, s = 16 + (e & 15);
         sm.QK[bb][t * PT + perm32(s)] = 0;
+        const int a = (e >> 6) & 1, tt = (e >> 3) & 7, ss = 8 + (e & 7);
+        sm.Td[bb][a * 256 + tt * 16 + ss] = 0;
     }
     vm_wait<0>();  // chunk 0's tiles and r have landed
-    if (!ISO && wave == 0) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
+    if (!ISO && wave == 7) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
     if (wave == 0 || wave == 1) {
@@ -759,14 +802,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             if (active) p = a.p0 ? a.p0[size_t(unit) * DK + i] : a.c0[h];
             settle(p);  // p is ready before the pipelined loop
             for (int c = 0; c < nit; ++c) {
-                // chunk c's tiles are in LDS buffer c & 1; chunk c + 1's are fetched meanwhile
+                // chunk c's tiles are in LDS buffer c & 1 (chunk c + 1's are
+                // fetched meanwhile by the formation waves)
                 const int buf = c & 1;
                 const int nvalid = min(L, a.T - c * L);
                 float g = 1.f;
-                uint32_t rnext = 0;
                 if (active) {
-                    chain_diag_issue<DK>(sm, a, b, h, c + 1, nchunks, wave);
-                    rnext = chain_r_load(a, b, h, c + 1, nchunks);
                     if (c < nchunks) {
                         if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, p, g, L, c % 3);
                         else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, p, g, nvalid, c % 3);
@@ -777,9 +818,6 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, p, g, L, c % 3);
                     else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, p, g, nvalid, c % 3);
                 }
-                vm_wait<0>();  // chunk c + 1's tiles and r have landed
-                settle(rnext);
-                if (wave == 0) chain_r_store<DK>(sm, c + 1, rnext, min(L, a.T - (c + 1) * L), a.mu);
                 bar();
             }
             if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
@@ -853,6 +891,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 FormRegs<DK>& X = half ? B : A;
                 FormRegs<DK>& Y = half ? A : B;
                 const int c = it + half - 1;
+                // the chain's inputs for chunk c + 2 (it consumes chunk c + 1 now)
+                uint32_t rnext = 0;
+                if (!ISO) {
+                    chain_diag_issue<DK>(sm, a, b, h, c + 2, nchunks, f);
+                    if (f == 3) rnext = chain_r_load(a, b, h, c + 2, nchunks);
+                }
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
                 if (c >= 0 && c < nchunks) {
                     const int nvalid = min(L, a.T - c * L);
@@ -861,6 +905,20 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 }
                 bar();
                 if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, c % 3, f);
+                // everything issued this iteration has landed: the chain's tiles
+                // for chunk c + 2 and q, k of chunk c + 1.  Settling the latter
+                // tells the compiler so; otherwise its wait before the next
+                // form_run would count the untracked copies and stall on them.
+                vm_wait<0>();
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) {
+                    settle(Y.kp[tt]);
+                    settle(Y.qp[tt]);
+                }
+                if (!ISO) {
+                    settle(rnext);
+                    if (f == 3) chain_r_store<DK>(sm, c + 2, rnext, min(L, a.T - (c + 2) * L), a.mu);
+                }
                 bar();
             }
         }
@@ -902,8 +960,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool chunked_supports(const FwdArgs& a) {
     if (a.dtype != 1 || (a.dk != 64 && a.dk != 128) || a.dv % DVT != 0 || a.dv < DVT) return false;
-    // 16-byte vector loads of k rows (isotropic) and 4-byte loads of q, k pairs
-    return aligned16(a.q) && aligned16(a.k);
+    // 16-byte direct copies of k, alpha, omega and v rows, 16-byte loads of k
+    // rows (isotropic), 8-byte stores of four output columns
+    return aligned16(a.q) && aligned16(a.k) && aligned16(a.v) && aligned16(a.alpha) && aligned16(a.omega) &&
+           (reinterpret_cast<uintptr_t>(a.o) & 7u) == 0;
 }
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
