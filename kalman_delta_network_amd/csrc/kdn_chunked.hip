@@ -198,7 +198,8 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // Asynchronous copies and synchronisation.
 //
 // g2lds16: direct global -> LDS copy of 16 bytes per lane (lane l's bytes from
-// `src` land at dst + 16 l, dst uniform across the wave).  It is issued from
+// base + off_l land at dst + 16 l; base and dst uniform across the wave, so
+// the address is a scalar base plus a 32-bit lane offset).  It is issued from
 // inline assembly so that the compiler does not track it: the compiler
 // otherwise waits for every such copy before the next LDS read, which would
 // serialise the prefetch.  Untracked copies only make the compiler's own
@@ -210,9 +211,9 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // bar(): workgroup barrier that waits for this wave's LDS traffic only.
 // Global loads in flight (prefetches) and global stores (outputs nobody in
 // the workgroup reads) may stay outstanding across it.
-__device__ __forceinline__ void g2lds16(const void* src, void* dst) {
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t off, void* dst) {
     const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)dst));
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -240,14 +241,17 @@ __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, si
     static_assert(PER * 64 * NW == L * PR, "pieces must split evenly over the issuing waves");
     const int lane = threadIdx.x & 63;
     const int buf = c & 1;
+    const int last = a.T - 1 - c * L;                  // last real row of the chunk (>= 0)
+    const size_t row0 = tokidx(a, b, h, c * L) * DK;  // the chunk's first row
+    const uint32_t rs = uint32_t(a.H) * DK * 2;        // bytes from one token's row to the next
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int blk = w + NW * m;  // 64-piece block of the tile
         const int pc = lane + 64 * blk;
-        const size_t off = tokidx(a, b, h, min(c * L + pc / PR, a.T - 1)) * DK + (pc % PR) * 8;
-        g2lds16(a.k + off, &sm.RK[buf][blk * 512]);
-        g2lds16(a.alpha + off, &sm.RA[buf][blk * 512]);
-        g2lds16(a.omega + off, &sm.RW[buf][blk * 512]);
+        const uint32_t off = uint32_t(min(pc / PR, last)) * rs + uint32_t(pc % PR) * 16;
+        g2lds16(a.k + row0, off, &sm.RK[buf][blk * 512]);
+        g2lds16(a.alpha + row0, off, &sm.RA[buf][blk * 512]);
+        g2lds16(a.omega + row0, off, &sm.RW[buf][blk * 512]);
     }
 }
 
@@ -405,9 +409,15 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
                                           int nchunks) {
     c = min(max(c, 0), nchunks - 1);  // always issue: see the loader note above
     const unsigned lane = threadIdx.x & 63;
+    // token c L + 8 f + tt, clamped to the last one: first row tb, then at
+    // most `last` rows further
+    const int tb = min(c * L + 8 * f, a.T - 1);
+    const int last = min(7, a.T - 1 - tb);
+    const size_t e0 = tokidx(a, b, h, tb) * DK;
+    const int rs = a.H * DK;  // elements from one token's row to the next
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-        const size_t e = tokidx(a, b, h, min(c * L + 8 * f + tt, a.T - 1)) * DK;
+        const size_t e = e0 + size_t(min(tt, last) * rs);
         if (DK == 128) {
             X.kp[tt] = reinterpret_cast<const uint32_t*>(a.k + e)[lane];
             X.qp[tt] = reinterpret_cast<const uint32_t*>(a.q + e)[lane];
@@ -635,11 +645,14 @@ __device__ __forceinline__ void state_issue_t(Smem<DK>& sm, const Args& a, size_
                                               int c, int nchunks) {
     c = min(max(c, 0), nchunks - 1);  // always exactly two instructions (the wait below counts them)
     const int lane = threadIdx.x & 63;
+    const int last = a.T - 1 - c * L;
+    const bf16_t* base = a.v + tokidx(a, b, h, c * L) * a.DV + colb;
+    const uint32_t rs = uint32_t(a.H) * uint32_t(a.DV) * 2;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const int pc = lane + 64 * m;  // piece: token pc / 4, columns 8 (pc % 4) ..
-        const size_t off = tokidx(a, b, h, min(c * L + pc / 4, a.T - 1)) * a.DV + colb + 8 * (pc % 4);
-        g2lds16(a.v + off, &sm.RV[c % 3][cw][m * 512]);
+        const uint32_t off = uint32_t(min(pc / 4, last)) * rs + uint32_t(pc % 4) * 16;
+        g2lds16(base, off, &sm.RV[c % 3][cw][m * 512]);
     }
 }
 
@@ -762,12 +775,19 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     __shared__ Smem<DK> sm;
     const int ntile = a.DV / DVT;
     const int bid = blockIdx.x;
-    // the column tiles of one (batch, head) pair share an XCD (and its L2)
-    const int unit = (bid / (8 * ntile)) * 8 + (bid % 8);
+    // Work items are dealt to the eight XCDs in turn (block bid runs on XCD
+    // bid % 8); the column tiles of one (batch, head) pair share an XCD and
+    // its L2.  Items are numbered batch-fastest, so with B a multiple of 8
+    // an XCD streams whole [H, d] token rows of its batches rather than a
+    // fixed slice of every row (which would keep hitting the same HBM
+    // channels).
+    const int item = (bid / (8 * ntile)) * 8 + (bid % 8);
     const int tile = (bid / 8) % ntile;
-    if (unit >= a.units) return;
-    const int h = unit % a.H;
-    const size_t b = size_t(unit / a.H);
+    if (item >= a.units) return;
+    const int nbatch = a.units / a.H;
+    const int h = item / nbatch;
+    const size_t b = size_t(item % nbatch);
+    const int unit = int(b) * a.H + h;  // (batch, head) index of the [B, H, ...] states
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
     const int nchunks = (a.T + L - 1) / L;
