@@ -51,7 +51,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
+#include <utility>
 
 namespace kdn {
 namespace {
@@ -61,7 +63,7 @@ constexpr int NT = L / 16;       // 16-token tiles per chunk
 constexpr int DVT = 64;          // value columns per workgroup
 constexpr int NTHREADS = 512;    // 8 waves
 constexpr int PT = L + 8;        // pitch (elements) of [rows][L] bf16 tiles
-constexpr int CHAIN_SPLIT = 18;  // chain tokens run before the mid-iteration barrier
+constexpr int CHAIN_SPLIT = 16;  // chain tokens run before the mid-iteration barrier
 static_assert(L == 32 && NT == 2, "the kernel is written for 32-token chunks");
 
 typedef uint16_t bf16_t;
@@ -82,6 +84,21 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     v[0] = (__bf16)lo;
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
+}
+// a * b + c as the three-operand form: the two-operand accumulate form would
+// overwrite c, which for the chain's omega is a loop-carried input register
+// that must keep its zero lower half (so the compiler would add a copy)
+__device__ __forceinline__ float fma3(float a, float b, float c) {
+    float r;
+    asm("v_fma_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// pack2 as one instruction the compiler cannot split again (it would convert
+// each half on its own when the halves are stored separately)
+__device__ __forceinline__ uint32_t pack2_opaque(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
 }
 __device__ __forceinline__ bf16_t to_bf(float x) {
     __bf16 b = (__bf16)x;
@@ -137,21 +154,24 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int DK>
 struct Smem {
+    // The chain's tiles come first: every per-token offset into them then
+    // fits the 16-bit immediate of the LDS instructions (a larger one makes
+    // the compiler keep one address register per token).
+    alignas(16) bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
+    alignas(16) bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
+    alignas(16) bf16_t RW[2][L * DK];
+    alignas(16) bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
+    alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
+    alignas(16) float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
+    alignas(16) bf16_t Kh[2][L * DK];    // kappa'_t / g_t (chain: diagonal; formation: isotropic)
     alignas(16) bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
     alignas(16) bf16_t Qt[2][L * DK];    //  q_t g_t
-    alignas(16) bf16_t Kh[2][L * DK];    // kappa'_t (chain), then kappa'_t / g_t (formation)
     alignas(16) bf16_t KhT[2][DK * PT];  // (kappa'_t / g_t)^T  [i][perm32(t)]
     alignas(16) bf16_t QK[2][L * PT];    // tril(Qt Kh^T)      [t][perm32(s)]
     alignas(16) bf16_t Td[2][NT * 256];  // inverses of M's diagonal blocks [a][t][s]
     alignas(16) bf16_t Mo[2][256];       // -M's block (1,0)   [t][s]
-    alignas(16) bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
-    alignas(16) bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
-    alignas(16) bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
-    alignas(16) bf16_t RW[2][L * DK];
     alignas(16) bf16_t RV[3][2][L * 32]; // v tiles of the two state waves, [t][32 columns], ring of 3
-    alignas(16) float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
     alignas(16) float rr[3][L];          // r_t (ring of three chunks: written a chunk ahead)
-    alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
     alignas(16) float bh[2][L];          // b_hat_t (isotropic)
     alignas(16) float gs[2][L];          // g_t (isotropic, scalar)
     alignas(16) float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
@@ -181,6 +201,11 @@ __device__ __forceinline__ size_t tokidx(const Args& a, size_t b, int h, int t) 
 }
 
 constexpr uint32_t BF_ONE = 0x3f80u;  // bf16 1.0
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 
 // ---------------------------------------------------------------------------
 // chain role, diagonal variant: lane = key channel
@@ -273,30 +298,88 @@ __device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h,
     return a.r[tokidx(a, b, h, min(c * L + min(lane, L - 1), a.T - 1))];
 }
 
-// tokens [T0, T1) of chunk buffer buf with nvalid real tokens; p carries
+// bf16 -> fp32 by loading the 16 bits into the upper half of a register whose
+// lower half is zero: the load is the conversion.  The compiler emits this
+// form only for a fresh register with an explicit clear, so the chain's reads
+// are issued from inline assembly into loop-carried input registers whose
+// lower halves are zero from the start and never written.  All 48 reads of a
+// 16-token range (k, alpha, omega) and the wait for them form ONE asm
+// statement: the registers are then defined only once the data is there (with
+// separate statements the compiler may copy a register before its load has
+// landed).
+constexpr int CHAIN_SLOTS = 16;  // tokens per chain segment
+static_assert(2 * CHAIN_SLOTS == L && CHAIN_SPLIT == CHAIN_SLOTS, "two 16-token chain segments per chunk");
+struct ChainIn {
+    uint32_t x[3 * CHAIN_SLOTS];  // k, alpha, omega of the segment's 16 tokens
+};
+#define KDN_LDH(d, o) "ds_read_u16_d16_hi %" #d ", %48 offset:%" #o "\n\t"
+#define KDN_LDH8(d0, d1, d2, d3, d4, d5, d6, d7, o0, o1, o2, o3, o4, o5, o6, o7) \
+    KDN_LDH(d0, o0) KDN_LDH(d1, o1) KDN_LDH(d2, o2) KDN_LDH(d3, o3) KDN_LDH(d4, o4) KDN_LDH(d5, o5) \
+    KDN_LDH(d6, o6) KDN_LDH(d7, o7)
+#define KDN_OUT8(b) \
+    "+v"(in.x[b]), "+v"(in.x[b + 1]), "+v"(in.x[b + 2]), "+v"(in.x[b + 3]), "+v"(in.x[b + 4]), \
+        "+v"(in.x[b + 5]), "+v"(in.x[b + 6]), "+v"(in.x[b + 7])
+#define KDN_IMM16(base)                                                                                     \
+    "i"(base), "i"(base + RS), "i"(base + 2 * RS), "i"(base + 3 * RS), "i"(base + 4 * RS), "i"(base + 5 * RS), \
+        "i"(base + 6 * RS), "i"(base + 7 * RS), "i"(base + 8 * RS), "i"(base + 9 * RS), "i"(base + 10 * RS),   \
+        "i"(base + 11 * RS), "i"(base + 12 * RS), "i"(base + 13 * RS), "i"(base + 14 * RS), "i"(base + 15 * RS)
+// in.x[16 m + j] <- tile m (k, alpha, omega) row T0 + j of buffer BUF, for the
+// lane address `addr` of column i in the first tile
+template <int DK, int BUF, int T0>
+__device__ __forceinline__ void chain_read16(ChainIn& in, uint32_t addr) {
+    constexpr int TILE = 2 * L * DK * 2;  // bytes of one raw tile pair (two buffers)
+    constexpr int RS = DK * 2;            // bytes per row
+    constexpr int K0 = BUF * L * DK * 2 + T0 * RS, A0 = TILE + K0, W0 = 2 * TILE + K0;
+    static_assert(W0 + 15 * RS < 65536, "LDS immediate offset");
+    asm volatile(KDN_LDH8(0, 1, 2, 3, 4, 5, 6, 7, 49, 50, 51, 52, 53, 54, 55, 56)
+                 KDN_LDH8(8, 9, 10, 11, 12, 13, 14, 15, 57, 58, 59, 60, 61, 62, 63, 64)
+                 KDN_LDH8(16, 17, 18, 19, 20, 21, 22, 23, 65, 66, 67, 68, 69, 70, 71, 72)
+                 KDN_LDH8(24, 25, 26, 27, 28, 29, 30, 31, 73, 74, 75, 76, 77, 78, 79, 80)
+                 KDN_LDH8(32, 33, 34, 35, 36, 37, 38, 39, 81, 82, 83, 84, 85, 86, 87, 88)
+                 KDN_LDH8(40, 41, 42, 43, 44, 45, 46, 47, 89, 90, 91, 92, 93, 94, 95, 96)
+                 "s_waitcnt lgkmcnt(0)"
+                 : KDN_OUT8(0), KDN_OUT8(8), KDN_OUT8(16), KDN_OUT8(24), KDN_OUT8(32), KDN_OUT8(40)
+                 : "v"(addr), KDN_IMM16(K0), KDN_IMM16(A0), KDN_IMM16(W0)
+                 : "memory");
+}
+#undef KDN_LDH
+#undef KDN_LDH8
+#undef KDN_OUT8
+#undef KDN_IMM16
+
+// tokens [T0, T1) of chunk buffer BUF with nvalid real tokens; p carries
 // across chunks, g restarts at every chunk.  Padding tokens (t >= nvalid) act
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
-template <int DK, int T0, int T1, bool MASK>
-__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, float& p, float& g, int nvalid,
+template <int DK, int BUF, int T0, int T1, bool MASK>
+__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i, float& p, float& g, int nvalid,
                                                int gring) {
+    constexpr int buf = BUF;  // compile-time, so every LDS offset below is an immediate
     constexpr int NTOK = T1 - T0;
-    // swizzled LDS offsets of this lane's gain column for rows 0..15; rows
-    // 16..31 repeat the pattern 16 rows further (the swizzle period divides 16)
-    const int pos = perm32(i);
-    int khoff[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) khoff[t] = sw<DK>(t, pos);
+    static_assert(NTOK == CHAIN_SLOTS, "one 16-token chain segment");
+    // swizzled LDS offset of this lane's gain column in row t:
+    //   sw(t, pos) = sw(0, pos) ^ ((t % NCH) (DK + 8)) + (t - t % NCH) DK
+    // (row t's chunk index is XORed into the column chunk and the row bits do
+    // not overlap the column bits), so each row costs one XOR
+    constexpr int NCH = DK / 8;
+    const int kh0 = sw<DK>(0, perm32(i));
     // read phase: every LDS read of the token range is issued before the
-    // recurrence starts (two waves per SIMD cannot hide LDS latency)
-    float kk[NTOK], al[NTOK], w[NTOK], cv[NTOK];
+    // recurrence starts (two waves per SIMD cannot hide LDS latency).  The raw
+    // tiles sit at the start of the LDS block: one lane address, immediate
+    // offsets for the three tiles, both buffers and every row.
+    static_assert(offsetof(Smem<DK>, RK) == 0 && offsetof(Smem<DK>, RA) == 2 * L * DK * 2 &&
+                      offsetof(Smem<DK>, RW) == 4 * L * DK * 2,
+                  "raw chain tiles must be contiguous at the start of the LDS block");
+    float cv[NTOK];
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) cv[j] = sm.cr[buf][T0 + j];  // same address on every lane: broadcast
+    chain_read16<DK, BUF, T0>(in, uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)&sm.RK[0][i])));
+    float kk[NTOK], al[NTOK], w[NTOK];
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
-        const int t = T0 + j;
-        kk[j] = bf1(sm.RK[buf][t * DK + i]);
-        al[j] = bf1(sm.RA[buf][t * DK + i]);
-        w[j] = bf1(sm.RW[buf][t * DK + i]);
-        cv[j] = sm.cr[buf][t];  // same address on every lane: broadcast
+        kk[j] = __uint_as_float(in.x[j]);
+        al[j] = __uint_as_float(in.x[CHAIN_SLOTS + j]);
+        w[j] = __uint_as_float(in.x[2 * CHAIN_SLOTS + j]);
     }
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
@@ -308,12 +391,18 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, int buf, int i, flo
             w[j] = ok ? w[j] : 0.f;
         }
         const float asq = al[j] * al[j];
-        const float u = cv[j] * kk[j] * kk[j];
-        const float ph = fmaf(asq, p, w[j]);  // the only loop-carried chain: ph -> p
-        p = ph * __builtin_amdgcn_rcpf(fmaf(u, ph, 1.f));
+        // the fewest instructions, rather than the shortest dependent path,
+        // is what makes this loop fast (one wave per SIMD issues it)
+        const float ck = cv[j] * kk[j];           // (mu / r) k
+        const float ph = fma3(asq, p, w[j]);      // the only loop-carried chain: ph -> p
+        const float kph = kk[j] * ph;             // kappa' = p_hat k
+        p = ph * __builtin_amdgcn_rcpf(fmaf(ck, kph, 1.f));  // 1 + (mu / r) k^2 p_hat
         g *= al[j];
-        sm.Kh[buf][khoff[t & 15] + (t >> 4) * 16 * DK] = to_bf(ph * kk[j]);
-        sm.G[buf][t * DK + i] = to_bf(g);
+        // the gain in the chunk's scaled frame, kappa'_t / g_t, and g_t: one
+        // conversion for both, the halves stored separately
+        const uint32_t pk = pack2_opaque(kph * __builtin_amdgcn_rcpf(g), g);
+        sm.Kh[buf][(kh0 ^ ((t % NCH) * (DK + 8))) + (t - t % NCH) * DK] = bf16_t(pk);
+        sm.G[buf][t * DK + i] = bf16_t(pk >> 16);
         if (t == L - 1) sm.gL[gring][i] = g;
     }
 }
@@ -435,7 +524,7 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     const int i0 = CPL * lane;             // first channel of this lane
     const int pos = perm32(i0);            // perm32(i0 + 1) == pos + 1
     // read phase: the chain's outputs for the wave's 8 tokens
-    uint32_t gw[8], kw[8];  // DK = 128: bf16 pairs of g and kappa'; DK = 64: low halves
+    uint32_t gw[8], kw[8];  // DK = 128: bf16 pairs of g and kappa' / g; DK = 64: low halves
     float gsv[8], bhv[8];   // isotropic scalars
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -450,56 +539,59 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             gw[tt] = sm.G[nb][t * DK + i0];
             kw[tt] = sm.Kh[nb][sw<DK>(t, pos)];
         }
+        // (diagonal variant: Kh already holds kappa'_t / g_t from the chain)
     }
-    uint32_t kt[4][CPL];  // Kh^T staging: 4 tokens of each of this lane's channels
+    uint32_t kw4[4];  // Kh^T staging: the bf16 pairs (DK = 128) or values of 4 tokens
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
         const int t = 8 * f + tt;
         const int off = sw<DK>(t, pos);
         const bool ok = !MASK || t < nvalid;  // tail chunk only: tokens past T read as zero
         const uint32_t kp = ok ? X.kp[tt] : 0u, qp = ok ? X.qp[tt] : 0u;
-        float kk[CPL], qq[CPL], g[CPL], kh[CPL];
+        float kk[CPL], qq[CPL], g[CPL];
         kk[0] = bf_lo(kp);
         qq[0] = bf_lo(qp);
         if (CPL == 2) {
             kk[CPL - 1] = bf_hi(kp);
             qq[CPL - 1] = bf_hi(qp);
         }
+        uint32_t khw;  // this lane's Kh entries of token t
         if (ISO) {
             const float sc = bhv[tt] * __builtin_amdgcn_rcpf(gsv[tt]);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                g[c] = gsv[tt];
-                kh[c] = kk[c] * sc;
-            }
+            for (int c = 0; c < CPL; ++c) g[c] = gsv[tt];
+            khw = CPL == 2 ? pack2(kk[0] * sc, kk[CPL - 1] * sc) : uint32_t(to_bf(kk[0] * sc));
+            if (CPL == 2) *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khw;
+            else sm.Kh[nb][off] = bf16_t(khw);
         } else {
+            // Kh already holds kappa'_t / g_t, written by the chain
             g[0] = bf_lo(gw[tt]);
-            kh[0] = bf_lo(kw[tt]) * __builtin_amdgcn_rcpf(g[0]);
-            if (CPL == 2) {
-                g[CPL - 1] = bf_hi(gw[tt]);
-                kh[CPL - 1] = bf_hi(kw[tt]) * __builtin_amdgcn_rcpf(g[CPL - 1]);
-            }
+            if (CPL == 2) g[CPL - 1] = bf_hi(gw[tt]);
+            khw = kw[tt];
         }
         if (CPL == 2) {
-            const uint32_t khp = pack2(kh[0], kh[CPL - 1]);
             *reinterpret_cast<uint32_t*>(&sm.Kn[nb][off]) = pack2(-kk[0] * g[0], -kk[CPL - 1] * g[CPL - 1]);
             *reinterpret_cast<uint32_t*>(&sm.Qt[nb][off]) = pack2(qq[0] * g[0], qq[CPL - 1] * g[CPL - 1]);
-            *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khp;
-            kt[tt & 3][0] = khp & 0xffffu;
-            kt[tt & 3][CPL - 1] = khp >> 16;
         } else {
-            const bf16_t khb = to_bf(kh[0]);
             sm.Kn[nb][off] = to_bf(-kk[0] * g[0]);
             sm.Qt[nb][off] = to_bf(qq[0] * g[0]);
-            sm.Kh[nb][off] = khb;
-            kt[tt & 3][0] = khb;
         }
+        kw4[tt & 3] = khw;
         if ((tt & 3) == 3) {
-            const int tp = perm32(t - 3);  // 4 consecutive positions
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + c) * PT + tp]) =
-                    u2{kt[0][c] | (kt[1][c] << 16), kt[2][c] | (kt[3][c] << 16)};
+            // Kh^T rows i0 (and i0 + 1): 4 consecutive token positions each
+            const int tp = perm32(t - 3);
+            if (CPL == 2) {
+                // byte selectors: low halves of two pairs, high halves of two pairs
+                const uint32_t lo01 = __builtin_amdgcn_perm(kw4[1], kw4[0], 0x05040100u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(kw4[3], kw4[2], 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(kw4[1], kw4[0], 0x07060302u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(kw4[3], kw4[2], 0x07060302u);
+                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) = u2{lo01, lo23};
+                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + 1) * PT + tp]) = u2{hi01, hi23};
+            } else {
+                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) =
+                    u2{(kw4[0] & 0xffffu) | (kw4[1] << 16), (kw4[2] & 0xffffu) | (kw4[3] << 16)};
+            }
         }
     }
 }
@@ -770,6 +862,20 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+// Wave w of the workgroup runs on SIMD w % 4.  Waves 0 and 1 run the chain;
+// ROLE_LAYOUT places the two state waves and the four formation waves
+// (formation index f = 0..3) on the SIMDs:
+//   0: state 4, 5;  formation 2, 3, 6, 7
+//   1: state 6, 7;  formation 2, 3, 4, 5
+//   2: state 6, 7;  formation 4, 5, 2, 3
+constexpr int ROLE_LAYOUT = 0;
+__device__ __forceinline__ bool is_state_wave(int w) {
+    return ROLE_LAYOUT == 0 ? (w == 4 || w == 5) : (w == 6 || w == 7);
+}
+__device__ __forceinline__ int state_index(int w) { return ROLE_LAYOUT == 0 ? w - 4 : w - 6; }
+__device__ __forceinline__ int form_index(int w) {
+    return ROLE_LAYOUT == 0 ? (w < 4 ? w - 2 : w - 4) : ROLE_LAYOUT == 1 ? w - 2 : (w >= 4 ? w - 4 : w);
+}
 template <int DK, bool ISO>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     __shared__ Smem<DK> sm;
@@ -794,12 +900,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int nit = ((nchunks + 2) + 1) & ~1;  // even number of pipeline iterations
 
     // the chain's first input tiles (issued by the formation waves)
-    const int fwave = wave < 4 ? wave - 2 : wave - 4;  // formation index of waves 2,3,6,7
-    const bool is_form = wave == 2 || wave == 3 || wave == 6 || wave == 7;
+    const bool is_form = wave >= 2 && !is_state_wave(wave);
+    const int fwave = form_index(wave);
     uint32_t r0 = 0;
     if (!ISO && is_form) {
         chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, fwave);
-        if (wave == 7) r0 = chain_r_load(a, b, h, 0, nchunks);
+        if (fwave == 3) r0 = chain_r_load(a, b, h, 0, nchunks);
     }
     // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31, and the block
     // (0,1) of each diagonal-block inverse is zero: write both once
@@ -810,7 +916,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         sm.Td[bb][a * 256 + tt * 16 + ss] = 0;
     }
     vm_wait<0>();  // chunk 0's tiles and r have landed
-    if (!ISO && wave == 7) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
+    if (!ISO && is_form && fwave == 3) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
     if (wave == 0 || wave == 1) {
@@ -821,24 +927,30 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             float p = 0.f;
             if (active) p = a.p0 ? a.p0[size_t(unit) * DK + i] : a.c0[h];
             settle(p);  // p is ready before the pipelined loop
-            for (int c = 0; c < nit; ++c) {
-                // chunk c's tiles are in LDS buffer c & 1 (chunk c + 1's are
-                // fetched meanwhile by the formation waves)
-                const int buf = c & 1;
+            // chunk c's tiles are in LDS buffer c & 1 (chunk c + 1's are
+            // fetched meanwhile by the formation waves); the loop runs two
+            // chunks per trip so that the buffer index is a constant
+            ChainIn in;
+#pragma unroll
+            for (int j = 0; j < 3 * CHAIN_SLOTS; ++j) in.x[j] = 0u;
+            auto step = [&](auto bufc, int c) {
+                constexpr int BUF = decltype(bufc)::value;
                 const int nvalid = min(L, a.T - c * L);
                 float g = 1.f;
-                if (active) {
-                    if (c < nchunks) {
-                        if (nvalid == L) chain_diag_run<DK, 0, CHAIN_SPLIT, false>(sm, buf, i, p, g, L, c % 3);
-                        else chain_diag_run<DK, 0, CHAIN_SPLIT, true>(sm, buf, i, p, g, nvalid, c % 3);
-                    }
+                if (active && c < nchunks) {
+                    if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false>(sm, in, i, p, g, L, c % 3);
+                    else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true>(sm, in, i, p, g, nvalid, c % 3);
                 }
                 bar();
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, CHAIN_SPLIT, L, false>(sm, buf, i, p, g, L, c % 3);
-                    else chain_diag_run<DK, CHAIN_SPLIT, L, true>(sm, buf, i, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false>(sm, in, i, p, g, L, c % 3);
+                    else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true>(sm, in, i, p, g, nvalid, c % 3);
                 }
                 bar();
+            };
+            for (int c = 0; c < nit; c += 2) {
+                step(IntC<0>{}, c);
+                step(IntC<1>{}, c + 1);
             }
             if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
         } else {
@@ -862,9 +974,9 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             }
             if (wave == 0 && lane == 0 && tile == 0) a.p_T[unit] = bprev;
         }
-    } else if (wave == 4 || wave == 5) {
+    } else if (is_state_wave(wave)) {
         // ---------------- state ----------------
-        const int cw = wave - 4;
+        const int cw = state_index(wave);
         const int colb = tile * DVT + cw * 32;
         const int n = lane & 15, g4 = (lane >> 4) * 4;
         StateAcc<DK> st;
@@ -902,7 +1014,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
     } else {
         // ---------------- formation ----------------
-        const int f = wave < 4 ? wave - 2 : wave - 4;  // 2,3,6,7 -> 0,1,2,3
+        const int f = fwave;
         FormRegs<DK> A, B;
         // chunk c is formed at iteration c + 1; its q, k are loaded one iteration earlier
         for (int it = 0; it < nit; it += 2) {
