@@ -237,8 +237,18 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // Global loads in flight (prefetches) and global stores (outputs nobody in
 // the workgroup reads) may stay outstanding across it.
 __device__ __forceinline__ void g2lds16(const void* base, uint32_t off, void* dst) {
-    const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)dst));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+    // both are uniform by construction; readfirstlane states it to the
+    // compiler (its divergence analysis does not always see it), and costs
+    // nothing for a value already in scalar registers
+    // (readfirstlane returns int: each half goes back through uint32_t so the
+    // low half is not sign-extended into the high one)
+    const uint32_t lds =
+        uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)dst))));
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
+    const uint64_t bu = (uint64_t(hi) << 32) | uint64_t(lo);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bu), "s"(lds) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -252,26 +262,26 @@ __device__ __forceinline__ void settle(const T& x) {
     asm volatile("" ::"v"(x));
 }
 
-// Issue the raw k, alpha, omega tiles of chunk c (the chain's input) into
-// LDS buffer c & 1.  The four formation waves (w = 0..3) split the 16-byte
-// pieces, so the chain waves spend their issue slots on the recurrence only;
-// rows past the end of the sequence repeat the last token (masked where used).
-template <int DK>
+// Issue rows 16 HALF .. 16 HALF + 15 of the raw k, alpha, omega tiles of
+// chunk c (the chain's input) into LDS buffer c & 1, split over NW issuing
+// waves (w = 0 .. NW - 1).  Rows 0..15 of a buffer are free once the chain's
+// first segment has read them, so they are fetched one segment earlier than
+// rows 16..31, by other waves.  Rows past the end of the sequence repeat the
+// last token (masked where used).
+template <int DK, int HALF, int NW>
 __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, size_t b, int h, int c,
                                                  int nchunks, int w) {
     if (c < 0 || c >= nchunks) return;
-    constexpr int NW = 4;                 // issuing waves
-    constexpr int PR = DK / 8;            // 16-byte pieces per row
-    constexpr int PER = L * PR / 64 / NW; // instructions per tile per wave
-    static_assert(PER * 64 * NW == L * PR, "pieces must split evenly over the issuing waves");
+    constexpr int PR = DK / 8;          // 16-byte pieces per row
+    constexpr int NB = L * PR / 64;     // 64-piece blocks per tile (four rows each at d_k = 128)
+    constexpr int B0 = HALF * NB / 2, B1 = B0 + NB / 2;
     const int lane = threadIdx.x & 63;
     const int buf = c & 1;
     const int last = a.T - 1 - c * L;                  // last real row of the chunk (>= 0)
     const size_t row0 = tokidx(a, b, h, c * L) * DK;  // the chunk's first row
     const uint32_t rs = uint32_t(a.H) * DK * 2;        // bytes from one token's row to the next
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        const int blk = w + NW * m;  // 64-piece block of the tile
+    for (int blk = B0 + w; blk < B1; blk += NW) {
         const int pc = lane + 64 * blk;
         const uint32_t off = uint32_t(min(pc / PR, last)) * rs + uint32_t(pc % PR) * 16;
         g2lds16(a.k + row0, off, &sm.RK[buf][blk * 512]);
@@ -751,8 +761,8 @@ __device__ __forceinline__ void state_issue_t(Smem<DK>& sm, const Args& a, size_
 template <int DK>
 struct StateAcc {
     f4 S[DK / 16][2];
-    f4 R[NT][2];
     f4 O[NT][2];
+    b8 Db[2];  // Dn of the chunk (bf16, B-operand layout), per 16-column tile
 };
 
 template <int DK>
@@ -776,11 +786,15 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
             aq[at][kk] = *reinterpret_cast<const b8*>(sm.Qt[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
         }
     }
+    const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
+    const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
+    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
     b8 Sb[KS][2];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
+    f4 R[NT][2];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
 #pragma unroll
@@ -797,9 +811,19 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
                 r = mfma32(ak[at][kk], Sb[kk][ct], r);  // V - Kt S
                 o = mfma32(Sb[kk][ct], aq[at][kk], o);  // (Qt S)^T: value column x token
             }
-            st.R[at][ct] = r;
+            R[at][ct] = r;
             st.O[at][ct] = o;
         }
+    }
+    // Dn = M^-1 R by block substitution (the inverses and -M_10 are ready
+    // since the previous iteration)
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const f4 d0 = mfma16(t0, pack4(R[0][ct]), zero);
+        const f4 r1 = mfma16(mo, pack4(d0), R[1][ct]);
+        const f4 d1 = mfma16(t1, pack4(r1), zero);
+        st.Db[ct] = pack8(d0, d1);
     }
 }
 
@@ -810,11 +834,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     const bool full = (c + 1) * L <= a.T;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
-    const f4 zero = {0.f, 0.f, 0.f, 0.f};
     // read phase: every LDS operand of the segment
-    const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
-    const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
-    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
     b8 aqk[NT], akh[DK / 16];
     f4 glv[DK / 16];
 #pragma unroll
@@ -824,14 +844,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
         akh[it] = *reinterpret_cast<const b8*>(&sm.KhT[b][(16 * it + n) * PT + kg8]);
         glv[it] = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
     }
-    b8 Db[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const f4 d0 = mfma16(t0, pack4(st.R[0][ct]), zero);
-        const f4 r1 = mfma16(mo, pack4(d0), st.R[1][ct]);
-        const f4 d1 = mfma16(t1, pack4(r1), zero);
-        Db[ct] = pack8(d0, d1);
-    }
+    const b8* Db = st.Db;
     // outputs, transposed: lane (n, g4) holds value columns g4 .. g4 + 3 of
     // token 16 at + n, written as one 8-byte store per tile
     bf16_t* orow = a.o + tokidx(a, bb, h, c * L + n) * a.DV + colb + g4;
@@ -904,7 +917,9 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int fwave = form_index(wave);
     uint32_t r0 = 0;
     if (!ISO && is_form) {
-        chain_diag_issue<DK>(sm, a, b, h, 0, nchunks, fwave);
+        chain_diag_issue<DK, 0, 4>(sm, a, b, h, 0, nchunks, fwave);
+        chain_diag_issue<DK, 1, 4>(sm, a, b, h, 0, nchunks, fwave);
+        chain_diag_issue<DK, 0, 4>(sm, a, b, h, 1, nchunks, fwave);
         if (fwave == 3) r0 = chain_r_load(a, b, h, 0, nchunks);
     }
     // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31, and the block
@@ -999,9 +1014,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             state_issue_t<DK>(sm, a, b, h, colb, cw, it, nchunks);
             if (c >= 0 && c < nchunks) state_seg1<DK>(st, sm, c & 1, cw, c % 3, min(L, a.T - c * L));
             // everything but the two loads just issued has landed: the v of
-            // chunk it - 1 and the previous iteration's stores
+            // chunk it - 1, the previous iteration's stores and chain rows
             vm_wait<2>();
             bar();
+            // rows 0..15 of the chain's chunk it + 2: the chain has read those
+            // rows of chunk it (same buffer) before the barrier above
+            if (!ISO) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
             if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
             bar();
         }
@@ -1026,7 +1044,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 // the chain's inputs for chunk c + 2 (it consumes chunk c + 1 now)
                 uint32_t rnext = 0;
                 if (!ISO) {
-                    chain_diag_issue<DK>(sm, a, b, h, c + 2, nchunks, f);
+                    chain_diag_issue<DK, 1, 4>(sm, a, b, h, c + 2, nchunks, f);  // rows 16..31
                     if (f == 3) rnext = chain_r_load(a, b, h, c + 2, nchunks);
                 }
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
