@@ -68,7 +68,7 @@ enum kdn_status {
     KDN_ERR_ALIAS = 6        /* an output overlaps an input it may not overlap */
 };
 /* forward algorithms (kdn_forward_algo).  The chunked algorithm takes bf16
- * inputs with dk 64 or 128 and dv a multiple of 64, q, k, v, alpha and omega
+ * inputs (dk and dv are 64 or 128 for every algorithm), q, k, v, alpha and omega
  * 16-byte aligned and o 8-byte aligned; KDN_ALGO_AUTO uses it whenever these
  * hold and the recurrent kernel otherwise, and an explicit KDN_ALGO_CHUNKED
  * call outside them returns KDN_ERR_UNSUPPORTED. */

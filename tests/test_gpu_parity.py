@@ -59,6 +59,31 @@ def test_forward_small(dev, algo, variant, dtype, dk, dv, T):
     check(f"{algo}/{variant}/{dtype}/dk{dk}/dv{dv}/T{T}", got, oracle_forward(w, x), dtype)
 
 
+# Shapes that exercise the chunked kernel's work mapping and range: more than
+# eight (batch, head) items (a ragged last group of XCD-dealt items), a
+# single head, batch counts that are not multiples of 8, one-token tails, and
+# strong decay (alpha ~ sigmoid(N(0, 0.5)) or sigmoid(N(-1, 0.5)), so the
+# in-chunk cumulative decay reaches 1e-10 .. 1e-18).
+SHAPES = [
+    # B, T, H, dk, dv, alpha_loc, omega_loc
+    (9, 97, 2, 128, 128, 0.0, -1.0),
+    (1, 130, 1, 64, 64, 2.0, -4.0),
+    (16, 40, 1, 128, 64, -1.0, -2.0),
+]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}_t{}_h{}_dk{}_dv{}_a{}".format(*s[:6]))
+def test_forward_shapes(dev, algo, variant, shape):
+    B, T, H, dk, dv, aloc, oloc = shape
+    w = wl.Workload("shape", variant, "bf16", B, T, H, dk, dv, float(dk), "uniform",
+                    700 + B + T + H + dv, alpha_loc=aloc, omega_loc=oloc)
+    x = wl.forward_inputs(w)
+    got = run_forward(dev, w, x, algo)
+    check(f"{algo}/{variant}/b{B}/t{T}/h{H}/dk{dk}/dv{dv}/a{aloc}", got, oracle_forward(w, x), "bf16")
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
 def test_forward_with_initial_state(dev, algo, variant):
