@@ -761,13 +761,23 @@ __device__ __forceinline__ void state_issue_t(Smem<DK>& sm, const Args& a, size_
 template <int DK>
 struct StateAcc {
     f4 S[DK / 16][2];
+    b8 Sb[DK / 32][2];  // S as bf16 MFMA operands (rebuilt after each update)
     f4 O[NT][2];
     b8 Db[2];  // Dn of the chunk (bf16, B-operand layout), per 16-column tile
 };
+template <int DK>
+__device__ __forceinline__ void pack_state(StateAcc<DK>& st) {
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) st.Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
+}
 
 template <int DK>
-__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b, int cw, int vslot,
-                                           int nvalid) {
+// Rows of a tail chunk past the sequence end need no masking here: their v
+// rows repeat the last token (finite), their Kt and Kh are zero, so their Dn
+// reaches neither S nor any stored output row.
+__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b, int cw, int vslot) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
@@ -789,11 +799,7 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
     const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
     const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
     const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
-    b8 Sb[KS][2];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
+    const b8 (&Sb)[KS][2] = st.Sb;
     f4 R[NT][2];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
@@ -801,10 +807,7 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
         for (int ct = 0; ct < 2; ++ct) {
             f4 r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t vb = 16 * at + g4 + e < nvalid ? vr[at][ct][e] : 0u;
-                r[e] = bf1(bf16_t(vb));
-            }
+            for (int e = 0; e < 4; ++e) r[e] = bf1(bf16_t(vr[at][ct][e]));
             f4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
@@ -870,6 +873,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
             st.S[it][ct] = s;
         }
     }
+    pack_state<DK>(st);  // operands of the next chunk's first segment
 }
 
 // ---------------------------------------------------------------------------
@@ -1007,12 +1011,13 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) settle(st.S[it][ct]);  // S0 is ready before the loop
+        pack_state<DK>(st);
         for (int it = 0; it < nit; ++it) {
             // chunk it's v is issued at iteration it, waited for at iteration
             // it + 1 and consumed at iteration it + 2 (ring slot it % 3)
             const int c = it - 2;  // chunk consumed at this iteration
             state_issue_t<DK>(sm, a, b, h, colb, cw, it, nchunks);
-            if (c >= 0 && c < nchunks) state_seg1<DK>(st, sm, c & 1, cw, c % 3, min(L, a.T - c * L));
+            if (c >= 0 && c < nchunks) state_seg1<DK>(st, sm, c & 1, cw, c % 3);
             // everything but the two loads just issued has landed: the v of
             // chunk it - 1, the previous iteration's stores and chain rows
             vm_wait<2>();
