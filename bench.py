@@ -4,7 +4,9 @@ One step = one kdn_forward call over the diagonal bf16 mixer-layer workload
 (B=8, T=4096, H=16, d_k=d_v=128, fp32 state), inputs resident in HBM.
 Prints ONE JSON line with the throughput in tokens/s (B*T per call), the
 HBM roofline of the forward kernel measured with HIP events on the stream it
-runs on, and the fp64 CPU oracle's rate on the same workload.
+runs on, and the fp64 CPU oracle's rate on the same workload.  Warm-up runs
+at least W steps and at least 0.3 s of GPU work (the clock ramps up over the
+first tens of milliseconds of sustained load).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--algo auto|recurrent|chunked]
                     [--no-cpu-baseline] [--no-extra]
@@ -67,6 +69,25 @@ def upload(x, dtype, dev):
     return out
 
 
+WARM_SECONDS = 0.3  # minimum busy time before timing: the GPU clock ramps over tens of ms
+
+
+def warm(fn, count, seconds=WARM_SECONDS):
+    """Run fn `count` times, then keep running it until the GPU has been busy
+    for `seconds` (a few steps alone leave the clock below its sustained
+    level; measured: ~350 us per forward launch in the first ~20 ms against
+    ~297 us afterwards).  Returns the number of calls made."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < count or time.perf_counter() - t0 < seconds:
+        for _ in range(max(1, count)):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_forward(kdn, w, t, steps, warmup, algo):
     """Returns (ms per step over the timed loop, mean single-launch ms)."""
     import torch
@@ -74,9 +95,7 @@ def time_forward(kdn, w, t, steps, warmup, algo):
            torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=t["q"].device),
            torch.empty((w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H),
                        dtype=torch.float32, device=t["q"].device))
-    for _ in range(warmup):
-        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
-    torch.cuda.synchronize()
+    warm(lambda: kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out), warmup)
     # whole timed loop
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -109,10 +128,9 @@ def bench_decode(kdn, w, dev, steps_cap=None):
         toks.append(upload(dict(wl.decode_tokens(w, s), c0=np.ones(1, np.float32)), w.dtype, dev))
     o = torch.empty((w.B, w.H, w.dv), dtype=toks[0]["q"].dtype, device=dev)
     names = ("q", "k", "v", "alpha", "omega", "r")
-    for s in range(min(3, nsteps)):  # warm-up on a scratch copy of the state
-        S2, p2 = S.clone(), p.clone()
-        kdn.step(**{n: toks[s][n] for n in names}, mu=w.mu, S=S2, p=p2, variant=w.variant, o=o)
-    torch.cuda.synchronize()
+    S2, p2 = S.clone(), p.clone()  # warm-up on a scratch copy of the state
+    warm(lambda: kdn.step(**{n: toks[0][n] for n in names}, mu=w.mu, S=S2, p=p2, variant=w.variant, o=o), 3)
+    del S2, p2
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for s in range(nsteps):
