@@ -422,7 +422,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
 // ---------------------------------------------------------------------------
 struct ChainIsoRegs {
     u4 kr[8];            // half a k row (DK/2 channels) of token lane & 31
-    uint32_t al, w, rv;  // alpha, omega, r of token lane & 31
+    bf16_t al, w, rv;  // alpha, omega, r of token lane & 31
 };
 
 template <int DK>
@@ -984,8 +984,13 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     ChainIsoRegs& Y = half ? A : B;
                     const int c = it + half;
                     if (wave == 0) {
-                        chain_iso_load<DK>(Y, a, b, h, c + 1, nchunks);
+                        // the next chunk's loads go out after this chunk's
+                        // registers are consumed: issued earlier, their
+                        // address temporaries would be placed in registers of
+                        // loads still in flight, and the compiler would wait
+                        // for those loads (a full memory round trip) first
                         if (c < nchunks) chain_iso_run<DK>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
+                        chain_iso_load<DK>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
                     bar();
