@@ -36,11 +36,12 @@
 //    inclusive cross-lane scan (5 shuffle levels, renormalised each level).
 //
 // Workgroup = one (batch, head) pair and 64 value columns, 8 waves in roles:
-//   waves 0,1      "chain":     uncertainty recurrence of chunk c+2 -> gain
-//                               numerators kappa' and decays g (LDS)
-//   waves 2,3,6,7  "formation": MFMA operands Kt, Qt, Kh, Kh^T of chunk c+1,
-//                               then M, tril(Qt Kh^T) and the diagonal-block
-//                               inverses of M
+//   waves 0,1      "chain":     uncertainty recurrence of chunk c+2 -> scaled
+//                               gains Kh (stored as Kh^T, the state's operand)
+//                               and decays g (LDS)
+//   waves 2,3,6,7  "formation": MFMA operands Kt, Qt, Kh (isotropic: also
+//                               Kh^T) of chunk c+1, then M, tril(Qt Kh^T) and
+//                               the diagonal-block inverses of M
 //   waves 4,5      "state":     memory pass of chunk c: 32 value columns each,
 //                               S (d_k x 32 fp32) in registers
 // Two workgroup barriers per iteration; every LDS buffer that crosses an
@@ -160,13 +161,13 @@ struct Smem {
     alignas(16) bf16_t RK[2][L * DK];    // raw k, alpha, omega tiles of the chain's next chunk,
     alignas(16) bf16_t RA[2][L * DK];    // [t][i] as in global memory (direct global -> LDS loads)
     alignas(16) bf16_t RW[2][L * DK];
-    alignas(16) bf16_t G[2][L * DK];     // g_t,i (diagonal variant)  [t][i]
+    alignas(16) bf16_t GQ[2][L * DK];    // g_t,i (diagonal variant)  [t / 8][i][t % 8]
     alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
     alignas(16) float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
-    alignas(16) bf16_t Kh[2][L * DK];    // kappa'_t / g_t (chain: diagonal; formation: isotropic)
+    alignas(16) bf16_t Kh[L * DK];       // kappa'_t / g_t    [t][perm32(i)], swizzled (read in the same iteration)
     alignas(16) bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
     alignas(16) bf16_t Qt[2][L * DK];    //  q_t g_t
-    alignas(16) bf16_t KhT[2][DK * PT];  // (kappa'_t / g_t)^T  [i][perm32(t)]
+    alignas(16) bf16_t KhQ[3][L * DK];   // (kappa'_t / g_t)^T  [P / 8][i][P % 8] with P = perm32(t) (ring of three)
     alignas(16) bf16_t QK[2][L * PT];    // tril(Qt Kh^T)      [t][perm32(s)]
     alignas(16) bf16_t Td[2][NT * 256];  // inverses of M's diagonal blocks [a][t][s]
     alignas(16) bf16_t Mo[2][256];       // -M's block (1,0)   [t][s]
@@ -357,7 +358,7 @@ __device__ __forceinline__ void chain_read16(ChainIn& in, uint32_t addr) {
 #undef KDN_OUT8
 #undef KDN_IMM16
 
-// tokens [T0, T1) of chunk buffer BUF with nvalid real tokens; p carries
+// tokens [T0, T1) of chunk buffer BUF (and KhQ slot gring) with nvalid real tokens; p carries
 // across chunks, g restarts at every chunk.  Padding tokens (t >= nvalid) act
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
@@ -367,12 +368,6 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
     constexpr int buf = BUF;  // compile-time, so every LDS offset below is an immediate
     constexpr int NTOK = T1 - T0;
     static_assert(NTOK == CHAIN_SLOTS, "one 16-token chain segment");
-    // swizzled LDS offset of this lane's gain column in row t:
-    //   sw(t, pos) = sw(0, pos) ^ ((t % NCH) (DK + 8)) + (t - t % NCH) DK
-    // (row t's chunk index is XORed into the column chunk and the row bits do
-    // not overlap the column bits), so each row costs one XOR
-    constexpr int NCH = DK / 8;
-    const int kh0 = sw<DK>(0, perm32(i));
     // read phase: every LDS read of the token range is issued before the
     // recurrence starts (two waves per SIMD cannot hide LDS latency).  The raw
     // tiles sit at the start of the LDS block: one lane address, immediate
@@ -384,7 +379,8 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) cv[j] = sm.cr[buf][T0 + j];  // same address on every lane: broadcast
     chain_read16<DK, BUF, T0>(in, uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)&sm.RK[0][i])));
-    float kk[NTOK], al[NTOK], w[NTOK];
+    float kk[NTOK], al[NTOK], w[NTOK], khv[NTOK], gv[NTOK];
+    uint32_t khp[NTOK / 2], gp[NTOK / 2];  // bf16 pairs of consecutive tokens
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
         kk[j] = __uint_as_float(in.x[j]);
@@ -408,11 +404,26 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         const float kph = kk[j] * ph;             // kappa' = p_hat k
         p = ph * __builtin_amdgcn_rcpf(fmaf(ck, kph, 1.f));  // 1 + (mu / r) k^2 p_hat
         g *= al[j];
-        // the gain in the chunk's scaled frame, kappa'_t / g_t, and g_t: one
-        // conversion for both, the halves stored separately
-        const uint32_t pk = pack2_opaque(kph * __builtin_amdgcn_rcpf(g), g);
-        sm.Kh[buf][(kh0 ^ ((t % NCH) * (DK + 8))) + (t - t % NCH) * DK] = bf16_t(pk);
-        sm.G[buf][t * DK + i] = bf16_t(pk >> 16);
+        // the gain in the chunk's scaled frame, kappa'_t / g_t, and g_t, as
+        // bf16 pairs of consecutive tokens.  Both go out in token groups, one
+        // wide store per group (a store per token and value would make LDS
+        // stores a third of this loop's instructions): g in groups of 8
+        // tokens, kappa'/g as Kh^T in the state's operand order, where the
+        // 8 positions of group P / 8 hold tokens 4 (P / 8) + 0..3 and
+        // 16 + 4 (P / 8) + 0..3, i.e. a 16-token segment fills one half of
+        // each of the four groups.
+        khv[j] = kph * __builtin_amdgcn_rcpf(g);
+        gv[j] = g;
+        if (j & 1) {
+            khp[j / 2] = pack2_opaque(khv[j - 1], khv[j]);
+            gp[j / 2] = pack2_opaque(gv[j - 1], gv[j]);
+        }
+        if ((j & 3) == 3)
+            *reinterpret_cast<u2*>(&sm.KhQ[gring][((j / 4) * DK + i) * 8 + 4 * (T0 / 16)]) =
+                u2{khp[j / 2 - 1], khp[j / 2]};
+        if ((j & 7) == 7)
+            *reinterpret_cast<u4*>(&sm.GQ[buf][((T0 + j) / 8 * DK + i) * 8]) =
+                u4{gp[j / 2 - 3], gp[j / 2 - 2], gp[j / 2 - 1], gp[j / 2]};
         if (t == L - 1) sm.gL[gring][i] = g;
     }
 }
@@ -528,30 +539,34 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
 }
 
 template <int DK, bool ISO, bool MASK>
-__device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int f, int nvalid) {
+__device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int kslot, int f, int nvalid) {
     const int lane = threadIdx.x & 63;
     constexpr int CPL = DK / 64;           // channels per lane
     const int i0 = CPL * lane;             // first channel of this lane
     const int pos = perm32(i0);            // perm32(i0 + 1) == pos + 1
+    // The wave's tokens 8f + 4h + u (h = 0, 1; u = 0..3) are positions
+    // u + 4 (f >> 1) of Kh^T group (2f + h) & 3.
+    const int hq = 4 * (f >> 1);
     // read phase: the chain's outputs for the wave's 8 tokens
-    uint32_t gw[8], kw[8];  // DK = 128: bf16 pairs of g and kappa' / g; DK = 64: low halves
-    float gsv[8], bhv[8];   // isotropic scalars
+    u4 gq[CPL];     // g of channel i0 + cc, tokens 8f .. 8f + 7 (diagonal variant)
+    u2 kq[CPL][2];  // kappa'/g of channel i0 + cc, tokens 8f + 4h .. 8f + 4h + 3 (diagonal variant)
+    float gsv[8], bhv[8];  // isotropic scalars
+    if (ISO) {
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-        const int t = 8 * f + tt;
-        if (ISO) {
-            gsv[tt] = sm.gs[nb][t];
-            bhv[tt] = sm.bh[nb][t];
-        } else if (CPL == 2) {
-            gw[tt] = *reinterpret_cast<const uint32_t*>(&sm.G[nb][t * DK + i0]);
-            kw[tt] = *reinterpret_cast<const uint32_t*>(&sm.Kh[nb][sw<DK>(t, pos)]);
-        } else {
-            gw[tt] = sm.G[nb][t * DK + i0];
-            kw[tt] = sm.Kh[nb][sw<DK>(t, pos)];
+        for (int tt = 0; tt < 8; ++tt) {
+            gsv[tt] = sm.gs[nb][8 * f + tt];
+            bhv[tt] = sm.bh[nb][8 * f + tt];
         }
-        // (diagonal variant: Kh already holds kappa'_t / g_t from the chain)
+    } else {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            gq[cc] = *reinterpret_cast<const u4*>(&sm.GQ[nb][(f * DK + i0 + cc) * 8]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                kq[cc][h] = *reinterpret_cast<const u2*>(&sm.KhQ[kslot][(((2 * f + h) & 3) * DK + i0 + cc) * 8 + hq]);
+        }
     }
-    uint32_t kw4[4];  // Kh^T staging: the bf16 pairs (DK = 128) or values of 4 tokens
+    uint32_t kw4[4];  // Kh^T staging (isotropic): the bf16 pairs (DK = 128) or values of 4 tokens
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
         const int t = 8 * f + tt;
@@ -571,14 +586,19 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
 #pragma unroll
             for (int c = 0; c < CPL; ++c) g[c] = gsv[tt];
             khw = CPL == 2 ? pack2(kk[0] * sc, kk[CPL - 1] * sc) : uint32_t(to_bf(kk[0] * sc));
-            if (CPL == 2) *reinterpret_cast<uint32_t*>(&sm.Kh[nb][off]) = khw;
-            else sm.Kh[nb][off] = bf16_t(khw);
         } else {
-            // Kh already holds kappa'_t / g_t, written by the chain
-            g[0] = bf_lo(gw[tt]);
-            if (CPL == 2) g[CPL - 1] = bf_hi(gw[tt]);
-            khw = kw[tt];
+            // kappa'_t / g_t and g_t from the chain's grouped stores
+            const int h = tt >> 2, u = tt & 3;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+                g[cc] = (tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1]);
+            if (CPL == 2)
+                khw = __builtin_amdgcn_perm(kq[1][h][u >> 1], kq[0][h][u >> 1], (u & 1) ? 0x07060302u : 0x05040100u);
+            else
+                khw = (u & 1) ? (kq[0][h][u >> 1] >> 16) : (kq[0][h][u >> 1] & 0xffffu);
         }
+        if (CPL == 2) *reinterpret_cast<uint32_t*>(&sm.Kh[off]) = khw;
+        else sm.Kh[off] = bf16_t(khw);
         if (CPL == 2) {
             *reinterpret_cast<uint32_t*>(&sm.Kn[nb][off]) = pack2(-kk[0] * g[0], -kk[CPL - 1] * g[CPL - 1]);
             *reinterpret_cast<uint32_t*>(&sm.Qt[nb][off]) = pack2(qq[0] * g[0], qq[CPL - 1] * g[CPL - 1]);
@@ -587,19 +607,21 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             sm.Qt[nb][off] = to_bf(qq[0] * g[0]);
         }
         kw4[tt & 3] = khw;
-        if ((tt & 3) == 3) {
-            // Kh^T rows i0 (and i0 + 1): 4 consecutive token positions each
-            const int tp = perm32(t - 3);
+        if (ISO && (tt & 3) == 3) {
+            // Kh^T rows i0 (and i0 + 1): the wave's 4 tokens 8f + 4h .. + 3
+            // are positions hq .. hq + 3 of group (2f + h) & 3 (the chain
+            // writes these in the diagonal variant)
+            const int q = ((2 * f + (tt >> 2)) & 3) * DK;
             if (CPL == 2) {
                 // byte selectors: low halves of two pairs, high halves of two pairs
                 const uint32_t lo01 = __builtin_amdgcn_perm(kw4[1], kw4[0], 0x05040100u);
                 const uint32_t lo23 = __builtin_amdgcn_perm(kw4[3], kw4[2], 0x05040100u);
                 const uint32_t hi01 = __builtin_amdgcn_perm(kw4[1], kw4[0], 0x07060302u);
                 const uint32_t hi23 = __builtin_amdgcn_perm(kw4[3], kw4[2], 0x07060302u);
-                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) = u2{lo01, lo23};
-                *reinterpret_cast<u2*>(&sm.KhT[nb][(i0 + 1) * PT + tp]) = u2{hi01, hi23};
+                *reinterpret_cast<u2*>(&sm.KhQ[kslot][(q + i0) * 8 + hq]) = u2{lo01, lo23};
+                *reinterpret_cast<u2*>(&sm.KhQ[kslot][(q + i0 + 1) * 8 + hq]) = u2{hi01, hi23};
             } else {
-                *reinterpret_cast<u2*>(&sm.KhT[nb][i0 * PT + tp]) =
+                *reinterpret_cast<u2*>(&sm.KhQ[kslot][(q + i0) * 8 + hq]) =
                     u2{(kw4[0] & 0xffffu) | (kw4[1] << 16), (kw4[2] & 0xffffu) | (kw4[3] << 16)};
             }
         }
@@ -689,7 +711,7 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             av[kk] = *reinterpret_cast<const b8*>(A + sw<DK>(ra + n, 32 * kk + kg8));
-            bv[kk] = *reinterpret_cast<const b8*>(sm.Kh[nb] + sw<DK>(rb + n, 32 * kk + kg8));
+            bv[kk] = *reinterpret_cast<const b8*>(sm.Kh + sw<DK>(rb + n, 32 * kk + kg8));
         }
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -844,7 +866,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     for (int at = 0; at < NT; ++at) aqk[at] = *reinterpret_cast<const b8*>(&sm.QK[b][(16 * at + n) * PT + kg8]);
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
-        akh[it] = *reinterpret_cast<const b8*>(&sm.KhT[b][(16 * it + n) * PT + kg8]);
+        akh[it] = *reinterpret_cast<const b8*>(&sm.KhQ[gring][((lane >> 4) * DK + 16 * it + n) * 8]);
         glv[it] = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
     }
     const b8* Db = st.Db;
@@ -1060,8 +1082,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
                 if (c >= 0 && c < nchunks) {
                     const int nvalid = min(L, a.T - c * L);
-                    if (nvalid == L) form_run<DK, ISO, false>(X, sm, c & 1, f, L);
-                    else form_run<DK, ISO, true>(X, sm, c & 1, f, nvalid);
+                    if (nvalid == L) form_run<DK, ISO, false>(X, sm, c & 1, c % 3, f, L);
+                    else form_run<DK, ISO, true>(X, sm, c & 1, c % 3, f, nvalid);
                 }
                 bar();
                 if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, c % 3, f);
