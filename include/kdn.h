@@ -111,6 +111,41 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
 /*
+ * kdn_forward_varlen -- kdn_forward over N sequences of different lengths
+ * packed along the token axis (a variable-length serving batch, e.g. the
+ * prompts of several requests).  Each sequence is run through the same
+ * recurrence from its own initial state, exactly as kdn_forward would run
+ * it alone (summary page, method steps 2-5; isotropic variant per its last
+ * sentence).  Sequence n owns the token rows [cu_seqlens[n],
+ * cu_seqlens[n + 1]) of the packed tensors:
+ *
+ *   q, k        [total,H,dk]   dtype
+ *   v           [total,H,dv]   dtype
+ *   alpha,omega [total,H,dk]   dtype (KDN_ISOTROPIC: [total,H])
+ *   r           [total,H]      dtype
+ *   cu_seqlens  [N+1]          int32, DEVICE pointer, read by the kernels:
+ *                              0 = cu[0] <= cu[1] <= ... <= cu[N] = total
+ *   c0          [H]            float (as kdn_forward)
+ *   S0          [N,H,dk,dv]    float or NULL;  p0 [N,H,dk] (KDN_ISOTROPIC: [N,H]) or NULL
+ *   o           [total,H,dv]   dtype, output
+ *   S_T         [N,H,dk,dv]    float, output;  p_T [N,H,dk] (KDN_ISOTROPIC: [N,H])
+ *   algo                       enum kdn_algo, as kdn_forward_algo
+ *
+ * The offsets live in device memory and are not inspected on the host.
+ * The kernels clamp every sequence into [0, total), so offsets that break
+ * the order above give meaningless values for the sequences involved, never
+ * an access outside the tensors.  An empty sequence (cu[n] = cu[n + 1])
+ * writes S_T = S_0 and p_T = p_0 for its heads.  Aliasing rules, dtypes and
+ * the remaining checks are those of kdn_forward (cu_seqlens counts as an
+ * input).
+ */
+int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* omega, const void* r, const int* cu_seqlens, const float* c0,
+                       float mu, int variant, int dtype, int N, int total, int H, int dk, int dv,
+                       const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                       void* stream, int algo);
+
+/*
  * kdn_step -- one decode step for N independent sequences: exactly one
  * token of the recurrence applied to the carried state (constant-memory
  * decoding; summary page, prerequisites on linear attention, and English
@@ -128,7 +163,7 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
              const void* r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
              float* S, float* p, void* o, void* stream);
 
-/* Host-only argument checks of kdn_forward / kdn_step: the same checks the
+/* Host-only argument checks of kdn_forward / kdn_step / kdn_forward_varlen: the same checks the
  * entry points run, with no device access and no launch.  Return a status. */
 int kdn_validate_forward(const void* q, const void* k, const void* v, const void* alpha,
                          const void* omega, const void* r, const float* c0, float mu,
@@ -138,6 +173,11 @@ int kdn_validate_forward(const void* q, const void* k, const void* v, const void
 int kdn_validate_step(const void* q, const void* k, const void* v, const void* alpha,
                       const void* omega, const void* r, float mu, int variant, int dtype, int N,
                       int H, int dk, int dv, float* S, float* p, void* o);
+int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                const void* omega, const void* r, const int* cu_seqlens,
+                                const float* c0, float mu, int variant, int dtype, int N, int total,
+                                int H, int dk, int dv, const float* S0, const float* p0, void* o,
+                                float* S_T, float* p_T, int algo);
 
 /* Static description of a status code (never NULL). */
 const char* kdn_status_string(int status);

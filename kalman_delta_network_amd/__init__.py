@@ -22,8 +22,9 @@ ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC}
 
 # exported symbols of include/kdn.h
-SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_step", "kdn_validate_forward",
-           "kdn_validate_step", "kdn_status_string", "kdn_last_error", "kdn_version")
+SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_step", "kdn_validate_forward",
+           "kdn_validate_forward_varlen", "kdn_validate_step", "kdn_status_string", "kdn_last_error",
+           "kdn_version")
 
 _lib = None
 
@@ -50,8 +51,12 @@ def load_library(path: str = LIB_PATH):
     step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
     lib.kdn_step.argtypes = step + [P]
     lib.kdn_validate_step.argtypes = step
+    varlen = [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
+    lib.kdn_forward_varlen.argtypes = varlen + [P, I]
+    lib.kdn_validate_forward_varlen.argtypes = varlen + [I]
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
-               lib.kdn_validate_step, lib.kdn_version):
+               lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
+               lib.kdn_version):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -142,6 +147,54 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
                               float(mu), var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
                               _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward")
+    return o, S_T, p_T
+
+
+def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagonal", S0=None, p0=None,
+                   algo="auto", out=None):
+    """KDN forward over N sequences packed along the token axis.
+
+    q, k [total,H,dk]; v [total,H,dv]; alpha, omega [total,H,dk] (isotropic
+    [total,H]); r [total,H] -- float32 or bfloat16.  cu_seqlens: int32 device
+    tensor [N+1] of token offsets (sequence n owns rows cu[n] .. cu[n+1]-1).
+    c0 [H]; S0 [N,H,dk,dv] / p0 [N,H,dk] (isotropic [N,H]) float32 or None.
+    Returns (o [total,H,dv], S_T [N,H,dk,dv], p_T); ``out`` may supply them.
+    """
+    torch = _torch()
+    lib = load_library()
+    var = VARIANTS[variant]
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens: expected a 1-D tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    gshape = (total, H, dk) if var == KDN_DIAGONAL else (total, H)
+    pshape = (N, H, dk) if var == KDN_DIAGONAL else (N, H)
+    for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
+                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (total, H))):
+        _need(t, name, shp, dt, dev)
+    if c0 is not None:
+        _need(c0, "c0", (H,), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if p0 is not None:
+        _need(p0, "p0", pshape, torch.float32, dev)
+    if out is None:
+        o = torch.empty((total, H, dv), dtype=dt, device=dev)
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        p_T = torch.empty(pshape, dtype=torch.float32, device=dev)
+    else:
+        o, S_T, p_T = out
+        _need(o, "o", (total, H, dv), dt, dev)
+        _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
+        _need(p_T, "p_T", pshape, torch.float32, dev)
+    st = lib.kdn_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r),
+                                _ptr(cu_seqlens), _ptr(c0), float(mu), var, _dtype_code(q), N, total, H,
+                                dk, dv, _ptr(S0), _ptr(p0), _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev),
+                                ALGOS[algo])
+    _check(st, "kdn_forward_varlen")
     return o, S_T, p_T
 
 

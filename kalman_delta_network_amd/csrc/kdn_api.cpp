@@ -65,19 +65,18 @@ int validate_common(int variant, int dtype, float mu, int dk, int dv) {
     return KDN_OK;
 }
 
-int validate_forward(const void* q, const void* k, const void* v, const void* alpha,
-                     const void* omega, const void* r, const float* c0, float mu, int variant,
-                     int dtype, int B, int T, int H, int dk, int dv, const float* S0,
-                     const float* p0, void* o, float* S_T, float* p_T, int algo) {
+// Checks shared by the [B,T,H] forward and the packed forward: `units`
+// (batch or sequence) x head pairs, `toks` token-head rows of the inputs,
+// `cu` the packed offsets (NULL for [B,T,H]; `ncu` entries).
+int validate_forward_core(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* omega, const void* r, const int* cu, int64_t ncu,
+                          const float* c0, float mu, int variant, int dtype, int64_t units,
+                          int64_t toks, int H, int dk, int dv, const float* S0, const float* p0,
+                          void* o, float* S_T, float* p_T, int algo) {
     int st = validate_common(variant, dtype, mu, dk, dv);
     if (st != KDN_OK) return st;
     if (algo != KDN_ALGO_AUTO && algo != KDN_ALGO_RECURRENT && algo != KDN_ALGO_CHUNKED)
         return fail(KDN_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
-    if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
-    const int64_t units = int64_t(B) * H;
-    const int64_t toks = units * T;
-    if (units > INT32_MAX || toks > kMaxElems / 128)
-        return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
     if (units == 0) return ok();  // nothing to read or write
     const bool iso = variant == KDN_ISOTROPIC;
     if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r || !o))
@@ -88,9 +87,10 @@ int validate_forward(const void* q, const void* k, const void* v, const void* al
     const size_t es = dtype == KDN_BF16 ? 2 : 4;
     const size_t nk = size_t(toks) * dk, nv = size_t(toks) * dv, ng = iso ? size_t(toks) : nk;
     const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * dk;
-    const Span in[] = {span(q, nk, es),      span(k, nk, es),       span(v, nv, es),
-                       span(alpha, ng, es),  span(omega, ng, es),   span(r, size_t(toks), es),
-                       span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4)};
+    const Span in[] = {span(q, nk, es),        span(k, nk, es),     span(v, nv, es),
+                       span(alpha, ng, es),    span(omega, ng, es), span(r, size_t(toks), es),
+                       span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4),
+                       span(cu, size_t(ncu), 4)};
     const Span so = span(o, nv, es), sS = span(S_T, ns, 4), sp = span(p_T, np, 4);
     for (const Span& x : in) {
         if (overlap(so, x) || overlap(sp, x)) return fail(KDN_ERR_ALIAS, "an output overlaps an input");
@@ -101,6 +101,35 @@ int validate_forward(const void* q, const void* k, const void* v, const void* al
     if (overlap(so, sS) || overlap(so, sp) || overlap(sS, sp))
         return fail(KDN_ERR_ALIAS, "outputs o, S_T, p_T overlap each other");
     return KDN_OK;
+}
+
+int validate_forward(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* omega, const void* r, const float* c0, float mu, int variant,
+                     int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                     const float* p0, void* o, float* S_T, float* p_T, int algo) {
+    if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
+    const int64_t units = int64_t(B) * H;
+    const int64_t toks = units * T;
+    if (units > INT32_MAX || toks > kMaxElems / 128)
+        return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
+    return validate_forward_core(q, k, v, alpha, omega, r, nullptr, 0, c0, mu, variant, dtype, units,
+                                 toks, H, dk, dv, S0, p0, o, S_T, p_T, algo);
+}
+
+int validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* omega, const void* r, const int* cu_seqlens,
+                            const float* c0, float mu, int variant, int dtype, int N, int total,
+                            int H, int dk, int dv, const float* S0, const float* p0, void* o,
+                            float* S_T, float* p_T, int algo) {
+    if (N < 0 || total < 0 || H < 0)
+        return fail(KDN_ERR_SHAPE, "negative size (N=%d, total=%d, H=%d)", N, total, H);
+    const int64_t units = int64_t(N) * H;
+    const int64_t toks = int64_t(total) * H;
+    if (units > INT32_MAX || toks > kMaxElems / 128)
+        return fail(KDN_ERR_SHAPE, "problem too large (N=%d, total=%d, H=%d)", N, total, H);
+    if (units > 0 && !cu_seqlens) return fail(KDN_ERR_NULL, "cu_seqlens must be non-NULL");
+    return validate_forward_core(q, k, v, alpha, omega, r, cu_seqlens, int64_t(N) + 1, c0, mu, variant,
+                                 dtype, units, toks, H, dk, dv, S0, p0, o, S_T, p_T, algo);
 }
 
 int validate_step(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
@@ -136,11 +165,24 @@ int hip_status(hipError_t e, const char* what) {
     return fail(KDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// launches a validated forward (a.cu_seqlens set for a packed batch)
+int run_forward(const kdn::FwdArgs& a, hipStream_t s, int algo) {
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    if (algo == KDN_ALGO_CHUNKED) {
+        if (!kdn::chunked_supports(a))
+            return fail(KDN_ERR_UNSUPPORTED, "the chunked algorithm does not support this shape");
+        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
+    }
+    if (algo == KDN_ALGO_AUTO && kdn::chunked_supports(a))
+        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
+    return hip_status(kdn::launch_recurrent(a, s), "recurrent forward");
+}
+
 }  // namespace
 
 extern "C" {
 
-int kdn_version(void) { return 100; }  // 0.1.0
+int kdn_version(void) { return 200; }  // 0.2.0: packed variable-length forward
 
 const char* kdn_status_string(int status) {
     switch (status) {
@@ -181,18 +223,35 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
                                     dv, S0, p0, o, S_T, p_T, algo);
     if (st != KDN_OK) return st;
     if (int64_t(B) * H == 0) return ok();
-    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
-    kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv,
+    const kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv,
+                         S0, p0, o, S_T, p_T};
+    return run_forward(a, static_cast<hipStream_t>(stream), algo);
+}
+
+int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                const void* omega, const void* r, const int* cu_seqlens,
+                                const float* c0, float mu, int variant, int dtype, int N, int total,
+                                int H, int dk, int dv, const float* S0, const float* p0, void* o,
+                                float* S_T, float* p_T, int algo) {
+    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, c0, mu, variant, dtype,
+                                           N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
+    return st == KDN_OK ? ok() : st;
+}
+
+int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* omega, const void* r, const int* cu_seqlens, const float* c0,
+                       float mu, int variant, int dtype, int N, int total, int H, int dk, int dv,
+                       const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                       void* stream, int algo) {
+    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, c0, mu, variant, dtype,
+                                           N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
+    if (st != KDN_OK) return st;
+    if (int64_t(N) * H == 0) return ok();
+    // N sequences over a [total, H] token grid: B = N, T = total, offsets on the device
+    kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, N, total, H, dk, dv,
                    S0, p0, o, S_T, p_T};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (algo == KDN_ALGO_CHUNKED) {
-        if (!kdn::chunked_supports(a))
-            return fail(KDN_ERR_UNSUPPORTED, "the chunked algorithm does not support this shape");
-        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
-    }
-    if (algo == KDN_ALGO_AUTO && kdn::chunked_supports(a))
-        return hip_status(kdn::launch_chunked(a, s), "chunked forward");
-    return hip_status(kdn::launch_recurrent(a, s), "recurrent forward");
+    a.cu_seqlens = cu_seqlens;
+    return run_forward(a, static_cast<hipStream_t>(stream), algo);
 }
 
 int kdn_forward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,

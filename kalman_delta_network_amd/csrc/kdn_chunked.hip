@@ -194,11 +194,14 @@ struct Args {
     bf16_t* o;
     float* S_T;
     float* p_T;
+    const int* cu;  // packed sequences: sequence n owns tokens [cu[n], cu[n + 1]); NULL: B x T
+    size_t tok0;    // set per workgroup: the first token of its sequence in the token grid
 };
 
-// position of token t of the sequence of (b, h) in the [B,T,H] token grid
-__device__ __forceinline__ size_t tokidx(const Args& a, size_t b, int h, int t) {
-    return (b * size_t(a.T) + size_t(t)) * size_t(a.H) + size_t(h);
+// position of token t of the workgroup's sequence (of head h) in the token
+// grid [tokens, H] (the sequence's tokens are consecutive rows of it)
+__device__ __forceinline__ size_t tokidx(const Args& a, size_t, int h, int t) {
+    return (a.tok0 + size_t(t)) * size_t(a.H) + size_t(h);
 }
 
 constexpr uint32_t BF_ONE = 0x3f80u;  // bf16 1.0
@@ -935,6 +938,32 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int unit = int(b) * a.H + h;  // (batch, head) index of the [B, H, ...] states
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
+    // this item's sequence: a.T tokens from grid row a.tok0 on.  Packed
+    // sequences take their bounds from the offsets, clamped into the grid
+    // (a.T is then the grid's token count), so no offset can reach outside it.
+    if (a.cu) {
+        const int total = a.T;
+        const int s0 = min(max(a.cu[b], 0), total);
+        const int s1 = min(max(a.cu[b + 1], s0), total);
+        a.tok0 = size_t(s0);
+        a.T = s1 - s0;
+    } else {
+        a.tok0 = b * size_t(a.T);
+    }
+    if (a.T == 0) {
+        // an empty sequence: the final state is the initial one
+        const size_t sb = size_t(unit) * DK * a.DV;
+        for (int e = threadIdx.x; e < DK * DVT; e += NTHREADS) {
+            const size_t x = sb + size_t(e / DVT) * a.DV + tile * DVT + e % DVT;
+            a.S_T[x] = a.S0 ? a.S0[x] : 0.f;
+        }
+        if (tile == 0) {
+            const int np = ISO ? 1 : DK;
+            for (int i = threadIdx.x; i < np; i += NTHREADS)
+                a.p_T[size_t(unit) * np + i] = a.p0 ? a.p0[size_t(unit) * np + i] : a.c0[h];
+        }
+        return;
+    }
     const int nchunks = (a.T + L - 1) / L;
     const int nit = ((nchunks + 2) + 1) & ~1;  // even number of pipeline iterations
 
@@ -1129,6 +1158,8 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     a.o = static_cast<bf16_t*>(f.o);
     a.S_T = f.S_T;
     a.p_T = f.p_T;
+    a.cu = f.cu_seqlens;
+    a.tok0 = 0;
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);

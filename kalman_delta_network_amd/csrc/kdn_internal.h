@@ -27,6 +27,10 @@ struct FwdArgs {
     void* o;
     float* S_T;
     float* p_T;
+    // packed variable-length batch: NULL for a [B,T,H] batch; otherwise B
+    // sequences, sequence b owning tokens [cu_seqlens[b], cu_seqlens[b + 1])
+    // of a [T,H] token grid (device pointer, B + 1 entries)
+    const int* cu_seqlens = nullptr;
 };
 
 // Token-by-token recurrence; one workgroup per (b, h) covering all d_v

@@ -19,6 +19,9 @@
 //   delta = v - S_hat^T k, readout o = S_hat^T q + (kappa^T q) delta (the
 //   post-write readout expanded), and the write S = S_hat + kappa delta^T.
 //
+// Packed variable-length batches: unit b * H + h runs sequence b, whose
+// tokens are rows [cu[b], cu[b + 1]) of the [T, H] token grid.
+//
 // The decode step is this kernel with T = 1 and the state updated in place:
 // a barrier after the initial state loads makes every wave read p before any
 // wave writes it back.
@@ -67,7 +70,8 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const Tin* __restrict__ v, const Tin* __restrict__ alpha,
                      const Tin* __restrict__ omega, const Tin* __restrict__ r,
                      const float* __restrict__ c0, float mu, int T, int H, const float* S0,
-                     const float* p0, Tin* __restrict__ o, float* S_T, float* p_T) {
+                     const float* p0, Tin* __restrict__ o, float* S_T, float* p_T,
+                     const int* __restrict__ cu) {
     constexpr int NW = DV / 32;   // waves per workgroup
     constexpr int CPL = DK / 64;  // channels per lane
     constexpr int RPT = DK / 8;   // memory rows per thread
@@ -83,6 +87,16 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     const int cq = lane & 7;
     const int rg = lane >> 3;
     const int col = wave * 32 + cq * 4;
+    // this unit's sequence: len tokens from token-grid row tok0 on (packed
+    // sequences: bounds from the offsets, clamped into the grid of T rows)
+    size_t tok0 = b * size_t(T);
+    int len = T;
+    if (cu) {
+        const int s0 = min(max(cu[b], 0), T);
+        const int s1 = min(max(cu[b + 1], s0), T);
+        tok0 = size_t(s0);
+        len = s1 - s0;
+    }
 
     const size_t sbase = size_t(unit) * DK * DV;
     float S[RPT][4];
@@ -107,8 +121,8 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     __syncthreads();  // all initial reads happen before any in-place write
 
     const float inv_dk = 1.0f / float(DK);
-    for (int t = 0; t < T; ++t) {
-        const size_t tok = (b * size_t(T) + size_t(t)) * size_t(H) + size_t(h);
+    for (int t = 0; t < len; ++t) {
+        const size_t tok = (tok0 + size_t(t)) * size_t(H) + size_t(h);
         const float rt = to_f32(r[tok]);
         float kk[CPL], qq[CPL], aa[CPL], kap[CPL];
         float mq;  // kappa^T q
@@ -221,7 +235,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
                        static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                        static_cast<const Tin*>(a.alpha), static_cast<const Tin*>(a.omega),
                        static_cast<const Tin*>(a.r), a.c0, a.mu, a.T, a.H, a.S0, a.p0,
-                       static_cast<Tin*>(a.o), a.S_T, a.p_T);
+                       static_cast<Tin*>(a.o), a.S_T, a.p_T, a.cu_seqlens);
     return hipGetLastError();
 }
 

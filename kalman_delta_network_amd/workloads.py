@@ -14,7 +14,10 @@ standard deviation s):
 * omega = softplus(N(omega_loc, 1)) with the same shape as alpha;
 * r = 0.01 + softplus(N(0, 1)) per head-token (the pages' r_min = 0.01);
 * c0 = 1.0 per head, or U(0.5, 2) per head;
-* decode state: S0 ~ N(0, 0.1), p0 ~ U(0.1, 1) (isotropic: one p0 per head).
+* decode state: S0 ~ N(0, 0.1), p0 ~ U(0.1, 1) (isotropic: one p0 per head);
+* packed variable-length batches: sequence lengths ~ U{lo, hi} (integers,
+  both ends included), then the tokens of all sequences drawn as one
+  [total, H] grid in the order above, then c0.
 
 For bf16 workloads every tensor above except c0, S0 and p0 is then rounded
 to bf16 (round to nearest, ties to even) and returned as float32 arrays that
@@ -127,6 +130,32 @@ def forward_inputs(w: Workload) -> dict:
     hold the exact values of ``w.dtype``) and c0 [H] float32."""
     rng = np.random.default_rng(w.seed)
     out = _draw_tokens(rng, w, (w.B, w.T, w.H))
+    out["c0"] = _draw_c0(rng, w)
+    return out
+
+
+# packed variable-length serving batch: 32 sequences of 256..1792 tokens
+# (about 32k tokens in all, the token count of the main forward workload)
+VARLEN = Workload("varlen_diag_bf16_n32_h16_d128", "diagonal", "bf16", 32, 0, 16, 128, 128, 128.0,
+                  "uniform", 1005)
+VARLEN_RANGE = (256, 1792)
+
+
+def varlen_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
+    """n sequence lengths drawn uniformly from lo..hi (inclusive), int64."""
+    return np.random.default_rng([seed, 0x5E]).integers(lo, hi + 1, size=n)
+
+
+def varlen_inputs(w: Workload, lengths) -> dict:
+    """Inputs of one packed forward over len(lengths) sequences: q,k,v,alpha,
+    omega,r with leading shape [total, H] (rows of sequence n are
+    cu_seqlens[n] .. cu_seqlens[n+1]-1), cu_seqlens int32 [N+1], c0 [H]."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    rng = np.random.default_rng(w.seed)
+    out = _draw_tokens(rng, w, (int(cu[-1]), w.H))
+    out["cu_seqlens"] = cu
     out["c0"] = _draw_c0(rng, w)
     return out
 

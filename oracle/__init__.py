@@ -10,6 +10,8 @@ it.
   Uncertainty-aware Associative Memory", summary page, section on the
   method steps, steps 2-5, and its closing sentence for the isotropic
   variant).
+* ``forward_varlen`` runs packed variable-length batches through the same
+  recurrence, one sequence at a time.
 * ``dense`` holds the brute-force dense-covariance filter (Bayesian Layer
   page, section 2.2, Proposition 1) used to pin the oracle.
 
@@ -118,6 +120,33 @@ def forward_diag(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False
 def forward_iso(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
     """Isotropic KDN forward.  alpha, omega, r [B,T,H]; p0 / returned p [B,H]."""
     return _forward("kdn_oracle_forward_iso", q, k, v, alpha, omega, r, c0, mu, S0, p0, trace)
+
+
+def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagonal", S0=None, p0=None):
+    """Packed variable-length forward: sequence n is the token rows
+    cu_seqlens[n] .. cu_seqlens[n+1]-1 of the [total,H,*] inputs, run from its
+    own initial state (S0[n], p0[n]; zero memory and c0 when absent) by
+    forward_diag / forward_iso.  The recurrence is per sequence; packing only
+    decides which rows belong to which sequence.
+    Returns o [total,H,dv], S [N,H,dk,dv], p [N,H,dk] (isotropic [N,H])."""
+    fn = forward_diag if variant == "diagonal" else forward_iso
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or len(cu) < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != len(q):
+        raise ValueError("cu_seqlens must rise from 0 to the number of token rows")
+    N = len(cu) - 1
+    total, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    o = np.zeros((total, H, dv))
+    S = np.zeros((N, H, dk, dv))
+    p = np.zeros((N, H, dk) if variant == "diagonal" else (N, H))
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        out = fn(*(np.asarray(x)[None, a:b] for x in (q, k, v, alpha, omega, r)), c0, mu,
+                 None if S0 is None else np.asarray(S0)[n:n + 1], None if p0 is None else np.asarray(p0)[n:n + 1])
+        o[a:b] = out["o"][0]
+        S[n] = out["S"][0]
+        p[n] = out["p"][0]
+    return {"o": o, "S": S, "p": p}
 
 
 def _step(name, q, k, v, alpha, omega, r, mu, S, p):

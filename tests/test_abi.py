@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(kdn.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kdn_version() == 100
+    assert lib.kdn_version() == 200
 
 
 def test_status_strings(lib):
@@ -182,6 +182,71 @@ def test_launch_error_path_without_gpu(lib, monkeypatch):
                          a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["S0"],
                          a["p0"], a["o"], a["S_T"], a["p_T"], None)
     assert st == kdn.KDN_ERR_VALUE
+
+
+def varlen_args(fake, N=3, total=40, H=2, dk=64, dv=64, variant=0, dtype=1, mu=64.0, algo=0, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), cu=fake(), c0=fake(),
+             mu=mu, variant=variant, dtype=dtype, N=N, total=total, H=H, dk=dk, dv=dv, S0=None, p0=None,
+             o=fake(), S_T=fake(), p_T=fake(), algo=algo)
+    a.update(over)
+    return a
+
+
+def call_validate_varlen(lib, a):
+    return lib.kdn_validate_forward_varlen(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["cu"],
+                                           a["c0"], a["mu"], a["variant"], a["dtype"], a["N"], a["total"],
+                                           a["H"], a["dk"], a["dv"], a["S0"], a["p0"], a["o"], a["S_T"],
+                                           a["p_T"], a["algo"])
+
+
+def test_validate_varlen_accepts_good_arguments(lib):
+    f = Fake()
+    for variant in (0, 1):
+        for dtype in (0, 1):
+            assert call_validate_varlen(lib, varlen_args(f, variant=variant, dtype=dtype)) == 0
+    assert call_validate_varlen(lib, varlen_args(f, N=0, cu=None, q=None, S_T=None)) == 0  # no sequence
+    # every sequence empty: no token input is read, the states are still written
+    assert call_validate_varlen(lib, varlen_args(f, total=0, q=None, k=None, v=None, o=None)) == 0
+    assert call_validate_varlen(lib, varlen_args(f, c0=None, p0=f())) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cu=None), kdn.KDN_ERR_NULL),
+    (dict(q=None), kdn.KDN_ERR_NULL),
+    (dict(S_T=None), kdn.KDN_ERR_NULL),
+    (dict(c0=None), kdn.KDN_ERR_NULL),
+    (dict(N=-1), kdn.KDN_ERR_SHAPE),
+    (dict(total=-5), kdn.KDN_ERR_SHAPE),
+    (dict(H=-2), kdn.KDN_ERR_SHAPE),
+    (dict(total=1 << 30, H=1 << 12), kdn.KDN_ERR_SHAPE),
+    (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(algo=7), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
+])
+def test_validate_varlen_rejects(lib, over, status):
+    f = Fake()
+    assert call_validate_varlen(lib, varlen_args(f, **over)) == status
+    assert lib.kdn_last_error()
+
+
+def test_validate_varlen_aliasing(lib):
+    f = Fake()
+    a = varlen_args(f)
+    assert call_validate_varlen(lib, dict(a, o=a["cu"])) == kdn.KDN_ERR_ALIAS  # the offsets are an input
+    assert call_validate_varlen(lib, dict(a, p_T=a["cu"])) == kdn.KDN_ERR_ALIAS
+    s = f()
+    assert call_validate_varlen(lib, dict(a, S0=s, S_T=s)) == 0
+
+
+def test_varlen_launch_error_path_without_gpu(lib, monkeypatch):
+    monkeypatch.setenv("KDN_FAULT", "launch")
+    f = Fake()
+    a = varlen_args(f)
+    args = [a[x] for x in ("q", "k", "v", "alpha", "omega", "r", "cu", "c0", "mu", "variant", "dtype", "N",
+                           "total", "H", "dk", "dv", "S0", "p0", "o", "S_T", "p_T")]
+    assert lib.kdn_forward_varlen(*args, None, 0) == kdn.KDN_ERR_HIP
+    args[6] = None  # no offsets: reported before the launch stage
+    assert lib.kdn_forward_varlen(*args, None, 0) == kdn.KDN_ERR_NULL
 
 
 def test_binding_raises_when_library_missing(tmp_path):

@@ -387,6 +387,76 @@ def test_oracle_step_and_split_continuation_match_forward(variant):
     np.testing.assert_allclose(S, ref["S"], rtol=1e-13, atol=1e-15)
 
 
+# --------------------------------------------------------------------------
+# Packed variable-length batches: bookkeeping around the pinned recurrence
+# --------------------------------------------------------------------------
+
+def _varlen_case(variant, lengths, seed=11, with_state=True):
+    w = wl.Workload("t", variant, "f32", len(lengths), 0, 3, 8, 5, 8.0, "uniform", seed)
+    x = wl.varlen_inputs(w, lengths)
+    N = len(lengths)
+    rng = np.random.default_rng(seed + 1)
+    S0 = rng.standard_normal((N, 3, 8, 5)) * 0.1 if with_state else None
+    p0 = rng.uniform(0.1, 1.0, (N, 3, 8) if variant == "diagonal" else (N, 3)) if with_state else None
+    return w, x, S0, p0
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_varlen_equal_lengths_is_the_batched_forward(variant):
+    # B sequences of one length packed along the tokens == the [B,T,H] forward
+    B, T = 3, 13
+    w, x, S0, p0 = _varlen_case(variant, [T] * B)
+    fwd = oracle.forward_iso if variant == "isotropic" else oracle.forward_diag
+    tok = {k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r")}
+    ref = fwd(**{k: v.reshape((B, T) + v.shape[1:]) for k, v in tok.items()}, c0=x["c0"], mu=w.mu,
+              S0=S0, p0=p0)
+    got = oracle.forward_varlen(**tok, c0=x["c0"], mu=w.mu, cu_seqlens=x["cu_seqlens"], variant=variant,
+                                S0=S0, p0=p0)
+    np.testing.assert_array_equal(got["o"], ref["o"].reshape(got["o"].shape))
+    np.testing.assert_array_equal(got["S"], ref["S"])
+    np.testing.assert_array_equal(got["p"], ref["p"])
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_varlen_permuting_sequences_permutes_results(variant):
+    lengths = [5, 0, 17, 1, 9]
+    w, x, S0, p0 = _varlen_case(variant, lengths)
+    tok = {k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r")}
+    cu = x["cu_seqlens"]
+    ref = oracle.forward_varlen(**tok, c0=x["c0"], mu=w.mu, cu_seqlens=cu, variant=variant, S0=S0, p0=p0)
+    perm = [2, 4, 0, 3, 1]
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in perm]).astype(np.int64)
+    cu2 = np.concatenate([[0], np.cumsum([lengths[n] for n in perm])])
+    got = oracle.forward_varlen(**{k: v[rows] for k, v in tok.items()}, c0=x["c0"], mu=w.mu, cu_seqlens=cu2,
+                                variant=variant, S0=S0[perm], p0=p0[perm])
+    np.testing.assert_array_equal(got["o"], ref["o"][rows])
+    np.testing.assert_array_equal(got["S"], ref["S"][perm])
+    np.testing.assert_array_equal(got["p"], ref["p"][perm])
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_varlen_empty_sequence_keeps_its_initial_state(variant):
+    w, x, S0, p0 = _varlen_case(variant, [4, 0, 3])
+    tok = {k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r")}
+    got = oracle.forward_varlen(**tok, c0=x["c0"], mu=w.mu, cu_seqlens=x["cu_seqlens"], variant=variant,
+                                S0=S0, p0=p0)
+    np.testing.assert_array_equal(got["S"][1], S0[1])
+    np.testing.assert_array_equal(got["p"][1], p0[1])
+    bare = oracle.forward_varlen(**tok, c0=x["c0"], mu=w.mu, cu_seqlens=x["cu_seqlens"], variant=variant)
+    assert not bare["S"][1].any()
+    np.testing.assert_array_equal(bare["p"][1], np.broadcast_to(
+        x["c0"].astype(np.float64)[:, None] if variant == "diagonal" else x["c0"].astype(np.float64),
+        bare["p"][1].shape))
+
+
+def test_varlen_rejects_offsets_that_do_not_cover_the_rows():
+    w, x, S0, p0 = _varlen_case("diagonal", [3, 4])
+    tok = {k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r")}
+    for bad in ([0, 3, 6], [1, 3, 7], [0, 5, 4, 7]):
+        with pytest.raises(ValueError):
+            oracle.forward_varlen(**tok, c0=x["c0"], mu=w.mu, cu_seqlens=bad)
+
+
 def test_bf16_rounding_matches_torch():
     import torch
     x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
