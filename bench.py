@@ -42,6 +42,16 @@ def forward_bytes(w) -> int:
     return toks * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4
 
 
+def varlen_bytes(w, total: int) -> int:
+    """Algorithmic HBM bytes of one packed forward over w.B sequences holding
+    `total` tokens in all: as forward_bytes, plus the N+1 offsets."""
+    es = 2 if w.dtype == "bf16" else 4
+    gate = w.dk if w.variant == "diagonal" else 1
+    per_tok = es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv
+    pdim = w.dk if w.variant == "diagonal" else 1
+    return total * w.H * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4 + (w.B + 1) * 4
+
+
 def step_bytes(w) -> int:
     """Algorithmic HBM bytes of one decode step: state read and written once,
     one token of inputs read, o written."""
@@ -144,6 +154,38 @@ def bench_decode(kdn, w, dev, steps_cap=None):
             "hbm_frac": step_bytes(w) / (ms / nsteps / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_varlen(kdn, dev, steps, algo):
+    """Time the packed serving batch: 32 sequences of 256..1792 tokens (16
+    heads, d = 128, diagonal bf16) in one kdn_forward_varlen call, scheduled
+    longest first."""
+    import torch
+    from kalman_delta_network_amd import workloads as wl
+    w = wl.VARLEN
+    lengths = wl.varlen_lengths(w.seed, w.B, *wl.VARLEN_RANGE)
+    x = wl.varlen_inputs(w, lengths)
+    t = upload(x, w.dtype, dev)
+    cu = torch.from_numpy(x["cu_seqlens"]).to(dev)
+    order = torch.from_numpy(kdn.longest_first(x["cu_seqlens"])).to(dev)  # schedule the longest first
+    total = int(x["cu_seqlens"][-1])
+    out = (torch.empty((total, w.H, w.dv), dtype=t["q"].dtype, device=dev),
+           torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev),
+           torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=dev))
+    call = lambda: kdn.forward_varlen(**t, cu_seqlens=cu, mu=w.mu, variant=w.variant, algo=algo, out=out,
+                                      order=order)
+    warm(call, 2)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = varlen_bytes(w, total)
+    return {"workload": w.name, "sequences": w.B, "tokens": total,
+            "lengths": [int(lengths.min()), int(lengths.max())], "ms_per_step": ms,
+            "tokens_per_s": total / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
 COPY_BYTES = 512 << 20  # calibration copy for the HBM byte counters
 
 
@@ -226,7 +268,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the isotropic and decode lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the isotropic, decode and packed-batch lines")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the workload of the rocprofv3 counter runs and exit")
@@ -276,6 +318,7 @@ def main():
         del ti
         extra["decode"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
                                        args.decode_steps)
+        extra["varlen"] = bench_varlen(kdn, dev, max(3, args.steps // 2), args.algo)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x)

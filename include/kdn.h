@@ -125,22 +125,29 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
  *   r           [total,H]      dtype
  *   cu_seqlens  [N+1]          int32, DEVICE pointer, read by the kernels:
  *                              0 = cu[0] <= cu[1] <= ... <= cu[N] = total
+ *   order       [N]            int32, DEVICE pointer or NULL: the order in which
+ *                              the sequences are scheduled, a permutation of
+ *                              0..N-1 (NULL = 0..N-1).  Longest first spreads
+ *                              the work evenly over the GPU; results do not
+ *                              depend on it.
  *   c0          [H]            float (as kdn_forward)
  *   S0          [N,H,dk,dv]    float or NULL;  p0 [N,H,dk] (KDN_ISOTROPIC: [N,H]) or NULL
  *   o           [total,H,dv]   dtype, output
  *   S_T         [N,H,dk,dv]    float, output;  p_T [N,H,dk] (KDN_ISOTROPIC: [N,H])
  *   algo                       enum kdn_algo, as kdn_forward_algo
  *
- * The offsets live in device memory and are not inspected on the host.
- * The kernels clamp every sequence into [0, total), so offsets that break
- * the order above give meaningless values for the sequences involved, never
- * an access outside the tensors.  An empty sequence (cu[n] = cu[n + 1])
+ * The offsets and the order live in device memory and are not inspected on
+ * the host.  The kernels clamp every sequence into [0, total) and every order
+ * entry into [0, N), so offsets that break the rule above, or an order that
+ * is not a permutation, give meaningless values for the sequences involved,
+ * never an access outside the tensors.  An empty sequence (cu[n] = cu[n + 1])
  * writes S_T = S_0 and p_T = p_0 for its heads.  Aliasing rules, dtypes and
  * the remaining checks are those of kdn_forward (cu_seqlens counts as an
  * input).
  */
 int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
-                       const void* omega, const void* r, const int* cu_seqlens, const float* c0,
+                       const void* omega, const void* r, const int* cu_seqlens, const int* order,
+                       const float* c0,
                        float mu, int variant, int dtype, int N, int total, int H, int dk, int dv,
                        const float* S0, const float* p0, void* o, float* S_T, float* p_T,
                        void* stream, int algo);
@@ -175,7 +182,7 @@ int kdn_validate_step(const void* q, const void* k, const void* v, const void* a
                       int H, int dk, int dv, float* S, float* p, void* o);
 int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
                                 const void* omega, const void* r, const int* cu_seqlens,
-                                const float* c0, float mu, int variant, int dtype, int N, int total,
+                                const int* order, const float* c0, float mu, int variant, int dtype, int N, int total,
                                 int H, int dk, int dv, const float* S0, const float* p0, void* o,
                                 float* S_T, float* p_T, int algo);
 

@@ -51,7 +51,7 @@ def load_library(path: str = LIB_PATH):
     step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
     lib.kdn_step.argtypes = step + [P]
     lib.kdn_validate_step.argtypes = step
-    varlen = [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
+    varlen = [P, P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
     lib.kdn_forward_varlen.argtypes = varlen + [P, I]
     lib.kdn_validate_forward_varlen.argtypes = varlen + [I]
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
@@ -150,14 +150,25 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
     return o, S_T, p_T
 
 
+def longest_first(cu_seqlens):
+    """Scheduling order for forward_varlen from host-side offsets (a list,
+    numpy array or CPU tensor of N+1 ints): sequence indices by decreasing
+    length, ties in index order, as an int32 numpy array."""
+    import numpy as np
+    cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+    return np.argsort(-(cu[1:] - cu[:-1]), kind="stable").astype(np.int32)
+
+
 def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagonal", S0=None, p0=None,
-                   algo="auto", out=None):
+                   algo="auto", out=None, order=None):
     """KDN forward over N sequences packed along the token axis.
 
     q, k [total,H,dk]; v [total,H,dv]; alpha, omega [total,H,dk] (isotropic
     [total,H]); r [total,H] -- float32 or bfloat16.  cu_seqlens: int32 device
     tensor [N+1] of token offsets (sequence n owns rows cu[n] .. cu[n+1]-1).
     c0 [H]; S0 [N,H,dk,dv] / p0 [N,H,dk] (isotropic [N,H]) float32 or None.
+    order: int32 device tensor [N], the scheduling order (a permutation;
+    ``longest_first`` of the host offsets balances the GPU), or None.
     Returns (o [total,H,dv], S_T [N,H,dk,dv], p_T); ``out`` may supply them.
     """
     torch = _torch()
@@ -175,6 +186,8 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagon
     for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
                          ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (total, H))):
         _need(t, name, shp, dt, dev)
+    if order is not None:
+        _need(order, "order", (N,), torch.int32, dev)
     if c0 is not None:
         _need(c0, "c0", (H,), torch.float32, dev)
     if S0 is not None:
@@ -191,7 +204,7 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagon
         _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
         _need(p_T, "p_T", pshape, torch.float32, dev)
     st = lib.kdn_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r),
-                                _ptr(cu_seqlens), _ptr(c0), float(mu), var, _dtype_code(q), N, total, H,
+                                _ptr(cu_seqlens), _ptr(order), _ptr(c0), float(mu), var, _dtype_code(q), N, total, H,
                                 dk, dv, _ptr(S0), _ptr(p0), _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev),
                                 ALGOS[algo])
     _check(st, "kdn_forward_varlen")

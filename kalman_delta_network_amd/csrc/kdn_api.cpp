@@ -69,7 +69,7 @@ int validate_common(int variant, int dtype, float mu, int dk, int dv) {
 // (batch or sequence) x head pairs, `toks` token-head rows of the inputs,
 // `cu` the packed offsets (NULL for [B,T,H]; `ncu` entries).
 int validate_forward_core(const void* q, const void* k, const void* v, const void* alpha,
-                          const void* omega, const void* r, const int* cu, int64_t ncu,
+                          const void* omega, const void* r, const int* cu, int64_t ncu, const int* ord,
                           const float* c0, float mu, int variant, int dtype, int64_t units,
                           int64_t toks, int H, int dk, int dv, const float* S0, const float* p0,
                           void* o, float* S_T, float* p_T, int algo) {
@@ -90,7 +90,7 @@ int validate_forward_core(const void* q, const void* k, const void* v, const voi
     const Span in[] = {span(q, nk, es),        span(k, nk, es),     span(v, nv, es),
                        span(alpha, ng, es),    span(omega, ng, es), span(r, size_t(toks), es),
                        span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4),
-                       span(cu, size_t(ncu), 4)};
+                       span(cu, size_t(ncu), 4),   span(ord, size_t(ncu > 0 ? ncu - 1 : 0), 4)};
     const Span so = span(o, nv, es), sS = span(S_T, ns, 4), sp = span(p_T, np, 4);
     for (const Span& x : in) {
         if (overlap(so, x) || overlap(sp, x)) return fail(KDN_ERR_ALIAS, "an output overlaps an input");
@@ -112,12 +112,12 @@ int validate_forward(const void* q, const void* k, const void* v, const void* al
     const int64_t toks = units * T;
     if (units > INT32_MAX || toks > kMaxElems / 128)
         return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
-    return validate_forward_core(q, k, v, alpha, omega, r, nullptr, 0, c0, mu, variant, dtype, units,
+    return validate_forward_core(q, k, v, alpha, omega, r, nullptr, 0, nullptr, c0, mu, variant, dtype, units,
                                  toks, H, dk, dv, S0, p0, o, S_T, p_T, algo);
 }
 
 int validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
-                            const void* omega, const void* r, const int* cu_seqlens,
+                            const void* omega, const void* r, const int* cu_seqlens, const int* order,
                             const float* c0, float mu, int variant, int dtype, int N, int total,
                             int H, int dk, int dv, const float* S0, const float* p0, void* o,
                             float* S_T, float* p_T, int algo) {
@@ -128,7 +128,7 @@ int validate_forward_varlen(const void* q, const void* k, const void* v, const v
     if (units > INT32_MAX || toks > kMaxElems / 128)
         return fail(KDN_ERR_SHAPE, "problem too large (N=%d, total=%d, H=%d)", N, total, H);
     if (units > 0 && !cu_seqlens) return fail(KDN_ERR_NULL, "cu_seqlens must be non-NULL");
-    return validate_forward_core(q, k, v, alpha, omega, r, cu_seqlens, int64_t(N) + 1, c0, mu, variant,
+    return validate_forward_core(q, k, v, alpha, omega, r, cu_seqlens, int64_t(N) + 1, order, c0, mu, variant,
                                  dtype, units, toks, H, dk, dv, S0, p0, o, S_T, p_T, algo);
 }
 
@@ -230,20 +230,21 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
 
 int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
                                 const void* omega, const void* r, const int* cu_seqlens,
-                                const float* c0, float mu, int variant, int dtype, int N, int total,
+                                const int* order, const float* c0, float mu, int variant, int dtype, int N, int total,
                                 int H, int dk, int dv, const float* S0, const float* p0, void* o,
                                 float* S_T, float* p_T, int algo) {
-    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, c0, mu, variant, dtype,
+    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, order, c0, mu, variant, dtype,
                                            N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
     return st == KDN_OK ? ok() : st;
 }
 
 int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* alpha,
-                       const void* omega, const void* r, const int* cu_seqlens, const float* c0,
+                       const void* omega, const void* r, const int* cu_seqlens, const int* order,
+                       const float* c0,
                        float mu, int variant, int dtype, int N, int total, int H, int dk, int dv,
                        const float* S0, const float* p0, void* o, float* S_T, float* p_T,
                        void* stream, int algo) {
-    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, c0, mu, variant, dtype,
+    const int st = validate_forward_varlen(q, k, v, alpha, omega, r, cu_seqlens, order, c0, mu, variant, dtype,
                                            N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
     if (st != KDN_OK) return st;
     if (int64_t(N) * H == 0) return ok();
@@ -251,6 +252,7 @@ int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* 
     kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, N, total, H, dk, dv,
                    S0, p0, o, S_T, p_T};
     a.cu_seqlens = cu_seqlens;
+    a.seq_order = order;
     return run_forward(a, static_cast<hipStream_t>(stream), algo);
 }
 

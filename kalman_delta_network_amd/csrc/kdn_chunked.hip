@@ -194,7 +194,8 @@ struct Args {
     bf16_t* o;
     float* S_T;
     float* p_T;
-    const int* cu;  // packed sequences: sequence n owns tokens [cu[n], cu[n + 1]); NULL: B x T
+    const int* cu;   // packed sequences: sequence n owns tokens [cu[n], cu[n + 1]); NULL: B x T
+    const int* ord;  // packed sequences: scheduling order of the sequences, or NULL
     size_t tok0;    // set per workgroup: the first token of its sequence in the token grid
 };
 
@@ -933,15 +934,21 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const int tile = (bid / 8) % ntile;
     if (item >= a.units) return;
     const int nbatch = a.units / a.H;
-    const int h = item / nbatch;
-    const size_t b = size_t(item % nbatch);
-    const int unit = int(b) * a.H + h;  // (batch, head) index of the [B, H, ...] states
+    int h = item / nbatch;  // [B,T,H] batch: items batch-fastest (above)
+    size_t b = size_t(item % nbatch);
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
     // this item's sequence: a.T tokens from grid row a.tok0 on.  Packed
-    // sequences take their bounds from the offsets, clamped into the grid
-    // (a.T is then the grid's token count), so no offset can reach outside it.
+    // sequences of different lengths are numbered head-fastest in their
+    // scheduling order (all heads of the first sequence of a.ord first):
+    // blocks start roughly in this order as CUs free up, so with the longest
+    // sequences first the work spreads evenly over the CUs.  Their bounds
+    // come from the offsets, clamped into the grid (a.T is then the grid's
+    // token count), so no offset can reach outside it.
     if (a.cu) {
+        h = item % a.H;
+        const int rank = item / a.H;
+        b = size_t(a.ord ? min(max(a.ord[rank], 0), nbatch - 1) : rank);
         const int total = a.T;
         const int s0 = min(max(a.cu[b], 0), total);
         const int s1 = min(max(a.cu[b + 1], s0), total);
@@ -950,6 +957,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     } else {
         a.tok0 = b * size_t(a.T);
     }
+    const int unit = int(b) * a.H + h;  // (batch, head) index of the [B, H, ...] states
     if (a.T == 0) {
         // an empty sequence: the final state is the initial one
         const size_t sb = size_t(unit) * DK * a.DV;
@@ -1159,6 +1167,7 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     a.S_T = f.S_T;
     a.p_T = f.p_T;
     a.cu = f.cu_seqlens;
+    a.ord = f.seq_order;
     a.tok0 = 0;
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;

@@ -31,6 +31,9 @@ struct FwdArgs {
     // sequences, sequence b owning tokens [cu_seqlens[b], cu_seqlens[b + 1])
     // of a [T,H] token grid (device pointer, B + 1 entries)
     const int* cu_seqlens = nullptr;
+    // packed batch only: the order in which sequences are scheduled (device
+    // pointer, B entries, a permutation of 0..B-1) or NULL for 0..B-1
+    const int* seq_order = nullptr;
 };
 
 // Token-by-token recurrence; one workgroup per (b, h) covering all d_v

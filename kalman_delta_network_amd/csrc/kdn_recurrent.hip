@@ -71,7 +71,7 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const Tin* __restrict__ omega, const Tin* __restrict__ r,
                      const float* __restrict__ c0, float mu, int T, int H, const float* S0,
                      const float* p0, Tin* __restrict__ o, float* S_T, float* p_T,
-                     const int* __restrict__ cu) {
+                     const int* __restrict__ cu, const int* __restrict__ ord, int nseq) {
     constexpr int NW = DV / 32;   // waves per workgroup
     constexpr int CPL = DK / 64;  // channels per lane
     constexpr int RPT = DK / 8;   // memory rows per thread
@@ -79,9 +79,12 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 
     __shared__ float4 chan[NW][DK];
 
-    const int unit = blockIdx.x;  // b * H + h
-    const int h = unit % H;
-    const size_t b = size_t(unit / H);
+    // block = rank * H + h; the sequence of rank `rank` is ord[rank] for a
+    // packed batch with a scheduling order (longest first balances the GPU)
+    const int h = int(blockIdx.x) % H;
+    const int rank = int(blockIdx.x) / H;
+    const size_t b = size_t(cu && ord ? min(max(ord[rank], 0), nseq - 1) : rank);
+    const int unit = int(b) * H + h;  // index of the [B, H, ...] states
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int cq = lane & 7;
@@ -235,7 +238,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
                        static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                        static_cast<const Tin*>(a.alpha), static_cast<const Tin*>(a.omega),
                        static_cast<const Tin*>(a.r), a.c0, a.mu, a.T, a.H, a.S0, a.p0,
-                       static_cast<Tin*>(a.o), a.S_T, a.p_T, a.cu_seqlens);
+                       static_cast<Tin*>(a.o), a.S_T, a.p_T, a.cu_seqlens, a.seq_order, a.B);
     return hipGetLastError();
 }
 

@@ -185,7 +185,7 @@ def test_launch_error_path_without_gpu(lib, monkeypatch):
 
 
 def varlen_args(fake, N=3, total=40, H=2, dk=64, dv=64, variant=0, dtype=1, mu=64.0, algo=0, **over):
-    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), cu=fake(), c0=fake(),
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), cu=fake(), order=None, c0=fake(),
              mu=mu, variant=variant, dtype=dtype, N=N, total=total, H=H, dk=dk, dv=dv, S0=None, p0=None,
              o=fake(), S_T=fake(), p_T=fake(), algo=algo)
     a.update(over)
@@ -194,7 +194,7 @@ def varlen_args(fake, N=3, total=40, H=2, dk=64, dv=64, variant=0, dtype=1, mu=6
 
 def call_validate_varlen(lib, a):
     return lib.kdn_validate_forward_varlen(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["cu"],
-                                           a["c0"], a["mu"], a["variant"], a["dtype"], a["N"], a["total"],
+                                           a["order"], a["c0"], a["mu"], a["variant"], a["dtype"], a["N"], a["total"],
                                            a["H"], a["dk"], a["dv"], a["S0"], a["p0"], a["o"], a["S_T"],
                                            a["p_T"], a["algo"])
 
@@ -208,6 +208,7 @@ def test_validate_varlen_accepts_good_arguments(lib):
     # every sequence empty: no token input is read, the states are still written
     assert call_validate_varlen(lib, varlen_args(f, total=0, q=None, k=None, v=None, o=None)) == 0
     assert call_validate_varlen(lib, varlen_args(f, c0=None, p0=f())) == 0
+    assert call_validate_varlen(lib, varlen_args(f, order=f())) == 0
 
 
 @pytest.mark.parametrize("over,status", [
@@ -234,6 +235,8 @@ def test_validate_varlen_aliasing(lib):
     a = varlen_args(f)
     assert call_validate_varlen(lib, dict(a, o=a["cu"])) == kdn.KDN_ERR_ALIAS  # the offsets are an input
     assert call_validate_varlen(lib, dict(a, p_T=a["cu"])) == kdn.KDN_ERR_ALIAS
+    order = f()
+    assert call_validate_varlen(lib, dict(a, order=order, o=order)) == kdn.KDN_ERR_ALIAS  # so is the order
     s = f()
     assert call_validate_varlen(lib, dict(a, S0=s, S_T=s)) == 0
 
@@ -242,7 +245,7 @@ def test_varlen_launch_error_path_without_gpu(lib, monkeypatch):
     monkeypatch.setenv("KDN_FAULT", "launch")
     f = Fake()
     a = varlen_args(f)
-    args = [a[x] for x in ("q", "k", "v", "alpha", "omega", "r", "cu", "c0", "mu", "variant", "dtype", "N",
+    args = [a[x] for x in ("q", "k", "v", "alpha", "omega", "r", "cu", "order", "c0", "mu", "variant", "dtype", "N",
                            "total", "H", "dk", "dv", "S0", "p0", "o", "S_T", "p_T")]
     assert lib.kdn_forward_varlen(*args, None, 0) == kdn.KDN_ERR_HIP
     args[6] = None  # no offsets: reported before the launch stage

@@ -27,15 +27,17 @@ def _state(w, N, seed):
     return S0, p0
 
 
-def run_varlen(dev, w, x, algo, S0=None, p0=None):
+def run_varlen(dev, w, x, algo, S0=None, p0=None, order=None):
     import torch
     import kalman_delta_network_amd as kdn
     t = to_dev(x, w.dtype, dev)
     cu = torch.from_numpy(x["cu_seqlens"]).to(dev)
     S0d = None if S0 is None else torch.from_numpy(S0).to(dev)
     p0d = None if p0 is None else torch.from_numpy(p0).to(dev)
+    od = None if order is None else torch.from_numpy(np.asarray(order, np.int32)).to(dev)
     try:
-        o, S, p = kdn.forward_varlen(**t, cu_seqlens=cu, mu=w.mu, variant=w.variant, S0=S0d, p0=p0d, algo=algo)
+        o, S, p = kdn.forward_varlen(**t, cu_seqlens=cu, mu=w.mu, variant=w.variant, S0=S0d, p0=p0d, algo=algo,
+                                     order=od)
     except kdn.KDNError as e:
         if e.status == kdn.KDN_ERR_UNSUPPORTED and algo == "chunked":
             pytest.skip("chunked algorithm does not cover this dtype")
@@ -92,6 +94,20 @@ def test_varlen_equal_lengths_is_the_batched_forward(dev, algo, variant):
 
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_varlen_scheduling_order_does_not_change_results(dev, algo, variant):
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("varlen_ord", variant, "bf16", len(LENGTHS), 0, 3, 128, 128, 128.0, "uniform", 43)
+    x = wl.varlen_inputs(w, LENGTHS)
+    S0, p0 = _state(w, len(LENGTHS), 7)
+    base = run_varlen(dev, w, x, algo, S0, p0)
+    for order in (kdn.longest_first(x["cu_seqlens"]), np.random.default_rng(1).permutation(len(LENGTHS))):
+        got = run_varlen(dev, w, x, algo, S0, p0, order=order)
+        for g, b in zip(got, base):
+            np.testing.assert_array_equal(g, b)
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
 def test_varlen_all_sequences_empty(dev, algo, variant):
     w = wl.Workload("varlen_empty", variant, "bf16", 3, 0, 2, 128, 128, 128.0, "uniform", 42)
     x = wl.varlen_inputs(w, [0, 0, 0])
@@ -104,12 +120,13 @@ def test_varlen_all_sequences_empty(dev, algo, variant):
 
 def test_varlen_serving_batch_sampled(dev):
     # the benchmark's packed batch (32 sequences of 256..1792 tokens, 16 heads,
-    # d = 128), in the launch configuration bench.py times; the oracle checks
-    # a sample of (sequence, head) pairs
+    # d = 128), in the launch configuration bench.py times (longest first);
+    # the oracle checks a sample of (sequence, head) pairs
+    import kalman_delta_network_amd as kdn
     w = wl.VARLEN
     lengths = wl.varlen_lengths(w.seed, w.B, *wl.VARLEN_RANGE)
     x = wl.varlen_inputs(w, lengths)
-    o, S, p = run_varlen(dev, w, x, "auto")
+    o, S, p = run_varlen(dev, w, x, "auto", order=kdn.longest_first(x["cu_seqlens"]))
     cu = x["cu_seqlens"]
     rng = np.random.default_rng(3)
     for n, h in [(0, 0), (w.B - 1, w.H - 1)] + [(int(a), int(b)) for a, b in
