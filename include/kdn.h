@@ -22,6 +22,15 @@
  *     S, o_t as above with the scalar decay alpha_t
  *     b     = b_hat / (1 + (mu / (d_k r_t)) |k_t|^2 b_hat)
  *
+ *   Isotropic variant with per-channel decay (KDN_ISOTROPIC_CHANNEL, the
+ *   general form of that sentence): alpha_t has one entry per key channel
+ *   and the memory decays by diag(alpha_t) as in the diagonal variant;
+ *   omega_t and r_t are scalars per head-token; the uncertainty scalar is
+ *   predicted with the trace projection a_t = (1/d_k) sum_i alpha_t,i^2:
+ *     b_hat = a_t b + omega_t / d_k;  kappa, b as in the isotropic variant.
+ *   Shapes: alpha [.., dk], omega [..] (no dk), p [B,H].  Only the
+ *   recurrent algorithm runs it (KDN_ALGO_AUTO picks it).
+ *
  * Initial state: S_0 = S0 (or zero when S0 is NULL); p_0 = p0 (or c0[h] on
  * every channel when p0 is NULL).  No 1/sqrt(d_k) scaling is applied to q.
  *
@@ -56,7 +65,7 @@
 extern "C" {
 #endif
 
-enum kdn_variant { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1 };
+enum kdn_variant { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1, KDN_ISOTROPIC_CHANNEL = 2 };
 enum kdn_dtype { KDN_F32 = 0, KDN_BF16 = 1 };
 enum kdn_status {
     KDN_OK = 0,
@@ -84,16 +93,17 @@ enum kdn_algo {
  *
  *   q, k        [B,T,H,dk]   dtype
  *   v           [B,T,H,dv]   dtype
- *   alpha,omega [B,T,H,dk]   dtype (KDN_ISOTROPIC: [B,T,H])
+ *   alpha,omega [B,T,H,dk]   dtype (KDN_ISOTROPIC: [B,T,H]; KDN_ISOTROPIC_CHANNEL:
+ *                            alpha [B,T,H,dk], omega [B,T,H])
  *   r           [B,T,H]      dtype
  *   c0          [H]          float, per-head initial uncertainty; may be NULL
  *                            only when p0 is given
  *   mu                       information scale of the posterior update
  *   S0          [B,H,dk,dv]  float or NULL (zero initial memory)
- *   p0          [B,H,dk]     float or NULL (KDN_ISOTROPIC: [B,H])
+ *   p0          [B,H,dk]     float or NULL (both isotropic variants: [B,H])
  *   o           [B,T,H,dv]   dtype, output
  *   S_T         [B,H,dk,dv]  float, output: memory after the last token
- *   p_T         [B,H,dk]     float, output (KDN_ISOTROPIC: [B,H])
+ *   p_T         [B,H,dk]     float, output (both isotropic variants: [B,H])
  * S_T may be the same buffer as S0 (the memory is continued in place).  No
  * other output may overlap an input or another output (KDN_ERR_ALIAS); in
  * particular p_T needs its own buffer.
@@ -121,7 +131,8 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
  *
  *   q, k        [total,H,dk]   dtype
  *   v           [total,H,dv]   dtype
- *   alpha,omega [total,H,dk]   dtype (KDN_ISOTROPIC: [total,H])
+ *   alpha,omega [total,H,dk]   dtype (KDN_ISOTROPIC: [total,H]; KDN_ISOTROPIC_CHANNEL:
+ *                              alpha [total,H,dk], omega [total,H])
  *   r           [total,H]      dtype
  *   cu_seqlens  [N+1]          int32, DEVICE pointer, read by the kernels:
  *                              0 = cu[0] <= cu[1] <= ... <= cu[N] = total
@@ -131,9 +142,9 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
  *                              the work evenly over the GPU; results do not
  *                              depend on it.
  *   c0          [H]            float (as kdn_forward)
- *   S0          [N,H,dk,dv]    float or NULL;  p0 [N,H,dk] (KDN_ISOTROPIC: [N,H]) or NULL
+ *   S0          [N,H,dk,dv]    float or NULL;  p0 [N,H,dk] (isotropic variants: [N,H]) or NULL
  *   o           [total,H,dv]   dtype, output
- *   S_T         [N,H,dk,dv]    float, output;  p_T [N,H,dk] (KDN_ISOTROPIC: [N,H])
+ *   S_T         [N,H,dk,dv]    float, output;  p_T [N,H,dk] (isotropic variants: [N,H])
  *   algo                       enum kdn_algo, as kdn_forward_algo
  *
  * The offsets and the order live in device memory and are not inspected on
@@ -160,10 +171,11 @@ int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* 
  *
  *   q, k        [N,H,dk]     dtype
  *   v           [N,H,dv]     dtype
- *   alpha,omega [N,H,dk]     dtype (KDN_ISOTROPIC: [N,H])
+ *   alpha,omega [N,H,dk]     dtype (KDN_ISOTROPIC: [N,H]; KDN_ISOTROPIC_CHANNEL:
+ *                            alpha [N,H,dk], omega [N,H])
  *   r           [N,H]        dtype
  *   S           [N,H,dk,dv]  float, read and overwritten in place
- *   p           [N,H,dk]     float, read and overwritten (KDN_ISOTROPIC: [N,H])
+ *   p           [N,H,dk]     float, read and overwritten (both isotropic variants: [N,H])
  *   o           [N,H,dv]     dtype, output
  */
 int kdn_step(const void* q, const void* k, const void* v, const void* alpha, const void* omega,

@@ -19,7 +19,15 @@ KDN_DIAGONAL, KDN_ISOTROPIC = 0, 1
 KDN_F32, KDN_BF16 = 0, 1
 KDN_OK, KDN_ERR_NULL, KDN_ERR_SHAPE, KDN_ERR_UNSUPPORTED, KDN_ERR_VALUE, KDN_ERR_HIP, KDN_ERR_ALIAS = range(7)
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
-VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC}
+KDN_ISOTROPIC_CHANNEL = 2
+VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC, "isochannel": KDN_ISOTROPIC_CHANNEL}
+
+
+def _gate_shapes(var, lead, dk):
+    """(alpha shape, omega shape) of a variant for token dims ``lead``."""
+    alpha = lead + (dk,) if var != KDN_ISOTROPIC else lead
+    omega = lead + (dk,) if var == KDN_DIAGONAL else lead
+    return alpha, omega
 
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_step", "kdn_validate_forward",
@@ -111,8 +119,9 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
             algo="auto", out=None):
     """KDN forward over [B,T,H,*] tensors on one GPU.
 
-    q, k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk] (isotropic [B,T,H]);
-    r [B,T,H] -- all float32 or all bfloat16.  c0 [H] float32 (may be None if
+    q, k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk] (isotropic [B,T,H];
+    "isochannel", the isotropic form with per-channel decay: alpha [B,T,H,dk],
+    omega [B,T,H]); r [B,T,H] -- all float32 or all bfloat16.  c0 [H] float32 (may be None if
     p0 is given); S0 [B,H,dk,dv] / p0 [B,H,dk] (isotropic [B,H]) float32 or None.
     Returns (o, S_T, p_T); ``out`` may supply preallocated (o, S_T, p_T).
     """
@@ -123,10 +132,10 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
     dv = v.shape[-1]
     dev = q.device
     dt = q.dtype
-    gshape = (B, T, H, dk) if var == KDN_DIAGONAL else (B, T, H)
+    ashape, wshape = _gate_shapes(var, (B, T, H), dk)
     pshape = (B, H, dk) if var == KDN_DIAGONAL else (B, H)
     for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (B, T, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (B, T, H))):
         _need(t, name, shp, dt, dev)
     if c0 is not None:
         _need(c0, "c0", (H,), torch.float32, dev)
@@ -181,10 +190,10 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagon
         raise ValueError("cu_seqlens: expected a 1-D tensor of N+1 offsets")
     N = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
-    gshape = (total, H, dk) if var == KDN_DIAGONAL else (total, H)
+    ashape, wshape = _gate_shapes(var, (total, H), dk)
     pshape = (N, H, dk) if var == KDN_DIAGONAL else (N, H)
     for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
-                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (total, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (total, H))):
         _need(t, name, shp, dt, dev)
     if order is not None:
         _need(order, "order", (N,), torch.int32, dev)
@@ -220,9 +229,9 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
-    gshape = (N, H, dk) if var == KDN_DIAGONAL else (N, H)
+    ashape, wshape = _gate_shapes(var, (N, H), dk)
     for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
-                         ("alpha", alpha, gshape), ("omega", omega, gshape), ("r", r, (N, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (N, H))):
         _need(t, name, shp, dt, dev)
     _need(S, "S", (N, H, dk, dv), torch.float32, dev)
     _need(p, "p", (N, H, dk) if var == KDN_DIAGONAL else (N, H), torch.float32, dev)

@@ -1181,6 +1181,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 bool chunked_supports(const FwdArgs& a) {
+    if (a.variant != 0 && a.variant != 1) return false;  // per-channel-decay isotropic: recurrent kernel
     if (a.dtype != 1 || (a.dk != 64 && a.dk != 128) || a.dv % DVT != 0 || a.dv < DVT) return false;
     // 16-byte direct copies of k, alpha, omega and v rows, 16-byte loads of k
     // rows (isotropic), 8-byte stores of four output columns

@@ -19,7 +19,7 @@ struct FwdArgs {
     const void* r;
     const float* c0;
     float mu;
-    int variant;  // 0 diagonal, 1 isotropic
+    int variant;  // 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
     int dtype;    // 0 f32, 1 bf16
     int B, T, H, dk, dv;
     const float* S0;

@@ -9,7 +9,9 @@
 // waves never wait for each other inside the token loop.
 //
 // Per token (KDN summary page, method steps 2-5; isotropic variant per the
-// closing sentence of that section):
+// closing sentence of that section, with a scalar decay or, in its general
+// form, one decay per key channel and the trace projection
+// a = mean_i alpha_i^2 for the uncertainty scalar):
 //   every wave redundantly runs the per-channel part (lane owns channels
 //   lane and lane + 64): predict p_hat, gain denominator r + sum p_hat k^2,
 //   kappa, kappa^T q, posterior p; it stages (alpha_i, k_i, q_i, kappa_i) in
@@ -64,7 +66,8 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DK, int DV, bool ISO, typename Tin>
+// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
+template <int DK, int DV, int VAR, typename Tin>
 __global__ void __launch_bounds__(DV * 2)
 kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const Tin* __restrict__ v, const Tin* __restrict__ alpha,
@@ -72,6 +75,8 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const float* __restrict__ c0, float mu, int T, int H, const float* S0,
                      const float* p0, Tin* __restrict__ o, float* S_T, float* p_T,
                      const int* __restrict__ cu, const int* __restrict__ ord, int nseq) {
+    constexpr bool ISO = VAR != 0;       // one uncertainty scalar per head
+    constexpr bool CHAN = VAR != 1;      // one decay per key channel
     constexpr int NW = DV / 32;   // waves per workgroup
     constexpr int CPL = DK / 64;  // channels per lane
     constexpr int RPT = DK / 8;   // memory rows per thread
@@ -135,16 +140,20 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
             qq[c] = to_f32(q[tok * DK + lane + 64 * c]);
         }
         if (ISO) {
-            const float a = to_f32(alpha[tok]);
+            // trace-projected predict b_hat = a b + omega / d_k; a = alpha^2,
+            // or with per-channel decay the mean of alpha_i^2 over the channels
             const float w = to_f32(omega[tok]);
-            const float bh = a * a * pb + w * inv_dk;
-            float n = 0.f, kq = 0.f;
+            float a2 = 0.f, n = 0.f, kq = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
+                aa[c] = CHAN ? to_f32(alpha[tok * DK + lane + 64 * c]) : to_f32(alpha[tok]);
+                a2 += aa[c] * aa[c];
                 n += kk[c] * kk[c];
                 kq += kk[c] * qq[c];
-                aa[c] = a;
             }
+            if (CHAN) a2 = wave_sum(a2) * inv_dk;
+            else a2 = aa[0] * aa[0];
+            const float bh = a2 * pb + w * inv_dk;
             n = wave_sum(n);
             kq = wave_sum(kq);
             const float beta = bh / (rt + bh * n);
@@ -229,11 +238,11 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool ISO, typename Tin>
+template <int DK, int DV, int VAR, typename Tin>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const long units = long(a.B) * a.H;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((kdn_recurrent_kernel<DK, DV, ISO, Tin>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((kdn_recurrent_kernel<DK, DV, VAR, Tin>), dim3(unsigned(units)),
                        dim3(DV * 2), 0, stream, static_cast<const Tin*>(a.q),
                        static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                        static_cast<const Tin*>(a.alpha), static_cast<const Tin*>(a.omega),
@@ -242,14 +251,15 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DK, int DV, bool ISO>
+template <int DK, int DV, int VAR>
 hipError_t launch_dtype(const FwdArgs& a, hipStream_t s) {
-    return a.dtype == 1 ? launch_t<DK, DV, ISO, bf16_t>(a, s) : launch_t<DK, DV, ISO, float>(a, s);
+    return a.dtype == 1 ? launch_t<DK, DV, VAR, bf16_t>(a, s) : launch_t<DK, DV, VAR, float>(a, s);
 }
 
 template <int DK, int DV>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t s) {
-    return a.variant == 1 ? launch_dtype<DK, DV, true>(a, s) : launch_dtype<DK, DV, false>(a, s);
+    if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
+    return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
 }
 
 }  // namespace

@@ -10,8 +10,10 @@ standard deviation s):
 
 * q, k ~ N(0, 1), each (b, t, h) row L2-normalised over its d_k channels;
 * v ~ N(0, 1);
-* alpha = sigmoid(N(alpha_loc, 0.5)) per channel (isotropic: per head-token);
-* omega = softplus(N(omega_loc, 1)) with the same shape as alpha;
+* alpha = sigmoid(N(alpha_loc, 0.5)) per channel (isotropic: per head-token;
+  isotropic with per-channel decay: per channel);
+* omega = softplus(N(omega_loc, 1)) per channel (both isotropic forms: per
+  head-token);
 * r = 0.01 + softplus(N(0, 1)) per head-token (the pages' r_min = 0.01);
 * c0 = 1.0 per head, or U(0.5, 2) per head;
 * decode state: S0 ~ N(0, 0.1), p0 ~ U(0.1, 1) (isotropic: one p0 per head);
@@ -35,7 +37,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    variant: str          # "diagonal" or "isotropic"
+    variant: str          # "diagonal", "isotropic" or "isochannel" (isotropic with per-channel decay)
     dtype: str            # "f32" or "bf16": dtype of q, k, v, alpha, omega, r and o
     B: int
     T: int
@@ -105,13 +107,14 @@ def _normal(rng, shape, loc=0.0, scale=1.0):
 
 def _draw_tokens(rng, w: Workload, lead: tuple) -> dict:
     """Draw q, k, v, alpha, omega, r with leading shape ``lead`` (e.g. (B,T,H))."""
-    gate_shape = lead + (w.dk,) if w.variant == "diagonal" else lead
+    alpha_shape = lead + (w.dk,) if w.variant in ("diagonal", "isochannel") else lead
+    omega_shape = lead + (w.dk,) if w.variant == "diagonal" else lead
     out = {
         "q": _l2norm(_normal(rng, lead + (w.dk,))),
         "k": _l2norm(_normal(rng, lead + (w.dk,))),
         "v": _normal(rng, lead + (w.dv,)),
-        "alpha": _sigmoid(_normal(rng, gate_shape, w.alpha_loc, 0.5)),
-        "omega": _softplus(_normal(rng, gate_shape, w.omega_loc, 1.0)),
+        "alpha": _sigmoid(_normal(rng, alpha_shape, w.alpha_loc, 0.5)),
+        "omega": _softplus(_normal(rng, omega_shape, w.omega_loc, 1.0)),
         "r": (np.float32(0.01) + _softplus(_normal(rng, lead))).astype(np.float32),
     }
     if w.dtype == "bf16":
@@ -165,7 +168,7 @@ def decode_state(w: Workload) -> dict:
     (isotropic: [N,H]) float32, N = w.B."""
     rng = np.random.default_rng([w.seed, 0xD0])
     S0 = _normal(rng, (w.B, w.H, w.dk, w.dv), 0.0, 0.1)
-    pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)
+    pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)  # isotropic forms: a scalar
     p0 = rng.uniform(0.1, 1.0, size=pshape).astype(np.float32)
     return {"S0": S0, "p0": p0}
 

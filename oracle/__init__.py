@@ -5,7 +5,8 @@ baseline leg of the benchmark may import this package.  It shares no code
 with the HIP library (kalman_delta_network_amd) and the library never calls
 it.
 
-* ``forward_diag`` / ``forward_iso`` / ``step_diag`` / ``step_iso`` wrap the
+* ``forward_diag`` / ``forward_iso`` / ``forward_isoc`` and the ``step_*``
+  decode steps wrap the
   sequential fp64 recurrence in ``kdn_oracle.c`` ("Kalman Delta Networks:
   Uncertainty-aware Associative Memory", summary page, section on the
   method steps, steps 2-5, and its closing sentence for the isotropic
@@ -52,12 +53,12 @@ def _load():
         I = ctypes.c_int
         D = ctypes.c_double
         fwd = [I, I, I, I, I, P, P, P, P, P, P, P, D, P, P, P, P, P, P, P, P]
-        for name in ("kdn_oracle_forward_diag", "kdn_oracle_forward_iso"):
+        for name in ("kdn_oracle_forward_diag", "kdn_oracle_forward_iso", "kdn_oracle_forward_isoc"):
             fn = getattr(lib, name)
             fn.argtypes = fwd
             fn.restype = I
         stp = [I, I, I, I, P, P, P, P, P, P, D, P, P, P]
-        for name in ("kdn_oracle_step_diag", "kdn_oracle_step_iso"):
+        for name in ("kdn_oracle_step_diag", "kdn_oracle_step_iso", "kdn_oracle_step_isoc"):
             fn = getattr(lib, name)
             fn.argtypes = stp
             fn.restype = I
@@ -87,7 +88,7 @@ def _forward(name, q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=Fal
     q, k, v, alpha, omega, r = (_f32(x) for x in (q, k, v, alpha, omega, r))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    iso = name.endswith("iso")
+    iso = name.endswith(("iso", "isoc"))
     c0 = _f32(np.broadcast_to(np.asarray(c0, np.float32), (H,)))
     S0, p0 = _f64(S0), _f64(p0)
     o = np.zeros((B, T, H, dv))
@@ -129,7 +130,7 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
     forward_diag / forward_iso.  The recurrence is per sequence; packing only
     decides which rows belong to which sequence.
     Returns o [total,H,dv], S [N,H,dk,dv], p [N,H,dk] (isotropic [N,H])."""
-    fn = forward_diag if variant == "diagonal" else forward_iso
+    fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc}[variant]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     if cu.ndim != 1 or len(cu) < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != len(q):
         raise ValueError("cu_seqlens must rise from 0 to the number of token rows")
@@ -138,7 +139,7 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
     dv = np.shape(v)[-1]
     o = np.zeros((total, H, dv))
     S = np.zeros((N, H, dk, dv))
-    p = np.zeros((N, H, dk) if variant == "diagonal" else (N, H))
+    p = np.zeros((N, H, dk) if variant == "diagonal" else (N, H))  # isotropic forms: one scalar per head
     for n in range(N):
         a, b = int(cu[n]), int(cu[n + 1])
         out = fn(*(np.asarray(x)[None, a:b] for x in (q, k, v, alpha, omega, r)), c0, mu,
@@ -147,6 +148,13 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
         S[n] = out["S"][0]
         p[n] = out["p"][0]
     return {"o": o, "S": S, "p": p}
+
+
+def forward_isoc(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
+    """Isotropic KDN with per-channel decay: alpha [B,T,H,dk] (the memory
+    decays by diag(alpha), the uncertainty scalar by mean_i alpha_i^2);
+    omega, r [B,T,H]; p0 / returned p [B,H]."""
+    return _forward("kdn_oracle_forward_isoc", q, k, v, alpha, omega, r, c0, mu, S0, p0, trace)
 
 
 def _step(name, q, k, v, alpha, omega, r, mu, S, p):
@@ -172,3 +180,8 @@ def step_diag(q, k, v, alpha, omega, r, mu, S, p):
 def step_iso(q, k, v, alpha, omega, r, mu, S, p):
     """Isotropic decode step: alpha, omega, r [N,H]; p [N,H]."""
     return _step("kdn_oracle_step_iso", q, k, v, alpha, omega, r, mu, S, p)
+
+
+def step_isoc(q, k, v, alpha, omega, r, mu, S, p):
+    """Per-channel-decay isotropic decode step: alpha [N,H,dk]; omega, r [N,H]; p [N,H]."""
+    return _step("kdn_oracle_step_isoc", q, k, v, alpha, omega, r, mu, S, p)

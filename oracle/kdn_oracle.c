@@ -29,10 +29,16 @@
  * b = b_hat / (1 + (mu/(d_k r)) |k|^2 b_hat).  That last formula is a reading
  * (the page does not print it); see the readings list of the repository.
  *
+ * Isotropic variant with per-channel decay (the general form of the same
+ * sentence): alpha has one decay per key channel, the memory decays by
+ * diag(alpha), omega and r are scalars per head-token, and the trace
+ * projection uses a = (1/d_k) sum_i alpha_i^2; gain and posterior as above.
+ *
  * Inputs arrive as float arrays holding exactly the values the GPU receives
  * (bf16 values widen to float without loss); all arithmetic is double.
  * Layouts (row-major, contiguous):
- *   q, k, alpha, omega : [B,T,H,dk]   (isotropic alpha, omega: [B,T,H])
+ *   q, k, alpha, omega : [B,T,H,dk]   (isotropic alpha, omega: [B,T,H];
+ *                                     per-channel-decay isotropic: omega [B,T,H])
  *   v, o               : [B,T,H,dv]
  *   r                  : [B,T,H]
  *   c0                 : [H]
@@ -180,6 +186,64 @@ static void iso_head(int b, int h, int T, int H, int dk, int dv,
     free(S); free(delta);
 }
 
+/* One (b,h) recurrence of the Isotropic KDN with per-channel decay: alpha
+ * [.., dk], omega and r scalars per head-token. */
+static void isoc_head(int b, int h, int T, int H, int dk, int dv,
+                      const float* q, const float* k, const float* v,
+                      const float* alpha, const float* omega, const float* r,
+                      const float* c0, double mu, const double* S0,
+                      const double* p0, double* o, double* S_T, double* p_T,
+                      double* tr_phat, double* tr_kappa, double* tr_p) {
+    const size_t state = ((size_t)b * H + h);
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* delta = (double*)malloc(sizeof(double) * dv);
+    double bcov = p0 ? p0[state] : (double)c0[h];
+    for (size_t e = 0; e < (size_t)dk * dv; ++e) S[e] = S0 ? S0[state * (size_t)dk * dv + e] : 0.0;
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = IDX_TOK(b, t, h, 0, T, H);
+        const float* kt = k + tok * dk;
+        const float* qt = q + tok * dk;
+        const float* vt = v + tok * dv;
+        const float* at = alpha + tok * dk;
+        const double w = omega[tok];
+        const double rt = r[tok];
+
+        /* trace-projected predict: b_hat = a b + omega/d_k, a = mean_i alpha_i^2 */
+        double a = 0.0;
+        for (int i = 0; i < dk; ++i) a += (double)at[i] * (double)at[i];
+        a /= (double)dk;
+        const double bh = a * bcov + w / (double)dk;
+        double n = 0.0;
+        for (int i = 0; i < dk; ++i) n += (double)kt[i] * (double)kt[i];
+        /* scalar gain beta = b_hat / (r + b_hat |k|^2), kappa = beta k */
+        const double beta = bh / (rt + bh * n);
+        /* predicted mean diag(alpha) S, innovation, residual write */
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += (double)at[i] * S[(size_t)i * dv + j] * (double)kt[i];
+            delta[j] = (double)vt[j] - pred;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = (double)at[i] * S[(size_t)i * dv + j] + beta * (double)kt[i] * delta[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * (double)qt[i];
+            o[tok * dv + j] = acc;
+        }
+        /* posterior: precision increment (mu/r)|k|^2 averaged over d_k channels */
+        bcov = bh / (1.0 + (mu / ((double)dk * rt)) * n * bh);
+        if (tr_phat) tr_phat[tok] = bh;
+        if (tr_kappa) for (int i = 0; i < dk; ++i) tr_kappa[tok * dk + i] = beta * (double)kt[i];
+        if (tr_p) tr_p[tok] = bcov;
+    }
+    if (p_T) p_T[state] = bcov;
+    if (S_T)
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) S_T[state * (size_t)dk * dv + e] = S[e];
+    free(S); free(delta);
+}
+
 typedef void (*head_fn)(int, int, int, int, int, int, const float*, const float*, const float*,
                         const float*, const float*, const float*, const float*, double,
                         const double*, const double*, double*, double*, double*, double*,
@@ -221,6 +285,16 @@ int kdn_oracle_forward_iso(int B, int T, int H, int dk, int dv,
                      o, S_T, p_T, tr_phat, tr_kappa, tr_p);
 }
 
+int kdn_oracle_forward_isoc(int B, int T, int H, int dk, int dv,
+                            const float* q, const float* k, const float* v,
+                            const float* alpha, const float* omega, const float* r,
+                            const float* c0, double mu, const double* S0, const double* p0,
+                            double* o, double* S_T, double* p_T,
+                            double* tr_phat, double* tr_kappa, double* tr_p) {
+    return run_heads(isoc_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
+                     o, S_T, p_T, tr_phat, tr_kappa, tr_p);
+}
+
 /*
  * Single-token decode step: exactly one iteration of the recurrence on the
  * carried state (S, p), for N independent sequences.  S [N,H,dk,dv] and
@@ -253,6 +327,12 @@ int kdn_oracle_step_iso(int N, int H, int dk, int dv, const float* q, const floa
                         const float* v, const float* alpha, const float* omega, const float* r,
                         double mu, double* S, double* p, double* o) {
     return step_common(iso_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
+}
+
+int kdn_oracle_step_isoc(int N, int H, int dk, int dv, const float* q, const float* k,
+                         const float* v, const float* alpha, const float* omega, const float* r,
+                         double mu, double* S, double* p, double* o) {
+    return step_common(isoc_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
 }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */

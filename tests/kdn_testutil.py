@@ -37,7 +37,8 @@ def to_dev(x: dict, dtype: str, device):
 
 
 def oracle_forward(w: wl.Workload, x: dict, S0=None, p0=None, trace=False):
-    fn = oracle.forward_iso if w.variant == "isotropic" else oracle.forward_diag
+    fn = {"diagonal": oracle.forward_diag, "isotropic": oracle.forward_iso,
+          "isochannel": oracle.forward_isoc}[w.variant]
     return fn(**{n: x[n] for n in TOKEN_INPUTS}, c0=x["c0"], mu=w.mu, S0=S0, p0=p0, trace=trace)
 
 

@@ -70,7 +70,7 @@ def call_validate(lib, a):
 
 def test_validate_forward_accepts_good_arguments(lib):
     f = Fake()
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         for dtype in (0, 1):
             for dk in (64, 128):
                 for dv in (64, 128):
@@ -92,7 +92,7 @@ def test_validate_forward_accepts_good_arguments(lib):
     (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dv=32), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dk=-64), kdn.KDN_ERR_SHAPE),
-    (dict(variant=2), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(variant=3), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dtype=7), kdn.KDN_ERR_UNSUPPORTED),
     (dict(algo=9), kdn.KDN_ERR_UNSUPPORTED),
     (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
@@ -149,6 +149,7 @@ def call_validate_step(lib, a):
     (dict(dk=32), kdn.KDN_ERR_UNSUPPORTED),
     (dict(mu=-2.0), kdn.KDN_ERR_VALUE),
     (dict(variant=5), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(variant=2), kdn.KDN_OK),
 ])
 def test_validate_step(lib, over, status):
     f = Fake()

@@ -281,6 +281,65 @@ def test_isotropic_covariance_reset_is_gated_delta_rule():
         S_kdn = new["S"]
 
 
+# Isotropic variant with per-channel decay (the summary page's general form:
+# memory decay diag(alpha), uncertainty scalar predicted with
+# a = (1/d_k) sum_i alpha_i^2)
+
+def test_isochannel_with_equal_channel_decays_is_the_isotropic_form():
+    w, x = small("isotropic", T=50)
+    args = {k: x[k] for k in ("q", "k", "v", "omega", "r", "c0")}
+    ref = oracle.forward_iso(**args, alpha=x["alpha"], mu=w.mu, trace=True)
+    a_ch = np.repeat(x["alpha"][..., None], w.dk, axis=-1)  # the same decay on every channel
+    got = oracle.forward_isoc(**args, alpha=a_ch, mu=w.mu, trace=True)
+    for key in ("o", "S", "p", "trace_p", "trace_p_hat"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-12, atol=1e-14)
+
+
+def test_isochannel_uncertainty_is_the_mobius_product():
+    w, x = small("isochannel", T=48, mu=8.0)
+    ref = oracle.forward_isoc(**{k: x[k] for k in ("q", "k", "v", "alpha", "omega", "r", "c0")},
+                              mu=w.mu, trace=True)
+    B, T, H, dk = x["k"].shape
+    for b in range(B):
+        for h in range(H):
+            Mp = np.eye(2)
+            for t in range(T):
+                a = float(np.mean(x["alpha"][b, t, h].astype(np.float64) ** 2))
+                om = float(x["omega"][b, t, h]) / dk
+                n = float(np.sum(x["k"][b, t, h].astype(np.float64) ** 2))
+                c = w.mu / (dk * float(x["r"][b, t, h])) * n
+                Mp = np.array([[a, om], [c * a, 1.0 + c * om]]) @ Mp
+                num, den = Mp @ np.array([float(x["c0"][h]), 1.0])
+                np.testing.assert_allclose(num / den, ref["trace_p"][b, t, h], rtol=1e-13)
+
+
+def test_isochannel_covariance_reset_is_kda_delta_rule():
+    # with b_hat forced each step the write is the fixed-gain residual form
+    # with a per-channel transition, S = (I - beta k k^T) diag(alpha) S + beta k v^T
+    N, H, dk, dv = 2, 2, 8, 6
+    w = wl.Workload("t", "isochannel", "f32", N, 1, H, dk, dv, 8.0, "one", 22, omega_loc=0.0)
+    st = wl.decode_state(w)
+    S_kdn = st["S0"].astype(np.float64)
+    S_kda = S_kdn.copy()
+    rng = np.random.default_rng(6)
+    for step in range(25):
+        x = wl.decode_tokens(w, step)
+        assert x["alpha"].shape == (N, H, dk) and x["omega"].shape == (N, H)
+        bhat = rng.uniform(0.05, 3.0, size=(N, H))
+        al = x["alpha"].astype(np.float64)
+        a = np.mean(al * al, axis=-1)
+        b_prev = (bhat - x["omega"].astype(np.float64) / dk) / a
+        new = oracle.step_isoc(**x, mu=w.mu, S=S_kdn, p=b_prev)
+        for n in range(N):
+            for h in range(H):
+                k = x["k"][n, h].astype(np.float64)
+                beta = bhat[n, h] / (float(x["r"][n, h]) + bhat[n, h] * (k @ k))
+                S_kda[n, h] = (np.eye(dk) - beta * np.outer(k, k)) @ (np.diag(al[n, h]) @ S_kda[n, h]) + \
+                    beta * np.outer(k, x["v"][n, h].astype(np.float64))
+        np.testing.assert_allclose(new["S"], S_kda, rtol=1e-12, atol=1e-12)
+        S_kdn = new["S"]
+
+
 def test_isotropic_posterior_at_mu_dk_is_dense_variance_along_unit_key():
     dk, dv = 8, 3
     rng = np.random.default_rng(9)
