@@ -31,13 +31,17 @@ MAIN = "diag_bf16_b8_t4096_h16_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _gate_elems(w) -> int:
+    """alpha plus omega elements per token-head."""
+    return {"diagonal": 2 * w.dk, "isotropic": 2, "isochannel": w.dk + 1}[w.variant]
+
+
 def forward_bytes(w) -> int:
     """Algorithmic HBM bytes of one forward call: every input read once, o
     written once in the input dtype, final state written, c0 read."""
     es = 2 if w.dtype == "bf16" else 4
     toks = w.B * w.T * w.H
-    gate = w.dk if w.variant == "diagonal" else 1
-    per_tok = es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv
+    per_tok = es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv
     pdim = w.dk if w.variant == "diagonal" else 1
     return toks * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4
 
@@ -46,8 +50,7 @@ def varlen_bytes(w, total: int) -> int:
     """Algorithmic HBM bytes of one packed forward over w.B sequences holding
     `total` tokens in all: as forward_bytes, plus the N+1 offsets."""
     es = 2 if w.dtype == "bf16" else 4
-    gate = w.dk if w.variant == "diagonal" else 1
-    per_tok = es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv
+    per_tok = es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv
     pdim = w.dk if w.variant == "diagonal" else 1
     return total * w.H * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4 + (w.B + 1) * 4
 
@@ -57,9 +60,8 @@ def step_bytes(w) -> int:
     one token of inputs read, o written."""
     es = 2 if w.dtype == "bf16" else 4
     units = w.B * w.H
-    gate = w.dk if w.variant == "diagonal" else 1
     pdim = w.dk if w.variant == "diagonal" else 1
-    return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + 2 * gate + 1) + es * w.dv)
+    return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv)
 
 
 def kernel_source_hash() -> str:
@@ -268,7 +270,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the isotropic, decode and packed-batch lines")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the isotropic, decode, packed-batch and per-channel-decay isotropic lines")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the workload of the rocprofv3 counter runs and exit")
@@ -319,6 +322,12 @@ def main():
         extra["decode"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
                                        args.decode_steps)
         extra["varlen"] = bench_varlen(kdn, dev, max(3, args.steps // 2), args.algo)
+        wc = wl.WORKLOADS["isoch_bf16_b8_t4096_h16_d128"]
+        tc = upload(wl.forward_inputs(wc), wc.dtype, dev)
+        mc, lc = time_forward(kdn, wc, tc, 3, 1, "auto")
+        extra["isochannel"] = {"workload": wc.name, "tokens_per_s": wc.B * wc.T / (mc / 1e3), "ms_per_step": mc,
+                               "hbm_frac": forward_bytes(wc) / (lc / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del tc
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x)

@@ -67,11 +67,14 @@ WORKLOADS = {
     "diag_bf16_b1_t65536_h16_d128": Workload(
         "diag_bf16_b1_t65536_h16_d128", "diagonal", "bf16", 1, 65536, 16, 128, 128, 128.0,
         "one", 1003, alpha_loc=4.0),
+    "isoch_bf16_b8_t4096_h16_d128": Workload(
+        "isoch_bf16_b8_t4096_h16_d128", "isochannel", "bf16", 8, 4096, 16, 128, 128, 128.0,
+        "uniform", 1006),
     "decode_diag_bf16_n256_h16_d128_s1024": Workload(
         "decode_diag_bf16_n256_h16_d128_s1024", "diagonal", "bf16", 256, 1, 16, 128, 128, 128.0,
         "one", 1004, decode_steps=1024),
 }
-# the five workloads in the order they are listed in the benchmark table
+# the workloads in the order they are listed in the benchmark table
 WORKLOAD_ORDER = list(WORKLOADS)
 
 

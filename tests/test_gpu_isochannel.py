@@ -109,8 +109,9 @@ def test_isochannel_packed_batch(dev):
 
 
 def test_isochannel_full_size_sampled(dev):
-    # B=8, T=4096, H=16, d=128 (the forward bench shape), oracle on sampled heads
-    w = wl.Workload("isoch_full", "isochannel", "bf16", 8, 4096, 16, 128, 128, 128.0, "uniform", 1006)
+    # the benchmark's workload (B=8, T=4096, H=16, d=128) in the configuration
+    # bench.py times; the oracle runs on sampled heads
+    w = wl.WORKLOADS["isoch_bf16_b8_t4096_h16_d128"]
     x = wl.forward_inputs(w)
     o, S, p = run(dev, w, x)
     pairs = sample_pairs(w.B, w.H, 3, seed=2)
