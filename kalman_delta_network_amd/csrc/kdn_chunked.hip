@@ -435,13 +435,15 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
 // ---------------------------------------------------------------------------
 // chain role, isotropic variant: lane = token (lanes 32..63 help with |k|^2)
 // ---------------------------------------------------------------------------
+template <int VAR>
 struct ChainIsoRegs {
-    u4 kr[8];            // half a k row (DK/2 channels) of token lane & 31
-    bf16_t al, w, rv;  // alpha, omega, r of token lane & 31
+    u4 kr[8];                       // half a k row (DK/2 channels) of token lane & 31
+    u4 ar[VAR == 2 ? 8 : 1];        // per-channel decay: the same half of the alpha row
+    bf16_t al, w, rv;               // alpha (scalar decay), omega, r of token lane & 31
 };
 
-template <int DK>
-__device__ __forceinline__ void chain_iso_load(ChainIsoRegs& X, const Args& a, size_t b, int h, int c,
+template <int DK, int VAR>
+__device__ __forceinline__ void chain_iso_load(ChainIsoRegs<VAR>& X, const Args& a, size_t b, int h, int c,
                                                int nchunks) {
     c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
@@ -450,32 +452,52 @@ __device__ __forceinline__ void chain_iso_load(ChainIsoRegs& X, const Args& a, s
     const u4* src = reinterpret_cast<const u4*>(a.k + e * DK + (lane >> 5) * (DK / 2));
 #pragma unroll
     for (int m = 0; m < NQ; ++m) X.kr[m] = src[m];
-    X.al = a.alpha[e];
+    if constexpr (VAR == 2) {
+        const u4* asrc = reinterpret_cast<const u4*>(a.alpha + e * DK + (lane >> 5) * (DK / 2));
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) X.ar[m] = asrc[m];
+    } else {
+        X.al = a.alpha[e];
+    }
     X.w = a.omega[e];
     X.rv = a.r[e];
 }
 
+// sum of squares of the bf16 pairs of half a row (lanes 0..31 and 32..63 hold
+// the two halves of token lane & 31's row; the result is the whole row's sum)
 template <int DK>
-__device__ __forceinline__ void chain_iso_run(const ChainIsoRegs& X, Smem<DK>& sm, int buf, float mu,
-                                              float& bprev, int nvalid, int gring) {
-    const int lane = threadIdx.x & 63;
-    const bool ok = (lane & 31) < nvalid;
+__device__ __forceinline__ float row_sumsq(const u4 (&r)[8]) {
     constexpr int NQ = DK / 16;
     float n = 0.f;
 #pragma unroll
     for (int m = 0; m < NQ; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float x0 = bf_lo(X.kr[m][e]), x1 = bf_hi(X.kr[m][e]);
+            const float x0 = bf_lo(r[m][e]), x1 = bf_hi(r[m][e]);
             n = fmaf(x0, x0, n);
             n = fmaf(x1, x1, n);
         }
-    n += __shfl_xor(n, 32, 64);
-    const float al = ok ? bf1(bf16_t(X.al)) : 1.f;
+    return n + __shfl_xor(n, 32, 64);
+}
+
+template <int DK, int VAR>
+__device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<DK>& sm, int buf, float mu,
+                                              float& bprev, int nvalid, int gring) {
+    const int lane = threadIdx.x & 63;
+    const bool ok = (lane & 31) < nvalid;
+    const float n = row_sumsq<DK>(X.kr);
     const float w = ok ? bf1(bf16_t(X.w)) * (1.f / float(DK)) : 0.f;
     const float rt = ok ? bf1(bf16_t(X.rv)) : 1.f;
     const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
-    const float asq = al * al;
+    // the uncertainty's decay: alpha^2, or with per-channel decay the trace
+    // projection mean_i alpha_i^2 (padding tokens: 1)
+    float al = 1.f, asq;
+    if constexpr (VAR == 2) {
+        asq = ok ? row_sumsq<DK>(X.ar) * (1.f / float(DK)) : 1.f;
+    } else {
+        al = ok ? bf1(bf16_t(X.al)) : 1.f;
+        asq = al * al;
+    }
     // this token's Mobius matrix [[m00, m01], [m10, m11]] and decay
     float m00 = asq, m01 = w, m10 = cn * asq, m11 = fmaf(cn, w, 1.f);
     float g = al;
@@ -501,12 +523,65 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs& X, Smem<DK>& s
     if ((lane & 31) == 0) bbefore = bprev;
     if (lane < L) {
         sm.bh[buf][lane] = fmaf(asq, bbefore, w);
-        sm.gs[buf][lane] = g;
+        if (VAR == 1) sm.gs[buf][lane] = g;
         sm.rr[gring][lane] = rt;
     }
     bprev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt), L - 1));
-    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
-    for (int i = lane; i < DK; i += 64) sm.gL[gring][i] = gl;
+    if (VAR == 1) {  // (per-channel decay: g and g_L come from the decay chain)
+        const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
+        for (int i = lane; i < DK; i += 64) sm.gL[gring][i] = gl;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decay chain (isotropic variant with per-channel decay): lane = channel
+// pair (d_k = 128) or channel (64); the cumulative decays g_t,i of a chunk
+// ---------------------------------------------------------------------------
+template <int DK>
+struct DecayRegs {
+    uint32_t ap[L];  // alpha of the lane's channel(s) for the chunk's 32 tokens (bf16 pair or value)
+};
+
+template <int DK>
+__device__ __forceinline__ void chain_decay_load(DecayRegs<DK>& X, const Args& a, size_t b, int h, int c,
+                                                 int nchunks) {
+    c = min(max(c, 0), nchunks - 1);  // always issue: see the loader note above
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        const size_t e = tokidx(a, b, h, min(c * L + t, a.T - 1)) * DK;
+        if (DK == 128) X.ap[t] = reinterpret_cast<const uint32_t*>(a.alpha + e)[lane];
+        else X.ap[t] = (a.alpha + e)[lane];
+    }
+}
+
+// g_t,i = prod_{s <= t} alpha_s,i in the chunk (padding tokens: alpha = 1),
+// stored as the diagonal variant's chain stores it (8-token groups) with g_L
+template <int DK>
+__device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>& sm, int buf, int nvalid,
+                                                int gring) {
+    constexpr int CPL = DK / 64;
+    const int i0 = CPL * (threadIdx.x & 63);
+    float g[CPL], gv[CPL][2];
+    uint32_t gp[CPL][4];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) g[cc] = 1.f;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        const bool ok = t < nvalid;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float al = cc ? bf_hi(X.ap[t]) : bf_lo(X.ap[t]);
+            g[cc] *= ok ? al : 1.f;
+            gv[cc][t & 1] = g[cc];
+            if (t & 1) gp[cc][(t >> 1) & 3] = pack2_opaque(gv[cc][0], gv[cc][1]);
+            if ((t & 7) == 7)
+                *reinterpret_cast<u4*>(&sm.GQ[buf][((t >> 3) * DK + i0 + cc) * 8]) =
+                    u4{gp[cc][0], gp[cc][1], gp[cc][2], gp[cc][3]};
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) sm.gL[gring][i0 + cc] = g[cc];
 }
 
 // ---------------------------------------------------------------------------
@@ -542,8 +617,9 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
     }
 }
 
-template <int DK, bool ISO, bool MASK>
+template <int DK, int VAR, bool MASK>
 __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int kslot, int f, int nvalid) {
+    constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head (Kh formed here)
     const int lane = threadIdx.x & 63;
     constexpr int CPL = DK / 64;           // channels per lane
     const int i0 = CPL * lane;             // first channel of this lane
@@ -552,22 +628,25 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     // u + 4 (f >> 1) of Kh^T group (2f + h) & 3.
     const int hq = 4 * (f >> 1);
     // read phase: the chain's outputs for the wave's 8 tokens
-    u4 gq[CPL];     // g of channel i0 + cc, tokens 8f .. 8f + 7 (diagonal variant)
+    u4 gq[CPL];     // g of channel i0 + cc, tokens 8f .. 8f + 7 (per-channel decay)
     u2 kq[CPL][2];  // kappa'/g of channel i0 + cc, tokens 8f + 4h .. 8f + 4h + 3 (diagonal variant)
-    float gsv[8], bhv[8];  // isotropic scalars
+    float gsv[8], bhv[8];  // isotropic scalars: g_t (scalar decay) and b_hat_t
     if (ISO) {
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
-            gsv[tt] = sm.gs[nb][8 * f + tt];
+            if (VAR == 1) gsv[tt] = sm.gs[nb][8 * f + tt];
             bhv[tt] = sm.bh[nb][8 * f + tt];
         }
-    } else {
+    }
+    if (VAR != 1) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             gq[cc] = *reinterpret_cast<const u4*>(&sm.GQ[nb][(f * DK + i0 + cc) * 8]);
+            if (VAR == 0)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                kq[cc][h] = *reinterpret_cast<const u2*>(&sm.KhQ[kslot][(((2 * f + h) & 3) * DK + i0 + cc) * 8 + hq]);
+                for (int h = 0; h < 2; ++h)
+                    kq[cc][h] = *reinterpret_cast<const u2*>(
+                        &sm.KhQ[kslot][(((2 * f + h) & 3) * DK + i0 + cc) * 8 + hq]);
         }
     }
     uint32_t kw4[4];  // Kh^T staging (isotropic): the bf16 pairs (DK = 128) or values of 4 tokens
@@ -585,11 +664,19 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             qq[CPL - 1] = bf_hi(qp);
         }
         uint32_t khw;  // this lane's Kh entries of token t
-        if (ISO) {
+        if (VAR == 1) {
             const float sc = bhv[tt] * __builtin_amdgcn_rcpf(gsv[tt]);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) g[c] = gsv[tt];
             khw = CPL == 2 ? pack2(kk[0] * sc, kk[CPL - 1] * sc) : uint32_t(to_bf(kk[0] * sc));
+        } else if (VAR == 2) {
+            // g_t per channel from the decay chain; Kh = b_hat_t k / g_t
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+                g[cc] = (tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1]);
+            const float k0 = kk[0] * (bhv[tt] * __builtin_amdgcn_rcpf(g[0]));
+            khw = CPL == 2 ? pack2(k0, kk[CPL - 1] * (bhv[tt] * __builtin_amdgcn_rcpf(g[CPL - 1])))
+                           : uint32_t(to_bf(k0));
         } else {
             // kappa'_t / g_t and g_t from the chain's grouped stores
             const int h = tt >> 2, u = tt & 3;
@@ -919,8 +1006,10 @@ __device__ __forceinline__ int state_index(int w) { return ROLE_LAYOUT == 0 ? w 
 __device__ __forceinline__ int form_index(int w) {
     return ROLE_LAYOUT == 0 ? (w < 4 ? w - 2 : w - 4) : ROLE_LAYOUT == 1 ? w - 2 : (w >= 4 ? w - 4 : w);
 }
-template <int DK, bool ISO>
+// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
+template <int DK, int VAR>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
+    constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
     __shared__ Smem<DK> sm;
     const int ntile = a.DV / DVT;
     const int bid = blockIdx.x;
@@ -979,7 +1068,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     const bool is_form = wave >= 2 && !is_state_wave(wave);
     const int fwave = form_index(wave);
     uint32_t r0 = 0;
-    if (!ISO && is_form) {
+    if (VAR == 0 && is_form) {
         chain_diag_issue<DK, 0, 4>(sm, a, b, h, 0, nchunks, fwave);
         chain_diag_issue<DK, 1, 4>(sm, a, b, h, 0, nchunks, fwave);
         chain_diag_issue<DK, 0, 4>(sm, a, b, h, 1, nchunks, fwave);
@@ -994,12 +1083,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         sm.Td[bb][a * 256 + tt * 16 + ss] = 0;
     }
     vm_wait<0>();  // chunk 0's tiles and r have landed
-    if (!ISO && is_form && fwave == 3) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
+    if (VAR == 0 && is_form && fwave == 3) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
     if (wave == 0 || wave == 1) {
         // ---------------- chain ----------------
-        if (!ISO) {
+        if (VAR == 0) {
             const bool active = wave < DK / 64;
             const int i = wave * 64 + lane;
             float p = 0.f;
@@ -1031,31 +1120,51 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 step(IntC<1>{}, c + 1);
             }
             if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
-        } else {
-            float bprev = a.p0 ? a.p0[unit] : a.c0[h];
-            settle(bprev);
-            ChainIsoRegs A, B;
-            if (wave == 0) chain_iso_load<DK>(A, a, b, h, 0, nchunks);
+        } else if (wave == 1) {
+            // the per-channel decays (isotropic variant with per-channel
+            // decay; otherwise this wave only keeps the barrier count)
+            DecayRegs<DK> A, B;
+            if (VAR == 2) chain_decay_load<DK>(A, a, b, h, 0, nchunks);
             for (int it = 0; it < nit; it += 2) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    ChainIsoRegs& X = half ? B : A;
-                    ChainIsoRegs& Y = half ? A : B;
+                    DecayRegs<DK>& X = half ? B : A;
+                    DecayRegs<DK>& Y = half ? A : B;
                     const int c = it + half;
-                    if (wave == 0) {
-                        // the next chunk's loads go out after this chunk's
-                        // registers are consumed: issued earlier, their
-                        // address temporaries would be placed in registers of
-                        // loads still in flight, and the compiler would wait
-                        // for those loads (a full memory round trip) first
-                        if (c < nchunks) chain_iso_run<DK>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
-                        chain_iso_load<DK>(Y, a, b, h, c + 1, nchunks);
+                    if (VAR == 2) {
+                        // next chunk's loads after this chunk's registers are consumed
+                        if (c < nchunks) chain_decay_run<DK>(X, sm, c & 1, min(L, a.T - c * L), c % 3);
+                        chain_decay_load<DK>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
                     bar();
                 }
             }
-            if (wave == 0 && lane == 0 && tile == 0) a.p_T[unit] = bprev;
+        } else {
+            float bprev = a.p0 ? a.p0[unit] : a.c0[h];
+            settle(bprev);
+            ChainIsoRegs<VAR> A, B;
+            chain_iso_load<DK, VAR>(A, a, b, h, 0, nchunks);
+            for (int it = 0; it < nit; it += 2) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    ChainIsoRegs<VAR>& X = half ? B : A;
+                    ChainIsoRegs<VAR>& Y = half ? A : B;
+                    const int c = it + half;
+                    {
+                        // the next chunk's loads go out after this chunk's
+                        // registers are consumed: issued earlier, their
+                        // address temporaries would be placed in registers of
+                        // loads still in flight, and the compiler would wait
+                        // for those loads (a full memory round trip) first
+                        if (c < nchunks) chain_iso_run<DK, VAR>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
+                        chain_iso_load<DK, VAR>(Y, a, b, h, c + 1, nchunks);
+                    }
+                    bar();
+                    bar();
+                }
+            }
+            if (lane == 0 && tile == 0) a.p_T[unit] = bprev;
         }
     } else if (is_state_wave(wave)) {
         // ---------------- state ----------------
@@ -1088,7 +1197,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             bar();
             // rows 0..15 of the chain's chunk it + 2: the chain has read those
             // rows of chunk it (same buffer) before the barrier above
-            if (!ISO) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
+            if (VAR == 0) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
             if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
             bar();
         }
@@ -1112,15 +1221,15 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 const int c = it + half - 1;
                 // the chain's inputs for chunk c + 2 (it consumes chunk c + 1 now)
                 uint32_t rnext = 0;
-                if (!ISO) {
+                if (VAR == 0) {
                     chain_diag_issue<DK, 1, 4>(sm, a, b, h, c + 2, nchunks, f);  // rows 16..31
                     if (f == 3) rnext = chain_r_load(a, b, h, c + 2, nchunks);
                 }
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
                 if (c >= 0 && c < nchunks) {
                     const int nvalid = min(L, a.T - c * L);
-                    if (nvalid == L) form_run<DK, ISO, false>(X, sm, c & 1, c % 3, f, L);
-                    else form_run<DK, ISO, true>(X, sm, c & 1, c % 3, f, nvalid);
+                    if (nvalid == L) form_run<DK, VAR, false>(X, sm, c & 1, c % 3, f, L);
+                    else form_run<DK, VAR, true>(X, sm, c & 1, c % 3, f, nvalid);
                 }
                 bar();
                 if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, c % 3, f);
@@ -1134,7 +1243,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     settle(Y.kp[tt]);
                     settle(Y.qp[tt]);
                 }
-                if (!ISO) {
+                if (VAR == 0) {
                     settle(rnext);
                     if (f == 3) chain_r_store<DK>(sm, c + 2, rnext, min(L, a.T - (c + 2) * L), a.mu);
                 }
@@ -1144,7 +1253,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     }
 }
 
-template <int DK, bool ISO>
+template <int DK, int VAR>
 hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0) return hipSuccess;
@@ -1172,7 +1281,7 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, ISO>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1181,7 +1290,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 bool chunked_supports(const FwdArgs& a) {
-    if (a.variant != 0 && a.variant != 1) return false;  // per-channel-decay isotropic: recurrent kernel
     if (a.dtype != 1 || (a.dk != 64 && a.dk != 128) || a.dv % DVT != 0 || a.dv < DVT) return false;
     // 16-byte direct copies of k, alpha, omega and v rows, 16-byte loads of k
     // rows (isotropic), 8-byte stores of four output columns
@@ -1192,8 +1300,12 @@ bool chunked_supports(const FwdArgs& a) {
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
-    if (a.dk == 128) return a.variant == 1 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
-    return a.variant == 1 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    if (a.dk == 128) {
+        if (a.variant == 2) return launch_t<128, 2>(a, stream);
+        return a.variant == 1 ? launch_t<128, 1>(a, stream) : launch_t<128, 0>(a, stream);
+    }
+    if (a.variant == 2) return launch_t<64, 2>(a, stream);
+    return a.variant == 1 ? launch_t<64, 1>(a, stream) : launch_t<64, 0>(a, stream);
 }
 
 }  // namespace kdn

@@ -1,8 +1,8 @@
 """GPU parity of the isotropic variant with per-channel decay
 (KDN_ISOTROPIC_CHANNEL: memory decay diag(alpha), uncertainty scalar predicted
-with a = mean_i alpha_i^2) against the fp64 oracle.  Only the recurrent
-algorithm runs it; AUTO picks that and an explicit chunked call reports
-KDN_ERR_UNSUPPORTED.  Tolerances 1e-4 (fp32 inputs) / 2e-2 (bf16 inputs)."""
+with a = mean_i alpha_i^2) against the fp64 oracle, on the recurrent and the
+chunked kernels (the chunked one takes bf16 inputs only).
+Tolerances 1e-4 (fp32 inputs) / 2e-2 (bf16 inputs)."""
 import numpy as np
 import pytest
 
@@ -35,12 +35,17 @@ def run(dev, w, x, algo="auto", S0=None, p0=None):
     t = to_dev(x, w.dtype, dev)
     S0d = None if S0 is None else torch.from_numpy(S0).to(dev)
     p0d = None if p0 is None else torch.from_numpy(p0).to(dev)
-    o, S, p = kdn.forward(**t, mu=w.mu, variant="isochannel", S0=S0d, p0=p0d, algo=algo)
+    try:
+        o, S, p = kdn.forward(**t, mu=w.mu, variant="isochannel", S0=S0d, p0=p0d, algo=algo)
+    except kdn.KDNError as e:
+        if e.status == kdn.KDN_ERR_UNSUPPORTED and algo == "chunked" and w.dtype == "f32":
+            pytest.skip("the chunked kernel takes bf16 inputs")
+        raise
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()
 
 
-@pytest.mark.parametrize("algo", ["auto", "recurrent"])
+@pytest.mark.parametrize("algo", ["auto", "recurrent", "chunked"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 @pytest.mark.parametrize("T", [1, 65, 200])
@@ -53,22 +58,26 @@ def test_isochannel_forward(dev, algo, dtype, dk, dv, T):
     check(f"isoch/{algo}/{dtype}/dk{dk}/dv{dv}/T{T}", run(dev, w, x, algo), oracle_forward(w, x), dtype)
 
 
-def test_isochannel_with_initial_state(dev):
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_isochannel_with_initial_state(dev, algo):
     w = wl.Workload("isoch_init", "isochannel", "bf16", 3, 150, 2, 128, 128, 128.0, "uniform", 78, omega_loc=0.0)
     x = wl.forward_inputs(w)
     st = wl.decode_state(w.with_(B=3))
     assert st["p0"].shape == (3, 2)
-    check("isoch/init", run(dev, w, x, S0=st["S0"], p0=st["p0"]),
+    check(f"isoch/init/{algo}", run(dev, w, x, algo, S0=st["S0"], p0=st["p0"]),
           oracle_forward(w, x, S0=st["S0"], p0=st["p0"]), "bf16")
 
 
-def test_isochannel_chunked_is_unsupported(dev):
-    import kalman_delta_network_amd as kdn
-    w = wl.Workload("isoch_ch", "isochannel", "bf16", 1, 40, 1, 128, 128, 128.0, "one", 79)
+@pytest.mark.parametrize("shape", [(9, 97, 2, 128, 128, 0.0), (16, 40, 1, 128, 64, -1.0), (1, 130, 1, 64, 64, 2.0)],
+                         ids=lambda s: "b{}_t{}_h{}_dk{}_dv{}_a{}".format(*s))
+def test_isochannel_chunked_shapes(dev, shape):
+    # ragged item groups, one head, strong per-channel decay
+    B, T, H, dk, dv, aloc = shape
+    w = wl.Workload("isoch_shape", "isochannel", "bf16", B, T, H, dk, dv, float(dk), "uniform", 950 + B + T,
+                    alpha_loc=aloc, omega_loc=-1.0)
     x = wl.forward_inputs(w)
-    with pytest.raises(kdn.KDNError) as e:
-        run(dev, w, x, algo="chunked")
-    assert e.value.status == kdn.KDN_ERR_UNSUPPORTED
+    check(f"isoch/chunked/b{B}/t{T}/h{H}/dk{dk}/dv{dv}/a{aloc}", run(dev, w, x, "chunked"),
+          oracle_forward(w, x), "bf16")
 
 
 def test_isochannel_decode_steps(dev):
@@ -91,7 +100,8 @@ def test_isochannel_decode_steps(dev):
               {"o": ref["o"], "S": Sr, "p": pr}, "bf16")
 
 
-def test_isochannel_packed_batch(dev):
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_isochannel_packed_batch(dev, algo):
     import torch
     import kalman_delta_network_amd as kdn
     lengths = [1, 33, 0, 90, 64]
@@ -100,12 +110,12 @@ def test_isochannel_packed_batch(dev):
     x = wl.varlen_inputs(w, lengths)
     t = to_dev(x, "bf16", dev)
     cu = torch.from_numpy(x["cu_seqlens"]).to(dev)
-    o, S, p = kdn.forward_varlen(**t, cu_seqlens=cu, mu=w.mu, variant="isochannel",
+    o, S, p = kdn.forward_varlen(**t, cu_seqlens=cu, mu=w.mu, variant="isochannel", algo=algo,
                                  order=torch.from_numpy(kdn.longest_first(x["cu_seqlens"])).to(dev))
     torch.cuda.synchronize()
     ref = oracle.forward_varlen(**{n: x[n] for n in TOKEN_INPUTS}, c0=x["c0"], mu=w.mu,
                                 cu_seqlens=x["cu_seqlens"], variant="isochannel")
-    check("isoch/varlen", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")
+    check(f"isoch/varlen/{algo}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")
 
 
 def test_isochannel_full_size_sampled(dev):
