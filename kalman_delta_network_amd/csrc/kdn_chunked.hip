@@ -34,6 +34,10 @@
 //  - Isotropic variant: one scalar per head, so the maps of a chunk's 32
 //    tokens (one per lane) are composed as 2 x 2 matrix products by an
 //    inclusive cross-lane scan (5 shuffle levels, renormalised each level).
+//  - Isotropic variant with per-channel decay (the general form of that
+//    sentence: diag(alpha) on the memory, a = mean_i alpha_i^2 on the
+//    uncertainty scalar): the isotropic scan with a, plus a decay chain
+//    (wave 1) for the per-channel cumulative decays.
 //
 // Workgroup = one (batch, head) pair and 64 value columns, 8 waves in roles:
 //   waves 0,1      "chain":     uncertainty recurrence of chunk c+2 -> scaled
