@@ -559,20 +559,19 @@ __device__ __forceinline__ void chain_decay_load(DecayRegs<DK>& X, const Args& a
     }
 }
 
-// g_t,i = prod_{s <= t} alpha_s,i in the chunk (padding tokens: alpha = 1),
-// stored as the diagonal variant's chain stores it (8-token groups) with g_L
-template <int DK>
+// g_t,i = prod_{s <= t} alpha_s,i for the chunk's tokens [T0, T1) (padding
+// tokens: alpha = 1), carried in g across the two calls of a chunk; stored as
+// the diagonal variant's chain stores it (8-token groups), g_L at the end
+template <int DK, int T0, int T1, bool MASK>
 __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>& sm, int buf, int nvalid,
-                                                int gring) {
+                                                int gring, float (&g)[DK / 64]) {
     constexpr int CPL = DK / 64;
     const int i0 = CPL * (threadIdx.x & 63);
-    float g[CPL], gv[CPL][2];
+    float gv[CPL][2];
     uint32_t gp[CPL][4];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) g[cc] = 1.f;
-#pragma unroll
-    for (int t = 0; t < L; ++t) {
-        const bool ok = t < nvalid;
+    for (int t = T0; t < T1; ++t) {
+        const bool ok = !MASK || t < nvalid;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const float al = cc ? bf_hi(X.ap[t]) : bf_lo(X.ap[t]);
@@ -584,8 +583,9 @@ __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>
                     u4{gp[cc][0], gp[cc][1], gp[cc][2], gp[cc][3]};
         }
     }
+    if (T1 == L)
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) sm.gL[gring][i0 + cc] = g[cc];
+        for (int cc = 0; cc < CPL; ++cc) sm.gL[gring][i0 + cc] = g[cc];
 }
 
 // ---------------------------------------------------------------------------
@@ -1135,12 +1135,25 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     DecayRegs<DK>& X = half ? B : A;
                     DecayRegs<DK>& Y = half ? A : B;
                     const int c = it + half;
+                    // tokens 0..15 of chunk c in the first segment, then the
+                    // loads of chunk c + 1 (into the other register set),
+                    // tokens 16..31 in the second segment
+                    const int nvalid = min(L, a.T - c * L);
+                    float g[DK / 64];
+#pragma unroll
+                    for (int cc = 0; cc < DK / 64; ++cc) g[cc] = 1.f;
                     if (VAR == 2) {
-                        // next chunk's loads after this chunk's registers are consumed
-                        if (c < nchunks) chain_decay_run<DK>(X, sm, c & 1, min(L, a.T - c * L), c % 3);
+                        if (c < nchunks) {
+                            if (nvalid == L) chain_decay_run<DK, 0, L / 2, false>(X, sm, c & 1, L, c % 3, g);
+                            else chain_decay_run<DK, 0, L / 2, true>(X, sm, c & 1, nvalid, c % 3, g);
+                        }
                         chain_decay_load<DK>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
+                    if (VAR == 2 && c < nchunks) {
+                        if (nvalid == L) chain_decay_run<DK, L / 2, L, false>(X, sm, c & 1, L, c % 3, g);
+                        else chain_decay_run<DK, L / 2, L, true>(X, sm, c & 1, nvalid, c % 3, g);
+                    }
                     bar();
                 }
             }
