@@ -484,12 +484,19 @@ __device__ __forceinline__ float row_sumsq(const u4 (&r)[8]) {
     return n + __shfl_xor(n, 32, 64);
 }
 
+// the row sums a chunk's scan needs: |k|^2 and (per-channel decay) the
+// trace projection mean_i alpha_i^2, of token lane & 31
+template <int DK, int VAR>
+__device__ __forceinline__ void chain_iso_sums(const ChainIsoRegs<VAR>& X, float& n, float& a2) {
+    n = row_sumsq<DK>(X.kr);
+    if constexpr (VAR == 2) a2 = row_sumsq<DK>(X.ar) * (1.f / float(DK));
+}
+
 template <int DK, int VAR>
 __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<DK>& sm, int buf, float mu,
-                                              float& bprev, int nvalid, int gring) {
+                                              float& bprev, int nvalid, int gring, float n, float a2) {
     const int lane = threadIdx.x & 63;
     const bool ok = (lane & 31) < nvalid;
-    const float n = row_sumsq<DK>(X.kr);
     const float w = ok ? bf1(bf16_t(X.w)) * (1.f / float(DK)) : 0.f;
     const float rt = ok ? bf1(bf16_t(X.rv)) : 1.f;
     const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
@@ -497,7 +504,7 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<D
     // projection mean_i alpha_i^2 (padding tokens: 1)
     float al = 1.f, asq;
     if constexpr (VAR == 2) {
-        asq = ok ? row_sumsq<DK>(X.ar) * (1.f / float(DK)) : 1.f;
+        asq = ok ? a2 : 1.f;
     } else {
         al = ok ? bf1(bf16_t(X.al)) : 1.f;
         asq = al * al;
@@ -1162,6 +1169,10 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             settle(bprev);
             ChainIsoRegs<VAR> A, B;
             chain_iso_load<DK, VAR>(A, a, b, h, 0, nchunks);
+            // the row sums of the next chunk are formed in the second segment
+            // (this wave's idle one), from the registers just loaded
+            float n = 0.f, a2 = 1.f;
+            chain_iso_sums<DK, VAR>(A, n, a2);
             for (int it = 0; it < nit; it += 2) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -1174,10 +1185,12 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                         // address temporaries would be placed in registers of
                         // loads still in flight, and the compiler would wait
                         // for those loads (a full memory round trip) first
-                        if (c < nchunks) chain_iso_run<DK, VAR>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3);
+                        if (c < nchunks)
+                            chain_iso_run<DK, VAR>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3, n, a2);
                         chain_iso_load<DK, VAR>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
+                    chain_iso_sums<DK, VAR>(Y, n, a2);
                     bar();
                 }
             }
