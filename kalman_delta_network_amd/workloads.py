@@ -181,3 +181,20 @@ def decode_tokens(w: Workload, step: int) -> dict:
     q,k,alpha,omega [N,H,dk] (isotropic alpha, omega [N,H]), v [N,H,dv], r [N,H]."""
     rng = np.random.default_rng([w.seed, 0x70, step])
     return _draw_tokens(rng, w, (w.B, w.H))
+
+
+def backward_cotangents(w: Workload, with_state: bool = True) -> dict:
+    """Cotangents of one backward call: dO ~ N(0, 1) [B,T,H,dv] (rounded to
+    bf16 for bf16 workloads), and with ``with_state`` dS_T ~ N(0, 0.1)
+    [B,H,dk,dv] and dp_T ~ N(0, 0.1) [B,H,dk] (isotropic forms [B,H]) in
+    float32; without it those two are None."""
+    rng = np.random.default_rng([w.seed, 0xBA])
+    dO = _normal(rng, (w.B, w.T, w.H, w.dv))
+    if w.dtype == "bf16":
+        dO = round_bf16(dO)
+    out = {"dO": dO, "dS_T": None, "dp_T": None}
+    if with_state:
+        out["dS_T"] = _normal(rng, (w.B, w.H, w.dk, w.dv), 0.0, 0.1)
+        pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)
+        out["dp_T"] = _normal(rng, pshape, 0.0, 0.1)
+    return out

@@ -13,6 +13,9 @@ it.
   variant).
 * ``forward_varlen`` runs packed variable-length batches through the same
   recurrence, one sequence at a time.
+* ``backward`` is the reverse-mode adjoint of the same recurrence (the
+  gradients a training step needs), pinned by central finite differences of
+  the forward.
 * ``dense`` holds the brute-force dense-covariance filter (Bayesian Layer
   page, section 2.2, Proposition 1) used to pin the oracle.
 
@@ -62,6 +65,8 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = stp
             fn.restype = I
+        lib.kdn_oracle_backward.argtypes = [I, I, I, I, I, I] + [P] * 7 + [D] + [P] * 14
+        lib.kdn_oracle_backward.restype = I
         lib.kdn_oracle_num_threads.restype = I
         _lib = lib
     return _lib
@@ -72,8 +77,9 @@ def num_threads() -> int:
     return int(_load().kdn_oracle_num_threads())
 
 
-def _f32(x):
-    return np.ascontiguousarray(x, dtype=np.float32)
+def _in(x):
+    """Token inputs as contiguous float64 (bf16 / fp32 values widen exactly)."""
+    return np.ascontiguousarray(x, dtype=np.float64)
 
 
 def _f64(x):
@@ -85,11 +91,11 @@ def _ptr(a):
 
 
 def _forward(name, q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False):
-    q, k, v, alpha, omega, r = (_f32(x) for x in (q, k, v, alpha, omega, r))
+    q, k, v, alpha, omega, r = (_in(x) for x in (q, k, v, alpha, omega, r))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     iso = name.endswith(("iso", "isoc"))
-    c0 = _f32(np.broadcast_to(np.asarray(c0, np.float32), (H,)))
+    c0 = _in(np.broadcast_to(np.asarray(c0, np.float64), (H,)))
     S0, p0 = _f64(S0), _f64(p0)
     o = np.zeros((B, T, H, dv))
     S_T = np.zeros((B, H, dk, dv))
@@ -158,7 +164,7 @@ def forward_isoc(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, trace=False
 
 
 def _step(name, q, k, v, alpha, omega, r, mu, S, p):
-    q, k, v, alpha, omega, r = (_f32(x) for x in (q, k, v, alpha, omega, r))
+    q, k, v, alpha, omega, r = (_in(x) for x in (q, k, v, alpha, omega, r))
     N, H, dk = q.shape
     dv = v.shape[-1]
     S = np.array(S, dtype=np.float64, order="C", copy=True)
@@ -185,3 +191,32 @@ def step_iso(q, k, v, alpha, omega, r, mu, S, p):
 def step_isoc(q, k, v, alpha, omega, r, mu, S, p):
     """Per-channel-decay isotropic decode step: alpha [N,H,dk]; omega, r [N,H]; p [N,H]."""
     return _step("kdn_oracle_step_isoc", q, k, v, alpha, omega, r, mu, S, p)
+
+
+_VARIANTS = {"diagonal": 0, "isotropic": 1, "isochannel": 2}
+
+
+def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, S0=None, p0=None,
+             variant="diagonal"):
+    """Gradients of L = sum(dO*o) + sum(dS_T*S_T) + sum(dp_T*p_T) for the
+    forward of ``variant`` on these inputs (any of dO, dS_T, dp_T may be None
+    for zero).  Returns dict dq, dk, dv, dalpha, domega, dr (input layouts),
+    dS0 [B,H,dk,dv], dp0 [B,H,dk] (isotropic forms [B,H]) and dc0 [H] (the sum
+    of dp0 over batch and channels: the c0 gradient when p0 is None)."""
+    var = _VARIANTS[variant]
+    q, k, v, alpha, omega, r = (_in(x) for x in (q, k, v, alpha, omega, r))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    c0 = _in(np.broadcast_to(np.asarray(c0, np.float64), (H,)))
+    S0, p0, dO, dS_T, dp_T = (_f64(x) for x in (S0, p0, dO, dS_T, dp_T))
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "dalpha": np.zeros_like(alpha), "domega": np.zeros_like(omega), "dr": np.zeros_like(r),
+           "dS0": np.zeros((B, H, dk, dv)), "dp0": np.zeros((B, H, dk) if var == 0 else (B, H)),
+           "dc0": np.zeros(H)}
+    rc = _load().kdn_oracle_backward(
+        var, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0),
+        float(mu), _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T), _ptr(dp_T),
+        *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dp0", "dc0")))
+    if rc != 0:
+        raise ValueError(f"backward: bad arguments (rc={rc})")
+    return out

@@ -34,8 +34,9 @@
  * diag(alpha), omega and r are scalars per head-token, and the trace
  * projection uses a = (1/d_k) sum_i alpha_i^2; gain and posterior as above.
  *
- * Inputs arrive as float arrays holding exactly the values the GPU receives
- * (bf16 values widen to float without loss); all arithmetic is double.
+ * Inputs arrive as double arrays holding exactly the values the GPU receives
+ * (bf16 and fp32 values widen to double without loss); all arithmetic is
+ * double.
  * Layouts (row-major, contiguous):
  *   q, k, alpha, omega : [B,T,H,dk]   (isotropic alpha, omega: [B,T,H];
  *                                     per-channel-decay isotropic: omega [B,T,H])
@@ -57,9 +58,9 @@
 
 /* One (b,h) recurrence of the Diagonal KDN, token by token. */
 static void diag_head(int b, int h, int T, int H, int dk, int dv,
-                      const float* q, const float* k, const float* v,
-                      const float* alpha, const float* omega, const float* r,
-                      const float* c0, double mu, const double* S0,
+                      const double* q, const double* k, const double* v,
+                      const double* alpha, const double* omega, const double* r,
+                      const double* c0, double mu, const double* S0,
                       const double* p0, double* o, double* S_T, double* p_T,
                       double* tr_phat, double* tr_kappa, double* tr_p) {
     (void)T;
@@ -80,11 +81,11 @@ static void diag_head(int b, int h, int T, int H, int dk, int dv,
 
     for (int t = 0; t < T; ++t) {
         const size_t tok = IDX_TOK(b, t, h, 0, T, H);
-        const float* kt = k + tok * dk;
-        const float* qt = q + tok * dk;
-        const float* vt = v + tok * dv;
-        const float* at = alpha + tok * dk;
-        const float* wt = omega + tok * dk;
+        const double* kt = k + tok * dk;
+        const double* qt = q + tok * dk;
+        const double* vt = v + tok * dv;
+        const double* at = alpha + tok * dk;
+        const double* wt = omega + tok * dk;
         const double rt = (double)r[tok];
 
         /* predict: p_hat = alpha^2 p + omega */
@@ -135,9 +136,9 @@ static void diag_head(int b, int h, int T, int H, int dk, int dv,
 
 /* One (b,h) recurrence of the Isotropic KDN (alpha, omega scalar per head-token). */
 static void iso_head(int b, int h, int T, int H, int dk, int dv,
-                     const float* q, const float* k, const float* v,
-                     const float* alpha, const float* omega, const float* r,
-                     const float* c0, double mu, const double* S0,
+                     const double* q, const double* k, const double* v,
+                     const double* alpha, const double* omega, const double* r,
+                     const double* c0, double mu, const double* S0,
                      const double* p0, double* o, double* S_T, double* p_T,
                      double* tr_phat, double* tr_kappa, double* tr_p) {
     const size_t state = ((size_t)b * H + h);
@@ -148,9 +149,9 @@ static void iso_head(int b, int h, int T, int H, int dk, int dv,
 
     for (int t = 0; t < T; ++t) {
         const size_t tok = IDX_TOK(b, t, h, 0, T, H);
-        const float* kt = k + tok * dk;
-        const float* qt = q + tok * dk;
-        const float* vt = v + tok * dv;
+        const double* kt = k + tok * dk;
+        const double* qt = q + tok * dk;
+        const double* vt = v + tok * dv;
         const double a = alpha[tok];
         const double w = omega[tok];
         const double rt = r[tok];
@@ -189,9 +190,9 @@ static void iso_head(int b, int h, int T, int H, int dk, int dv,
 /* One (b,h) recurrence of the Isotropic KDN with per-channel decay: alpha
  * [.., dk], omega and r scalars per head-token. */
 static void isoc_head(int b, int h, int T, int H, int dk, int dv,
-                      const float* q, const float* k, const float* v,
-                      const float* alpha, const float* omega, const float* r,
-                      const float* c0, double mu, const double* S0,
+                      const double* q, const double* k, const double* v,
+                      const double* alpha, const double* omega, const double* r,
+                      const double* c0, double mu, const double* S0,
                       const double* p0, double* o, double* S_T, double* p_T,
                       double* tr_phat, double* tr_kappa, double* tr_p) {
     const size_t state = ((size_t)b * H + h);
@@ -202,10 +203,10 @@ static void isoc_head(int b, int h, int T, int H, int dk, int dv,
 
     for (int t = 0; t < T; ++t) {
         const size_t tok = IDX_TOK(b, t, h, 0, T, H);
-        const float* kt = k + tok * dk;
-        const float* qt = q + tok * dk;
-        const float* vt = v + tok * dv;
-        const float* at = alpha + tok * dk;
+        const double* kt = k + tok * dk;
+        const double* qt = q + tok * dk;
+        const double* vt = v + tok * dv;
+        const double* at = alpha + tok * dk;
         const double w = omega[tok];
         const double rt = r[tok];
 
@@ -244,14 +245,14 @@ static void isoc_head(int b, int h, int T, int H, int dk, int dv,
     free(S); free(delta);
 }
 
-typedef void (*head_fn)(int, int, int, int, int, int, const float*, const float*, const float*,
-                        const float*, const float*, const float*, const float*, double,
+typedef void (*head_fn)(int, int, int, int, int, int, const double*, const double*, const double*,
+                        const double*, const double*, const double*, const double*, double,
                         const double*, const double*, double*, double*, double*, double*,
                         double*, double*);
 
 static int run_heads(head_fn fn, int B, int T, int H, int dk, int dv,
-                     const float* q, const float* k, const float* v, const float* alpha,
-                     const float* omega, const float* r, const float* c0, double mu,
+                     const double* q, const double* k, const double* v, const double* alpha,
+                     const double* omega, const double* r, const double* c0, double mu,
                      const double* S0, const double* p0, double* o, double* S_T, double* p_T,
                      double* tr_phat, double* tr_kappa, double* tr_p) {
     if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return 1;
@@ -266,9 +267,9 @@ static int run_heads(head_fn fn, int B, int T, int H, int dk, int dv,
 }
 
 int kdn_oracle_forward_diag(int B, int T, int H, int dk, int dv,
-                            const float* q, const float* k, const float* v,
-                            const float* alpha, const float* omega, const float* r,
-                            const float* c0, double mu, const double* S0, const double* p0,
+                            const double* q, const double* k, const double* v,
+                            const double* alpha, const double* omega, const double* r,
+                            const double* c0, double mu, const double* S0, const double* p0,
                             double* o, double* S_T, double* p_T,
                             double* tr_phat, double* tr_kappa, double* tr_p) {
     return run_heads(diag_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
@@ -276,9 +277,9 @@ int kdn_oracle_forward_diag(int B, int T, int H, int dk, int dv,
 }
 
 int kdn_oracle_forward_iso(int B, int T, int H, int dk, int dv,
-                           const float* q, const float* k, const float* v,
-                           const float* alpha, const float* omega, const float* r,
-                           const float* c0, double mu, const double* S0, const double* p0,
+                           const double* q, const double* k, const double* v,
+                           const double* alpha, const double* omega, const double* r,
+                           const double* c0, double mu, const double* S0, const double* p0,
                            double* o, double* S_T, double* p_T,
                            double* tr_phat, double* tr_kappa, double* tr_p) {
     return run_heads(iso_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
@@ -286,9 +287,9 @@ int kdn_oracle_forward_iso(int B, int T, int H, int dk, int dv,
 }
 
 int kdn_oracle_forward_isoc(int B, int T, int H, int dk, int dv,
-                            const float* q, const float* k, const float* v,
-                            const float* alpha, const float* omega, const float* r,
-                            const float* c0, double mu, const double* S0, const double* p0,
+                            const double* q, const double* k, const double* v,
+                            const double* alpha, const double* omega, const double* r,
+                            const double* c0, double mu, const double* S0, const double* p0,
                             double* o, double* S_T, double* p_T,
                             double* tr_phat, double* tr_kappa, double* tr_p) {
     return run_heads(isoc_head, B, T, H, dk, dv, q, k, v, alpha, omega, r, c0, mu, S0, p0,
@@ -302,8 +303,8 @@ int kdn_oracle_forward_isoc(int B, int T, int H, int dk, int dv,
  * inputs use the forward layouts with T = 1.
  */
 static int step_common(head_fn fn, int pdim, int N, int H, int dk, int dv,
-                       const float* q, const float* k, const float* v, const float* alpha,
-                       const float* omega, const float* r, double mu, double* S, double* p,
+                       const double* q, const double* k, const double* v, const double* alpha,
+                       const double* omega, const double* r, double mu, double* S, double* p,
                        double* o) {
     if (!S || !p) return 1;
     const size_t ns = (size_t)N * H * dk * dv, np_ = (size_t)N * H * pdim;
@@ -317,20 +318,20 @@ static int step_common(head_fn fn, int pdim, int N, int H, int dk, int dv,
     return rc;
 }
 
-int kdn_oracle_step_diag(int N, int H, int dk, int dv, const float* q, const float* k,
-                         const float* v, const float* alpha, const float* omega, const float* r,
+int kdn_oracle_step_diag(int N, int H, int dk, int dv, const double* q, const double* k,
+                         const double* v, const double* alpha, const double* omega, const double* r,
                          double mu, double* S, double* p, double* o) {
     return step_common(diag_head, dk, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
 }
 
-int kdn_oracle_step_iso(int N, int H, int dk, int dv, const float* q, const float* k,
-                        const float* v, const float* alpha, const float* omega, const float* r,
+int kdn_oracle_step_iso(int N, int H, int dk, int dv, const double* q, const double* k,
+                        const double* v, const double* alpha, const double* omega, const double* r,
                         double mu, double* S, double* p, double* o) {
     return step_common(iso_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
 }
 
-int kdn_oracle_step_isoc(int N, int H, int dk, int dv, const float* q, const float* k,
-                         const float* v, const float* alpha, const float* omega, const float* r,
+int kdn_oracle_step_isoc(int N, int H, int dk, int dv, const double* q, const double* k,
+                         const double* v, const double* alpha, const double* omega, const double* r,
                          double mu, double* S, double* p, double* o) {
     return step_common(isoc_head, 1, N, H, dk, dv, q, k, v, alpha, omega, r, mu, S, p, o);
 }
@@ -345,4 +346,236 @@ int kdn_oracle_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/*
+ * Backward pass (reverse-mode adjoint of the recurrence above), for training.
+ *
+ * For cotangents dO [B,T,H,dv], dS_T [B,H,dk,dv] and dp_T [B,H,dk]
+ * (isotropic forms [B,H]), both nullable (= 0), the scalar being
+ * differentiated is
+ *     L = sum dO (.) o + sum dS_T (.) S_T + sum dp_T (.) p_T,
+ * and the outputs are dL/d(q, k, v, alpha, omega, r) in the input layouts,
+ * dL/dS0 [B,H,dk,dv] and dL/dp0 [B,H,dk] (isotropic [B,H]).  When p0 is NULL
+ * (p_0 = c0[h] on every channel) dL/dc0[h] is the sum of dL/dp0 over the
+ * batch and the channels; dc0 [H] receives that sum in every case.
+ *
+ * Plain two-sweep form: a forward sweep stores every pre-token memory
+ * S_{t-1} and uncertainty p_{t-1}; the reverse sweep walks t = T-1 .. 0 and
+ * applies the chain rule to each equation of the token step in reverse
+ * order (readout, residual write, predicted mean, gain, posterior,
+ * predict).  `var` is 0 diagonal, 1 isotropic, 2 isotropic with
+ * per-channel decay.
+ */
+static void backward_head(int var, int b, int h, int T, int H, int dk, int dv,
+                          const double* q, const double* k, const double* v,
+                          const double* alpha, const double* omega, const double* r,
+                          const double* c0, double mu, const double* S0, const double* p0,
+                          const double* dO, const double* dS_T, const double* dp_T,
+                          double* dq, double* dkk, double* dvv, double* dalpha,
+                          double* domega, double* dr, double* dS0, double* dp0) {
+    const size_t state = ((size_t)b * H + h);
+    const size_t SZ = (size_t)dk * dv;
+    const int pd = var == 0 ? dk : 1;                  /* uncertainty entries */
+    const int ad = var == 1 ? 1 : dk;                  /* decay entries per token */
+    const int wd = var == 0 ? dk : 1;                  /* process-noise entries */
+    double* Sall = (double*)malloc(sizeof(double) * SZ * ((size_t)T + 1));
+    double* pall = (double*)malloc(sizeof(double) * (size_t)pd * ((size_t)T + 1));
+    double* Sh = (double*)malloc(sizeof(double) * SZ);
+    double* dS = (double*)malloc(sizeof(double) * SZ);
+    double* dSh = (double*)malloc(sizeof(double) * SZ);
+    double* ph = (double*)malloc(sizeof(double) * dk);
+    double* kap = (double*)malloc(sizeof(double) * dk);
+    double* dkap = (double*)malloc(sizeof(double) * dk);
+    double* dp = (double*)malloc(sizeof(double) * pd);
+    double* delta = (double*)malloc(sizeof(double) * dv);
+    double* ddel = (double*)malloc(sizeof(double) * dv);
+
+    /* ---- forward sweep: store S_{t-1}, p_{t-1} for every token ---- */
+    for (size_t e = 0; e < SZ; ++e) Sall[e] = S0 ? S0[state * SZ + e] : 0.0;
+    for (int i = 0; i < pd; ++i) pall[i] = p0 ? p0[state * pd + i] : c0[h];
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = IDX_TOK(b, t, h, 0, T, H);
+        const double* kt = k + tok * dk;
+        const double* at = alpha + tok * ad;
+        const double rt = r[tok];
+        const double* S = Sall + SZ * t;
+        double* Sn = Sall + SZ * (t + 1);
+        const double* p = pall + (size_t)pd * t;
+        double* pn = pall + (size_t)pd * (t + 1);
+        if (var == 0) {
+            double s = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                ph[i] = at[i] * at[i] * p[i] + omega[tok * dk + i];
+                s += ph[i] * kt[i] * kt[i];
+            }
+            for (int i = 0; i < dk; ++i) kap[i] = ph[i] * kt[i] / (rt + s);
+            for (int i = 0; i < dk; ++i) pn[i] = ph[i] / (1.0 + (mu / rt) * kt[i] * kt[i] * ph[i]);
+        } else {
+            double a = 0.0, n = 0.0;
+            if (var == 1) a = at[0] * at[0];
+            else { for (int i = 0; i < dk; ++i) a += at[i] * at[i]; a /= dk; }
+            for (int i = 0; i < dk; ++i) n += kt[i] * kt[i];
+            const double bh = a * p[0] + omega[tok] / dk;
+            const double beta = bh / (rt + bh * n);
+            for (int i = 0; i < dk; ++i) kap[i] = beta * kt[i];
+            pn[0] = bh / (1.0 + (mu / ((double)dk * rt)) * n * bh);
+        }
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += at[var == 1 ? 0 : i] * S[(size_t)i * dv + j] * kt[i];
+            delta[j] = v[tok * dv + j] - pred;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sn[(size_t)i * dv + j] = at[var == 1 ? 0 : i] * S[(size_t)i * dv + j] + kap[i] * delta[j];
+    }
+
+    /* ---- reverse sweep ---- */
+    for (size_t e = 0; e < SZ; ++e) dS[e] = dS_T ? dS_T[state * SZ + e] : 0.0;
+    for (int i = 0; i < pd; ++i) dp[i] = dp_T ? dp_T[state * pd + i] : 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+        const size_t tok = IDX_TOK(b, t, h, 0, T, H);
+        const double* kt = k + tok * dk;
+        const double* qt = q + tok * dk;
+        const double* at = alpha + tok * ad;
+        const double* dot = dO ? dO + tok * dv : NULL;
+        const double rt = r[tok];
+        const double* S = Sall + SZ * t;        /* S_{t-1} */
+        const double* Sn = Sall + SZ * (t + 1); /* S_t, the memory read out at t */
+        const double* p = pall + (size_t)pd * t;
+        const double* pn = pall + (size_t)pd * (t + 1);
+
+        /* recompute the token's forward quantities from S_{t-1}, p_{t-1} */
+        double s = 0.0, n = 0.0, a = 0.0, bh = 0.0, beta = 0.0;
+        if (var == 0) {
+            for (int i = 0; i < dk; ++i) {
+                ph[i] = at[i] * at[i] * p[i] + omega[tok * dk + i];
+                s += ph[i] * kt[i] * kt[i];
+            }
+            for (int i = 0; i < dk; ++i) kap[i] = ph[i] * kt[i] / (rt + s);
+        } else {
+            if (var == 1) a = at[0] * at[0];
+            else { for (int i = 0; i < dk; ++i) a += at[i] * at[i]; a /= dk; }
+            for (int i = 0; i < dk; ++i) n += kt[i] * kt[i];
+            bh = a * p[0] + omega[tok] / dk;
+            beta = bh / (rt + bh * n);
+            for (int i = 0; i < dk; ++i) kap[i] = beta * kt[i];
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) Sh[(size_t)i * dv + j] = at[var == 1 ? 0 : i] * S[(size_t)i * dv + j];
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += Sh[(size_t)i * dv + j] * kt[i];
+            delta[j] = v[tok * dv + j] - pred;
+        }
+
+        /* readout o = S_t^T q */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                const double g = dot ? dot[j] : 0.0;
+                acc += Sn[(size_t)i * dv + j] * g;
+                dS[(size_t)i * dv + j] += qt[i] * g;
+            }
+            dq[tok * dk + i] = acc;
+        }
+        /* residual write S_t = S_hat + kappa delta^T, delta = v - S_hat^T k */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += dS[(size_t)i * dv + j] * kap[i];
+            ddel[j] = acc;
+            dvv[tok * dv + j] = acc;
+        }
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0, acck = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += dS[(size_t)i * dv + j] * delta[j];
+                dSh[(size_t)i * dv + j] = dS[(size_t)i * dv + j] - kt[i] * ddel[j];
+                acck -= Sh[(size_t)i * dv + j] * ddel[j];
+            }
+            dkap[i] = acc;
+            dkk[tok * dk + i] = acck;
+        }
+        /* predicted mean S_hat = diag(alpha) S_{t-1} (scalar alpha: alpha S_{t-1}) */
+        double dasum = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += S[(size_t)i * dv + j] * dSh[(size_t)i * dv + j];
+                dS[(size_t)i * dv + j] = at[var == 1 ? 0 : i] * dSh[(size_t)i * dv + j];
+            }
+            if (var == 1) dasum += acc;
+            else dalpha[tok * dk + i] = acc;
+        }
+
+        if (var == 0) {
+            /* gain kappa_i = p_hat_i k_i / d, d = r + sum p_hat k^2;
+             * posterior p_i = p_hat_i / (1 + u_i p_hat_i), u_i = (mu/r) k_i^2;
+             * predict p_hat = alpha^2 p + omega */
+            const double d = rt + s;
+            double dd = 0.0, drr = 0.0;
+            for (int i = 0; i < dk; ++i) dd -= dkap[i] * kap[i] / d;
+            for (int i = 0; i < dk; ++i) {
+                const double u = (mu / rt) * kt[i] * kt[i];
+                const double den = 1.0 + u * ph[i];
+                const double du = -dp[i] * pn[i] * pn[i];
+                const double dph = dp[i] / (den * den) + dkap[i] * kt[i] / d + dd * kt[i] * kt[i];
+                drr += du * (-mu * kt[i] * kt[i] / (rt * rt));
+                dkk[tok * dk + i] += dkap[i] * ph[i] / d + 2.0 * dd * ph[i] * kt[i]
+                                     + 2.0 * du * (mu / rt) * kt[i];
+                dalpha[tok * dk + i] += 2.0 * dph * at[i] * p[i];
+                domega[tok * dk + i] = dph;
+                dp[i] = dph * at[i] * at[i];
+            }
+            dr[tok] = dd + drr;
+        } else {
+            /* gain beta = b_hat / (r + b_hat n), n = |k|^2, kappa = beta k;
+             * posterior b = b_hat / (1 + c n b_hat), c = mu / (d_k r);
+             * predict b_hat = a b + omega / d_k */
+            const double dg = rt + bh * n;
+            const double c = mu / ((double)dk * rt);
+            const double dpn = 1.0 + c * n * bh;
+            const double bt = pn[0];
+            double dbeta = 0.0;
+            for (int i = 0; i < dk; ++i) dbeta += dkap[i] * kt[i];
+            const double dbh = dbeta * rt / (dg * dg) + dp[0] / (dpn * dpn);
+            const double dn = dbeta * (-bh * bh / (dg * dg)) - dp[0] * bt * bt * c;
+            dr[tok] = dbeta * (-bh / (dg * dg)) + dp[0] * bt * bt * c * n / rt;
+            for (int i = 0; i < dk; ++i) dkk[tok * dk + i] += beta * dkap[i] + 2.0 * dn * kt[i];
+            if (var == 1) dalpha[tok] = dasum + 2.0 * dbh * at[0] * p[0];
+            else for (int i = 0; i < dk; ++i) dalpha[tok * dk + i] += dbh * p[0] * 2.0 * at[i] / dk;
+            domega[tok] = dbh / dk;
+            dp[0] = dbh * a;
+        }
+    }
+    for (size_t e = 0; e < SZ; ++e) dS0[state * SZ + e] = dS[e];
+    for (int i = 0; i < pd; ++i) dp0[state * pd + i] = dp[i];
+    free(Sall); free(pall); free(Sh); free(dS); free(dSh); free(ph); free(kap); free(dkap);
+    free(dp); free(delta); free(ddel);
+}
+
+int kdn_oracle_backward(int var, int B, int T, int H, int dk, int dv,
+                        const double* q, const double* k, const double* v,
+                        const double* alpha, const double* omega, const double* r,
+                        const double* c0, double mu, const double* S0, const double* p0,
+                        const double* dO, const double* dS_T, const double* dp_T,
+                        double* dq, double* dk_out, double* dv_out, double* dalpha,
+                        double* domega, double* dr, double* dS0, double* dp0, double* dc0) {
+    if (var < 0 || var > 2 || B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return 1;
+    if (!q || !k || !v || !alpha || !omega || !r || (!c0 && !p0)) return 1;
+    if (!dq || !dk_out || !dv_out || !dalpha || !domega || !dr || !dS0 || !dp0 || !dc0) return 1;
+    const long units = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u)
+        backward_head(var, (int)(u / H), (int)(u % H), T, H, dk, dv, q, k, v, alpha, omega, r, c0,
+                      mu, S0, p0, dO, dS_T, dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0);
+    const int pd = var == 0 ? dk : 1;
+    for (int h = 0; h < H; ++h) {
+        double acc = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int i = 0; i < pd; ++i) acc += dp0[((size_t)b * H + h) * pd + i];
+        dc0[h] = acc;
+    }
+    return 0;
 }
