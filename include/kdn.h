@@ -74,7 +74,8 @@ enum kdn_status {
     KDN_ERR_UNSUPPORTED = 3, /* unsupported variant, dtype, d_k, d_v or algorithm */
     KDN_ERR_VALUE = 4,       /* mu is negative or not finite */
     KDN_ERR_HIP = 5,         /* the HIP runtime refused a launch */
-    KDN_ERR_ALIAS = 6        /* an output overlaps an input it may not overlap */
+    KDN_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap */
+    KDN_ERR_WORKSPACE = 7    /* the workspace is missing, too small or misaligned */
 };
 /* forward algorithms (kdn_forward_algo).  The chunked algorithm takes bf16
  * inputs (dk and dv are 64 or 128 for every algorithm), q, k, v, alpha and omega
@@ -182,7 +183,54 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
              const void* r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
              float* S, float* p, void* o, void* stream);
 
-/* Host-only argument checks of kdn_forward / kdn_step / kdn_forward_varlen: the same checks the
+/*
+ * kdn_backward -- gradients of the forward recurrence, for training (the
+ * reverse-mode adjoint of method steps 2-5 of the summary page, for all
+ * three variants).  The scalar differentiated is
+ *     L = sum dO (.) o + sum dS_T (.) S_T + sum dp_T (.) p_T
+ * where (o, S_T, p_T) is what kdn_forward returns for the same inputs,
+ * c0, mu, S0 and p0.
+ *
+ *   q, k, v, alpha, omega, r, c0, S0, p0, variant, dtype, sizes: as kdn_forward
+ *   dO    [B,T,H,dv]   dtype, may be NULL (zero)
+ *   dS_T  [B,H,dk,dv]  float, may be NULL (zero)
+ *   dp_T  [B,H,dk]     float ([B,H] for both isotropic variants), may be NULL (zero)
+ *   dq, dk, dv, dalpha, domega, dr: float outputs in the layouts of
+ *                      q, k, v, alpha, omega, r
+ *   dS0   [B,H,dk,dv]  float output (gradient with respect to S0, or to the
+ *                      zero initial memory when S0 is NULL)
+ *   dp0   [B,H,dk]     float output ([B,H] for both isotropic variants)
+ *   dc0   [H]          float output, may be NULL: the sum of dp0 over the
+ *                      batch and the channels, which is the gradient with
+ *                      respect to c0 when p0 is NULL
+ *   workspace          device memory of at least kdn_backward_workspace_size()
+ *                      bytes, 16-byte aligned (the recomputation checkpoints);
+ *                      its contents on entry do not matter
+ *
+ * S0, dS_T, dS0 and dv must be 8-byte aligned (KDN_ERR_UNSUPPORTED
+ * otherwise) and the workspace 16-byte aligned (KDN_ERR_WORKSPACE).  No output may overlap
+ * an input, another output or the workspace (KDN_ERR_ALIAS).  Arithmetic is
+ * fp32 throughout; calls are asynchronous on `stream` like kdn_forward, and
+ * the results are bitwise repeatable.
+ */
+int kdn_backward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                 const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                 int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                 const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                 float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
+                 void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
+ * B*H*(ceil(T/32)*(dk*dv + (dv/16)*dk) + 32*dk*dv)*4. */
+size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv);
+int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* omega, const void* r, const float* c0, float mu, int variant,
+                          int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                          const float* p0, const void* dO, const float* dS_T, const float* dp_T,
+                          float* dq, float* dk_out, float* dv_out, float* dalpha, float* domega,
+                          float* dr, float* dS0, float* dp0, float* dc0, void* workspace,
+                          size_t workspace_bytes);
+
+/* Host-only argument checks of kdn_forward / kdn_step / kdn_forward_varlen / kdn_backward: the same checks the
  * entry points run, with no device access and no launch.  Return a status. */
 int kdn_validate_forward(const void* q, const void* k, const void* v, const void* alpha,
                          const void* omega, const void* r, const float* c0, float mu,

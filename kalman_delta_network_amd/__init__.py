@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libkdn.so")
 
 KDN_DIAGONAL, KDN_ISOTROPIC = 0, 1
 KDN_F32, KDN_BF16 = 0, 1
-KDN_OK, KDN_ERR_NULL, KDN_ERR_SHAPE, KDN_ERR_UNSUPPORTED, KDN_ERR_VALUE, KDN_ERR_HIP, KDN_ERR_ALIAS = range(7)
+(KDN_OK, KDN_ERR_NULL, KDN_ERR_SHAPE, KDN_ERR_UNSUPPORTED, KDN_ERR_VALUE, KDN_ERR_HIP, KDN_ERR_ALIAS,
+ KDN_ERR_WORKSPACE) = range(8)
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 KDN_ISOTROPIC_CHANNEL = 2
 VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC, "isochannel": KDN_ISOTROPIC_CHANNEL}
@@ -31,8 +32,8 @@ def _gate_shapes(var, lead, dk):
 
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_step", "kdn_validate_forward",
-           "kdn_validate_forward_varlen", "kdn_validate_step", "kdn_status_string", "kdn_last_error",
-           "kdn_version")
+           "kdn_validate_forward_varlen", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
+           "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
 _lib = None
 
@@ -62,9 +63,14 @@ def load_library(path: str = LIB_PATH):
     varlen = [P, P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
     lib.kdn_forward_varlen.argtypes = varlen + [P, I]
     lib.kdn_validate_forward_varlen.argtypes = varlen + [I]
+    bwd = fwd[:17] + [P] * 12
+    lib.kdn_backward.argtypes = bwd + [P, ctypes.c_size_t, P]
+    lib.kdn_validate_backward.argtypes = bwd + [P, ctypes.c_size_t]
+    lib.kdn_backward_workspace_size.argtypes = [I, I, I, I, I]
+    lib.kdn_backward_workspace_size.restype = ctypes.c_size_t
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
-               lib.kdn_version):
+               lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -243,3 +249,55 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
                       _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
     _check(st, "kdn_step")
     return o
+
+
+def backward_workspace_size(B, T, H, dk, dv) -> int:
+    """Bytes of device workspace kdn_backward needs for these sizes."""
+    return int(load_library().kdn_backward_workspace_size(B, T, H, dk, dv))
+
+
+def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
+             S0=None, p0=None, workspace=None):
+    """Gradients of L = sum(dO*o) + sum(dS_T*S_T) + sum(dp_T*p_T), where
+    (o, S_T, p_T) = forward(q, k, v, alpha, omega, r, c0, mu, variant, S0, p0).
+
+    Inputs as ``forward``; dO [B,T,H,dv] in the input dtype, dS_T
+    [B,H,dk,dv] and dp_T [B,H,dk] (isotropic forms [B,H]) float32; any of the
+    three may be None (zero).  ``workspace``: a uint8 device tensor of at
+    least backward_workspace_size() bytes, or None to allocate one.
+    Returns a dict of float32 tensors dq, dk, dv, dalpha, domega, dr (input
+    layouts), dS0, dp0 and dc0 [H] (sum of dp0 over batch and channels).
+    """
+    torch = _torch()
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    ashape, wshape = _gate_shapes(var, (B, T, H), dk)
+    pshape = (B, H, dk) if var == KDN_DIAGONAL else (B, H)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if dO is not None:
+        _need(dO, "dO", (B, T, H, dv), dt, dev)
+    for name, t, shp in (("c0", c0, (H,)), ("S0", S0, (B, H, dk, dv)), ("p0", p0, pshape),
+                         ("dS_T", dS_T, (B, H, dk, dv)), ("dp_T", dp_T, pshape)):
+        if t is not None:
+            _need(t, name, shp, torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+         "dv": torch.empty((B, T, H, dv), **f32), "dalpha": torch.empty(ashape, **f32),
+         "domega": torch.empty(wshape, **f32), "dr": torch.empty((B, T, H), **f32),
+         "dS0": torch.empty((B, H, dk, dv), **f32), "dp0": torch.empty(pshape, **f32),
+         "dc0": torch.empty((H,), **f32)}
+    need = backward_workspace_size(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0), float(mu),
+                          var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T),
+                          _ptr(dp_T), *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0",
+                                                             "dp0", "dc0")),
+                          _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kdn_backward")
+    return g

@@ -162,6 +162,57 @@ int validate_step(const void* q, const void* k, const void* v, const void* alpha
     return KDN_OK;
 }
 
+int validate_backward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                      const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                      int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                      const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                      float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
+                      void* work, size_t work_bytes) {
+    int st = validate_common(variant, dtype, mu, dk, dv);
+    if (st != KDN_OK) return st;
+    if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
+    const int64_t units = int64_t(B) * H;
+    const int64_t toks = units * T;
+    if (units > INT32_MAX || toks > kMaxElems / 128)
+        return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
+    if (units == 0) return ok();
+    const bool iso = variant != KDN_DIAGONAL, chan = variant != KDN_ISOTROPIC;
+    if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r))
+        return fail(KDN_ERR_NULL, "q, k, v, alpha, omega and r must be non-NULL");
+    if (toks > 0 && (!dq || !dk_out || !dv_out || !dalpha || !domega || !dr))
+        return fail(KDN_ERR_NULL, "dq, dk, dv, dalpha, domega and dr must be non-NULL");
+    if (!dS0 || !dp0) return fail(KDN_ERR_NULL, "dS0 and dp0 must be non-NULL");
+    if (!c0 && !p0) return fail(KDN_ERR_NULL, "c0 may be NULL only when p0 is given");
+    const size_t need = kdn::backward_workspace_bytes(B, T, H, dk, dv);
+    if (need > 0 && (!work || work_bytes < need))
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, work_bytes);
+    const auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
+    if (need > 0 && mis16(work)) return fail(KDN_ERR_WORKSPACE, "the workspace must be 16-byte aligned");
+    const auto mis8 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 7u) != 0; };
+    if (mis8(S0) || mis8(dS_T) || mis8(dS0) || mis8(dv_out))
+        return fail(KDN_ERR_UNSUPPORTED, "S0, dS_T, dS0 and dv must be 8-byte aligned");
+
+    const size_t es = dtype == KDN_BF16 ? 2 : 4;
+    const size_t nk = size_t(toks) * dk, nv = size_t(toks) * dv;
+    const size_t na = chan ? nk : size_t(toks), nw = iso ? size_t(toks) : nk;
+    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * dk;
+    const Span in[] = {span(q, nk, es),     span(k, nk, es),        span(v, nv, es),
+                       span(alpha, na, es), span(omega, nw, es),    span(r, size_t(toks), es),
+                       span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4),
+                       span(dO, nv, es),    span(dS_T, ns, 4),      span(dp_T, np, 4)};
+    const Span out[] = {span(dq, nk, 4),     span(dk_out, nk, 4), span(dv_out, nv, 4),
+                        span(dalpha, na, 4), span(domega, nw, 4), span(dr, size_t(toks), 4),
+                        span(dS0, ns, 4),    span(dp0, np, 4),    span(dc0, size_t(H), 4),
+                        span(work, need, 1)};
+    for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+        for (const Span& x : in)
+            if (overlap(out[i], x)) return fail(KDN_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
+        for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
+            if (overlap(out[i], out[j])) return fail(KDN_ERR_ALIAS, "gradient outputs or the workspace overlap each other");
+    }
+    return KDN_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     if (e == hipErrorNotSupported) return fail(KDN_ERR_UNSUPPORTED, "%s: shape not supported by this algorithm", what);
@@ -185,7 +236,7 @@ int run_forward(const kdn::FwdArgs& a, hipStream_t s, int algo) {
 
 extern "C" {
 
-int kdn_version(void) { return 200; }  // 0.2.0: packed variable-length forward
+int kdn_version(void) { return 300; }  // 0.3.0: backward pass
 
 const char* kdn_status_string(int status) {
     switch (status) {
@@ -196,6 +247,7 @@ const char* kdn_status_string(int status) {
         case KDN_ERR_VALUE: return "invalid scalar argument";
         case KDN_ERR_HIP: return "HIP runtime error";
         case KDN_ERR_ALIAS: return "an output overlaps an input";
+        case KDN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         default: return "unknown status";
     }
 }
@@ -278,6 +330,42 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
     kdn::FwdArgs a{q, k, v, alpha, omega, r, nullptr, mu, variant, dtype, N, 1, H, dk, dv,
                    S, p, o, S, p};
     return hip_status(kdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "decode step");
+}
+
+size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
+    return kdn::backward_workspace_bytes(B, T, H, dk, dv);
+}
+
+int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* omega, const void* r, const float* c0, float mu, int variant,
+                          int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                          const float* p0, const void* dO, const float* dS_T, const float* dp_T,
+                          float* dq, float* dk_out, float* dv_out, float* dalpha, float* domega,
+                          float* dr, float* dS0, float* dp0, float* dc0, void* workspace,
+                          size_t workspace_bytes) {
+    const int st = validate_backward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0,
+                                     dO, dS_T, dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0,
+                                     workspace, workspace_bytes);
+    return st == KDN_OK ? ok() : st;
+}
+
+int kdn_backward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                 const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                 int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                 const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                 float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate_backward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0,
+                                     dO, dS_T, dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0,
+                                     workspace, workspace_bytes);
+    if (st != KDN_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    const kdn::BwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, dO, dS_T,
+                         dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0,
+                         static_cast<float*>(workspace)};
+    return hip_status(kdn::launch_backward(a, static_cast<hipStream_t>(stream)), "backward");
 }
 
 }  // extern "C"

@@ -1,0 +1,604 @@
+// kdn_backward.hip -- reverse-mode gradients of the KDN recurrence for gfx950.
+//
+// The forward token step (KDN summary page, method steps 2-5; isotropic forms
+// per the closing sentence of that section) is
+//   p_hat = alpha^2 p + omega,  kappa = p_hat k / (r + sum p_hat k^2),
+//   S_hat = diag(alpha) S,  delta = v - S_hat^T k,  S' = S_hat + kappa delta^T,
+//   o = S'^T q,  p' = p_hat / (1 + (mu / r) k^2 p_hat),
+// and this kernel runs its adjoint backwards in time.  The adjoint splits in
+// two coupled parts:
+//   * the memory part, on the d_k x d_v cotangent dS, needs only kappa, alpha,
+//     k, q from the uncertainty path:
+//       dS += q dO^T;  d_delta = dS^T kappa (= dv);  d_kappa = dS delta;
+//       dq = S' dO;  dS_hat = dS - k d_delta^T;  dk_mem = -S_hat d_delta;
+//       dalpha_mem = rowsum(S (.) dS_hat);  dS <- diag(alpha) dS_hat;
+//   * the uncertainty part, per key channel, needs d_kappa from the memory
+//     part and carries dp backwards through the posterior, the gain and the
+//     prediction (dk, dalpha, domega, dr).
+//
+// One workgroup per (batch, head).  Waves 0 .. NW-1 (NW = d_v / 16) own the
+// memory columns: lane = (row group rg, column pair cq), holding rows rg + 8m
+// of 2 consecutive columns, so that each column reduction over the key
+// dimension stays inside one wave (registers, then 3 lane-xor steps); wave NW
+// is the uncertainty wave (lane owns channels lane, lane + 64).
+//
+// The memory S_{t-1} is needed at every token of the reverse sweep.  A first
+// forward sweep stores a checkpoint of (S, p) every SEG tokens in the
+// workspace; then, segment by segment from the last, the memory waves re-run
+// the segment's forward from its checkpoint, storing each token's S_{t-1} in
+// a per-workgroup stash (workspace) and the token's (alpha, k, q, kappa) and
+// p_{t-1} in LDS, and walk the segment backwards.  The memory waves reduce
+// their four per-row partial sums (dq, d_kappa, dk_mem, dalpha_mem) over the
+// lanes of a row with a reduce-scatter and leave them in LDS; the uncertainty
+// wave consumes them one token behind (double-buffered), so the two parts
+// overlap and meet at one barrier per token.
+#include "kdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kdn {
+namespace {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+constexpr int SEG = 32;  // tokens per checkpoint segment
+constexpr int NC = 2;    // memory columns per lane
+constexpr int WCOLS = 8 * NC;  // memory columns per wave
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// workspace floats per (batch, head): S and p checkpoints (p once per memory
+// wave, so that every lane reads back only what it wrote) and the stash
+__host__ __device__ inline size_t unit_floats(int T, int dk, int dv) {
+    const size_t nseg = (size_t(T) + SEG - 1) / SEG;
+    const size_t nw = size_t(dv) / WCOLS;
+    return nseg * (size_t(dk) * dv + nw * dk) + size_t(SEG) * dk * dv;
+}
+
+template <int DK, int DV>
+struct BwdSmem {
+    float4 seg_chan[SEG][DK];           // (alpha, k, q, kappa) of each token of the segment
+    float seg_p[SEG][DK];               // p_{t-1} of each token (isotropic forms: entry 0)
+    float part[2][4][DV / WCOLS][DK];   // per-wave row sums: dq, d_kappa, dk_mem, dalpha_mem
+    float4 chan[DV / WCOLS][DK];        // forward staging, one slice per memory wave
+};
+
+template <int DK, int VAR, typename Tin>
+struct TokIn {
+    static constexpr int CPL = DK / 64;
+    float k[CPL], q[CPL], a[CPL], w[CPL];
+    float r;
+    float v[NC];
+};
+
+template <int DK, int VAR, typename Tin>
+__device__ __forceinline__ void load_tok(TokIn<DK, VAR, Tin>& x, const BwdArgs& A, size_t tok, int lane,
+                                         int col, int DVv) {
+    constexpr int CPL = DK / 64;
+    const Tin* q = static_cast<const Tin*>(A.q);
+    const Tin* k = static_cast<const Tin*>(A.k);
+    const Tin* v = static_cast<const Tin*>(A.v);
+    const Tin* al = static_cast<const Tin*>(A.alpha);
+    const Tin* om = static_cast<const Tin*>(A.omega);
+    const Tin* r = static_cast<const Tin*>(A.r);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const size_t e = tok * DK + lane + 64 * c;
+        x.k[c] = to_f32(k[e]);
+        x.q[c] = to_f32(q[e]);
+        x.a[c] = VAR == 1 ? to_f32(al[tok]) : to_f32(al[e]);
+        x.w[c] = VAR == 0 ? to_f32(om[e]) : to_f32(om[tok]);
+    }
+    x.r = to_f32(r[tok]);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) x.v[j] = to_f32(v[tok * DVv + col + j]);
+}
+
+// One forward token on a memory wave's columns (the recurrent forward's
+// arithmetic, without the readout).  Optionally records the token's
+// (alpha, k, q, kappa) and p_{t-1} for the reverse sweep (wave 0) and the
+// pre-token memory S_{t-1} in the stash (every memory wave).
+template <int DK, int DV, int VAR, typename Tin>
+__device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&S)[DK / 8][NC],
+                                          float (&p)[DK / 64], float& pb, float mu, float4* chanw,
+                                          float4* rec_chan, float* rec_p, float2* stash_tok, int lane,
+                                          int rg, int tid) {
+    constexpr int CPL = DK / 64, RPT = DK / 8, NT = (DV / WCOLS) * 64;
+    constexpr bool ISO = VAR != 0;
+    float kap[CPL];
+    if (ISO) {
+        float a2 = 0.f, n = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            a2 += x.a[c] * x.a[c];
+            n += x.k[c] * x.k[c];
+        }
+        a2 = VAR == 2 ? wave_sum(a2) * (1.0f / float(DK)) : x.a[0] * x.a[0];
+        n = wave_sum(n);
+        const float bh = a2 * pb + x.w[0] * (1.0f / float(DK));
+        const float beta = bh / (x.r + bh * n);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) kap[c] = beta * x.k[c];
+        if (rec_p && lane == 0) rec_p[0] = pb;
+        pb = bh / (1.0f + (mu / (float(DK) * x.r)) * n * bh);
+    } else {
+        float ph[CPL];
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            ph[c] = x.a[c] * x.a[c] * p[c] + x.w[c];
+            s += ph[c] * x.k[c] * x.k[c];
+        }
+        s = wave_sum(s);
+        const float inv = 1.0f / (x.r + s);
+        const float mr = mu / x.r;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            kap[c] = ph[c] * x.k[c] * inv;
+            if (rec_p) rec_p[lane + 64 * c] = p[c];
+            p[c] = ph[c] / (1.0f + mr * x.k[c] * x.k[c] * ph[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const float4 e = make_float4(x.a[c], x.k[c], x.q[c], kap[c]);
+        chanw[lane + 64 * c] = e;
+        if (rec_chan) rec_chan[lane + 64 * c] = e;
+    }
+    wave_lds_sync();
+    if (stash_tok) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) stash_tok[size_t(m) * NT + tid] = make_float2(S[m][0], S[m][1]);
+    }
+    float Ak[NC] = {};
+    float kr[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const float4 c4 = chanw[rg + 8 * m];
+        kr[m] = c4.w;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            S[m][j] *= c4.x;
+            Ak[j] += S[m][j] * c4.y;
+        }
+    }
+#pragma unroll
+    for (int off = 8; off <= 32; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) Ak[j] += __shfl_xor(Ak[j], off, 64);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) S[m][j] += kr[m] * (x.v[j] - Ak[j]);
+    wave_lds_sync();  // chanw is rewritten by the next token
+}
+
+// In-place halving reduce-scatter over the 8 column-pair lanes of a row
+// group: on entry every lane holds N values; on exit lane cq holds, in
+// vals[0 .. N/8), the sums over the 8 lanes of flat entries
+// [cq * N / 8, (cq + 1) * N / 8).
+template <int N>
+__device__ __forceinline__ void rowsum_scatter(float (&vals)[N], int cq) {
+#pragma unroll
+    for (int step = 0; step < 3; ++step) {
+        const int X = 4 >> step;
+        const int half = N >> (step + 1);
+        const bool hi = (cq & X) != 0;
+#pragma unroll
+        for (int f = 0; f < half; ++f) {
+            const float keep = hi ? vals[f + half] : vals[f];
+            const float send = hi ? vals[f] : vals[f + half];
+            vals[f] = keep + __shfl_xor(send, X, 64);
+        }
+    }
+}
+
+template <int DK, int DV, int VAR, typename Tin>
+__global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
+    constexpr int NW = DV / WCOLS;  // memory waves
+    constexpr int CPL = DK / 64;  // channels per lane
+    constexpr int RPT = DK / 8;   // memory rows per lane
+    constexpr int NT = NW * 64;   // memory threads
+    constexpr bool ISO = VAR != 0;
+    static_assert(DK % 64 == 0 && DV % 32 == 0, "unsupported tile");
+
+    __shared__ BwdSmem<DK, DV> sm;
+
+    const int unit = int(blockIdx.x);
+    const int h = unit % A.H;
+    const size_t b = size_t(unit / A.H);
+    const int T = A.T;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int cq = lane & 7;
+    const int rg = lane >> 3;
+    const int col = wave * WCOLS + cq * NC;
+    const bool memw = wave < NW;
+    const int nseg = (T + SEG - 1) / SEG;
+    const float mu = A.mu;
+
+    float* ckS = A.work + size_t(unit) * unit_floats(T, DK, DV);
+    float* ckP = ckS + size_t(nseg) * DK * DV;
+    float2* stash = reinterpret_cast<float2*>(ckP + size_t(nseg) * NW * DK);
+    float2* ckS2 = reinterpret_cast<float2*>(ckS);
+    const size_t sbase = size_t(unit) * DK * DV;
+    const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
+
+    // ---- forward sweep: checkpoints of (S, p) at every segment start ----
+    float S[RPT][NC];
+    float p[CPL];
+    float pb = 0.f;
+    if (memw) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + 8 * m;
+            if (A.S0) {
+                const float2 s2 = *reinterpret_cast<const float2*>(A.S0 + sbase + size_t(i) * DV + col);
+                S[m][0] = s2.x; S[m][1] = s2.y;
+            } else {
+                S[m][0] = S[m][1] = 0.f;
+            }
+        }
+        if (ISO) {
+            pb = A.p0 ? A.p0[unit] : A.c0[h];
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) p[c] = A.p0 ? A.p0[size_t(unit) * DK + lane + 64 * c] : A.c0[h];
+        }
+        for (int seg = 0; seg < nseg; ++seg) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m)
+                ckS2[(size_t(seg) * RPT + m) * NT + tid] = make_float2(S[m][0], S[m][1]);
+            float* cp = ckP + (size_t(seg) * NW + wave) * DK;
+            if (ISO) {
+                if (lane == 0) cp[0] = pb;
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) cp[lane + 64 * c] = p[c];
+            }
+            if (seg == nseg - 1) break;  // the last segment's tokens are re-run below
+            for (int t = seg * SEG; t < (seg + 1) * SEG; ++t) {
+                TokIn<DK, VAR, Tin> x;
+                load_tok(x, A, tokidx(t), lane, col, DV);
+                fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
+                                            tid);
+            }
+        }
+    }
+
+    // ---- reverse sweep, segment by segment ----
+    float dS[RPT][NC];
+    float dp[CPL];
+    float db = 0.f;
+    if (memw) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + 8 * m;
+            if (A.dS_T) {
+                const float2 s2 = *reinterpret_cast<const float2*>(A.dS_T + sbase + size_t(i) * DV + col);
+                dS[m][0] = s2.x; dS[m][1] = s2.y;
+            } else {
+                dS[m][0] = dS[m][1] = 0.f;
+            }
+        }
+    } else {
+        if (ISO) {
+            db = A.dp_T ? A.dp_T[unit] : 0.f;
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) dp[c] = A.dp_T ? A.dp_T[size_t(unit) * DK + lane + 64 * c] : 0.f;
+        }
+    }
+    const Tin* dO = static_cast<const Tin*>(A.dO);
+    const Tin* omg = static_cast<const Tin*>(A.omega);
+    const Tin* rr = static_cast<const Tin*>(A.r);
+    const Tin* vin = static_cast<const Tin*>(A.v);
+
+    for (int seg = nseg - 1; seg >= 0; --seg) {
+        const int t0 = seg * SEG;
+        const int n = min(SEG, T - t0);
+        if (memw) {
+            // re-run the segment from its checkpoint, recording what the reverse sweep needs
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const float2 s2 = ckS2[(size_t(seg) * RPT + m) * NT + tid];
+                S[m][0] = s2.x; S[m][1] = s2.y;
+            }
+            const float* cp = ckP + (size_t(seg) * NW + wave) * DK;
+            if (ISO) {
+                pb = cp[0];
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) p[c] = cp[lane + 64 * c];
+            }
+            for (int tt = 0; tt < n; ++tt) {
+                TokIn<DK, VAR, Tin> x;
+                load_tok(x, A, tokidx(t0 + tt), lane, col, DV);
+                fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], wave == 0 ? sm.seg_chan[tt] : nullptr,
+                                            wave == 0 ? sm.seg_p[tt] : nullptr, stash + size_t(tt) * RPT * NT,
+                                            lane, rg, tid);
+            }
+        }
+        __syncthreads();
+
+        // iteration it: memory waves take token t0 + n - 1 - it, the
+        // uncertainty wave the token the memory waves took one iteration before
+        for (int it = 0; it <= n; ++it) {
+            if (memw && it < n) {
+                const int tt = n - 1 - it;
+                const size_t tok = tokidx(t0 + tt);
+                const int slot = it & 1;
+                float Sp[RPT][NC];  // S_{t-1}
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float2 s2 = stash[(size_t(tt) * RPT + m) * NT + tid];
+                    Sp[m][0] = s2.x; Sp[m][1] = s2.y;
+                }
+                float g[NC], vv[NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    g[j] = dO ? to_f32(dO[tok * DV + col + j]) : 0.f;
+                    vv[j] = to_f32(vin[tok * DV + col + j]);
+                }
+                const float4* crow = sm.seg_chan[tt];
+                // innovation delta = v - S_hat^T k, with S_hat = diag(alpha) S_{t-1};
+                // readout cotangent into dS, then d_delta = dS^T kappa
+                float Ak[NC] = {}, Ek[NC] = {};
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float4 c4 = crow[rg + 8 * m];  // (alpha, k, q, kappa) of row rg + 8m
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        Ak[j] += c4.x * Sp[m][j] * c4.y;
+                        dS[m][j] += c4.z * g[j];
+                        Ek[j] += dS[m][j] * c4.w;
+                    }
+                }
+#pragma unroll
+                for (int off = 8; off <= 32; off <<= 1)
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        Ak[j] += __shfl_xor(Ak[j], off, 64);
+                        Ek[j] += __shfl_xor(Ek[j], off, 64);
+                    }
+                float dl[NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) dl[j] = vv[j] - Ak[j];
+                if (rg == 0) *reinterpret_cast<float2*>(A.dv_ + tok * DV + col) = make_float2(Ek[0], Ek[1]);
+                // per-row partial sums over the lane's 2 columns, two quantities
+                // at a time: [0] dq = S' dO, [1] d_kappa = dS delta, then
+                // [2] dk_mem = -S_hat d_delta, [3] dalpha_mem = sum S_{t-1} (.) dS_hat
+                // (and dS <- diag(alpha) dS_hat); after each reduce-scatter lane cq
+                // holds quantity cq / 4 of the pair for rows 4 (cq & 3) + e
+                const int qh = cq >> 2;
+                float vals[2 * RPT];
+                // re-read the row operands from LDS in each pass instead of
+                // keeping all of them live across the passes
+                __asm__ volatile("" ::: "memory");
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float4 c4 = crow[rg + 8 * m];
+                    float pq = 0.f, pk = 0.f;
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        pq += (c4.x * Sp[m][j] + c4.w * dl[j]) * g[j];
+                        pk += dS[m][j] * dl[j];
+                    }
+                    vals[m] = pq;
+                    vals[RPT + m] = pk;
+                }
+                rowsum_scatter<2 * RPT>(vals, cq);
+#pragma unroll
+                for (int e = 0; e < RPT / 4; ++e)
+                    sm.part[slot][qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
+                __asm__ volatile("" ::: "memory");
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float4 c4 = crow[rg + 8 * m];
+                    float pks = 0.f, pa = 0.f;
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        pks -= c4.x * Sp[m][j] * Ek[j];
+                        const float dsh = dS[m][j] - c4.y * Ek[j];
+                        pa += Sp[m][j] * dsh;
+                        dS[m][j] = c4.x * dsh;
+                    }
+                    vals[m] = pks;
+                    vals[RPT + m] = pa;
+                }
+                rowsum_scatter<2 * RPT>(vals, cq);
+#pragma unroll
+                for (int e = 0; e < RPT / 4; ++e)
+                    sm.part[slot][2 + qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
+            }
+            if (!memw && it >= 1) {
+                const int tt = n - it;
+                const size_t tok = tokidx(t0 + tt);
+                const int slot = (it - 1) & 1;
+                const float rt = to_f32(rr[tok]);
+                float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int i = lane + 64 * c;
+                    const float4 c4 = sm.seg_chan[tt][i];
+                    al[c] = c4.x;
+                    kk[c] = c4.y;
+                    pp[c] = ISO ? 0.f : sm.seg_p[tt][i];
+                    gq[c] = gk[c] = gks[c] = ga[c] = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        gq[c] += sm.part[slot][0][w][i];
+                        gk[c] += sm.part[slot][1][w][i];
+                        gks[c] += sm.part[slot][2][w][i];
+                        ga[c] += sm.part[slot][3][w][i];
+                    }
+                    A.dq[tok * DK + i] = gq[c];
+                }
+                if (!ISO) {
+                    // gain kappa = p_hat k / d, d = r + sum p_hat k^2; posterior
+                    // p' = p_hat / (1 + u p_hat), u = (mu / r) k^2; predict
+                    // p_hat = alpha^2 p + omega
+                    float ph[CPL];
+                    float s = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const float w = to_f32(omg[tok * DK + lane + 64 * c]);
+                        ph[c] = al[c] * al[c] * pp[c] + w;
+                        s += ph[c] * kk[c] * kk[c];
+                    }
+                    s = wave_sum(s);
+                    const float d = rt + s;
+                    const float inv = 1.0f / d;
+                    float kd = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) kd += gk[c] * ph[c] * kk[c];
+                    const float dd = -wave_sum(kd) * inv * inv;
+                    const float mr = mu / rt;
+                    float drr = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int i = lane + 64 * c;
+                        const float k2 = kk[c] * kk[c];
+                        const float den = 1.0f + mr * k2 * ph[c];
+                        const float pn = ph[c] / den;
+                        const float du = -dp[c] * pn * pn;
+                        const float dph = dp[c] / (den * den) + gk[c] * kk[c] * inv + dd * k2;
+                        drr -= du * mr * k2 / rt;
+                        A.dk_[tok * DK + i] = gks[c] + gk[c] * ph[c] * inv + 2.0f * dd * ph[c] * kk[c] +
+                                              2.0f * du * mr * kk[c];
+                        A.dalpha[tok * DK + i] = ga[c] + 2.0f * dph * al[c] * pp[c];
+                        A.domega[tok * DK + i] = dph;
+                        dp[c] = dph * al[c] * al[c];
+                    }
+                    drr = wave_sum(drr);
+                    if (lane == 0) A.dr[tok] = dd + drr;
+                } else {
+                    // scalar gain beta = b_hat / (r + b_hat n), n = |k|^2; posterior
+                    // b' = b_hat / (1 + c n b_hat), c = mu / (d_k r); predict
+                    // b_hat = a b + omega / d_k, a = alpha^2 or mean_i alpha_i^2
+                    const float bprev = sm.seg_p[tt][0];
+                    const float w = to_f32(omg[tok]);
+                    float a2 = 0.f, nn = 0.f, kb = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        a2 += al[c] * al[c];
+                        nn += kk[c] * kk[c];
+                        kb += gk[c] * kk[c];
+                    }
+                    a2 = VAR == 2 ? wave_sum(a2) * (1.0f / float(DK)) : al[0] * al[0];
+                    nn = wave_sum(nn);
+                    const float dbeta = wave_sum(kb);
+                    const float bh = a2 * bprev + w * (1.0f / float(DK));
+                    const float dg = rt + bh * nn;
+                    const float beta = bh / dg;
+                    const float cc = mu / (float(DK) * rt);
+                    const float dpn = 1.0f + cc * nn * bh;
+                    const float bt = bh / dpn;
+                    const float idg2 = 1.0f / (dg * dg);
+                    const float dbh = dbeta * rt * idg2 + db / (dpn * dpn);
+                    const float dn = -dbeta * bh * bh * idg2 - db * bt * bt * cc;
+                    const float dR = -dbeta * bh * idg2 + db * bt * bt * cc * nn / rt;
+                    float gas = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int i = lane + 64 * c;
+                        A.dk_[tok * DK + i] = gks[c] + beta * gk[c] + 2.0f * dn * kk[c];
+                        if (VAR == 2) A.dalpha[tok * DK + i] = ga[c] + dbh * bprev * 2.0f * al[c] * (1.0f / float(DK));
+                        gas += ga[c];
+                    }
+                    if (VAR == 1) gas = wave_sum(gas);
+                    if (lane == 0) {
+                        if (VAR == 1) A.dalpha[tok] = gas + 2.0f * dbh * al[0] * bprev;
+                        A.domega[tok] = dbh * (1.0f / float(DK));
+                        A.dr[tok] = dR;
+                    }
+                    db = dbh * a2;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    if (memw) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + 8 * m;
+            *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
+        }
+    } else {
+        if (ISO) {
+            if (lane == 0) A.dp0[unit] = db;
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) A.dp0[size_t(unit) * DK + lane + 64 * c] = dp[c];
+        }
+    }
+}
+
+// dc0[h] = sum over the batch and the channels of dp0 (the c0 gradient when
+// p_0 = c0[h] on every channel); fixed summation order
+__global__ void kdn_dc0_kernel(const float* __restrict__ dp0, float* __restrict__ dc0, int B, int H, int pd) {
+    const int h = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
+    if (h >= H) return;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < pd; ++i) acc += dp0[(size_t(b) * H + h) * pd + i];
+    dc0[h] = acc;
+}
+
+template <int DK, int DV, int VAR, typename Tin>
+hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((kdn_backward_kernel<DK, DV, VAR, Tin>), dim3(unsigned(long(a.B) * a.H)),
+                       dim3(DV * 4 + 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int VAR>
+hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
+    return a.dtype == 1 ? launch_t<DK, DV, VAR, bf16_t>(a, s) : launch_t<DK, DV, VAR, float>(a, s);
+}
+
+template <int DK, int DV>
+hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
+    if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
+    return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
+    if (long(B) * H == 0 || T == 0) return 0;
+    return size_t(B) * size_t(H) * unit_floats(T, dk, dv) * sizeof(float);
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+    hipError_t e;
+    if (a.dk == 128 && a.dv == 128) e = launch_variant<128, 128>(a, stream);
+    else if (a.dk == 128 && a.dv == 64) e = launch_variant<128, 64>(a, stream);
+    else if (a.dk == 64 && a.dv == 128) e = launch_variant<64, 128>(a, stream);
+    else if (a.dk == 64 && a.dv == 64) e = launch_variant<64, 64>(a, stream);
+    else return hipErrorNotSupported;
+    if (e != hipSuccess || !a.dc0) return e;
+    const int pd = a.variant == 0 ? a.dk : 1;
+    hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned((a.H + 63) / 64)), dim3(64), 0, stream, a.dp0, a.dc0, a.B,
+                       a.H, pd);
+    return hipGetLastError();
+}
+
+}  // namespace kdn

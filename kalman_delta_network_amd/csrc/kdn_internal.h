@@ -36,6 +36,41 @@ struct FwdArgs {
     const int* seq_order = nullptr;
 };
 
+// One backward call, after host validation.  Pointers are device pointers;
+// gradients are fp32 in the layouts of the inputs they belong to.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* alpha;
+    const void* omega;
+    const void* r;
+    const float* c0;
+    float mu;
+    int variant;  // as FwdArgs
+    int dtype;    // 0 f32, 1 bf16 (of the token inputs and dO)
+    int B, T, H, dk, dv;
+    const float* S0;
+    const float* p0;
+    const void* dO;     // [B,T,H,dv] dtype, may be NULL (zero)
+    const float* dS_T;  // may be NULL (zero)
+    const float* dp_T;  // may be NULL (zero)
+    float* dq;
+    float* dk_;
+    float* dv_;
+    float* dalpha;
+    float* domega;
+    float* dr;
+    float* dS0;
+    float* dp0;
+    float* dc0;   // may be NULL
+    float* work;  // backward_workspace_bytes() bytes
+};
+
+// Bytes of device workspace one backward call needs (0 for an empty call).
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 // Token-by-token recurrence; one workgroup per (b, h) covering all d_v
 // columns.  Also the decode step (T = 1, S_T == S0, p_T == p0 in place).
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t stream);

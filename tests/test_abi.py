@@ -34,11 +34,11 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(kdn.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kdn_version() == 200
+    assert lib.kdn_version() == 300
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.kdn_status_string(s)
     assert lib.kdn_status_string(99) == b"unknown status"
 
@@ -261,3 +261,92 @@ def test_binding_raises_when_library_missing(tmp_path):
             kdn.load_library(str(tmp_path / "nope.so"))
     finally:
         kdn._lib = saved
+
+
+# ---------------------------------------------------------------------------
+# kdn_backward
+# ---------------------------------------------------------------------------
+
+BWD_OUT = ("g_q", "g_k", "g_v", "g_alpha", "g_omega", "g_r", "g_S0", "g_p0", "g_c0")  # dq .. dc0
+
+
+def bwd_args(fake, lib, B=2, T=40, H=2, dk=64, dv=64, variant=0, dtype=1, mu=64.0, **over):
+    a = dict(q=fake(), k=fake(), v=fake(), alpha=fake(), omega=fake(), r=fake(), c0=fake(), mu=mu,
+             variant=variant, dtype=dtype, B=B, T=T, H=H, dk=dk, dv=dv, S0=None, p0=None, dO=fake(),
+             dS_T=None, dp_T=None, work=fake())
+    for n in BWD_OUT:
+        a[n] = fake()
+    a["work_bytes"] = lib.kdn_backward_workspace_size(B, T, H, dk, dv)
+    a.update(over)
+    return a
+
+
+def _bwd_list(a):
+    return [a[n] for n in ("q", "k", "v", "alpha", "omega", "r", "c0", "mu", "variant", "dtype", "B", "T", "H",
+                           "dk", "dv", "S0", "p0", "dO", "dS_T", "dp_T")] + [a[n] for n in BWD_OUT] + \
+        [a["work"], a["work_bytes"]]
+
+
+def call_validate_bwd(lib, a):
+    return lib.kdn_validate_backward(*_bwd_list(a))
+
+
+def test_backward_workspace_size_formula(lib):
+    # ceil(T/32) checkpoints of S and of p (one copy per 16 value columns), plus a 32-token stash
+    for B, T, H, dk, dv in ((2, 40, 3, 64, 128), (8, 4096, 16, 128, 128), (1, 1, 1, 128, 64)):
+        nseg = -(-T // 32)
+        want = B * H * (nseg * (dk * dv + (dv // 16) * dk) + 32 * dk * dv) * 4
+        assert lib.kdn_backward_workspace_size(B, T, H, dk, dv) == want
+    assert lib.kdn_backward_workspace_size(0, 10, 2, 64, 64) == 0
+    assert lib.kdn_backward_workspace_size(2, 0, 2, 64, 64) == 0
+
+
+def test_validate_backward_accepts_good_arguments(lib):
+    f = Fake()
+    for variant in (0, 1, 2):
+        for dtype in (0, 1):
+            for dk in (64, 128):
+                for dv in (64, 128):
+                    assert call_validate_bwd(lib, bwd_args(f, lib, variant=variant, dtype=dtype, dk=dk, dv=dv)) == 0
+    f = Fake()
+    assert call_validate_bwd(lib, bwd_args(f, lib, dO=None, g_c0=None)) == 0  # cotangent and dc0 optional
+    assert call_validate_bwd(lib, bwd_args(f, lib, S0=f(), p0=f(), c0=None, dS_T=f(), dp_T=f())) == 0
+    assert call_validate_bwd(lib, bwd_args(f, lib, T=0, q=None, work=None)) == 0  # nothing to recompute
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
+    (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(variant=3), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(T=-1), kdn.KDN_ERR_SHAPE),
+    (dict(q=None), kdn.KDN_ERR_NULL),
+    (dict(g_k=None), kdn.KDN_ERR_NULL),
+    (dict(g_p0=None), kdn.KDN_ERR_NULL),
+    (dict(c0=None), kdn.KDN_ERR_NULL),
+    (dict(work=None), kdn.KDN_ERR_WORKSPACE),
+    (dict(work_bytes=100), kdn.KDN_ERR_WORKSPACE),
+    (dict(work=ctypes.c_void_p((1 << 44) + 8)), kdn.KDN_ERR_WORKSPACE),
+    (dict(S0=ctypes.c_void_p((1 << 45) + 4)), kdn.KDN_ERR_UNSUPPORTED),
+])
+def test_validate_backward_rejects(lib, over, status):
+    f = Fake()
+    a = bwd_args(f, lib)
+    assert call_validate_bwd(lib, dict(a, **over)) == status
+
+
+def test_validate_backward_aliasing(lib):
+    f = Fake()
+    a = bwd_args(f, lib)
+    assert call_validate_bwd(lib, dict(a, g_q=a["q"])) == kdn.KDN_ERR_ALIAS
+    assert call_validate_bwd(lib, dict(a, g_v=a["dO"])) == kdn.KDN_ERR_ALIAS
+    assert call_validate_bwd(lib, dict(a, g_S0=a["g_q"])) == kdn.KDN_ERR_ALIAS
+    assert call_validate_bwd(lib, dict(a, work=a["g_r"])) == kdn.KDN_ERR_ALIAS
+
+
+def test_backward_launch_error_path_without_gpu(lib, monkeypatch):
+    monkeypatch.setenv("KDN_FAULT", "launch")
+    f = Fake()
+    a = bwd_args(f, lib)
+    assert lib.kdn_backward(*_bwd_list(a), None) == kdn.KDN_ERR_HIP
+    assert b"KDN_FAULT" in lib.kdn_last_error()
+    assert lib.kdn_backward(*_bwd_list(dict(a, mu=float("nan"))), None) == kdn.KDN_ERR_VALUE
