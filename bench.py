@@ -64,12 +64,24 @@ def step_bytes(w) -> int:
     return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv)
 
 
+def backward_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: the forward's inputs and
+    dO read once, the fp32 gradients of q, k, v, alpha, omega, r written
+    once, plus dS0, dp0 and dc0 (the recomputation checkpoints are the
+    implementation's own traffic and are not counted)."""
+    es = 2 if w.dtype == "bf16" else 4
+    toks = w.B * w.T * w.H
+    n_in = 2 * w.dk + w.dv + _gate_elems(w) + 1
+    pdim = w.dk if w.variant == "diagonal" else 1
+    return toks * (es * (n_in + w.dv) + 4 * n_in) + w.B * w.H * (w.dk * w.dv + pdim) * 4 + 2 * w.H * 4
+
+
 def kernel_source_hash() -> str:
+    """Hash of the source of the forward's dominant kernel (the chunked
+    kernel): HBM counters taken on other source are not reported."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "kalman_delta_network_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    with open(os.path.join(ROOT, "kalman_delta_network_amd", "csrc", "kdn_chunked.hip"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -188,6 +200,27 @@ def bench_varlen(kdn, dev, steps, algo):
             "tokens_per_s": total / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_backward(kdn, w, dev, steps):
+    """Time kdn_backward on workload w (cotangent dO only), inputs resident."""
+    import torch
+    from kalman_delta_network_amd import workloads as wl
+    t = upload(wl.forward_inputs(w), w.dtype, dev)
+    dO = torch.from_numpy(wl.backward_cotangents(w, with_state=False)["dO"]).to(t["q"].dtype).to(dev)
+    ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    call = lambda: kdn.backward(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
+    warm(call, 1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+            "hbm_frac": backward_bytes(w) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "workspace_bytes": int(ws.numel())}
+
+
 COPY_BYTES = 512 << 20  # calibration copy for the HBM byte counters
 
 
@@ -271,7 +304,7 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the isotropic, decode, packed-batch and per-channel-decay isotropic lines")
+                    help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic and backward lines")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the workload of the rocprofv3 counter runs and exit")
@@ -328,6 +361,7 @@ def main():
         extra["isochannel"] = {"workload": wc.name, "tokens_per_s": wc.B * wc.T / (mc / 1e3), "ms_per_step": mc,
                                "hbm_frac": forward_bytes(wc) / (lc / 1e3) / 1e9 / HBM_PEAK_GBS}
         del tc
+        extra["backward"] = bench_backward(kdn, w, dev, 3)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x)

@@ -19,8 +19,10 @@
 // One workgroup per (batch, head).  Waves 0 .. NW-1 (NW = d_v / 16) own the
 // memory columns: lane = (row group rg, column pair cq), holding rows rg + 8m
 // of 2 consecutive columns, so that each column reduction over the key
-// dimension stays inside one wave (registers, then 3 lane-xor steps); wave NW
-// is the uncertainty wave (lane owns channels lane, lane + 64).
+// dimension stays inside one wave (registers, then 3 lane-xor steps).  Wave 0
+// also runs the uncertainty part (lane owns channels lane, lane + 64); with
+// d_v = 128 the eight waves sit two per SIMD and each may hold 256 VGPRs.
+// Every global load of the token loops is issued one token ahead.
 //
 // The memory S_{t-1} is needed at every token of the reverse sweep.  A first
 // forward sweep stores a checkpoint of (S, p) every SEG tokens in the
@@ -30,8 +32,8 @@
 // p_{t-1} in LDS, and walk the segment backwards.  The memory waves reduce
 // their four per-row partial sums (dq, d_kappa, dk_mem, dalpha_mem) over the
 // lanes of a row with a reduce-scatter and leave them in LDS; the uncertainty
-// wave consumes them one token behind (double-buffered), so the two parts
-// overlap and meet at one barrier per token.
+// part consumes them one token behind (double-buffered), so that the two
+// parts of consecutive tokens meet at one barrier per token.
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -57,9 +59,17 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // One wave's LDS operations execute in order, so waiting for this wave's
+    // own LDS traffic and keeping the compiler from moving memory accesses
+    // across is enough; a memory fence would also wait for every global load
+    // still in flight (the next token's prefetch).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier for LDS data only: global loads in flight (prefetches)
+// stay in flight across it.
+__device__ __forceinline__ void block_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // workspace floats per (batch, head): S and p checkpoints (p once per memory
@@ -116,9 +126,9 @@ __device__ __forceinline__ void load_tok(TokIn<DK, VAR, Tin>& x, const BwdArgs& 
 template <int DK, int DV, int VAR, typename Tin>
 __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&S)[DK / 8][NC],
                                           float (&p)[DK / 64], float& pb, float mu, float4* chanw,
-                                          float4* rec_chan, float* rec_p, float2* stash_tok, int lane,
+                                          float4* rec_chan, float* rec_p, float4* stash_tok, int lane,
                                           int rg, int tid) {
-    constexpr int CPL = DK / 64, RPT = DK / 8, NT = (DV / WCOLS) * 64;
+    constexpr int CPL = DK / 64, RPT = DK / 8;
     constexpr bool ISO = VAR != 0;
     float kap[CPL];
     if (ISO) {
@@ -163,7 +173,8 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
     wave_lds_sync();
     if (stash_tok) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) stash_tok[size_t(m) * NT + tid] = make_float2(S[m][0], S[m][1]);
+        for (int m = 0; m < RPT; m += 2)
+            stash_tok[tid * (RPT / 2) + m / 2] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
     }
     float Ak[NC] = {};
     float kr[RPT];
@@ -192,24 +203,31 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
 // group: on entry every lane holds N values; on exit lane cq holds, in
 // vals[0 .. N/8), the sums over the 8 lanes of flat entries
 // [cq * N / 8, (cq + 1) * N / 8).
+// The halves are chosen with a per-lane bit mask (one bitfield insert per
+// value) rather than a compare-and-select, which needs a lane mask in scalar
+// registers for every select.
+__device__ __forceinline__ float pick(uint32_t mask, float if_set, float if_clear) {
+    return __uint_as_float((mask & __float_as_uint(if_set)) | (~mask & __float_as_uint(if_clear)));
+}
+
 template <int N>
 __device__ __forceinline__ void rowsum_scatter(float (&vals)[N], int cq) {
 #pragma unroll
     for (int step = 0; step < 3; ++step) {
         const int X = 4 >> step;
         const int half = N >> (step + 1);
-        const bool hi = (cq & X) != 0;
+        const uint32_t hi = 0u - uint32_t((cq >> (2 - step)) & 1);  // all ones when bit X of cq is set
 #pragma unroll
         for (int f = 0; f < half; ++f) {
-            const float keep = hi ? vals[f + half] : vals[f];
-            const float send = hi ? vals[f] : vals[f + half];
+            const float keep = pick(hi, vals[f + half], vals[f]);
+            const float send = pick(hi, vals[f], vals[f + half]);
             vals[f] = keep + __shfl_xor(send, X, 64);
         }
     }
 }
 
 template <int DK, int DV, int VAR, typename Tin>
-__global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
+__global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
     constexpr int NW = DV / WCOLS;  // memory waves
     constexpr int CPL = DK / 64;  // channels per lane
     constexpr int RPT = DK / 8;   // memory rows per lane
@@ -229,14 +247,16 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
     const int cq = lane & 7;
     const int rg = lane >> 3;
     const int col = wave * WCOLS + cq * NC;
-    const bool memw = wave < NW;
     const int nseg = (T + SEG - 1) / SEG;
     const float mu = A.mu;
 
     float* ckS = A.work + size_t(unit) * unit_floats(T, DK, DV);
     float* ckP = ckS + size_t(nseg) * DK * DV;
-    float2* stash = reinterpret_cast<float2*>(ckP + size_t(nseg) * NW * DK);
-    float2* ckS2 = reinterpret_cast<float2*>(ckS);
+    // memory snapshots keep each thread's RPT x NC block contiguous (one
+    // per-lane offset, the rows as immediate offsets): float4 (m, m + 1) pairs
+    float4* stash = reinterpret_cast<float4*>(ckP + size_t(nseg) * NW * DK);
+    float4* ckS4 = reinterpret_cast<float4*>(ckS);
+    constexpr int SNAP = NT * (RPT / 2);  // float4 per snapshot
     const size_t sbase = size_t(unit) * DK * DV;
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
 
@@ -244,7 +264,7 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
     float S[RPT][NC];
     float p[CPL];
     float pb = 0.f;
-    if (memw) {
+    {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + 8 * m;
@@ -262,9 +282,10 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
             for (int c = 0; c < CPL; ++c) p[c] = A.p0 ? A.p0[size_t(unit) * DK + lane + 64 * c] : A.c0[h];
         }
         for (int seg = 0; seg < nseg; ++seg) {
+            float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m)
-                ckS2[(size_t(seg) * RPT + m) * NT + tid] = make_float2(S[m][0], S[m][1]);
+            for (int m = 0; m < RPT; m += 2)
+                ck[tid * (RPT / 2) + m / 2] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
             float* cp = ckP + (size_t(seg) * NW + wave) * DK;
             if (ISO) {
                 if (lane == 0) cp[0] = pb;
@@ -273,11 +294,14 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
                 for (int c = 0; c < CPL; ++c) cp[lane + 64 * c] = p[c];
             }
             if (seg == nseg - 1) break;  // the last segment's tokens are re-run below
+            TokIn<DK, VAR, Tin> x;
+            load_tok(x, A, tokidx(seg * SEG), lane, col, DV);
             for (int t = seg * SEG; t < (seg + 1) * SEG; ++t) {
-                TokIn<DK, VAR, Tin> x;
-                load_tok(x, A, tokidx(t), lane, col, DV);
+                TokIn<DK, VAR, Tin> xn;  // next token, issued before this one's arithmetic
+                load_tok(xn, A, tokidx(min(t + 1, T - 1)), lane, col, DV);
                 fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
                                             tid);
+                x = xn;
             }
         }
     }
@@ -286,18 +310,17 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
     float dS[RPT][NC];
     float dp[CPL];
     float db = 0.f;
-    if (memw) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + 8 * m;
-            if (A.dS_T) {
-                const float2 s2 = *reinterpret_cast<const float2*>(A.dS_T + sbase + size_t(i) * DV + col);
-                dS[m][0] = s2.x; dS[m][1] = s2.y;
-            } else {
-                dS[m][0] = dS[m][1] = 0.f;
-            }
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + 8 * m;
+        if (A.dS_T) {
+            const float2 s2 = *reinterpret_cast<const float2*>(A.dS_T + sbase + size_t(i) * DV + col);
+            dS[m][0] = s2.x; dS[m][1] = s2.y;
+        } else {
+            dS[m][0] = dS[m][1] = 0.f;
         }
-    } else {
+    }
+    if (wave == 0) {
         if (ISO) {
             db = A.dp_T ? A.dp_T[unit] : 0.f;
         } else {
@@ -313,12 +336,13 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
     for (int seg = nseg - 1; seg >= 0; --seg) {
         const int t0 = seg * SEG;
         const int n = min(SEG, T - t0);
-        if (memw) {
+        {
             // re-run the segment from its checkpoint, recording what the reverse sweep needs
+            const float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const float2 s2 = ckS2[(size_t(seg) * RPT + m) * NT + tid];
-                S[m][0] = s2.x; S[m][1] = s2.y;
+            for (int m = 0; m < RPT; m += 2) {
+                const float4 s4 = ck[tid * (RPT / 2) + m / 2];
+                S[m][0] = s4.x; S[m][1] = s4.y; S[m + 1][0] = s4.z; S[m + 1][1] = s4.w;
             }
             const float* cp = ckP + (size_t(seg) * NW + wave) * DK;
             if (ISO) {
@@ -327,35 +351,63 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) p[c] = cp[lane + 64 * c];
             }
+            TokIn<DK, VAR, Tin> x;
+            load_tok(x, A, tokidx(t0), lane, col, DV);
             for (int tt = 0; tt < n; ++tt) {
-                TokIn<DK, VAR, Tin> x;
-                load_tok(x, A, tokidx(t0 + tt), lane, col, DV);
+                TokIn<DK, VAR, Tin> xn;
+                load_tok(xn, A, tokidx(t0 + min(tt + 1, n - 1)), lane, col, DV);
                 fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], wave == 0 ? sm.seg_chan[tt] : nullptr,
-                                            wave == 0 ? sm.seg_p[tt] : nullptr, stash + size_t(tt) * RPT * NT,
+                                            wave == 0 ? sm.seg_p[tt] : nullptr, stash + size_t(tt) * SNAP,
                                             lane, rg, tid);
+                x = xn;
             }
         }
-        __syncthreads();
+        block_lds_sync();
 
-        // iteration it: memory waves take token t0 + n - 1 - it, the
-        // uncertainty wave the token the memory waves took one iteration before
+        // one token ahead: the memory part's S_{t-1}, dO_t, v_t and the
+        // uncertainty part's omega_t, r_t
+        float Spn[RPT][NC], gn[NC], vvn[NC], wn[CPL], rn = 0.f;
+        const auto load_rev = [&](int tt) {
+            const size_t tok = tokidx(t0 + tt);
+            const float4* sn = stash + size_t(tt) * SNAP;
+#pragma unroll
+            for (int m = 0; m < RPT; m += 2) {
+                const float4 s4 = sn[tid * (RPT / 2) + m / 2];
+                Spn[m][0] = s4.x; Spn[m][1] = s4.y; Spn[m + 1][0] = s4.z; Spn[m + 1][1] = s4.w;
+            }
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                gn[j] = dO ? to_f32(dO[tok * DV + col + j]) : 0.f;
+                vvn[j] = to_f32(vin[tok * DV + col + j]);
+            }
+        };
+        const auto load_unc = [&](int tt) {
+            const size_t tok = tokidx(t0 + tt);
+            rn = to_f32(rr[tok]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) wn[c] = VAR == 0 ? to_f32(omg[tok * DK + lane + 64 * c]) : to_f32(omg[tok]);
+        };
+        load_rev(n - 1);
+        if (wave == 0) load_unc(n - 1);
+
+        // iteration it: the memory part takes token t0 + n - 1 - it, the
+        // uncertainty part (wave 0) the token of the iteration before
         for (int it = 0; it <= n; ++it) {
-            if (memw && it < n) {
+            if (it < n) {
                 const int tt = n - 1 - it;
                 const size_t tok = tokidx(t0 + tt);
                 const int slot = it & 1;
-                float Sp[RPT][NC];  // S_{t-1}
+                float Sp[RPT][NC], g[NC], vv[NC];  // S_{t-1}, dO_t, v_t
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
-                    const float2 s2 = stash[(size_t(tt) * RPT + m) * NT + tid];
-                    Sp[m][0] = s2.x; Sp[m][1] = s2.y;
+                    Sp[m][0] = Spn[m][0]; Sp[m][1] = Spn[m][1];
                 }
-                float g[NC], vv[NC];
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
-                    g[j] = dO ? to_f32(dO[tok * DV + col + j]) : 0.f;
-                    vv[j] = to_f32(vin[tok * DV + col + j]);
+                    g[j] = gn[j];
+                    vv[j] = vvn[j];
                 }
+                load_rev(max(tt - 1, 0));
                 const float4* crow = sm.seg_chan[tt];
                 // innovation delta = v - S_hat^T k, with S_hat = diag(alpha) S_{t-1};
                 // readout cotangent into dS, then d_delta = dS^T kappa
@@ -427,11 +479,15 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
                 for (int e = 0; e < RPT / 4; ++e)
                     sm.part[slot][2 + qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
             }
-            if (!memw && it >= 1) {
+            if (wave == 0 && it >= 1) {
                 const int tt = n - it;
                 const size_t tok = tokidx(t0 + tt);
                 const int slot = (it - 1) & 1;
-                const float rt = to_f32(rr[tok]);
+                const float rt = rn;
+                float wc[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) wc[c] = wn[c];
+                load_unc(max(tt - 1, 0));
                 float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
@@ -458,8 +514,7 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
                     float s = 0.f;
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
-                        const float w = to_f32(omg[tok * DK + lane + 64 * c]);
-                        ph[c] = al[c] * al[c] * pp[c] + w;
+                        ph[c] = al[c] * al[c] * pp[c] + wc[c];
                         s += ph[c] * kk[c] * kk[c];
                     }
                     s = wave_sum(s);
@@ -493,7 +548,7 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
                     // b' = b_hat / (1 + c n b_hat), c = mu / (d_k r); predict
                     // b_hat = a b + omega / d_k, a = alpha^2 or mean_i alpha_i^2
                     const float bprev = sm.seg_p[tt][0];
-                    const float w = to_f32(omg[tok]);
+                    const float w = wc[0];
                     float a2 = 0.f, nn = 0.f, kb = 0.f;
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
@@ -531,17 +586,16 @@ __global__ void __launch_bounds__(DV * 4 + 64) kdn_backward_kernel(BwdArgs A) {
                     db = dbh * a2;
                 }
             }
-            __syncthreads();
+            block_lds_sync();
         }
     }
 
-    if (memw) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = rg + 8 * m;
-            *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
-        }
-    } else {
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + 8 * m;
+        *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
+    }
+    if (wave == 0) {
         if (ISO) {
             if (lane == 0) A.dp0[unit] = db;
         } else {
@@ -565,7 +619,7 @@ __global__ void kdn_dc0_kernel(const float* __restrict__ dp0, float* __restrict_
 template <int DK, int DV, int VAR, typename Tin>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((kdn_backward_kernel<DK, DV, VAR, Tin>), dim3(unsigned(long(a.B) * a.H)),
-                       dim3(DV * 4 + 64), 0, stream, a);
+                       dim3(DV * 4), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -61,9 +61,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 // LDS written by some lanes of a wave and read by other lanes of the same
 // wave: order the accesses at wavefront scope (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // One wave's LDS operations execute in order, so waiting for this wave's
+    // own LDS traffic and keeping the compiler from moving memory accesses
+    // across is enough; a memory fence would also wait for every global load
+    // still in flight (the next token's prefetch).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
