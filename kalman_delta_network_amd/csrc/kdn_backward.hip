@@ -88,6 +88,16 @@ struct BwdSmem {
     float4 chan[DV / WCOLS][DK];        // forward staging, one slice per memory wave
 };
 
+// float4 index, within one memory snapshot, of rows (m, m + 1) of thread
+// tid: each wave owns RPT / 2 blocks of 64 float4 (1 KB), one per row pair,
+// with the lanes contiguous, so every snapshot access is one coalesced 1 KB
+// run per wave and the row pairs of a thread differ by immediate offsets
+template <int RPT>
+__device__ __forceinline__ int snap_idx(int tid, int m) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    return (wave * (RPT / 2) + m / 2) * 64 + (tid & 63);
+}
+
 template <int DK, int VAR, typename Tin>
 struct TokIn {
     static constexpr int CPL = DK / 64;
@@ -174,7 +184,7 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
     if (stash_tok) {
 #pragma unroll
         for (int m = 0; m < RPT; m += 2)
-            stash_tok[tid * (RPT / 2) + m / 2] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
+            stash_tok[snap_idx<RPT>(tid, m)] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
     }
     float Ak[NC] = {};
     float kr[RPT];
@@ -252,8 +262,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
 
     float* ckS = A.work + size_t(unit) * unit_floats(T, DK, DV);
     float* ckP = ckS + size_t(nseg) * DK * DV;
-    // memory snapshots keep each thread's RPT x NC block contiguous (one
-    // per-lane offset, the rows as immediate offsets): float4 (m, m + 1) pairs
+    // memory snapshots as float4 (m, m + 1) row pairs, see snap_idx
     float4* stash = reinterpret_cast<float4*>(ckP + size_t(nseg) * NW * DK);
     float4* ckS4 = reinterpret_cast<float4*>(ckS);
     constexpr int SNAP = NT * (RPT / 2);  // float4 per snapshot
@@ -285,7 +294,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
             float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
             for (int m = 0; m < RPT; m += 2)
-                ck[tid * (RPT / 2) + m / 2] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
+                ck[snap_idx<RPT>(tid, m)] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
             float* cp = ckP + (size_t(seg) * NW + wave) * DK;
             if (ISO) {
                 if (lane == 0) cp[0] = pb;
@@ -341,7 +350,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
             const float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
             for (int m = 0; m < RPT; m += 2) {
-                const float4 s4 = ck[tid * (RPT / 2) + m / 2];
+                const float4 s4 = ck[snap_idx<RPT>(tid, m)];
                 S[m][0] = s4.x; S[m][1] = s4.y; S[m + 1][0] = s4.z; S[m + 1][1] = s4.w;
             }
             const float* cp = ckP + (size_t(seg) * NW + wave) * DK;
@@ -372,7 +381,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
             const float4* sn = stash + size_t(tt) * SNAP;
 #pragma unroll
             for (int m = 0; m < RPT; m += 2) {
-                const float4 s4 = sn[tid * (RPT / 2) + m / 2];
+                const float4 s4 = sn[snap_idx<RPT>(tid, m)];
                 Spn[m][0] = s4.x; Spn[m][1] = s4.y; Spn[m + 1][0] = s4.z; Spn[m + 1][1] = s4.w;
             }
 #pragma unroll
