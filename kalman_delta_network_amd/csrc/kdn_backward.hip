@@ -52,10 +52,43 @@ constexpr int WCOLS = 8 * NC;  // memory columns per wave
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
+// Cross-lane exchanges without the LDS pipe: DPP within rows of 16 lanes
+// and the gfx950 row-swap instructions across rows.  Each pair sums a + b
+// on both sides, so every lane of a group ends with the same bits.
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15 - i within 16
+constexpr int DPP_ROR8 = 0x128;        // lane i <-> i ^ 8 within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// x[l] + x[l ^ 16] and x[l] + x[l ^ 32] in every lane
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// sum over the 64 lanes, in every lane
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    x += dpp<DPP_MIRROR>(x);
+    return add_xor32(add_xor16(x));
+}
+
+// sum over the 8 row groups (lane bits 3..5) of a memory wave, in every lane
+__device__ __forceinline__ float rowgroup_sum(float x) {
+    x += dpp<DPP_ROR8>(x);
+    return add_xor32(add_xor16(x));
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -199,9 +232,7 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
         }
     }
 #pragma unroll
-    for (int off = 8; off <= 32; off <<= 1)
-#pragma unroll
-        for (int j = 0; j < NC; ++j) Ak[j] += __shfl_xor(Ak[j], off, 64);
+    for (int j = 0; j < NC; ++j) Ak[j] = rowgroup_sum(Ak[j]);
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
 #pragma unroll
@@ -212,7 +243,9 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
 // In-place halving reduce-scatter over the 8 column-pair lanes of a row
 // group: on entry every lane holds N values; on exit lane cq holds, in
 // vals[0 .. N/8), the sums over the 8 lanes of flat entries
-// [cq * N / 8, (cq + 1) * N / 8).
+// [cq * N / 8, (cq + 1) * N / 8).  Step s pairs each lane with one whose
+// bit 2 - s differs (7 - cq, then cq ^ 2, then cq ^ 1); each keeps the half
+// its own bit selects and receives the partner's copy of that half.
 // The halves are chosen with a per-lane bit mask (one bitfield insert per
 // value) rather than a compare-and-select, which needs a lane mask in scalar
 // registers for every select.
@@ -224,14 +257,14 @@ template <int N>
 __device__ __forceinline__ void rowsum_scatter(float (&vals)[N], int cq) {
 #pragma unroll
     for (int step = 0; step < 3; ++step) {
-        const int X = 4 >> step;
         const int half = N >> (step + 1);
         const uint32_t hi = 0u - uint32_t((cq >> (2 - step)) & 1);  // all ones when bit X of cq is set
 #pragma unroll
         for (int f = 0; f < half; ++f) {
             const float keep = pick(hi, vals[f + half], vals[f]);
             const float send = pick(hi, vals[f], vals[f + half]);
-            vals[f] = keep + __shfl_xor(send, X, 64);
+            const float recv = step == 0 ? dpp<DPP_HALF_MIRROR>(send) : step == 1 ? dpp<DPP_XOR2>(send) : dpp<DPP_XOR1>(send);
+            vals[f] = keep + recv;
         }
     }
 }
@@ -432,12 +465,10 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
                     }
                 }
 #pragma unroll
-                for (int off = 8; off <= 32; off <<= 1)
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) {
-                        Ak[j] += __shfl_xor(Ak[j], off, 64);
-                        Ek[j] += __shfl_xor(Ek[j], off, 64);
-                    }
+                for (int j = 0; j < NC; ++j) {
+                    Ak[j] = rowgroup_sum(Ak[j]);
+                    Ek[j] = rowgroup_sum(Ek[j]);
+                }
                 float dl[NC];
 #pragma unroll
                 for (int j = 0; j < NC; ++j) dl[j] = vv[j] - Ak[j];
