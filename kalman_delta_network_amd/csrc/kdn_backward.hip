@@ -646,14 +646,17 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
 }
 
 // dc0[h] = sum over the batch and the channels of dp0 (the c0 gradient when
-// p_0 = c0[h] on every channel); fixed summation order
-__global__ void kdn_dc0_kernel(const float* __restrict__ dp0, float* __restrict__ dc0, int B, int H, int pd) {
-    const int h = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
-    if (h >= H) return;
+// p_0 = c0[h] on every channel): one wave per head, each lane summing a fixed
+// strided subset, then a fixed-order wave sum
+__global__ void __launch_bounds__(64) kdn_dc0_kernel(const float* __restrict__ dp0, float* __restrict__ dc0,
+                                                     int B, int H, int pd) {
+    const int h = int(blockIdx.x);
+    const int lane = int(threadIdx.x);
+    const long n = long(B) * pd;
     float acc = 0.f;
-    for (int b = 0; b < B; ++b)
-        for (int i = 0; i < pd; ++i) acc += dp0[(size_t(b) * H + h) * pd + i];
-    dc0[h] = acc;
+    for (long e = lane; e < n; e += 64) acc += dp0[(size_t(e / pd) * H + h) * pd + size_t(e % pd)];
+    acc = wave_sum(acc);
+    if (lane == 0) dc0[h] = acc;
 }
 
 template <int DK, int DV, int VAR, typename Tin>
@@ -690,8 +693,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     else return hipErrorNotSupported;
     if (e != hipSuccess || !a.dc0) return e;
     const int pd = a.variant == 0 ? a.dk : 1;
-    hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned((a.H + 63) / 64)), dim3(64), 0, stream, a.dp0, a.dc0, a.B,
-                       a.H, pd);
+    hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned(a.H)), dim3(64), 0, stream, a.dp0, a.dc0, a.B, a.H, pd);
     return hipGetLastError();
 }
 
