@@ -105,8 +105,9 @@ __device__ __forceinline__ void block_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// workspace floats per (batch, head): S and p checkpoints (p once per memory
-// wave, so that every lane reads back only what it wrote) and the stash
+// workspace floats per (batch, head, column tile of dv columns): S and p
+// checkpoints (p once per memory wave, so that every lane reads back only
+// what it wrote) and the stash
 __host__ __device__ inline size_t unit_floats(int T, int dk, int dv) {
     const size_t nseg = (size_t(T) + SEG - 1) / SEG;
     const size_t nw = size_t(dv) / WCOLS;
@@ -116,7 +117,6 @@ __host__ __device__ inline size_t unit_floats(int T, int dk, int dv) {
 template <int DK, int DV>
 struct BwdSmem {
     float4 seg_chan[SEG][DK];           // (alpha, k, q, kappa) of each token of the segment
-    float seg_p[SEG][DK];               // p_{t-1} of each token (isotropic forms: entry 0)
     float part[2][4][DV / WCOLS][DK];   // per-wave row sums: dq, d_kappa, dk_mem, dalpha_mem
     float4 chan[DV / WCOLS][DK];        // forward staging, one slice per memory wave
 };
@@ -269,18 +269,28 @@ __device__ __forceinline__ void rowsum_scatter(float (&vals)[N], int cq) {
     }
 }
 
+constexpr int TILE = 64;  // value columns per memory-adjoint workgroup
+
+// Memory adjoint of one (batch, head) pair over TILE value columns: the
+// checkpoint sweep, and per segment the re-run with the stash and the
+// reverse walk.  Each token's four per-row sums of the tile (dq, d_kappa,
+// dk_mem, dalpha_mem) go to the workspace for the uncertainty kernel; tile 0
+// also stores p_{t-1} of every token there.
 template <int DK, int DV, int VAR, typename Tin>
-__global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
-    constexpr int NW = DV / WCOLS;  // memory waves
-    constexpr int CPL = DK / 64;  // channels per lane
-    constexpr int RPT = DK / 8;   // memory rows per lane
-    constexpr int NT = NW * 64;   // memory threads
+__global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
+    constexpr int NTILE = DV / TILE;
+    constexpr int NW = TILE / WCOLS;  // memory waves
+    constexpr int CPL = DK / 64;      // channels per lane
+    constexpr int RPT = DK / 8;       // memory rows per lane
+    constexpr int NT = NW * 64;       // threads
     constexpr bool ISO = VAR != 0;
-    static_assert(DK % 64 == 0 && DV % 32 == 0, "unsupported tile");
+    static_assert(DK % 64 == 0 && DV % TILE == 0 && NW == 4, "unsupported tile");
 
-    __shared__ BwdSmem<DK, DV> sm;
+    __shared__ BwdSmem<DK, TILE> sm;
 
-    const int unit = int(blockIdx.x);
+    const int nunit = A.B * A.H;
+    const int tile = int(blockIdx.x) / nunit;  // the tiles of one head are nunit blocks apart
+    const int unit = int(blockIdx.x) % nunit;
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
@@ -289,16 +299,18 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
     const int tid = threadIdx.x;
     const int cq = lane & 7;
     const int rg = lane >> 3;
-    const int col = wave * WCOLS + cq * NC;
+    const int col = tile * TILE + wave * WCOLS + cq * NC;
     const int nseg = (T + SEG - 1) / SEG;
     const float mu = A.mu;
 
-    float* ckS = A.work + size_t(unit) * unit_floats(T, DK, DV);
-    float* ckP = ckS + size_t(nseg) * DK * DV;
+    float* ckS = A.work + (size_t(unit) * NTILE + tile) * unit_floats(T, DK, TILE);
+    float* ckP = ckS + size_t(nseg) * DK * TILE;
     // memory snapshots as float4 (m, m + 1) row pairs, see snap_idx
     float4* stash = reinterpret_cast<float4*>(ckP + size_t(nseg) * NW * DK);
     float4* ckS4 = reinterpret_cast<float4*>(ckS);
     constexpr int SNAP = NT * (RPT / 2);  // float4 per snapshot
+    float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);  // [unit][T][NTILE][4][DK]
+    float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;                    // [unit][T][DK]
     const size_t sbase = size_t(unit) * DK * DV;
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
 
@@ -341,8 +353,8 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
             for (int t = seg * SEG; t < (seg + 1) * SEG; ++t) {
                 TokIn<DK, VAR, Tin> xn;  // next token, issued before this one's arithmetic
                 load_tok(xn, A, tokidx(min(t + 1, T - 1)), lane, col, DV);
-                fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
-                                            tid);
+                fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
+                                              tid);
                 x = xn;
             }
         }
@@ -350,8 +362,6 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
 
     // ---- reverse sweep, segment by segment ----
     float dS[RPT][NC];
-    float dp[CPL];
-    float db = 0.f;
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + 8 * m;
@@ -362,17 +372,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
             dS[m][0] = dS[m][1] = 0.f;
         }
     }
-    if (wave == 0) {
-        if (ISO) {
-            db = A.dp_T ? A.dp_T[unit] : 0.f;
-        } else {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) dp[c] = A.dp_T ? A.dp_T[size_t(unit) * DK + lane + 64 * c] : 0.f;
-        }
-    }
     const Tin* dO = static_cast<const Tin*>(A.dO);
-    const Tin* omg = static_cast<const Tin*>(A.omega);
-    const Tin* rr = static_cast<const Tin*>(A.r);
     const Tin* vin = static_cast<const Tin*>(A.v);
 
     for (int seg = nseg - 1; seg >= 0; --seg) {
@@ -393,22 +393,23 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) p[c] = cp[lane + 64 * c];
             }
+            const bool rec = wave == 0;
+            const bool rec_p = rec && tile == 0;
             TokIn<DK, VAR, Tin> x;
             load_tok(x, A, tokidx(t0), lane, col, DV);
             for (int tt = 0; tt < n; ++tt) {
                 TokIn<DK, VAR, Tin> xn;
                 load_tok(xn, A, tokidx(t0 + min(tt + 1, n - 1)), lane, col, DV);
-                fwd_token<DK, DV, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], wave == 0 ? sm.seg_chan[tt] : nullptr,
-                                            wave == 0 ? sm.seg_p[tt] : nullptr, stash + size_t(tt) * SNAP,
-                                            lane, rg, tid);
+                fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], rec ? sm.seg_chan[tt] : nullptr,
+                                              rec_p ? pbuf + (size_t(unit) * T + t0 + tt) * DK : nullptr,
+                                              stash + size_t(tt) * SNAP, lane, rg, tid);
                 x = xn;
             }
         }
         block_lds_sync();
 
-        // one token ahead: the memory part's S_{t-1}, dO_t, v_t and the
-        // uncertainty part's omega_t, r_t
-        float Spn[RPT][NC], gn[NC], vvn[NC], wn[CPL], rn = 0.f;
+        // one token ahead: S_{t-1}, dO_t, v_t
+        float Spn[RPT][NC], gn[NC], vvn[NC];
         const auto load_rev = [&](int tt) {
             const size_t tok = tokidx(t0 + tt);
             const float4* sn = stash + size_t(tt) * SNAP;
@@ -423,18 +424,23 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
                 vvn[j] = to_f32(vin[tok * DV + col + j]);
             }
         };
-        const auto load_unc = [&](int tt) {
-            const size_t tok = tokidx(t0 + tt);
-            rn = to_f32(rr[tok]);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) wn[c] = VAR == 0 ? to_f32(omg[tok * DK + lane + 64 * c]) : to_f32(omg[tok]);
-        };
         load_rev(n - 1);
-        if (wave == 0) load_unc(n - 1);
 
-        // iteration it: the memory part takes token t0 + n - 1 - it, the
-        // uncertainty part (wave 0) the token of the iteration before
+        // iteration it: token t0 + n - 1 - it; wave w then writes the tile's
+        // sum of quantity w for the token of the iteration before
         for (int it = 0; it <= n; ++it) {
+            if (it >= 1) {
+                const int slot = (it - 1) & 1;
+                float* dst = partial + ((size_t(unit) * T + t0 + n - it) * NTILE + tile) * 4 * DK + size_t(wave) * DK;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int i = lane + 64 * c;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) acc += sm.part[slot][wave][w][i];
+                    dst[i] = acc;
+                }
+            }
             if (it < n) {
                 const int tt = n - 1 - it;
                 const size_t tok = tokidx(t0 + tt);
@@ -519,33 +525,86 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
                 for (int e = 0; e < RPT / 4; ++e)
                     sm.part[slot][2 + qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
             }
-            if (wave == 0 && it >= 1) {
-                const int tt = n - it;
-                const size_t tok = tokidx(t0 + tt);
-                const int slot = (it - 1) & 1;
-                const float rt = rn;
-                float wc[CPL];
+            block_lds_sync();
+        }
+    }
+
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) wc[c] = wn[c];
-                load_unc(max(tt - 1, 0));
-                float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL];
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + 8 * m;
+        *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
+    }
+}
+
+// Uncertainty adjoint of one (batch, head) pair, one wave (lane owns channels
+// lane and lane + 64), backwards over the tokens: sums the memory kernel's
+// per-tile row sums, writes dq, dk, dalpha, domega, dr and carries dp.
+template <int DK, int DV, int VAR, typename Tin>
+__global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
+    constexpr int NTILE = DV / TILE;
+    constexpr int CPL = DK / 64;
+    constexpr bool ISO = VAR != 0;
+    const int nunit = A.B * A.H;
+    const int unit = int(blockIdx.x);
+    const int h = unit % A.H;
+    const size_t b = size_t(unit / A.H);
+    const int T = A.T;
+    const int lane = threadIdx.x;
+    const float mu = A.mu;
+    const float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);
+    const float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;
+    const Tin* kin = static_cast<const Tin*>(A.k);
+    const Tin* ain = static_cast<const Tin*>(A.alpha);
+    const Tin* omg = static_cast<const Tin*>(A.omega);
+    const Tin* rr = static_cast<const Tin*>(A.r);
+    const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
+
+    float dp[CPL];
+    float db = 0.f;
+    if (ISO) {
+        db = A.dp_T ? A.dp_T[unit] : 0.f;
+    } else {
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int i = lane + 64 * c;
-                    const float4 c4 = sm.seg_chan[tt][i];
-                    al[c] = c4.x;
-                    kk[c] = c4.y;
-                    pp[c] = ISO ? 0.f : sm.seg_p[tt][i];
-                    gq[c] = gk[c] = gks[c] = ga[c] = 0.f;
+        for (int c = 0; c < CPL; ++c) dp[c] = A.dp_T ? A.dp_T[size_t(unit) * DK + lane + 64 * c] : 0.f;
+    }
+
+    // one token ahead: the tile sums, p_{t-1} and the token's alpha, k, omega, r
+    float nq[CPL], nk[CPL], nks[CPL], na[CPL], nal[CPL], nkk[CPL], npp[CPL], nw[CPL], nr = 0.f;
+    const auto load = [&](int t) {
+        const size_t tok = tokidx(t);
+        const float* src = partial + (size_t(unit) * T + t) * NTILE * 4 * DK;
 #pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        gq[c] += sm.part[slot][0][w][i];
-                        gk[c] += sm.part[slot][1][w][i];
-                        gks[c] += sm.part[slot][2][w][i];
-                        ga[c] += sm.part[slot][3][w][i];
-                    }
-                    A.dq[tok * DK + i] = gq[c];
-                }
+        for (int c = 0; c < CPL; ++c) {
+            const int i = lane + 64 * c;
+            nq[c] = nk[c] = nks[c] = na[c] = 0.f;
+#pragma unroll
+            for (int tl = 0; tl < NTILE; ++tl) {
+                nq[c] += src[(tl * 4 + 0) * DK + i];
+                nk[c] += src[(tl * 4 + 1) * DK + i];
+                nks[c] += src[(tl * 4 + 2) * DK + i];
+                na[c] += src[(tl * 4 + 3) * DK + i];
+            }
+            nal[c] = VAR == 1 ? to_f32(ain[tok]) : to_f32(ain[tok * DK + i]);
+            nkk[c] = to_f32(kin[tok * DK + i]);
+            npp[c] = ISO ? pbuf[(size_t(unit) * T + t) * DK] : pbuf[(size_t(unit) * T + t) * DK + i];
+            nw[c] = VAR == 0 ? to_f32(omg[tok * DK + i]) : to_f32(omg[tok]);
+        }
+        nr = to_f32(rr[tok]);
+    };
+    if (T > 0) load(T - 1);
+
+    for (int t = T - 1; t >= 0; --t) {
+        const size_t tok = tokidx(t);
+        float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL], wc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            al[c] = nal[c]; kk[c] = nkk[c]; pp[c] = npp[c]; wc[c] = nw[c];
+            gq[c] = nq[c]; gk[c] = nk[c]; gks[c] = nks[c]; ga[c] = na[c];
+        }
+        const float rt = nr;
+        load(max(t - 1, 0));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) A.dq[tok * DK + lane + 64 * c] = gq[c];
                 if (!ISO) {
                     // gain kappa = p_hat k / d, d = r + sum p_hat k^2; posterior
                     // p' = p_hat / (1 + u p_hat), u = (mu / r) k^2; predict
@@ -587,7 +646,7 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
                     // scalar gain beta = b_hat / (r + b_hat n), n = |k|^2; posterior
                     // b' = b_hat / (1 + c n b_hat), c = mu / (d_k r); predict
                     // b_hat = a b + omega / d_k, a = alpha^2 or mean_i alpha_i^2
-                    const float bprev = sm.seg_p[tt][0];
+                    const float bprev = pp[0];
                     const float w = wc[0];
                     float a2 = 0.f, nn = 0.f, kb = 0.f;
 #pragma unroll
@@ -625,23 +684,13 @@ __global__ void __launch_bounds__(DV * 4) kdn_backward_kernel(BwdArgs A) {
                     }
                     db = dbh * a2;
                 }
-            }
-            block_lds_sync();
-        }
     }
 
+    if (ISO) {
+        if (lane == 0) A.dp0[unit] = db;
+    } else {
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = rg + 8 * m;
-        *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
-    }
-    if (wave == 0) {
-        if (ISO) {
-            if (lane == 0) A.dp0[unit] = db;
-        } else {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) A.dp0[size_t(unit) * DK + lane + 64 * c] = dp[c];
-        }
+        for (int c = 0; c < CPL; ++c) A.dp0[size_t(unit) * DK + lane + 64 * c] = dp[c];
     }
 }
 
@@ -661,8 +710,12 @@ __global__ void __launch_bounds__(64) kdn_dc0_kernel(const float* __restrict__ d
 
 template <int DK, int DV, int VAR, typename Tin>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((kdn_backward_kernel<DK, DV, VAR, Tin>), dim3(unsigned(long(a.B) * a.H)),
-                       dim3(DV * 4), 0, stream, a);
+    const unsigned units = unsigned(long(a.B) * a.H);
+    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, VAR, Tin>), dim3(units * (DV / TILE)), dim3(TILE * 4), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kdn_backward_unc_kernel<DK, DV, VAR, Tin>), dim3(units), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -681,7 +734,9 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (long(B) * H == 0 || T == 0) return 0;
-    return size_t(B) * size_t(H) * unit_floats(T, dk, dv) * sizeof(float);
+    const size_t units = size_t(B) * size_t(H), ntile = size_t(dv) / TILE;
+    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1}
+    return (units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * (ntile * 4 + 1) * dk) * sizeof(float);
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
