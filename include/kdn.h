@@ -220,7 +220,7 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
                  float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
                  void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
- * B*H*((dv/64)*(ceil(T/32)*(64*dk + 4*dk) + 32*64*dk) + T*((dv/64)*4 + 1)*dk)*4
+ * B*H*((dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk) + T*((dv/64)*4 + 1)*dk)*4
  * (recomputation checkpoints per 64-column tile, plus per-token partial sums). */
 size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv);
 int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,

@@ -16,24 +16,25 @@
 //     part and carries dp backwards through the posterior, the gain and the
 //     prediction (dk, dalpha, domega, dr).
 //
-// One workgroup per (batch, head).  Waves 0 .. NW-1 (NW = d_v / 16) own the
-// memory columns: lane = (row group rg, column pair cq), holding rows rg + 8m
-// of 2 consecutive columns, so that each column reduction over the key
-// dimension stays inside one wave (registers, then 3 lane-xor steps).  Wave 0
-// also runs the uncertainty part (lane owns channels lane, lane + 64); with
-// d_v = 128 the eight waves sit two per SIMD and each may hold 256 VGPRs.
-// Every global load of the token loops is issued one token ahead.
+// Two kernels.  The memory kernel takes one workgroup per (batch, head, 64
+// value columns) with 8 waves: lane = (row group rg, column cq), holding rows
+// rg + 8m of one column, so that each column reduction over the key
+// dimension stays inside one wave (DPP within rows, row swaps across).  The
+// uncertainty kernel takes one wave per (batch, head) (lane owns channels
+// lane, lane + 64).  Every global load of the token loops is issued one
+// token ahead.
 //
 // The memory S_{t-1} is needed at every token of the reverse sweep.  A first
 // forward sweep stores a checkpoint of (S, p) every SEG tokens in the
 // workspace; then, segment by segment from the last, the memory waves re-run
 // the segment's forward from its checkpoint, storing each token's S_{t-1} in
-// a per-workgroup stash (workspace) and the token's (alpha, k, q, kappa) and
-// p_{t-1} in LDS, and walk the segment backwards.  The memory waves reduce
-// their four per-row partial sums (dq, d_kappa, dk_mem, dalpha_mem) over the
-// lanes of a row with a reduce-scatter and leave them in LDS; the uncertainty
-// part consumes them one token behind (double-buffered), so that the two
-// parts of consecutive tokens meet at one barrier per token.
+// a per-workgroup stash (workspace) and the token's (alpha, k, q, kappa) in
+// LDS (and p_{t-1} in the workspace), and walk the segment backwards.  They
+// reduce their four per-row partial sums (dq, d_kappa, dk_mem, dalpha_mem)
+// over the lanes of a row with a reduce-scatter, then over the waves through
+// LDS one token behind, and store the tile's sums per token in the
+// workspace; the uncertainty kernel adds the tiles and runs its part
+// backwards over the tokens.
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -46,7 +47,8 @@ namespace {
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 constexpr int SEG = 32;  // tokens per checkpoint segment
-constexpr int NC = 2;    // memory columns per lane
+constexpr int NC = 1;    // memory columns per lane
+constexpr int SG = 4 / NC;  // memory rows per float4 of a snapshot
 constexpr int WCOLS = 8 * NC;  // memory columns per wave
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -121,22 +123,37 @@ struct BwdSmem {
     float4 chan[DV / WCOLS][DK];        // forward staging, one slice per memory wave
 };
 
-// float4 index, within one memory snapshot, of rows (m, m + 1) of thread
-// tid: each wave owns RPT / 2 blocks of 64 float4 (1 KB), one per row pair,
-// with the lanes contiguous, so every snapshot access is one coalesced 1 KB
-// run per wave and the row pairs of a thread differ by immediate offsets
+// float4 index, within one memory snapshot, of rows m .. m + SG - 1 of
+// thread tid: each wave owns RPT / SG blocks of 64 float4 (1 KB), one per row
+// group, with the lanes contiguous, so every snapshot access is one coalesced
+// 1 KB run per wave and the row groups of a thread differ by immediate offsets
 template <int RPT>
 __device__ __forceinline__ int snap_idx(int tid, int m) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    return (wave * (RPT / 2) + m / 2) * 64 + (tid & 63);
+    return (wave * (RPT / SG) + m / SG) * 64 + (tid & 63);
 }
 
+// rows m .. m + SG - 1 (all NC columns) of a lane's memory block as one float4
+template <int RPT>
+__device__ __forceinline__ float4 snap_pack(const float (&S)[RPT][NC], int m) {
+    return make_float4(S[m + 0 / NC][0 % NC], S[m + 1 / NC][1 % NC], S[m + 2 / NC][2 % NC], S[m + 3 / NC][3 % NC]);
+}
+template <int RPT>
+__device__ __forceinline__ void snap_unpack(float (&S)[RPT][NC], int m, float4 v) {
+    S[m + 0 / NC][0 % NC] = v.x;
+    S[m + 1 / NC][1 % NC] = v.y;
+    S[m + 2 / NC][2 % NC] = v.z;
+    S[m + 3 / NC][3 % NC] = v.w;
+}
+
+// One token's inputs as loaded (raw bf16 or fp32): a prefetch is converted
+// where it is used, so that nothing waits for it earlier.
 template <int DK, int VAR, typename Tin>
 struct TokIn {
     static constexpr int CPL = DK / 64;
-    float k[CPL], q[CPL], a[CPL], w[CPL];
-    float r;
-    float v[NC];
+    Tin k[CPL], q[CPL], a[CPL], w[CPL];
+    Tin r;
+    Tin v[NC];
 };
 
 template <int DK, int VAR, typename Tin>
@@ -152,14 +169,14 @@ __device__ __forceinline__ void load_tok(TokIn<DK, VAR, Tin>& x, const BwdArgs& 
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const size_t e = tok * DK + lane + 64 * c;
-        x.k[c] = to_f32(k[e]);
-        x.q[c] = to_f32(q[e]);
-        x.a[c] = VAR == 1 ? to_f32(al[tok]) : to_f32(al[e]);
-        x.w[c] = VAR == 0 ? to_f32(om[e]) : to_f32(om[tok]);
+        x.k[c] = k[e];
+        x.q[c] = q[e];
+        x.a[c] = VAR == 1 ? al[tok] : al[e];
+        x.w[c] = VAR == 0 ? om[e] : om[tok];
     }
-    x.r = to_f32(r[tok]);
+    x.r = r[tok];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) x.v[j] = to_f32(v[tok * DVv + col + j]);
+    for (int j = 0; j < NC; ++j) x.v[j] = v[tok * DVv + col + j];
 }
 
 // One forward token on a memory wave's columns (the recurrent forward's
@@ -173,51 +190,61 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
                                           int rg, int tid) {
     constexpr int CPL = DK / 64, RPT = DK / 8;
     constexpr bool ISO = VAR != 0;
+    float xk[CPL], xq[CPL], xa[CPL], xw[CPL], xv[NC];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        xk[c] = to_f32(x.k[c]);
+        xq[c] = to_f32(x.q[c]);
+        xa[c] = to_f32(x.a[c]);
+        xw[c] = to_f32(x.w[c]);
+    }
+    const float xr = to_f32(x.r);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) xv[j] = to_f32(x.v[j]);
     float kap[CPL];
     if (ISO) {
         float a2 = 0.f, n = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            a2 += x.a[c] * x.a[c];
-            n += x.k[c] * x.k[c];
+            a2 += xa[c] * xa[c];
+            n += xk[c] * xk[c];
         }
-        a2 = VAR == 2 ? wave_sum(a2) * (1.0f / float(DK)) : x.a[0] * x.a[0];
+        a2 = VAR == 2 ? wave_sum(a2) * (1.0f / float(DK)) : xa[0] * xa[0];
         n = wave_sum(n);
-        const float bh = a2 * pb + x.w[0] * (1.0f / float(DK));
-        const float beta = bh / (x.r + bh * n);
+        const float bh = a2 * pb + xw[0] * (1.0f / float(DK));
+        const float beta = bh / (xr + bh * n);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) kap[c] = beta * x.k[c];
+        for (int c = 0; c < CPL; ++c) kap[c] = beta * xk[c];
         if (rec_p && lane == 0) rec_p[0] = pb;
-        pb = bh / (1.0f + (mu / (float(DK) * x.r)) * n * bh);
+        pb = bh / (1.0f + (mu / (float(DK) * xr)) * n * bh);
     } else {
         float ph[CPL];
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            ph[c] = x.a[c] * x.a[c] * p[c] + x.w[c];
-            s += ph[c] * x.k[c] * x.k[c];
+            ph[c] = xa[c] * xa[c] * p[c] + xw[c];
+            s += ph[c] * xk[c] * xk[c];
         }
         s = wave_sum(s);
-        const float inv = 1.0f / (x.r + s);
-        const float mr = mu / x.r;
+        const float inv = 1.0f / (xr + s);
+        const float mr = mu / xr;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            kap[c] = ph[c] * x.k[c] * inv;
+            kap[c] = ph[c] * xk[c] * inv;
             if (rec_p) rec_p[lane + 64 * c] = p[c];
-            p[c] = ph[c] / (1.0f + mr * x.k[c] * x.k[c] * ph[c]);
+            p[c] = ph[c] / (1.0f + mr * xk[c] * xk[c] * ph[c]);
         }
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const float4 e = make_float4(x.a[c], x.k[c], x.q[c], kap[c]);
+        const float4 e = make_float4(xa[c], xk[c], xq[c], kap[c]);
         chanw[lane + 64 * c] = e;
         if (rec_chan) rec_chan[lane + 64 * c] = e;
     }
     wave_lds_sync();
     if (stash_tok) {
 #pragma unroll
-        for (int m = 0; m < RPT; m += 2)
-            stash_tok[snap_idx<RPT>(tid, m)] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
+        for (int m = 0; m < RPT; m += SG) stash_tok[snap_idx<RPT>(tid, m)] = snap_pack<RPT>(S, m);
     }
     float Ak[NC] = {};
     float kr[RPT];
@@ -236,11 +263,11 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
 #pragma unroll
-        for (int j = 0; j < NC; ++j) S[m][j] += kr[m] * (x.v[j] - Ak[j]);
+        for (int j = 0; j < NC; ++j) S[m][j] += kr[m] * (xv[j] - Ak[j]);
     wave_lds_sync();  // chanw is rewritten by the next token
 }
 
-// In-place halving reduce-scatter over the 8 column-pair lanes of a row
+// In-place halving reduce-scatter over the 8 column lanes of a row
 // group: on entry every lane holds N values; on exit lane cq holds, in
 // vals[0 .. N/8), the sums over the 8 lanes of flat entries
 // [cq * N / 8, (cq + 1) * N / 8).  Step s pairs each lane with one whose
@@ -277,14 +304,14 @@ constexpr int TILE = 64;  // value columns per memory-adjoint workgroup
 // dk_mem, dalpha_mem) go to the workspace for the uncertainty kernel; tile 0
 // also stores p_{t-1} of every token there.
 template <int DK, int DV, int VAR, typename Tin>
-__global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
+__global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(BwdArgs A) {
     constexpr int NTILE = DV / TILE;
     constexpr int NW = TILE / WCOLS;  // memory waves
     constexpr int CPL = DK / 64;      // channels per lane
     constexpr int RPT = DK / 8;       // memory rows per lane
     constexpr int NT = NW * 64;       // threads
     constexpr bool ISO = VAR != 0;
-    static_assert(DK % 64 == 0 && DV % TILE == 0 && NW == 4, "unsupported tile");
+    static_assert(DK % 64 == 0 && DV % TILE == 0 && NW >= 4, "unsupported tile");
 
     __shared__ BwdSmem<DK, TILE> sm;
 
@@ -308,7 +335,7 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
     // memory snapshots as float4 (m, m + 1) row pairs, see snap_idx
     float4* stash = reinterpret_cast<float4*>(ckP + size_t(nseg) * NW * DK);
     float4* ckS4 = reinterpret_cast<float4*>(ckS);
-    constexpr int SNAP = NT * (RPT / 2);  // float4 per snapshot
+    constexpr int SNAP = NT * (RPT / SG);  // float4 per snapshot
     float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);  // [unit][T][NTILE][4][DK]
     float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;                    // [unit][T][DK]
     const size_t sbase = size_t(unit) * DK * DV;
@@ -322,12 +349,8 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + 8 * m;
-            if (A.S0) {
-                const float2 s2 = *reinterpret_cast<const float2*>(A.S0 + sbase + size_t(i) * DV + col);
-                S[m][0] = s2.x; S[m][1] = s2.y;
-            } else {
-                S[m][0] = S[m][1] = 0.f;
-            }
+#pragma unroll
+            for (int j = 0; j < NC; ++j) S[m][j] = A.S0 ? A.S0[sbase + size_t(i) * DV + col + j] : 0.f;
         }
         if (ISO) {
             pb = A.p0 ? A.p0[unit] : A.c0[h];
@@ -338,8 +361,7 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
         for (int seg = 0; seg < nseg; ++seg) {
             float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
-            for (int m = 0; m < RPT; m += 2)
-                ck[snap_idx<RPT>(tid, m)] = make_float4(S[m][0], S[m][1], S[m + 1][0], S[m + 1][1]);
+            for (int m = 0; m < RPT; m += SG) ck[snap_idx<RPT>(tid, m)] = snap_pack<RPT>(S, m);
             float* cp = ckP + (size_t(seg) * NW + wave) * DK;
             if (ISO) {
                 if (lane == 0) cp[0] = pb;
@@ -348,14 +370,17 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
                 for (int c = 0; c < CPL; ++c) cp[lane + 64 * c] = p[c];
             }
             if (seg == nseg - 1) break;  // the last segment's tokens are re-run below
-            TokIn<DK, VAR, Tin> x;
-            load_tok(x, A, tokidx(seg * SEG), lane, col, DV);
-            for (int t = seg * SEG; t < (seg + 1) * SEG; ++t) {
-                TokIn<DK, VAR, Tin> xn;  // next token, issued before this one's arithmetic
-                load_tok(xn, A, tokidx(min(t + 1, T - 1)), lane, col, DV);
-                fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
+            // two token buffers used in turn: the next token is issued before this
+            // one's arithmetic, and no register copy has to wait for it
+            TokIn<DK, VAR, Tin> xa, xb;
+            load_tok(xa, A, tokidx(seg * SEG), lane, col, DV);
+            for (int t = seg * SEG; t < (seg + 1) * SEG; t += 2) {
+                load_tok(xb, A, tokidx(t + 1), lane, col, DV);
+                fwd_token<DK, TILE, VAR, Tin>(xa, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
                                               tid);
-                x = xn;
+                load_tok(xa, A, tokidx(min(t + 2, T - 1)), lane, col, DV);
+                fwd_token<DK, TILE, VAR, Tin>(xb, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
+                                              tid);
             }
         }
     }
@@ -365,15 +390,12 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + 8 * m;
-        if (A.dS_T) {
-            const float2 s2 = *reinterpret_cast<const float2*>(A.dS_T + sbase + size_t(i) * DV + col);
-            dS[m][0] = s2.x; dS[m][1] = s2.y;
-        } else {
-            dS[m][0] = dS[m][1] = 0.f;
-        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) dS[m][j] = A.dS_T ? A.dS_T[sbase + size_t(i) * DV + col + j] : 0.f;
     }
-    const Tin* dO = static_cast<const Tin*>(A.dO);
     const Tin* vin = static_cast<const Tin*>(A.v);
+    const Tin* g_src = A.dO ? static_cast<const Tin*>(A.dO) : vin;
+    const float g_scale = A.dO ? 1.0f : 0.0f;
 
     for (int seg = nseg - 1; seg >= 0; --seg) {
         const int t0 = seg * SEG;
@@ -382,10 +404,7 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
             // re-run the segment from its checkpoint, recording what the reverse sweep needs
             const float4* ck = ckS4 + size_t(seg) * SNAP;
 #pragma unroll
-            for (int m = 0; m < RPT; m += 2) {
-                const float4 s4 = ck[snap_idx<RPT>(tid, m)];
-                S[m][0] = s4.x; S[m][1] = s4.y; S[m + 1][0] = s4.z; S[m + 1][1] = s4.w;
-            }
+            for (int m = 0; m < RPT; m += SG) snap_unpack<RPT>(S, m, ck[snap_idx<RPT>(tid, m)]);
             const float* cp = ckP + (size_t(seg) * NW + wave) * DK;
             if (ISO) {
                 pb = cp[0];
@@ -395,41 +414,47 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
             }
             const bool rec = wave == 0;
             const bool rec_p = rec && tile == 0;
-            TokIn<DK, VAR, Tin> x;
-            load_tok(x, A, tokidx(t0), lane, col, DV);
-            for (int tt = 0; tt < n; ++tt) {
-                TokIn<DK, VAR, Tin> xn;
-                load_tok(xn, A, tokidx(t0 + min(tt + 1, n - 1)), lane, col, DV);
+            const auto run = [&](const TokIn<DK, VAR, Tin>& x, int tt) {
                 fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], rec ? sm.seg_chan[tt] : nullptr,
                                               rec_p ? pbuf + (size_t(unit) * T + t0 + tt) * DK : nullptr,
                                               stash + size_t(tt) * SNAP, lane, rg, tid);
-                x = xn;
+            };
+            TokIn<DK, VAR, Tin> xa, xb;
+            load_tok(xa, A, tokidx(t0), lane, col, DV);
+            for (int tt = 0; tt < n; tt += 2) {
+                load_tok(xb, A, tokidx(t0 + min(tt + 1, n - 1)), lane, col, DV);
+                run(xa, tt);
+                if (tt + 1 < n) {
+                    load_tok(xa, A, tokidx(t0 + min(tt + 2, n - 1)), lane, col, DV);
+                    run(xb, tt + 1);
+                }
             }
         }
         block_lds_sync();
 
-        // one token ahead: S_{t-1}, dO_t, v_t
-        float Spn[RPT][NC], gn[NC], vvn[NC];
-        const auto load_rev = [&](int tt) {
+        // one token ahead, in two buffers used in turn: S_{t-1}, dO_t, v_t
+        struct RevIn {
+            float Sp[RPT][NC];
+            Tin g[NC], v[NC];
+        };
+        const auto load_rev = [&](RevIn& r, int tt) {
             const size_t tok = tokidx(t0 + tt);
             const float4* sn = stash + size_t(tt) * SNAP;
 #pragma unroll
-            for (int m = 0; m < RPT; m += 2) {
-                const float4 s4 = sn[snap_idx<RPT>(tid, m)];
-                Spn[m][0] = s4.x; Spn[m][1] = s4.y; Spn[m + 1][0] = s4.z; Spn[m + 1][1] = s4.w;
-            }
+            for (int m = 0; m < RPT; m += SG) snap_unpack<RPT>(r.Sp, m, sn[snap_idx<RPT>(tid, m)]);
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
-                gn[j] = dO ? to_f32(dO[tok * DV + col + j]) : 0.f;
-                vvn[j] = to_f32(vin[tok * DV + col + j]);
+                // unconditional load (a branch here makes the compiler wait for
+                // the prefetch at once): without dO, read v and scale by zero
+                r.g[j] = g_src[tok * DV + col + j];
+                r.v[j] = vin[tok * DV + col + j];
             }
         };
-        load_rev(n - 1);
 
-        // iteration it: token t0 + n - 1 - it; wave w then writes the tile's
-        // sum of quantity w for the token of the iteration before
-        for (int it = 0; it <= n; ++it) {
-            if (it >= 1) {
+        // iteration it: token t0 + n - 1 - it; wave w < 4 first writes the
+        // tile's sum of quantity w for the token of the iteration before
+        const auto iter = [&](int it, const RevIn& cur, RevIn& nxt) {
+            if (it >= 1 && wave < 4) {
                 const int slot = (it - 1) & 1;
                 float* dst = partial + ((size_t(unit) * T + t0 + n - it) * NTILE + tile) * 4 * DK + size_t(wave) * DK;
 #pragma unroll
@@ -445,17 +470,14 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
                 const int tt = n - 1 - it;
                 const size_t tok = tokidx(t0 + tt);
                 const int slot = it & 1;
-                float Sp[RPT][NC], g[NC], vv[NC];  // S_{t-1}, dO_t, v_t
-#pragma unroll
-                for (int m = 0; m < RPT; ++m) {
-                    Sp[m][0] = Spn[m][0]; Sp[m][1] = Spn[m][1];
-                }
+                const float (&Sp)[RPT][NC] = cur.Sp;  // S_{t-1}
+                float g[NC], vv[NC];                   // dO_t, v_t
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
-                    g[j] = gn[j];
-                    vv[j] = vvn[j];
+                    g[j] = g_scale * to_f32(cur.g[j]);
+                    vv[j] = to_f32(cur.v[j]);
                 }
-                load_rev(max(tt - 1, 0));
+                load_rev(nxt, max(tt - 1, 0));
                 const float4* crow = sm.seg_chan[tt];
                 // innovation delta = v - S_hat^T k, with S_hat = diag(alpha) S_{t-1};
                 // readout cotangent into dS, then d_delta = dS^T kappa
@@ -478,7 +500,10 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
                 float dl[NC];
 #pragma unroll
                 for (int j = 0; j < NC; ++j) dl[j] = vv[j] - Ak[j];
-                if (rg == 0) *reinterpret_cast<float2*>(A.dv_ + tok * DV + col) = make_float2(Ek[0], Ek[1]);
+                if (rg == 0) {
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) A.dv_[tok * DV + col + j] = Ek[j];
+                }
                 // per-row partial sums over the lane's 2 columns, two quantities
                 // at a time: [0] dq = S' dO, [1] d_kappa = dS delta, then
                 // [2] dk_mem = -S_hat d_delta, [3] dalpha_mem = sum S_{t-1} (.) dS_hat
@@ -526,13 +551,20 @@ __global__ void __launch_bounds__(TILE * 4) kdn_backward_mem_kernel(BwdArgs A) {
                     sm.part[slot][2 + qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
             }
             block_lds_sync();
+        };
+        RevIn ra, rb;
+        load_rev(ra, n - 1);
+        for (int it = 0; it <= n; it += 2) {
+            iter(it, ra, rb);
+            if (it + 1 <= n) iter(it + 1, rb, ra);
         }
     }
 
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + 8 * m;
-        *reinterpret_cast<float2*>(A.dS0 + sbase + size_t(i) * DV + col) = make_float2(dS[m][0], dS[m][1]);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) A.dS0[sbase + size_t(i) * DV + col + j] = dS[m][j];
     }
 }
 
@@ -568,41 +600,43 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
         for (int c = 0; c < CPL; ++c) dp[c] = A.dp_T ? A.dp_T[size_t(unit) * DK + lane + 64 * c] : 0.f;
     }
 
-    // one token ahead: the tile sums, p_{t-1} and the token's alpha, k, omega, r
-    float nq[CPL], nk[CPL], nks[CPL], na[CPL], nal[CPL], nkk[CPL], npp[CPL], nw[CPL], nr = 0.f;
-    const auto load = [&](int t) {
+    // one token ahead, in two buffers used in turn: the tile sums, p_{t-1}
+    // and the token's alpha, k, omega, r
+    struct UncIn {
+        float q[CPL], k[CPL], ks[CPL], a[CPL], pp[CPL];
+        Tin al[CPL], kk[CPL], w[CPL], r;
+    };
+    const auto load = [&](UncIn& u, int t) {
         const size_t tok = tokidx(t);
         const float* src = partial + (size_t(unit) * T + t) * NTILE * 4 * DK;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int i = lane + 64 * c;
-            nq[c] = nk[c] = nks[c] = na[c] = 0.f;
+            u.q[c] = u.k[c] = u.ks[c] = u.a[c] = 0.f;
 #pragma unroll
             for (int tl = 0; tl < NTILE; ++tl) {
-                nq[c] += src[(tl * 4 + 0) * DK + i];
-                nk[c] += src[(tl * 4 + 1) * DK + i];
-                nks[c] += src[(tl * 4 + 2) * DK + i];
-                na[c] += src[(tl * 4 + 3) * DK + i];
+                u.q[c] += src[(tl * 4 + 0) * DK + i];
+                u.k[c] += src[(tl * 4 + 1) * DK + i];
+                u.ks[c] += src[(tl * 4 + 2) * DK + i];
+                u.a[c] += src[(tl * 4 + 3) * DK + i];
             }
-            nal[c] = VAR == 1 ? to_f32(ain[tok]) : to_f32(ain[tok * DK + i]);
-            nkk[c] = to_f32(kin[tok * DK + i]);
-            npp[c] = ISO ? pbuf[(size_t(unit) * T + t) * DK] : pbuf[(size_t(unit) * T + t) * DK + i];
-            nw[c] = VAR == 0 ? to_f32(omg[tok * DK + i]) : to_f32(omg[tok]);
+            u.al[c] = VAR == 1 ? ain[tok] : ain[tok * DK + i];
+            u.kk[c] = kin[tok * DK + i];
+            u.pp[c] = ISO ? pbuf[(size_t(unit) * T + t) * DK] : pbuf[(size_t(unit) * T + t) * DK + i];
+            u.w[c] = VAR == 0 ? omg[tok * DK + i] : omg[tok];
         }
-        nr = to_f32(rr[tok]);
+        u.r = rr[tok];
     };
-    if (T > 0) load(T - 1);
-
-    for (int t = T - 1; t >= 0; --t) {
+    const auto step = [&](int t, const UncIn& u, UncIn& nxt) {
         const size_t tok = tokidx(t);
         float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL], wc[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            al[c] = nal[c]; kk[c] = nkk[c]; pp[c] = npp[c]; wc[c] = nw[c];
-            gq[c] = nq[c]; gk[c] = nk[c]; gks[c] = nks[c]; ga[c] = na[c];
+            al[c] = to_f32(u.al[c]); kk[c] = to_f32(u.kk[c]); pp[c] = u.pp[c]; wc[c] = to_f32(u.w[c]);
+            gq[c] = u.q[c]; gk[c] = u.k[c]; gks[c] = u.ks[c]; ga[c] = u.a[c];
         }
-        const float rt = nr;
-        load(max(t - 1, 0));
+        const float rt = to_f32(u.r);
+        load(nxt, max(t - 1, 0));
 #pragma unroll
         for (int c = 0; c < CPL; ++c) A.dq[tok * DK + lane + 64 * c] = gq[c];
                 if (!ISO) {
@@ -684,7 +718,14 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
                     }
                     db = dbh * a2;
                 }
+    };
+    UncIn ua, ub;
+    if (T > 0) load(ua, T - 1);
+    for (int t = T - 1; t >= 0; t -= 2) {
+        step(t, ua, ub);
+        if (t - 1 >= 0) step(t - 1, ub, ua);
     }
+
 
     if (ISO) {
         if (lane == 0) A.dp0[unit] = db;
@@ -711,7 +752,7 @@ __global__ void __launch_bounds__(64) kdn_dc0_kernel(const float* __restrict__ d
 template <int DK, int DV, int VAR, typename Tin>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
     const unsigned units = unsigned(long(a.B) * a.H);
-    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, VAR, Tin>), dim3(units * (DV / TILE)), dim3(TILE * 4), 0,
+    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, VAR, Tin>), dim3(units * (DV / TILE)), dim3(TILE / WCOLS * 64), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
