@@ -21,8 +21,8 @@
 // rg + 8m of one column, so that each column reduction over the key
 // dimension stays inside one wave (DPP within rows, row swaps across).  The
 // uncertainty kernel takes one wave per (batch, head) (lane owns channels
-// lane, lane + 64).  Every global load of the token loops is issued one
-// token ahead.
+// lane, lane + 64).  Every global load of the token loops is issued three
+// tokens ahead into a ring of four buffers.
 //
 // The memory S_{t-1} is needed at every token of the reverse sweep.  A first
 // forward sweep stores a checkpoint of (S, p) every SEG tokens in the
@@ -49,6 +49,7 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 constexpr int SEG = 32;  // tokens per checkpoint segment
 constexpr int NC = 1;    // memory columns per lane
 constexpr int SG = 4 / NC;  // memory rows per float4 of a snapshot
+constexpr int PF = 4;       // prefetch ring: token loads are issued PF - 1 tokens ahead
 constexpr int WCOLS = 8 * NC;  // memory columns per wave
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -311,7 +312,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     constexpr int RPT = DK / 8;       // memory rows per lane
     constexpr int NT = NW * 64;       // threads
     constexpr bool ISO = VAR != 0;
-    static_assert(DK % 64 == 0 && DV % TILE == 0 && NW >= 4, "unsupported tile");
+    static_assert(DK % 64 == 0 && DV % TILE == 0 && NW >= 4 && SEG % PF == 0, "unsupported tile");
 
     __shared__ BwdSmem<DK, TILE> sm;
 
@@ -370,17 +371,29 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
                 for (int c = 0; c < CPL; ++c) cp[lane + 64 * c] = p[c];
             }
             if (seg == nseg - 1) break;  // the last segment's tokens are re-run below
-            // two token buffers used in turn: the next token is issued before this
-            // one's arithmetic, and no register copy has to wait for it
-            TokIn<DK, VAR, Tin> xa, xb;
-            load_tok(xa, A, tokidx(seg * SEG), lane, col, DV);
-            for (int t = seg * SEG; t < (seg + 1) * SEG; t += 2) {
-                load_tok(xb, A, tokidx(t + 1), lane, col, DV);
-                fwd_token<DK, TILE, VAR, Tin>(xa, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
+            // a ring of PF token buffers used in turn: token t + PF - 1 is issued
+            // before token t's arithmetic, and no register copy waits for a load
+            const int s0 = seg * SEG;
+            const auto ld = [&](TokIn<DK, VAR, Tin>& x, int t) {
+                load_tok(x, A, tokidx(min(t, T - 1)), lane, col, DV);
+            };
+            const auto run = [&](const TokIn<DK, VAR, Tin>& x) {
+                fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
                                               tid);
-                load_tok(xa, A, tokidx(min(t + 2, T - 1)), lane, col, DV);
-                fwd_token<DK, TILE, VAR, Tin>(xb, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
-                                              tid);
+            };
+            TokIn<DK, VAR, Tin> x0, x1, x2, x3;
+            ld(x0, s0);
+            ld(x1, s0 + 1);
+            ld(x2, s0 + 2);
+            for (int t = s0; t < s0 + SEG; t += PF) {
+                ld(x3, t + 3);
+                run(x0);
+                ld(x0, t + 4);
+                run(x1);
+                ld(x1, t + 5);
+                run(x2);
+                ld(x2, t + 6);
+                run(x3);
             }
         }
     }
@@ -419,20 +432,27 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
                                               rec_p ? pbuf + (size_t(unit) * T + t0 + tt) * DK : nullptr,
                                               stash + size_t(tt) * SNAP, lane, rg, tid);
             };
-            TokIn<DK, VAR, Tin> xa, xb;
-            load_tok(xa, A, tokidx(t0), lane, col, DV);
-            for (int tt = 0; tt < n; tt += 2) {
-                load_tok(xb, A, tokidx(t0 + min(tt + 1, n - 1)), lane, col, DV);
-                run(xa, tt);
-                if (tt + 1 < n) {
-                    load_tok(xa, A, tokidx(t0 + min(tt + 2, n - 1)), lane, col, DV);
-                    run(xb, tt + 1);
-                }
+            const auto ld = [&](TokIn<DK, VAR, Tin>& x, int tt) {
+                load_tok(x, A, tokidx(t0 + min(tt, n - 1)), lane, col, DV);
+            };
+            TokIn<DK, VAR, Tin> x0, x1, x2, x3;
+            ld(x0, 0);
+            ld(x1, 1);
+            ld(x2, 2);
+            for (int tt = 0; tt < n; tt += PF) {  // loads are always issued (clamped)
+                ld(x3, tt + 3);
+                run(x0, tt);
+                ld(x0, tt + 4);
+                if (tt + 1 < n) run(x1, tt + 1);
+                ld(x1, tt + 5);
+                if (tt + 2 < n) run(x2, tt + 2);
+                ld(x2, tt + 6);
+                if (tt + 3 < n) run(x3, tt + 3);
             }
         }
         block_lds_sync();
 
-        // one token ahead, in two buffers used in turn: S_{t-1}, dO_t, v_t
+        // PF - 1 tokens ahead, in a ring of PF buffers: S_{t-1}, dO_t, v_t
         struct RevIn {
             float Sp[RPT][NC];
             Tin g[NC], v[NC];
@@ -453,7 +473,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
 
         // iteration it: token t0 + n - 1 - it; wave w < 4 first writes the
         // tile's sum of quantity w for the token of the iteration before
-        const auto iter = [&](int it, const RevIn& cur, RevIn& nxt) {
+        const auto iter = [&](int it, const RevIn& cur, RevIn& ahead) {
             if (it >= 1 && wave < 4) {
                 const int slot = (it - 1) & 1;
                 float* dst = partial + ((size_t(unit) * T + t0 + n - it) * NTILE + tile) * 4 * DK + size_t(wave) * DK;
@@ -477,14 +497,21 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
                     g[j] = g_scale * to_f32(cur.g[j]);
                     vv[j] = to_f32(cur.v[j]);
                 }
-                load_rev(nxt, max(tt - 1, 0));
+                load_rev(ahead, max(tt - (PF - 1), 0));
                 const float4* crow = sm.seg_chan[tt];
                 // innovation delta = v - S_hat^T k, with S_hat = diag(alpha) S_{t-1};
                 // readout cotangent into dS, then d_delta = dS^T kappa
+                // the row operands are read from LDS once per token and kept for
+                // the three passes (re-reading them in each pass made the LDS
+                // return path the limit: 8 waves x 16 rows x 16 B per pass)
+                float ra[RPT], rk[RPT], rkap[RPT];
                 float Ak[NC] = {}, Ek[NC] = {};
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
                     const float4 c4 = crow[rg + 8 * m];  // (alpha, k, q, kappa) of row rg + 8m
+                    ra[m] = c4.x;
+                    rk[m] = c4.y;
+                    rkap[m] = c4.w;
 #pragma unroll
                     for (int j = 0; j < NC; ++j) {
                         Ak[j] += c4.x * Sp[m][j] * c4.y;
@@ -504,23 +531,19 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
 #pragma unroll
                     for (int j = 0; j < NC; ++j) A.dv_[tok * DV + col + j] = Ek[j];
                 }
-                // per-row partial sums over the lane's 2 columns, two quantities
+                // per-row partial sums over the lane's columns, two quantities
                 // at a time: [0] dq = S' dO, [1] d_kappa = dS delta, then
                 // [2] dk_mem = -S_hat d_delta, [3] dalpha_mem = sum S_{t-1} (.) dS_hat
                 // (and dS <- diag(alpha) dS_hat); after each reduce-scatter lane cq
                 // holds quantity cq / 4 of the pair for rows 4 (cq & 3) + e
                 const int qh = cq >> 2;
                 float vals[2 * RPT];
-                // re-read the row operands from LDS in each pass instead of
-                // keeping all of them live across the passes
-                __asm__ volatile("" ::: "memory");
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
-                    const float4 c4 = crow[rg + 8 * m];
                     float pq = 0.f, pk = 0.f;
 #pragma unroll
                     for (int j = 0; j < NC; ++j) {
-                        pq += (c4.x * Sp[m][j] + c4.w * dl[j]) * g[j];
+                        pq += (ra[m] * Sp[m][j] + rkap[m] * dl[j]) * g[j];
                         pk += dS[m][j] * dl[j];
                     }
                     vals[m] = pq;
@@ -530,17 +553,15 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
 #pragma unroll
                 for (int e = 0; e < RPT / 4; ++e)
                     sm.part[slot][qh][wave][rg + 8 * ((cq & 3) * (RPT / 4) + e)] = vals[e];
-                __asm__ volatile("" ::: "memory");
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
-                    const float4 c4 = crow[rg + 8 * m];
                     float pks = 0.f, pa = 0.f;
 #pragma unroll
                     for (int j = 0; j < NC; ++j) {
-                        pks -= c4.x * Sp[m][j] * Ek[j];
-                        const float dsh = dS[m][j] - c4.y * Ek[j];
+                        pks -= ra[m] * Sp[m][j] * Ek[j];
+                        const float dsh = dS[m][j] - rk[m] * Ek[j];
                         pa += Sp[m][j] * dsh;
-                        dS[m][j] = c4.x * dsh;
+                        dS[m][j] = ra[m] * dsh;
                     }
                     vals[m] = pks;
                     vals[RPT + m] = pa;
@@ -552,11 +573,15 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
             }
             block_lds_sync();
         };
-        RevIn ra, rb;
-        load_rev(ra, n - 1);
-        for (int it = 0; it <= n; it += 2) {
-            iter(it, ra, rb);
-            if (it + 1 <= n) iter(it + 1, rb, ra);
+        RevIn r0, r1, r2, r3;
+        load_rev(r0, n - 1);
+        load_rev(r1, max(n - 2, 0));
+        load_rev(r2, max(n - 3, 0));
+        for (int it = 0; it <= n; it += PF) {
+            iter(it, r0, r3);
+            if (it + 1 <= n) iter(it + 1, r1, r0);
+            if (it + 2 <= n) iter(it + 2, r2, r1);
+            if (it + 3 <= n) iter(it + 3, r3, r2);
         }
     }
 
@@ -600,7 +625,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
         for (int c = 0; c < CPL; ++c) dp[c] = A.dp_T ? A.dp_T[size_t(unit) * DK + lane + 64 * c] : 0.f;
     }
 
-    // one token ahead, in two buffers used in turn: the tile sums, p_{t-1}
+    // PF - 1 tokens ahead, in a ring of PF buffers: the tile sums, p_{t-1}
     // and the token's alpha, k, omega, r
     struct UncIn {
         float q[CPL], k[CPL], ks[CPL], a[CPL], pp[CPL];
@@ -627,7 +652,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
         }
         u.r = rr[tok];
     };
-    const auto step = [&](int t, const UncIn& u, UncIn& nxt) {
+    const auto step = [&](int t, const UncIn& u, UncIn& ahead) {
         const size_t tok = tokidx(t);
         float al[CPL], kk[CPL], pp[CPL], gq[CPL], gk[CPL], gks[CPL], ga[CPL], wc[CPL];
 #pragma unroll
@@ -636,7 +661,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
             gq[c] = u.q[c]; gk[c] = u.k[c]; gks[c] = u.ks[c]; ga[c] = u.a[c];
         }
         const float rt = to_f32(u.r);
-        load(nxt, max(t - 1, 0));
+        load(ahead, max(t - (PF - 1), 0));
 #pragma unroll
         for (int c = 0; c < CPL; ++c) A.dq[tok * DK + lane + 64 * c] = gq[c];
                 if (!ISO) {
@@ -719,11 +744,17 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
                     db = dbh * a2;
                 }
     };
-    UncIn ua, ub;
-    if (T > 0) load(ua, T - 1);
-    for (int t = T - 1; t >= 0; t -= 2) {
-        step(t, ua, ub);
-        if (t - 1 >= 0) step(t - 1, ub, ua);
+    UncIn u0, u1, u2, u3;
+    if (T > 0) {
+        load(u0, T - 1);
+        load(u1, max(T - 2, 0));
+        load(u2, max(T - 3, 0));
+    }
+    for (int t = T - 1; t >= 0; t -= PF) {
+        step(t, u0, u3);
+        if (t - 1 >= 0) step(t - 1, u1, u0);
+        if (t - 2 >= 0) step(t - 2, u2, u1);
+        if (t - 3 >= 0) step(t - 3, u3, u2);
     }
 
 
