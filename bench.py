@@ -304,7 +304,8 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic and backward lines")
+                    help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic, long-context "
+                         "and backward lines")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the workload of the rocprofv3 counter runs and exit")
@@ -361,6 +362,14 @@ def main():
         extra["isochannel"] = {"workload": wc.name, "tokens_per_s": wc.B * wc.T / (mc / 1e3), "ms_per_step": mc,
                                "hbm_frac": forward_bytes(wc) / (lc / 1e3) / 1e9 / HBM_PEAK_GBS}
         del tc
+        wlc = wl.WORKLOADS["diag_bf16_b1_t65536_h16_d128"]
+        tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)
+        mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "auto")
+        extra["long_context"] = {"workload": wlc.name, "tokens_per_s": wlc.B * wlc.T / (mlc / 1e3),
+                                 "ms_per_step": mlc,
+                                 "hbm_frac": forward_bytes(wlc) / (llc / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                 "workgroups": wlc.B * wlc.H * (wlc.dv // 64)}
+        del tlc
         extra["backward"] = bench_backward(kdn, w, dev, 3)
     cpu = None
     if not args.no_cpu_baseline:
