@@ -14,7 +14,8 @@ standard deviation s):
   isotropic with per-channel decay: per channel);
 * omega = softplus(N(omega_loc, 1)) per channel (both isotropic forms: per
   head-token);
-* r = 0.01 + softplus(N(0, 1)) per head-token (the pages' r_min = 0.01);
+* r = 0.01 + softplus(N(0, 1)) per head-token (the pages' r_min = 0.01; the
+  grouped variant: per head-token and group of value columns);
 * c0 = 1.0 per head, or U(0.5, 2) per head;
 * decode state: S0 ~ N(0, 0.1), p0 ~ U(0.1, 1) (isotropic: one p0 per head);
 * packed variable-length batches: sequence lengths ~ U{lo, hi} (integers,
@@ -50,6 +51,7 @@ class Workload:
     alpha_loc: float = 2.0
     omega_loc: float = -4.0
     decode_steps: int = 0  # > 0: a decode workload with B sequences and T = 1 per step
+    rgroups: int = 1       # "grouped" variant: observation noise r per group of d_v / rgroups value columns
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -70,6 +72,10 @@ WORKLOADS = {
     "isoch_bf16_b8_t4096_h16_d128": Workload(
         "isoch_bf16_b8_t4096_h16_d128", "isochannel", "bf16", 8, 4096, 16, 128, 128, 128.0,
         "uniform", 1006),
+    # grouped observation noise: one r per group of 64 value columns (2 groups)
+    "grouped_bf16_b8_t4096_h16_d128": Workload(
+        "grouped_bf16_b8_t4096_h16_d128", "grouped", "bf16", 8, 4096, 16, 128, 128, 128.0,
+        "uniform", 1007, rgroups=2),
     "decode_diag_bf16_n256_h16_d128_s1024": Workload(
         "decode_diag_bf16_n256_h16_d128_s1024", "diagonal", "bf16", 256, 1, 16, 128, 128, 128.0,
         "one", 1004, decode_steps=1024),
@@ -110,15 +116,16 @@ def _normal(rng, shape, loc=0.0, scale=1.0):
 
 def _draw_tokens(rng, w: Workload, lead: tuple) -> dict:
     """Draw q, k, v, alpha, omega, r with leading shape ``lead`` (e.g. (B,T,H))."""
-    alpha_shape = lead + (w.dk,) if w.variant in ("diagonal", "isochannel") else lead
-    omega_shape = lead + (w.dk,) if w.variant == "diagonal" else lead
+    alpha_shape = lead + (w.dk,) if w.variant in ("diagonal", "isochannel", "grouped") else lead
+    omega_shape = lead + (w.dk,) if w.variant in ("diagonal", "grouped") else lead
+    r_shape = lead + (w.rgroups,) if w.variant == "grouped" else lead
     out = {
         "q": _l2norm(_normal(rng, lead + (w.dk,))),
         "k": _l2norm(_normal(rng, lead + (w.dk,))),
         "v": _normal(rng, lead + (w.dv,)),
         "alpha": _sigmoid(_normal(rng, alpha_shape, w.alpha_loc, 0.5)),
         "omega": _softplus(_normal(rng, omega_shape, w.omega_loc, 1.0)),
-        "r": (np.float32(0.01) + _softplus(_normal(rng, lead))).astype(np.float32),
+        "r": (np.float32(0.01) + _softplus(_normal(rng, r_shape))).astype(np.float32),
     }
     if w.dtype == "bf16":
         out = {key: round_bf16(val) for key, val in out.items()}
@@ -171,7 +178,7 @@ def decode_state(w: Workload) -> dict:
     (isotropic: [N,H]) float32, N = w.B."""
     rng = np.random.default_rng([w.seed, 0xD0])
     S0 = _normal(rng, (w.B, w.H, w.dk, w.dv), 0.0, 0.1)
-    pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)  # isotropic forms: a scalar
+    pshape = {"diagonal": (w.B, w.H, w.dk), "grouped": (w.B, w.H, w.rgroups, w.dk)}.get(w.variant, (w.B, w.H))
     p0 = rng.uniform(0.1, 1.0, size=pshape).astype(np.float32)
     return {"S0": S0, "p0": p0}
 
@@ -195,6 +202,6 @@ def backward_cotangents(w: Workload, with_state: bool = True) -> dict:
     out = {"dO": dO, "dS_T": None, "dp_T": None}
     if with_state:
         out["dS_T"] = _normal(rng, (w.B, w.H, w.dk, w.dv), 0.0, 0.1)
-        pshape = (w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H)
+        pshape = {"diagonal": (w.B, w.H, w.dk), "grouped": (w.B, w.H, w.rgroups, w.dk)}.get(w.variant, (w.B, w.H))
         out["dp_T"] = _normal(rng, pshape, 0.0, 0.1)
     return out

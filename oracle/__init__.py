@@ -13,6 +13,8 @@ it.
   variant).
 * ``forward_varlen`` runs packed variable-length batches through the same
   recurrence, one sequence at a time.
+* ``forward_grouped`` is the diagonal recurrence with block-diagonal
+  observation noise over groups of value columns (one per group).
 * ``backward`` is the reverse-mode adjoint of the same recurrence (the
   gradients a training step needs), pinned by central finite differences of
   the forward.
@@ -136,7 +138,8 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
     forward_diag / forward_iso.  The recurrence is per sequence; packing only
     decides which rows belong to which sequence.
     Returns o [total,H,dv], S [N,H,dk,dv], p [N,H,dk] (isotropic [N,H])."""
-    fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc}[variant]
+    fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc,
+          "grouped": forward_grouped}[variant]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     if cu.ndim != 1 or len(cu) < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != len(q):
         raise ValueError("cu_seqlens must rise from 0 to the number of token rows")
@@ -145,7 +148,8 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
     dv = np.shape(v)[-1]
     o = np.zeros((total, H, dv))
     S = np.zeros((N, H, dk, dv))
-    p = np.zeros((N, H, dk) if variant == "diagonal" else (N, H))  # isotropic forms: one scalar per head
+    pshape = {"diagonal": (N, H, dk), "grouped": (N, H, np.shape(r)[-1], dk)}.get(variant, (N, H))
+    p = np.zeros(pshape)  # isotropic forms: one scalar per head
     for n in range(N):
         a, b = int(cu[n]), int(cu[n + 1])
         out = fn(*(np.asarray(x)[None, a:b] for x in (q, k, v, alpha, omega, r)), c0, mu,
@@ -153,6 +157,36 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, mu, cu_seqlens, variant="diagon
         o[a:b] = out["o"][0]
         S[n] = out["S"][0]
         p[n] = out["p"][0]
+    return {"o": o, "S": S, "p": p}
+
+
+def forward_grouped(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None):
+    """Diagonal KDN with grouped observation noise ("Memory by Design:
+    Probabilistic Sequence Layers", section on per-column and grouped
+    observation noise): the noise covariance is block diagonal over G groups
+    of d_v / G value columns, diag[r_1 I, ..., r_G I], so each group keeps its
+    own key-space uncertainty and gain.  The groups share q, k, alpha, omega
+    and are otherwise independent, so each is the diagonal recurrence
+    (forward_diag) on its value columns with its own r and p.
+    Shapes as forward_diag except r [B,T,H,G], p0 / returned p [B,H,G,dk]."""
+    r = np.asarray(r)
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    G = r.shape[-1]
+    if dv % G:
+        raise ValueError("d_v must be a multiple of the number of groups")
+    gw = dv // G
+    o = np.zeros((B, T, H, dv))
+    S = np.zeros((B, H, dk, dv))
+    p = np.zeros((B, H, G, dk))
+    for g in range(G):
+        cols = slice(g * gw, (g + 1) * gw)
+        out = forward_diag(q, k, np.asarray(v)[..., cols], alpha, omega, r[..., g], c0, mu,
+                           None if S0 is None else np.asarray(S0)[..., cols],
+                           None if p0 is None else np.asarray(p0)[:, :, g])
+        o[..., cols] = out["o"]
+        S[..., cols] = out["S"]
+        p[:, :, g] = out["p"]
     return {"o": o, "S": S, "p": p}
 
 

@@ -522,3 +522,43 @@ def test_bf16_rounding_matches_torch():
     ours = wl.round_bf16(x)
     theirs = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(ours, theirs)
+
+
+# --------------------------------------------------------------------------
+# Grouped observation noise (Bayesian Layer page, per-column and grouped
+# observation noise: R = diag[r_1 I, ..., r_G I] over groups of value columns)
+# --------------------------------------------------------------------------
+
+def test_grouped_noise_axis_aligned_keys_match_one_dense_filter_per_group():
+    # each column group is an exact Kalman filter with its own covariance and
+    # gain (one-hot keys, mu = 1, diagonal P0: the posteriors stay diagonal)
+    T, dk, dv, G = 50, 4, 6, 3
+    w = wl.Workload("g", "grouped", "f32", 1, T, 1, dk, dv, 1.0, "uniform", 21, rgroups=G)
+    x = wl.forward_inputs(w)
+    rng = np.random.default_rng(4)
+    idx = rng.integers(0, dk, size=T)
+    x["k"][0, :, 0, :] = np.eye(dk, dtype=np.float32)[idx] * rng.choice([-1, 1], size=(T, 1))
+    ref = oracle.forward_grouped(**{n: x[n] for n in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=1.0)
+    A = [np.diag(x["alpha"][0, t, 0].astype(np.float64)) for t in range(T)]
+    Q = [np.diag(x["omega"][0, t, 0].astype(np.float64)) for t in range(T)]
+    gw = dv // G
+    for g in range(G):
+        cols = slice(g * gw, (g + 1) * gw)
+        out = dense.dense_filter(x["k"][0, :, 0], x["v"][0, :, 0, cols], A, Q, x["r"][0, :, 0, g].astype(np.float64),
+                                 float(x["c0"][0]) * np.eye(dk), queries=x["q"][0, :, 0])
+        np.testing.assert_allclose(ref["S"][0, 0][:, cols], out["M"][-1], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ref["p"][0, 0, g], np.diag(out["P"][-1]), rtol=1e-12)
+        np.testing.assert_allclose(ref["o"][0, :, 0, cols], np.array(out["y"]), rtol=1e-12, atol=1e-13)
+
+
+def test_grouped_noise_with_equal_groups_is_the_diagonal_form():
+    w = wl.Workload("g", "grouped", "f32", 2, 40, 3, 8, 6, 8.0, "uniform", 22, rgroups=2)
+    x = wl.forward_inputs(w)
+    x["r"][..., 1] = x["r"][..., 0]
+    names = ("q", "k", "v", "alpha", "omega")
+    g = oracle.forward_grouped(**{n: x[n] for n in names}, r=x["r"], c0=x["c0"], mu=w.mu)
+    d = oracle.forward_diag(**{n: x[n] for n in names}, r=x["r"][..., 0], c0=x["c0"], mu=w.mu)
+    np.testing.assert_array_equal(g["o"], d["o"])
+    np.testing.assert_array_equal(g["S"], d["S"])
+    np.testing.assert_array_equal(g["p"][:, :, 0], d["p"])
+    np.testing.assert_array_equal(g["p"][:, :, 1], d["p"])
