@@ -28,8 +28,16 @@
  *   omega_t and r_t are scalars per head-token; the uncertainty scalar is
  *   predicted with the trace projection a_t = (1/d_k) sum_i alpha_t,i^2:
  *     b_hat = a_t b + omega_t / d_k;  kappa, b as in the isotropic variant.
- *   Shapes: alpha [.., dk], omega [..] (no dk), p [B,H].  Only the
- *   recurrent algorithm runs it (KDN_ALGO_AUTO picks it).
+ *   Shapes: alpha [.., dk], omega [..] (no dk), p [B,H].
+ *
+ *   Diagonal variant with grouped observation noise (KDN_DIAGONAL_GROUPED;
+ *   "Memory by Design: Probabilistic Sequence Layers", per-column and grouped
+ *   observation noise): the noise covariance is block diagonal over groups of
+ *   64 value columns, diag[r_1 I, ..., r_G I] with G = d_v / 64, so each
+ *   group keeps its own uncertainty p_g and gain; the groups share q, k,
+ *   alpha, omega, and each is the diagonal recurrence above on its columns
+ *   with r_t,g.  Shapes: r [.., G], p0 / p_T / the decode p [B,H,G,dk].
+ *   kdn_backward does not cover it (KDN_ERR_UNSUPPORTED).
  *
  * Initial state: S_0 = S0 (or zero when S0 is NULL); p_0 = p0 (or c0[h] on
  * every channel when p0 is NULL).  No 1/sqrt(d_k) scaling is applied to q.
@@ -65,7 +73,7 @@
 extern "C" {
 #endif
 
-enum kdn_variant { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1, KDN_ISOTROPIC_CHANNEL = 2 };
+enum kdn_variant { KDN_DIAGONAL = 0, KDN_ISOTROPIC = 1, KDN_ISOTROPIC_CHANNEL = 2, KDN_DIAGONAL_GROUPED = 3 };
 enum kdn_dtype { KDN_F32 = 0, KDN_BF16 = 1 };
 enum kdn_status {
     KDN_OK = 0,

@@ -21,14 +21,31 @@ KDN_F32, KDN_BF16 = 0, 1
  KDN_ERR_WORKSPACE) = range(8)
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 KDN_ISOTROPIC_CHANNEL = 2
-VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC, "isochannel": KDN_ISOTROPIC_CHANNEL}
+KDN_DIAGONAL_GROUPED = 3
+VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC, "isochannel": KDN_ISOTROPIC_CHANNEL,
+            "grouped": KDN_DIAGONAL_GROUPED}
+GROUP_COLS = 64  # value columns per observation-noise group of the grouped variant
 
 
 def _gate_shapes(var, lead, dk):
     """(alpha shape, omega shape) of a variant for token dims ``lead``."""
     alpha = lead + (dk,) if var != KDN_ISOTROPIC else lead
-    omega = lead + (dk,) if var == KDN_DIAGONAL else lead
+    omega = lead + (dk,) if var in (KDN_DIAGONAL, KDN_DIAGONAL_GROUPED) else lead
     return alpha, omega
+
+
+def _r_shape(var, lead, dv):
+    """Shape of r: one entry per head-token, or per group of value columns."""
+    return lead + (dv // GROUP_COLS,) if var == KDN_DIAGONAL_GROUPED else lead
+
+
+def _p_shape(var, lead, dk, dv):
+    """Shape of the uncertainty state for state dims ``lead`` (e.g. (B, H))."""
+    if var == KDN_DIAGONAL:
+        return lead + (dk,)
+    if var == KDN_DIAGONAL_GROUPED:
+        return lead + (dv // GROUP_COLS, dk)
+    return lead
 
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_step", "kdn_validate_forward",
@@ -139,9 +156,9 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
     dev = q.device
     dt = q.dtype
     ashape, wshape = _gate_shapes(var, (B, T, H), dk)
-    pshape = (B, H, dk) if var == KDN_DIAGONAL else (B, H)
+    pshape = _p_shape(var, (B, H), dk, dv)
     for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (B, T, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, _r_shape(var, (B, T, H), dv))):
         _need(t, name, shp, dt, dev)
     if c0 is not None:
         _need(c0, "c0", (H,), torch.float32, dev)
@@ -197,9 +214,9 @@ def forward_varlen(q, k, v, alpha, omega, r, c0, cu_seqlens, mu, variant="diagon
     N = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     ashape, wshape = _gate_shapes(var, (total, H), dk)
-    pshape = (N, H, dk) if var == KDN_DIAGONAL else (N, H)
+    pshape = _p_shape(var, (N, H), dk, dv)
     for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
-                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (total, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, _r_shape(var, (total, H), dv))):
         _need(t, name, shp, dt, dev)
     if order is not None:
         _need(order, "order", (N,), torch.int32, dev)
@@ -237,10 +254,10 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
     dev, dt = q.device, q.dtype
     ashape, wshape = _gate_shapes(var, (N, H), dk)
     for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
-                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (N, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, _r_shape(var, (N, H), dv))):
         _need(t, name, shp, dt, dev)
     _need(S, "S", (N, H, dk, dv), torch.float32, dev)
-    _need(p, "p", (N, H, dk) if var == KDN_DIAGONAL else (N, H), torch.float32, dev)
+    _need(p, "p", _p_shape(var, (N, H), dk, dv), torch.float32, dev)
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
@@ -271,6 +288,8 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
+    if var == KDN_DIAGONAL_GROUPED:
+        raise KDNError(KDN_ERR_UNSUPPORTED, "kdn_backward", "grouped observation noise is not covered")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype

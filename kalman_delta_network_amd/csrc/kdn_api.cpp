@@ -54,8 +54,16 @@ bool overlap(Span a, Span b) {
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from overflow
 
+// both isotropic forms carry one uncertainty scalar per head
+bool is_iso(int variant) { return variant == KDN_ISOTROPIC || variant == KDN_ISOTROPIC_CHANNEL; }
+
+// entries of r per head-token (and of p per head and channel): one per group
+// of 64 value columns for grouped observation noise, else one
+size_t noise_groups(int variant, int dv) { return variant == KDN_DIAGONAL_GROUPED ? size_t(dv / 64) : 1; }
+
 int validate_common(int variant, int dtype, float mu, int dk, int dv) {
-    if (variant != KDN_DIAGONAL && variant != KDN_ISOTROPIC && variant != KDN_ISOTROPIC_CHANNEL)
+    if (variant != KDN_DIAGONAL && variant != KDN_ISOTROPIC && variant != KDN_ISOTROPIC_CHANNEL &&
+        variant != KDN_DIAGONAL_GROUPED)
         return fail(KDN_ERR_UNSUPPORTED, "unknown variant %d", variant);
     if (dtype != KDN_F32 && dtype != KDN_BF16) return fail(KDN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     if (!std::isfinite(mu) || mu < 0.f) return fail(KDN_ERR_VALUE, "mu must be finite and >= 0 (got %g)", double(mu));
@@ -78,7 +86,8 @@ int validate_forward_core(const void* q, const void* k, const void* v, const voi
     if (algo != KDN_ALGO_AUTO && algo != KDN_ALGO_RECURRENT && algo != KDN_ALGO_CHUNKED)
         return fail(KDN_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
     if (units == 0) return ok();  // nothing to read or write
-    const bool iso = variant != KDN_DIAGONAL;              // one uncertainty scalar per head
+    const bool iso = is_iso(variant);                      // one uncertainty scalar per head
+    const size_t ng = noise_groups(variant, dv);           // r and p entries per head-token / head
     const bool chan = variant != KDN_ISOTROPIC;            // one decay per key channel
     if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r || !o))
         return fail(KDN_ERR_NULL, "q, k, v, alpha, omega, r and o must be non-NULL");
@@ -88,9 +97,9 @@ int validate_forward_core(const void* q, const void* k, const void* v, const voi
     const size_t es = dtype == KDN_BF16 ? 2 : 4;
     const size_t nk = size_t(toks) * dk, nv = size_t(toks) * dv;
     const size_t na = chan ? nk : size_t(toks), nw = iso ? size_t(toks) : nk;
-    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * dk;
+    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * ng * dk;
     const Span in[] = {span(q, nk, es),        span(k, nk, es),     span(v, nv, es),
-                       span(alpha, na, es),    span(omega, nw, es), span(r, size_t(toks), es),
+                       span(alpha, na, es),    span(omega, nw, es), span(r, size_t(toks) * ng, es),
                        span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4),
                        span(cu, size_t(ncu), 4),   span(ord, size_t(ncu > 0 ? ncu - 1 : 0), 4)};
     const Span so = span(o, nv, es), sS = span(S_T, ns, 4), sp = span(p_T, np, 4);
@@ -146,14 +155,15 @@ int validate_step(const void* q, const void* k, const void* v, const void* alpha
     if (units == 0) return ok();
     if (!q || !k || !v || !alpha || !omega || !r || !o || !S || !p)
         return fail(KDN_ERR_NULL, "every pointer of kdn_step must be non-NULL");
-    const bool iso = variant != KDN_DIAGONAL, chan = variant != KDN_ISOTROPIC;
+    const bool iso = is_iso(variant), chan = variant != KDN_ISOTROPIC;
+    const size_t ng = noise_groups(variant, dv);
     const size_t es = dtype == KDN_BF16 ? 2 : 4;
     const size_t nk = size_t(units) * dk, nv = size_t(units) * dv;
     const size_t na = chan ? nk : size_t(units), nw = iso ? size_t(units) : nk;
     const Span in[] = {span(q, nk, es), span(k, nk, es), span(v, nv, es),
-                       span(alpha, na, es), span(omega, nw, es), span(r, size_t(units), es)};
+                       span(alpha, na, es), span(omega, nw, es), span(r, size_t(units) * ng, es)};
     const Span so = span(o, nv, es), sS = span(S, size_t(units) * dk * dv, 4),
-               sp = span(p, iso ? size_t(units) : nk, 4);
+               sp = span(p, iso ? size_t(units) : nk * ng, 4);
     for (const Span& x : in)
         if (overlap(so, x) || overlap(sS, x) || overlap(sp, x))
             return fail(KDN_ERR_ALIAS, "the state or o overlaps a token input");
@@ -176,7 +186,9 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     if (units > INT32_MAX || toks > kMaxElems / 128)
         return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
     if (units == 0) return ok();
-    const bool iso = variant != KDN_DIAGONAL, chan = variant != KDN_ISOTROPIC;
+    if (variant == KDN_DIAGONAL_GROUPED)
+        return fail(KDN_ERR_UNSUPPORTED, "the backward pass does not cover grouped observation noise");
+    const bool iso = is_iso(variant), chan = variant != KDN_ISOTROPIC;
     if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r))
         return fail(KDN_ERR_NULL, "q, k, v, alpha, omega and r must be non-NULL");
     if (toks > 0 && (!dq || !dk_out || !dv_out || !dalpha || !domega || !dr))

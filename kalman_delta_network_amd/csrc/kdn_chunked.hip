@@ -310,11 +310,16 @@ __device__ __forceinline__ void chain_r_store(Smem<DK>& sm, int c, uint32_t rbit
     if (lane < L) sm.rr[c % 3][lane] = rt;
 }
 
-// r_t of chunk c for lane t (lanes >= L repeat the chunk's last token)
-__device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h, int c, int nchunks) {
+// r_t of chunk c for lane t (lanes >= L repeat the chunk's last token).
+// GR: grouped observation noise, r [.., ntile] with one entry per group of
+// DVT value columns; this workgroup's columns are group `tile`
+template <bool GR>
+__device__ __forceinline__ uint32_t chain_r_load(const Args& a, size_t b, int h, int c, int nchunks, int tile,
+                                                 int ntile) {
     c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
-    return a.r[tokidx(a, b, h, min(c * L + min(lane, L - 1), a.T - 1))];
+    const size_t tok = tokidx(a, b, h, min(c * L + min(lane, L - 1), a.T - 1));
+    return a.r[GR ? tok * size_t(ntile) + size_t(tile) : tok];
 }
 
 // bf16 -> fp32 by loading the 16 bits into the upper half of a register whose
@@ -1017,10 +1022,14 @@ __device__ __forceinline__ int state_index(int w) { return ROLE_LAYOUT == 0 ? w 
 __device__ __forceinline__ int form_index(int w) {
     return ROLE_LAYOUT == 0 ? (w < 4 ? w - 2 : w - 4) : ROLE_LAYOUT == 1 ? w - 2 : (w >= 4 ? w - 4 : w);
 }
-// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
-template <int DK, int VAR>
+// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay.
+// GR (diagonal only): grouped observation noise, one r and one uncertainty
+// state p per group of DVT value columns, i.e. per column tile; the tiles of
+// a head are then independent diagonal recurrences sharing q, k, alpha, omega.
+template <int DK, int VAR, bool GR = false>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
+    static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
     __shared__ Smem<DK> sm;
     const int ntile = a.DV / DVT;
     const int bid = blockIdx.x;
@@ -1065,10 +1074,10 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const size_t x = sb + size_t(e / DVT) * a.DV + tile * DVT + e % DVT;
             a.S_T[x] = a.S0 ? a.S0[x] : 0.f;
         }
-        if (tile == 0) {
+        if (GR || tile == 0) {
             const int np = ISO ? 1 : DK;
-            for (int i = threadIdx.x; i < np; i += NTHREADS)
-                a.p_T[size_t(unit) * np + i] = a.p0 ? a.p0[size_t(unit) * np + i] : a.c0[h];
+            const size_t pb = GR ? (size_t(unit) * ntile + tile) * np : size_t(unit) * np;
+            for (int i = threadIdx.x; i < np; i += NTHREADS) a.p_T[pb + i] = a.p0 ? a.p0[pb + i] : a.c0[h];
         }
         return;
     }
@@ -1083,7 +1092,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         chain_diag_issue<DK, 0, 4>(sm, a, b, h, 0, nchunks, fwave);
         chain_diag_issue<DK, 1, 4>(sm, a, b, h, 0, nchunks, fwave);
         chain_diag_issue<DK, 0, 4>(sm, a, b, h, 1, nchunks, fwave);
-        if (fwave == 3) r0 = chain_r_load(a, b, h, 0, nchunks);
+        if (fwave == 3) r0 = chain_r_load<GR>(a, b, h, 0, nchunks, tile, ntile);
     }
     // rows 0..15 of tril(Qt Kh^T) never touch tokens 16..31, and the block
     // (0,1) of each diagonal-block inverse is zero: write both once
@@ -1103,7 +1112,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const bool active = wave < DK / 64;
             const int i = wave * 64 + lane;
             float p = 0.f;
-            if (active) p = a.p0 ? a.p0[size_t(unit) * DK + i] : a.c0[h];
+            const size_t pidx = (GR ? size_t(unit) * ntile + tile : size_t(unit)) * DK + i;
+            if (active) p = a.p0 ? a.p0[pidx] : a.c0[h];
             settle(p);  // p is ready before the pipelined loop
             // chunk c's tiles are in LDS buffer c & 1 (chunk c + 1's are
             // fetched meanwhile by the formation waves); the loop runs two
@@ -1130,7 +1140,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 step(IntC<0>{}, c);
                 step(IntC<1>{}, c + 1);
             }
-            if (active && tile == 0) a.p_T[size_t(unit) * DK + i] = p;
+            if (active && (GR || tile == 0)) a.p_T[pidx] = p;
         } else if (wave == 1) {
             // the per-channel decays (isotropic variant with per-channel
             // decay; otherwise this wave only keeps the barrier count)
@@ -1253,7 +1263,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 uint32_t rnext = 0;
                 if (VAR == 0) {
                     chain_diag_issue<DK, 1, 4>(sm, a, b, h, c + 2, nchunks, f);  // rows 16..31
-                    if (f == 3) rnext = chain_r_load(a, b, h, c + 2, nchunks);
+                    if (f == 3) rnext = chain_r_load<GR>(a, b, h, c + 2, nchunks, tile, ntile);
                 }
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
                 if (c >= 0 && c < nchunks) {
@@ -1283,7 +1293,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     }
 }
 
-template <int DK, int VAR>
+template <int DK, int VAR, bool GR = false>
 hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0) return hipSuccess;
@@ -1311,7 +1321,7 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR, GR>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1330,10 +1340,13 @@ bool chunked_supports(const FwdArgs& a) {
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
+    // variant 3: diagonal with grouped observation noise (one group per tile)
     if (a.dk == 128) {
+        if (a.variant == 3) return launch_t<128, 0, true>(a, stream);
         if (a.variant == 2) return launch_t<128, 2>(a, stream);
         return a.variant == 1 ? launch_t<128, 1>(a, stream) : launch_t<128, 0>(a, stream);
     }
+    if (a.variant == 3) return launch_t<64, 0, true>(a, stream);
     if (a.variant == 2) return launch_t<64, 2>(a, stream);
     return a.variant == 1 ? launch_t<64, 1>(a, stream) : launch_t<64, 0>(a, stream);
 }

@@ -68,8 +68,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay
-template <int DK, int DV, int VAR, typename Tin>
+// VAR: 0 diagonal, 1 isotropic, 2 isotropic with per-channel decay.
+// GR (diagonal only): grouped observation noise, one r and one uncertainty
+// state p per group of 64 value columns (waves 2g, 2g + 1 form group g)
+template <int DK, int DV, int VAR, typename Tin, bool GR = false>
 __global__ void __launch_bounds__(DV * 2)
 kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const Tin* __restrict__ v, const Tin* __restrict__ alpha,
@@ -83,6 +85,8 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     constexpr int CPL = DK / 64;  // channels per lane
     constexpr int RPT = DK / 8;   // memory rows per thread
     static_assert(DK % 64 == 0 && DV % 32 == 0, "unsupported tile");
+    static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
+    constexpr int NG = GR ? DV / 64 : 1;  // uncertainty groups
 
     __shared__ float4 chan[NW][DK];
 
@@ -97,6 +101,7 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     const int cq = lane & 7;
     const int rg = lane >> 3;
     const int col = wave * 32 + cq * 4;
+    const int grp = GR ? wave / 2 : 0;  // uncertainty group of this wave's columns
     // this unit's sequence: len tokens from token-grid row tok0 on (packed
     // sequences: bounds from the offsets, clamped into the grid of T rows)
     size_t tok0 = b * size_t(T);
@@ -126,14 +131,14 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         pb = p0 ? p0[unit] : c0[h];
     } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) p[c] = p0 ? p0[size_t(unit) * DK + lane + 64 * c] : c0[h];
+        for (int c = 0; c < CPL; ++c) p[c] = p0 ? p0[(size_t(unit) * NG + grp) * DK + lane + 64 * c] : c0[h];
     }
     __syncthreads();  // all initial reads happen before any in-place write
 
     const float inv_dk = 1.0f / float(DK);
     for (int t = 0; t < len; ++t) {
         const size_t tok = (tok0 + size_t(t)) * size_t(H) + size_t(h);
-        const float rt = to_f32(r[tok]);
+        const float rt = to_f32(r[GR ? tok * NG + grp : tok]);
         float kk[CPL], qq[CPL], aa[CPL], kap[CPL];
         float mq;  // kappa^T q
 #pragma unroll
@@ -230,21 +235,21 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         *reinterpret_cast<float4*>(S_T + sbase + size_t(i) * DV + col) =
             make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
     }
-    if (wave == 0) {
+    if (wave == (GR ? 2 * grp : 0)) {  // the first wave of each group
         if (ISO) {
             if (lane == 0) p_T[unit] = pb;
         } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) p_T[size_t(unit) * DK + lane + 64 * c] = p[c];
+            for (int c = 0; c < CPL; ++c) p_T[(size_t(unit) * NG + grp) * DK + lane + 64 * c] = p[c];
         }
     }
 }
 
-template <int DK, int DV, int VAR, typename Tin>
+template <int DK, int DV, int VAR, typename Tin, bool GR = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const long units = long(a.B) * a.H;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((kdn_recurrent_kernel<DK, DV, VAR, Tin>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((kdn_recurrent_kernel<DK, DV, VAR, Tin, GR>), dim3(unsigned(units)),
                        dim3(DV * 2), 0, stream, static_cast<const Tin*>(a.q),
                        static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                        static_cast<const Tin*>(a.alpha), static_cast<const Tin*>(a.omega),
@@ -253,13 +258,14 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DK, int DV, int VAR>
+template <int DK, int DV, int VAR, bool GR = false>
 hipError_t launch_dtype(const FwdArgs& a, hipStream_t s) {
-    return a.dtype == 1 ? launch_t<DK, DV, VAR, bf16_t>(a, s) : launch_t<DK, DV, VAR, float>(a, s);
+    return a.dtype == 1 ? launch_t<DK, DV, VAR, bf16_t, GR>(a, s) : launch_t<DK, DV, VAR, float, GR>(a, s);
 }
 
 template <int DK, int DV>
 hipError_t launch_variant(const FwdArgs& a, hipStream_t s) {
+    if (a.variant == 3) return launch_dtype<DK, DV, 0, true>(a, s);  // grouped observation noise
     if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
     return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
 }

@@ -70,7 +70,7 @@ def call_validate(lib, a):
 
 def test_validate_forward_accepts_good_arguments(lib):
     f = Fake()
-    for variant in (0, 1, 2):
+    for variant in (0, 1, 2, 3):
         for dtype in (0, 1):
             for dk in (64, 128):
                 for dv in (64, 128):
@@ -92,7 +92,7 @@ def test_validate_forward_accepts_good_arguments(lib):
     (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dv=32), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dk=-64), kdn.KDN_ERR_SHAPE),
-    (dict(variant=3), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(variant=4), kdn.KDN_ERR_UNSUPPORTED),
     (dict(dtype=7), kdn.KDN_ERR_UNSUPPORTED),
     (dict(algo=9), kdn.KDN_ERR_UNSUPPORTED),
     (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
@@ -351,3 +351,15 @@ def test_backward_launch_error_path_without_gpu(lib, monkeypatch):
     assert lib.kdn_backward(*_bwd_list(a), None) == kdn.KDN_ERR_HIP
     assert b"KDN_FAULT" in lib.kdn_last_error()
     assert lib.kdn_backward(*_bwd_list(dict(a, mu=float("nan"))), None) == kdn.KDN_ERR_VALUE
+
+
+def test_grouped_noise_is_a_forward_variant_without_backward(lib):
+    f = Fake()
+    assert call_validate(lib, fwd_args(f, variant=3, dv=128)) == 0
+    assert call_validate(lib, fwd_args(f, variant=4)) == kdn.KDN_ERR_UNSUPPORTED
+    assert call_validate_bwd(lib, bwd_args(f, lib, variant=3)) == kdn.KDN_ERR_UNSUPPORTED
+    # r and p hold one entry per group of 64 value columns: an output placed
+    # right after a single-group r overlaps the second group's entries
+    a = fwd_args(f, variant=3, dk=64, dv=128, B=1, T=8, H=1)
+    r_end = ctypes.c_void_p(a["r"].value + 8 * 2)  # bf16, 8 tokens x 1 group
+    assert call_validate(lib, dict(a, o=r_end)) == kdn.KDN_ERR_ALIAS
