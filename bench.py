@@ -32,8 +32,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def _gate_elems(w) -> int:
-    """alpha plus omega elements per token-head."""
-    return {"diagonal": 2 * w.dk, "isotropic": 2, "isochannel": w.dk + 1}[w.variant]
+    """alpha plus omega elements per token-head, and the r entries beyond one."""
+    return {"diagonal": 2 * w.dk, "isotropic": 2, "isochannel": w.dk + 1,
+            "grouped": 2 * w.dk + w.rgroups - 1}[w.variant]
+
+
+def _pdim(w) -> int:
+    """Entries of the uncertainty state per (batch, head)."""
+    return {"diagonal": w.dk, "grouped": w.rgroups * w.dk}.get(w.variant, 1)
 
 
 def forward_bytes(w) -> int:
@@ -42,7 +48,7 @@ def forward_bytes(w) -> int:
     es = 2 if w.dtype == "bf16" else 4
     toks = w.B * w.T * w.H
     per_tok = es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv
-    pdim = w.dk if w.variant == "diagonal" else 1
+    pdim = _pdim(w)
     return toks * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4
 
 
@@ -51,7 +57,7 @@ def varlen_bytes(w, total: int) -> int:
     `total` tokens in all: as forward_bytes, plus the N+1 offsets."""
     es = 2 if w.dtype == "bf16" else 4
     per_tok = es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv
-    pdim = w.dk if w.variant == "diagonal" else 1
+    pdim = _pdim(w)
     return total * w.H * per_tok + w.B * w.H * (w.dk * w.dv + pdim) * 4 + w.H * 4 + (w.B + 1) * 4
 
 
@@ -60,7 +66,7 @@ def step_bytes(w) -> int:
     one token of inputs read, o written."""
     es = 2 if w.dtype == "bf16" else 4
     units = w.B * w.H
-    pdim = w.dk if w.variant == "diagonal" else 1
+    pdim = _pdim(w)
     return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv)
 
 
@@ -72,7 +78,7 @@ def backward_bytes(w) -> int:
     es = 2 if w.dtype == "bf16" else 4
     toks = w.B * w.T * w.H
     n_in = 2 * w.dk + w.dv + _gate_elems(w) + 1
-    pdim = w.dk if w.variant == "diagonal" else 1
+    pdim = _pdim(w)
     return toks * (es * (n_in + w.dv) + 4 * n_in) + w.B * w.H * (w.dk * w.dv + pdim) * 4 + 2 * w.H * 4
 
 
@@ -117,7 +123,7 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     import torch
     out = (torch.empty((w.B, w.T, w.H, w.dv), dtype=t["q"].dtype, device=t["q"].device),
            torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=t["q"].device),
-           torch.empty((w.B, w.H, w.dk) if w.variant == "diagonal" else (w.B, w.H),
+           torch.empty({"diagonal": (w.B, w.H, w.dk), "grouped": (w.B, w.H, w.rgroups, w.dk)}.get(w.variant, (w.B, w.H)),
                        dtype=torch.float32, device=t["q"].device))
     warm(lambda: kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out), warmup)
     # whole timed loop
@@ -304,8 +310,8 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic, long-context "
-                         "and backward lines")
+                    help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic, grouped-noise, "
+                         "long-context and backward lines")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the workload of the rocprofv3 counter runs and exit")
@@ -362,6 +368,12 @@ def main():
         extra["isochannel"] = {"workload": wc.name, "tokens_per_s": wc.B * wc.T / (mc / 1e3), "ms_per_step": mc,
                                "hbm_frac": forward_bytes(wc) / (lc / 1e3) / 1e9 / HBM_PEAK_GBS}
         del tc
+        wg = wl.WORKLOADS["grouped_bf16_b8_t4096_h16_d128"]
+        tg = upload(wl.forward_inputs(wg), wg.dtype, dev)
+        mg, lg = time_forward(kdn, wg, tg, 3, 1, "auto")
+        extra["grouped"] = {"workload": wg.name, "tokens_per_s": wg.B * wg.T / (mg / 1e3), "ms_per_step": mg,
+                            "hbm_frac": forward_bytes(wg) / (lg / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del tg
         wlc = wl.WORKLOADS["diag_bf16_b1_t65536_h16_d128"]
         tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)
         mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "auto")
