@@ -183,7 +183,8 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
     const int64_t units = int64_t(B) * H;
     const int64_t toks = units * T;
-    if (units > INT32_MAX || toks > kMaxElems / 128)
+    // the memory kernel launches one workgroup per (batch, head, 64 value columns)
+    if (units * (dv / 64) > INT32_MAX || toks > kMaxElems / 128)
         return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
     if (units == 0) return ok();
     if (variant == KDN_DIAGONAL_GROUPED)
