@@ -144,8 +144,10 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
 
     q, k [B,T,H,dk]; v [B,T,H,dv]; alpha, omega [B,T,H,dk] (isotropic [B,T,H];
     "isochannel", the isotropic form with per-channel decay: alpha [B,T,H,dk],
-    omega [B,T,H]); r [B,T,H] -- all float32 or all bfloat16.  c0 [H] float32 (may be None if
-    p0 is given); S0 [B,H,dk,dv] / p0 [B,H,dk] (isotropic [B,H]) float32 or None.
+    omega [B,T,H]); r [B,T,H] ("grouped", grouped observation noise: [B,T,H,dv/64])
+    -- all float32 or all bfloat16.  c0 [H] float32 (may be None if p0 is given);
+    S0 [B,H,dk,dv] / p0 [B,H,dk] (isotropic [B,H]; grouped [B,H,dv/64,dk])
+    float32 or None.
     Returns (o, S_T, p_T); ``out`` may supply preallocated (o, S_T, p_T).
     """
     torch = _torch()
