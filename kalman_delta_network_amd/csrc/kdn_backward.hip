@@ -275,10 +275,14 @@ __device__ __forceinline__ void fwd_token(const TokIn<DK, VAR, Tin>& x, float (&
 // bit 2 - s differs (7 - cq, then cq ^ 2, then cq ^ 1); each keeps the half
 // its own bit selects and receives the partner's copy of that half.
 // The halves are chosen with a per-lane bit mask (one bitfield insert per
-// value) rather than a compare-and-select, which needs a lane mask in scalar
-// registers for every select.
+// value) rather than a compare-and-select, which kept a lane mask in scalar
+// registers per select and spilled them.
 __device__ __forceinline__ float pick(uint32_t mask, float if_set, float if_clear) {
-    return __uint_as_float((mask & __float_as_uint(if_set)) | (~mask & __float_as_uint(if_clear)));
+    // (mask & if_set) | (~mask & if_clear) as one bitfield insert; written
+    // out, the compiler emits an and plus an and-or per value
+    float r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(if_set), "v"(if_clear));
+    return r;
 }
 
 template <int N>
