@@ -122,16 +122,17 @@ def test_backward_deterministic(dev):
         assert torch.equal(a[n], b[n]), n
 
 
-def test_backward_full_size_sampled_heads(dev):
-    """The B=8, T=4096, H=16, d=128 diagonal workload in the launch
-    configuration the benchmark times; the oracle runs on sampled heads."""
+@pytest.mark.parametrize("name", ["diag_bf16_b8_t4096_h16_d128", "iso_bf16_b8_t4096_h16_d128"])
+def test_backward_full_size_sampled_heads(dev, name):
+    """The B=8, T=4096, H=16, d=128 workloads (the diagonal one in the launch
+    configuration the benchmark times); the oracle runs on sampled heads."""
     import torch
     import kalman_delta_network_amd as kdn
-    w = wl.WORKLOADS["diag_bf16_b8_t4096_h16_d128"]
+    w = wl.WORKLOADS[name]
     x = wl.forward_inputs(w)
     ct = wl.backward_cotangents(w, with_state=False)
     t = to_dev(x, "bf16", dev)
-    g = kdn.backward(**t, mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev))
+    g = kdn.backward(**t, mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev), variant=w.variant)
     torch.cuda.synchronize()
     got = {n: v.cpu().numpy() for n, v in g.items()}
     pairs = sample_pairs(w.B, w.H, 2, seed=w.seed)
@@ -143,7 +144,7 @@ def test_backward_full_size_sampled_heads(dev):
         for k in GRADS:
             gk = got[k][b:b + 1, :, h:h + 1] if k not in ("dS0", "dp0") else got[k][b:b + 1, h:h + 1]
             worst[k] = max(worst[k], rel_err(gk, ref[k]))
-    print(f"full size pairs={pairs}: " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)
+    print(f"full size {name} pairs={pairs}: " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)
     for k, e in worst.items():
         assert e <= tol("bf16"), (k, e)
     for k in GRADS:
