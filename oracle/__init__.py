@@ -230,13 +230,46 @@ def step_isoc(q, k, v, alpha, omega, r, mu, S, p):
 _VARIANTS = {"diagonal": 0, "isotropic": 1, "isochannel": 2}
 
 
+def _backward_grouped(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, S0, p0):
+    """Adjoint of forward_grouped: the groups are independent diagonal
+    recurrences on their value columns that share q, k, alpha, omega, so the
+    gradients of the shared inputs are the sums over the groups of each
+    group's diagonal adjoint, and those of v, r, S0, p0 are the groups' own."""
+    r = np.asarray(r)
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    G = r.shape[-1]
+    gw = dv // G
+    out = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, H, dk)), "dv": np.zeros((B, T, H, dv)),
+           "dalpha": np.zeros((B, T, H, dk)), "domega": np.zeros((B, T, H, dk)), "dr": np.zeros((B, T, H, G)),
+           "dS0": np.zeros((B, H, dk, dv)), "dp0": np.zeros((B, H, G, dk)), "dc0": np.zeros(H)}
+    for g in range(G):
+        cols = slice(g * gw, (g + 1) * gw)
+        res = backward(q, k, np.asarray(v)[..., cols], alpha, omega, r[..., g], c0, mu,
+                       None if dO is None else np.asarray(dO)[..., cols],
+                       None if dS_T is None else np.asarray(dS_T)[..., cols],
+                       None if dp_T is None else np.asarray(dp_T)[:, :, g],
+                       None if S0 is None else np.asarray(S0)[..., cols],
+                       None if p0 is None else np.asarray(p0)[:, :, g], "diagonal")
+        for n in ("dq", "dk", "dalpha", "domega", "dc0"):
+            out[n] += res[n]
+        out["dv"][..., cols] = res["dv"]
+        out["dr"][..., g] = res["dr"]
+        out["dS0"][..., cols] = res["dS0"]
+        out["dp0"][:, :, g] = res["dp0"]
+    return out
+
+
 def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, S0=None, p0=None,
              variant="diagonal"):
     """Gradients of L = sum(dO*o) + sum(dS_T*S_T) + sum(dp_T*p_T) for the
     forward of ``variant`` on these inputs (any of dO, dS_T, dp_T may be None
     for zero).  Returns dict dq, dk, dv, dalpha, domega, dr (input layouts),
-    dS0 [B,H,dk,dv], dp0 [B,H,dk] (isotropic forms [B,H]) and dc0 [H] (the sum
-    of dp0 over batch and channels: the c0 gradient when p0 is None)."""
+    dS0 [B,H,dk,dv], dp0 [B,H,dk] (isotropic forms [B,H]; grouped noise
+    [B,H,G,dk], dr [B,T,H,G]) and dc0 [H] (the sum of dp0 over batch, groups
+    and channels: the c0 gradient when p0 is None)."""
+    if variant == "grouped":
+        return _backward_grouped(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, S0, p0)
     var = _VARIANTS[variant]
     q, k, v, alpha, omega, r = (_in(x) for x in (q, k, v, alpha, omega, r))
     B, T, H, dk = q.shape

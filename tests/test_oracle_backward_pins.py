@@ -15,13 +15,14 @@ import pytest
 import oracle
 from kalman_delta_network_amd import workloads as wl
 
-FWD = {"diagonal": oracle.forward_diag, "isotropic": oracle.forward_iso, "isochannel": oracle.forward_isoc}
+FWD = {"diagonal": oracle.forward_diag, "isotropic": oracle.forward_iso, "isochannel": oracle.forward_isoc,
+       "grouped": oracle.forward_grouped}
 TOKEN = ("q", "k", "v", "alpha", "omega", "r")
 
 
-def _case(variant, with_state, seed, B=2, T=6, H=2, dk=4, dv=3, omega_loc=-1.0, mu=None):
+def _case(variant, with_state, seed, B=2, T=6, H=2, dk=4, dv=3, omega_loc=-1.0, mu=None, rgroups=1):
     w = wl.Workload("fd", variant, "f32", B, T, H, dk, dv, float(dk if mu is None else mu), "uniform",
-                    seed, omega_loc=omega_loc)
+                    seed, omega_loc=omega_loc, rgroups=rgroups)
     x = {n: np.asarray(a, np.float64) for n, a in wl.forward_inputs(w).items()}
     ct = wl.backward_cotangents(w, with_state=True)
     st = wl.decode_state(w) if with_state else {"S0": None, "p0": None}
@@ -72,6 +73,22 @@ def test_backward_matches_finite_differences(variant, with_state):
         # p_0 = c0[h] on every channel: dc0 is the derivative with respect to c0
         _check(g["dc0"], _fd(w, x, ct, st, x, "c0"), "c0")
         np.testing.assert_allclose(g["dc0"], g["dp0"].reshape(w.B, w.H, -1).sum(axis=(0, 2)), rtol=1e-12)
+
+
+@pytest.mark.parametrize("with_state", [True, False])
+def test_grouped_noise_backward_matches_finite_differences(with_state):
+    w, x, ct, st = _case("grouped", with_state, seed=41 + with_state, dv=4, rgroups=2)
+    if with_state:
+        st = {n: np.asarray(a, np.float64) for n, a in st.items()}
+    g = oracle.backward(**{n: x[n] for n in TOKEN}, c0=x["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
+                        dp_T=ct["dp_T"], S0=st["S0"], p0=st["p0"], variant="grouped")
+    for name in TOKEN:
+        _check(g["d" + name], _fd(w, x, ct, st, x, name), name)
+    if with_state:
+        _check(g["dS0"], _fd(w, x, ct, st, st, "S0"), "S0")
+        _check(g["dp0"], _fd(w, x, ct, st, st, "p0"), "p0")
+    else:
+        _check(g["dc0"], _fd(w, x, ct, st, x, "c0"), "c0")
 
 
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
