@@ -36,8 +36,8 @@
  *   64 value columns, diag[r_1 I, ..., r_G I] with G = d_v / 64, so each
  *   group keeps its own uncertainty p_g and gain; the groups share q, k,
  *   alpha, omega, and each is the diagonal recurrence above on its columns
- *   with r_t,g.  Shapes: r [.., G], p0 / p_T / the decode p [B,H,G,dk].
- *   kdn_backward does not cover it (KDN_ERR_UNSUPPORTED).
+ *   with r_t,g.  Shapes: r [.., G], p0 / p_T / the decode p [B,H,G,dk]
+ *   (kdn_backward: dr [.., G], dp_T / dp0 [B,H,G,dk]).
  *
  * Initial state: S_0 = S0 (or zero when S0 is NULL); p_0 = p0 (or c0[h] on
  * every channel when p0 is NULL).  No 1/sqrt(d_k) scaling is applied to q.
@@ -202,7 +202,8 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
  *   q, k, v, alpha, omega, r, c0, S0, p0, variant, dtype, sizes: as kdn_forward
  *   dO    [B,T,H,dv]   dtype, may be NULL (zero)
  *   dS_T  [B,H,dk,dv]  float, may be NULL (zero)
- *   dp_T  [B,H,dk]     float ([B,H] for both isotropic variants), may be NULL (zero)
+ *   dp_T  [B,H,dk]     float ([B,H] for both isotropic variants, [B,H,dv/64,dk] for
+ *                      grouped observation noise), may be NULL (zero)
  *   dq, dk, dv, dalpha, domega, dr: float outputs in the layouts of
  *                      q, k, v, alpha, omega, r
  *   dS0   [B,H,dk,dv]  float output (gradient with respect to S0, or to the
@@ -228,8 +229,9 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
                  float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
                  void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
- * B*H*((dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk) + T*((dv/64)*4 + 1)*dk)*4
- * (recomputation checkpoints per 64-column tile, plus per-token partial sums). */
+ * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4
+ * (recomputation checkpoints per 64-column tile, plus per-token partial sums
+ * and uncertainties per tile). */
 size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv);
 int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
                           const void* omega, const void* r, const float* c0, float mu, int variant,

@@ -290,15 +290,14 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
-    if var == KDN_DIAGONAL_GROUPED:
-        raise KDNError(KDN_ERR_UNSUPPORTED, "kdn_backward", "grouped observation noise is not covered")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     ashape, wshape = _gate_shapes(var, (B, T, H), dk)
-    pshape = (B, H, dk) if var == KDN_DIAGONAL else (B, H)
+    pshape = _p_shape(var, (B, H), dk, dv)
+    rshape = _r_shape(var, (B, T, H), dv)
     for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, (B, T, H))):
+                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, rshape)):
         _need(t, name, shp, dt, dev)
     if dO is not None:
         _need(dO, "dO", (B, T, H, dv), dt, dev)
@@ -309,7 +308,7 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     f32 = dict(dtype=torch.float32, device=dev)
     g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
          "dv": torch.empty((B, T, H, dv), **f32), "dalpha": torch.empty(ashape, **f32),
-         "domega": torch.empty(wshape, **f32), "dr": torch.empty((B, T, H), **f32),
+         "domega": torch.empty(wshape, **f32), "dr": torch.empty(rshape, **f32),
          "dS0": torch.empty((B, H, dk, dv), **f32), "dp0": torch.empty(pshape, **f32),
          "dc0": torch.empty((H,), **f32)}
     need = backward_workspace_size(B, T, H, dk, dv)

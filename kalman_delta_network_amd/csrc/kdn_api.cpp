@@ -187,9 +187,8 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     if (units * (dv / 64) > INT32_MAX || toks > kMaxElems / 128)
         return fail(KDN_ERR_SHAPE, "problem too large (B=%d, T=%d, H=%d)", B, T, H);
     if (units == 0) return ok();
-    if (variant == KDN_DIAGONAL_GROUPED)
-        return fail(KDN_ERR_UNSUPPORTED, "the backward pass does not cover grouped observation noise");
     const bool iso = is_iso(variant), chan = variant != KDN_ISOTROPIC;
+    const size_t ng = noise_groups(variant, dv);
     if (toks > 0 && (!q || !k || !v || !alpha || !omega || !r))
         return fail(KDN_ERR_NULL, "q, k, v, alpha, omega and r must be non-NULL");
     if (toks > 0 && (!dq || !dk_out || !dv_out || !dalpha || !domega || !dr))
@@ -208,13 +207,13 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     const size_t es = dtype == KDN_BF16 ? 2 : 4;
     const size_t nk = size_t(toks) * dk, nv = size_t(toks) * dv;
     const size_t na = chan ? nk : size_t(toks), nw = iso ? size_t(toks) : nk;
-    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * dk;
+    const size_t ns = size_t(units) * dk * dv, np = iso ? size_t(units) : size_t(units) * ng * dk;
     const Span in[] = {span(q, nk, es),     span(k, nk, es),        span(v, nv, es),
-                       span(alpha, na, es), span(omega, nw, es),    span(r, size_t(toks), es),
+                       span(alpha, na, es), span(omega, nw, es),    span(r, size_t(toks) * ng, es),
                        span(c0, size_t(H), 4), span(S0, ns, 4),     span(p0, np, 4),
                        span(dO, nv, es),    span(dS_T, ns, 4),      span(dp_T, np, 4)};
     const Span out[] = {span(dq, nk, 4),     span(dk_out, nk, 4), span(dv_out, nv, 4),
-                        span(dalpha, na, 4), span(domega, nw, 4), span(dr, size_t(toks), 4),
+                        span(dalpha, na, 4), span(domega, nw, 4), span(dr, size_t(toks) * ng, 4),
                         span(dS0, ns, 4),    span(dp0, np, 4),    span(dc0, size_t(H), 4),
                         span(work, need, 1)};
     for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {

@@ -157,9 +157,10 @@ struct TokIn {
     Tin v[NC];
 };
 
-template <int DK, int VAR, typename Tin>
+// GR: grouped observation noise, r [.., ngroups]; this tile's group is rg_off
+template <int DK, int VAR, typename Tin, bool GR = false>
 __device__ __forceinline__ void load_tok(TokIn<DK, VAR, Tin>& x, const BwdArgs& A, size_t tok, int lane,
-                                         int col, int DVv) {
+                                         int col, int DVv, int ngroups = 1, int rg_off = 0) {
     constexpr int CPL = DK / 64;
     const Tin* q = static_cast<const Tin*>(A.q);
     const Tin* k = static_cast<const Tin*>(A.k);
@@ -175,7 +176,7 @@ __device__ __forceinline__ void load_tok(TokIn<DK, VAR, Tin>& x, const BwdArgs& 
         x.a[c] = VAR == 1 ? al[tok] : al[e];
         x.w[c] = VAR == 0 ? om[e] : om[tok];
     }
-    x.r = r[tok];
+    x.r = r[GR ? tok * size_t(ngroups) + size_t(rg_off) : tok];
 #pragma unroll
     for (int j = 0; j < NC; ++j) x.v[j] = v[tok * DVv + col + j];
 }
@@ -308,7 +309,9 @@ constexpr int TILE = 64;  // value columns per memory-adjoint workgroup
 // reverse walk.  Each token's four per-row sums of the tile (dq, d_kappa,
 // dk_mem, dalpha_mem) go to the workspace for the uncertainty kernel; tile 0
 // also stores p_{t-1} of every token there.
-template <int DK, int DV, int VAR, typename Tin>
+// GR (diagonal only): grouped observation noise, one r and one uncertainty
+// state per tile; the tile's chain uses its group's r and p.
+template <int DK, int DV, int VAR, typename Tin, bool GR = false>
 __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(BwdArgs A) {
     constexpr int NTILE = DV / TILE;
     constexpr int NW = TILE / WCOLS;  // memory waves
@@ -317,6 +320,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     constexpr int NT = NW * 64;       // threads
     constexpr bool ISO = VAR != 0;
     static_assert(DK % 64 == 0 && DV % TILE == 0 && NW >= 4 && SEG % PF == 0, "unsupported tile");
+    static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
 
     __shared__ BwdSmem<DK, TILE> sm;
 
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     float4* ckS4 = reinterpret_cast<float4*>(ckS);
     constexpr int SNAP = NT * (RPT / SG);  // float4 per snapshot
     float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);  // [unit][T][NTILE][4][DK]
-    float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;                    // [unit][T][DK]
+    float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;                    // [unit][T][NTILE][DK]
     const size_t sbase = size_t(unit) * DK * DV;
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
 
@@ -361,7 +365,8 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
             pb = A.p0 ? A.p0[unit] : A.c0[h];
         } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) p[c] = A.p0 ? A.p0[size_t(unit) * DK + lane + 64 * c] : A.c0[h];
+            for (int c = 0; c < CPL; ++c)
+                p[c] = A.p0 ? A.p0[(GR ? size_t(unit) * NTILE + tile : size_t(unit)) * DK + lane + 64 * c] : A.c0[h];
         }
         for (int seg = 0; seg < nseg; ++seg) {
             float4* ck = ckS4 + size_t(seg) * SNAP;
@@ -379,7 +384,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
             // before token t's arithmetic, and no register copy waits for a load
             const int s0 = seg * SEG;
             const auto ld = [&](TokIn<DK, VAR, Tin>& x, int t) {
-                load_tok(x, A, tokidx(min(t, T - 1)), lane, col, DV);
+                load_tok<DK, VAR, Tin, GR>(x, A, tokidx(min(t, T - 1)), lane, col, DV, NTILE, tile);
             };
             const auto run = [&](const TokIn<DK, VAR, Tin>& x) {
                 fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], nullptr, nullptr, nullptr, lane, rg,
@@ -430,14 +435,14 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
                 for (int c = 0; c < CPL; ++c) p[c] = cp[lane + 64 * c];
             }
             const bool rec = wave == 0;
-            const bool rec_p = rec && tile == 0;
+            const bool rec_p = rec && (GR || tile == 0);  // p_{t-1} of each group
             const auto run = [&](const TokIn<DK, VAR, Tin>& x, int tt) {
                 fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], rec ? sm.seg_chan[tt] : nullptr,
-                                              rec_p ? pbuf + (size_t(unit) * T + t0 + tt) * DK : nullptr,
+                                              rec_p ? pbuf + ((size_t(unit) * T + t0 + tt) * NTILE + tile) * DK : nullptr,
                                               stash + size_t(tt) * SNAP, lane, rg, tid);
             };
             const auto ld = [&](TokIn<DK, VAR, Tin>& x, int tt) {
-                load_tok(x, A, tokidx(t0 + min(tt, n - 1)), lane, col, DV);
+                load_tok<DK, VAR, Tin, GR>(x, A, tokidx(t0 + min(tt, n - 1)), lane, col, DV, NTILE, tile);
             };
             TokIn<DK, VAR, Tin> x0, x1, x2, x3;
             ld(x0, 0);
@@ -651,7 +656,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
             }
             u.al[c] = VAR == 1 ? ain[tok] : ain[tok * DK + i];
             u.kk[c] = kin[tok * DK + i];
-            u.pp[c] = ISO ? pbuf[(size_t(unit) * T + t) * DK] : pbuf[(size_t(unit) * T + t) * DK + i];
+            u.pp[c] = ISO ? pbuf[(size_t(unit) * T + t) * NTILE * DK] : pbuf[(size_t(unit) * T + t) * NTILE * DK + i];
             u.w[c] = VAR == 0 ? omg[tok * DK + i] : omg[tok];
         }
         u.r = rr[tok];
@@ -770,6 +775,138 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
     }
 }
 
+// Uncertainty adjoint of the grouped-noise form, one wave per (batch, head):
+// per token and group, the diagonal uncertainty adjoint with the group's r,
+// p_{t-1}, carried dp and its tile's row sums; the gradients of the shared
+// k, alpha, omega are summed over the groups, dr and dp0 are per group.
+template <int DK, int DV, typename Tin>
+__global__ void __launch_bounds__(64) kdn_backward_unc_grouped_kernel(BwdArgs A) {
+    constexpr int G = DV / TILE;
+    constexpr int CPL = DK / 64;
+    const int nunit = A.B * A.H;
+    const int unit = int(blockIdx.x);
+    const int h = unit % A.H;
+    const size_t b = size_t(unit / A.H);
+    const int T = A.T;
+    const int lane = threadIdx.x;
+    const float mu = A.mu;
+    const float* partial = A.work + size_t(nunit) * G * unit_floats(T, DK, TILE);
+    const float* pbuf = partial + size_t(nunit) * T * G * 4 * DK;
+    const Tin* kin = static_cast<const Tin*>(A.k);
+    const Tin* ain = static_cast<const Tin*>(A.alpha);
+    const Tin* omg = static_cast<const Tin*>(A.omega);
+    const Tin* rr = static_cast<const Tin*>(A.r);
+    const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
+
+    float dp[G][CPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            dp[g][c] = A.dp_T ? A.dp_T[(size_t(unit) * G + g) * DK + lane + 64 * c] : 0.f;
+
+    struct UncG {
+        float q[CPL], k[G][CPL], ks[G][CPL], a[G][CPL], pp[G][CPL];
+        Tin al[CPL], kk[CPL], w[CPL], r[G];
+    };
+    const auto load = [&](UncG& u, int t) {
+        const size_t tok = tokidx(t);
+        const float* src = partial + (size_t(unit) * T + t) * G * 4 * DK;
+        const float* ps = pbuf + (size_t(unit) * T + t) * G * DK;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int i = lane + 64 * c;
+            u.q[c] = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                u.q[c] += src[(g * 4 + 0) * DK + i];
+                u.k[g][c] = src[(g * 4 + 1) * DK + i];
+                u.ks[g][c] = src[(g * 4 + 2) * DK + i];
+                u.a[g][c] = src[(g * 4 + 3) * DK + i];
+                u.pp[g][c] = ps[g * DK + i];
+            }
+            u.al[c] = ain[tok * DK + i];
+            u.kk[c] = kin[tok * DK + i];
+            u.w[c] = omg[tok * DK + i];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) u.r[g] = rr[tok * G + g];
+    };
+    const auto step = [&](int t, const UncG& u, UncG& ahead) {
+        const size_t tok = tokidx(t);
+        float al[CPL], kk[CPL], wc[CPL], dkacc[CPL], daacc[CPL], dwacc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            al[c] = to_f32(u.al[c]);
+            kk[c] = to_f32(u.kk[c]);
+            wc[c] = to_f32(u.w[c]);
+            dkacc[c] = daacc[c] = dwacc[c] = 0.f;
+            A.dq[tok * DK + lane + 64 * c] = u.q[c];
+        }
+        float rg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) rg[g] = to_f32(u.r[g]);
+        load(ahead, max(t - (PF - 1), 0));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            // the diagonal uncertainty adjoint of group g (gain, posterior, predict)
+            const float rt = rg[g];
+            float ph[CPL];
+            float s = 0.f, kd = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                ph[c] = al[c] * al[c] * u.pp[g][c] + wc[c];
+                s += ph[c] * kk[c] * kk[c];
+                kd += u.k[g][c] * ph[c] * kk[c];
+            }
+            s = wave_sum(s);
+            const float d = rt + s;
+            const float inv = 1.0f / d;
+            const float dd = -wave_sum(kd) * inv * inv;
+            const float mr = mu / rt;
+            float drr = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float k2 = kk[c] * kk[c];
+                const float den = 1.0f + mr * k2 * ph[c];
+                const float pn = ph[c] / den;
+                const float du = -dp[g][c] * pn * pn;
+                const float dph = dp[g][c] / (den * den) + u.k[g][c] * kk[c] * inv + dd * k2;
+                drr -= du * mr * k2 / rt;
+                dkacc[c] += u.ks[g][c] + u.k[g][c] * ph[c] * inv + 2.0f * dd * ph[c] * kk[c] + 2.0f * du * mr * kk[c];
+                daacc[c] += u.a[g][c] + 2.0f * dph * al[c] * u.pp[g][c];
+                dwacc[c] += dph;
+                dp[g][c] = dph * al[c] * al[c];
+            }
+            drr = wave_sum(drr);
+            if (lane == 0) A.dr[tok * G + g] = dd + drr;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int i = lane + 64 * c;
+            A.dk_[tok * DK + i] = dkacc[c];
+            A.dalpha[tok * DK + i] = daacc[c];
+            A.domega[tok * DK + i] = dwacc[c];
+        }
+    };
+    UncG u0, u1, u2, u3;
+    if (T > 0) {
+        load(u0, T - 1);
+        load(u1, max(T - 2, 0));
+        load(u2, max(T - 3, 0));
+    }
+    for (int t = T - 1; t >= 0; t -= PF) {
+        step(t, u0, u3);
+        if (t - 1 >= 0) step(t - 1, u1, u0);
+        if (t - 2 >= 0) step(t - 2, u2, u1);
+        if (t - 3 >= 0) step(t - 3, u3, u2);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) A.dp0[(size_t(unit) * G + g) * DK + lane + 64 * c] = dp[g][c];
+}
+
 // dc0[h] = sum over the batch and the channels of dp0 (the c0 gradient when
 // p_0 = c0[h] on every channel): one wave per head, each lane summing a fixed
 // strided subset, then a fixed-order wave sum
@@ -800,8 +937,21 @@ hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
     return a.dtype == 1 ? launch_t<DK, DV, VAR, bf16_t>(a, s) : launch_t<DK, DV, VAR, float>(a, s);
 }
 
+template <int DK, int DV, typename Tin>
+hipError_t launch_grouped_t(const BwdArgs& a, hipStream_t stream) {
+    const unsigned units = unsigned(long(a.B) * a.H);
+    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, 0, Tin, true>), dim3(units * (DV / TILE)),
+                       dim3(TILE / WCOLS * 64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kdn_backward_unc_grouped_kernel<DK, DV, Tin>), dim3(units), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DK, int DV>
 hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
+    if (a.variant == 3)  // diagonal with grouped observation noise
+        return a.dtype == 1 ? launch_grouped_t<DK, DV, bf16_t>(a, s) : launch_grouped_t<DK, DV, float>(a, s);
     if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
     return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
 }
@@ -811,8 +961,8 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (long(B) * H == 0 || T == 0) return 0;
     const size_t units = size_t(B) * size_t(H), ntile = size_t(dv) / TILE;
-    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1}
-    return (units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * (ntile * 4 + 1) * dk) * sizeof(float);
+    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1} (per tile)
+    return (units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * ntile * 5 * dk) * sizeof(float);
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
@@ -823,7 +973,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     else if (a.dk == 64 && a.dv == 64) e = launch_variant<64, 64>(a, stream);
     else return hipErrorNotSupported;
     if (e != hipSuccess || !a.dc0) return e;
-    const int pd = a.variant == 0 ? a.dk : 1;
+    const int pd = a.variant == 0 ? a.dk : a.variant == 3 ? (a.dv / TILE) * a.dk : 1;
     hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned(a.H)), dim3(64), 0, stream, a.dp0, a.dc0, a.B, a.H, pd);
     return hipGetLastError();
 }

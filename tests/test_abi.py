@@ -292,11 +292,11 @@ def call_validate_bwd(lib, a):
 
 
 def test_backward_workspace_size_formula(lib):
-    # per 64-column tile: ceil(T/32) checkpoints of S and of p (one copy per 8 value columns) and a
-    # 32-token stash; per token: the tiles' four row sums and p_{t-1}
+    # per 64-column tile: ceil(T/32) checkpoints of S and of p (one copy per 8 value columns), a
+    # 32-token stash, and per token the tile's four row sums and p_{t-1}
     for B, T, H, dk, dv in ((2, 40, 3, 64, 128), (8, 4096, 16, 128, 128), (1, 1, 1, 128, 64)):
         nseg, nt = -(-T // 32), dv // 64
-        want = B * H * (nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk) + T * (nt * 4 + 1) * dk) * 4
+        want = B * H * nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk + 5 * T * dk) * 4
         assert lib.kdn_backward_workspace_size(B, T, H, dk, dv) == want
     assert lib.kdn_backward_workspace_size(0, 10, 2, 64, 64) == 0
     assert lib.kdn_backward_workspace_size(2, 0, 2, 64, 64) == 0
@@ -318,7 +318,7 @@ def test_validate_backward_accepts_good_arguments(lib):
 @pytest.mark.parametrize("over,status", [
     (dict(mu=-1.0), kdn.KDN_ERR_VALUE),
     (dict(dk=96), kdn.KDN_ERR_UNSUPPORTED),
-    (dict(variant=3), kdn.KDN_ERR_UNSUPPORTED),
+    (dict(variant=4), kdn.KDN_ERR_UNSUPPORTED),
     (dict(T=-1), kdn.KDN_ERR_SHAPE),
     (dict(q=None), kdn.KDN_ERR_NULL),
     (dict(g_k=None), kdn.KDN_ERR_NULL),
@@ -353,11 +353,12 @@ def test_backward_launch_error_path_without_gpu(lib, monkeypatch):
     assert lib.kdn_backward(*_bwd_list(dict(a, mu=float("nan"))), None) == kdn.KDN_ERR_VALUE
 
 
-def test_grouped_noise_is_a_forward_variant_without_backward(lib):
+def test_grouped_noise_variant(lib):
     f = Fake()
     assert call_validate(lib, fwd_args(f, variant=3, dv=128)) == 0
     assert call_validate(lib, fwd_args(f, variant=4)) == kdn.KDN_ERR_UNSUPPORTED
-    assert call_validate_bwd(lib, bwd_args(f, lib, variant=3)) == kdn.KDN_ERR_UNSUPPORTED
+    assert call_validate_bwd(lib, bwd_args(f, lib, variant=3, dv=128)) == 0
+    assert call_validate_bwd(lib, bwd_args(f, lib, variant=4)) == kdn.KDN_ERR_UNSUPPORTED
     # r and p hold one entry per group of 64 value columns: an output placed
     # right after a single-group r overlaps the second group's entries
     a = fwd_args(f, variant=3, dk=64, dv=128, B=1, T=8, H=1)

@@ -68,6 +68,20 @@ def test_backward_small(dev, variant, dtype, dk, dv, T):
     check(f"{variant}/{dtype}/dk{dk}/dv{dv}/T{T}", got, ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
+@pytest.mark.parametrize("T", [1, 33, 100])
+def test_backward_grouped_noise(dev, dtype, dk, dv, T):
+    w = wl.Workload("bwd_grp", "grouped", dtype, 2, T, 2, dk, dv, float(dk), "uniform", 400 + T, omega_loc=0.0,
+                    rgroups=dv // 64)
+    x = wl.forward_inputs(w)
+    ct = wl.backward_cotangents(w, with_state=True)
+    st = wl.decode_state(w) if T == 33 else {"S0": None, "p0": None}
+    got = run_backward(dev, w, x, ct, st)
+    ref = oracle_backward(w, x, ct, st)
+    check(f"grouped/{dtype}/dk{dk}/dv{dv}/T{T}", got, ref, dtype)
+
+
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
 def test_backward_with_initial_state_and_config_distributions(dev, variant):
     w = wl.Workload("bwd_state", variant, "bf16", 3, 77, 2, 128, 128, 128.0, "uniform", 7)
