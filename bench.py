@@ -27,6 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+CHUNK = 32  # tokens per chunk of the chunked forward
 MAIN = "diag_bf16_b8_t4096_h16_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -68,6 +70,14 @@ def step_bytes(w) -> int:
     units = w.B * w.H
     pdim = _pdim(w)
     return units * (2 * 4 * (w.dk * w.dv + pdim) + es * (2 * w.dk + w.dv + _gate_elems(w) + 1) + es * w.dv)
+
+
+def forward_flops(w) -> int:
+    """Algorithmic matrix flops of one chunked forward: per token-head
+    2 L (d_k + d_v) for the chunk's triangular L x L products (tril(Kt Kh^T),
+    tril(Qt Kh^T), the solve and tril(Qt Kh^T) Dn) plus 6 d_k d_v for
+    Kt S, Qt S and the state update, at L = CHUNK."""
+    return w.B * w.T * w.H * (2 * CHUNK * (w.dk + w.dv) + 6 * w.dk * w.dv)
 
 
 def backward_bytes(w) -> int:
@@ -404,6 +414,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "launch_ms": ms_launch},
+        "mfma": {"achieved": forward_flops(w) / (ms_launch / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": forward_flops(w) / (ms_launch / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "flops": forward_flops(w)},
         "cpu_baseline": cpu,
         "extra": extra,
     }
