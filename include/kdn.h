@@ -88,12 +88,18 @@ enum kdn_status {
 /* forward algorithms (kdn_forward_algo).  The chunked algorithm takes bf16
  * inputs (dk and dv are 64 or 128 for every algorithm), q, k, v, alpha and omega
  * 16-byte aligned and o 8-byte aligned; KDN_ALGO_AUTO uses it whenever these
- * hold and the recurrent kernel otherwise, and an explicit KDN_ALGO_CHUNKED
- * call outside them returns KDN_ERR_UNSUPPORTED. */
+ * hold and the recurrent kernel otherwise, and an explicit KDN_ALGO_CHUNKED*
+ * call outside them returns KDN_ERR_UNSUPPORTED.  One chunked workgroup
+ * handles one (batch, head) pair and 64 value columns, or 32 when that
+ * leaves more than half of the GPU's 256 compute units idle (AUTO and
+ * CHUNKED choose; _WIDE and _NARROW force a width). */
 enum kdn_algo {
     KDN_ALGO_AUTO = 0,      /* the library picks (chunked when available) */
     KDN_ALGO_RECURRENT = 1, /* token-by-token recurrence, state in registers */
-    KDN_ALGO_CHUNKED = 2    /* chunkwise WY/UT form on matrix cores */
+    KDN_ALGO_CHUNKED = 2,   /* chunkwise WY/UT form on matrix cores */
+    KDN_ALGO_CHUNKED_WIDE = 3,   /* chunked, 64 value columns per workgroup */
+    KDN_ALGO_CHUNKED_NARROW = 4  /* chunked, 32 value columns per workgroup (not with
+                                    grouped observation noise) */
 };
 
 /*

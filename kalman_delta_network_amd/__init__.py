@@ -19,7 +19,7 @@ KDN_DIAGONAL, KDN_ISOTROPIC = 0, 1
 KDN_F32, KDN_BF16 = 0, 1
 (KDN_OK, KDN_ERR_NULL, KDN_ERR_SHAPE, KDN_ERR_UNSUPPORTED, KDN_ERR_VALUE, KDN_ERR_HIP, KDN_ERR_ALIAS,
  KDN_ERR_WORKSPACE) = range(8)
-ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_wide": 3, "chunked_narrow": 4}
 KDN_ISOTROPIC_CHANNEL = 2
 KDN_DIAGONAL_GROUPED = 3
 VARIANTS = {"diagonal": KDN_DIAGONAL, "isotropic": KDN_ISOTROPIC, "isochannel": KDN_ISOTROPIC_CHANNEL,

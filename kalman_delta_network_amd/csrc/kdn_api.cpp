@@ -83,7 +83,8 @@ int validate_forward_core(const void* q, const void* k, const void* v, const voi
                           void* o, float* S_T, float* p_T, int algo) {
     int st = validate_common(variant, dtype, mu, dk, dv);
     if (st != KDN_OK) return st;
-    if (algo != KDN_ALGO_AUTO && algo != KDN_ALGO_RECURRENT && algo != KDN_ALGO_CHUNKED)
+    if (algo != KDN_ALGO_AUTO && algo != KDN_ALGO_RECURRENT && algo != KDN_ALGO_CHUNKED &&
+        algo != KDN_ALGO_CHUNKED_WIDE && algo != KDN_ALGO_CHUNKED_NARROW)
         return fail(KDN_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
     if (units == 0) return ok();  // nothing to read or write
     const bool iso = is_iso(variant);                      // one uncertainty scalar per head
@@ -232,11 +233,14 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // launches a validated forward (a.cu_seqlens set for a packed batch)
-int run_forward(const kdn::FwdArgs& a, hipStream_t s, int algo) {
+int run_forward(kdn::FwdArgs a, hipStream_t s, int algo) {
     if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
-    if (algo == KDN_ALGO_CHUNKED) {
+    if (algo == KDN_ALGO_CHUNKED || algo == KDN_ALGO_CHUNKED_WIDE || algo == KDN_ALGO_CHUNKED_NARROW) {
         if (!kdn::chunked_supports(a))
             return fail(KDN_ERR_UNSUPPORTED, "the chunked algorithm does not support this shape");
+        a.chunk_width = algo == KDN_ALGO_CHUNKED_WIDE ? 64 : algo == KDN_ALGO_CHUNKED_NARROW ? 32 : 0;
+        if (a.chunk_width == 32 && a.variant == KDN_DIAGONAL_GROUPED)
+            return fail(KDN_ERR_UNSUPPORTED, "grouped observation noise needs 64-column workgroups");
         return hip_status(kdn::launch_chunked(a, s), "chunked forward");
     }
     if (algo == KDN_ALGO_AUTO && kdn::chunked_supports(a))

@@ -65,7 +65,12 @@ namespace {
 
 constexpr int L = 32;            // tokens per chunk
 constexpr int NT = L / 16;       // 16-token tiles per chunk
-constexpr int DVT = 64;          // value columns per workgroup
+constexpr int DVT = 64;          // value columns per workgroup (two state waves x two 16-column tiles)
+// A narrow workgroup (NCT = 1: one 16-column tile per state wave, 32 value
+// columns) doubles the workgroups of a head for batches too small to fill the
+// CUs; chain and formation work is per head, so it is repeated per tile.
+template <int NCT>
+__host__ __device__ constexpr int dvt_of() { return 32 * NCT; }
 constexpr int NTHREADS = 512;    // 8 waves
 constexpr int PT = L + 8;        // pitch (elements) of [rows][L] bf16 tiles
 constexpr int CHAIN_SPLIT = 16;  // chain tokens run before the mid-iteration barrier
@@ -866,59 +871,60 @@ __device__ __forceinline__ void mphase(Smem<DK>& sm, int nb, int rslot, int f) {
 }
 
 // ---------------------------------------------------------------------------
-// state role: wave cw in {0,1} owns 32 value columns, S in registers
+// state role: wave cw in {0,1} owns 16 NCT value columns, S in registers
 // ---------------------------------------------------------------------------
-// The state wave's v tile (L tokens x its 32 columns) of chunk c goes to LDS
-// ring slot c % 3 by direct loads, two chunks ahead: 128 16-byte pieces, two
-// instructions per wave.
-template <int DK>
+// The state wave's v tile (L tokens x its 16 NCT columns) of chunk c goes to
+// LDS ring slot c % 3 by direct loads, two chunks ahead: 64 NCT 16-byte
+// pieces, NCT instructions per wave.
+template <int DK, int NCT>
 __device__ __forceinline__ void state_issue_t(Smem<DK>& sm, const Args& a, size_t b, int h, int colb, int cw,
                                               int c, int nchunks) {
-    c = min(max(c, 0), nchunks - 1);  // always exactly two instructions (the wait below counts them)
+    c = min(max(c, 0), nchunks - 1);  // always exactly NCT instructions (the wait below counts them)
     const int lane = threadIdx.x & 63;
     const int last = a.T - 1 - c * L;
     const bf16_t* base = a.v + tokidx(a, b, h, c * L) * a.DV + colb;
     const uint32_t rs = uint32_t(a.H) * uint32_t(a.DV) * 2;
+    constexpr int PPT = 2 * NCT;  // 16-byte pieces per token
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int pc = lane + 64 * m;  // piece: token pc / 4, columns 8 (pc % 4) ..
-        const uint32_t off = uint32_t(min(pc / 4, last)) * rs + uint32_t(pc % 4) * 16;
+    for (int m = 0; m < NCT; ++m) {
+        const int pc = lane + 64 * m;  // piece: token pc / PPT, columns 8 (pc % PPT) ..
+        const uint32_t off = uint32_t(min(pc / PPT, last)) * rs + uint32_t(pc % PPT) * 16;
         g2lds16(base, off, &sm.RV[c % 3][cw][m * 512]);
     }
 }
 
-template <int DK>
+template <int DK, int NCT>
 struct StateAcc {
-    f4 S[DK / 16][2];
-    b8 Sb[DK / 32][2];  // S as bf16 MFMA operands (rebuilt after each update)
-    f4 O[NT][2];
-    b8 Db[2];  // Dn of the chunk (bf16, B-operand layout), per 16-column tile
+    f4 S[DK / 16][NCT];
+    b8 Sb[DK / 32][NCT];  // S as bf16 MFMA operands (rebuilt after each update)
+    f4 O[NT][NCT];
+    b8 Db[NCT];  // Dn of the chunk (bf16, B-operand layout), per 16-column tile
 };
-template <int DK>
-__device__ __forceinline__ void pack_state(StateAcc<DK>& st) {
+template <int DK, int NCT>
+__device__ __forceinline__ void pack_state(StateAcc<DK, NCT>& st) {
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) st.Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
+        for (int ct = 0; ct < NCT; ++ct) st.Sb[kk][ct] = pack8(st.S[2 * kk][ct], st.S[2 * kk + 1][ct]);
 }
 
-template <int DK>
+template <int DK, int NCT>
 // Rows of a tail chunk past the sequence end need no masking here: their v
 // rows repeat the last token (finite), their Kt and Kh are zero, so their Dn
 // reaches neither S nor any stored output row.
-__device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b, int cw, int vslot) {
+__device__ __forceinline__ void state_seg1(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, int cw, int vslot) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
     // read phase: v and every A operand of the segment
-    uint32_t vr[NT][2][4];
+    uint32_t vr[NT][NCT][4];
     b8 ak[NT][KS], aq[NT][KS];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vr[at][ct][e] = sm.RV[vslot][cw][(16 * at + g4 + e) * 32 + 16 * ct + n];
+            for (int e = 0; e < 4; ++e) vr[at][ct][e] = sm.RV[vslot][cw][(16 * at + g4 + e) * (16 * NCT) + 16 * ct + n];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             ak[at][kk] = *reinterpret_cast<const b8*>(sm.Kn[b] + sw<DK>(16 * at + n, 32 * kk + kg8));
@@ -928,12 +934,12 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
     const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[b][n * 16 + g4]);
     const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[b][256 + n * 16 + g4]);
     const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[b][n * 16 + g4]);
-    const b8 (&Sb)[KS][2] = st.Sb;
-    f4 R[NT][2];
+    const b8 (&Sb)[KS][NCT] = st.Sb;
+    f4 R[NT][NCT];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f4 r;
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = bf1(bf16_t(vr[at][ct][e]));
@@ -951,7 +957,7 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
     // since the previous iteration)
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
         const f4 d0 = mfma16(t0, pack4(R[0][ct]), zero);
         const f4 r1 = mfma16(mo, pack4(d0), R[1][ct]);
         const f4 d1 = mfma16(t1, pack4(r1), zero);
@@ -959,8 +965,8 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK>& st, Smem<DK>& sm, int b
     }
 }
 
-template <int DK>
-__device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
+template <int DK, int NCT>
+__device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
                                            int h, int colb, int c) {
     const int gring = c % 3;
     const bool full = (c + 1) * L <= a.T;
@@ -985,7 +991,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
     for (int at = 0; at < NT; ++at) {
         const bool ok = full || c * L + 16 * at + n < a.T;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             const f4 o = mfma32(Db[ct], aqk[at], st.O[at][ct]);  // (tril(Qt Kh^T) Dn)^T
             if (ok) *reinterpret_cast<u2*>(orow + 16 * ct) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
         }
@@ -995,14 +1001,14 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK>& st, Smem<DK>& sm, int b
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f4 s = mfma32(akh[it], Db[ct], st.S[it][ct]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[e] *= glv[it][e];
             st.S[it][ct] = s;
         }
     }
-    pack_state<DK>(st);  // operands of the next chunk's first segment
+    pack_state<DK, NCT>(st);  // operands of the next chunk's first segment
 }
 
 // ---------------------------------------------------------------------------
@@ -1026,12 +1032,14 @@ __device__ __forceinline__ int form_index(int w) {
 // GR (diagonal only): grouped observation noise, one r and one uncertainty
 // state p per group of DVT value columns, i.e. per column tile; the tiles of
 // a head are then independent diagonal recurrences sharing q, k, alpha, omega.
-template <int DK, int VAR, bool GR = false>
+template <int DK, int VAR, bool GR = false, int NCT = 2>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
     static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
+    static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
+    constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
     __shared__ Smem<DK> sm;
-    const int ntile = a.DV / DVT;
+    const int ntile = a.DV / DVTN;
     const int bid = blockIdx.x;
     // Work items are dealt to the eight XCDs in turn (block bid runs on XCD
     // bid % 8); the column tiles of one (batch, head) pair share an XCD and
@@ -1070,8 +1078,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     if (a.T == 0) {
         // an empty sequence: the final state is the initial one
         const size_t sb = size_t(unit) * DK * a.DV;
-        for (int e = threadIdx.x; e < DK * DVT; e += NTHREADS) {
-            const size_t x = sb + size_t(e / DVT) * a.DV + tile * DVT + e % DVT;
+        for (int e = threadIdx.x; e < DK * DVTN; e += NTHREADS) {
+            const size_t x = sb + size_t(e / DVTN) * a.DV + tile * DVTN + e % DVTN;
             a.S_T[x] = a.S0 ? a.S0[x] : 0.f;
         }
         if (GR || tile == 0) {
@@ -1209,42 +1217,42 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     } else if (is_state_wave(wave)) {
         // ---------------- state ----------------
         const int cw = state_index(wave);
-        const int colb = tile * DVT + cw * 32;
+        const int colb = tile * DVTN + cw * (16 * NCT);
         const int n = lane & 15, g4 = (lane >> 4) * 4;
-        StateAcc<DK> st;
+        StateAcc<DK, NCT> st;
         const size_t sbase = size_t(unit) * DK * a.DV;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     st.S[it][ct][e] = a.S0 ? a.S0[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] : 0.f;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) settle(st.S[it][ct]);  // S0 is ready before the loop
-        pack_state<DK>(st);
+            for (int ct = 0; ct < NCT; ++ct) settle(st.S[it][ct]);  // S0 is ready before the loop
+        pack_state<DK, NCT>(st);
         for (int it = 0; it < nit; ++it) {
             // chunk it's v is issued at iteration it, waited for at iteration
             // it + 1 and consumed at iteration it + 2 (ring slot it % 3)
             const int c = it - 2;  // chunk consumed at this iteration
-            state_issue_t<DK>(sm, a, b, h, colb, cw, it, nchunks);
-            if (c >= 0 && c < nchunks) state_seg1<DK>(st, sm, c & 1, cw, c % 3);
-            // everything but the two loads just issued has landed: the v of
+            state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (c >= 0 && c < nchunks) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
+            // everything but the NCT loads just issued has landed: the v of
             // chunk it - 1, the previous iteration's stores and chain rows
-            vm_wait<2>();
+            vm_wait<NCT>();
             bar();
             // rows 0..15 of the chain's chunk it + 2: the chain has read those
             // rows of chunk it (same buffer) before the barrier above
             if (VAR == 0) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
-            if (c >= 0 && c < nchunks) state_seg2<DK>(st, sm, c & 1, a, b, h, colb, c);
+            if (c >= 0 && c < nchunks) state_seg2<DK, NCT>(st, sm, c & 1, a, b, h, colb, c);
             bar();
         }
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
@@ -1293,7 +1301,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     }
 }
 
-template <int DK, int VAR, bool GR = false>
+template <int DK, int VAR, bool GR = false, int NCT = 2>
 hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0) return hipSuccess;
@@ -1318,14 +1326,24 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     a.cu = f.cu_seqlens;
     a.ord = f.seq_order;
     a.tok0 = 0;
-    const int ntile = f.dv / DVT;
+    const int ntile = f.dv / dvt_of<NCT>();
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR, GR>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR, GR, NCT>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Narrow workgroups (32 value columns) when the 64-column tiling leaves more
+// than half of the 256 CUs without a workgroup: one workgroup holds one CU
+// (its LDS), and a chunk takes as long in either width, so twice the
+// workgroups halve the time while they still fit on the CUs at once.
+constexpr long kNumCUs = 256;
+bool narrow_pays(const FwdArgs& a) {
+    if (a.chunk_width != 0) return a.chunk_width == dvt_of<1>();
+    return long(a.B) * a.H * (a.dv / DVT) * 2 <= kNumCUs;
+}
 
 }  // namespace
 
@@ -1339,14 +1357,23 @@ bool chunked_supports(const FwdArgs& a) {
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
+    if (a.variant == 3 && a.chunk_width == dvt_of<1>()) return hipErrorNotSupported;  // groups are 64 columns
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
     // variant 3: diagonal with grouped observation noise (one group per tile)
     if (a.dk == 128) {
         if (a.variant == 3) return launch_t<128, 0, true>(a, stream);
+        if (narrow_pays(a)) {
+            if (a.variant == 2) return launch_t<128, 2, false, 1>(a, stream);
+            return a.variant == 1 ? launch_t<128, 1, false, 1>(a, stream) : launch_t<128, 0, false, 1>(a, stream);
+        }
         if (a.variant == 2) return launch_t<128, 2>(a, stream);
         return a.variant == 1 ? launch_t<128, 1>(a, stream) : launch_t<128, 0>(a, stream);
     }
     if (a.variant == 3) return launch_t<64, 0, true>(a, stream);
+    if (narrow_pays(a)) {
+        if (a.variant == 2) return launch_t<64, 2, false, 1>(a, stream);
+        return a.variant == 1 ? launch_t<64, 1, false, 1>(a, stream) : launch_t<64, 0, false, 1>(a, stream);
+    }
     if (a.variant == 2) return launch_t<64, 2>(a, stream);
     return a.variant == 1 ? launch_t<64, 1>(a, stream) : launch_t<64, 0>(a, stream);
 }

@@ -34,6 +34,9 @@ struct FwdArgs {
     // packed batch only: the order in which sequences are scheduled (device
     // pointer, B entries, a permutation of 0..B-1) or NULL for 0..B-1
     const int* seq_order = nullptr;
+    // chunked forward: value columns per workgroup (64 or 32), 0 = chosen by
+    // occupancy
+    int chunk_width = 0;
 };
 
 // One backward call, after host validation.  Pointers are device pointers;
