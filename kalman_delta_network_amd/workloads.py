@@ -147,6 +147,28 @@ def forward_inputs(w: Workload) -> dict:
     return out
 
 
+def gated_inputs(w: Workload) -> dict:
+    """Inputs of one gated forward (diagonal layer): q, k, v as in
+    ``forward_inputs`` and, in place of alpha, omega and r, their gate
+    pre-activations z_alpha ~ N(alpha_loc, 0.5), z_omega ~ N(omega_loc, 1)
+    [B,T,H,dk] and z_r ~ N(0, 1) [B,T,H] (the distributions whose gated values
+    ``forward_inputs`` draws), all rounded to bf16 for bf16 workloads; c0 [H]."""
+    rng = np.random.default_rng([w.seed, 0x6A])
+    lead = (w.B, w.T, w.H)
+    out = {
+        "q": _l2norm(_normal(rng, lead + (w.dk,))),
+        "k": _l2norm(_normal(rng, lead + (w.dk,))),
+        "v": _normal(rng, lead + (w.dv,)),
+        "z_alpha": _normal(rng, lead + (w.dk,), w.alpha_loc, 0.5),
+        "z_omega": _normal(rng, lead + (w.dk,), w.omega_loc, 1.0),
+        "z_r": _normal(rng, lead),
+    }
+    if w.dtype == "bf16":
+        out = {key: round_bf16(val) for key, val in out.items()}
+    out["c0"] = _draw_c0(rng, w)
+    return out
+
+
 # packed variable-length serving batch: 32 sequences of 256..1792 tokens
 # (about 32k tokens in all, the token count of the main forward workload)
 VARLEN = Workload("varlen_diag_bf16_n32_h16_d128", "diagonal", "bf16", 32, 0, 16, 128, 128, 128.0,

@@ -18,6 +18,10 @@ it.
 * ``backward`` is the reverse-mode adjoint of the same recurrence (the
   gradients a training step needs), pinned by central finite differences of
   the forward.
+* ``gates`` and ``forward_gated``: the gate step that precedes the
+  recurrence (same summary page, method step 1): decay alpha = sigmoid(z),
+  process noise omega = softplus(z) and observation noise
+  r = r_min + softplus(z) with r_min = 0.01, from their pre-activations.
 * ``dense`` holds the brute-force dense-covariance filter (Bayesian Layer
   page, section 2.2, Proposition 1) used to pin the oracle.
 
@@ -287,3 +291,39 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, S0
     if rc != 0:
         raise ValueError(f"backward: bad arguments (rc={rc})")
     return out
+
+
+R_MIN = 0.01  # floor of the observation noise (summary page, method step 1)
+
+
+def sigmoid(z):
+    """Logistic function 1 / (1 + e^-z) in fp64, evaluated so that no
+    exponential overflows: e^-|z| lies in (0, 1]."""
+    z = np.asarray(z, np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def softplus(z):
+    """log(1 + e^z) in fp64 as max(z, 0) + log1p(e^-|z|) (no overflow, no
+    cancellation for large |z|)."""
+    z = np.asarray(z, np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def gates(z_alpha, z_omega, z_r):
+    """The gate step of the diagonal layer (summary page, method step 1):
+    per-channel decay alpha = sigmoid(z_alpha), per-channel process noise
+    omega = softplus(z_omega), per-token observation noise
+    r = 0.01 + softplus(z_r).  The pre-activations are what the token's
+    projections produce; the projections themselves are not part of this
+    step.  Returns (alpha, omega, r) in fp64."""
+    return sigmoid(_f64(z_alpha)), softplus(_f64(z_omega)), R_MIN + softplus(_f64(z_r))
+
+
+def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None):
+    """The diagonal forward fed through the gate step: ``gates`` on the
+    pre-activations, then ``forward_diag`` on the resulting alpha, omega, r."""
+    alpha, omega, r = gates(z_alpha, z_omega, z_r)
+    return forward_diag(q, k, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
+

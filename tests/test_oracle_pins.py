@@ -562,3 +562,58 @@ def test_grouped_noise_with_equal_groups_is_the_diagonal_form():
     np.testing.assert_array_equal(g["S"], d["S"])
     np.testing.assert_array_equal(g["p"][:, :, 0], d["p"])
     np.testing.assert_array_equal(g["p"][:, :, 1], d["p"])
+
+
+# --------------------------------------------------------------------------
+# The gate step (summary page, method step 1): sigmoid, softplus, r_min
+# --------------------------------------------------------------------------
+
+def test_gate_values_at_zero_and_in_the_tails():
+    # sigmoid(0) = 1/2, softplus(0) = ln 2, r(0) = r_min + ln 2 with r_min = 0.01
+    a, w, r = oracle.gates(np.zeros(3), np.zeros(3), np.zeros(3))
+    assert np.all(a == 0.5)
+    assert np.allclose(w, math.log(2.0), rtol=0, atol=1e-16)
+    assert np.allclose(r, 0.01 + math.log(2.0), rtol=0, atol=1e-16)
+    # tails: sigmoid(-z) ~ e^-z, softplus(-z) ~ e^-z, softplus(z) ~ z + e^-z
+    z = np.array([30.0, 50.0, 700.0])
+    assert np.allclose(oracle.sigmoid(-z), np.exp(-z), rtol=1e-12, atol=0)
+    assert np.allclose(oracle.softplus(-z), np.exp(-z), rtol=1e-12, atol=0)
+    assert np.all(np.abs(oracle.softplus(z) - (z + np.exp(-z))) <= 2 * np.spacing(z))
+    assert np.all(oracle.sigmoid(z) <= 1.0) and np.all(np.isfinite(oracle.softplus(z)))
+    # the observation noise never drops below its floor
+    assert np.all(oracle.gates(z, z, -z)[2] >= 0.01) and np.all(oracle.gates(z, z, z)[2] > z)
+
+
+def test_gate_symmetries_and_derivative():
+    z = np.random.default_rng(3).normal(0.0, 4.0, size=2000)
+    # sigmoid(z) + sigmoid(-z) = 1 and softplus(z) - softplus(-z) = z
+    assert np.max(np.abs(oracle.sigmoid(z) + oracle.sigmoid(-z) - 1.0)) < 1e-15
+    assert np.max(np.abs(oracle.softplus(z) - oracle.softplus(-z) - z)) < 1e-13
+    # e^softplus(z) = 1 + e^z
+    zm = z[np.abs(z) < 30]
+    assert np.allclose(np.exp(oracle.softplus(zm)), 1.0 + np.exp(zm), rtol=1e-13, atol=0)
+    # softplus' = sigmoid and sigmoid' = sigmoid (1 - sigmoid), by central differences
+    h = 1e-5
+    ds = (oracle.softplus(z + h) - oracle.softplus(z - h)) / (2 * h)
+    assert np.max(np.abs(ds - oracle.sigmoid(z))) < 1e-9
+    dsig = (oracle.sigmoid(z + h) - oracle.sigmoid(z - h)) / (2 * h)
+    sg = oracle.sigmoid(z)
+    assert np.max(np.abs(dsig - sg * (1 - sg))) < 1e-9
+
+
+def test_gated_forward_inverts_through_logit_and_inverse_softplus():
+    # pre-activations built with the inverse maps (logit for the decay,
+    # log(e^x - 1) for both softplus gates) reproduce the plain diagonal
+    # forward on the gated values: a swapped gate, a wrong sign or a missing
+    # r_min fails here
+    w, x = small("diagonal", T=37, seed=41)
+    a = np.asarray(x["alpha"], np.float64)
+    om = np.asarray(x["omega"], np.float64)
+    r = np.asarray(x["r"], np.float64)
+    za = np.log(a) - np.log1p(-a)
+    zw = np.log(np.expm1(om))
+    zr = np.log(np.expm1(r - 0.01))
+    ref = oracle.forward_diag(x["q"], x["k"], x["v"], a, om, r, x["c0"], w.mu)
+    got = oracle.forward_gated(x["q"], x["k"], x["v"], za, zw, zr, x["c0"], w.mu)
+    for key in ("o", "S", "p"):
+        assert np.allclose(got[key], ref[key], rtol=1e-10, atol=1e-12), key
