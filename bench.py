@@ -112,7 +112,8 @@ def kernel_source_hash() -> str:
 def upload(x, dtype, dev):
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    out = {n: torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v", "alpha", "omega", "r")}
+    names = ("q", "k", "v", "z_alpha", "z_omega", "z_r") if "z_alpha" in x else ("q", "k", "v", "alpha", "omega", "r")
+    out = {n: torch.from_numpy(x[n]).to(tdt).to(dev) for n in names}
     out["c0"] = torch.from_numpy(x["c0"]).to(dev)
     return out
 
@@ -137,18 +138,25 @@ def warm(fn, count, seconds=WARM_SECONDS):
 
 
 def time_forward(kdn, w, t, steps, warmup, algo):
-    """Returns (ms per step over the timed loop, mean single-launch ms)."""
+    """Returns (ms per step over the timed loop, mean single-launch ms).
+    Inputs holding z_alpha, z_omega, z_r run the gated forward."""
     import torch
     out = (torch.empty((w.B, w.T, w.H, w.dv), dtype=t["q"].dtype, device=t["q"].device),
            torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=t["q"].device),
            torch.empty({"diagonal": (w.B, w.H, w.dk), "grouped": (w.B, w.H, w.rgroups, w.dk)}.get(w.variant, (w.B, w.H)),
                        dtype=torch.float32, device=t["q"].device))
-    warm(lambda: kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out), warmup)
+    if "z_alpha" in t:
+        def call():
+            kdn.forward_gated(**t, mu=w.mu, algo=algo, out=out)
+    else:
+        def call():
+            kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+    warm(call, warmup)
     # whole timed loop
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
-        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+        call()
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
@@ -156,7 +164,7 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record()
-        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+        call()
         b.record()
     torch.cuda.synchronize()
     ms_launch = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -392,6 +400,11 @@ def main():
         extra["grouped"] = {"workload": wg.name, "tokens_per_s": wg.B * wg.T / (mg / 1e3), "ms_per_step": mg,
                             "hbm_frac": forward_bytes(wg) / (lg / 1e3) / 1e9 / HBM_PEAK_GBS}
         del tg
+        tz = upload(wl.gated_inputs(w), w.dtype, dev)
+        mz, lz = time_forward(kdn, w, tz, 3, 1, "auto")
+        extra["gated"] = {"workload": w.name + " (gate pre-activations)", "tokens_per_s": w.B * w.T / (mz / 1e3),
+                          "ms_per_step": mz, "hbm_frac": forward_bytes(w) / (lz / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del tz
         wlc = wl.WORKLOADS["diag_bf16_b1_t65536_h16_d128"]
         tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)
         mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "auto")

@@ -92,7 +92,11 @@ enum kdn_status {
  * call outside them returns KDN_ERR_UNSUPPORTED.  One chunked workgroup
  * handles one (batch, head) pair and 64 value columns, or 32 when that
  * leaves more than half of the GPU's 256 compute units idle (AUTO and
- * CHUNKED choose; _WIDE and _NARROW force a width). */
+ * CHUNKED choose; _WIDE and _NARROW force a width).  The chunked form divides
+ * by the product of the decays over up to 32 tokens of a chunk: it needs every
+ * alpha >= 0.07 (kdn_forward_gated: z_alpha >= -2.6), or that product
+ * underflows and the outputs overflow; the recurrent algorithm has no such
+ * bound. */
 enum kdn_algo {
     KDN_ALGO_AUTO = 0,      /* the library picks (chunked when available) */
     KDN_ALGO_RECURRENT = 1, /* token-by-token recurrence, state in registers */
@@ -134,6 +138,33 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
                      const void* omega, const void* r, const float* c0, float mu, int variant,
                      int dtype, int B, int T, int H, int dk, int dv, const float* S0,
                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
+
+/*
+ * kdn_forward_gated -- kdn_forward of the diagonal layer (variant must be
+ * KDN_DIAGONAL) with its gate step done inside the kernel (summary page,
+ * method step 1): the three gate arguments hold pre-activations, and the
+ * kernel uses
+ *
+ *   alpha = sigmoid(z_alpha)          [B,T,H,dk]  per-channel decay
+ *   omega = softplus(z_omega)         [B,T,H,dk]  per-channel process noise
+ *   r     = 0.01 + softplus(z_r)      [B,T,H]     observation noise (r_min = 0.01)
+ *
+ * in place of alpha, omega and r.  Same layouts, dtypes, alignment,
+ * algorithms, aliasing rules and results as kdn_forward_algo fed with those
+ * values (up to fp32 rounding of the gates: about 1 ulp each, and at most
+ * about 6e-8 absolute in softplus); no extra memory is read or written.  Any
+ * other variant returns KDN_ERR_UNSUPPORTED.
+ */
+int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                      const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
+                      int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
+
+/* The host-side checks of kdn_forward_gated, with no device access. */
+int kdn_validate_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                               const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
+                               int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                               const float* p0, void* o, float* S_T, float* p_T, int algo);
 
 /*
  * kdn_forward_varlen -- kdn_forward over N sequences of different lengths

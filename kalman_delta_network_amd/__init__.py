@@ -48,8 +48,8 @@ def _p_shape(var, lead, dk, dv):
     return lead
 
 # exported symbols of include/kdn.h
-SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_step", "kdn_validate_forward",
-           "kdn_validate_forward_varlen", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
+SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated", "kdn_step",
+           "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
 _lib = None
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_forward.argtypes = fwd + [P]
     lib.kdn_forward_algo.argtypes = fwd + [P, I]
     lib.kdn_validate_forward.argtypes = fwd + [I]
+    lib.kdn_forward_gated.argtypes = fwd + [P, I]
+    lib.kdn_validate_forward_gated.argtypes = fwd + [I]
     step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
     lib.kdn_step.argtypes = step + [P]
     lib.kdn_validate_step.argtypes = step
@@ -87,7 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_workspace_size.restype = ctypes.c_size_t
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
-               lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version):
+               lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version, lib.kdn_forward_gated,
+               lib.kdn_validate_forward_gated):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -181,6 +184,44 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
                               float(mu), var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
                               _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward")
+    return o, S_T, p_T
+
+
+def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, algo="auto", out=None):
+    """Diagonal KDN forward with the gate step inside the kernel: z_alpha,
+    z_omega [B,T,H,dk] and z_r [B,T,H] are pre-activations, and the kernel
+    uses alpha = sigmoid(z_alpha), omega = softplus(z_omega),
+    r = 0.01 + softplus(z_r).  Other arguments and results as ``forward``
+    with variant "diagonal"."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("z_alpha", z_alpha, (B, T, H, dk)), ("z_omega", z_omega, (B, T, H, dk)),
+                         ("z_r", z_r, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if c0 is not None:
+        _need(c0, "c0", (H,), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if p0 is not None:
+        _need(p0, "p0", (B, H, dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        p_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T, p_T = out
+        _need(o, "o", (B, T, H, dv), dt, dev)
+        _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+        _need(p_T, "p_T", (B, H, dk), torch.float32, dev)
+    st = lib.kdn_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r), _ptr(c0),
+                               float(mu), KDN_DIAGONAL, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
+                               _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
+    _check(st, "kdn_forward_gated")
     return o, S_T, p_T
 
 

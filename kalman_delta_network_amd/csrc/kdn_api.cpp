@@ -252,7 +252,7 @@ int run_forward(kdn::FwdArgs a, hipStream_t s, int algo) {
 
 extern "C" {
 
-int kdn_version(void) { return 300; }  // 0.3.0: backward pass
+int kdn_version(void) { return 400; }  // 0.4.0: gate step, chunked widths
 
 const char* kdn_status_string(int status) {
     switch (status) {
@@ -296,6 +296,32 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
     if (int64_t(B) * H == 0) return ok();
     const kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv,
                          S0, p0, o, S_T, p_T};
+    return run_forward(a, static_cast<hipStream_t>(stream), algo);
+}
+
+int kdn_validate_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                               const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
+                               int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                               const float* p0, void* o, float* S_T, float* p_T, int algo) {
+    const int st = validate_forward(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv,
+                                    S0, p0, o, S_T, p_T, algo);
+    if (st != KDN_OK) return st;
+    if (variant != KDN_DIAGONAL)
+        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    return ok();
+}
+
+int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                      const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
+                      int dtype, int B, int T, int H, int dk, int dv, const float* S0,
+                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo) {
+    const int st = kdn_validate_forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H,
+                                              dk, dv, S0, p0, o, S_T, p_T, algo);
+    if (st != KDN_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    kdn::FwdArgs a{q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv,
+                   S0, p0, o, S_T, p_T};
+    a.gates = true;
     return run_forward(a, static_cast<hipStream_t>(stream), algo);
 }
 

@@ -52,6 +52,7 @@
 // iteration is double buffered, and global inputs are prefetched into
 // registers one iteration ahead.  Roles run on all four SIMDs so the chain's
 // VALU work overlaps the MFMA work of the other roles.
+#include "kdn_gates.h"
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -305,12 +306,15 @@ __device__ __forceinline__ void chain_diag_issue(Smem<DK>& sm, const Args& a, si
 }
 
 // lane t: r_t and mu / r_t of a chunk with nvalid real tokens into LDS
-// (padding tokens: r = 1, no precision increment)
-template <int DK>
+// (padding tokens: r = 1, no precision increment).  GATE: rbits holds the
+// pre-activation z and r_t = r_min + softplus(z).
+template <int DK, bool GATE = false>
 __device__ __forceinline__ void chain_r_store(Smem<DK>& sm, int c, uint32_t rbits, int nvalid, float mu) {
     const int lane = threadIdx.x & 63;
     const bool ok = lane < nvalid;
-    const float rt = ok ? bf1(bf16_t(rbits)) : 1.f;
+    float rz = bf1(bf16_t(rbits));
+    if (GATE) rz = kGateRMin + gate_softplus(rz);
+    const float rt = ok ? rz : 1.f;
     sm.cr[c & 1][lane] = ok ? mu / rt : 0.f;
     if (lane < L) sm.rr[c % 3][lane] = rt;
 }
@@ -380,7 +384,7 @@ __device__ __forceinline__ void chain_read16(ChainIn& in, uint32_t addr) {
 // across chunks, g restarts at every chunk.  Padding tokens (t >= nvalid) act
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
-template <int DK, int BUF, int T0, int T1, bool MASK>
+template <int DK, int BUF, int T0, int T1, bool MASK, bool GATE>
 __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i, float& p, float& g, int nvalid,
                                                int gring) {
     constexpr int buf = BUF;  // compile-time, so every LDS offset below is an immediate
@@ -404,6 +408,11 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         kk[j] = __uint_as_float(in.x[j]);
         al[j] = __uint_as_float(in.x[CHAIN_SLOTS + j]);
         w[j] = __uint_as_float(in.x[2 * CHAIN_SLOTS + j]);
+        if (GATE) {
+            // the decay and process noise from their pre-activations
+            al[j] = gate_sigmoid(al[j]);
+            w[j] = gate_softplus(w[j]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
@@ -1032,9 +1041,10 @@ __device__ __forceinline__ int form_index(int w) {
 // GR (diagonal only): grouped observation noise, one r and one uncertainty
 // state p per group of DVT value columns, i.e. per column tile; the tiles of
 // a head are then independent diagonal recurrences sharing q, k, alpha, omega.
-template <int DK, int VAR, bool GR = false, int NCT = 2>
+template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
+    static_assert(!GATE || (VAR == 0 && !GR), "the gate step is the diagonal layer's");
     static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
     static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
     constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
@@ -1111,7 +1121,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         sm.Td[bb][a * 256 + tt * 16 + ss] = 0;
     }
     vm_wait<0>();  // chunk 0's tiles and r have landed
-    if (VAR == 0 && is_form && fwave == 3) chain_r_store<DK>(sm, 0, r0, min(L, a.T), a.mu);
+    if (VAR == 0 && is_form && fwave == 3) chain_r_store<DK, GATE>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
     if (wave == 0 || wave == 1) {
@@ -1134,13 +1144,13 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 const int nvalid = min(L, a.T - c * L);
                 float g = 1.f;
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false>(sm, in, i, p, g, L, c % 3);
-                    else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true>(sm, in, i, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, L, c % 3);
+                    else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true, GATE>(sm, in, i, p, g, nvalid, c % 3);
                 }
                 bar();
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false>(sm, in, i, p, g, L, c % 3);
-                    else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true>(sm, in, i, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false, GATE>(sm, in, i, p, g, L, c % 3);
+                    else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true, GATE>(sm, in, i, p, g, nvalid, c % 3);
                 }
                 bar();
             };
@@ -1293,7 +1303,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 }
                 if (VAR == 0) {
                     settle(rnext);
-                    if (f == 3) chain_r_store<DK>(sm, c + 2, rnext, min(L, a.T - (c + 2) * L), a.mu);
+                    if (f == 3) chain_r_store<DK, GATE>(sm, c + 2, rnext, min(L, a.T - (c + 2) * L), a.mu);
                 }
                 bar();
             }
@@ -1301,7 +1311,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     }
 }
 
-template <int DK, int VAR, bool GR = false, int NCT = 2>
+template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false>
 hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0) return hipSuccess;
@@ -1329,7 +1339,7 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
     const int ntile = f.dv / dvt_of<NCT>();
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR, GR, NCT>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, VAR, GR, NCT, GATE>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1359,6 +1369,13 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
     if (a.variant == 3 && a.chunk_width == dvt_of<1>()) return hipErrorNotSupported;  // groups are 64 columns
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
+    if (a.gates) {
+        // the diagonal layer with its gate step (alpha, omega, r as pre-activations)
+        if (a.variant != 0) return hipErrorNotSupported;
+        const bool nw = narrow_pays(a);
+        if (a.dk == 128) return nw ? launch_t<128, 0, false, 1, true>(a, stream) : launch_t<128, 0, false, 2, true>(a, stream);
+        return nw ? launch_t<64, 0, false, 1, true>(a, stream) : launch_t<64, 0, false, 2, true>(a, stream);
+    }
     // variant 3: diagonal with grouped observation noise (one group per tile)
     if (a.dk == 128) {
         if (a.variant == 3) return launch_t<128, 0, true>(a, stream);

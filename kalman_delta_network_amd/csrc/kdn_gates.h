@@ -1,0 +1,34 @@
+// Gate step of the diagonal KDN layer, evaluated inside the forward kernels
+// on pre-activations ("Kalman Delta Networks: Uncertainty-aware Associative
+// Memory", summary page, method step 1): per-channel decay alpha = sigmoid(z),
+// per-channel process noise omega = softplus(z), per-token observation noise
+// r = r_min + softplus(z) with r_min = 0.01.
+//
+// fp32 on the hardware exp2 / log2 / reciprocal (v_exp_f32, v_log_f32,
+// v_rcp_f32, about 1 ulp each):
+//  - sigmoid(z) = 1 / (1 + 2^(-z log2 e)); for z < -88 the power is +inf and
+//    the result 0 (true value below 1e-38);
+//  - softplus(z) = max(z, 0) + ln 2 * log2(1 + 2^(-|z| log2 e)); the power lies
+//    in (0, 1], so nothing overflows.  Rounding 1 + e to fp32 costs at most
+//    about 6e-8 absolute (for z < -17 the result is max(z, 0) = 0 where the
+//    true value is below 4e-8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kdn {
+
+constexpr float kGateRMin = 0.01f;
+constexpr float kLog2E = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float gate_sigmoid(float z) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2E * z));
+}
+
+__device__ __forceinline__ float gate_softplus(float z) {
+    const float e = __builtin_amdgcn_exp2f(-kLog2E * fabsf(z));
+    return fmaf(kLn2, __builtin_amdgcn_logf(1.f + e), fmaxf(z, 0.f));
+}
+
+}  // namespace kdn

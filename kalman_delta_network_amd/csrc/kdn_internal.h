@@ -37,6 +37,9 @@ struct FwdArgs {
     // chunked forward: value columns per workgroup (64 or 32), 0 = chosen by
     // occupancy
     int chunk_width = 0;
+    // diagonal variant: alpha, omega and r hold the gate pre-activations;
+    // the kernels apply sigmoid, softplus and r_min + softplus themselves
+    bool gates = false;
 };
 
 // One backward call, after host validation.  Pointers are device pointers;

@@ -27,6 +27,7 @@
 // The decode step is this kernel with T = 1 and the state updated in place:
 // a barrier after the initial state loads makes every wave read p before any
 // wave writes it back.
+#include "kdn_gates.h"
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -78,7 +79,7 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                      const Tin* __restrict__ omega, const Tin* __restrict__ r,
                      const float* __restrict__ c0, float mu, int T, int H, const float* S0,
                      const float* p0, Tin* __restrict__ o, float* S_T, float* p_T,
-                     const int* __restrict__ cu, const int* __restrict__ ord, int nseq) {
+                     const int* __restrict__ cu, const int* __restrict__ ord, int nseq, int gates) {
     constexpr bool ISO = VAR != 0;       // one uncertainty scalar per head
     constexpr bool CHAN = VAR != 1;      // one decay per key channel
     constexpr int NW = DV / 32;   // waves per workgroup
@@ -138,7 +139,9 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
     const float inv_dk = 1.0f / float(DK);
     for (int t = 0; t < len; ++t) {
         const size_t tok = (tok0 + size_t(t)) * size_t(H) + size_t(h);
-        const float rt = to_f32(r[GR ? tok * NG + grp : tok]);
+        float rt = to_f32(r[GR ? tok * NG + grp : tok]);
+        // gates (diagonal layer): alpha, omega and r arrive as pre-activations
+        if (!ISO && gates) rt = kGateRMin + gate_softplus(rt);
         float kk[CPL], qq[CPL], aa[CPL], kap[CPL];
         float mq;  // kappa^T q
 #pragma unroll
@@ -174,7 +177,11 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 aa[c] = to_f32(alpha[tok * DK + lane + 64 * c]);
-                const float w = to_f32(omega[tok * DK + lane + 64 * c]);
+                float w = to_f32(omega[tok * DK + lane + 64 * c]);
+                if (gates) {
+                    aa[c] = gate_sigmoid(aa[c]);
+                    w = gate_softplus(w);
+                }
                 ph[c] = aa[c] * aa[c] * p[c] + w;
                 s += ph[c] * kk[c] * kk[c];
                 kq += ph[c] * kk[c] * qq[c];
@@ -254,7 +261,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
                        static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                        static_cast<const Tin*>(a.alpha), static_cast<const Tin*>(a.omega),
                        static_cast<const Tin*>(a.r), a.c0, a.mu, a.T, a.H, a.S0, a.p0,
-                       static_cast<Tin*>(a.o), a.S_T, a.p_T, a.cu_seqlens, a.seq_order, a.B);
+                       static_cast<Tin*>(a.o), a.S_T, a.p_T, a.cu_seqlens, a.seq_order, a.B,
+                       a.gates ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(kdn.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kdn_version() == 300
+    assert lib.kdn_version() == 400
 
 
 def test_status_strings(lib):
@@ -364,3 +364,25 @@ def test_grouped_noise_variant(lib):
     a = fwd_args(f, variant=3, dk=64, dv=128, B=1, T=8, H=1)
     r_end = ctypes.c_void_p(a["r"].value + 8 * 2)  # bf16, 8 tokens x 1 group
     assert call_validate(lib, dict(a, o=r_end)) == kdn.KDN_ERR_ALIAS
+
+
+def call_validate_gated(lib, a):
+    return lib.kdn_validate_forward_gated(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["c0"],
+                                          a["mu"], a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"],
+                                          a["dv"], a["S0"], a["p0"], a["o"], a["S_T"], a["p_T"], a["algo"])
+
+
+def test_validate_gated_forward(lib):
+    # the gate step belongs to the diagonal layer: every other variant is refused,
+    # the rest of the checks are those of the plain forward
+    f = Fake()
+    for dtype in (0, 1):
+        for algo in (0, 1, 2, 3, 4):
+            assert call_validate_gated(lib, fwd_args(f, dtype=dtype, algo=algo)) == 0
+    for variant in (1, 2, 3):
+        assert call_validate_gated(lib, fwd_args(f, variant=variant)) == kdn.KDN_ERR_UNSUPPORTED
+        assert b"diagonal" in lib.kdn_last_error()
+    assert call_validate_gated(lib, fwd_args(f, q=None)) == kdn.KDN_ERR_NULL
+    assert call_validate_gated(lib, fwd_args(f, dk=96)) == kdn.KDN_ERR_UNSUPPORTED
+    assert call_validate_gated(lib, fwd_args(f, mu=-1.0)) == kdn.KDN_ERR_VALUE
+    assert call_validate_gated(lib, fwd_args(f, B=0, q=None, o=None, S_T=None)) == 0

@@ -1,0 +1,127 @@
+"""GPU parity of the gated forward (kdn_forward_gated: the diagonal layer with
+its gate step, alpha = sigmoid(z), omega = softplus(z), r = 0.01 + softplus(z),
+done inside the kernels) against oracle.forward_gated on the same
+pre-activations, through the C ABI.  Tolerance: max relative error 1e-4
+(fp32 inputs) or 2e-2 (bf16 inputs, fp32 state), per output tensor."""
+import numpy as np
+import pytest
+
+import oracle
+from kalman_delta_network_amd import workloads as wl
+from kdn_testutil import rel_err, sample_pairs, tol
+
+pytestmark = pytest.mark.gpu
+
+GATED = ("q", "k", "v", "z_alpha", "z_omega", "z_r")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    import kalman_delta_network_amd as kdn
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kdn.load_library()
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dtype, dev):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(tdt).to(dev) for n in GATED}
+    out["c0"] = torch.from_numpy(np.ascontiguousarray(x["c0"], np.float32)).to(dev)
+    return out
+
+
+def run(dev, w, x, algo, S0=None, p0=None):
+    import torch
+    import kalman_delta_network_amd as kdn
+    f32 = (lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float32)).to(dev))
+    o, S, p = kdn.forward_gated(**to_dev(x, w.dtype, dev), mu=w.mu, S0=f32(S0), p0=f32(p0), algo=algo)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()
+
+
+def oracle_gated(w, x, S0=None, p0=None):
+    return oracle.forward_gated(**{n: x[n] for n in GATED}, c0=x["c0"], mu=w.mu, S0=S0, p0=p0)
+
+
+def check(name, got, ref, dtype):
+    errs = {k: rel_err(g, ref[k]) for k, g in zip(("o", "S", "p"), got)}
+    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= tol(dtype), (name, k, e)
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked_wide", "chunked_narrow"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("T", [1, 63, 65, 200])
+def test_gated_forward(dev, algo, dtype, dk, dv, T):
+    if dtype == "f32" and algo != "recurrent":
+        pytest.skip("the chunked kernel takes bf16 inputs")
+    # omega_loc 0: softplus near its bend, z_alpha around 2 (decay ~0.88)
+    w = wl.Workload("gated", "diagonal", dtype, 2, T, 3, dk, dv, float(dk), "uniform", 1500 + T + dk + dv,
+                    omega_loc=0.0 if T % 2 else -4.0)
+    x = wl.gated_inputs(w)
+    assert x["z_alpha"].shape == (2, T, 3, dk) and x["z_r"].shape == (2, T, 3)
+    check(f"gated/{algo}/{dtype}/dk{dk}/dv{dv}/T{T}", run(dev, w, x, algo), oracle_gated(w, x), dtype)
+
+
+def test_gated_extreme_pre_activations(dev):
+    # pre-activations far in the tails: softplus at 0 and at z, r at its floor
+    # 0.01, the decay saturated at 1; the decay's low end stays at the chunked
+    # kernel's bound (alpha >= 0.07, i.e. z_alpha >= -2.6)
+    w = wl.Workload("gated_ext", "diagonal", "bf16", 2, 97, 2, 128, 128, 128.0, "uniform", 1601)
+    x = wl.gated_inputs(w)
+    rng = np.random.default_rng(5)
+    for n, s in (("z_alpha", 30.0), ("z_omega", 30.0), ("z_r", 30.0)):
+        z = rng.normal(0.0, s, size=x[n].shape).astype(np.float32)
+        if n == "z_alpha":
+            z = np.maximum(z, np.float32(-2.5))
+        x[n] = wl.round_bf16(z)
+    for algo in ("recurrent", "chunked"):
+        check(f"gated/extreme/{algo}", run(dev, w, x, algo), oracle_gated(w, x), "bf16")
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_gated_with_initial_state(dev, algo):
+    w = wl.Workload("gated_init", "diagonal", "bf16", 2, 150, 2, 128, 128, 128.0, "uniform", 1602, omega_loc=-1.0)
+    x = wl.gated_inputs(w)
+    st = wl.decode_state(w)
+    check(f"gated/init/{algo}", run(dev, w, x, algo, S0=st["S0"], p0=st["p0"]),
+          oracle_gated(w, x, S0=st["S0"], p0=st["p0"]), "bf16")
+
+
+def test_gated_rejects_other_variants(dev):
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("gated_var", "diagonal", "bf16", 1, 8, 1, 128, 128, 128.0, "uniform", 1603)
+    t = to_dev(wl.gated_inputs(w), "bf16", dev)
+    o = torch.empty((1, 8, 1, 128), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((1, 1, 128, 128), dtype=torch.float32, device=dev)
+    p = torch.empty((1, 1), dtype=torch.float32, device=dev)
+    lib = kdn.load_library()
+    st = lib.kdn_forward_gated(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["z_alpha"].data_ptr(),
+                               t["z_omega"].data_ptr(), t["z_r"].data_ptr(), t["c0"].data_ptr(), 128.0,
+                               kdn.KDN_ISOTROPIC, 1, 1, 8, 1, 128, 128, None, None, o.data_ptr(), S.data_ptr(),
+                               p.data_ptr(), None, 0)
+    assert st == kdn.KDN_ERR_UNSUPPORTED
+
+
+def test_gated_full_size_sampled_heads(dev):
+    # the main forward's shape (B=8, T=4096, H=16, d=128, bf16) through the gates,
+    # in the launch configuration the benchmark times; oracle on sampled heads
+    w = wl.WORKLOADS["diag_bf16_b8_t4096_h16_d128"]
+    x = wl.gated_inputs(w)
+    o, S, p = run(dev, w, x, "auto")
+    worst = {"o": 0.0, "S": 0.0, "p": 0.0}
+    pairs = sample_pairs(w.B, w.H, 4, seed=w.seed)
+    for b, h in pairs:
+        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in GATED}
+        rr = oracle.forward_gated(**sub, c0=x["c0"][h:h + 1], mu=w.mu)
+        got = (o[b:b + 1, :, h:h + 1], S[b:b + 1, h:h + 1], p[b:b + 1, h:h + 1])
+        for key, g in zip(("o", "S", "p"), got):
+            worst[key] = max(worst[key], rel_err(g, rr[key]))
+    print(f"gated full size pairs={pairs}: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    for k, e in worst.items():
+        assert e <= tol("bf16"), (k, e)
