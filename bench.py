@@ -171,8 +171,9 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     return ms_step, ms_launch
 
 
-def bench_decode(kdn, w, dev, steps_cap=None):
-    """Time w.decode_steps consecutive kdn_step calls (tokens pre-uploaded)."""
+def bench_decode(kdn, w, dev, steps_cap=None, gated=False):
+    """Time w.decode_steps consecutive kdn_step calls (tokens pre-uploaded);
+    ``gated``: kdn_step_gated on gate pre-activations."""
     import torch
     from kalman_delta_network_amd import workloads as wl
     nsteps = w.decode_steps if steps_cap is None else min(steps_cap, w.decode_steps)
@@ -181,16 +182,23 @@ def bench_decode(kdn, w, dev, steps_cap=None):
     p = torch.from_numpy(st["p0"]).to(dev)
     toks = []
     for s in range(nsteps):
-        toks.append(upload(dict(wl.decode_tokens(w, s), c0=np.ones(1, np.float32)), w.dtype, dev))
+        tok = wl.gated_decode_tokens(w, s) if gated else wl.decode_tokens(w, s)
+        toks.append(upload(dict(tok, c0=np.ones(1, np.float32)), w.dtype, dev))
     o = torch.empty((w.B, w.H, w.dv), dtype=toks[0]["q"].dtype, device=dev)
-    names = ("q", "k", "v", "alpha", "omega", "r")
+    if gated:
+        names = ("q", "k", "v", "z_alpha", "z_omega", "z_r")
+        step = lambda tk, S_, p_: kdn.step_gated(**{n: tk[n] for n in names}, mu=w.mu, S=S_, p=p_, o=o)
+    else:
+        names = ("q", "k", "v", "alpha", "omega", "r")
+        step = lambda tk, S_, p_: kdn.step(**{n: tk[n] for n in names}, mu=w.mu, S=S_, p=p_, variant=w.variant,
+                                           o=o)
     S2, p2 = S.clone(), p.clone()  # warm-up on a scratch copy of the state
-    warm(lambda: kdn.step(**{n: toks[0][n] for n in names}, mu=w.mu, S=S2, p=p2, variant=w.variant, o=o), 3)
+    warm(lambda: step(toks[0], S2, p2), 3)
     del S2, p2
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for s in range(nsteps):
-        kdn.step(**{n: toks[s][n] for n in names}, mu=w.mu, S=S, p=p, variant=w.variant, o=o)
+        step(toks[s], S, p)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -387,6 +395,8 @@ def main():
         del ti
         extra["decode"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
                                        args.decode_steps)
+        extra["decode_gated"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
+                                             min(256, args.decode_steps or 256), gated=True)
         extra["varlen"] = bench_varlen(kdn, dev, max(3, args.steps // 2), args.algo)
         wc = wl.WORKLOADS["isoch_bf16_b8_t4096_h16_d128"]
         tc = upload(wl.forward_inputs(wc), wc.dtype, dev)

@@ -160,6 +160,23 @@ int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z
                       int dtype, int B, int T, int H, int dk, int dv, const float* S0,
                       const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
+/* kdn_forward_varlen with the gate step of kdn_forward_gated: z_alpha,
+ * z_omega [total,H,dk] and z_r [total,H] are pre-activations; KDN_DIAGONAL
+ * only.  Same layouts, checks and results as kdn_forward_varlen fed with the
+ * gated values. */
+int kdn_forward_varlen_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                             const void* z_omega, const void* z_r, const int* cu_seqlens, const int* order,
+                             const float* c0, float mu, int variant, int dtype, int N, int total, int H, int dk,
+                             int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                             void* stream, int algo);
+
+/* kdn_step with the gate step of kdn_forward_gated: z_alpha, z_omega
+ * [N,H,dk] and z_r [N,H] are pre-activations; KDN_DIAGONAL only.  S and p
+ * are updated in place as by kdn_step. */
+int kdn_step_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
+                   const void* z_r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
+                   float* S, float* p, void* o, void* stream);
+
 /* The host-side checks of kdn_forward_gated, with no device access. */
 int kdn_validate_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
                                const void* z_omega, const void* z_r, const float* c0, float mu, int variant,

@@ -48,7 +48,8 @@ def _p_shape(var, lead, dk, dv):
     return lead
 
 # exported symbols of include/kdn.h
-SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated", "kdn_step",
+SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
+           "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_validate_step.argtypes = step
     varlen = [P, P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, P, P, P, P, P]
     lib.kdn_forward_varlen.argtypes = varlen + [P, I]
+    lib.kdn_forward_varlen_gated.argtypes = varlen + [P, I]
+    lib.kdn_step_gated.argtypes = step + [P]
     lib.kdn_validate_forward_varlen.argtypes = varlen + [I]
     bwd = fwd[:17] + [P] * 12
     lib.kdn_backward.argtypes = bwd + [P, ctypes.c_size_t, P]
@@ -90,7 +93,7 @@ def load_library(path: str = LIB_PATH):
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
                lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version, lib.kdn_forward_gated,
-               lib.kdn_validate_forward_gated):
+               lib.kdn_validate_forward_gated, lib.kdn_forward_varlen_gated, lib.kdn_step_gated):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -309,6 +312,65 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
                       _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
     _check(st, "kdn_step")
     return o
+
+
+def step_gated(q, k, v, z_alpha, z_omega, z_r, mu, S, p, o=None):
+    """One decode step of the diagonal layer from gate pre-activations
+    z_alpha, z_omega [N,H,dk] and z_r [N,H] (the kernel applies sigmoid,
+    softplus and 0.01 + softplus); S [N,H,dk,dv] and p [N,H,dk] float32 are
+    updated in place.  Returns o [N,H,dv]."""
+    torch = _torch()
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
+                         ("z_alpha", z_alpha, (N, H, dk)), ("z_omega", z_omega, (N, H, dk)), ("z_r", z_r, (N, H))):
+        _need(t, name, shp, dt, dev)
+    _need(S, "S", (N, H, dk, dv), torch.float32, dev)
+    _need(p, "p", (N, H, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _need(o, "o", (N, H, dv), dt, dev)
+    st = lib.kdn_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r), float(mu),
+                            KDN_DIAGONAL, _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
+    _check(st, "kdn_step_gated")
+    return o
+
+
+def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, S0=None, p0=None, algo="auto",
+                         order=None):
+    """``forward_varlen`` of the diagonal layer from gate pre-activations
+    z_alpha, z_omega [total,H,dk] and z_r [total,H]."""
+    torch = _torch()
+    lib = load_library()
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    N = int(cu_seqlens.shape[0]) - 1
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
+                         ("z_alpha", z_alpha, (total, H, dk)), ("z_omega", z_omega, (total, H, dk)),
+                         ("z_r", z_r, (total, H))):
+        _need(t, name, shp, dt, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if order is not None:
+        _need(order, "order", (N,), torch.int32, dev)
+    if c0 is not None:
+        _need(c0, "c0", (H,), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if p0 is not None:
+        _need(p0, "p0", (N, H, dk), torch.float32, dev)
+    o = torch.empty((total, H, dv), dtype=dt, device=dev)
+    S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    p_T = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    st = lib.kdn_forward_varlen_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r),
+                                      _ptr(cu_seqlens), _ptr(order), _ptr(c0), float(mu), KDN_DIAGONAL,
+                                      _dtype_code(q), N, total, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(o),
+                                      _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
+    _check(st, "kdn_forward_varlen_gated")
+    return o, S_T, p_T
 
 
 def backward_workspace_size(B, T, H, dk, dv) -> int:

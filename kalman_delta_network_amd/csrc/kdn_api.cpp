@@ -353,6 +353,40 @@ int kdn_forward_varlen(const void* q, const void* k, const void* v, const void* 
     return run_forward(a, static_cast<hipStream_t>(stream), algo);
 }
 
+int kdn_forward_varlen_gated(const void* q, const void* k, const void* v, const void* z_alpha,
+                             const void* z_omega, const void* z_r, const int* cu_seqlens, const int* order,
+                             const float* c0, float mu, int variant, int dtype, int N, int total, int H, int dk,
+                             int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                             void* stream, int algo) {
+    const int st = validate_forward_varlen(q, k, v, z_alpha, z_omega, z_r, cu_seqlens, order, c0, mu, variant,
+                                           dtype, N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
+    if (st != KDN_OK) return st;
+    if (variant != KDN_DIAGONAL)
+        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    if (int64_t(N) * H == 0) return ok();
+    kdn::FwdArgs a{q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, N, total, H, dk, dv,
+                   S0, p0, o, S_T, p_T};
+    a.cu_seqlens = cu_seqlens;
+    a.seq_order = order;
+    a.gates = true;
+    return run_forward(a, static_cast<hipStream_t>(stream), algo);
+}
+
+int kdn_step_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
+                   const void* z_r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
+                   float* S, float* p, void* o, void* stream) {
+    const int st = validate_step(q, k, v, z_alpha, z_omega, z_r, mu, variant, dtype, N, H, dk, dv, S, p, o);
+    if (st != KDN_OK) return st;
+    if (variant != KDN_DIAGONAL)
+        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    if (int64_t(N) * H == 0) return ok();
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    kdn::FwdArgs a{q, k, v, z_alpha, z_omega, z_r, nullptr, mu, variant, dtype, N, 1, H, dk, dv,
+                   S, p, o, S, p};
+    a.gates = true;
+    return hip_status(kdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "gated decode step");
+}
+
 int kdn_forward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
                 const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
                 int H, int dk, int dv, const float* S0, const float* p0, void* o, float* S_T,

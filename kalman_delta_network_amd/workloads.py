@@ -212,6 +212,25 @@ def decode_tokens(w: Workload, step: int) -> dict:
     return _draw_tokens(rng, w, (w.B, w.H))
 
 
+def gated_decode_tokens(w: Workload, step: int) -> dict:
+    """The token of decode step ``step`` for all N = w.B sequences of the
+    diagonal layer, with gate pre-activations: q, k, z_alpha, z_omega
+    [N,H,dk], v [N,H,dv], z_r [N,H] (distributions as ``gated_inputs``)."""
+    rng = np.random.default_rng([w.seed, 0x71, step])
+    lead = (w.B, w.H)
+    out = {
+        "q": _l2norm(_normal(rng, lead + (w.dk,))),
+        "k": _l2norm(_normal(rng, lead + (w.dk,))),
+        "v": _normal(rng, lead + (w.dv,)),
+        "z_alpha": _normal(rng, lead + (w.dk,), w.alpha_loc, 0.5),
+        "z_omega": _normal(rng, lead + (w.dk,), w.omega_loc, 1.0),
+        "z_r": _normal(rng, lead),
+    }
+    if w.dtype == "bf16":
+        out = {key: round_bf16(val) for key, val in out.items()}
+    return out
+
+
 def backward_cotangents(w: Workload, with_state: bool = True) -> dict:
     """Cotangents of one backward call: dO ~ N(0, 1) [B,T,H,dv] (rounded to
     bf16 for bf16 workloads), and with ``with_state`` dS_T ~ N(0, 0.1)

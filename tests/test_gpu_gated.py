@@ -125,3 +125,47 @@ def test_gated_full_size_sampled_heads(dev):
     print(f"gated full size pairs={pairs}: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
     for k, e in worst.items():
         assert e <= tol("bf16"), (k, e)
+
+
+def test_gated_decode_steps(dev):
+    # four consecutive decode steps from pre-activations; token s of each
+    # sequence is position s of a gated input draw
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("gated_dec", "diagonal", "bf16", 8, 4, 4, 128, 128, 128.0, "uniform", 1604, omega_loc=-1.0)
+    x = wl.gated_inputs(w)
+    st = wl.decode_state(w)
+    S = torch.from_numpy(st["S0"]).to(dev)
+    p = torch.from_numpy(st["p0"]).to(dev)
+    Sr, pr = st["S0"].astype(np.float64), st["p0"].astype(np.float64)
+    for s in range(w.T):
+        tok = {n: np.ascontiguousarray(x[n][:, s]) for n in GATED}
+        t = {n: torch.from_numpy(tok[n]).to(torch.bfloat16).to(dev) for n in GATED}
+        o = kdn.step_gated(**t, mu=w.mu, S=S, p=p)
+        a, om, r = oracle.gates(tok["z_alpha"], tok["z_omega"], tok["z_r"])
+        ref = oracle.step_diag(tok["q"], tok["k"], tok["v"], a, om, r, mu=w.mu, S=Sr, p=pr)
+        Sr, pr = ref["S"], ref["p"]
+        torch.cuda.synchronize()
+        check(f"gated/decode/step{s}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()),
+              {"o": ref["o"], "S": Sr, "p": pr}, "bf16")
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+def test_gated_packed_batch(dev, algo):
+    import torch
+    import kalman_delta_network_amd as kdn
+    lengths = [1, 33, 0, 90, 64, 129]
+    total = sum(lengths)
+    w = wl.Workload("gated_var", "diagonal", "bf16", 1, total, 3, 128, 128, 128.0, "uniform", 1605, omega_loc=-1.0)
+    x = {n: (v[0] if n != "c0" else v) for n, v in wl.gated_inputs(w).items()}  # [total, H, *]
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev) for n in GATED}
+    o, S, p = kdn.forward_varlen_gated(**t, c0=torch.from_numpy(x["c0"]).to(dev),
+                                       cu_seqlens=torch.from_numpy(cu).to(dev), mu=w.mu, algo=algo,
+                                       order=torch.from_numpy(kdn.longest_first(cu)).to(dev))
+    torch.cuda.synchronize()
+    a, om, r = oracle.gates(x["z_alpha"], x["z_omega"], x["z_r"])
+    ref = oracle.forward_varlen(x["q"], x["k"], x["v"], a, om, r, c0=x["c0"], mu=w.mu, cu_seqlens=cu,
+                                variant="diagonal")
+    check(f"gated/varlen/{algo}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")
