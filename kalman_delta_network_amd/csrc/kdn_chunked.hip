@@ -385,8 +385,8 @@ __device__ __forceinline__ void chain_read16(ChainIn& in, uint32_t addr) {
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
 template <int DK, int BUF, int T0, int T1, bool MASK, bool GATE>
-__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i, float& p, float& g, int nvalid,
-                                               int gring) {
+__device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i, float& p, float& g, float& gi,
+                                               int nvalid, int gring) {
     constexpr int buf = BUF;  // compile-time, so every LDS offset below is an immediate
     constexpr int NTOK = T1 - T0;
     static_assert(NTOK == CHAIN_SLOTS, "one 16-token chain segment");
@@ -402,6 +402,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
     for (int j = 0; j < NTOK; ++j) cv[j] = sm.cr[buf][T0 + j];  // same address on every lane: broadcast
     chain_read16<DK, BUF, T0>(in, uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)&sm.RK[0][i])));
     float kk[NTOK], al[NTOK], w[NTOK], khv[NTOK], gv[NTOK];
+    float ez[NTOK];                        // GATE: e^-z of the decay's pre-activation
     uint32_t khp[NTOK / 2], gp[NTOK / 2];  // bf16 pairs of consecutive tokens
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) {
@@ -409,8 +410,10 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         al[j] = __uint_as_float(in.x[CHAIN_SLOTS + j]);
         w[j] = __uint_as_float(in.x[2 * CHAIN_SLOTS + j]);
         if (GATE) {
-            // the decay and process noise from their pre-activations
-            al[j] = gate_sigmoid(al[j]);
+            // the decay alpha = 1 / (1 + e^-z) and the process noise from
+            // their pre-activations; e^-z is kept for 1 / g below
+            ez[j] = __builtin_amdgcn_exp2f(-kLog2E * al[j]);
+            al[j] = __builtin_amdgcn_rcpf(1.f + ez[j]);
             w[j] = gate_softplus(w[j]);
         }
     }
@@ -422,6 +425,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
             kk[j] = ok ? kk[j] : 0.f;
             al[j] = ok ? al[j] : 1.f;
             w[j] = ok ? w[j] : 0.f;
+            if (GATE) ez[j] = ok ? ez[j] : 0.f;
         }
         const float asq = al[j] * al[j];
         // the fewest instructions, rather than the shortest dependent path,
@@ -439,7 +443,12 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         // 8 positions of group P / 8 hold tokens 4 (P / 8) + 0..3 and
         // 16 + 4 (P / 8) + 0..3, i.e. a 16-token segment fills one half of
         // each of the four groups.
-        khv[j] = kph * __builtin_amdgcn_rcpf(g);
+        if (GATE) {
+            gi = fmaf(gi, ez[j], gi);  // 1 / g as the product of the (1 + e^-z): no reciprocal
+            khv[j] = kph * gi;
+        } else {
+            khv[j] = kph * __builtin_amdgcn_rcpf(g);
+        }
         gv[j] = g;
         if (j & 1) {
             khp[j / 2] = pack2_opaque(khv[j - 1], khv[j]);
@@ -1142,15 +1151,15 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             auto step = [&](auto bufc, int c) {
                 constexpr int BUF = decltype(bufc)::value;
                 const int nvalid = min(L, a.T - c * L);
-                float g = 1.f;
+                float g = 1.f, gi = 1.f;
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, L, c % 3);
-                    else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true, GATE>(sm, in, i, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
+                    else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true, GATE>(sm, in, i, p, g, gi, nvalid, c % 3);
                 }
                 bar();
                 if (active && c < nchunks) {
-                    if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false, GATE>(sm, in, i, p, g, L, c % 3);
-                    else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true, GATE>(sm, in, i, p, g, nvalid, c % 3);
+                    if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
+                    else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true, GATE>(sm, in, i, p, g, gi, nvalid, c % 3);
                 }
                 bar();
             };
