@@ -147,7 +147,7 @@ def time_forward(kdn, w, t, steps, warmup, algo):
                        dtype=torch.float32, device=t["q"].device))
     if "z_alpha" in t:
         def call():
-            kdn.forward_gated(**t, mu=w.mu, algo=algo, out=out)
+            kdn.forward_gated(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
     else:
         def call():
             kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
@@ -414,6 +414,13 @@ def main():
         mz, lz = time_forward(kdn, w, tz, 3, 1, "auto")
         extra["gated"] = {"workload": w.name + " (gate pre-activations)", "tokens_per_s": w.B * w.T / (mz / 1e3),
                           "ms_per_step": mz, "hbm_frac": forward_bytes(w) / (lz / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del tz
+        wiz = wl.WORKLOADS["iso_bf16_b8_t4096_h16_d128"]
+        tz = upload(wl.gated_inputs(wiz), wiz.dtype, dev)
+        mz, lz = time_forward(kdn, wiz, tz, 3, 1, "auto")
+        extra["gated_isotropic"] = {"workload": wiz.name + " (gate pre-activations)",
+                                    "tokens_per_s": wiz.B * wiz.T / (mz / 1e3), "ms_per_step": mz,
+                                    "hbm_frac": forward_bytes(wiz) / (lz / 1e3) / 1e9 / HBM_PEAK_GBS}
         del tz
         wlc = wl.WORKLOADS["diag_bf16_b1_t65536_h16_d128"]
         tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)

@@ -140,20 +140,21 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
 /*
- * kdn_forward_gated -- kdn_forward of the diagonal layer (variant must be
- * KDN_DIAGONAL) with its gate step done inside the kernel (summary page,
- * method step 1): the three gate arguments hold pre-activations, and the
- * kernel uses
+ * kdn_forward_gated -- kdn_forward with the gate step done inside the kernel
+ * (summary page, method step 1, and its core-method paragraph: decay, process
+ * noise and observation noise come from the token through sigmoid / softplus):
+ * the three gate arguments hold pre-activations, and the kernel uses
  *
- *   alpha = sigmoid(z_alpha)          [B,T,H,dk]  per-channel decay
- *   omega = softplus(z_omega)         [B,T,H,dk]  per-channel process noise
- *   r     = 0.01 + softplus(z_r)      [B,T,H]     observation noise (r_min = 0.01)
+ *   alpha = sigmoid(z_alpha)          decay
+ *   omega = softplus(z_omega)         process noise
+ *   r     = 0.01 + softplus(z_r)      observation noise (r_min = 0.01)
  *
- * in place of alpha, omega and r.  Same layouts, dtypes, alignment,
+ * in place of alpha, omega and r, in the layouts kdn_forward gives them for
+ * the variant (KDN_DIAGONAL, KDN_ISOTROPIC or KDN_ISOTROPIC_CHANNEL;
+ * KDN_DIAGONAL_GROUPED returns KDN_ERR_UNSUPPORTED).  Same dtypes, alignment,
  * algorithms, aliasing rules and results as kdn_forward_algo fed with those
  * values (up to fp32 rounding of the gates: about 1 ulp each, and at most
- * about 6e-8 absolute in softplus); no extra memory is read or written.  Any
- * other variant returns KDN_ERR_UNSUPPORTED.
+ * about 6e-8 absolute in softplus); no extra memory is read or written.
  */
 int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
                       const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
@@ -161,18 +162,18 @@ int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z
                       const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
 /* kdn_forward_varlen with the gate step of kdn_forward_gated: z_alpha,
- * z_omega [total,H,dk] and z_r [total,H] are pre-activations; KDN_DIAGONAL
- * only.  Same layouts, checks and results as kdn_forward_varlen fed with the
- * gated values. */
+ * z_omega and z_r are pre-activations in the layouts of alpha, omega and r
+ * (not KDN_DIAGONAL_GROUPED).  Same checks and results as kdn_forward_varlen
+ * fed with the gated values. */
 int kdn_forward_varlen_gated(const void* q, const void* k, const void* v, const void* z_alpha,
                              const void* z_omega, const void* z_r, const int* cu_seqlens, const int* order,
                              const float* c0, float mu, int variant, int dtype, int N, int total, int H, int dk,
                              int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
                              void* stream, int algo);
 
-/* kdn_step with the gate step of kdn_forward_gated: z_alpha, z_omega
- * [N,H,dk] and z_r [N,H] are pre-activations; KDN_DIAGONAL only.  S and p
- * are updated in place as by kdn_step. */
+/* kdn_step with the gate step of kdn_forward_gated: z_alpha, z_omega and
+ * z_r are pre-activations in the layouts of alpha, omega and r (not
+ * KDN_DIAGONAL_GROUPED).  S and p are updated in place as by kdn_step. */
 int kdn_step_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
                    const void* z_r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
                    float* S, float* p, void* o, void* stream);

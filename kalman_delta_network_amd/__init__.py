@@ -190,39 +190,42 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
     return o, S_T, p_T
 
 
-def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, algo="auto", out=None):
-    """Diagonal KDN forward with the gate step inside the kernel: z_alpha,
-    z_omega [B,T,H,dk] and z_r [B,T,H] are pre-activations, and the kernel
-    uses alpha = sigmoid(z_alpha), omega = softplus(z_omega),
-    r = 0.01 + softplus(z_r).  Other arguments and results as ``forward``
-    with variant "diagonal"."""
+def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant="diagonal", S0=None, p0=None, algo="auto",
+                  out=None):
+    """KDN forward with the gate step inside the kernel: z_alpha, z_omega and
+    z_r are pre-activations in the layouts ``forward`` gives alpha, omega and
+    r for the variant ("diagonal", "isotropic" or "isochannel"), and the
+    kernel uses alpha = sigmoid(z_alpha), omega = softplus(z_omega),
+    r = 0.01 + softplus(z_r).  Other arguments and results as ``forward``."""
     torch = _torch()
     lib = load_library()
+    var = VARIANTS[variant]
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     dt = q.dtype
+    ashape, wshape = _gate_shapes(var, (B, T, H), dk)
+    pshape = _p_shape(var, (B, H), dk, dv)
     for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                         ("z_alpha", z_alpha, (B, T, H, dk)), ("z_omega", z_omega, (B, T, H, dk)),
-                         ("z_r", z_r, (B, T, H))):
+                         ("z_alpha", z_alpha, ashape), ("z_omega", z_omega, wshape), ("z_r", z_r, (B, T, H))):
         _need(t, name, shp, dt, dev)
     if c0 is not None:
         _need(c0, "c0", (H,), torch.float32, dev)
     if S0 is not None:
         _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     if p0 is not None:
-        _need(p0, "p0", (B, H, dk), torch.float32, dev)
+        _need(p0, "p0", pshape, torch.float32, dev)
     if out is None:
         o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-        p_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        p_T = torch.empty(pshape, dtype=torch.float32, device=dev)
     else:
         o, S_T, p_T = out
         _need(o, "o", (B, T, H, dv), dt, dev)
         _need(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
-        _need(p_T, "p_T", (B, H, dk), torch.float32, dev)
+        _need(p_T, "p_T", pshape, torch.float32, dev)
     st = lib.kdn_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r), _ptr(c0),
-                               float(mu), KDN_DIAGONAL, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
+                               float(mu), var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
                                _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward_gated")
     return o, S_T, p_T
@@ -314,44 +317,48 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
     return o
 
 
-def step_gated(q, k, v, z_alpha, z_omega, z_r, mu, S, p, o=None):
-    """One decode step of the diagonal layer from gate pre-activations
-    z_alpha, z_omega [N,H,dk] and z_r [N,H] (the kernel applies sigmoid,
-    softplus and 0.01 + softplus); S [N,H,dk,dv] and p [N,H,dk] float32 are
-    updated in place.  Returns o [N,H,dv]."""
+def step_gated(q, k, v, z_alpha, z_omega, z_r, mu, S, p, variant="diagonal", o=None):
+    """One decode step from gate pre-activations z_alpha, z_omega, z_r in the
+    layouts ``step`` gives alpha, omega, r (the kernel applies sigmoid,
+    softplus and 0.01 + softplus); S and p float32 are updated in place.
+    Returns o [N,H,dv]."""
     torch = _torch()
     lib = load_library()
+    var = VARIANTS[variant]
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
+    ashape, wshape = _gate_shapes(var, (N, H), dk)
     for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
-                         ("z_alpha", z_alpha, (N, H, dk)), ("z_omega", z_omega, (N, H, dk)), ("z_r", z_r, (N, H))):
+                         ("z_alpha", z_alpha, ashape), ("z_omega", z_omega, wshape), ("z_r", z_r, (N, H))):
         _need(t, name, shp, dt, dev)
     _need(S, "S", (N, H, dk, dv), torch.float32, dev)
-    _need(p, "p", (N, H, dk), torch.float32, dev)
+    _need(p, "p", _p_shape(var, (N, H), dk, dv), torch.float32, dev)
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _need(o, "o", (N, H, dv), dt, dev)
     st = lib.kdn_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r), float(mu),
-                            KDN_DIAGONAL, _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
+                            var, _dtype_code(q), N, H, dk, dv, _ptr(S), _ptr(p), _ptr(o), _stream(dev))
     _check(st, "kdn_step_gated")
     return o
 
 
-def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, S0=None, p0=None, algo="auto",
-                         order=None):
-    """``forward_varlen`` of the diagonal layer from gate pre-activations
-    z_alpha, z_omega [total,H,dk] and z_r [total,H]."""
+def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, variant="diagonal", S0=None,
+                         p0=None, algo="auto", order=None):
+    """``forward_varlen`` from gate pre-activations z_alpha, z_omega, z_r in
+    the layouts ``forward_varlen`` gives alpha, omega, r."""
     torch = _torch()
     lib = load_library()
+    var = VARIANTS[variant]
     total, H, dk = q.shape
     dv = v.shape[-1]
     N = int(cu_seqlens.shape[0]) - 1
     dev, dt = q.device, q.dtype
+    ashape, wshape = _gate_shapes(var, (total, H), dk)
+    pshape = _p_shape(var, (N, H), dk, dv)
     for name, t, shp in (("q", q, (total, H, dk)), ("k", k, (total, H, dk)), ("v", v, (total, H, dv)),
-                         ("z_alpha", z_alpha, (total, H, dk)), ("z_omega", z_omega, (total, H, dk)),
-                         ("z_r", z_r, (total, H))):
+                         ("z_alpha", z_alpha, ashape), ("z_omega", z_omega, wshape), ("z_r", z_r, (total, H))):
         _need(t, name, shp, dt, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     if order is not None:
@@ -361,12 +368,12 @@ def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, S0=
     if S0 is not None:
         _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
     if p0 is not None:
-        _need(p0, "p0", (N, H, dk), torch.float32, dev)
+        _need(p0, "p0", pshape, torch.float32, dev)
     o = torch.empty((total, H, dv), dtype=dt, device=dev)
     S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    p_T = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    p_T = torch.empty(pshape, dtype=torch.float32, device=dev)
     st = lib.kdn_forward_varlen_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z_alpha), _ptr(z_omega), _ptr(z_r),
-                                      _ptr(cu_seqlens), _ptr(order), _ptr(c0), float(mu), KDN_DIAGONAL,
+                                      _ptr(cu_seqlens), _ptr(order), _ptr(c0), float(mu), var,
                                       _dtype_code(q), N, total, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(o),
                                       _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward_varlen_gated")

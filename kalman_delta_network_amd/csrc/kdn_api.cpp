@@ -306,8 +306,8 @@ int kdn_validate_forward_gated(const void* q, const void* k, const void* v, cons
     const int st = validate_forward(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv,
                                     S0, p0, o, S_T, p_T, algo);
     if (st != KDN_OK) return st;
-    if (variant != KDN_DIAGONAL)
-        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    if (variant == KDN_DIAGONAL_GROUPED)
+        return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
     return ok();
 }
 
@@ -361,8 +361,8 @@ int kdn_forward_varlen_gated(const void* q, const void* k, const void* v, const 
     const int st = validate_forward_varlen(q, k, v, z_alpha, z_omega, z_r, cu_seqlens, order, c0, mu, variant,
                                            dtype, N, total, H, dk, dv, S0, p0, o, S_T, p_T, algo);
     if (st != KDN_OK) return st;
-    if (variant != KDN_DIAGONAL)
-        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    if (variant == KDN_DIAGONAL_GROUPED)
+        return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
     if (int64_t(N) * H == 0) return ok();
     kdn::FwdArgs a{q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, N, total, H, dk, dv,
                    S0, p0, o, S_T, p_T};
@@ -377,8 +377,8 @@ int kdn_step_gated(const void* q, const void* k, const void* v, const void* z_al
                    float* S, float* p, void* o, void* stream) {
     const int st = validate_step(q, k, v, z_alpha, z_omega, z_r, mu, variant, dtype, N, H, dk, dv, S, p, o);
     if (st != KDN_OK) return st;
-    if (variant != KDN_DIAGONAL)
-        return fail(KDN_ERR_UNSUPPORTED, "the gate step is defined for the diagonal variant only (got %d)", variant);
+    if (variant == KDN_DIAGONAL_GROUPED)
+        return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
     if (int64_t(N) * H == 0) return ok();
     if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
     kdn::FwdArgs a{q, k, v, z_alpha, z_omega, z_r, nullptr, mu, variant, dtype, N, 1, H, dk, dv,

@@ -514,19 +514,42 @@ __device__ __forceinline__ float row_sumsq(const u4 (&r)[8]) {
 
 // the row sums a chunk's scan needs: |k|^2 and (per-channel decay) the
 // trace projection mean_i alpha_i^2, of token lane & 31
-template <int DK, int VAR>
+template <int DK, int VAR, bool GATE = false>
 __device__ __forceinline__ void chain_iso_sums(const ChainIsoRegs<VAR>& X, float& n, float& a2) {
     n = row_sumsq<DK>(X.kr);
-    if constexpr (VAR == 2) a2 = row_sumsq<DK>(X.ar) * (1.f / float(DK));
+    if constexpr (VAR == 2) {
+        if constexpr (GATE) {
+            // the decays from their pre-activations, then mean_i alpha_i^2
+            constexpr int NQ = DK / 16;
+            float s2 = 0.f;
+#pragma unroll
+            for (int m = 0; m < NQ; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = gate_sigmoid(bf_lo(X.ar[m][e])), x1 = gate_sigmoid(bf_hi(X.ar[m][e]));
+                    s2 = fmaf(x0, x0, s2);
+                    s2 = fmaf(x1, x1, s2);
+                }
+            a2 = (s2 + __shfl_xor(s2, 32, 64)) * (1.f / float(DK));
+        } else {
+            a2 = row_sumsq<DK>(X.ar) * (1.f / float(DK));
+        }
+    }
 }
 
-template <int DK, int VAR>
+template <int DK, int VAR, bool GATE = false>
 __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<DK>& sm, int buf, float mu,
                                               float& bprev, int nvalid, int gring, float n, float a2) {
     const int lane = threadIdx.x & 63;
     const bool ok = (lane & 31) < nvalid;
-    const float w = ok ? bf1(bf16_t(X.w)) * (1.f / float(DK)) : 0.f;
-    const float rt = ok ? bf1(bf16_t(X.rv)) : 1.f;
+    float wz = bf1(bf16_t(X.w)), rz = bf1(bf16_t(X.rv));
+    if (GATE) {
+        // process and observation noise from their pre-activations
+        wz = gate_softplus(wz);
+        rz = kGateRMin + gate_softplus(rz);
+    }
+    const float w = ok ? wz * (1.f / float(DK)) : 0.f;
+    const float rt = ok ? rz : 1.f;
     const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
     // the uncertainty's decay: alpha^2, or with per-channel decay the trace
     // projection mean_i alpha_i^2 (padding tokens: 1)
@@ -534,7 +557,9 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<D
     if constexpr (VAR == 2) {
         asq = ok ? a2 : 1.f;
     } else {
-        al = ok ? bf1(bf16_t(X.al)) : 1.f;
+        float az = bf1(bf16_t(X.al));
+        if (GATE) az = gate_sigmoid(az);
+        al = ok ? az : 1.f;
         asq = al * al;
     }
     // this token's Mobius matrix [[m00, m01], [m10, m11]] and decay
@@ -597,7 +622,7 @@ __device__ __forceinline__ void chain_decay_load(DecayRegs<DK>& X, const Args& a
 // g_t,i = prod_{s <= t} alpha_s,i for the chunk's tokens [T0, T1) (padding
 // tokens: alpha = 1), carried in g across the two calls of a chunk; stored as
 // the diagonal variant's chain stores it (8-token groups), g_L at the end
-template <int DK, int T0, int T1, bool MASK>
+template <int DK, int T0, int T1, bool MASK, bool GATE = false>
 __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>& sm, int buf, int nvalid,
                                                 int gring, float (&g)[DK / 64]) {
     constexpr int CPL = DK / 64;
@@ -609,7 +634,8 @@ __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>
         const bool ok = !MASK || t < nvalid;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-            const float al = cc ? bf_hi(X.ap[t]) : bf_lo(X.ap[t]);
+            float al = cc ? bf_hi(X.ap[t]) : bf_lo(X.ap[t]);
+            if (GATE) al = gate_sigmoid(al);
             g[cc] *= ok ? al : 1.f;
             gv[cc][t & 1] = g[cc];
             if (t & 1) gp[cc][(t >> 1) & 3] = pack2_opaque(gv[cc][0], gv[cc][1]);
@@ -1053,7 +1079,7 @@ __device__ __forceinline__ int form_index(int w) {
 template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
-    static_assert(!GATE || (VAR == 0 && !GR), "the gate step is the diagonal layer's");
+    static_assert(!GATE || !GR, "no gate step with grouped observation noise");
     static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
     static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
     constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
@@ -1188,15 +1214,15 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     for (int cc = 0; cc < DK / 64; ++cc) g[cc] = 1.f;
                     if (VAR == 2) {
                         if (c < nchunks) {
-                            if (nvalid == L) chain_decay_run<DK, 0, L / 2, false>(X, sm, c & 1, L, c % 3, g);
-                            else chain_decay_run<DK, 0, L / 2, true>(X, sm, c & 1, nvalid, c % 3, g);
+                            if (nvalid == L) chain_decay_run<DK, 0, L / 2, false, GATE>(X, sm, c & 1, L, c % 3, g);
+                            else chain_decay_run<DK, 0, L / 2, true, GATE>(X, sm, c & 1, nvalid, c % 3, g);
                         }
                         chain_decay_load<DK>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
                     if (VAR == 2 && c < nchunks) {
-                        if (nvalid == L) chain_decay_run<DK, L / 2, L, false>(X, sm, c & 1, L, c % 3, g);
-                        else chain_decay_run<DK, L / 2, L, true>(X, sm, c & 1, nvalid, c % 3, g);
+                        if (nvalid == L) chain_decay_run<DK, L / 2, L, false, GATE>(X, sm, c & 1, L, c % 3, g);
+                        else chain_decay_run<DK, L / 2, L, true, GATE>(X, sm, c & 1, nvalid, c % 3, g);
                     }
                     bar();
                 }
@@ -1209,7 +1235,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             // the row sums of the next chunk are formed in the second segment
             // (this wave's idle one), from the registers just loaded
             float n = 0.f, a2 = 1.f;
-            chain_iso_sums<DK, VAR>(A, n, a2);
+            chain_iso_sums<DK, VAR, GATE>(A, n, a2);
             for (int it = 0; it < nit; it += 2) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -1223,11 +1249,11 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                         // loads still in flight, and the compiler would wait
                         // for those loads (a full memory round trip) first
                         if (c < nchunks)
-                            chain_iso_run<DK, VAR>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3, n, a2);
+                            chain_iso_run<DK, VAR, GATE>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3, n, a2);
                         chain_iso_load<DK, VAR>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
-                    chain_iso_sums<DK, VAR>(Y, n, a2);
+                    chain_iso_sums<DK, VAR, GATE>(Y, n, a2);
                     bar();
                 }
             }
@@ -1364,6 +1390,16 @@ bool narrow_pays(const FwdArgs& a) {
     return long(a.B) * a.H * (a.dv / DVT) * 2 <= kNumCUs;
 }
 
+template <int DK>
+hipError_t launch_gated(const FwdArgs& a, hipStream_t stream) {
+    if (narrow_pays(a)) {
+        if (a.variant == 2) return launch_t<DK, 2, false, 1, true>(a, stream);
+        return a.variant == 1 ? launch_t<DK, 1, false, 1, true>(a, stream) : launch_t<DK, 0, false, 1, true>(a, stream);
+    }
+    if (a.variant == 2) return launch_t<DK, 2, false, 2, true>(a, stream);
+    return a.variant == 1 ? launch_t<DK, 1, false, 2, true>(a, stream) : launch_t<DK, 0, false, 2, true>(a, stream);
+}
+
 }  // namespace
 
 bool chunked_supports(const FwdArgs& a) {
@@ -1379,11 +1415,9 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (a.variant == 3 && a.chunk_width == dvt_of<1>()) return hipErrorNotSupported;  // groups are 64 columns
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
     if (a.gates) {
-        // the diagonal layer with its gate step (alpha, omega, r as pre-activations)
-        if (a.variant != 0) return hipErrorNotSupported;
-        const bool nw = narrow_pays(a);
-        if (a.dk == 128) return nw ? launch_t<128, 0, false, 1, true>(a, stream) : launch_t<128, 0, false, 2, true>(a, stream);
-        return nw ? launch_t<64, 0, false, 1, true>(a, stream) : launch_t<64, 0, false, 2, true>(a, stream);
+        // the gate step inside (alpha, omega, r as pre-activations)
+        if (a.variant == 3) return hipErrorNotSupported;
+        return a.dk == 128 ? launch_gated<128>(a, stream) : launch_gated<64>(a, stream);
     }
     // variant 3: diagonal with grouped observation noise (one group per tile)
     if (a.dk == 128) {

@@ -141,7 +141,7 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         const size_t tok = (tok0 + size_t(t)) * size_t(H) + size_t(h);
         float rt = to_f32(r[GR ? tok * NG + grp : tok]);
         // gates (diagonal layer): alpha, omega and r arrive as pre-activations
-        if (!ISO && gates) rt = kGateRMin + gate_softplus(rt);
+        if (gates) rt = kGateRMin + gate_softplus(rt);
         float kk[CPL], qq[CPL], aa[CPL], kap[CPL];
         float mq;  // kappa^T q
 #pragma unroll
@@ -152,11 +152,13 @@ kdn_recurrent_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
         if (ISO) {
             // trace-projected predict b_hat = a b + omega / d_k; a = alpha^2,
             // or with per-channel decay the mean of alpha_i^2 over the channels
-            const float w = to_f32(omega[tok]);
+            float w = to_f32(omega[tok]);
+            if (gates) w = gate_softplus(w);
             float a2 = 0.f, n = 0.f, kq = 0.f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 aa[c] = CHAN ? to_f32(alpha[tok * DK + lane + 64 * c]) : to_f32(alpha[tok]);
+                if (gates) aa[c] = gate_sigmoid(aa[c]);
                 a2 += aa[c] * aa[c];
                 n += kk[c] * kk[c];
                 kq += kk[c] * qq[c];

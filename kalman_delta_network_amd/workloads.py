@@ -148,10 +148,10 @@ def forward_inputs(w: Workload) -> dict:
 
 
 def gated_inputs(w: Workload) -> dict:
-    """Inputs of one gated forward (diagonal layer): q, k, v as in
-    ``forward_inputs`` and, in place of alpha, omega and r, their gate
-    pre-activations z_alpha ~ N(alpha_loc, 0.5), z_omega ~ N(omega_loc, 1)
-    [B,T,H,dk] and z_r ~ N(0, 1) [B,T,H] (the distributions whose gated values
+    """Inputs of one gated forward: q, k, v as in ``forward_inputs`` and, in
+    place of alpha, omega and r, their gate pre-activations
+    z_alpha ~ N(alpha_loc, 0.5), z_omega ~ N(omega_loc, 1), z_r ~ N(0, 1) in
+    the variant's layouts (the distributions whose gated values
     ``forward_inputs`` draws), all rounded to bf16 for bf16 workloads; c0 [H]."""
     rng = np.random.default_rng([w.seed, 0x6A])
     lead = (w.B, w.T, w.H)
@@ -159,8 +159,9 @@ def gated_inputs(w: Workload) -> dict:
         "q": _l2norm(_normal(rng, lead + (w.dk,))),
         "k": _l2norm(_normal(rng, lead + (w.dk,))),
         "v": _normal(rng, lead + (w.dv,)),
-        "z_alpha": _normal(rng, lead + (w.dk,), w.alpha_loc, 0.5),
-        "z_omega": _normal(rng, lead + (w.dk,), w.omega_loc, 1.0),
+        "z_alpha": _normal(rng, lead + (w.dk,) if w.variant in ("diagonal", "isochannel") else lead,
+                           w.alpha_loc, 0.5),
+        "z_omega": _normal(rng, lead + (w.dk,) if w.variant == "diagonal" else lead, w.omega_loc, 1.0),
         "z_r": _normal(rng, lead),
     }
     if w.dtype == "bf16":
@@ -213,17 +214,18 @@ def decode_tokens(w: Workload, step: int) -> dict:
 
 
 def gated_decode_tokens(w: Workload, step: int) -> dict:
-    """The token of decode step ``step`` for all N = w.B sequences of the
-    diagonal layer, with gate pre-activations: q, k, z_alpha, z_omega
-    [N,H,dk], v [N,H,dv], z_r [N,H] (distributions as ``gated_inputs``)."""
+    """The token of decode step ``step`` for all N = w.B sequences, with gate
+    pre-activations in the variant's layouts (q, k [N,H,dk], v [N,H,dv],
+    z_r [N,H]; distributions as ``gated_inputs``)."""
     rng = np.random.default_rng([w.seed, 0x71, step])
     lead = (w.B, w.H)
     out = {
         "q": _l2norm(_normal(rng, lead + (w.dk,))),
         "k": _l2norm(_normal(rng, lead + (w.dk,))),
         "v": _normal(rng, lead + (w.dv,)),
-        "z_alpha": _normal(rng, lead + (w.dk,), w.alpha_loc, 0.5),
-        "z_omega": _normal(rng, lead + (w.dk,), w.omega_loc, 1.0),
+        "z_alpha": _normal(rng, lead + (w.dk,) if w.variant in ("diagonal", "isochannel") else lead,
+                           w.alpha_loc, 0.5),
+        "z_omega": _normal(rng, lead + (w.dk,) if w.variant == "diagonal" else lead, w.omega_loc, 1.0),
         "z_r": _normal(rng, lead),
     }
     if w.dtype == "bf16":

@@ -321,9 +321,12 @@ def gates(z_alpha, z_omega, z_r):
     return sigmoid(_f64(z_alpha)), softplus(_f64(z_omega)), R_MIN + softplus(_f64(z_r))
 
 
-def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None):
-    """The diagonal forward fed through the gate step: ``gates`` on the
-    pre-activations, then ``forward_diag`` on the resulting alpha, omega, r."""
+def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, variant="diagonal"):
+    """The forward fed through the gate step: ``gates`` on the
+    pre-activations, then ``forward_diag`` / ``forward_iso`` /
+    ``forward_isoc`` on the resulting alpha, omega, r (the gates are
+    elementwise, so they apply to every variant's layouts alike)."""
     alpha, omega, r = gates(z_alpha, z_omega, z_r)
-    return forward_diag(q, k, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
+    fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc}[variant]
+    return fn(q, k, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
 

@@ -373,29 +373,30 @@ def call_validate_gated(lib, a):
 
 
 def test_validate_gated_forward(lib):
-    # the gate step belongs to the diagonal layer: every other variant is refused,
-    # the rest of the checks are those of the plain forward
+    # no gate step with grouped observation noise; the rest of the checks are
+    # those of the plain forward
     f = Fake()
     for dtype in (0, 1):
         for algo in (0, 1, 2, 3, 4):
             assert call_validate_gated(lib, fwd_args(f, dtype=dtype, algo=algo)) == 0
-    for variant in (1, 2, 3):
-        assert call_validate_gated(lib, fwd_args(f, variant=variant)) == kdn.KDN_ERR_UNSUPPORTED
-        assert b"diagonal" in lib.kdn_last_error()
+    for variant in (1, 2):
+        assert call_validate_gated(lib, fwd_args(f, variant=variant)) == 0
+    assert call_validate_gated(lib, fwd_args(f, variant=3)) == kdn.KDN_ERR_UNSUPPORTED
+    assert b"grouped" in lib.kdn_last_error()
     assert call_validate_gated(lib, fwd_args(f, q=None)) == kdn.KDN_ERR_NULL
     assert call_validate_gated(lib, fwd_args(f, dk=96)) == kdn.KDN_ERR_UNSUPPORTED
     assert call_validate_gated(lib, fwd_args(f, mu=-1.0)) == kdn.KDN_ERR_VALUE
     assert call_validate_gated(lib, fwd_args(f, B=0, q=None, o=None, S_T=None)) == 0
 
 
-def test_gated_serving_entry_points_refuse_other_variants_before_any_launch(lib):
+def test_gated_serving_entry_points_refuse_grouped_noise_before_any_launch(lib):
     # argument errors return before anything touches the device
     f = Fake()
-    assert lib.kdn_step_gated(f(), f(), f(), f(), f(), f(), 128.0, 1, 1, 2, 3, 128, 128, f(), f(), f(),
+    assert lib.kdn_step_gated(f(), f(), f(), f(), f(), f(), 128.0, 3, 1, 2, 3, 128, 128, f(), f(), f(),
                               None) == kdn.KDN_ERR_UNSUPPORTED
     assert lib.kdn_step_gated(None, f(), f(), f(), f(), f(), 128.0, 0, 1, 2, 3, 128, 128, f(), f(), f(),
                               None) == kdn.KDN_ERR_NULL
-    assert lib.kdn_forward_varlen_gated(f(), f(), f(), f(), f(), f(), f(), None, f(), 128.0, 2, 1, 2, 10, 3,
+    assert lib.kdn_forward_varlen_gated(f(), f(), f(), f(), f(), f(), f(), None, f(), 128.0, 3, 1, 2, 10, 3,
                                         128, 128, None, None, f(), f(), f(), None, 0) == kdn.KDN_ERR_UNSUPPORTED
     assert lib.kdn_step_gated(f(), f(), f(), f(), f(), f(), 128.0, 0, 1, 0, 3, 128, 128, f(), f(), f(),
                               None) == kdn.KDN_OK  # empty batch: nothing to launch

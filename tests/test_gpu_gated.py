@@ -1,7 +1,8 @@
-"""GPU parity of the gated forward (kdn_forward_gated: the diagonal layer with
-its gate step, alpha = sigmoid(z), omega = softplus(z), r = 0.01 + softplus(z),
-done inside the kernels) against oracle.forward_gated on the same
-pre-activations, through the C ABI.  Tolerance: max relative error 1e-4
+"""GPU parity of the gated forward (kdn_forward_gated and its decode and
+packed-batch forms: the gate step alpha = sigmoid(z), omega = softplus(z),
+r = 0.01 + softplus(z) done inside the kernels, for the diagonal, isotropic
+and per-channel-decay isotropic variants) against oracle.forward_gated on the
+same pre-activations, through the C ABI.  Tolerance: max relative error 1e-4
 (fp32 inputs) or 2e-2 (bf16 inputs, fp32 state), per output tensor."""
 import numpy as np
 import pytest
@@ -36,13 +37,14 @@ def run(dev, w, x, algo, S0=None, p0=None):
     import torch
     import kalman_delta_network_amd as kdn
     f32 = (lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float32)).to(dev))
-    o, S, p = kdn.forward_gated(**to_dev(x, w.dtype, dev), mu=w.mu, S0=f32(S0), p0=f32(p0), algo=algo)
+    o, S, p = kdn.forward_gated(**to_dev(x, w.dtype, dev), mu=w.mu, variant=w.variant, S0=f32(S0), p0=f32(p0),
+                                algo=algo)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()
 
 
 def oracle_gated(w, x, S0=None, p0=None):
-    return oracle.forward_gated(**{n: x[n] for n in GATED}, c0=x["c0"], mu=w.mu, S0=S0, p0=p0)
+    return oracle.forward_gated(**{n: x[n] for n in GATED}, c0=x["c0"], mu=w.mu, S0=S0, p0=p0, variant=w.variant)
 
 
 def check(name, got, ref, dtype):
@@ -52,19 +54,22 @@ def check(name, got, ref, dtype):
         assert e <= tol(dtype), (name, k, e)
 
 
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
 @pytest.mark.parametrize("algo", ["recurrent", "chunked_wide", "chunked_narrow"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 @pytest.mark.parametrize("T", [1, 63, 65, 200])
-def test_gated_forward(dev, algo, dtype, dk, dv, T):
+def test_gated_forward(dev, variant, algo, dtype, dk, dv, T):
     if dtype == "f32" and algo != "recurrent":
         pytest.skip("the chunked kernel takes bf16 inputs")
     # omega_loc 0: softplus near its bend, z_alpha around 2 (decay ~0.88)
-    w = wl.Workload("gated", "diagonal", dtype, 2, T, 3, dk, dv, float(dk), "uniform", 1500 + T + dk + dv,
+    w = wl.Workload("gated", variant, dtype, 2, T, 3, dk, dv, float(dk), "uniform", 1500 + T + dk + dv,
                     omega_loc=0.0 if T % 2 else -4.0)
     x = wl.gated_inputs(w)
-    assert x["z_alpha"].shape == (2, T, 3, dk) and x["z_r"].shape == (2, T, 3)
-    check(f"gated/{algo}/{dtype}/dk{dk}/dv{dv}/T{T}", run(dev, w, x, algo), oracle_gated(w, x), dtype)
+    assert x["z_r"].shape == (2, T, 3)
+    assert x["z_alpha"].shape == ((2, T, 3) if variant == "isotropic" else (2, T, 3, dk))
+    assert x["z_omega"].shape == ((2, T, 3, dk) if variant == "diagonal" else (2, T, 3))
+    check(f"gated/{variant}/{algo}/{dtype}/dk{dk}/dv{dv}/T{T}", run(dev, w, x, algo), oracle_gated(w, x), dtype)
 
 
 def test_gated_extreme_pre_activations(dev):
@@ -83,16 +88,17 @@ def test_gated_extreme_pre_activations(dev):
         check(f"gated/extreme/{algo}", run(dev, w, x, algo), oracle_gated(w, x), "bf16")
 
 
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
-def test_gated_with_initial_state(dev, algo):
-    w = wl.Workload("gated_init", "diagonal", "bf16", 2, 150, 2, 128, 128, 128.0, "uniform", 1602, omega_loc=-1.0)
+def test_gated_with_initial_state(dev, variant, algo):
+    w = wl.Workload("gated_init", variant, "bf16", 2, 150, 2, 128, 128, 128.0, "uniform", 1602, omega_loc=-1.0)
     x = wl.gated_inputs(w)
     st = wl.decode_state(w)
-    check(f"gated/init/{algo}", run(dev, w, x, algo, S0=st["S0"], p0=st["p0"]),
+    check(f"gated/init/{variant}/{algo}", run(dev, w, x, algo, S0=st["S0"], p0=st["p0"]),
           oracle_gated(w, x, S0=st["S0"], p0=st["p0"]), "bf16")
 
 
-def test_gated_rejects_other_variants(dev):
+def test_gated_rejects_grouped_noise(dev):
     import torch
     import kalman_delta_network_amd as kdn
     w = wl.Workload("gated_var", "diagonal", "bf16", 1, 8, 1, 128, 128, 128.0, "uniform", 1603)
@@ -103,7 +109,7 @@ def test_gated_rejects_other_variants(dev):
     lib = kdn.load_library()
     st = lib.kdn_forward_gated(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["z_alpha"].data_ptr(),
                                t["z_omega"].data_ptr(), t["z_r"].data_ptr(), t["c0"].data_ptr(), 128.0,
-                               kdn.KDN_ISOTROPIC, 1, 1, 8, 1, 128, 128, None, None, o.data_ptr(), S.data_ptr(),
+                               kdn.KDN_DIAGONAL_GROUPED, 1, 1, 8, 1, 128, 128, None, None, o.data_ptr(), S.data_ptr(),
                                p.data_ptr(), None, 0)
     assert st == kdn.KDN_ERR_UNSUPPORTED
 
@@ -127,12 +133,13 @@ def test_gated_full_size_sampled_heads(dev):
         assert e <= tol("bf16"), (k, e)
 
 
-def test_gated_decode_steps(dev):
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
+def test_gated_decode_steps(dev, variant):
     # four consecutive decode steps from pre-activations; token s of each
     # sequence is position s of a gated input draw
     import torch
     import kalman_delta_network_amd as kdn
-    w = wl.Workload("gated_dec", "diagonal", "bf16", 8, 4, 4, 128, 128, 128.0, "uniform", 1604, omega_loc=-1.0)
+    w = wl.Workload("gated_dec", variant, "bf16", 8, 4, 4, 128, 128, 128.0, "uniform", 1604, omega_loc=-1.0)
     x = wl.gated_inputs(w)
     st = wl.decode_state(w)
     S = torch.from_numpy(st["S0"]).to(dev)
@@ -141,31 +148,33 @@ def test_gated_decode_steps(dev):
     for s in range(w.T):
         tok = {n: np.ascontiguousarray(x[n][:, s]) for n in GATED}
         t = {n: torch.from_numpy(tok[n]).to(torch.bfloat16).to(dev) for n in GATED}
-        o = kdn.step_gated(**t, mu=w.mu, S=S, p=p)
+        o = kdn.step_gated(**t, mu=w.mu, S=S, p=p, variant=variant)
         a, om, r = oracle.gates(tok["z_alpha"], tok["z_omega"], tok["z_r"])
-        ref = oracle.step_diag(tok["q"], tok["k"], tok["v"], a, om, r, mu=w.mu, S=Sr, p=pr)
+        fn = {"diagonal": oracle.step_diag, "isotropic": oracle.step_iso, "isochannel": oracle.step_isoc}[variant]
+        ref = fn(tok["q"], tok["k"], tok["v"], a, om, r, mu=w.mu, S=Sr, p=pr)
         Sr, pr = ref["S"], ref["p"]
         torch.cuda.synchronize()
-        check(f"gated/decode/step{s}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()),
+        check(f"gated/decode/{variant}/step{s}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()),
               {"o": ref["o"], "S": Sr, "p": pr}, "bf16")
 
 
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
-def test_gated_packed_batch(dev, algo):
+def test_gated_packed_batch(dev, variant, algo):
     import torch
     import kalman_delta_network_amd as kdn
     lengths = [1, 33, 0, 90, 64, 129]
     total = sum(lengths)
-    w = wl.Workload("gated_var", "diagonal", "bf16", 1, total, 3, 128, 128, 128.0, "uniform", 1605, omega_loc=-1.0)
+    w = wl.Workload("gated_var", variant, "bf16", 1, total, 3, 128, 128, 128.0, "uniform", 1605, omega_loc=-1.0)
     x = {n: (v[0] if n != "c0" else v) for n, v in wl.gated_inputs(w).items()}  # [total, H, *]
     cu = np.zeros(len(lengths) + 1, np.int32)
     cu[1:] = np.cumsum(lengths)
     t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev) for n in GATED}
     o, S, p = kdn.forward_varlen_gated(**t, c0=torch.from_numpy(x["c0"]).to(dev),
-                                       cu_seqlens=torch.from_numpy(cu).to(dev), mu=w.mu, algo=algo,
+                                       cu_seqlens=torch.from_numpy(cu).to(dev), mu=w.mu, variant=variant, algo=algo,
                                        order=torch.from_numpy(kdn.longest_first(cu)).to(dev))
     torch.cuda.synchronize()
     a, om, r = oracle.gates(x["z_alpha"], x["z_omega"], x["z_r"])
     ref = oracle.forward_varlen(x["q"], x["k"], x["v"], a, om, r, c0=x["c0"], mu=w.mu, cu_seqlens=cu,
-                                variant="diagonal")
-    check(f"gated/varlen/{algo}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")
+                                variant=variant)
+    check(f"gated/varlen/{variant}/{algo}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")
