@@ -330,3 +330,19 @@ def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, vari
     fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc}[variant]
     return fn(q, k, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
 
+
+def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, dp_T=None, S0=None, p0=None,
+                   variant="diagonal"):
+    """Gradients of ``forward_gated``: ``backward`` on the gated values, then
+    the chain rule through the gates, d z_alpha = d alpha sigmoid'(z_alpha)
+    with sigmoid' = sigmoid (1 - sigmoid), d z_omega = d omega
+    sigmoid(z_omega) and d z_r = d r sigmoid(z_r) (softplus' = sigmoid).
+    Returns dq, dk, dv, dz_alpha, dz_omega, dz_r, dS0, dp0, dc0."""
+    alpha, omega, r = gates(z_alpha, z_omega, z_r)
+    g = backward(q, k, v, alpha, omega, r, c0, mu, dO=dO, dS_T=dS_T, dp_T=dp_T, S0=S0, p0=p0, variant=variant)
+    out = {n: g[n] for n in ("dq", "dk", "dv", "dS0", "dp0", "dc0")}
+    out["dz_alpha"] = g["dalpha"] * alpha * (1.0 - alpha)
+    out["dz_omega"] = g["domega"] * sigmoid(_f64(z_omega))
+    out["dz_r"] = g["dr"] * sigmoid(_f64(z_r))
+    return out
+

@@ -122,3 +122,34 @@ def test_uncertainty_gradient_closed_form_without_dynamics():
     prec = 1.0 / p0 + w.mu * np.sum(x["k"][0, :, 0, :] ** 2 / x["r"][0, :, 0, None], axis=0)[None, None, :]
     pT = 1.0 / prec
     np.testing.assert_allclose(g["dp0"], (pT / p0) ** 2, rtol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
+def test_gated_backward_matches_finite_differences_of_the_gated_forward(variant):
+    # gradients with respect to the gate pre-activations, against central
+    # differences of oracle.forward_gated (the gate step of the summary page,
+    # method step 1)
+    w, x, ct, _ = _case(variant, False, seed=51)
+    z = {n: np.asarray(a, np.float64) for n, a in wl.gated_inputs(w).items()}
+    names = ("q", "k", "v", "z_alpha", "z_omega", "z_r")
+
+    def loss():
+        out = oracle.forward_gated(**{n: z[n] for n in names}, c0=z["c0"], mu=w.mu, variant=variant)
+        return np.sum(out["o"] * ct["dO"]) + np.sum(out["S"] * ct["dS_T"]) + np.sum(out["p"] * ct["dp_T"])
+
+    g = oracle.backward_gated(**{n: z[n] for n in names}, c0=z["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
+                              dp_T=ct["dp_T"], variant=variant)
+    for name in ("z_alpha", "z_omega", "z_r", "k"):
+        arr = z[name]
+        fd = np.zeros(arr.shape)
+        flat, gflat = arr.reshape(-1), fd.reshape(-1)
+        for e in range(flat.size):
+            base = flat[e]
+            h = 1e-6 * max(1.0, abs(base))
+            flat[e] = base + h
+            lp = loss()
+            flat[e] = base - h
+            lm = loss()
+            flat[e] = base
+            gflat[e] = (lp - lm) / (2 * h)
+        _check(g["d" + name], fd, name)
