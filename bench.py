@@ -240,14 +240,20 @@ def bench_varlen(kdn, dev, steps, algo):
             "tokens_per_s": total / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_backward(kdn, w, dev, steps):
-    """Time kdn_backward on workload w (cotangent dO only), inputs resident."""
+def bench_backward(kdn, w, dev, steps, gated=False):
+    """Time kdn_backward (``gated``: kdn_backward_gated on gate
+    pre-activations) on workload w (cotangent dO only), inputs resident."""
     import torch
     from kalman_delta_network_amd import workloads as wl
-    t = upload(wl.forward_inputs(w), w.dtype, dev)
+    t = upload(wl.gated_inputs(w) if gated else wl.forward_inputs(w), w.dtype, dev)
     dO = torch.from_numpy(wl.backward_cotangents(w, with_state=False)["dO"]).to(t["q"].dtype).to(dev)
-    ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
-    call = lambda: kdn.backward(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
+    if gated:
+        ws = torch.empty(kdn.backward_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.variant),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: kdn.backward_gated(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
+    else:
+        ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+        call = lambda: kdn.backward(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
     warm(call, 1)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
@@ -431,6 +437,7 @@ def main():
                                  "workgroups": chunked_workgroups(wlc)}
         del tlc
         extra["backward"] = bench_backward(kdn, w, dev, 3)
+        extra["backward_gated"] = bench_backward(kdn, w, dev, 3, gated=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x)

@@ -314,6 +314,29 @@ int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, con
 
 /* Static description of a status code (never NULL). */
 const char* kdn_status_string(int status);
+/*
+ * kdn_backward_gated -- kdn_backward of the gated layer (kdn_forward_gated):
+ * z_alpha, z_omega, z_r are the gate pre-activations (layouts of alpha, omega
+ * and r; not KDN_DIAGONAL_GROUPED), and dz_alpha, dz_omega, dz_r receive the
+ * gradients with respect to them (fp32, same layouts):
+ *   dz_alpha = d alpha * sigmoid(z) sigmoid(-z),  dz_omega = d omega * sigmoid(z),
+ *   dz_r = d r * sigmoid(z).
+ * Everything else as kdn_backward, except the workspace:
+ * kdn_backward_gated_workspace_size() bytes, 16-byte aligned.
+ */
+int kdn_backward_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
+                       const void* z_r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                       int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                       const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                       float* dz_alpha, float* dz_omega, float* dz_r, float* dS0, float* dp0, float* dc0,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kdn_backward_gated: the adjoint's workspace
+ * (kdn_backward_workspace_size) rounded up to 256 bytes, then fp32 copies of
+ * q, k, v, dO and the gated alpha, omega, r, each rounded up to 256 bytes.
+ * 0 for negative sizes, an unknown variant or grouped noise. */
+size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv);
+
 /* Detail of the last error on the calling thread ("" if none). */
 const char* kdn_last_error(void);
 /* ABI version: major * 10000 + minor * 100 + patch. */

@@ -49,7 +49,8 @@ def _p_shape(var, lead, dk, dv):
 
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
-           "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated",
+           "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated", "kdn_backward_gated",
+           "kdn_backward_gated_workspace_size",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
@@ -90,10 +91,14 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_validate_backward.argtypes = bwd + [P, ctypes.c_size_t]
     lib.kdn_backward_workspace_size.argtypes = [I, I, I, I, I]
     lib.kdn_backward_workspace_size.restype = ctypes.c_size_t
+    lib.kdn_backward_gated.argtypes = bwd + [P, ctypes.c_size_t, P]
+    lib.kdn_backward_gated_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kdn_backward_gated_workspace_size.restype = ctypes.c_size_t
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
                lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version, lib.kdn_forward_gated,
-               lib.kdn_validate_forward_gated, lib.kdn_forward_varlen_gated, lib.kdn_step_gated):
+               lib.kdn_validate_forward_gated, lib.kdn_forward_varlen_gated, lib.kdn_step_gated,
+               lib.kdn_backward_gated):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -397,6 +402,26 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     Returns a dict of float32 tensors dq, dk, dv, dalpha, domega, dr (input
     layouts), dS0, dp0 and dc0 [H] (sum of dp0 over batch and channels).
     """
+    return _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, False)
+
+
+def backward_gated_workspace_size(B, T, H, dk, dv, variant="diagonal") -> int:
+    """Bytes of device workspace kdn_backward_gated needs for these sizes."""
+    return int(load_library().kdn_backward_gated_workspace_size(VARIANTS[variant], B, T, H, dk, dv))
+
+
+def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
+                   S0=None, p0=None, workspace=None):
+    """Gradients of the gated forward (``forward_gated``) with respect to its
+    inputs, the gate pre-activations included.  Arguments as ``backward``
+    with z_alpha, z_omega, z_r in place of alpha, omega, r; the workspace is
+    backward_gated_workspace_size() bytes.  Returns dq, dk, dv, dz_alpha,
+    dz_omega, dz_r, dS0, dp0, dc0."""
+    g = _backward(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, True)
+    return {("dz_" + n[1:] if n in ("dalpha", "domega", "dr") else n): t for n, t in g.items()}
+
+
+def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, gated):
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
@@ -406,8 +431,9 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     ashape, wshape = _gate_shapes(var, (B, T, H), dk)
     pshape = _p_shape(var, (B, H), dk, dv)
     rshape = _r_shape(var, (B, T, H), dv)
+    names = ("z_alpha", "z_omega", "z_r") if gated else ("alpha", "omega", "r")
     for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                         ("alpha", alpha, ashape), ("omega", omega, wshape), ("r", r, rshape)):
+                         (names[0], alpha, ashape), (names[1], omega, wshape), (names[2], r, rshape)):
         _need(t, name, shp, dt, dev)
     if dO is not None:
         _need(dO, "dO", (B, T, H, dv), dt, dev)
@@ -421,13 +447,13 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
          "domega": torch.empty(wshape, **f32), "dr": torch.empty(rshape, **f32),
          "dS0": torch.empty((B, H, dk, dv), **f32), "dp0": torch.empty(pshape, **f32),
          "dc0": torch.empty((H,), **f32)}
-    need = backward_workspace_size(B, T, H, dk, dv)
+    need = backward_gated_workspace_size(B, T, H, dk, dv, variant) if gated else backward_workspace_size(B, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib.kdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0), float(mu),
-                          var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T),
-                          _ptr(dp_T), *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0",
-                                                             "dp0", "dc0")),
-                          _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, "kdn_backward")
+    fn = lib.kdn_backward_gated if gated else lib.kdn_backward
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0), float(mu),
+            var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T),
+            _ptr(dp_T), *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dp0", "dc0")),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "kdn_backward_gated" if gated else "kdn_backward")
     return g

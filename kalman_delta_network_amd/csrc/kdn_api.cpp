@@ -178,7 +178,7 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
                       int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
                       const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
                       float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
-                      void* work, size_t work_bytes) {
+                      void* work, size_t work_bytes, bool gated = false) {
     int st = validate_common(variant, dtype, mu, dk, dv);
     if (st != KDN_OK) return st;
     if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
@@ -196,7 +196,10 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
         return fail(KDN_ERR_NULL, "dq, dk, dv, dalpha, domega and dr must be non-NULL");
     if (!dS0 || !dp0) return fail(KDN_ERR_NULL, "dS0 and dp0 must be non-NULL");
     if (!c0 && !p0) return fail(KDN_ERR_NULL, "c0 may be NULL only when p0 is given");
-    const size_t need = kdn::backward_workspace_bytes(B, T, H, dk, dv);
+    if (gated && variant == KDN_DIAGONAL_GROUPED)
+        return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
+    const size_t need = gated ? kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv)
+                              : kdn::backward_workspace_bytes(B, T, H, dk, dv);
     if (need > 0 && (!work || work_bytes < need))
         return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, work_bytes);
     const auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
@@ -442,6 +445,29 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
                          dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0,
                          static_cast<float*>(workspace)};
     return hip_status(kdn::launch_backward(a, static_cast<hipStream_t>(stream)), "backward");
+}
+
+size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || variant < 0 || variant > 2) return 0;
+    return kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv);
+}
+
+int kdn_backward_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
+                       const void* z_r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                       int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                       const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                       float* dz_alpha, float* dz_omega, float* dz_r, float* dS0, float* dp0, float* dc0,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate_backward(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv, S0,
+                                     p0, dO, dS_T, dp_T, dq, dk_out, dv_out, dz_alpha, dz_omega, dz_r, dS0, dp0,
+                                     dc0, workspace, workspace_bytes, true);
+    if (st != KDN_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    const kdn::BwdArgs a{q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, dO, dS_T,
+                         dp_T, dq, dk_out, dv_out, dz_alpha, dz_omega, dz_r, dS0, dp0, dc0,
+                         static_cast<float*>(workspace)};
+    return hip_status(kdn::launch_backward_gated(a, static_cast<hipStream_t>(stream)), "gated backward");
 }
 
 }  // extern "C"

@@ -1,0 +1,142 @@
+// Backward of the gated layer: gradients with respect to the gate
+// pre-activations ("Kalman Delta Networks: Uncertainty-aware Associative
+// Memory", summary page, method step 1: alpha = sigmoid(z), omega =
+// softplus(z), r = r_min + softplus(z)).
+//
+// The backward of the recurrence is the fp32 one of kdn_backward.hip, run on
+// the gated values: one elementwise pass widens q, k, v and dO to fp32 and
+// evaluates the gates into the workspace (the same fp32 gate functions as the
+// gated forward), the adjoint runs on them, and a second elementwise pass
+// turns d alpha, d omega, d r into gradients of the pre-activations:
+//   d z_alpha = d alpha * sigmoid(z) sigmoid(-z),
+//   d z_omega = d omega * sigmoid(z),   d z_r = d r * sigmoid(z).
+// Both passes move a few bytes per token next to the adjoint's recomputation,
+// which bounds this path.
+#include "kdn_gates.h"
+#include "kdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kdn {
+namespace {
+
+enum GateOp { kCopy = 0, kSigmoid = 1, kSoftplus = 2, kRSoftplus = 3 };
+
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// y[i] = op(x[i]) in fp32
+template <typename Tin>
+__global__ void __launch_bounds__(256) gate_forward_kernel(const Tin* __restrict__ x, float* __restrict__ y,
+                                                           size_t n, int op) {
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float z = widen(x[i]);
+        float out = z;
+        if (op == kSigmoid) out = gate_sigmoid(z);
+        else if (op == kSoftplus) out = gate_softplus(z);
+        else if (op == kRSoftplus) out = kGateRMin + gate_softplus(z);
+        y[i] = out;
+    }
+}
+
+// d[i] *= the derivative of the gate at z[i]
+template <typename Tin>
+__global__ void __launch_bounds__(256) gate_grad_kernel(const Tin* __restrict__ z, float* __restrict__ d, size_t n,
+                                                        int op) {
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = widen(z[i]);
+        // sigmoid' = sigmoid(z) sigmoid(-z) (no cancellation in 1 - sigmoid);
+        // softplus' = sigmoid
+        const float g = op == kSigmoid ? gate_sigmoid(x) * gate_sigmoid(-x) : gate_sigmoid(x);
+        d[i] *= g;
+    }
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct GatedSizes {
+    size_t nk, nv, na, nw, nr;
+};
+
+GatedSizes gated_sizes(int variant, int B, int T, int H, int dk, int dv) {
+    const size_t toks = size_t(B) * size_t(T) * size_t(H);
+    const bool iso = variant == 1 || variant == 2, chan = variant != 1;
+    return {toks * dk, toks * dv, chan ? toks * dk : toks, iso ? toks : toks * dk, toks};
+}
+
+template <typename Tin>
+hipError_t run(const BwdArgs& a, hipStream_t s) {
+    const GatedSizes n = gated_sizes(a.variant, a.B, a.T, a.H, a.dk, a.dv);
+    char* w = reinterpret_cast<char*>(a.work) + round256(backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv));
+    auto take = [&](size_t count) {
+        float* p = reinterpret_cast<float*>(w);
+        w += round256(count * sizeof(float));
+        return p;
+    };
+    float* fq = take(n.nk);
+    float* fk = take(n.nk);
+    float* fv = take(n.nv);
+    float* fa = take(n.na);
+    float* fw = take(n.nw);
+    float* fr = take(n.nr);
+    float* fdo = take(n.nv);
+    const auto fwd = [&](const void* x, float* y, size_t count, int op) {
+        if (count == 0) return;
+        const unsigned blocks = unsigned(count / 256 + 1 < 8192 ? count / 256 + 1 : 8192);
+        hipLaunchKernelGGL(gate_forward_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(x), y,
+                           count, op);
+    };
+    fwd(a.q, fq, n.nk, kCopy);
+    fwd(a.k, fk, n.nk, kCopy);
+    fwd(a.v, fv, n.nv, kCopy);
+    fwd(a.alpha, fa, n.na, kSigmoid);
+    fwd(a.omega, fw, n.nw, kSoftplus);
+    fwd(a.r, fr, n.nr, kRSoftplus);
+    if (a.dO) fwd(a.dO, fdo, n.nv, kCopy);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    BwdArgs f = a;
+    f.q = fq;
+    f.k = fk;
+    f.v = fv;
+    f.alpha = fa;
+    f.omega = fw;
+    f.r = fr;
+    f.dO = a.dO ? fdo : nullptr;
+    f.dtype = 0;  // the adjoint runs on the fp32 copies
+    e = launch_backward(f, s);
+    if (e != hipSuccess) return e;
+    const auto grad = [&](const void* z, float* d, size_t count, int op) {
+        if (count == 0) return;
+        const unsigned blocks = unsigned(count / 256 + 1 < 8192 ? count / 256 + 1 : 8192);
+        hipLaunchKernelGGL(gate_grad_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(z), d,
+                           count, op);
+    };
+    grad(a.alpha, a.dalpha, n.na, kSigmoid);
+    grad(a.omega, a.domega, n.nw, kSoftplus);
+    grad(a.r, a.dr, n.nr, kSoftplus);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_gated_workspace_bytes(int variant, int B, int T, int H, int dk, int dv) {
+    const size_t base = backward_workspace_bytes(B, T, H, dk, dv);
+    if (base == 0) return 0;
+    const GatedSizes n = gated_sizes(variant, B, T, H, dk, dv);
+    const size_t f = sizeof(float);
+    return round256(base) + 2 * round256(n.nk * f) + 2 * round256(n.nv * f) + round256(n.na * f) +
+           round256(n.nw * f) + round256(n.nr * f);
+}
+
+hipError_t launch_backward_gated(const BwdArgs& a, hipStream_t stream) {
+    if (a.variant == 3) return hipErrorNotSupported;  // no gate step with grouped noise
+    return a.dtype == 1 ? run<uint16_t>(a, stream) : run<float>(a, stream);
+}
+
+}  // namespace kdn

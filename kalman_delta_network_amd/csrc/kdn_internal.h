@@ -76,6 +76,12 @@ struct BwdArgs {
 // Bytes of device workspace one backward call needs (0 for an empty call).
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// Backward of the gated layer: a.alpha, a.omega, a.r hold the gate
+// pre-activations and d alpha, d omega, d r come out as their gradients.
+// a.work holds backward_gated_workspace_bytes() bytes (the adjoint's
+// workspace, then fp32 copies of the token inputs, the gated values and dO).
+size_t backward_gated_workspace_bytes(int variant, int B, int T, int H, int dk, int dv);
+hipError_t launch_backward_gated(const BwdArgs& a, hipStream_t stream);
 
 // Token-by-token recurrence; one workgroup per (b, h) covering all d_v
 // columns.  Also the decode step (T = 1, S_T == S0, p_T == p0 in place).

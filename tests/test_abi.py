@@ -400,3 +400,17 @@ def test_gated_serving_entry_points_refuse_grouped_noise_before_any_launch(lib):
                                         128, 128, None, None, f(), f(), f(), None, 0) == kdn.KDN_ERR_UNSUPPORTED
     assert lib.kdn_step_gated(f(), f(), f(), f(), f(), f(), 128.0, 0, 1, 0, 3, 128, 128, f(), f(), f(),
                               None) == kdn.KDN_OK  # empty batch: nothing to launch
+
+
+def test_gated_backward_workspace_size_formula(lib):
+    # the adjoint's workspace, then fp32 q, k, v, dO, alpha, omega, r, each
+    # rounded up to 256 bytes; none for grouped noise
+    base = kdn.backward_workspace_size(2, 33, 2, 128, 64)
+    r256 = lambda n: (n + 255) // 256 * 256
+    toks = 2 * 33 * 2
+    assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64) == (
+        r256(base) + 2 * r256(toks * 128 * 4) + 2 * r256(toks * 64 * 4) + 2 * r256(toks * 128 * 4) + r256(toks * 4))
+    assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64, "isotropic") == (
+        r256(base) + 2 * r256(toks * 128 * 4) + 2 * r256(toks * 64 * 4) + 3 * r256(toks * 4))
+    assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64, "grouped") == 0
+    assert kdn.backward_gated_workspace_size(0, 33, 2, 128, 64) == 0
