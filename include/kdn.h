@@ -91,12 +91,15 @@ enum kdn_status {
  * hold and the recurrent kernel otherwise, and an explicit KDN_ALGO_CHUNKED*
  * call outside them returns KDN_ERR_UNSUPPORTED.  One chunked workgroup
  * handles one (batch, head) pair and 64 value columns, or 32 when that
- * leaves more than half of the GPU's 256 compute units idle (AUTO and
- * CHUNKED choose; _WIDE and _NARROW force a width).  The chunked form divides
- * by the product of the decays over up to 32 tokens of a chunk: it needs every
- * alpha >= 0.07 (kdn_forward_gated: z_alpha >= -2.6), or that product
- * underflows and the outputs overflow; the recurrent algorithm has no such
- * bound. */
+ * leaves more than half of the device's compute units idle (AUTO and
+ * CHUNKED choose; _WIDE and _NARROW force a width).  Both algorithms are
+ * valid for every 0 < alpha <= 1.  The chunked form scales its matrix
+ * operands by the decay over at most one half-chunk (16 tokens); a chunk
+ * whose half-chunk decay falls below 2^-96 on some channel (a geometric mean
+ * below about 0.015 per token) is outside that form, and its workgroup
+ * finishes the sequence with the token recurrence from that chunk on: same
+ * results, slower for that (batch, head) pair.  The chunked form's operand
+ * scaling leaves 2^31 of headroom for |q|, |k| and p_hat |k|. */
 enum kdn_algo {
     KDN_ALGO_AUTO = 0,      /* the library picks (chunked when available) */
     KDN_ALGO_RECURRENT = 1, /* token-by-token recurrence, state in registers */

@@ -10,21 +10,36 @@
 //   p = p_hat / (1 + (mu / r) k^2 p_hat)
 //
 // Chunk form (our derivation from those steps).  The sequence is cut into
-// chunks of L = 32 tokens.  Inside a chunk let g_t be the cumulative decay
-// prod_{s<=t} alpha_s (per key channel), kappa'_t = p_hat_t * k_t the gain
-// numerator and d_t = r_t + sum_i p_hat_t,i k_t,i^2 its denominator.  With
-//   Kt_t = k_t g_t,  Qt_t = q_t g_t,  Kh_t = kappa'_t / g_t
-// and Dn_t = (v_t - (diag(alpha_t) S_{t-1})^T k_t) / d_t, the chunk's writes
-// satisfy
-//   M Dn = V - Kt S_c,        M = diag(r) + tril(Kt Kh^T)  (diagonal included:
+// chunks of L = 32 tokens.  Inside a chunk the decay from token s to a later
+// token t is prod_{s<u<=t} alpha_u (per key channel).  It is factored as
+// rho_t / rho_s with rho referenced to the chunk's midpoint (between tokens
+// 15 and 16): with g_t = prod_{u<=t} alpha_u from the chunk start,
+//   rho_t = g_t / g_15 (t <= 15),   rho_t = prod_{16<=u<=t} alpha_u (t >= 16),
+// so rho_t >= 1 in the first half and <= 1 in the second, and no factor spans
+// more than one 16-token half.  With kappa'_t = p_hat_t * k_t the gain
+// numerator, d_t = r_t + sum_i p_hat_t,i k_t,i^2 its denominator,
+//   Kt_t = k_t rho_t,  Qt_t = q_t rho_t,  Kh_t = kappa'_t / rho_t,
+//   Sg = diag(g_15) S_c,  Dn_t = (v_t - (diag(alpha_t) S_{t-1})^T k_t) / d_t,
+// the chunk's writes satisfy
+//   M Dn = V - Kt Sg,        M = diag(r) + tril(Kt Kh^T)  (diagonal included:
 //                                                        M_tt = d_t)
-//   O    = Qt S_c + tril(Qt Kh^T) Dn
-//   S_{c+1} = diag(g_L) (S_c + Kh^T Dn)
+//   O    = Qt Sg + tril(Qt Kh^T) Dn
+//   S_{c+1} = diag(gb_31) (Sg + Kh^T Dn),   gb_31 = prod_{16<=u<=31} alpha_u
 // which is the token recurrence rewritten exactly.  M is lower triangular;
 // its two 16 x 16 diagonal blocks are inverted in fp32 and the solve is a
 // two-step block substitution on MFMA.  Operands are bf16 with fp32
 // accumulation; S, p and every scalar recurrence stay fp32.
 //
+// Range.  The largest factor is 1 / (the decay over one half-chunk), on
+// either side, and every product used (t >= s) is at most |k| |kappa'|.  A
+// chunk whose half-chunk decays g_15 or gb_31 fall below 2^-96 on some
+// channel is outside this form's range: the chain flags it, every role stops
+// after the chunk before it, and the workgroup finishes its sequence with the
+// token recurrence (kdn_recurrent_core.h) from that chunk on, from the state
+// the chunked form carried to it.  Results are then exact for every
+// 0 < alpha <= 1, and the chunked form covers decays down to a geometric mean
+// of about 2^-6 per token (alpha ~ 0.015).
+
 // The uncertainty recurrence is a Mobius map of p (summary page, step 5):
 // p_t = (a p + w) / (u a p + 1 + u w) with a = alpha^2, w = omega, u = mu k^2 / r.
 //  - Diagonal variant: 128 independent channels per head fill a wave's lanes,
@@ -54,9 +69,12 @@
 // VALU work overlaps the MFMA work of the other roles.
 #include "kdn_gates.h"
 #include "kdn_internal.h"
+#include "kdn_recurrent_core.h"
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <climits>
 #include <cstddef>
 #include <cstdint>
 #include <utility>
@@ -173,7 +191,10 @@ struct Smem {
     alignas(16) bf16_t RW[2][L * DK];
     alignas(16) bf16_t GQ[2][L * DK];    // g_t,i (diagonal variant)  [t / 8][i][t % 8]
     alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
-    alignas(16) float gL[3][DK];         // g at the chunk end, fp32 (ring of three chunks)
+    alignas(16) float gL[3][DK];         // gb_31, the second half's decay, fp32 (ring of three chunks)
+    alignas(16) float g15[3][DK];        // g_15, the first half's decay, fp32 (ring of three chunks)
+    alignas(16) float fL[3][DK];         // gb_31 of chunk c times g_15 of chunk c + 1 (slot c % 3)
+    int fsub[3][2];                      // fL of slot c % 3 is below 2^-124 on some channel (per chain wave)
     alignas(16) bf16_t Kh[L * DK];       // kappa'_t / g_t    [t][perm32(i)], swizzled (read in the same iteration)
     alignas(16) bf16_t Kn[2][L * DK];    // -k_t g_t           [t][perm32(i)], swizzled
     alignas(16) bf16_t Qt[2][L * DK];    //  q_t g_t
@@ -187,6 +208,23 @@ struct Smem {
     alignas(16) float gs[2][L];          // g_t (isotropic, scalar)
     alignas(16) float Md[NT * 256];      // M's diagonal blocks, column-major [a][s][t] (fp32)
     alignas(16) float Wi[NT][2][64];     // inverses of their 8x8 diagonal sub-blocks, column-major
+    int bad;                             // first chunk outside the chunked form's range (INT_MAX: none)
+};
+
+// Smallest half-chunk decay the chunked form accepts (see the range note at
+// the top): factors up to 2^96 leave 2^31 of headroom below the bf16 / fp32
+// maximum for |k|, |q| and |kappa'|.
+constexpr float kRangeMin = 0x1p-96f;
+
+// After the chunked roles stop, the start of the LDS block (the chain's raw
+// tiles, idle by then) holds the hand-off to the token recurrence: the memory
+// of the workgroup's columns, the uncertainty, and the recurrence's per-wave
+// staging slices.
+template <int DK>
+struct Handoff {
+    float S[DK][64];
+    float p[DK];
+    float4 chan[2][DK];
 };
 
 struct Args {
@@ -380,8 +418,12 @@ __device__ __forceinline__ void chain_read16(ChainIn& in, uint32_t addr) {
 #undef KDN_OUT8
 #undef KDN_IMM16
 
-// tokens [T0, T1) of chunk buffer BUF (and KhQ slot gring) with nvalid real tokens; p carries
-// across chunks, g restarts at every chunk.  Padding tokens (t >= nvalid) act
+// tokens [T0, T1) of chunk buffer BUF (and KhQ slot gring) with nvalid real
+// tokens; p carries across chunks.  g restarts at each half: the first half
+// (T0 = 0) forms g_t from the chunk start and stores g_15; the second forms
+// gb_t = prod_{16<=u<=t} alpha_u and stores gb_31.  Kh = kappa' / rho: in the
+// first half kappa' times the reverse product prod_{t<u<=15} alpha_u (no
+// reciprocal), in the second kappa' / gb_t.  Padding tokens (t >= nvalid) act
 // as alpha = 1, omega = 0, k = 0: they leave p and g unchanged and write zero
 // gain.
 template <int DK, int BUF, int T0, int T1, bool MASK, bool GATE>
@@ -389,6 +431,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
                                                int nvalid, int gring) {
     constexpr int buf = BUF;  // compile-time, so every LDS offset below is an immediate
     constexpr int NTOK = T1 - T0;
+    constexpr bool FIRST = T0 == 0;
     static_assert(NTOK == CHAIN_SLOTS, "one 16-token chain segment");
     // read phase: every LDS read of the token range is issued before the
     // recurrence starts (two waves per SIMD cannot hide LDS latency).  The raw
@@ -416,17 +459,25 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
             al[j] = __builtin_amdgcn_rcpf(1.f + ez[j]);
             w[j] = gate_softplus(w[j]);
         }
-    }
-#pragma unroll
-    for (int j = 0; j < NTOK; ++j) {
-        const int t = T0 + j;
         if (MASK) {
-            const bool ok = t < nvalid;
+            const bool ok = T0 + j < nvalid;
             kk[j] = ok ? kk[j] : 0.f;
             al[j] = ok ? al[j] : 1.f;
             w[j] = ok ? w[j] : 0.f;
             if (GATE) ez[j] = ok ? ez[j] : 0.f;
         }
+    }
+    // first half: hr[j] = prod_{j<u<16} alpha_u (independent of p, so these
+    // multiplies fill the recurrence's dependency gaps)
+    float hr[NTOK];
+    if (FIRST) {
+        hr[NTOK - 1] = 1.f;
+#pragma unroll
+        for (int j = NTOK - 2; j >= 0; --j) hr[j] = hr[j + 1] * al[j + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        const int t = T0 + j;
         const float asq = al[j] * al[j];
         // the fewest instructions, rather than the shortest dependent path,
         // is what makes this loop fast (one wave per SIMD issues it)
@@ -435,16 +486,18 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         const float kph = kk[j] * ph;             // kappa' = p_hat k
         p = ph * __builtin_amdgcn_rcpf(fmaf(ck, kph, 1.f));  // 1 + (mu / r) k^2 p_hat
         g *= al[j];
-        // the gain in the chunk's scaled frame, kappa'_t / g_t, and g_t, as
-        // bf16 pairs of consecutive tokens.  Both go out in token groups, one
-        // wide store per group (a store per token and value would make LDS
-        // stores a third of this loop's instructions): g in groups of 8
-        // tokens, kappa'/g as Kh^T in the state's operand order, where the
-        // 8 positions of group P / 8 hold tokens 4 (P / 8) + 0..3 and
-        // 16 + 4 (P / 8) + 0..3, i.e. a 16-token segment fills one half of
-        // each of the four groups.
-        if (GATE) {
-            gi = fmaf(gi, ez[j], gi);  // 1 / g as the product of the (1 + e^-z): no reciprocal
+        // the gain in the chunk's midpoint frame, kappa'_t / rho_t, and the
+        // decay (g_t or gb_t), as bf16 pairs of consecutive tokens.  Both go
+        // out in token groups, one wide store per group (a store per token
+        // and value would make LDS stores a third of this loop's
+        // instructions): the decay in groups of 8 tokens, kappa' / rho as
+        // Kh^T in the state's operand order, where the 8 positions of group
+        // P / 8 hold tokens 4 (P / 8) + 0..3 and 16 + 4 (P / 8) + 0..3, i.e.
+        // a 16-token segment fills one half of each of the four groups.
+        if (FIRST) {
+            khv[j] = kph * hr[j];
+        } else if (GATE) {
+            gi = fmaf(gi, ez[j], gi);  // 1 / gb as the product of the (1 + e^-z): no reciprocal
             khv[j] = kph * gi;
         } else {
             khv[j] = kph * __builtin_amdgcn_rcpf(g);
@@ -460,8 +513,28 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         if ((j & 7) == 7)
             *reinterpret_cast<u4*>(&sm.GQ[buf][((T0 + j) / 8 * DK + i) * 8]) =
                 u4{gp[j / 2 - 3], gp[j / 2 - 2], gp[j / 2 - 1], gp[j / 2]};
+        if (t == L / 2 - 1) sm.g15[gring][i] = g;
         if (t == L - 1) sm.gL[gring][i] = g;
     }
+}
+
+// Chunk c is outside the chunked form's range when a half-chunk decay (the
+// g just formed by a chain) is below kRangeMin on any lane: the first such
+// chunk is recorded (every role reads it between barriers).
+__device__ __forceinline__ void flag_range(int* bad, float g, int c) {
+    if (__any(g < kRangeMin) && (threadIdx.x & 63) == 0) atomicMin(bad, c);
+}
+
+// The state carries Sg = diag(g_15) S.  Its per-chunk factor, from chunk c's
+// Sg to chunk c + 1's, is f = gb_31(c) g_15(c + 1) (one multiply per
+// element).  Where f would fall below the normal fp32 range the state applies
+// the two factors one after the other instead; wave w of a chain records that
+// for its channels in fsub[slot][w].
+template <int DK>
+__device__ __forceinline__ void store_fl(Smem<DK>& sm, int slot, int i, float f, int w) {
+    sm.fL[slot][i] = f;
+    const bool sub = __any(f < 0x1p-124f);
+    if ((threadIdx.x & 63) == 0) sm.fsub[slot][w] = sub ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -539,7 +612,8 @@ __device__ __forceinline__ void chain_iso_sums(const ChainIsoRegs<VAR>& X, float
 
 template <int DK, int VAR, bool GATE = false>
 __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<DK>& sm, int buf, float mu,
-                                              float& bprev, int nvalid, int gring, float n, float a2) {
+                                              float& bprev, int nvalid, int gring, float n, float a2, int c,
+                                              float& glprev, bool& flagged) {
     const int lane = threadIdx.x & 63;
     const bool ok = (lane & 31) < nvalid;
     float wz = bf1(bf16_t(X.w)), rz = bf1(bf16_t(X.rv));
@@ -579,7 +653,9 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<D
             m01 = y01 * s;
             m10 = y10 * s;
             m11 = 1.f;
-            g *= gg;
+            // the decays restart at token 16, the chunk's midpoint: lanes of
+            // the second half take no factor from the first
+            if ((lane & 31) < L / 2 || (lane & 31) - d >= L / 2) g *= gg;
         }
     }
     const float bt = (m00 * bprev + m01) / (m10 * bprev + m11);  // b after token t
@@ -587,13 +663,29 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<D
     if ((lane & 31) == 0) bbefore = bprev;
     if (lane < L) {
         sm.bh[buf][lane] = fmaf(asq, bbefore, w);
-        if (VAR == 1) sm.gs[buf][lane] = g;
         sm.rr[gring][lane] = rt;
     }
     bprev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt), L - 1));
-    if (VAR == 1) {  // (per-channel decay: g and g_L come from the decay chain)
+    if (VAR == 1) {  // (per-channel decay: the decays come from the decay chain)
+        // rho_t = g_t / g_15 in the first half, gb_t in the second
+        const float g15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L / 2 - 1));
         const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
-        for (int i = lane; i < DK; i += 64) sm.gL[gring][i] = gl;
+        if (lane < L) sm.gs[buf][lane] = (lane < L / 2) ? g * __builtin_amdgcn_rcpf(g15) : g;
+        // one decay per token: the state reads these three at index 0 (every
+        // lane stores the same value there)
+        sm.gL[gring][0] = gl;
+        sm.g15[gring][0] = g15;
+        if (c > 0) {
+            const float f = glprev * g15;
+            sm.fL[(c - 1) % 3][0] = f;
+            sm.fsub[(c - 1) % 3][0] = f < 0x1p-124f ? 1 : 0;
+        }
+        // the only chain that flags in this variant: the first flag stands
+        if ((g15 < kRangeMin || gl < kRangeMin) && !flagged) {
+            sm.bad = c;
+            flagged = true;
+        }
+        glprev = gl;
     }
 }
 
@@ -619,12 +711,15 @@ __device__ __forceinline__ void chain_decay_load(DecayRegs<DK>& X, const Args& a
     }
 }
 
-// g_t,i = prod_{s <= t} alpha_s,i for the chunk's tokens [T0, T1) (padding
-// tokens: alpha = 1), carried in g across the two calls of a chunk; stored as
-// the diagonal variant's chain stores it (8-token groups), g_L at the end
+// The cumulative decays of the chunk's tokens [T0, T1) (padding tokens:
+// alpha = 1): g_t,i = prod_{s <= t} alpha_s,i in the first half, gb_t,i =
+// prod_{16 <= s <= t} alpha_s,i in the second (g restarts at 1 between the
+// two calls), stored as the diagonal variant's chain stores them (8-token
+// groups), g_15 and gb_31 at the ends of the halves; a half-chunk decay below
+// the chunked form's range flags chunk c
 template <int DK, int T0, int T1, bool MASK, bool GATE = false>
 __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>& sm, int buf, int nvalid,
-                                                int gring, float (&g)[DK / 64]) {
+                                                int gring, float (&g)[DK / 64], int c, float (&gprev)[DK / 64]) {
     constexpr int CPL = DK / 64;
     const int i0 = CPL * (threadIdx.x & 63);
     float gv[CPL][2];
@@ -644,9 +739,24 @@ __device__ __forceinline__ void chain_decay_run(const DecayRegs<DK>& X, Smem<DK>
                     u4{gp[cc][0], gp[cc][1], gp[cc][2], gp[cc][3]};
         }
     }
-    if (T1 == L)
+    float gmin = g[0], fmin = 1.f;
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) sm.gL[gring][i0 + cc] = g[cc];
+    for (int cc = 0; cc < CPL; ++cc) {
+        if (T1 == L) {
+            sm.gL[gring][i0 + cc] = g[cc];
+            gprev[cc] = g[cc];
+        } else {
+            sm.g15[gring][i0 + cc] = g[cc];
+            if (c > 0) sm.fL[(c - 1) % 3][i0 + cc] = gprev[cc] * g[cc];
+            fmin = fminf(fmin, gprev[cc] * g[cc]);
+        }
+        gmin = fminf(gmin, g[cc]);
+    }
+    if (T1 != L && c > 0) {
+        const bool sub = __any(fmin < 0x1p-124f);
+        if ((threadIdx.x & 63) == 0) sm.fsub[(c - 1) % 3][0] = sm.fsub[(c - 1) % 3][1] = sub ? 1 : 0;
+    }
+    flag_range(&sm.bad, gmin, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -714,6 +824,12 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
                         &sm.KhQ[kslot][(((2 * f + h) & 3) * DK + i0 + cc) * 8 + hq]);
         }
     }
+    // per-channel decays (diagonal and per-channel-decay forms): the chain
+    // stores g_t in the first half and gb_t in the second; rho_t is g_t / g_15
+    // in the first half (waves f = 0, 1) and gb_t in the second
+    float rg[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) rg[cc] = (VAR != 1 && f < 2) ? __builtin_amdgcn_rcpf(sm.g15[kslot][i0 + cc]) : 1.f;
     uint32_t kw4[4];  // Kh^T staging (isotropic): the bf16 pairs (DK = 128) or values of 4 tokens
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -735,19 +851,19 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             for (int c = 0; c < CPL; ++c) g[c] = gsv[tt];
             khw = CPL == 2 ? pack2(kk[0] * sc, kk[CPL - 1] * sc) : uint32_t(to_bf(kk[0] * sc));
         } else if (VAR == 2) {
-            // g_t per channel from the decay chain; Kh = b_hat_t k / g_t
+            // rho_t per channel from the decay chain; Kh = b_hat_t k / rho_t
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
-                g[cc] = (tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1]);
+                g[cc] = ((tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1])) * rg[cc];
             const float k0 = kk[0] * (bhv[tt] * __builtin_amdgcn_rcpf(g[0]));
             khw = CPL == 2 ? pack2(k0, kk[CPL - 1] * (bhv[tt] * __builtin_amdgcn_rcpf(g[CPL - 1])))
                            : uint32_t(to_bf(k0));
         } else {
-            // kappa'_t / g_t and g_t from the chain's grouped stores
+            // kappa'_t / rho_t and rho_t from the chain's grouped stores
             const int h = tt >> 2, u = tt & 3;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
-                g[cc] = (tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1]);
+                g[cc] = ((tt & 1) ? bf_hi(gq[cc][tt >> 1]) : bf_lo(gq[cc][tt >> 1])) * rg[cc];
             if (CPL == 2)
                 khw = __builtin_amdgcn_perm(kq[1][h][u >> 1], kq[0][h][u >> 1], (u & 1) ? 0x07060302u : 0x05040100u);
             else
@@ -956,6 +1072,7 @@ template <int DK, int NCT>
 // Rows of a tail chunk past the sequence end need no masking here: their v
 // rows repeat the last token (finite), their Kt and Kh are zero, so their Dn
 // reaches neither S nor any stored output row.
+// S holds Sg = diag(g_15) S_c of this chunk (fp32), Sb its bf16 operands.
 __device__ __forceinline__ void state_seg1(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, int cw, int vslot) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
@@ -1009,9 +1126,29 @@ __device__ __forceinline__ void state_seg1(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
     }
 }
 
-template <int DK, int NCT>
+// S <- diag(g_15) S with g_15 of the chunk in ring slot `slot`
+// (SC: one decay per token, the factor sits at index 0)
+template <int DK, int NCT, bool SC>
+__device__ __forceinline__ void state_scale(StateAcc<DK, NCT>& st, Smem<DK>& sm, int slot) {
+    const int g4 = ((threadIdx.x & 63) >> 4) * 4;
+    const float g0 = SC ? sm.g15[slot][0] : 0.f;
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+        const f4 gh = SC ? f4{g0, g0, g0, g0} : *reinterpret_cast<const f4*>(&sm.g15[slot][16 * it + g4]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.S[it][ct][e] *= gh[e];
+    }
+}
+
+// The update's factor (mode): 0 gb_31 (S itself leaves: the last chunk, or
+// the next one is outside the chunked form's range), 1 fL (the next chunk's
+// Sg in one multiply), 2 gb_31 then g_15 of the next chunk (fL would leave
+// the normal fp32 range).  SC: one decay per token, factors at index 0.
+template <int DK, int NCT, bool SC>
 __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
-                                           int h, int colb, int c) {
+                                           int h, int colb, int c, int mode) {
     const int gring = c % 3;
     const bool full = (c + 1) * L <= a.T;
     const int lane = threadIdx.x & 63;
@@ -1024,7 +1161,12 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
         akh[it] = *reinterpret_cast<const b8*>(&sm.KhQ[gring][((lane >> 4) * DK + 16 * it + n) * 8]);
-        glv[it] = *reinterpret_cast<const f4*>(&sm.gL[gring][16 * it + g4]);
+        if (!SC) glv[it] = *reinterpret_cast<const f4*>(mode == 1 ? &sm.fL[gring][16 * it + g4] : &sm.gL[gring][16 * it + g4]);
+    }
+    if (SC) {
+        const float g0 = mode == 1 ? sm.fL[gring][0] : sm.gL[gring][0];
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it) glv[it] = f4{g0, g0, g0, g0};
     }
     const b8* Db = st.Db;
     // outputs, transposed: lane (n, g4) holds value columns g4 .. g4 + 3 of
@@ -1041,7 +1183,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
         }
         orow += ostep;
     }
-    // S <- diag(g_L) (S + Kh^T Dn)
+    // S <- diag(gb_31) (Sg + Kh^T Dn), and the next chunk's Sg
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
 #pragma unroll
@@ -1052,6 +1194,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
             st.S[it][ct] = s;
         }
     }
+    if (mode == 2) state_scale<DK, NCT, SC>(st, sm, (c + 1) % 3);
     pack_state<DK, NCT>(st);  // operands of the next chunk's first segment
 }
 
@@ -1155,10 +1298,24 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         const int a = (e >> 6) & 1, tt = (e >> 3) & 7, ss = 8 + (e & 7);
         sm.Td[bb][a * 256 + tt * 16 + ss] = 0;
     }
+    if (threadIdx.x == 0) sm.bad = INT_MAX;
+    if (threadIdx.x < 6) sm.fsub[threadIdx.x >> 1][threadIdx.x & 1] = 0;
     vm_wait<0>();  // chunk 0's tiles and r have landed
     if (VAR == 0 && is_form && fwave == 3) chain_r_store<DK, GATE>(sm, 0, r0, min(L, a.T), a.mu);
     bar();
 
+    // Range flags.  A chain flags chunk c (sm.bad, the smallest such c)
+    // during iteration c when a half-chunk decay leaves the chunked form's
+    // range.  The roles still run every iteration (the chunks from bad on
+    // compute values nobody stores); the state waves skip chunks from bad on,
+    // so their S stays the state at chunk bad's start, and the chains keep the
+    // uncertainty at that start.  After the loop every wave reads the same
+    // sm.bad; if it is set, the workgroup finishes the sequence with the token
+    // recurrence from chunk bad on (below).
+    int bad_seen = INT_MAX;
+    // chain: the uncertainty at the start of the last two chunks, and at the
+    // start of the first flagged chunk (diagonal: per lane)
+    float pst[2] = {0.f, 0.f}, psave = 0.f;
     if (wave == 0 || wave == 1) {
         // ---------------- chain ----------------
         if (VAR == 0) {
@@ -1174,18 +1331,28 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             ChainIn in;
 #pragma unroll
             for (int j = 0; j < 3 * CHAIN_SLOTS; ++j) in.x[j] = 0u;
+            float gprev = 1.f;  // gb_31 of the previous chunk
             auto step = [&](auto bufc, int c) {
                 constexpr int BUF = decltype(bufc)::value;
                 const int nvalid = min(L, a.T - c * L);
+                bad_seen = sm.bad;  // flags of chunks before c
+                if (bad_seen == c - 1) psave = pst[BUF ^ 1];
+                pst[BUF] = p;
                 float g = 1.f, gi = 1.f;
                 if (active && c < nchunks) {
                     if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
                     else chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, true, GATE>(sm, in, i, p, g, gi, nvalid, c % 3);
+                    flag_range(&sm.bad, g, c);
+                    if (c > 0) store_fl(sm, (c - 1) % 3, i, gprev * g, wave);
                 }
                 bar();
+                g = 1.f;
+                gi = 1.f;
                 if (active && c < nchunks) {
                     if (nvalid == L) chain_diag_run<DK, BUF, CHAIN_SPLIT, L, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
                     else chain_diag_run<DK, BUF, CHAIN_SPLIT, L, true, GATE>(sm, in, i, p, g, gi, nvalid, c % 3);
+                    flag_range(&sm.bad, g, c);
+                    gprev = g;
                 }
                 bar();
             };
@@ -1193,12 +1360,16 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 step(IntC<0>{}, c);
                 step(IntC<1>{}, c + 1);
             }
-            if (active && (GR || tile == 0)) a.p_T[pidx] = p;
+            bad_seen = sm.bad;
+            if (bad_seen >= nchunks && active && (GR || tile == 0)) a.p_T[pidx] = p;
         } else if (wave == 1) {
             // the per-channel decays (isotropic variant with per-channel
             // decay; otherwise this wave only keeps the barrier count)
             DecayRegs<DK> A, B;
             if (VAR == 2) chain_decay_load<DK>(A, a, b, h, 0, nchunks);
+            float gprev[DK / 64];
+#pragma unroll
+            for (int cc = 0; cc < DK / 64; ++cc) gprev[cc] = 1.f;
             for (int it = 0; it < nit; it += 2) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -1214,19 +1385,22 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     for (int cc = 0; cc < DK / 64; ++cc) g[cc] = 1.f;
                     if (VAR == 2) {
                         if (c < nchunks) {
-                            if (nvalid == L) chain_decay_run<DK, 0, L / 2, false, GATE>(X, sm, c & 1, L, c % 3, g);
-                            else chain_decay_run<DK, 0, L / 2, true, GATE>(X, sm, c & 1, nvalid, c % 3, g);
+                            if (nvalid == L) chain_decay_run<DK, 0, L / 2, false, GATE>(X, sm, c & 1, L, c % 3, g, c, gprev);
+                            else chain_decay_run<DK, 0, L / 2, true, GATE>(X, sm, c & 1, nvalid, c % 3, g, c, gprev);
                         }
                         chain_decay_load<DK>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
+#pragma unroll
+                    for (int cc = 0; cc < DK / 64; ++cc) g[cc] = 1.f;
                     if (VAR == 2 && c < nchunks) {
-                        if (nvalid == L) chain_decay_run<DK, L / 2, L, false, GATE>(X, sm, c & 1, L, c % 3, g);
-                        else chain_decay_run<DK, L / 2, L, true, GATE>(X, sm, c & 1, nvalid, c % 3, g);
+                        if (nvalid == L) chain_decay_run<DK, L / 2, L, false, GATE>(X, sm, c & 1, L, c % 3, g, c, gprev);
+                        else chain_decay_run<DK, L / 2, L, true, GATE>(X, sm, c & 1, nvalid, c % 3, g, c, gprev);
                     }
                     bar();
                 }
             }
+            bad_seen = sm.bad;
         } else {
             float bprev = a.p0 ? a.p0[unit] : a.c0[h];
             settle(bprev);
@@ -1234,7 +1408,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             chain_iso_load<DK, VAR>(A, a, b, h, 0, nchunks);
             // the row sums of the next chunk are formed in the second segment
             // (this wave's idle one), from the registers just loaded
-            float n = 0.f, a2 = 1.f;
+            float n = 0.f, a2 = 1.f, glprev = 1.f;
+            bool flagged = false;
             chain_iso_sums<DK, VAR, GATE>(A, n, a2);
             for (int it = 0; it < nit; it += 2) {
 #pragma unroll
@@ -1242,6 +1417,13 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     ChainIsoRegs<VAR>& X = half ? B : A;
                     ChainIsoRegs<VAR>& Y = half ? A : B;
                     const int c = it + half;
+                    if (VAR == 2) {
+                        bad_seen = sm.bad;  // the decay chain's flags of chunks before c
+                        if (bad_seen == c - 1) psave = pst[half ^ 1];
+                    } else if (!flagged) {
+                        psave = bprev;  // this chain flags: keep the start of the last unflagged chunk
+                    }
+                    pst[half] = bprev;
                     {
                         // the next chunk's loads go out after this chunk's
                         // registers are consumed: issued earlier, their
@@ -1249,7 +1431,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                         // loads still in flight, and the compiler would wait
                         // for those loads (a full memory round trip) first
                         if (c < nchunks)
-                            chain_iso_run<DK, VAR, GATE>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3, n, a2);
+                            chain_iso_run<DK, VAR, GATE>(X, sm, c & 1, a.mu, bprev, min(L, a.T - c * L), c % 3, n, a2,
+                                                         c, glprev, flagged);
                         chain_iso_load<DK, VAR>(Y, a, b, h, c + 1, nchunks);
                     }
                     bar();
@@ -1257,7 +1440,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     bar();
                 }
             }
-            if (lane == 0 && tile == 0) a.p_T[unit] = bprev;
+            bad_seen = sm.bad;
+            if (bad_seen >= nchunks && lane == 0 && tile == 0) a.p_T[unit] = bprev;
         }
     } else if (is_state_wave(wave)) {
         // ---------------- state ----------------
@@ -1277,13 +1461,33 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) settle(st.S[it][ct]);  // S0 is ready before the loop
-        pack_state<DK, NCT>(st);
-        for (int it = 0; it < nit; ++it) {
-            // chunk it's v is issued at iteration it, waited for at iteration
-            // it + 1 and consumed at iteration it + 2 (ring slot it % 3)
-            const int c = it - 2;  // chunk consumed at this iteration
+        // Chunk it's v is issued at iteration it, waited for at iteration
+        // it + 1 and consumed at iteration it + 2 (ring slot it % 3).
+        // Iterations 0 and 1 consume nothing; at iteration 1 the chain has
+        // stored chunk 0's g_15, and S0 becomes chunk 0's Sg.
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            bad_seen = sm.bad;
             state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
-            if (c >= 0 && c < nchunks) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
+            vm_wait<NCT>();
+            bar();
+            if (VAR == 0) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
+            if (it == 1) {
+                if (0 < bad_seen) state_scale<DK, NCT, VAR == 1>(st, sm, 0);
+                pack_state<DK, NCT>(st);
+            }
+            bar();
+        }
+        for (int it = 2; it < nit; ++it) {
+            // Chunks from the first one outside the chunked form's range on
+            // are skipped (its flag is visible since iteration c + 1): S then
+            // stays the state at that chunk's start.
+            const int c = it - 2;  // chunk consumed at this iteration
+            bad_seen = sm.bad;
+            const int fsub = sm.fsub[c % 3][0] | sm.fsub[c % 3][1];  // read early: its use is a segment away
+            const bool run = c < nchunks && c < bad_seen;
+            state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
             // everything but the NCT loads just issued has landed: the v of
             // chunk it - 1, the previous iteration's stores and chain rows
             vm_wait<NCT>();
@@ -1291,16 +1495,35 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             // rows 0..15 of the chain's chunk it + 2: the chain has read those
             // rows of chunk it (same buffer) before the barrier above
             if (VAR == 0) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
-            if (c >= 0 && c < nchunks) state_seg2<DK, NCT>(st, sm, c & 1, a, b, h, colb, c);
+            if (run) {
+                const bool next = c + 1 < nchunks && c + 1 < bad_seen;
+                const int mode = !next ? 0 : fsub ? 2 : 1;
+                state_seg2<DK, NCT, VAR == 1>(st, sm, c & 1, a, b, h, colb, c, mode);
+            }
             bar();
         }
+        bad_seen = sm.bad;
+        if (bad_seen >= nchunks) {
 #pragma unroll
-        for (int it = 0; it < DK / 16; ++it)
+            for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
+                    for (int e = 0; e < 4; ++e)
+                        a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
+        } else {
+            // hand-off: S_bad of this wave's columns
+            vm_wait<0>();
+            bar();
+            Handoff<DK>& hf = *reinterpret_cast<Handoff<DK>*>(&sm);
+#pragma unroll
+            for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        hf.S[16 * it + g4 + e][cw * (16 * NCT) + 16 * ct + n] = st.S[it][ct][e];
+        }
     } else {
         // ---------------- formation ----------------
         const int f = fwave;
@@ -1343,6 +1566,62 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 bar();
             }
         }
+        bad_seen = sm.bad;
+    }
+    if (bad_seen >= nchunks) {
+        vm_wait<0>();  // no direct copy may land after the workgroup's LDS is released
+        return;
+    }
+
+    // ---------------- hand-off to the token recurrence ----------------
+    // chunk bad_seen and the rest of the sequence, from the state the chunked
+    // form carried to the start of that chunk (the state waves wrote S above)
+    Handoff<DK>& hf = *reinterpret_cast<Handoff<DK>*>(&sm);
+    if (!is_state_wave(wave)) {
+        vm_wait<0>();  // direct copies still in flight land before their LDS is reused
+        bar();
+        if (wave < 2) {
+            if (VAR == 0) {
+                if (wave < DK / 64) hf.p[wave * 64 + lane] = psave;
+            } else if (wave == 0 && lane == 0) {
+                hf.p[0] = psave;
+            }
+        }
+    }
+    bar();
+    constexpr int NRW = DVTN / 32;  // recurrence waves: 32 value columns each
+    if (wave >= NRW) return;
+    constexpr int CPL = DK / 64, RPT = DK / 8;
+    const int cq = lane & 7, rg = lane >> 3;
+    const int lcol = wave * 32 + cq * 4;  // column within the workgroup's tile
+    float S[RPT][4], p[CPL], pb = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[m][j] = hf.S[rg + 8 * m][lcol + j];
+    if (VAR != 0) {
+        pb = hf.p[0];
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) p[c] = hf.p[lane + 64 * c];
+    }
+    const int col = tile * DVTN + lcol;  // column within the head
+    const rec::RecIO<bf16_t> io{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.o, a.mu, a.H, a.DV, h, a.tok0, col,
+                                ntile, tile, GATE};
+    rec::run_tokens<DK, VAR, bf16_t, GR>(io, S, p, pb, hf.chan[wave], bad_seen * L, a.T);
+    const size_t sbase = size_t(unit) * DK * a.DV;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        *reinterpret_cast<float4*>(a.S_T + sbase + size_t(rg + 8 * m) * a.DV + col) =
+            make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
+    if (wave == 0 && (GR || tile == 0)) {
+        if (VAR != 0) {
+            if (lane == 0) a.p_T[unit] = pb;
+        } else {
+            const size_t pb0 = (GR ? size_t(unit) * ntile + tile : size_t(unit)) * DK;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) a.p_T[pb0 + lane + 64 * c] = p[c];
+        }
     }
 }
 
@@ -1380,14 +1659,28 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Compute units of the current device (read once per device and cached; 256
+// on MI355X).  A failed query gives 256.
+long device_cus() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Narrow workgroups (32 value columns) when the 64-column tiling leaves more
-// than half of the 256 CUs without a workgroup: one workgroup holds one CU
-// (its LDS), and a chunk takes as long in either width, so twice the
+// than half of the device's CUs without a workgroup: one workgroup holds one
+// CU (its LDS), and a chunk takes as long in either width, so twice the
 // workgroups halve the time while they still fit on the CUs at once.
-constexpr long kNumCUs = 256;
 bool narrow_pays(const FwdArgs& a) {
     if (a.chunk_width != 0) return a.chunk_width == dvt_of<1>();
-    return long(a.B) * a.H * (a.dv / DVT) * 2 <= kNumCUs;
+    return long(a.B) * a.H * (a.dv / DVT) * 2 <= device_cus();
 }
 
 template <int DK>

@@ -8,10 +8,13 @@
 // v_rcp_f32, about 1 ulp each):
 //  - sigmoid(z) = 1 / (1 + 2^(-z log2 e)); for z < -88 the power is +inf and
 //    the result 0 (true value below 1e-38);
-//  - softplus(z) = max(z, 0) + ln 2 * log2(1 + 2^(-|z| log2 e)); the power lies
-//    in (0, 1], so nothing overflows.  Rounding 1 + e to fp32 costs at most
-//    about 6e-8 absolute (for z < -17 the result is max(z, 0) = 0 where the
-//    true value is below 4e-8).
+//  - softplus(z) = max(z, 0) + log(1 + e) with e = 2^(-|z| log2 e) in (0, 1],
+//    so nothing overflows.  log(1 + e) is ln 2 * log2(u) for u = fl(1 + e),
+//    plus the rounding error of u, e - (u - 1) (both differences are exact):
+//    log(u + d) = log(u) + d / u + O(d^2) and u = 1 + O(e), so adding d instead
+//    of d / u errs by about d e.  The result keeps fp32 relative accuracy for
+//    every z, including z << 0 where softplus(z) = e (1 - e / 2 + ...) and a
+//    bare log2(fl(1 + e)) would lose every digit below 2^-24.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,7 +31,9 @@ __device__ __forceinline__ float gate_sigmoid(float z) {
 
 __device__ __forceinline__ float gate_softplus(float z) {
     const float e = __builtin_amdgcn_exp2f(-kLog2E * fabsf(z));
-    return fmaf(kLn2, __builtin_amdgcn_logf(1.f + e), fmaxf(z, 0.f));
+    const float u = 1.f + e;
+    const float d = e - (u - 1.f);  // rounding error of u (exact)
+    return fmaf(kLn2, __builtin_amdgcn_logf(u), d + fmaxf(z, 0.f));
 }
 
 }  // namespace kdn

@@ -27,6 +27,19 @@ def rel_err(x, ref) -> float:
     return float(np.max(np.abs(x - ref)) / (scale if scale > 0 else 1.0))
 
 
+def p_rel_err(x, ref) -> float:
+    """Elementwise relative error of the uncertainty p, which is strictly
+    positive: max |x - ref| / ref.  Unlike the per-tensor metric it does not
+    hide errors on small channels."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    assert np.all(ref > 0), "the oracle's p must be positive"
+    return float(np.max(np.abs(x - ref) / ref))
+
+
 def to_dev(x: dict, dtype: str, device):
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32

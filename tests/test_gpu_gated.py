@@ -74,18 +74,25 @@ def test_gated_forward(dev, variant, algo, dtype, dk, dv, T):
 
 def test_gated_extreme_pre_activations(dev):
     # pre-activations far in the tails: softplus at 0 and at z, r at its floor
-    # 0.01, the decay saturated at 1; the decay's low end stays at the chunked
-    # kernel's bound (alpha >= 0.07, i.e. z_alpha >= -2.6)
+    # 0.01, the decay anywhere from saturated at 1 to about 1e-30 (the chunked
+    # kernel hands such chunks to the token recurrence)
     w = wl.Workload("gated_ext", "diagonal", "bf16", 2, 97, 2, 128, 128, 128.0, "uniform", 1601)
     x = wl.gated_inputs(w)
     rng = np.random.default_rng(5)
     for n, s in (("z_alpha", 30.0), ("z_omega", 30.0), ("z_r", 30.0)):
-        z = rng.normal(0.0, s, size=x[n].shape).astype(np.float32)
-        if n == "z_alpha":
-            z = np.maximum(z, np.float32(-2.5))
-        x[n] = wl.round_bf16(z)
+        x[n] = wl.round_bf16(rng.normal(0.0, s, size=x[n].shape).astype(np.float32))
     for algo in ("recurrent", "chunked"):
         check(f"gated/extreme/{algo}", run(dev, w, x, algo), oracle_gated(w, x), "bf16")
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
+def test_gated_small_process_noise_f32(dev, variant):
+    # z_omega ~ N(-10, 1): softplus(z) ~ e^z, where rounding 1 + e^z alone
+    # would lose the value; fp32 tolerance 1e-4 on every output
+    w = wl.Workload("gated_small_omega", variant, "f32", 2, 70, 2, 128, 128, 128.0, "uniform", 1606,
+                    omega_loc=-10.0)
+    x = wl.gated_inputs(w)
+    check(f"gated/small_omega/{variant}", run(dev, w, x, "recurrent"), oracle_gated(w, x), "f32")
 
 
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
