@@ -286,6 +286,31 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
                  const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
                  float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
                  void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * kdn_backward_noalloc -- kdn_backward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight training or serving loops,
+ * harnesses that forbid hipMalloc.  There is no workspace argument: the
+ * library's static device scratch of KDN_NOALLOC_SCRATCH_BYTES takes its
+ * place.  Each device holds its own copy of the scratch from the library's
+ * loading on that device until the process ends.  Same arguments (minus the
+ * workspace), checks, kernels and results (bit for bit) as kdn_backward.
+ *  - Sizes whose workspace (kdn_backward_workspace_size) exceeds the scratch
+ *    return KDN_ERR_WORKSPACE and launch nothing (dk = dv = 128, H = 16, B = 1:
+ *    T up to 1974; B = 2: T up to 840).
+ *  - Nothing is allocated: no hipMalloc, hipFree or allocating library call.
+ *  - Every call on one device shares that device's scratch and leaves its
+ *    contents behind (the kernels need none on entry).  Calls that overlap in
+ *    time on one device (two streams, two host threads) race on it and give
+ *    undefined results: order them.
+ */
+#define KDN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                         const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
+                         int H, int dk, int dv, const float* S0, const float* p0, const void* dO,
+                         const float* dS_T, const float* dp_T, float* dq, float* dk_out, float* dv_out,
+                         float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
+                         void* stream);
+
 /* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
  * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4
  * (recomputation checkpoints per 64-column tile, plus per-token partial sums

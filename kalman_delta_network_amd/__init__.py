@@ -50,8 +50,9 @@ def _p_shape(var, lead, dk, dv):
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
            "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated", "kdn_backward_gated",
-           "kdn_backward_gated_workspace_size",
-           "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated", "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
+           "kdn_backward_gated_workspace_size", "kdn_backward_noalloc",
+           "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated",
+           "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
 _lib = None
@@ -92,13 +93,14 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_workspace_size.argtypes = [I, I, I, I, I]
     lib.kdn_backward_workspace_size.restype = ctypes.c_size_t
     lib.kdn_backward_gated.argtypes = bwd + [P, ctypes.c_size_t, P]
+    lib.kdn_backward_noalloc.argtypes = bwd + [P]
     lib.kdn_backward_gated_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kdn_backward_gated_workspace_size.restype = ctypes.c_size_t
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
                lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version, lib.kdn_forward_gated,
                lib.kdn_validate_forward_gated, lib.kdn_forward_varlen_gated, lib.kdn_step_gated,
-               lib.kdn_backward_gated):
+               lib.kdn_backward_gated, lib.kdn_backward_noalloc):
         fn.restype = I
     lib.kdn_status_string.argtypes = [I]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -405,6 +407,21 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     return _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, False)
 
 
+def backward_noalloc(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
+                     S0=None, p0=None, out=None):
+    """``backward`` through kdn_backward_noalloc: the library's static device
+    scratch replaces the workspace, so the C call allocates nothing (sizes
+    whose workspace exceeds NOALLOC_SCRATCH_BYTES raise KDNError with
+    KDN_ERR_WORKSPACE).  ``out``: an optional dict of preallocated gradient
+    tensors (the keys ``backward`` returns); missing ones are allocated here,
+    by torch, before the call."""
+    return _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, None, False, noalloc=True,
+                     out=out)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # KDN_NOALLOC_SCRATCH_BYTES of kdn.h
+
+
 def backward_gated_workspace_size(B, T, H, dk, dv, variant="diagonal") -> int:
     """Bytes of device workspace kdn_backward_gated needs for these sizes."""
     return int(load_library().kdn_backward_gated_workspace_size(VARIANTS[variant], B, T, H, dk, dv))
@@ -421,7 +438,8 @@ def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, d
     return {("dz_" + n[1:] if n in ("dalpha", "domega", "dr") else n): t for n, t in g.items()}
 
 
-def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, gated):
+def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0, workspace, gated, noalloc=False,
+              out=None):
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
@@ -442,11 +460,23 @@ def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0,
         if t is not None:
             _need(t, name, shp, torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
-         "dv": torch.empty((B, T, H, dv), **f32), "dalpha": torch.empty(ashape, **f32),
-         "domega": torch.empty(wshape, **f32), "dr": torch.empty(rshape, **f32),
-         "dS0": torch.empty((B, H, dk, dv), **f32), "dp0": torch.empty(pshape, **f32),
-         "dc0": torch.empty((H,), **f32)}
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dalpha": ashape, "domega": wshape,
+              "dr": rshape, "dS0": (B, H, dk, dv), "dp0": pshape, "dc0": (H,)}
+    out = out or {}
+    g = {}
+    for n, shp in shapes.items():
+        if n in out:
+            _need(out[n], n, shp, torch.float32, dev)
+            g[n] = out[n]
+        else:
+            g[n] = torch.empty(shp, **f32)
+    if noalloc:
+        st = lib.kdn_backward_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0), float(mu), var, _dtype_code(q),
+            B, T, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T), _ptr(dp_T),
+            *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dp0", "dc0")), _stream(dev))
+        _check(st, "kdn_backward_noalloc")
+        return g
     need = backward_gated_workspace_size(B, T, H, dk, dv, variant) if gated else backward_workspace_size(B, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

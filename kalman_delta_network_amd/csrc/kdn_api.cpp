@@ -447,6 +447,31 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
     return hip_status(kdn::launch_backward(a, static_cast<hipStream_t>(stream)), "backward");
 }
 
+int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                         const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H,
+                         int dk, int dv, const float* S0, const float* p0, const void* dO, const float* dS_T,
+                         const float* dp_T, float* dq, float* dk_out, float* dv_out, float* dalpha, float* domega,
+                         float* dr, float* dS0, float* dp0, float* dc0, void* stream) {
+    // the checks of kdn_backward, with the static scratch standing for the
+    // workspace: its size first (no device access), then its address
+    int st = validate_common(variant, dtype, mu, dk, dv);
+    if (st != KDN_OK) return st;
+    if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
+    const size_t need = kdn::backward_workspace_bytes(B, T, H, dk, dv);
+    if (need > kdn::kNoallocScratchBytes)
+        return fail(KDN_ERR_WORKSPACE,
+                    "kdn_backward_noalloc: these sizes need %zu bytes of workspace, more than the %zu-byte static "
+                    "scratch (use kdn_backward with a workspace)", need, kdn::kNoallocScratchBytes);
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    void* scratch = nullptr;
+    if (need > 0 && int64_t(B) * H > 0) {
+        const hipError_t e = kdn::noalloc_scratch(&scratch);
+        if (e != hipSuccess) return fail(KDN_ERR_HIP, "kdn_backward_noalloc: device scratch: %s", hipGetErrorString(e));
+    }
+    return kdn_backward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, dO, dS_T, dp_T, dq,
+                        dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0, scratch, scratch ? need : 0, stream);
+}
+
 size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv) {
     if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || variant < 0 || variant > 2) return 0;
     return kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv);

@@ -83,6 +83,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 size_t backward_gated_workspace_bytes(int variant, int B, int T, int H, int dk, int dv);
 hipError_t launch_backward_gated(const BwdArgs& a, hipStream_t stream);
 
+// kdn_backward_noalloc: the workspace is a static device array of this many
+// bytes per device (kdn_noalloc.hip); noalloc_scratch() gives the current
+// device's copy (its address resolved once per device, nothing allocated).
+constexpr size_t kNoallocScratchBytes = size_t(256) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Token-by-token recurrence; one workgroup per (b, h) covering all d_v
 // columns.  Also the decode step (T = 1, S_T == S0, p_T == p0 in place).
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t stream);

@@ -414,3 +414,26 @@ def test_gated_backward_workspace_size_formula(lib):
         r256(base) + 2 * r256(toks * 128 * 4) + 2 * r256(toks * 64 * 4) + 3 * r256(toks * 4))
     assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64, "grouped") == 0
     assert kdn.backward_gated_workspace_size(0, 33, 2, 128, 64) == 0
+
+
+def test_noalloc_backward_host_checks_without_gpu(lib, monkeypatch):
+    # kdn_backward_noalloc: sizes whose workspace exceeds the static scratch are
+    # refused before any device access; with the launch fault hook the call
+    # reports the launch error (its remaining checks and the scratch need a GPU)
+    f = Fake()
+    big = bwd_args(f, lib, B=1, T=2048, H=16, dk=128, dv=128)
+    assert lib.kdn_backward_workspace_size(1, 2048, 16, 128, 128) > kdn.NOALLOC_SCRATCH_BYTES
+    noalloc = lambda a: lib.kdn_backward_noalloc(*_bwd_list(a)[:-2], None)
+    assert noalloc(big) == kdn.KDN_ERR_WORKSPACE
+    assert b"static scratch" in lib.kdn_last_error()
+    assert noalloc(bwd_args(f, lib, mu=-1.0)) == kdn.KDN_ERR_VALUE
+    assert noalloc(bwd_args(f, lib, dk=96)) == kdn.KDN_ERR_UNSUPPORTED
+    monkeypatch.setenv("KDN_FAULT", "launch")
+    assert noalloc(bwd_args(f, lib)) == kdn.KDN_ERR_HIP
+    assert b"KDN_FAULT" in lib.kdn_last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kdn.NOALLOC_SCRATCH_BYTES
