@@ -97,5 +97,9 @@ hipError_t launch_recurrent(const FwdArgs& a, hipStream_t stream);
 // for shapes it does not handle (the caller then reports KDN_ERR_UNSUPPORTED).
 bool chunked_supports(const FwdArgs& a);
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream);
+// Chunkwise forward of the isotropic variant (variant 1) on Gram matrices of
+// the raw keys (kdn_iso.hip); narrow = 32 value columns per workgroup, else 64.
+// Same preconditions as launch_chunked, and T > 0.
+hipError_t launch_iso(const FwdArgs& a, bool narrow, hipStream_t stream);
 
 }  // namespace kdn

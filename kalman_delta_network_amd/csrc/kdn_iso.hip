@@ -1,0 +1,714 @@
+// kdn_iso.hip -- chunkwise forward of the isotropic KDN variant on gfx950,
+// with the decay weights applied to Gram matrices of the raw keys.
+//
+// Method ("Kalman Delta Networks: Uncertainty-aware Associative Memory",
+// summary page, method steps 2-5 and the isotropic closing sentence).  Per
+// (batch, head), one uncertainty scalar b and scalar decay alpha_t per token:
+//   b_hat = alpha^2 b + omega / d_k;  kappa = k b_hat / (r + b_hat |k|^2)
+//   S = alpha S + kappa (v - alpha S^T k)^T;  o = S^T q
+//   b = b_hat / (1 + (mu / (d_k r)) |k|^2 b_hat)
+//
+// Chunk form (our derivation from those steps).  With chunks of L = 32 tokens,
+// G_t = sum_{u<=t in the chunk} log2 alpha_u, and Dn_t the innovation over its
+// gain denominator d_t = r_t + b_hat_t |k_t|^2, the token recurrence inside a
+// chunk is exactly
+//   M Dn = V - diag(2^G) K S_c,     M_ts = r_t [t = s] + b_hat_s 2^(G_t - G_s) (k_t . k_s)   (s <= t)
+//   O    = diag(2^G) Q S_c + P Dn,  P_ts = b_hat_s 2^(G_t - G_s) (q_t . k_s)                   (s <= t)
+//   S_{c+1} = 2^(G_L) S_c + K^T diag(w) Dn,   w_s = b_hat_s 2^(G_L - G_s)
+// Because the decay is one scalar per token, every decay factor lands on a
+// row or a column: the matrix cores take the raw bf16 k and q tiles (the Gram
+// matrices K K^T and Q K^T, K S_c, Q S_c, K^T Dn) and the weights are applied
+// in fp32 to 32 x 32 matrices and to rows.  Every weight used is
+// 2^(non-positive), so the form holds for every 0 < alpha <= 1 with nothing
+// to overflow (log2 alpha is floored at -150, below which 2^x is zero in
+// fp32 anyway).
+//
+// The memory is carried as S = Gamma S~ with a scalar Gamma in [2^-64, 1]:
+// the chunk's own decay goes into Gamma (and into the row weights of R and
+// O and the column weights of the update), so the state needs no per-chunk
+// rescale; only when Gamma would fall below 2^-64 is S~ multiplied through.
+//
+// Workgroup = one (batch, head) pair and 64 value columns (32 when the
+// 64-column tiling would leave more than half of the CUs idle), 8 waves:
+//   wave 0  scan:      the uncertainty scalar's Mobius maps over the chunk's
+//                      32 tokens (lane = token), composed as 2 x 2 matrix
+//                      products by an inclusive cross-lane scan on DPP row
+//                      shifts and a row broadcast; the log-decay prefix sums
+//                      the same way; per-token weights to LDS
+//   wave 1  Gram K K^T of the chunk (matrix cores), weighted into M's
+//           diagonal blocks and -M_10; then k^T of the previous chunk for
+//           the update's operand
+//   wave 2  inverses of M's diagonal blocks; the direct copies of the k and
+//           q tiles two chunks ahead
+//   wave 3  Gram Q K^T, weighted into P = tril(...)
+//   waves 4..7  state: 16 value columns each, S~ in registers (fp32)
+// Two workgroup barriers per iteration; a chunk is scanned and Gram-weighted
+// at iteration c, inverted and transposed at c + 1 and consumed by the state
+// at c + 2.
+#include "kdn_device.h"
+#include "kdn_gates.h"
+#include "kdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kdn {
+namespace {
+
+using namespace dev;
+
+constexpr int L = 32;          // tokens per chunk
+constexpr int NT = L / 16;     // 16-token tiles per chunk
+constexpr int NTHREADS = 512;  // 8 waves
+constexpr int PT = L + 8;      // pitch of the bf16 P rows
+constexpr int KR = 4;          // ring of k and q tiles (copied two chunks ahead, read until two chunks later)
+constexpr float kLogFloor = -150.f;  // log2 alpha below this: 2^x is zero in fp32
+constexpr float kFrameMin = 0x1p-64f;  // Gamma is kept at or above this
+
+template <int DK>
+struct IsoSmem {
+    alignas(16) bf16_t K[KR][L * DK];     // k tiles [t][sw(i)] (direct copies)
+    alignas(16) bf16_t Q[KR][L * DK];     // q tiles [t][sw(i)]
+    alignas(16) bf16_t KT[2][L * DK];     // k^T [P / 8][i][P % 8] with P = perm32(t): the update's A operand
+    alignas(16) bf16_t RV[3][4][L * 16];  // v tiles of the state waves (16 columns each), ring of three
+    alignas(16) float sc[4][4][L];        // per chunk (slot c % 4): r, b_hat, G, row weight 2^G Gamma_c
+    alignas(16) float ws[4][L];           // update column weights w_s / (the frame change), per chunk
+    alignas(16) float ch[4][4];           // per chunk: the C-input factor of the update (1 = none), Gamma_c
+    alignas(16) bf16_t P[3][L * PT];      // tril(P) [t][perm32(s)] (ring of three)
+    alignas(16) bf16_t Td[2][NT * 256];   // inverses of M's diagonal blocks [a][t][s]
+    alignas(16) bf16_t Mo[2][256];        // -M_10 [t][s]
+    alignas(16) float Md[NT * 256];       // M's diagonal blocks, column-major [a][s][t]
+    alignas(16) float Wi[NT][2][64];      // block-inverse scratch
+};
+
+struct IsoArgs {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const bf16_t* alpha;
+    const bf16_t* omega;
+    const bf16_t* r;
+    const float* c0;
+    float mu;
+    int T, H, DV, units;
+    const float* S0;
+    const float* p0;
+    bf16_t* o;
+    float* S_T;
+    float* p_T;
+    const int* cu;
+    const int* ord;
+    size_t tok0;
+};
+
+__device__ __forceinline__ size_t tokidx(const IsoArgs& a, int h, int t) {
+    return (a.tok0 + size_t(t)) * size_t(a.H) + size_t(h);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane steps on DPP (data moves inside a VALU instruction).  Within
+// each 16-lane row, row_shr:d takes lane i - d (lanes below d keep `old`);
+// row_bcast:15 with row mask 0b1010 gives rows 1 and 3 lane 15 of the row
+// below.  Lanes 0..31 and 32..63 are two copies of the same 32 tokens.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp(float old, float src) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, ROWMASK,
+                                                      0xf, false));
+}
+constexpr int kRowShr = 0x110;     // + shift
+constexpr int kRowBcast15 = 0x142;
+constexpr int kWaveShr1 = 0x138;
+
+// one level of the inclusive scan of 2 x 2 Mobius matrices (this x earlier,
+// renormalised so that m11 = 1) and of the log-decay sums
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void scan_level(float& m00, float& m01, float& m10, float& m11, float& g) {
+    const float x00 = dpp<CTRL, ROWMASK>(1.f, m00), x01 = dpp<CTRL, ROWMASK>(0.f, m01);
+    const float x10 = dpp<CTRL, ROWMASK>(0.f, m10), x11 = dpp<CTRL, ROWMASK>(1.f, m11);
+    const float xg = dpp<CTRL, ROWMASK>(0.f, g);
+    const float y00 = fmaf(m00, x00, m01 * x10), y01 = fmaf(m00, x01, m01 * x11);
+    const float y10 = fmaf(m10, x00, m11 * x10), y11 = fmaf(m10, x01, m11 * x11);
+    const float s = __builtin_amdgcn_rcpf(y11);
+    m00 = y00 * s;
+    m01 = y01 * s;
+    m10 = y10 * s;
+    m11 = 1.f;
+    g += xg;
+}
+
+// ---------------------------------------------------------------------------
+// scan wave: lane = token (lanes 32..63 help with |k|^2)
+// ---------------------------------------------------------------------------
+template <int DK>
+struct ScanRegs {
+    u4 kr[DK / 16];      // half a k row of token lane & 31
+    bf16_t al, w, rv;    // alpha, omega, r of token lane & 31
+};
+
+template <int DK>
+__device__ __forceinline__ void scan_load(ScanRegs<DK>& X, const IsoArgs& a, int h, int c, int nchunks) {
+    c = min(max(c, 0), nchunks - 1);
+    const int lane = threadIdx.x & 63;
+    const size_t e = tokidx(a, h, min(c * L + (lane & 31), a.T - 1));
+    const u4* src = reinterpret_cast<const u4*>(a.k + e * DK + (lane >> 5) * (DK / 2));
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m) X.kr[m] = src[m];
+    X.al = a.alpha[e];
+    X.w = a.omega[e];
+    X.rv = a.r[e];
+}
+
+template <int DK>
+__device__ __forceinline__ float scan_rowsum(const ScanRegs<DK>& X) {
+    float n = 0.f;
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = bf_lo(X.kr[m][e]), x1 = bf_hi(X.kr[m][e]);
+            n = fmaf(x0, x0, n);
+            n = fmaf(x1, x1, n);
+        }
+    return n + __shfl_xor(n, 32, 64);
+}
+
+// The scan of chunk c (slot c % 4): b_hat_t, G_t, the row weights 2^G_t Gamma
+// and the update's column weights and C-input factor for the frame S = Gamma S~.
+template <int DK, bool GATE>
+__device__ __forceinline__ void scan_run(const ScanRegs<DK>& X, IsoSmem<DK>& sm, int c, float n, float mu,
+                                         float& bprev, float& gam, int nvalid) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane & 31;
+    const bool ok = t < nvalid;
+    float az = bf1(X.al), wz = bf1(X.w), rz = bf1(X.rv);
+    float lg;  // log2 alpha
+    float al;
+    if (GATE) {
+        // alpha = 1 / (1 + e^-z): log2 alpha = -log2(1 + e^-z), exact also where alpha underflows
+        const float ez = __builtin_amdgcn_exp2f(-kLog2E * az);
+        al = __builtin_amdgcn_rcpf(1.f + ez);
+        lg = -__builtin_amdgcn_logf(1.f + ez);
+        wz = gate_softplus(wz);
+        rz = kGateRMin + gate_softplus(rz);
+    } else {
+        al = az;
+        lg = __builtin_amdgcn_logf(az);
+    }
+    lg = ok ? fmaxf(lg, kLogFloor) : 0.f;
+    al = ok ? al : 1.f;
+    const float asq = al * al;
+    const float w = ok ? wz * (1.f / float(DK)) : 0.f;
+    const float rt = ok ? rz : 1.f;
+    const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
+    // this token's Mobius matrix [[m00, m01], [m10, m11]], composed over the
+    // chunk's tokens by an inclusive scan; G by an inclusive sum
+    float m00 = asq, m01 = w, m10 = cn * asq, m11 = fmaf(cn, w, 1.f);
+    float g = lg;
+    scan_level<kRowShr + 1, 0xf>(m00, m01, m10, m11, g);
+    scan_level<kRowShr + 2, 0xf>(m00, m01, m10, m11, g);
+    scan_level<kRowShr + 4, 0xf>(m00, m01, m10, m11, g);
+    scan_level<kRowShr + 8, 0xf>(m00, m01, m10, m11, g);
+    scan_level<kRowBcast15, 0xa>(m00, m01, m10, m11, g);
+    const float bt = (m00 * bprev + m01) / (m10 * bprev + m11);  // b after token t
+    const float bbefore = dpp<kWaveShr1>(bprev, bt);              // b before token t (lane 0: bprev)
+    const float bh = ok ? fmaf(asq, bbefore, w) : 0.f;             // b_hat (padding tokens: no write)
+    const float gL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), L - 1));
+    // frame: S_c = gam S~_c.  After the chunk S_{c+1} = 2^G_L S_c + K^T diag(w) Dn.
+    // Either the frame absorbs the decay (gam' = gam 2^G_L >= 2^-64, S~ unchanged
+    // apart from the write, whose weights are w / gam'), or S~ takes the factor
+    // gam 2^G_L (C-input) and gam' = 1.
+    const float dL = __builtin_amdgcn_exp2f(gL);
+    const float gnext = gam * dL;
+    const bool absorb = gnext >= kFrameMin;
+    const float wcol = bh * __builtin_amdgcn_exp2f(gL - g);  // w_s
+    const int slot = c & 3;
+    if (lane < L) {
+        sm.sc[slot][0][lane] = rt;
+        sm.sc[slot][1][lane] = bh;
+        sm.sc[slot][2][lane] = g;
+        sm.sc[slot][3][lane] = __builtin_amdgcn_exp2f(g) * gam;  // row weight of R and O: 2^G_t Gamma_c
+        sm.ws[slot][lane] = absorb ? wcol * __builtin_amdgcn_rcpf(gnext) : wcol;
+    }
+    if (lane == 0) {
+        sm.ch[slot][0] = absorb ? 1.f : gnext;  // the update's C-input factor
+        sm.ch[slot][1] = gam;                   // the frame at the chunk's start
+        sm.ch[slot][2] = absorb ? gnext : 1.f;  // the frame after the chunk
+    }
+    gam = absorb ? gnext : 1.f;
+    bprev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt), L - 1));
+}
+
+// ---------------------------------------------------------------------------
+// direct copies of k, q tiles into LDS ([t][sw(i)]: lane slot P of the tile is
+// row P / NCH, 16-byte piece P % NCH of the swizzled row)
+// ---------------------------------------------------------------------------
+template <int DK>
+__device__ __forceinline__ void tile_issue(bf16_t* dst, const bf16_t* src, const IsoArgs& a, int h, int c,
+                                           int nchunks) {
+    c = min(max(c, 0), nchunks - 1);  // always the same number of copies (the waits count them)
+    constexpr int NCH = DK / 8;
+    const int lane = threadIdx.x & 63;
+    const int last = a.T - 1 - c * L;
+    const bf16_t* base = src + tokidx(a, h, c * L) * DK;
+    const uint32_t rs = uint32_t(a.H) * DK * 2;
+#pragma unroll
+    for (int m = 0; m < L * NCH / 64; ++m) {
+        const int pc = lane + 64 * m;
+        const int row = pc / NCH, slot = pc % NCH;
+        const int cg = (slot ^ row) & (NCH - 1);
+        const uint32_t off = uint32_t(min(row, last)) * rs + uint32_t(cg) * 16;
+        g2lds16(base, off, dst + m * 512);
+    }
+}
+template <int DK>
+constexpr int tile_copies() {
+    return L * (DK / 8) / 64;
+}
+
+// ---------------------------------------------------------------------------
+// Gram wave: the chunk's 32 x 32 products on the raw tiles, weighted
+// ---------------------------------------------------------------------------
+// acc[e] = (A B^T)[16 ta + g4 + e][16 tb + n] for row tiles ta, tb of A, B
+template <int DK>
+__device__ __forceinline__ f4 gram_tile(const bf16_t* A, const bf16_t* B, int ta, int tb) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, kg8 = (lane >> 4) * 8;
+    constexpr int KS = DK / 32;
+    b8 av[KS], bv[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        av[kk] = *reinterpret_cast<const b8*>(A + sw<DK>(16 * ta + n, 32 * kk + kg8));
+        bv[kk] = *reinterpret_cast<const b8*>(B + sw<DK>(16 * tb + n, 32 * kk + kg8));
+    }
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) acc = mfma32(av[kk], bv[kk], acc);
+    return acc;
+}
+
+// the pair weights b_hat_s 2^(G_t - G_s) of tile (ta, tb) for lane (rows
+// 16 ta + g4 + e, column 16 tb + n); zero above the diagonal
+template <int DK>
+__device__ __forceinline__ f4 pair_weights(const IsoSmem<DK>& sm, int slot, int ta, int tb) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    const int s = 16 * tb + n;
+    const float bs = sm.sc[slot][1][s], gs = sm.sc[slot][2][s];
+    const f4 gt = *reinterpret_cast<const f4*>(&sm.sc[slot][2][16 * ta + g4]);
+    f4 wv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ta + g4 + e;
+        wv[e] = t >= s ? bs * __builtin_amdgcn_exp2f(gt[e] - gs) : 0.f;
+    }
+    return wv;
+}
+
+// M's diagonal blocks (fp32, column-major) and -M_10 (bf16) of the chunk in slot `slot`
+template <int DK>
+__device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int mo) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    const bf16_t* K = sm.K[kslot];
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+        const f4 acc = gram_tile<DK>(K, K, a, a);
+        const f4 wv = pair_weights<DK>(sm, slot, a, a);
+        const f4 rv = *reinterpret_cast<const f4*>(&sm.sc[slot][0][16 * a + g4]);
+        f4 mv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mv[e] = fmaf(wv[e], acc[e], g4 + e == n ? rv[e] : 0.f);
+        *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;
+    }
+    const f4 acc = gram_tile<DK>(K, K, 1, 0);
+    const f4 wv = pair_weights<DK>(sm, slot, 1, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Mo[mo][(g4 + e) * 16 + n] = to_bf(-wv[e] * acc[e]);
+}
+
+// P = tril(weighted Q K^T) of the chunk, bf16 [t][perm32(s)]
+template <int DK>
+__device__ __forceinline__ void gram_p(IsoSmem<DK>& sm, int kslot, int slot, int pslot) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    const bf16_t* K = sm.K[kslot];
+    const bf16_t* Q = sm.Q[kslot];
+    const f4 a00 = gram_tile<DK>(Q, K, 0, 0), a10 = gram_tile<DK>(Q, K, 1, 0), a11 = gram_tile<DK>(Q, K, 1, 1);
+    const f4 w00 = pair_weights<DK>(sm, slot, 0, 0), w10 = pair_weights<DK>(sm, slot, 1, 0),
+             w11 = pair_weights<DK>(sm, slot, 1, 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sm.P[pslot][(g4 + e) * PT + perm32(n)] = to_bf(w00[e] * a00[e]);
+        sm.P[pslot][(16 + g4 + e) * PT + perm32(n)] = to_bf(w10[e] * a10[e]);
+        sm.P[pslot][(16 + g4 + e) * PT + perm32(16 + n)] = to_bf(w11[e] * a11[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// state: one wave = 16 value columns, S~ (d_k x 16 fp32) in registers
+// ---------------------------------------------------------------------------
+// Register row p of S~ (p = 16 it + g4 + e in the accumulator layout) holds
+// key channel chan_of(p): within each block of 32, rows 4g..4g+3 hold
+// channels 8g..8g+3 and rows 16+4g..16+4g+3 channels 8g+4..8g+7.  The bf16
+// operand built from rows {32kk + 4g + e, 32kk + 16 + 4g + e} then covers the
+// 8 consecutive channels 32kk + 8g.. that lane group g reads from a k or q
+// tile in natural order, and k^T is stored in the same row order.
+__device__ __forceinline__ int chan_of(int p) {
+    const int q = p & 31;
+    return (p & ~31) + (q < 16 ? 8 * (q >> 2) + (q & 3) : 8 * ((q - 16) >> 2) + 4 + (q & 3));
+}
+__device__ __forceinline__ int pos_of(int ch) {
+    const int j = ch & 7, g = (ch >> 3) & 3;
+    return (ch & ~31) + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+}
+// k^T of a chunk for the update's A operand, rows in the state's order:
+// lane (q = lane >> 4, channel group cg = lane & 15) transposes the 8 x 8
+// block of tokens {4q..4q+3, 16+4q..+3} and channels 8 cg .. 8 cg + 7
+// (DK = 64: lanes with cg < 8)
+template <int DK>
+__device__ __forceinline__ void transpose_k(bf16_t* KT, const bf16_t* K) {
+    const int lane = threadIdx.x & 63;
+    const int qg = lane >> 4, cg = lane & 15;
+    if (cg >= DK / 8) return;
+    u4 rw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = (j < 4 ? 4 * qg + j : 16 + 4 * qg + j - 4);
+        rw[j] = *reinterpret_cast<const u4*>(K + sw<DK>(t, 8 * cg));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+        const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+        u4 outv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) outv[m] = __builtin_amdgcn_perm(rw[2 * m + 1][cc >> 1], rw[2 * m][cc >> 1], sel);
+        *reinterpret_cast<u4*>(KT + (qg * DK + pos_of(8 * cg + cc)) * 8) = outv;
+    }
+}
+
+template <int DK>
+struct IsoState {
+    f4 S[DK / 16];    // rows 16 it + g4 + e, column n
+    b8 Sb[DK / 32];   // bf16 operands of S~
+};
+template <int DK>
+__device__ __forceinline__ void iso_pack(IsoState<DK>& st) {
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) st.Sb[kk] = pack8(st.S[2 * kk], st.S[2 * kk + 1]);
+}
+
+// v tile (32 tokens x 16 columns) of chunk c into ring slot c % 3: 64 pieces, one copy
+template <int DK>
+__device__ __forceinline__ void v_issue(IsoSmem<DK>& sm, const IsoArgs& a, int h, int col0, int sw_, int c,
+                                        int nchunks) {
+    c = min(max(c, 0), nchunks - 1);
+    const int lane = threadIdx.x & 63;
+    const int last = a.T - 1 - c * L;
+    const bf16_t* base = a.v + tokidx(a, h, c * L) * a.DV + col0;
+    const uint32_t rs = uint32_t(a.H) * uint32_t(a.DV) * 2;
+    const uint32_t off = uint32_t(min(lane >> 1, last)) * rs + uint32_t(lane & 1) * 16;
+    g2lds16(base, off, &sm.RV[c % 3][sw_][0]);
+}
+
+struct SegCarry {
+    f4 O[NT];  // (Q S)^T of the chunk, scaled: value column x token
+    b8 Db;     // Dn (bf16, B operand) for P Dn
+    b8 Dw;     // diag(w) Dn for the update
+};
+
+template <int DK>
+__device__ __forceinline__ void iso_seg1(IsoState<DK>& st, SegCarry& cy, IsoSmem<DK>& sm, int c, int sw_) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
+    constexpr int KS = DK / 32;
+    const int kslot = c % KR, slot = c & 3, vslot = c % 3, mb = c & 1;
+    // read phase
+    uint32_t vr[NT][4];
+    b8 ak[NT][KS], aq[NT][KS];
+    f4 rw[NT];
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[at][e] = sm.RV[vslot][sw_][(16 * at + g4 + e) * 16 + n];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            ak[at][kk] = *reinterpret_cast<const b8*>(sm.K[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
+            aq[at][kk] = *reinterpret_cast<const b8*>(sm.Q[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
+        }
+        rw[at] = *reinterpret_cast<const f4*>(&sm.sc[slot][3][16 * at + g4]);
+    }
+    const float rq0 = sm.sc[slot][3][n], rq1 = sm.sc[slot][3][16 + n];
+    const f4 wc0 = *reinterpret_cast<const f4*>(&sm.ws[slot][g4]);
+    const f4 wc1 = *reinterpret_cast<const f4*>(&sm.ws[slot][16 + g4]);
+    const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[mb][n * 16 + g4]);
+    const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[mb][256 + n * 16 + g4]);
+    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[mb][n * 16 + g4]);
+    f4 R[NT];
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+        f4 ks = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            ks = mfma32(ak[at][kk], st.Sb[kk], ks);  // K S~: token x value column
+            o = mfma32(st.Sb[kk], aq[at][kk], o);    // (Q S~)^T: value column x token
+        }
+        // R = V - diag(2^G Gamma) K S~,  O = diag(2^G Gamma) Q S~
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[at][e] = fmaf(-rw[at][e], ks[e], bf1(bf16_t(vr[at][e])));
+        const float rq = at ? rq1 : rq0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= rq;
+        cy.O[at] = o;
+    }
+    // Dn = M^-1 R by block substitution
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f4 d0 = mfma16(t0, pack4(R[0]), zero);
+    const f4 r1 = mfma16(mo, pack4(d0), R[1]);
+    const f4 d1 = mfma16(t1, pack4(r1), zero);
+    cy.Db = pack8(d0, d1);
+    f4 e0, e1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        e0[e] = d0[e] * wc0[e];
+        e1[e] = d1[e] * wc1[e];
+    }
+    cy.Dw = pack8(e0, e1);
+}
+
+template <int DK>
+__device__ __forceinline__ void iso_seg2(IsoState<DK>& st, const SegCarry& cy, IsoSmem<DK>& sm, const IsoArgs& a,
+                                         int h, int col0, int c) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
+    const int slot = c & 3;
+    const bool full = (c + 1) * L <= a.T;
+    b8 ap[NT], akt[DK / 16];
+#pragma unroll
+    for (int at = 0; at < NT; ++at) ap[at] = *reinterpret_cast<const b8*>(&sm.P[c % 3][(16 * at + n) * PT + kg8]);
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it)
+        akt[it] = *reinterpret_cast<const b8*>(&sm.KT[c & 1][((lane >> 4) * DK + 16 * it + n) * 8]);
+    const float cin = sm.ch[slot][0];
+    // outputs, transposed: lane (n, g4) holds value columns g4 .. g4 + 3 of token 16 at + n
+    bf16_t* orow = a.o + tokidx(a, h, c * L + n) * a.DV + col0 + g4;
+    const size_t ostep = size_t(16) * a.H * a.DV;
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+        const f4 o = mfma32(cy.Db, ap[at], cy.O[at]);  // + (P Dn)^T
+        if (full || c * L + 16 * at + n < a.T) *reinterpret_cast<u2*>(orow) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+        orow += ostep;
+    }
+    // S~ <- cin S~ + K^T diag(w') Dn  (cin = 1 unless the frame is renormalised)
+    if (cin != 1.f) {
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.S[it][e] *= cin;
+    }
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) st.S[it] = mfma32(akt[it], cy.Dw, st.S[it]);
+    iso_pack<DK>(st);
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int DK, int NSW, bool GATE>
+__global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
+    constexpr int DVTN = 16 * NSW;  // value columns of this workgroup
+    __shared__ IsoSmem<DK> sm;
+    const int ntile = a.DV / DVTN;
+    const int bid = blockIdx.x;
+    // work items dealt to the eight XCDs in turn, batch-fastest; the column
+    // tiles of one (batch, head) share an XCD
+    const int item = (bid / (8 * ntile)) * 8 + (bid % 8);
+    const int tile = (bid / 8) % ntile;
+    if (item >= a.units) return;
+    const int nbatch = a.units / a.H;
+    int h = item / nbatch;
+    size_t b = size_t(item % nbatch);
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    if (a.cu) {
+        h = item % a.H;
+        const int rank = item / a.H;
+        b = size_t(a.ord ? min(max(a.ord[rank], 0), nbatch - 1) : rank);
+        const int total = a.T;
+        const int s0 = min(max(a.cu[b], 0), total);
+        const int s1 = min(max(a.cu[b + 1], s0), total);
+        a.tok0 = size_t(s0);
+        a.T = s1 - s0;
+    } else {
+        a.tok0 = b * size_t(a.T);
+    }
+    const int unit = int(b) * a.H + h;
+    if (a.T == 0) {
+        const size_t sb = size_t(unit) * DK * a.DV;
+        for (int e = threadIdx.x; e < DK * DVTN; e += NTHREADS) {
+            const size_t x = sb + size_t(e / DVTN) * a.DV + tile * DVTN + e % DVTN;
+            a.S_T[x] = a.S0 ? a.S0[x] : 0.f;
+        }
+        if (tile == 0 && threadIdx.x == 0) a.p_T[unit] = a.p0 ? a.p0[unit] : a.c0[h];
+        return;
+    }
+    const int nchunks = (a.T + L - 1) / L;
+    const int nit = nchunks + 2;
+    constexpr int NK = 2 * tile_copies<DK>();  // copies per chunk (k and q)
+
+    // the zero upper block of P's first row tile and of each inverse, once
+    for (int e = threadIdx.x; e < 3 * 16 * 16; e += NTHREADS) {
+        const int s3 = e >> 8, t = (e >> 4) & 15, s = 16 + (e & 15);
+        sm.P[s3][t * PT + perm32(s)] = 0;
+    }
+    for (int e = threadIdx.x; e < 2 * 2 * 64; e += NTHREADS) {
+        const int bb = e >> 7, a2 = (e >> 6) & 1, tt = (e >> 3) & 7, ss = 8 + (e & 7);
+        sm.Td[bb][a2 * 256 + tt * 16 + ss] = 0;
+    }
+    if (wave == 2) {
+        tile_issue<DK>(sm.K[0], a.k, a, h, 0, nchunks);
+        tile_issue<DK>(sm.Q[0], a.q, a, h, 0, nchunks);
+        tile_issue<DK>(sm.K[1], a.k, a, h, 1, nchunks);
+        tile_issue<DK>(sm.Q[1], a.q, a, h, 1, nchunks);
+        vm_wait<0>();
+    }
+    bar();
+
+    if (wave == 0) {
+        // ---------------- scan ----------------
+        float bprev = a.p0 ? a.p0[unit] : a.c0[h];
+        float gam = 1.f;  // the state's frame
+        ScanRegs<DK> A, B;
+        scan_load<DK>(A, a, h, 0, nchunks);
+        float n = scan_rowsum<DK>(A);
+        for (int it = 0; it < nit; it += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                ScanRegs<DK>& X = half ? B : A;
+                ScanRegs<DK>& Y = half ? A : B;
+                const int c = it + half;
+                if (c >= nit) break;  // nit may be odd: the same number of barriers as the other waves
+                if (c < nchunks) scan_run<DK, GATE>(X, sm, c, n, a.mu, bprev, gam, min(L, a.T - c * L));
+                scan_load<DK>(Y, a, h, c + 1, nchunks);
+                bar();
+                n = scan_rowsum<DK>(Y);
+                bar();
+            }
+        }
+        if (lane == 0 && tile == 0) a.p_T[unit] = bprev;
+        vm_wait<0>();
+    } else if (wave == 1 || wave == 3) {
+        // ---------------- Gram waves (and k^T) ----------------
+        for (int it = 0; it < nit; ++it) {
+            const int c = it;
+            if (wave == 1 && it >= 1 && it - 1 < nchunks) transpose_k<DK>(sm.KT[(it - 1) & 1], sm.K[(it - 1) % KR]);
+            bar();
+            if (c < nchunks) {
+                if (wave == 1) gram_m<DK>(sm, c % KR, c & 3, c & 1);
+                else gram_p<DK>(sm, c % KR, c & 3, c % 3);
+            }
+            bar();
+        }
+    } else if (wave == 2) {
+        // ---------------- inverses and the tile copies ----------------
+        for (int it = 0; it < nit; ++it) {
+            if (it >= 1 && it - 1 < nchunks) block_inverse(sm.Md, sm.Wi, sm.Td[(it - 1) & 1], lane);
+            bar();
+            // chunk it + 2 into slot (it + 2) % KR: its last reader (chunk it - 2) finished its
+            // first segment before the barrier above
+            tile_issue<DK>(sm.K[(it + 2) % KR], a.k, a, h, it + 2, nchunks);
+            tile_issue<DK>(sm.Q[(it + 2) % KR], a.q, a, h, it + 2, nchunks);
+            vm_wait<NK>();  // chunk it + 1's tiles have landed
+            bar();
+        }
+        vm_wait<0>();
+    } else if (wave >= 4 && wave < 4 + NSW) {
+        // ---------------- state ----------------
+        const int sw_ = wave - 4;
+        const int col0 = tile * DVTN + 16 * sw_;  // first column within the head
+        const int n = lane & 15, g4 = (lane >> 4) * 4;
+        IsoState<DK> st;
+        SegCarry cy;
+        const size_t sbase = size_t(unit) * DK * a.DV;
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.S[it][e] = a.S0 ? a.S0[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + n] : 0.f;
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it) settle(st.S[it]);
+        iso_pack<DK>(st);
+        for (int it = 0; it < nit; ++it) {
+            const int c = it - 2;
+            v_issue<DK>(sm, a, h, col0, sw_, it, nchunks);
+            if (c >= 0) iso_seg1<DK>(st, cy, sm, c, sw_);
+            vm_wait<1>();  // the v of chunk it - 1 has landed
+            bar();
+            if (c >= 0) iso_seg2<DK>(st, cy, sm, a, h, col0, c);
+            bar();
+        }
+        // S = Gamma S~ with the frame after the last chunk
+        const float gam = sm.ch[(nchunks - 1) & 3][2];
+        vm_wait<0>();
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.S_T[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + n] = st.S[it][e] * gam;
+    } else {
+        for (int it = 0; it < nit; ++it) {
+            bar();
+            bar();
+        }
+    }
+}
+
+template <int DK, int NSW, bool GATE>
+hipError_t launch_iso_t(const FwdArgs& f, hipStream_t stream) {
+    const int units = f.B * f.H;
+    if (units == 0) return hipSuccess;
+    IsoArgs a;
+    a.q = static_cast<const bf16_t*>(f.q);
+    a.k = static_cast<const bf16_t*>(f.k);
+    a.v = static_cast<const bf16_t*>(f.v);
+    a.alpha = static_cast<const bf16_t*>(f.alpha);
+    a.omega = static_cast<const bf16_t*>(f.omega);
+    a.r = static_cast<const bf16_t*>(f.r);
+    a.c0 = f.c0;
+    a.mu = f.mu;
+    a.T = f.T;
+    a.H = f.H;
+    a.DV = f.dv;
+    a.units = units;
+    a.S0 = f.S0;
+    a.p0 = f.p0;
+    a.o = static_cast<bf16_t*>(f.o);
+    a.S_T = f.S_T;
+    a.p_T = f.p_T;
+    a.cu = f.cu_seqlens;
+    a.ord = f.seq_order;
+    a.tok0 = 0;
+    const int ntile = f.dv / (16 * NSW);
+    const int groups = (units + 7) / 8;
+    const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
+    hipLaunchKernelGGL((kdn_iso_kernel<DK, NSW, GATE>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, bool GATE>
+hipError_t launch_iso_dk(const FwdArgs& a, bool narrow, hipStream_t stream) {
+    return narrow ? launch_iso_t<DK, 2, GATE>(a, stream) : launch_iso_t<DK, 4, GATE>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_iso(const FwdArgs& a, bool narrow, hipStream_t stream) {
+    if (a.variant != 1) return hipErrorNotSupported;
+    if (a.dk == 128) return a.gates ? launch_iso_dk<128, true>(a, narrow, stream) : launch_iso_dk<128, false>(a, narrow, stream);
+    if (a.dk == 64) return a.gates ? launch_iso_dk<64, true>(a, narrow, stream) : launch_iso_dk<64, false>(a, narrow, stream);
+    return hipErrorNotSupported;
+}
+
+}  // namespace kdn

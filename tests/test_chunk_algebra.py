@@ -163,3 +163,112 @@ def test_chunk_start_reference_overflows_where_midpoint_does_not():
     g15 = g[15]
     rho = np.concatenate([g[:16] / g15, np.cumprod(a[16:], axis=0)])
     assert np.max(rho) < 2.0 ** THETA and np.max(1.0 / rho) < 2.0 ** THETA
+
+
+# ---------------------------------------------------------------------------
+# isotropic variant: decay weights on Gram matrices of the raw keys
+# ---------------------------------------------------------------------------
+# With one decay per token, G_t = sum_{u<=t in the chunk} log2 alpha_u, the
+# chunk's recurrence is
+#   M = diag(r) + tril(b_hat_s 2^(G_t - G_s) K K^T),  Dn = M^-1 (V - diag(2^G) K S_c)
+#   O = diag(2^G) Q S_c + tril(b_hat_s 2^(G_t - G_s) Q K^T) Dn
+#   S_{c+1} = 2^(G_L) S_c + K^T diag(b_hat_s 2^(G_L - G_s)) Dn
+# and every weight is 2^(non-positive).  The state is carried as S = Gamma S~
+# with a scalar frame Gamma in [2^-64, 1]: a chunk's decay goes into Gamma
+# while that stays >= 2^-64, else S~ is multiplied through and Gamma = 1.
+FRAME_MIN = 2.0 ** -64
+LOG_FLOOR = -150.0
+
+
+def iso_gram_model(q, k, v, alpha, omega, r, c0, mu, emulate=False):
+    """One (batch, head) pair: q, k [T, dk]; v [T, dv]; alpha, omega, r [T].
+    Returns o, S_T, p_T, the numbers of chunks whose decay the frame absorbed
+    and of renormalised chunks, and the largest |operand|."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    St = np.zeros((dk, dv))  # S~
+    gam = 1.0
+    b = float(c0)
+    o = np.zeros((T, dv))
+    absorbed = renorm = 0
+    big = 0.0
+    for c in range((T + L - 1) // L):
+        t0, t1 = c * L, min(T, (c + 1) * L)
+        K, Q, V = k[t0:t1], q[t0:t1], v[t0:t1]
+        # the scalar uncertainty over the chunk's tokens
+        bh = np.zeros(t1 - t0)
+        for j in range(t1 - t0):
+            bh[j] = alpha[t0 + j] ** 2 * b + omega[t0 + j] / dk
+            b = bh[j] / (1.0 + (mu / (dk * r[t0 + j])) * float(K[j] @ K[j]) * bh[j])
+        G = np.cumsum(np.maximum(np.log2(alpha[t0:t1]), LOG_FLOOR))
+        Wts = np.tril(bh[None, :] * np.exp2(np.minimum(G[:, None] - G[None, :], 0.0)))
+        M = np.diag(r[t0:t1]) + Wts * _ft(K @ K.T, emulate)
+        Pm = _bf(Wts * _ft(Q @ K.T, emulate), emulate)
+        rw = np.exp2(G) * gam
+        Sb = _bf(St, emulate)
+        R = _ft(V - rw[:, None] * _ft(K @ Sb, emulate), emulate)
+        Dn = np.linalg.solve(M, R)
+        o[t0:t1] = _ft(rw[:, None] * _ft(Q @ Sb, emulate) + Pm @ _bf(Dn, emulate), emulate)
+        gnext = gam * 2.0 ** G[-1]
+        w = bh * np.exp2(G[-1] - G)
+        if gnext >= FRAME_MIN:
+            absorbed += 1
+            St = _ft(St + K.T @ _bf((w / gnext)[:, None] * Dn, emulate), emulate)
+            gam = gnext
+        else:
+            renorm += 1
+            St = _ft(gnext * St + K.T @ _bf(w[:, None] * Dn, emulate), emulate)
+            gam = 1.0
+        big = max(big, float(np.max(np.abs(St))), float(np.max(np.abs(M))), float(np.max(np.abs(Pm))))
+    return o, gam * St, b, absorbed, renorm, big
+
+
+def _iso_inputs(T, dk, dv, alpha_loc, seed, alpha_const=None, const_chunk=None):
+    w = wl.Workload("model", "isotropic", "bf16", 1, T, 1, dk, dv, float(dk), "one", seed, alpha_loc=alpha_loc,
+                    omega_loc=-2.0)
+    x = wl.forward_inputs(w)
+    x = {n: (x[n][0, :, 0].astype(np.float64) if n != "c0" else x[n]) for n in x}
+    if alpha_const is not None:
+        lo, hi = const_chunk * L, (const_chunk + 1) * L
+        x["alpha"][lo:hi] = float(wl.round_bf16(np.array([alpha_const], np.float32))[0])
+    return x, w.mu
+
+
+def _iso_ref(x, mu):
+    res = oracle.forward_iso(**{n: x[n][None, :, None] for n in ("q", "k", "v")},
+                             **{n: x[n][None, :, None] for n in ("alpha", "omega", "r")}, c0=x["c0"][:1], mu=mu)
+    return res["o"][0, :, 0], res["S"][0, 0], float(res["p"][0, 0])
+
+
+@pytest.mark.parametrize("alpha_loc,expect", [(2.0, "absorb"), (0.0, "both"), (-3.0, "renorm")])
+def test_iso_gram_form_is_the_recurrence(alpha_loc, expect):
+    # fp64: the Gram form with the scalar frame equals the token recurrence.
+    # alpha ~ 0.88: the frame absorbs every chunk; alpha ~ 0.5 (2^-32 a chunk):
+    # absorbed twice, then renormalised; alpha ~ 0.05: renormalised every full chunk
+    x, mu = _iso_inputs(200, 64, 64, alpha_loc, 41)
+    o, S, p, absorbed, renorm, _ = iso_gram_model(x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], 1.0, mu)
+    assert {"absorb": renorm == 0, "both": absorbed > 0 and renorm > 0, "renorm": renorm == 200 // L}[expect]
+    ro, rS, rp = _iso_ref(x, mu)
+    assert _rel(o, ro) < 1e-10 and _rel(S, rS) < 1e-10 and abs(p - rp) < 1e-12 * abs(rp)
+
+
+@pytest.mark.parametrize("alpha_const", [1e-3, 1e-6, 1e-30])
+def test_iso_gram_form_full_chunk_of_tiny_decay(alpha_const):
+    # no range limit: a full chunk at alpha = 1e-3, 1e-6 or 1e-30 (2^-100 a token)
+    x, mu = _iso_inputs(150, 64, 64, 2.0, 42, alpha_const=alpha_const, const_chunk=2)
+    o, S, p, _, renorm, _ = iso_gram_model(x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], 1.0, mu)
+    assert renorm >= 1
+    ro, rS, rp = _iso_ref(x, mu)
+    assert _rel(o, ro) < 1e-10 and _rel(S, rS) < 1e-10 and abs(p - rp) < 1e-12 * abs(rp)
+
+
+@pytest.mark.parametrize("alpha_loc", [2.0, 0.0, -3.0])
+def test_iso_gram_form_in_fp32_with_bf16_operands(alpha_loc):
+    # the kernel's precisions: S~ below 2^64 times the state's scale, the
+    # outputs within the bf16 tolerance of the fp64 recurrence
+    x, mu = _iso_inputs(256, 128, 128, alpha_loc, 43)
+    o, S, p, _, _, big = iso_gram_model(x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], 1.0, mu,
+                                        emulate=True)
+    assert np.isfinite(big) and big < 2.0 ** 100
+    ro, rS, rp = _iso_ref(x, mu)
+    assert _rel(o, ro) < 2e-2 and _rel(S, rS) < 2e-2 and abs(p - rp) < 1e-6 * abs(rp)
