@@ -29,22 +29,23 @@
 // rescale; only when Gamma would fall below 2^-64 is S~ multiplied through.
 //
 // Workgroup = one (batch, head) pair and 64 value columns (32 when the
-// 64-column tiling would leave more than half of the CUs idle), 8 waves:
-//   wave 0  scan:      the uncertainty scalar's Mobius maps over the chunk's
-//                      32 tokens (lane = token), composed as 2 x 2 matrix
-//                      products by an inclusive cross-lane scan on DPP row
-//                      shifts and a row broadcast; the log-decay prefix sums
-//                      the same way; per-token weights to LDS
-//   wave 1  Gram K K^T of the chunk (matrix cores), weighted into M's
-//           diagonal blocks and -M_10; then k^T of the previous chunk for
-//           the update's operand
-//   wave 2  inverses of M's diagonal blocks; the direct copies of the k and
-//           q tiles two chunks ahead
-//   wave 3  Gram Q K^T, weighted into P = tril(...)
-//   waves 4..7  state: 16 value columns each, S~ in registers (fp32)
-// Two workgroup barriers per iteration; a chunk is scanned and Gram-weighted
-// at iteration c, inverted and transposed at c + 1 and consumed by the state
-// at c + 2.
+// 64-column tiling would leave more than half of the CUs idle), 8 waves, in a
+// software pipeline with one workgroup barrier per iteration: at iteration i
+//   wave 0  scan of chunk i: |k_t|^2 from its k tile, then the uncertainty
+//           scalar's Mobius maps over the chunk's 32 tokens (lane = token),
+//           composed as 2 x 2 matrix products by an inclusive cross-lane scan
+//           on DPP row shifts and a row broadcast; the log-decay prefix sums
+//           the same way; per-token weights to LDS
+//   wave 1  Gram K K^T of chunk i - 1 (matrix cores), weighted into M's
+//           diagonal blocks and -M_10; k^T of chunk i - 2 for the update
+//   wave 2  inverses of M's diagonal blocks of chunk i - 2
+//   wave 3  direct copies of the k and q tiles of chunk i + 2; Gram Q K^T of
+//           chunk i - 1, weighted into P = tril(...)
+//   waves 4..7  state update of chunk i - 3: 16 value columns each, S~ in
+//           registers (fp32)
+// Everything a wave reads at iteration i was written before the barrier that
+// ended iteration i - 1, so the roles overlap and an iteration costs the
+// slowest of them.
 #include "kdn_device.h"
 #include "kdn_gates.h"
 #include "kdn_internal.h"
@@ -63,7 +64,8 @@ constexpr int L = 32;          // tokens per chunk
 constexpr int NT = L / 16;     // 16-token tiles per chunk
 constexpr int NTHREADS = 512;  // 8 waves
 constexpr int PT = L + 8;      // pitch of the bf16 P rows
-constexpr int KR = 4;          // ring of k and q tiles (copied two chunks ahead, read until two chunks later)
+constexpr int KR = 6;          // ring of k and q tiles: a chunk's tiles live from their copy (two iterations
+                               // ahead) to the state's read (three iterations behind)
 constexpr float kLogFloor = -150.f;  // log2 alpha below this: 2^x is zero in fp32
 constexpr float kFrameMin = 0x1p-64f;  // Gamma is kept at or above this
 
@@ -72,14 +74,14 @@ struct IsoSmem {
     alignas(16) bf16_t K[KR][L * DK];     // k tiles [t][sw(i)] (direct copies)
     alignas(16) bf16_t Q[KR][L * DK];     // q tiles [t][sw(i)]
     alignas(16) bf16_t KT[2][L * DK];     // k^T [P / 8][i][P % 8] with P = perm32(t): the update's A operand
-    alignas(16) bf16_t RV[3][4][L * 16];  // v tiles of the state waves (16 columns each), ring of three
+    alignas(16) bf16_t RV[3][L * 64];     // v tiles of the state waves ([wave][t][16 NCW columns]), ring of three
     alignas(16) float sc[4][4][L];        // per chunk (slot c % 4): r, b_hat, G, row weight 2^G Gamma_c
     alignas(16) float ws[4][L];           // update column weights w_s / (the frame change), per chunk
     alignas(16) float ch[4][4];           // per chunk: the C-input factor of the update (1 = none), Gamma_c
     alignas(16) bf16_t P[3][L * PT];      // tril(P) [t][perm32(s)] (ring of three)
     alignas(16) bf16_t Td[2][NT * 256];   // inverses of M's diagonal blocks [a][t][s]
-    alignas(16) bf16_t Mo[2][256];        // -M_10 [t][s]
-    alignas(16) float Md[NT * 256];       // M's diagonal blocks, column-major [a][s][t]
+    alignas(16) bf16_t Mo[3][256];        // -M_10 [t][s]
+    alignas(16) float Md[2][NT * 256];    // M's diagonal blocks, column-major [a][s][t]
     alignas(16) float Wi[NT][2][64];      // block-inverse scratch
 };
 
@@ -140,45 +142,44 @@ __device__ __forceinline__ void scan_level(float& m00, float& m01, float& m10, f
 }
 
 // ---------------------------------------------------------------------------
-// scan wave: lane = token (lanes 32..63 help with |k|^2)
+// scan wave: lane = token (lanes 32..63 repeat lanes 0..31)
 // ---------------------------------------------------------------------------
-template <int DK>
 struct ScanRegs {
-    u4 kr[DK / 16];      // half a k row of token lane & 31
-    bf16_t al, w, rv;    // alpha, omega, r of token lane & 31
+    bf16_t al, w, rv;  // alpha, omega, r of token lane & 31
 };
 
-template <int DK>
-__device__ __forceinline__ void scan_load(ScanRegs<DK>& X, const IsoArgs& a, int h, int c, int nchunks) {
+__device__ __forceinline__ void scan_load(ScanRegs& X, const IsoArgs& a, int h, int c, int nchunks) {
     c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
     const size_t e = tokidx(a, h, min(c * L + (lane & 31), a.T - 1));
-    const u4* src = reinterpret_cast<const u4*>(a.k + e * DK + (lane >> 5) * (DK / 2));
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m) X.kr[m] = src[m];
     X.al = a.alpha[e];
     X.w = a.omega[e];
     X.rv = a.r[e];
 }
 
+// |k_t|^2 of token t = lane & 31 of a k tile (lanes l and l + 32 each sum
+// half of the row in fp32, then exchange)
 template <int DK>
-__device__ __forceinline__ float scan_rowsum(const ScanRegs<DK>& X) {
+__device__ __forceinline__ float tile_norm(const bf16_t* K) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane & 31, half = lane >> 5;
+    constexpr int PCS = DK / 16;  // 16-byte pieces per half row
     float n = 0.f;
 #pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
+    for (int m = 0; m < PCS; ++m) {
+        const u4 x = *reinterpret_cast<const u4*>(K + sw<DK>(t, 8 * (half * PCS + m)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float x0 = bf_lo(X.kr[m][e]), x1 = bf_hi(X.kr[m][e]);
+            const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
             n = fmaf(x0, x0, n);
             n = fmaf(x1, x1, n);
         }
+    }
     return n + __shfl_xor(n, 32, 64);
 }
 
-// The scan of chunk c (slot c % 4): b_hat_t, G_t, the row weights 2^G_t Gamma
-// and the update's column weights and C-input factor for the frame S = Gamma S~.
 template <int DK, bool GATE>
-__device__ __forceinline__ void scan_run(const ScanRegs<DK>& X, IsoSmem<DK>& sm, int c, float n, float mu,
+__device__ __forceinline__ void scan_run(const ScanRegs& X, IsoSmem<DK>& sm, int c, float n, float mu,
                                          float& bprev, float& gam, int nvalid) {
     const int lane = threadIdx.x & 63;
     const int t = lane & 31;
@@ -271,21 +272,28 @@ constexpr int tile_copies() {
 // ---------------------------------------------------------------------------
 // Gram wave: the chunk's 32 x 32 products on the raw tiles, weighted
 // ---------------------------------------------------------------------------
-// acc[e] = (A B^T)[16 ta + g4 + e][16 tb + n] for row tiles ta, tb of A, B
+// Row tile ta (16 rows) of a [t][sw(i)] tile as matrix-core operands: lane
+// (n, kg8) holds row 16 ta + n, channels 32 kk + kg8 .. + 7.  The same
+// registers serve as A (rows of the product) and as B (its columns).
 template <int DK>
-__device__ __forceinline__ f4 gram_tile(const bf16_t* A, const bf16_t* B, int ta, int tb) {
+struct RowTile {
+    b8 x[DK / 32];
+};
+template <int DK>
+__device__ __forceinline__ RowTile<DK> row_tile(const bf16_t* A, int ta) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, kg8 = (lane >> 4) * 8;
-    constexpr int KS = DK / 32;
-    b8 av[KS], bv[KS];
+    RowTile<DK> r;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        av[kk] = *reinterpret_cast<const b8*>(A + sw<DK>(16 * ta + n, 32 * kk + kg8));
-        bv[kk] = *reinterpret_cast<const b8*>(B + sw<DK>(16 * tb + n, 32 * kk + kg8));
-    }
+    for (int kk = 0; kk < DK / 32; ++kk) r.x[kk] = *reinterpret_cast<const b8*>(A + sw<DK>(16 * ta + n, 32 * kk + kg8));
+    return r;
+}
+// acc[e] = (A B^T)[g4 + e][n] for 16-row tiles A, B
+template <int DK>
+__device__ __forceinline__ f4 gram_tile(const RowTile<DK>& A, const RowTile<DK>& B) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) acc = mfma32(av[kk], bv[kk], acc);
+    for (int kk = 0; kk < DK / 32; ++kk) acc = mfma32(A.x[kk], B.x[kk], acc);
     return acc;
 }
 
@@ -309,21 +317,21 @@ __device__ __forceinline__ f4 pair_weights(const IsoSmem<DK>& sm, int slot, int 
 
 // M's diagonal blocks (fp32, column-major) and -M_10 (bf16) of the chunk in slot `slot`
 template <int DK>
-__device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int mo) {
+__device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int md, int mo) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4;
-    const bf16_t* K = sm.K[kslot];
+    const RowTile<DK> k0 = row_tile<DK>(sm.K[kslot], 0), k1 = row_tile<DK>(sm.K[kslot], 1);
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
-        const f4 acc = gram_tile<DK>(K, K, a, a);
+        const f4 acc = gram_tile<DK>(a ? k1 : k0, a ? k1 : k0);
         const f4 wv = pair_weights<DK>(sm, slot, a, a);
         const f4 rv = *reinterpret_cast<const f4*>(&sm.sc[slot][0][16 * a + g4]);
         f4 mv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) mv[e] = fmaf(wv[e], acc[e], g4 + e == n ? rv[e] : 0.f);
-        *reinterpret_cast<f4*>(&sm.Md[a * 256 + n * 16 + g4]) = mv;
+        *reinterpret_cast<f4*>(&sm.Md[md][a * 256 + n * 16 + g4]) = mv;
     }
-    const f4 acc = gram_tile<DK>(K, K, 1, 0);
+    const f4 acc = gram_tile<DK>(k1, k0);
     const f4 wv = pair_weights<DK>(sm, slot, 1, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.Mo[mo][(g4 + e) * 16 + n] = to_bf(-wv[e] * acc[e]);
@@ -334,9 +342,9 @@ template <int DK>
 __device__ __forceinline__ void gram_p(IsoSmem<DK>& sm, int kslot, int slot, int pslot) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4;
-    const bf16_t* K = sm.K[kslot];
-    const bf16_t* Q = sm.Q[kslot];
-    const f4 a00 = gram_tile<DK>(Q, K, 0, 0), a10 = gram_tile<DK>(Q, K, 1, 0), a11 = gram_tile<DK>(Q, K, 1, 1);
+    const RowTile<DK> k0 = row_tile<DK>(sm.K[kslot], 0), k1 = row_tile<DK>(sm.K[kslot], 1);
+    const RowTile<DK> q0 = row_tile<DK>(sm.Q[kslot], 0), q1 = row_tile<DK>(sm.Q[kslot], 1);
+    const f4 a00 = gram_tile<DK>(q0, k0), a10 = gram_tile<DK>(q1, k0), a11 = gram_tile<DK>(q1, k1);
     const f4 w00 = pair_weights<DK>(sm, slot, 0, 0), w10 = pair_weights<DK>(sm, slot, 1, 0),
              w11 = pair_weights<DK>(sm, slot, 1, 1);
 #pragma unroll
@@ -389,50 +397,65 @@ __device__ __forceinline__ void transpose_k(bf16_t* KT, const bf16_t* K) {
     }
 }
 
-template <int DK>
+// A state wave holds NCW tiles of 16 value columns: S~ (d_k x 16 NCW fp32)
+// in registers, tile j in S[j]
+template <int DK, int NCW>
 struct IsoState {
-    f4 S[DK / 16];    // rows 16 it + g4 + e, column n
-    b8 Sb[DK / 32];   // bf16 operands of S~
+    f4 S[NCW][DK / 16];   // rows 16 it + g4 + e, column 16 j + n
+    b8 Sb[NCW][DK / 32];  // bf16 operands of S~
 };
-template <int DK>
-__device__ __forceinline__ void iso_pack(IsoState<DK>& st) {
+template <int DK, int NCW>
+__device__ __forceinline__ void iso_pack(IsoState<DK, NCW>& st) {
 #pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) st.Sb[kk] = pack8(st.S[2 * kk], st.S[2 * kk + 1]);
+    for (int j = 0; j < NCW; ++j)
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) st.Sb[j][kk] = pack8(st.S[j][2 * kk], st.S[j][2 * kk + 1]);
 }
 
-// v tile (32 tokens x 16 columns) of chunk c into ring slot c % 3: 64 pieces, one copy
-template <int DK>
+// v tile (32 tokens x 16 NCW columns) of chunk c (clamped into the sequence)
+// into state wave sw_'s part of RV[slot]: NCW copies of 64 pieces
+template <int DK, int NCW>
 __device__ __forceinline__ void v_issue(IsoSmem<DK>& sm, const IsoArgs& a, int h, int col0, int sw_, int c,
-                                        int nchunks) {
+                                        int slot, int nchunks) {
     c = min(max(c, 0), nchunks - 1);
     const int lane = threadIdx.x & 63;
     const int last = a.T - 1 - c * L;
     const bf16_t* base = a.v + tokidx(a, h, c * L) * a.DV + col0;
     const uint32_t rs = uint32_t(a.H) * uint32_t(a.DV) * 2;
-    const uint32_t off = uint32_t(min(lane >> 1, last)) * rs + uint32_t(lane & 1) * 16;
-    g2lds16(base, off, &sm.RV[c % 3][sw_][0]);
+#pragma unroll
+    for (int m = 0; m < NCW; ++m) {
+        const int pc = lane + 64 * m, row = pc / (2 * NCW), piece = pc % (2 * NCW);
+        const uint32_t off = uint32_t(min(row, last)) * rs + uint32_t(piece) * 16;
+        g2lds16(base, off, &sm.RV[slot][(sw_ * NCW + m) * 512]);
+    }
 }
 
+template <int NCW>
 struct SegCarry {
-    f4 O[NT];  // (Q S)^T of the chunk, scaled: value column x token
-    b8 Db;     // Dn (bf16, B operand) for P Dn
-    b8 Dw;     // diag(w) Dn for the update
+    f4 O[NCW][NT];  // (Q S)^T of the chunk, scaled: value column x token
+    b8 Db[NCW];     // Dn (bf16, A operand) for P Dn
+    b8 Dw[NCW];     // diag(w) Dn for the update
 };
 
-template <int DK>
-__device__ __forceinline__ void iso_seg1(IsoState<DK>& st, SegCarry& cy, IsoSmem<DK>& sm, int c, int sw_) {
+template <int DK, int NCW>
+__device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& cy, IsoSmem<DK>& sm, int c,
+                                         int sw_) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
-    const int kslot = c % KR, slot = c & 3, vslot = c % 3, mb = c & 1;
+    constexpr int VP = 16 * NCW;  // v row pitch
+    const int kslot = c % KR, slot = c & 3, vslot = c % 3, mb = c & 1, m3 = c % 3;
+    const bf16_t* rv = &sm.RV[vslot][sw_ * NCW * 512];
     // read phase
-    uint32_t vr[NT][4];
+    uint32_t vr[NCW][NT][4];
     b8 ak[NT][KS], aq[NT][KS];
     f4 rw[NT];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[at][e] = sm.RV[vslot][sw_][(16 * at + g4 + e) * 16 + n];
+        for (int j = 0; j < NCW; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[j][at][e] = rv[(16 * at + g4 + e) * VP + 16 * j + n];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             ak[at][kk] = *reinterpret_cast<const b8*>(sm.K[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
@@ -445,42 +468,45 @@ __device__ __forceinline__ void iso_seg1(IsoState<DK>& st, SegCarry& cy, IsoSmem
     const f4 wc1 = *reinterpret_cast<const f4*>(&sm.ws[slot][16 + g4]);
     const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[mb][n * 16 + g4]);
     const s4 t1 = *reinterpret_cast<const s4*>(&sm.Td[mb][256 + n * 16 + g4]);
-    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[mb][n * 16 + g4]);
-    f4 R[NT];
+    const s4 mo = *reinterpret_cast<const s4*>(&sm.Mo[m3][n * 16 + g4]);
 #pragma unroll
-    for (int at = 0; at < NT; ++at) {
-        f4 ks = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NCW; ++j) {
+        f4 R[NT];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            ks = mfma32(ak[at][kk], st.Sb[kk], ks);  // K S~: token x value column
-            o = mfma32(st.Sb[kk], aq[at][kk], o);    // (Q S~)^T: value column x token
+        for (int at = 0; at < NT; ++at) {
+            f4 ks = {0.f, 0.f, 0.f, 0.f}, o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                ks = mfma32(ak[at][kk], st.Sb[j][kk], ks);  // K S~: token x value column
+                o = mfma32(st.Sb[j][kk], aq[at][kk], o);    // (Q S~)^T: value column x token
+            }
+            // R = V - diag(2^G Gamma) K S~,  O = diag(2^G Gamma) Q S~
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[at][e] = fmaf(-rw[at][e], ks[e], bf1(bf16_t(vr[j][at][e])));
+            const float rq = at ? rq1 : rq0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] *= rq;
+            cy.O[j][at] = o;
         }
-        // R = V - diag(2^G Gamma) K S~,  O = diag(2^G Gamma) Q S~
+        // Dn = M^-1 R by block substitution
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f4 d0 = mfma16(t0, pack4(R[0]), zero);
+        const f4 r1 = mfma16(mo, pack4(d0), R[1]);
+        const f4 d1 = mfma16(t1, pack4(r1), zero);
+        cy.Db[j] = pack8(d0, d1);
+        f4 e0, e1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[at][e] = fmaf(-rw[at][e], ks[e], bf1(bf16_t(vr[at][e])));
-        const float rq = at ? rq1 : rq0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] *= rq;
-        cy.O[at] = o;
+        for (int e = 0; e < 4; ++e) {
+            e0[e] = d0[e] * wc0[e];
+            e1[e] = d1[e] * wc1[e];
+        }
+        cy.Dw[j] = pack8(e0, e1);
     }
-    // Dn = M^-1 R by block substitution
-    const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    const f4 d0 = mfma16(t0, pack4(R[0]), zero);
-    const f4 r1 = mfma16(mo, pack4(d0), R[1]);
-    const f4 d1 = mfma16(t1, pack4(r1), zero);
-    cy.Db = pack8(d0, d1);
-    f4 e0, e1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        e0[e] = d0[e] * wc0[e];
-        e1[e] = d1[e] * wc1[e];
-    }
-    cy.Dw = pack8(e0, e1);
 }
 
-template <int DK>
-__device__ __forceinline__ void iso_seg2(IsoState<DK>& st, const SegCarry& cy, IsoSmem<DK>& sm, const IsoArgs& a,
-                                         int h, int col0, int c) {
+template <int DK, int NCW>
+__device__ __forceinline__ void iso_seg2(IsoState<DK, NCW>& st, const SegCarry<NCW>& cy, IsoSmem<DK>& sm,
+                                         const IsoArgs& a, int h, int col0, int c) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     const int slot = c & 3;
@@ -492,25 +518,33 @@ __device__ __forceinline__ void iso_seg2(IsoState<DK>& st, const SegCarry& cy, I
     for (int it = 0; it < DK / 16; ++it)
         akt[it] = *reinterpret_cast<const b8*>(&sm.KT[c & 1][((lane >> 4) * DK + 16 * it + n) * 8]);
     const float cin = sm.ch[slot][0];
-    // outputs, transposed: lane (n, g4) holds value columns g4 .. g4 + 3 of token 16 at + n
+    // outputs, transposed: lane (n, g4) holds value columns 16 j + g4 .. + 3 of token 16 at + n
     bf16_t* orow = a.o + tokidx(a, h, c * L + n) * a.DV + col0 + g4;
     const size_t ostep = size_t(16) * a.H * a.DV;
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
-        const f4 o = mfma32(cy.Db, ap[at], cy.O[at]);  // + (P Dn)^T
-        if (full || c * L + 16 * at + n < a.T) *reinterpret_cast<u2*>(orow) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const f4 o = mfma32(cy.Db[j], ap[at], cy.O[j][at]);  // + (P Dn)^T
+            if (full || c * L + 16 * at + n < a.T)
+                *reinterpret_cast<u2*>(orow + 16 * j) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+        }
         orow += ostep;
     }
     // S~ <- cin S~ + K^T diag(w') Dn  (cin = 1 unless the frame is renormalised)
     if (cin != 1.f) {
 #pragma unroll
-        for (int it = 0; it < DK / 16; ++it)
+        for (int j = 0; j < NCW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st.S[it][e] *= cin;
+            for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.S[j][it][e] *= cin;
     }
 #pragma unroll
-    for (int it = 0; it < DK / 16; ++it) st.S[it] = mfma32(akt[it], cy.Dw, st.S[it]);
-    iso_pack<DK>(st);
+    for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) st.S[j][it] = mfma32(akt[it], cy.Dw[j], st.S[j][it]);
+    iso_pack<DK, NCW>(st);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,7 +552,8 @@ __device__ __forceinline__ void iso_seg2(IsoState<DK>& st, const SegCarry& cy, I
 // ---------------------------------------------------------------------------
 template <int DK, int NSW, bool GATE>
 __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
-    constexpr int DVTN = 16 * NSW;  // value columns of this workgroup
+    constexpr int NCW = 1;                // 16-column tiles per state wave
+    constexpr int DVTN = 16 * NSW * NCW;  // value columns of this workgroup
     __shared__ IsoSmem<DK> sm;
     const int ntile = a.DV / DVTN;
     const int bid = blockIdx.x;
@@ -555,7 +590,9 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         return;
     }
     const int nchunks = (a.T + L - 1) / L;
-    const int nit = nchunks + 2;
+    // iteration i: scan of chunk i, Gram products of chunk i - 1, inverses and
+    // k^T of chunk i - 2, state update of chunk i - 3; one barrier each
+    const int nit = nchunks + 3;
     constexpr int NK = 2 * tile_copies<DK>();  // copies per chunk (k and q)
 
     // the zero upper block of P's first row tile and of each inverse, once
@@ -567,101 +604,110 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         const int bb = e >> 7, a2 = (e >> 6) & 1, tt = (e >> 3) & 7, ss = 8 + (e & 7);
         sm.Td[bb][a2 * 256 + tt * 16 + ss] = 0;
     }
-    if (wave == 2) {
+    if (wave == 3) {
         tile_issue<DK>(sm.K[0], a.k, a, h, 0, nchunks);
         tile_issue<DK>(sm.Q[0], a.q, a, h, 0, nchunks);
         tile_issue<DK>(sm.K[1], a.k, a, h, 1, nchunks);
         tile_issue<DK>(sm.Q[1], a.q, a, h, 1, nchunks);
-        vm_wait<0>();
+        vm_wait<NK>();  // chunk 0 has landed
     }
     bar();
 
     if (wave == 0) {
-        // ---------------- scan ----------------
+        // ---------------- scan of chunk i ----------------
         float bprev = a.p0 ? a.p0[unit] : a.c0[h];
         float gam = 1.f;  // the state's frame
-        ScanRegs<DK> A, B;
-        scan_load<DK>(A, a, h, 0, nchunks);
-        float n = scan_rowsum<DK>(A);
-        for (int it = 0; it < nit; it += 2) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                ScanRegs<DK>& X = half ? B : A;
-                ScanRegs<DK>& Y = half ? A : B;
-                const int c = it + half;
-                if (c >= nit) break;  // nit may be odd: the same number of barriers as the other waves
-                if (c < nchunks) scan_run<DK, GATE>(X, sm, c, n, a.mu, bprev, gam, min(L, a.T - c * L));
-                scan_load<DK>(Y, a, h, c + 1, nchunks);
-                bar();
-                n = scan_rowsum<DK>(Y);
-                bar();
+        ScanRegs X;
+        scan_load(X, a, h, 0, nchunks);
+        for (int i = 0; i < nit; ++i) {
+            if (i < nchunks) {
+                const float nrm = tile_norm<DK>(sm.K[i % KR]);
+                scan_run<DK, GATE>(X, sm, i, nrm, a.mu, bprev, gam, min(L, a.T - i * L));
             }
+            scan_load(X, a, h, i + 1, nchunks);  // used at the next iteration
+            bar();
         }
         if (lane == 0 && tile == 0) a.p_T[unit] = bprev;
-        vm_wait<0>();
-    } else if (wave == 1 || wave == 3) {
-        // ---------------- Gram waves (and k^T) ----------------
-        for (int it = 0; it < nit; ++it) {
-            const int c = it;
-            if (wave == 1 && it >= 1 && it - 1 < nchunks) transpose_k<DK>(sm.KT[(it - 1) & 1], sm.K[(it - 1) % KR]);
-            bar();
-            if (c < nchunks) {
-                if (wave == 1) gram_m<DK>(sm, c % KR, c & 3, c & 1);
-                else gram_p<DK>(sm, c % KR, c & 3, c % 3);
-            }
+    } else if (wave == 1) {
+        // ---------------- M of chunk i - 1; k^T of chunk i - 2 ----------------
+        for (int i = 0; i < nit; ++i) {
+            const int c = i - 1;
+            if (c >= 0 && c < nchunks) gram_m<DK>(sm, c % KR, c & 3, c & 1, c % 3);
+            if (c >= 1 && c <= nchunks) transpose_k<DK>(sm.KT[(c - 1) & 1], sm.K[(c - 1) % KR]);
             bar();
         }
     } else if (wave == 2) {
-        // ---------------- inverses and the tile copies ----------------
-        for (int it = 0; it < nit; ++it) {
-            if (it >= 1 && it - 1 < nchunks) block_inverse(sm.Md, sm.Wi, sm.Td[(it - 1) & 1], lane);
+        // ---------------- inverses of chunk i - 2 ----------------
+        for (int i = 0; i < nit; ++i) {
+            const int c = i - 2;
+            if (c >= 0 && c < nchunks) block_inverse(sm.Md[c & 1], sm.Wi, sm.Td[c & 1], lane);
             bar();
-            // chunk it + 2 into slot (it + 2) % KR: its last reader (chunk it - 2) finished its
-            // first segment before the barrier above
-            tile_issue<DK>(sm.K[(it + 2) % KR], a.k, a, h, it + 2, nchunks);
-            tile_issue<DK>(sm.Q[(it + 2) % KR], a.q, a, h, it + 2, nchunks);
-            vm_wait<NK>();  // chunk it + 1's tiles have landed
+        }
+    } else if (wave == 3) {
+        // ---------------- tile copies; P of chunk i - 1 ----------------
+        for (int i = 0; i < nit; ++i) {
+            // chunk i + 2 into slot (i + 2) % KR: its previous occupant, chunk
+            // i + 2 - KR, was last read at iteration i - 1
+            tile_issue<DK>(sm.K[(i + 2) % KR], a.k, a, h, i + 2, nchunks);
+            tile_issue<DK>(sm.Q[(i + 2) % KR], a.q, a, h, i + 2, nchunks);
+            const int c = i - 1;
+            if (c >= 0 && c < nchunks) gram_p<DK>(sm, c % KR, c & 3, c % 3);
+            vm_wait<NK>();  // chunk i + 1 (copied at iteration i - 1) has landed; chunk i + 2 may not have
             bar();
         }
         vm_wait<0>();
     } else if (wave >= 4 && wave < 4 + NSW) {
-        // ---------------- state ----------------
+        // ---------------- state: chunk i - 3 ----------------
         const int sw_ = wave - 4;
-        const int col0 = tile * DVTN + 16 * sw_;  // first column within the head
+        const int col0 = tile * DVTN + 16 * NCW * sw_;  // first column within the head
         const int n = lane & 15, g4 = (lane >> 4) * 4;
-        IsoState<DK> st;
-        SegCarry cy;
+        IsoState<DK, NCW> st;
+        SegCarry<NCW> cy;
         const size_t sbase = size_t(unit) * DK * a.DV;
 #pragma unroll
-        for (int it = 0; it < DK / 16; ++it)
+        for (int j = 0; j < NCW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                st.S[it][e] = a.S0 ? a.S0[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + n] : 0.f;
+            for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
-        for (int it = 0; it < DK / 16; ++it) settle(st.S[it]);
-        iso_pack<DK>(st);
-        for (int it = 0; it < nit; ++it) {
-            const int c = it - 2;
-            v_issue<DK>(sm, a, h, col0, sw_, it, nchunks);
-            if (c >= 0) iso_seg1<DK>(st, cy, sm, c, sw_);
-            vm_wait<1>();  // the v of chunk it - 1 has landed
-            bar();
-            if (c >= 0) iso_seg2<DK>(st, cy, sm, a, h, col0, c);
+                for (int e = 0; e < 4; ++e)
+                    st.S[j][it][e] =
+                        a.S0 ? a.S0[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + 16 * j + n] : 0.f;
+#pragma unroll
+        for (int j = 0; j < NCW; ++j)
+#pragma unroll
+            for (int it = 0; it < DK / 16; ++it) settle(st.S[j][it]);
+        iso_pack<DK, NCW>(st);
+        for (int i = 0; i < nit; ++i) {
+            const int c = i - 3;
+            // v of chunk i - 1 into slot (i - 1) mod 3 = (i + 2) % 3
+            v_issue<DK, NCW>(sm, a, h, col0, sw_, i - 1, (i + 2) % 3, nchunks);
+            if (c >= 0) {
+                // the v of chunk c (copied at iteration i - 2) has landed: the
+                // memory counter drains in order, and after that copy come the
+                // v copies of iterations i - 1 and i (NCW each) and the NT NCW
+                // output stores of iterations i - 2 and i - 1 where those
+                // updated a chunk
+                constexpr int NV = NCW, NS = NT * NCW;
+                if (i >= 5) vm_wait<2 * NS + 2 * NV>();
+                else if (i == 4) vm_wait<NS + 2 * NV>();
+                else vm_wait<2 * NV>();
+                iso_seg1<DK, NCW>(st, cy, sm, c, sw_);
+                iso_seg2<DK, NCW>(st, cy, sm, a, h, col0, c);
+            }
             bar();
         }
         // S = Gamma S~ with the frame after the last chunk
         const float gam = sm.ch[(nchunks - 1) & 3][2];
         vm_wait<0>();
 #pragma unroll
-        for (int it = 0; it < DK / 16; ++it)
+        for (int j = 0; j < NCW; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.S_T[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + n] = st.S[it][e] * gam;
+            for (int it = 0; it < DK / 16; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a.S_T[sbase + size_t(chan_of(16 * it + g4 + e)) * a.DV + col0 + 16 * j + n] = st.S[j][it][e] * gam;
     } else {
-        for (int it = 0; it < nit; ++it) {
-            bar();
-            bar();
-        }
+        for (int i = 0; i < nit; ++i) bar();
     }
 }
 
