@@ -92,21 +92,52 @@ def backward_bytes(w) -> int:
     return toks * (es * (n_in + w.dv) + 4 * n_in) + w.B * w.H * (w.dk * w.dv + pdim) * 4 + 2 * w.H * 4
 
 
-def chunked_workgroups(w) -> int:
+def chunked_workgroups(w, cus: int = 256) -> int:
     """Workgroups of the chunked forward under the library's own choice: one
     per (batch, head) and 64 value columns, or per 32 columns when the
-    64-column tiling fills at most half of the 256 compute units."""
+    64-column tiling fills at most half of the device's compute units."""
     wide = w.B * w.H * (w.dv // 64)
-    return 2 * wide if 2 * wide <= 256 else wide
+    return 2 * wide if 2 * wide <= cus else wide
 
 
-def kernel_source_hash() -> str:
-    """Hash of the source of the forward's dominant kernel (the chunked
-    kernel): HBM counters taken on other source are not reported."""
+# bench lines whose dominant kernel's HBM bytes are counted: workload, a
+# substring of the kernel's name, the sources it is built from (counters
+# taken on other source are not reported), and how one call is run
+COUNTED = {
+    "main": ("diag_bf16_b8_t4096_h16_d128", "kdn_chunk_kernel", ("kdn_chunked.hip", "kdn_device.h")),
+    "isotropic": ("iso_bf16_b8_t4096_h16_d128", "kdn_iso_kernel", ("kdn_iso.hip", "kdn_device.h", "kdn_gates.h")),
+    "long_context": ("diag_bf16_b1_t65536_h16_d128", "kdn_chunk_kernel", ("kdn_chunked.hip", "kdn_device.h")),
+    "decode": ("decode_diag_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
+               ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
+    "decode_isotropic": ("decode_iso_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
+                         ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
+    # the backward's kernels (uncertainty adjoint, memory adjoint, d c0): the
+    # counters pass runs no other library kernel
+    "backward": ("diag_bf16_b8_t4096_h16_d128", "kdn_", ("kdn_backward.hip",)),
+}
+
+
+def kernel_source_hash(line: str = "main") -> str:
+    """Hash of the sources of a counted line's kernel: HBM counters taken on
+    other source are not reported."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "kalman_delta_network_amd", "csrc", "kdn_chunked.hip"), "rb") as f:
-        h.update(f.read())
+    for name in COUNTED[line][2]:
+        with open(os.path.join(ROOT, "kalman_delta_network_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def traffic_for(line: str, algo: str = "auto"):
+    """Counted HBM bytes per call of a line's kernel, or None when there is no
+    entry taken on the current source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    ent = tr.get(line + "/" + algo)
+    if ent and ent.get("kernel_hash") == kernel_source_hash(line):
+        return ent["bytes_per_launch"]
+    return None
 
 
 def upload(x, dtype, dev):
@@ -171,9 +202,10 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     return ms_step, ms_launch
 
 
-def bench_decode(kdn, w, dev, steps_cap=None, gated=False):
+def bench_decode(kdn, w, dev, steps_cap=None, gated=False, warm_up=True):
     """Time w.decode_steps consecutive kdn_step calls (tokens pre-uploaded);
-    ``gated``: kdn_step_gated on gate pre-activations."""
+    ``gated``: kdn_step_gated on gate pre-activations; ``warm_up``: first
+    run steps on a scratch copy of the state until the clock has ramped."""
     import torch
     from kalman_delta_network_amd import workloads as wl
     nsteps = w.decode_steps if steps_cap is None else min(steps_cap, w.decode_steps)
@@ -192,9 +224,10 @@ def bench_decode(kdn, w, dev, steps_cap=None, gated=False):
         names = ("q", "k", "v", "alpha", "omega", "r")
         step = lambda tk, S_, p_: kdn.step(**{n: tk[n] for n in names}, mu=w.mu, S=S_, p=p_, variant=w.variant,
                                            o=o)
-    S2, p2 = S.clone(), p.clone()  # warm-up on a scratch copy of the state
-    warm(lambda: step(toks[0], S2, p2), 3)
-    del S2, p2
+    if warm_up:
+        S2, p2 = S.clone(), p.clone()  # warm-up on a scratch copy of the state
+        warm(lambda: step(toks[0], S2, p2), 3)
+        del S2, p2
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for s in range(nsteps):
@@ -240,9 +273,9 @@ def bench_varlen(kdn, dev, steps, algo):
             "tokens_per_s": total / (ms / 1e3), "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_backward(kdn, w, dev, steps, gated=False):
-    """Time kdn_backward (``gated``: kdn_backward_gated on gate
-    pre-activations) on workload w (cotangent dO only), inputs resident."""
+def backward_call(kdn, w, dev, gated=False):
+    """(call, workspace): one kdn_backward call (``gated``: kdn_backward_gated
+    on gate pre-activations) on workload w with cotangent dO only."""
     import torch
     from kalman_delta_network_amd import workloads as wl
     t = upload(wl.gated_inputs(w) if gated else wl.forward_inputs(w), w.dtype, dev)
@@ -254,6 +287,14 @@ def bench_backward(kdn, w, dev, steps, gated=False):
     else:
         ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
         call = lambda: kdn.backward(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
+    return call, ws
+
+
+def bench_backward(kdn, w, dev, steps, gated=False):
+    """Time kdn_backward (``gated``: kdn_backward_gated) on workload w, inputs
+    resident."""
+    import torch
+    call, ws = backward_call(kdn, w, dev, gated)
     warm(call, 1)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
@@ -271,8 +312,9 @@ COPY_BYTES = 512 << 20  # calibration copy for the HBM byte counters
 
 
 def counters_pass(args):
-    """Workload for the rocprofv3 counter runs: one device-to-device copy of
-    COPY_BYTES (the calibration kernel), then a few forward calls."""
+    """Workload for the rocprofv3 counter runs of one counted line: one
+    device-to-device copy of COPY_BYTES (the calibration kernel), then three
+    calls of the line (decode: 16 steps)."""
     import torch
     import kalman_delta_network_amd as kdn
     from kalman_delta_network_amd import workloads as wl
@@ -283,10 +325,19 @@ def counters_pass(args):
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    w = wl.WORKLOADS[MAIN]
-    t = upload(wl.forward_inputs(w), w.dtype, dev)
-    for _ in range(3):
-        kdn.forward(**t, mu=w.mu, variant=w.variant, algo=args.algo)
+    del src, dst
+    line = args.counters_pass
+    w = wl.WORKLOADS[COUNTED[line][0]]
+    if line.startswith("decode"):
+        bench_decode(kdn, w, dev, 16, warm_up=False)
+    elif line == "backward":
+        call, _ = backward_call(kdn, w, dev)
+        for _ in range(4):
+            call()
+    else:
+        t = upload(wl.forward_inputs(w), w.dtype, dev)
+        for _ in range(3):
+            kdn.forward(**t, mu=w.mu, variant=w.variant, algo=args.algo)
     torch.cuda.synchronize()
     print("counters pass done", flush=True)
 
@@ -306,40 +357,74 @@ def _read_counter_csv(run_dir, counter):
     return rows
 
 
-def traffic_from(fetch_dir, write_dir, out_path, algo):
-    """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by the same counter of the calibration copy."""
+def traffic_from(fetch_dir, write_dir, out_path, algo, line):
+    """HBM bytes per launch of a counted line's kernel from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by the same counter of the
+    calibration copy.  The backward's bytes are per backward call (the sum
+    over its kernels' dispatches, divided by the number of calls)."""
     res = {}
+    kname = COUNTED[line][1]
     for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _read_counter_csv(run_dir, counter)
         copies = [v for n, v in rows.values() if "kdn" not in n and v > 0]
-        fwd = [v for n, v in rows.values() if "kdn_chunk_kernel" in n]
-        if not copies or not fwd:
-            raise SystemExit(f"{counter}: no calibration copy or forward dispatch in {run_dir}")
+        hits = [v for n, v in rows.values() if kname in n]
+        if not copies or not hits:
+            raise SystemExit(f"{counter}: no calibration copy or {kname} dispatch in {run_dir}")
         scale = COPY_BYTES / (max(copies) * 1024.0)  # bytes per counted byte
-        res[counter] = {"kib_per_launch": float(np.mean(fwd)), "copy_kib": max(copies), "scale": scale,
-                        "bytes_per_launch": float(np.mean(fwd)) * 1024.0 * scale}
-    entry = {"kernel_hash": kernel_source_hash(), "algo": algo,
+        per = float(np.sum(hits)) / 4.0 if line == "backward" else float(np.mean(hits))  # 4 backward calls
+        res[counter] = {"kib_per_launch": per, "dispatches": len(hits), "copy_kib": max(copies), "scale": scale,
+                        "bytes_per_launch": per * 1024.0 * scale}
+    entry = {"workload": COUNTED[line][0], "kernel": kname, "kernel_hash": kernel_source_hash(line), "algo": algo,
              "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
              "counters": res}
     data = {}
     if os.path.exists(out_path):
         with open(out_path) as f:
             data = json.load(f)
-    data[MAIN + "/" + algo] = entry
+    data.pop(MAIN + "/" + algo, None)  # entries keyed by workload name predate the per-line keys
+    data[line + "/" + algo] = entry
     with open(out_path, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(entry))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x):
+    """The fp64 oracle on the host: the whole workload on all its OpenMP
+    threads (one (batch, head) pair per thread at a time), then the first
+    two batch rows on one thread."""
     import oracle
-    t0 = time.perf_counter()
     fn = oracle.forward_diag if w.variant == "diagonal" else oracle.forward_iso
-    fn(**{n: x[n] for n in ("q", "k", "v", "alpha", "omega", "r", "c0")}, mu=w.mu)
+    names = ("q", "k", "v", "alpha", "omega", "r")
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    fn(**{n: x[n] for n in names}, c0=x["c0"], mu=w.mu)
     dt = time.perf_counter() - t0
-    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the full {w.name} workload (B={w.B}, T={w.T}, H={w.H}), fp64, {dt:.1f} s wall"}
+    nb = min(2, w.B)
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        fn(**{n: x[n][:nb] for n in names}, c0=x["c0"], mu=w.mu)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {w.name} workload (B={w.B}, T={w.T}, H={w.H}), fp64, {dt:.1f} s wall "
+                      f"on {threads} threads",
+            "value_1thread": nb * w.T / dt1,
+            "sample_1thread": f"batch rows 0..{nb - 1} of the same workload on 1 thread, {dt1:.1f} s wall",
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -353,14 +438,18 @@ def main():
                     help="skip the isotropic, decode, packed-batch, per-channel-decay isotropic, grouped-noise, "
                          "long-context and backward lines")
     ap.add_argument("--decode-steps", type=int, default=None)
-    ap.add_argument("--counters-pass", action="store_true",
-                    help="run the workload of the rocprofv3 counter runs and exit")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc CSV runs into a traffic entry and exit")
+    ap.add_argument("--counters-pass", choices=sorted(COUNTED),
+                    help="run the workload of the rocprofv3 counter runs of one bench line and exit")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("LINE", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc CSV runs of a line's counters pass into its traffic entry "
+                         "and exit")
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from(args.traffic_from[0], args.traffic_from[1], args.traffic_out, args.algo)
+        line, fetch_dir, write_dir = args.traffic_from
+        if line not in COUNTED:
+            raise SystemExit(f"unknown line {line}; counted lines: {sorted(COUNTED)}")
+        traffic_from(fetch_dir, write_dir, args.traffic_out, args.algo, line)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -384,23 +473,27 @@ def main():
     ms_step, ms_launch = time_forward(kdn, w, t, args.steps, args.warmup, args.algo)
     nbytes = forward_bytes(w)
     achieved = nbytes / (ms_launch / 1e3) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        ent = tr.get(MAIN + "/" + args.algo) or tr.get(MAIN)
-        if ent and ent.get("kernel_hash") == kernel_source_hash():
-            traffic = ent["bytes_per_launch"]
+    traffic = traffic_for("main", args.algo)
     extra = {}
     if not args.no_extra:
         wi = wl.WORKLOADS["iso_bf16_b8_t4096_h16_d128"]
         ti = upload(wl.forward_inputs(wi), wi.dtype, dev)
         mi, li = time_forward(kdn, wi, ti, max(3, args.steps // 2), 2, args.algo)
         extra["isotropic"] = {"workload": wi.name, "tokens_per_s": wi.B * wi.T / (mi / 1e3),
-                              "ms_per_step": mi, "hbm_frac": forward_bytes(wi) / (li / 1e3) / 1e9 / HBM_PEAK_GBS}
+                              "ms_per_step": mi, "launch_ms": li, "algorithmic_bytes": forward_bytes(wi),
+                              "hbm_frac": forward_bytes(wi) / (li / 1e3) / 1e9 / HBM_PEAK_GBS,
+                              "traffic": traffic_for("isotropic", args.algo)}
         del ti
         extra["decode"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
                                        args.decode_steps)
+        extra["decode"]["traffic"] = traffic_for("decode")
+        extra["decode_isotropic"] = bench_decode(kdn, wl.WORKLOADS["decode_iso_bf16_n256_h16_d128_s1024"], dev,
+                                                 args.decode_steps)
+        extra["decode_isotropic"]["traffic"] = traffic_for("decode_isotropic")
+        # the same decode at N = 1024 sequences: a 1.07 GB state, four times the
+        # 256 MB Infinity Cache, so the per-byte rate of this line is HBM's
+        wd = wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"].with_(name="decode_diag_bf16_n1024_h16_d128", B=1024)
+        extra["decode_n1024"] = bench_decode(kdn, wd, dev, min(64, args.decode_steps or 64))
         extra["decode_gated"] = bench_decode(kdn, wl.WORKLOADS["decode_diag_bf16_n256_h16_d128_s1024"], dev,
                                              min(256, args.decode_steps or 256), gated=True)
         extra["varlen"] = bench_varlen(kdn, dev, max(3, args.steps // 2), args.algo)
@@ -432,11 +525,14 @@ def main():
         tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)
         mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "auto")
         extra["long_context"] = {"workload": wlc.name, "tokens_per_s": wlc.B * wlc.T / (mlc / 1e3),
-                                 "ms_per_step": mlc,
+                                 "ms_per_step": mlc, "launch_ms": llc, "algorithmic_bytes": forward_bytes(wlc),
                                  "hbm_frac": forward_bytes(wlc) / (llc / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                 "workgroups": chunked_workgroups(wlc)}
+                                 "workgroups": chunked_workgroups(
+                                     wlc, torch.cuda.get_device_properties(dev).multi_processor_count),
+                                 "traffic": traffic_for("long_context")}
         del tlc
         extra["backward"] = bench_backward(kdn, w, dev, 3)
+        extra["backward"]["traffic"] = traffic_for("backward")
         extra["backward_gated"] = bench_backward(kdn, w, dev, 3, gated=True)
     cpu = None
     if not args.no_cpu_baseline:

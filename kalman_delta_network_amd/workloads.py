@@ -79,6 +79,9 @@ WORKLOADS = {
     "decode_diag_bf16_n256_h16_d128_s1024": Workload(
         "decode_diag_bf16_n256_h16_d128_s1024", "diagonal", "bf16", 256, 1, 16, 128, 128, 128.0,
         "one", 1004, decode_steps=1024),
+    "decode_iso_bf16_n256_h16_d128_s1024": Workload(
+        "decode_iso_bf16_n256_h16_d128_s1024", "isotropic", "bf16", 256, 1, 16, 128, 128, 128.0,
+        "one", 1007, decode_steps=1024),
 }
 # the workloads in the order they are listed in the benchmark table
 WORKLOAD_ORDER = list(WORKLOADS)

@@ -74,6 +74,8 @@ def _load():
         lib.kdn_oracle_backward.argtypes = [I, I, I, I, I, I] + [P] * 7 + [D] + [P] * 14
         lib.kdn_oracle_backward.restype = I
         lib.kdn_oracle_num_threads.restype = I
+        lib.kdn_oracle_set_num_threads.argtypes = [I]
+        lib.kdn_oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -81,6 +83,11 @@ def _load():
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().kdn_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Use n threads in the oracle's OpenMP loops from now on."""
+    _load().kdn_oracle_set_num_threads(int(n))
 
 
 def _in(x):

@@ -348,6 +348,15 @@ int kdn_oracle_num_threads(void) {
 #endif
 }
 
+/* Set the number of OpenMP threads of the oracle's parallel loops (n >= 1). */
+void kdn_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Backward pass (reverse-mode adjoint of the recurrence above), for training.
  *

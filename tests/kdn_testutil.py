@@ -40,6 +40,20 @@ def p_rel_err(x, ref) -> float:
     return float(np.max(np.abs(x - ref) / ref))
 
 
+def check_forward(name, got, ref, dtype):
+    """Compare (o, S_T, p_T) with the oracle's: the per-tensor metric on each
+    and the elementwise one on p, every entry finite, all within tol(dtype).
+    Returns the errors."""
+    errs = {k: rel_err(g, ref[k]) for k, g in zip(("o", "S", "p"), got)}
+    errs["p_elem"] = p_rel_err(got[2], ref["p"])
+    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, g in zip(("o", "S", "p"), got):
+        assert np.all(np.isfinite(np.asarray(g, np.float64))), (name, k, "non-finite")
+    for k, e in errs.items():
+        assert e <= tol(dtype), (name, k, e)
+    return errs
+
+
 def to_dev(x: dict, dtype: str, device):
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from kalman_delta_network_amd import workloads as wl
-from kdn_testutil import TOKEN_INPUTS, oracle_forward, p_rel_err, rel_err, to_dev, tol
+from kdn_testutil import check_forward, TOKEN_INPUTS, oracle_forward, p_rel_err, rel_err, to_dev, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -38,12 +38,7 @@ def set_alpha(x, variant, lo, hi, value, gated=False):
 
 
 def check(name, got, ref):
-    errs = {k: rel_err(g, ref[k]) for k, g in zip(("o", "S", "p"), got)}
-    errs["p_elem"] = p_rel_err(got[2], ref["p"])
-    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1])) and np.all(np.isfinite(got[2]))
-    for k, e in errs.items():
-        assert e <= tol("bf16"), (name, k, e)
+    return check_forward(name, got, ref, "bf16")
 
 
 def run(dev, w, x, algo, gated=False):

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from kalman_delta_network_amd import workloads as wl
-from kdn_testutil import rel_err, sample_pairs, tol
+from kdn_testutil import check_forward, rel_err, sample_pairs, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -48,10 +48,7 @@ def oracle_gated(w, x, S0=None, p0=None):
 
 
 def check(name, got, ref, dtype):
-    errs = {k: rel_err(g, ref[k]) for k, g in zip(("o", "S", "p"), got)}
-    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, e in errs.items():
-        assert e <= tol(dtype), (name, k, e)
+    return check_forward(name, got, ref, dtype)
 
 
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])

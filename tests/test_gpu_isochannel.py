@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 from kalman_delta_network_amd import workloads as wl
-from kdn_testutil import TOKEN_INPUTS, oracle_forward, oracle_forward_heads, rel_err, sample_pairs, to_dev, tol
+from kdn_testutil import (check_forward, TOKEN_INPUTS, oracle_forward, oracle_forward_heads, rel_err, sample_pairs,
+                          to_dev, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,10 +24,7 @@ def dev():
 
 
 def check(name, got, ref, dtype):
-    errs = {k: rel_err(g, ref[k]) for k, g in zip(("o", "S", "p"), got)}
-    print(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, e in errs.items():
-        assert e <= tol(dtype), (name, k, e)
+    return check_forward(name, got, ref, dtype)
 
 
 def run(dev, w, x, algo="auto", S0=None, p0=None):
