@@ -164,6 +164,48 @@ int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z
                       int dtype, int B, int T, int H, int dk, int dv, const float* S0,
                       const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
+/*
+ * kdn_forward_split -- kdn_forward (diagonal variant, bf16 inputs, the
+ * chunked algorithm's alignment) for batches too small to fill the device:
+ * each sequence is cut into segments that run concurrently.  Both
+ * recurrences compose across a cut (summary page, method steps 4-5): the
+ * uncertainty update of each channel is a Mobius map, so the uncertainty
+ * entering a segment is p0 carried through the earlier segments' composed
+ * maps; and with the gains known the memory update is affine in S, so over
+ * segment g, S_end = Phi_g S_start + Psi_g.  One launch runs every segment
+ * from S = 0 on the v columns (Psi_g) and from S = I on d_k extra columns
+ * with v = 0 (Phi_g, and Phi_t^T q_t per token); then the segments' start
+ * states are chained and o_t += (Phi_t^T q_t)^T S_start is added to the
+ * tokens of every segment after the first.  About twice the arithmetic of
+ * kdn_forward, spread over segments x (batch, head) x column tiles.
+ *
+ *   segments           0: chosen from the device (as many as fill its
+ *                      compute units with one workgroup each, segments of at
+ *                      least 2048 tokens, at most 16); > 0: about that many
+ *                      (segment lengths are a multiple of 32 tokens).  When
+ *                      the choice is 1 the call is kdn_forward_algo(AUTO).
+ *   workspace          device memory of kdn_forward_split_workspace_size()
+ *                      bytes (16-byte aligned, overlapping no argument), owned
+ *                      by the caller; unused when no split is made.
+ * Other arguments, layouts and results as kdn_forward, up to rounding: the
+ * corrections add one bf16 rounding of Phi_t^T q_t and of S_start.  Errors
+ * as kdn_forward_algo(KDN_ALGO_CHUNKED), plus KDN_ERR_UNSUPPORTED for another
+ * variant or dtype, KDN_ERR_VALUE for segments < 0 and KDN_ERR_WORKSPACE /
+ * KDN_ERR_ALIAS for the workspace.
+ */
+int kdn_forward_split(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                      const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H, int dk,
+                      int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T, int segments,
+                      void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes of kdn_forward_split for these sizes and segment request
+ * (0 when no split is made or the sizes are invalid). */
+size_t kdn_forward_split_workspace_size(int B, int T, int H, int dk, int dv, int segments);
+/* The checks of kdn_forward_split without a launch. */
+int kdn_validate_forward_split(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                               const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H,
+                               int dk, int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                               int segments, void* workspace, size_t workspace_bytes);
+
 /* kdn_forward_varlen with the gate step of kdn_forward_gated: z_alpha,
  * z_omega and z_r are pre-activations in the layouts of alpha, omega and r
  * (not KDN_DIAGONAL_GROUPED).  Same checks and results as kdn_forward_varlen

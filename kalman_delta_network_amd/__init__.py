@@ -50,7 +50,8 @@ def _p_shape(var, lead, dk, dv):
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
            "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated", "kdn_backward_gated",
-           "kdn_backward_gated_workspace_size", "kdn_backward_noalloc",
+           "kdn_backward_gated_workspace_size", "kdn_backward_noalloc", "kdn_forward_split",
+           "kdn_forward_split_workspace_size", "kdn_validate_forward_split",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated",
            "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
@@ -78,6 +79,10 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_forward_algo.argtypes = fwd + [P, I]
     lib.kdn_validate_forward.argtypes = fwd + [I]
     lib.kdn_forward_gated.argtypes = fwd + [P, I]
+    lib.kdn_forward_split.argtypes = fwd + [I, P, ctypes.c_size_t, P]
+    lib.kdn_validate_forward_split.argtypes = fwd + [I, P, ctypes.c_size_t]
+    lib.kdn_forward_split_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kdn_forward_split_workspace_size.restype = ctypes.c_size_t
     lib.kdn_validate_forward_gated.argtypes = fwd + [I]
     step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
     lib.kdn_step.argtypes = step + [P]
@@ -194,6 +199,49 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
                               float(mu), var, _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0),
                               _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward")
+    return o, S_T, p_T
+
+
+def forward_split_workspace_size(B, T, H, dk, dv, segments=0) -> int:
+    """Workspace bytes of ``forward_split`` (0: no split for these sizes)."""
+    return int(load_library().kdn_forward_split_workspace_size(B, T, H, dk, dv, segments))
+
+
+def forward_split(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, segments=0, workspace=None, out=None):
+    """Diagonal KDN forward (bf16) with each sequence cut into segments that
+    run concurrently, for batches too small to fill the device.  segments: 0
+    chooses from the device, > 0 asks for about that many.  ``workspace``: a
+    uint8 device tensor of at least forward_split_workspace_size(...) bytes,
+    allocated here when None.  Arguments and results as ``forward``."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                         ("alpha", alpha, (B, T, H, dk)), ("omega", omega, (B, T, H, dk)), ("r", r, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if c0 is not None:
+        _need(c0, "c0", (H,), torch.float32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if p0 is not None:
+        _need(p0, "p0", (B, H, dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        p_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T, p_T = out
+    need = int(lib.kdn_forward_split_workspace_size(B, T, H, dk, dv, segments))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kdn_forward_split(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(omega), _ptr(r), _ptr(c0), float(mu),
+                               VARIANTS["diagonal"], _dtype_code(q), B, T, H, dk, dv, _ptr(S0), _ptr(p0), _ptr(o),
+                               _ptr(S_T), _ptr(p_T), int(segments), _ptr(workspace), int(workspace.numel()),
+                               _stream(dev))
+    _check(st, "kdn_forward_split")
     return o, S_T, p_T
 
 

@@ -251,9 +251,73 @@ int run_forward(kdn::FwdArgs a, hipStream_t s, int algo) {
     return hip_status(kdn::launch_recurrent(a, s), "recurrent forward");
 }
 
+// Sizes of the split forward: the segments used and the workspace they need.
+int split_nseg(int B, int T, int H, int dk, int dv, int segments) {
+    return kdn::split_segments(B, T, H, dk, dv, segments, segments > 0 ? 0 : kdn::device_cus());
+}
+
+int validate_forward_split(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                           const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H,
+                           int dk, int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                           int segments, void* work, size_t work_bytes) {
+    int st = validate_forward(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, o, S_T,
+                              p_T, KDN_ALGO_CHUNKED);
+    if (st != KDN_OK) return st;
+    if (variant != KDN_DIAGONAL || dtype != KDN_BF16)
+        return fail(KDN_ERR_UNSUPPORTED, "the split forward takes the diagonal variant with bf16 inputs");
+    if (segments < 0) return fail(KDN_ERR_VALUE, "segments must be >= 0 (got %d)", segments);
+    if (int64_t(B) * H == 0 || T == 0) return KDN_OK;
+    const int n = split_nseg(B, T, H, dk, dv, segments);
+    const size_t need = kdn::split_workspace_bytes(B, T, H, dk, dv, n);
+    if (need == 0) return KDN_OK;
+    if (!work || work_bytes < need)
+        return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, work_bytes);
+    if ((reinterpret_cast<uintptr_t>(work) & 15u) != 0)
+        return fail(KDN_ERR_WORKSPACE, "the workspace must be 16-byte aligned");
+    const size_t toks = size_t(B) * T * H, units = size_t(B) * H;
+    const Span ws = span(work, need, 1);
+    const Span other[] = {span(q, toks * dk, 2),      span(k, toks * dk, 2),     span(v, toks * dv, 2),
+                          span(alpha, toks * dk, 2),  span(omega, toks * dk, 2), span(r, toks, 2),
+                          span(c0, size_t(H), 4),     span(S0, units * dk * dv, 4), span(p0, units * dk, 4),
+                          span(o, toks * dv, 2),      span(S_T, units * dk * dv, 4), span(p_T, units * dk, 4)};
+    for (const Span& x : other)
+        if (overlap(ws, x)) return fail(KDN_ERR_ALIAS, "the workspace overlaps an input or an output");
+    return KDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t kdn_forward_split_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
+    if (B <= 0 || T <= 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || segments < 0) return 0;
+    return kdn::split_workspace_bytes(B, T, H, dk, dv, split_nseg(B, T, H, dk, dv, segments));
+}
+
+int kdn_validate_forward_split(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                               const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H,
+                               int dk, int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
+                               int segments, void* workspace, size_t workspace_bytes) {
+    const int st = validate_forward_split(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0,
+                                          o, S_T, p_T, segments, workspace, workspace_bytes);
+    return st == KDN_OK ? ok() : st;
+}
+
+int kdn_forward_split(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
+                      const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H, int dk,
+                      int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T, int segments,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate_forward_split(q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0,
+                                          o, S_T, p_T, segments, workspace, workspace_bytes);
+    if (st != KDN_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    const kdn::FwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, o, S_T, p_T};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) return run_forward(a, s, KDN_ALGO_AUTO);
+    if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
+    return hip_status(kdn::launch_split(a, split_nseg(B, T, H, dk, dv, segments), workspace, workspace_bytes, s),
+                      "split forward");
+}
 
 int kdn_version(void) { return 400; }  // 0.4.0: gate step, chunked widths
 

@@ -162,6 +162,16 @@ struct Args {
     const int* cu;   // packed sequences: sequence n owns tokens [cu[n], cu[n + 1]); NULL: B x T
     const int* ord;  // packed sequences: scheduling order of the sequences, or NULL
     size_t tok0;    // set per workgroup: the first token of its sequence in the token grid
+    // segment mode (seg > 0; diagonal, ungated): every sequence is cut into
+    // nseg segments of seg tokens, run concurrently.  Column tiles below
+    // vtiles hold v columns; the d_k tiles from vtiles on hold the identity
+    // columns (start I, v = 0) that carry the segment's state transition.
+    // Segment g starts from S = 0 (g > 0) or S0, and from the uncertainty its
+    // predecessors' Mobius products (mob) carry p0 to.
+    int seg = 0, nseg = 1, vtiles = 0;
+    const float* mob = nullptr;  // [B*H][nseg][DK][4] Mobius products of the segments
+    bf16_t* ophi = nullptr;      // o of the identity columns, [tokens][H][DK]
+    float* sseg = nullptr;       // segment end states [B*H][nseg][DK][DV + DK]
 };
 
 // position of token t of the workgroup's sequence (of head h) in the token
@@ -1016,7 +1026,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
     constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
     __shared__ Smem<DK> sm;
-    const int ntile = a.DV / DVTN;
+    const int ntile = a.seg ? a.vtiles + DK / DVTN : a.DV / DVTN;
     const int bid = blockIdx.x;
     // Work items are dealt to the eight XCDs in turn (block bid runs on XCD
     // bid % 8); the column tiles of one (batch, head) pair share an XCD and
@@ -1039,7 +1049,21 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     // sequences first the work spreads evenly over the CUs.  Their bounds
     // come from the offsets, clamped into the grid (a.T is then the grid's
     // token count), so no offset can reach outside it.
-    if (a.cu) {
+    int seg_g = 0;     // segment mode: this workgroup's segment
+    bool phi = false;  // segment mode: a tile of the identity columns
+    if (a.seg) {
+        const int nunit = a.units / a.nseg;  // (batch, head) pairs
+        seg_g = item / nunit;
+        const int u = item % nunit;
+        b = size_t(u / a.H);
+        h = u % a.H;
+        const int total = a.T;
+        const int s0 = seg_g * a.seg;
+        a.tok0 = b * size_t(total) + size_t(s0);
+        a.T = min(a.seg, total - s0);
+        phi = tile >= a.vtiles;
+        if (phi && seg_g == 0) return;  // the first segment starts from S0 itself
+    } else if (a.cu) {
         h = item % a.H;
         const int rank = item / a.H;
         b = size_t(a.ord ? min(max(a.ord[rank], 0), nbatch - 1) : rank);
@@ -1112,7 +1136,16 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const int i = wave * 64 + lane;
             float p = 0.f;
             const size_t pidx = (GR ? size_t(unit) * ntile + tile : size_t(unit)) * DK + i;
-            if (active) p = a.p0 ? a.p0[pidx] : a.c0[h];
+            if (active) {
+                p = a.p0 ? a.p0[pidx] : a.c0[h];
+                // segment mode: the uncertainty at the segment's start, the
+                // preceding segments' Mobius maps applied to p0 in order
+                for (int gg = 0; gg < seg_g; ++gg) {
+                    const float4 m = *reinterpret_cast<const float4*>(
+                        a.mob + ((size_t(unit) * a.nseg + gg) * DK + i) * 4);
+                    p = (m.x * p + m.y) / (m.z * p + m.w);
+                }
+            }
             settle(p);  // p is ready before the pipelined loop
             // chunk c's tiles are in LDS buffer c & 1 (chunk c + 1's are
             // fetched meanwhile by the formation waves); the loop runs two
@@ -1150,7 +1183,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 step(IntC<1>{}, c + 1);
             }
             bad_seen = sm.bad;
-            if (bad_seen >= nchunks && active && (GR || tile == 0)) a.p_T[pidx] = p;
+            if (bad_seen >= nchunks && active && (GR || tile == 0) && seg_g == a.nseg - 1) a.p_T[pidx] = p;
         } else if (wave == 1) {
             // the per-channel decays (isotropic variant with per-channel
             // decay; otherwise this wave only keeps the barrier count)
@@ -1239,13 +1272,30 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         const int n = lane & 15, g4 = (lane >> 4) * 4;
         StateAcc<DK, NCT> st;
         const size_t sbase = size_t(unit) * DK * a.DV;
+        const bool s0in = a.S0 && seg_g == 0;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    st.S[it][ct][e] = a.S0 ? a.S0[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * it + g4 + e, col = colb + 16 * ct + n;
+                    st.S[it][ct][e] = phi ? (row == col - a.DV ? 1.f : 0.f)
+                                          : s0in ? a.S0[sbase + size_t(row) * a.DV + col] : 0.f;
+                }
+        // identity columns: v = 0 (their v ring holds zeros, never reloaded),
+        // o to the identity outputs
+        if (phi) {
+#pragma unroll
+            for (int sl = 0; sl < 3; ++sl)
+                for (int x = lane; x < L * 32 / 8; x += 64) *reinterpret_cast<u4*>(&sm.RV[sl][cw][8 * x]) = u4{0u, 0u, 0u, 0u};
+        }
+        Args ao = a;
+        if (phi) {
+            ao.o = a.ophi;
+            ao.DV = DK;
+        }
+        const int colo = phi ? colb - a.DV : colb;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
@@ -1257,7 +1307,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             bad_seen = sm.bad;
-            state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (!phi) state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
             vm_wait<NCT>();
             bar();
             if (VAR == 0) chain_diag_issue<DK, 0, 2>(sm, a, b, h, it + 2, nchunks, cw);
@@ -1275,7 +1325,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             bad_seen = sm.bad;
             const int fsub = sm.fsub[c % 3][0] | sm.fsub[c % 3][1];  // read early: its use is a segment away
             const bool run = c < nchunks && c < bad_seen;
-            state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (!phi) state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
             if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
             // everything but the NCT loads just issued has landed: the v of
             // chunk it - 1, the previous iteration's stores and chain rows
@@ -1287,19 +1337,22 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             if (run) {
                 const bool next = c + 1 < nchunks && c + 1 < bad_seen;
                 const int mode = !next ? 0 : fsub ? 2 : 1;
-                state_seg2<DK, NCT, VAR == 1>(st, sm, c & 1, a, b, h, colb, c, mode);
+                state_seg2<DK, NCT, VAR == 1>(st, sm, c & 1, ao, b, h, colo, c, mode);
             }
             bar();
         }
         bad_seen = sm.bad;
         if (bad_seen >= nchunks) {
+            // segment mode: the segment's end state, [v | identity] columns
+            float* sout = a.seg ? a.sseg + (size_t(unit) * a.nseg + seg_g) * DK * (a.DV + DK) : a.S_T + sbase;
+            const int sstride = a.seg ? a.DV + DK : a.DV;
 #pragma unroll
             for (int it = 0; it < DK / 16; ++it)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        a.S_T[sbase + size_t(16 * it + g4 + e) * a.DV + colb + 16 * ct + n] = st.S[it][ct][e];
+                        sout[size_t(16 * it + g4 + e) * sstride + colb + 16 * ct + n] = st.S[it][ct][e];
         } else {
             // hand-off: S_bad of this wave's columns
             vm_wait<0>();
@@ -1394,16 +1447,18 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) p[c] = hf.p[lane + 64 * c];
     }
-    const int col = tile * DVTN + lcol;  // column within the head
-    const rec::RecIO<bf16_t> io{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.o, a.mu, a.H, a.DV, h, a.tok0, col,
-                                ntile, tile, GATE};
+    const int col = tile * DVTN + lcol;  // column within the head ([v | identity] in segment mode)
+    // identity columns: no v, outputs to the identity outputs
+    const rec::RecIO<bf16_t> io{a.q, a.k, phi ? nullptr : a.v, a.alpha, a.omega, a.r, phi ? a.ophi : a.o, a.mu, a.H,
+                                phi ? DK : a.DV, h, a.tok0, phi ? col - a.DV : col, ntile, tile, GATE};
     rec::run_tokens<DK, VAR, bf16_t, GR>(io, S, p, pb, hf.chan[wave], bad_seen * L, a.T);
-    const size_t sbase = size_t(unit) * DK * a.DV;
+    float* sout = a.seg ? a.sseg + (size_t(unit) * a.nseg + seg_g) * DK * (a.DV + DK) : a.S_T + size_t(unit) * DK * a.DV;
+    const int sstride = a.seg ? a.DV + DK : a.DV;
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        *reinterpret_cast<float4*>(a.S_T + sbase + size_t(rg + 8 * m) * a.DV + col) =
+        *reinterpret_cast<float4*>(sout + size_t(rg + 8 * m) * sstride + col) =
             make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
-    if (wave == 0 && (GR || tile == 0)) {
+    if (wave == 0 && (GR || tile == 0) && seg_g == a.nseg - 1) {
         if (VAR != 0) {
             if (lane == 0) a.p_T[unit] = pb;
         } else {
@@ -1448,6 +1503,49 @@ hipError_t launch_t(const FwdArgs& f, hipStream_t stream) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Segment mode of the diagonal form (64-column tiles): B * H * nseg items,
+// each with d_v / 64 tiles of v columns and d_k / 64 tiles of identity columns.
+template <int DK>
+hipError_t launch_segments_t(const FwdArgs& f, int seg, int nseg, const float* mob, bf16_t* ophi, float* sseg,
+                             hipStream_t stream) {
+    const int units = f.B * f.H * nseg;
+    if (units == 0) return hipSuccess;
+    Args a;
+    a.q = static_cast<const bf16_t*>(f.q);
+    a.k = static_cast<const bf16_t*>(f.k);
+    a.v = static_cast<const bf16_t*>(f.v);
+    a.alpha = static_cast<const bf16_t*>(f.alpha);
+    a.omega = static_cast<const bf16_t*>(f.omega);
+    a.r = static_cast<const bf16_t*>(f.r);
+    a.c0 = f.c0;
+    a.mu = f.mu;
+    a.T = f.T;
+    a.H = f.H;
+    a.DV = f.dv;
+    a.units = units;
+    a.S0 = f.S0;
+    a.p0 = f.p0;
+    a.o = static_cast<bf16_t*>(f.o);
+    a.S_T = f.S_T;
+    a.p_T = f.p_T;
+    a.cu = nullptr;
+    a.ord = nullptr;
+    a.tok0 = 0;
+    a.seg = seg;
+    a.nseg = nseg;
+    a.vtiles = f.dv / DVT;
+    a.mob = mob;
+    a.ophi = ophi;
+    a.sseg = sseg;
+    const int ntile = a.vtiles + DK / DVT;
+    const int groups = (units + 7) / 8;
+    const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, 0, false, 2, false>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 // Compute units of the current device (read once per device and cached; 256
 // on MI355X).  A failed query gives 256.
 long device_cus() {
@@ -1462,6 +1560,8 @@ long device_cus() {
     }
     return n;
 }
+
+namespace {
 
 // Narrow workgroups (32 value columns) when the 64-column tiling leaves more
 // than half of the device's CUs without a workgroup: one workgroup holds one
@@ -1490,6 +1590,15 @@ bool chunked_supports(const FwdArgs& a) {
     // rows (isotropic), 8-byte stores of four output columns
     return aligned16(a.q) && aligned16(a.k) && aligned16(a.v) && aligned16(a.alpha) && aligned16(a.omega) &&
            (reinterpret_cast<uintptr_t>(a.o) & 7u) == 0;
+}
+
+hipError_t launch_chunked_segments(const FwdArgs& a, int seg, int nseg, const float* mob, void* ophi, float* sseg,
+                                   hipStream_t stream) {
+    if (!chunked_supports(a) || a.variant != 0 || a.gates || a.cu_seqlens || seg <= 0 || seg % L != 0 || nseg < 1)
+        return hipErrorNotSupported;
+    bf16_t* op = static_cast<bf16_t*>(ophi);
+    return a.dk == 128 ? launch_segments_t<128>(a, seg, nseg, mob, op, sseg, stream)
+                       : launch_segments_t<64>(a, seg, nseg, mob, op, sseg, stream);
 }
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {

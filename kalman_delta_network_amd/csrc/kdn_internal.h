@@ -97,6 +97,26 @@ hipError_t launch_recurrent(const FwdArgs& a, hipStream_t stream);
 // for shapes it does not handle (the caller then reports KDN_ERR_UNSUPPORTED).
 bool chunked_supports(const FwdArgs& a);
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream);
+// Compute units of the current device (cached per device; 256 if the query fails).
+long device_cus();
+
+// The diagonal forward of a long sequence cut into segments that run
+// concurrently (kdn_split.hip).  split_segments: the number of segments used
+// for these sizes (requested > 0: about that many; 0: chosen from the
+// device's cus; 1: no split).  split_workspace_bytes: device workspace of a
+// split with that many segments (0 when nseg < 2).  launch_split: the forward
+// (nseg < 2: the plain chunked forward; the workspace is then unused).
+int split_segments(int B, int T, int H, int dk, int dv, int requested, long cus);
+size_t split_workspace_bytes(int B, int T, int H, int dk, int dv, int nseg);
+hipError_t launch_split(const FwdArgs& a, int nseg, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+// Segment mode of the diagonal chunked forward (kdn_split.hip drives it): the
+// sequence cut into nseg segments of seg tokens (a multiple of 32) run
+// concurrently; mob: [B*H][nseg][dk][4] Mobius products of the segments'
+// uncertainty maps; ophi: [B*T][H][dk] bf16 outputs of the identity columns;
+// sseg: [B*H][nseg][dk][dv + dk] segment end states.
+hipError_t launch_chunked_segments(const FwdArgs& a, int seg, int nseg, const float* mob, void* ophi, float* sseg,
+                                   hipStream_t stream);
 // Chunkwise forward of the isotropic variant (variant 1) on Gram matrices of
 // the raw keys (kdn_iso.hip); narrow = 32 value columns per workgroup, else 64.
 // Same preconditions as launch_chunked, and T > 0.

@@ -69,7 +69,7 @@ template <typename Tin>
 struct RecIO {
     const Tin* q;
     const Tin* k;
-    const Tin* v;
+    const Tin* v;  // NULL: v = 0 (columns that carry a state transition)
     const Tin* alpha;
     const Tin* omega;
     const Tin* r;
@@ -186,7 +186,7 @@ __device__ __forceinline__ void run_tokens(const RecIO<Tin>& a, float (&S)[DK / 
         }
         float d[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d[j] = to_f32(a.v[tok * a.dv + a.col + j]) - A[j];
+        for (int j = 0; j < 4; ++j) d[j] = (a.v ? to_f32(a.v[tok * a.dv + a.col + j]) : 0.f) - A[j];
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
 #pragma unroll

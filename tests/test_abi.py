@@ -437,3 +437,49 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define KDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == kdn.NOALLOC_SCRATCH_BYTES
+
+
+# ---------------------------------------------------------------------------
+# kdn_forward_split: validation and workspace sizes (host only)
+# ---------------------------------------------------------------------------
+
+def call_validate_split(lib, a, segments, ws, ws_bytes):
+    return lib.kdn_validate_forward_split(a["q"], a["k"], a["v"], a["alpha"], a["omega"], a["r"], a["c0"],
+                                          a["mu"], a["variant"], a["dtype"], a["B"], a["T"], a["H"], a["dk"],
+                                          a["dv"], a["S0"], a["p0"], a["o"], a["S_T"], a["p_T"], segments, ws,
+                                          ws_bytes)
+
+
+def test_split_workspace_size(lib):
+    size = lib.kdn_forward_split_workspace_size
+    # no split: one segment asked for, or a sequence too short to cut
+    assert size(1, 8192, 2, 128, 128, 1) == 0
+    assert size(1, 40, 2, 128, 128, 4) == 0
+    # four segments of 2048 tokens (sub-segments of 256), B=1, H=2,
+    # d_k=d_v=128: sub-segment and
+    # segment products, identity-column outputs (bf16), end states [v | I]
+    # (fp32) and start states (bf16), each region rounded up to 256 bytes
+    units, nseg, nsub, T = 2, 4, 8, 8192
+    r256 = lambda x: (x + 255) // 256 * 256
+    want = (r256(units * nseg * nsub * 128 * 16) + r256(units * nseg * 128 * 16) + r256(T * 2 * 128 * 2)
+            + r256(units * nseg * 128 * 256 * 4) + r256(units * nseg * 128 * 128 * 2))
+    assert size(1, T, 2, 128, 128, 4) == want
+    assert size(0, T, 2, 128, 128, 4) == 0 and size(1, T, 2, 96, 128, 4) == 0 and size(1, T, 2, 128, 128, -1) == 0
+
+
+def test_validate_split(lib):
+    f = Fake()
+    a = fwd_args(f, B=1, T=8192, H=2, dk=128, dv=128)
+    need = lib.kdn_forward_split_workspace_size(1, 8192, 2, 128, 128, 4)
+    ws = f()
+    assert need > 0
+    assert call_validate_split(lib, a, 4, ws, need) == 0
+    assert call_validate_split(lib, a, 1, None, 0) == 0  # no split: no workspace needed
+    assert call_validate_split(lib, a, 4, None, need) == kdn.KDN_ERR_WORKSPACE
+    assert call_validate_split(lib, a, 4, ws, need - 1) == kdn.KDN_ERR_WORKSPACE
+    assert call_validate_split(lib, a, 4, ctypes.c_void_p(ws.value + 8), need) == kdn.KDN_ERR_WORKSPACE
+    assert call_validate_split(lib, a, 4, a["o"], need) == kdn.KDN_ERR_ALIAS
+    assert call_validate_split(lib, a, -1, ws, need) == kdn.KDN_ERR_VALUE
+    assert call_validate_split(lib, dict(a, variant=1), 4, ws, need) == kdn.KDN_ERR_UNSUPPORTED
+    assert call_validate_split(lib, dict(a, dtype=0), 4, ws, need) == kdn.KDN_ERR_UNSUPPORTED
+    assert call_validate_split(lib, dict(a, q=None), 4, ws, need) == kdn.KDN_ERR_NULL
