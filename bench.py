@@ -106,7 +106,9 @@ def chunked_workgroups(w, cus: int = 256) -> int:
 COUNTED = {
     "main": ("diag_bf16_b8_t4096_h16_d128", "kdn_chunk_kernel", ("kdn_chunked.hip", "kdn_device.h")),
     "isotropic": ("iso_bf16_b8_t4096_h16_d128", "kdn_iso_kernel", ("kdn_iso.hip", "kdn_device.h", "kdn_gates.h")),
-    "long_context": ("diag_bf16_b1_t65536_h16_d128", "kdn_chunk_kernel", ("kdn_chunked.hip", "kdn_device.h")),
+    # the split forward's kernels (Mobius pre-pass, chunked segments, state
+    # chaining, output correction): bytes per call
+    "long_context": ("diag_bf16_b1_t65536_h16_d128", "kdn_", ("kdn_chunked.hip", "kdn_split.hip", "kdn_device.h")),
     "decode": ("decode_diag_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
                ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
     "decode_isotropic": ("decode_iso_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
@@ -115,6 +117,11 @@ COUNTED = {
     # counters pass runs no other library kernel
     "backward": ("diag_bf16_b8_t4096_h16_d128", "kdn_", ("kdn_backward.hip",)),
 }
+
+
+def segments_of(kdn, w) -> int:
+    """Segments the split forward cuts w's sequences into on this device."""
+    return kdn.forward_split_segments(w.B, w.T, w.H, w.dk, w.dv)
 
 
 def kernel_source_hash(line: str = "main") -> str:
@@ -179,6 +186,12 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     if "z_alpha" in t:
         def call():
             kdn.forward_gated(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
+    elif algo == "split":
+        ws = torch.empty(max(1, kdn.forward_split_workspace_size(w.B, w.T, w.H, w.dk, w.dv)), dtype=torch.uint8,
+                         device=t["q"].device)
+
+        def call():
+            kdn.forward_split(**t, mu=w.mu, workspace=ws, out=out)
     else:
         def call():
             kdn.forward(**t, mu=w.mu, variant=w.variant, algo=algo, out=out)
@@ -309,6 +322,8 @@ def bench_backward(kdn, w, dev, steps, gated=False):
 
 
 COPY_BYTES = 512 << 20  # calibration copy for the HBM byte counters
+PER_CALL = ("backward", "long_context")  # lines of several kernels: bytes per call
+PER_CALL_RUNS = 4  # calls in their counters pass
 
 
 def counters_pass(args):
@@ -332,8 +347,14 @@ def counters_pass(args):
         bench_decode(kdn, w, dev, 16, warm_up=False)
     elif line == "backward":
         call, _ = backward_call(kdn, w, dev)
-        for _ in range(4):
+        for _ in range(PER_CALL_RUNS):
             call()
+    elif line == "long_context":
+        t = upload(wl.forward_inputs(w), w.dtype, dev)
+        ws = torch.empty(max(1, kdn.forward_split_workspace_size(w.B, w.T, w.H, w.dk, w.dv)), dtype=torch.uint8,
+                         device=dev)
+        for _ in range(PER_CALL_RUNS):
+            kdn.forward_split(**t, mu=w.mu, workspace=ws)
     else:
         t = upload(wl.forward_inputs(w), w.dtype, dev)
         for _ in range(3):
@@ -360,8 +381,9 @@ def _read_counter_csv(run_dir, counter):
 def traffic_from(fetch_dir, write_dir, out_path, algo, line):
     """HBM bytes per launch of a counted line's kernel from FETCH_SIZE /
     WRITE_SIZE (KiB per dispatch), each scaled by the same counter of the
-    calibration copy.  The backward's bytes are per backward call (the sum
-    over its kernels' dispatches, divided by the number of calls)."""
+    calibration copy.  The backward's and the split forward's bytes are per
+    call (the sum over their kernels' dispatches, divided by the number of
+    calls)."""
     res = {}
     kname = COUNTED[line][1]
     for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -371,7 +393,7 @@ def traffic_from(fetch_dir, write_dir, out_path, algo, line):
         if not copies or not hits:
             raise SystemExit(f"{counter}: no calibration copy or {kname} dispatch in {run_dir}")
         scale = COPY_BYTES / (max(copies) * 1024.0)  # bytes per counted byte
-        per = float(np.sum(hits)) / 4.0 if line == "backward" else float(np.mean(hits))  # 4 backward calls
+        per = float(np.sum(hits)) / PER_CALL_RUNS if line in PER_CALL else float(np.mean(hits))
         res[counter] = {"kib_per_launch": per, "dispatches": len(hits), "copy_kib": max(copies), "scale": scale,
                         "bytes_per_launch": per * 1024.0 * scale}
     entry = {"workload": COUNTED[line][0], "kernel": kname, "kernel_hash": kernel_source_hash(line), "algo": algo,
@@ -523,11 +545,14 @@ def main():
         del tz
         wlc = wl.WORKLOADS["diag_bf16_b1_t65536_h16_d128"]
         tlc = upload(wl.forward_inputs(wlc), wlc.dtype, dev)
-        mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "auto")
-        extra["long_context"] = {"workload": wlc.name, "tokens_per_s": wlc.B * wlc.T / (mlc / 1e3),
+        mlc, llc = time_forward(kdn, wlc, tlc, 3, 1, "split")
+        mlp, _ = time_forward(kdn, wlc, tlc, 2, 1, "auto")
+        extra["long_context"] = {"workload": wlc.name, "algo": "split", "tokens_per_s": wlc.B * wlc.T / (mlc / 1e3),
                                  "ms_per_step": mlc, "launch_ms": llc, "algorithmic_bytes": forward_bytes(wlc),
                                  "hbm_frac": forward_bytes(wlc) / (llc / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                 "workgroups": chunked_workgroups(
+                                 "segments": segments_of(kdn, wlc),
+                                 "ms_per_step_unsplit": mlp,
+                                 "workgroups_unsplit": chunked_workgroups(
                                      wlc, torch.cuda.get_device_properties(dev).multi_processor_count),
                                  "traffic": traffic_for("long_context")}
         del tlc

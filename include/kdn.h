@@ -197,6 +197,9 @@ int kdn_forward_split(const void* q, const void* k, const void* v, const void* a
                       const void* r, const float* c0, float mu, int variant, int dtype, int B, int T, int H, int dk,
                       int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T, int segments,
                       void* workspace, size_t workspace_bytes, void* stream);
+/* Segments kdn_forward_split cuts each sequence into for these sizes and
+ * segment request on the current device (1: no split; 0: invalid sizes). */
+int kdn_forward_split_segments(int B, int T, int H, int dk, int dv, int segments);
 /* Workspace bytes of kdn_forward_split for these sizes and segment request
  * (0 when no split is made or the sizes are invalid). */
 size_t kdn_forward_split_workspace_size(int B, int T, int H, int dk, int dv, int segments);

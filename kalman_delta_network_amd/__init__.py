@@ -51,7 +51,7 @@ def _p_shape(var, lead, dk, dv):
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
            "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated", "kdn_backward_gated",
            "kdn_backward_gated_workspace_size", "kdn_backward_noalloc", "kdn_forward_split",
-           "kdn_forward_split_workspace_size", "kdn_validate_forward_split",
+           "kdn_forward_split_segments", "kdn_forward_split_workspace_size", "kdn_validate_forward_split",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated",
            "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_validate_forward_split.argtypes = fwd + [I, P, ctypes.c_size_t]
     lib.kdn_forward_split_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kdn_forward_split_workspace_size.restype = ctypes.c_size_t
+    lib.kdn_forward_split_segments.argtypes = [I, I, I, I, I, I]
+    lib.kdn_forward_split_segments.restype = I
     lib.kdn_validate_forward_gated.argtypes = fwd + [I]
     step = [P, P, P, P, P, P, F, I, I, I, I, I, I, P, P, P]
     lib.kdn_step.argtypes = step + [P]
@@ -200,6 +202,11 @@ def forward(q, k, v, alpha, omega, r, c0, mu, variant="diagonal", S0=None, p0=No
                               _ptr(o), _ptr(S_T), _ptr(p_T), _stream(dev), ALGOS[algo])
     _check(st, "kdn_forward")
     return o, S_T, p_T
+
+
+def forward_split_segments(B, T, H, dk, dv, segments=0) -> int:
+    """Segments ``forward_split`` cuts each sequence into on this device."""
+    return int(load_library().kdn_forward_split_segments(B, T, H, dk, dv, segments))
 
 
 def forward_split_workspace_size(B, T, H, dk, dv, segments=0) -> int:

@@ -289,6 +289,11 @@ int validate_forward_split(const void* q, const void* k, const void* v, const vo
 
 extern "C" {
 
+int kdn_forward_split_segments(int B, int T, int H, int dk, int dv, int segments) {
+    if (B <= 0 || T <= 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || segments < 0) return 0;
+    return split_nseg(B, T, H, dk, dv, segments);
+}
+
 size_t kdn_forward_split_workspace_size(int B, int T, int H, int dk, int dv, int segments) {
     if (B <= 0 || T <= 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || segments < 0) return 0;
     return kdn::split_workspace_bytes(B, T, H, dk, dv, split_nseg(B, T, H, dk, dv, segments));

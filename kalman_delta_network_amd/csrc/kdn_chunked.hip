@@ -1448,10 +1448,11 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         for (int c = 0; c < CPL; ++c) p[c] = hf.p[lane + 64 * c];
     }
     const int col = tile * DVTN + lcol;  // column within the head ([v | identity] in segment mode)
-    // identity columns: no v, outputs to the identity outputs
+    // identity columns: v = 0 (not read), outputs to the identity outputs
     const rec::RecIO<bf16_t> io{a.q, a.k, phi ? nullptr : a.v, a.alpha, a.omega, a.r, phi ? a.ophi : a.o, a.mu, a.H,
                                 phi ? DK : a.DV, h, a.tok0, phi ? col - a.DV : col, ntile, tile, GATE};
-    rec::run_tokens<DK, VAR, bf16_t, GR>(io, S, p, pb, hf.chan[wave], bad_seen * L, a.T);
+    if (phi) rec::run_tokens<DK, VAR, bf16_t, GR, true>(io, S, p, pb, hf.chan[wave], bad_seen * L, a.T);
+    else rec::run_tokens<DK, VAR, bf16_t, GR>(io, S, p, pb, hf.chan[wave], bad_seen * L, a.T);
     float* sout = a.seg ? a.sseg + (size_t(unit) * a.nseg + seg_g) * DK * (a.DV + DK) : a.S_T + size_t(unit) * DK * a.DV;
     const int sstride = a.seg ? a.DV + DK : a.DV;
 #pragma unroll

@@ -69,7 +69,7 @@ template <typename Tin>
 struct RecIO {
     const Tin* q;
     const Tin* k;
-    const Tin* v;  // NULL: v = 0 (columns that carry a state transition)
+    const Tin* v;  // not read when run_tokens is instantiated with VZ (v = 0)
     const Tin* alpha;
     const Tin* omega;
     const Tin* r;
@@ -86,8 +86,9 @@ struct RecIO {
 
 // Tokens [t_begin, t_end) of the sequence.  S: rows rg + 8 m, columns
 // col .. col + 3; p: channels lane + 64 c (diagonal) or pb (isotropic forms).
-// chan: this wave's own LDS slice of d_k float4.
-template <int DK, int VAR, typename Tin, bool GR>
+// chan: this wave's own LDS slice of d_k float4.  VZ: v = 0 (columns that
+// carry a state transition; a.v is not read).
+template <int DK, int VAR, typename Tin, bool GR, bool VZ = false>
 __device__ __forceinline__ void run_tokens(const RecIO<Tin>& a, float (&S)[DK / 8][4], float (&p)[DK / 64],
                                            float& pb, float4* chan, int t_begin, int t_end) {
     constexpr bool ISO = VAR != 0;   // one uncertainty scalar per head
@@ -186,7 +187,7 @@ __device__ __forceinline__ void run_tokens(const RecIO<Tin>& a, float (&S)[DK / 
         }
         float d[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d[j] = (a.v ? to_f32(a.v[tok * a.dv + a.col + j]) : 0.f) - A[j];
+        for (int j = 0; j < 4; ++j) d[j] = (VZ ? 0.f : to_f32(a.v[tok * a.dv + a.col + j])) - A[j];
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
 #pragma unroll

@@ -467,6 +467,19 @@ def test_split_workspace_size(lib):
     assert size(0, T, 2, 128, 128, 4) == 0 and size(1, T, 2, 96, 128, 4) == 0 and size(1, T, 2, 128, 128, -1) == 0
 
 
+def test_split_segments(lib):
+    seg = lib.kdn_forward_split_segments
+    assert seg(1, 8192, 2, 128, 128, 4) == 4
+    assert seg(1, 8192, 2, 128, 128, 1) == 1
+    assert seg(1, 1000, 2, 128, 128, 3) == 3  # segments of 352, 352 and 296 tokens
+    assert seg(1, 40, 2, 128, 128, 4) == 1    # too short to cut
+    assert seg(0, 8192, 2, 128, 128, 4) == 0 and seg(1, 8192, 2, 128, 128, -1) == 0
+    # chosen: as many segments as fill the compute units (here at least the
+    # 256 of the fallback when no device is visible, or the device's own)
+    assert seg(8, 4096, 16, 128, 128, 0) == 1  # B x H already fills the device
+    assert seg(1, 65536, 16, 128, 128, 0) >= 2
+
+
 def test_validate_split(lib):
     f = Fake()
     a = fwd_args(f, B=1, T=8192, H=2, dk=128, dv=128)
