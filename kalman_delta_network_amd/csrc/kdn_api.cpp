@@ -324,7 +324,7 @@ int kdn_forward_split(const void* q, const void* k, const void* v, const void* a
                       "split forward");
 }
 
-int kdn_version(void) { return 400; }  // 0.4.0: gate step, chunked widths
+int kdn_version(void) { return 500; }  // 0.5.0: split forward, isotropic Gram kernel
 
 const char* kdn_status_string(int status) {
     switch (status) {

@@ -1577,10 +1577,10 @@ template <int DK>
 hipError_t launch_gated(const FwdArgs& a, hipStream_t stream) {
     if (narrow_pays(a)) {
         if (a.variant == 2) return launch_t<DK, 2, false, 1, true>(a, stream);
-        return a.variant == 1 ? launch_t<DK, 1, false, 1, true>(a, stream) : launch_t<DK, 0, false, 1, true>(a, stream);
+        return launch_t<DK, 0, false, 1, true>(a, stream);
     }
     if (a.variant == 2) return launch_t<DK, 2, false, 2, true>(a, stream);
-    return a.variant == 1 ? launch_t<DK, 1, false, 2, true>(a, stream) : launch_t<DK, 0, false, 2, true>(a, stream);
+    return launch_t<DK, 0, false, 2, true>(a, stream);
 }
 
 }  // namespace
@@ -1606,6 +1606,8 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
     if (!chunked_supports(a)) return hipErrorNotSupported;
     if (a.variant == 3 && a.chunk_width == dvt_of<1>()) return hipErrorNotSupported;  // groups are 64 columns
     if (a.T == 0) return launch_recurrent(a, stream);  // only copies the initial state
+    // the plain isotropic variant runs in its own kernel (kdn_iso.hip); the
+    // isotropic chain below serves the per-channel-decay form (variant 2)
     if (a.variant == 1) return launch_iso(a, narrow_pays(a), stream);
     if (a.gates) {
         // the gate step inside (alpha, omega, r as pre-activations)
@@ -1617,18 +1619,18 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t stream) {
         if (a.variant == 3) return launch_t<128, 0, true>(a, stream);
         if (narrow_pays(a)) {
             if (a.variant == 2) return launch_t<128, 2, false, 1>(a, stream);
-            return a.variant == 1 ? launch_t<128, 1, false, 1>(a, stream) : launch_t<128, 0, false, 1>(a, stream);
+            return launch_t<128, 0, false, 1>(a, stream);
         }
         if (a.variant == 2) return launch_t<128, 2>(a, stream);
-        return a.variant == 1 ? launch_t<128, 1>(a, stream) : launch_t<128, 0>(a, stream);
+        return launch_t<128, 0>(a, stream);
     }
     if (a.variant == 3) return launch_t<64, 0, true>(a, stream);
     if (narrow_pays(a)) {
         if (a.variant == 2) return launch_t<64, 2, false, 1>(a, stream);
-        return a.variant == 1 ? launch_t<64, 1, false, 1>(a, stream) : launch_t<64, 0, false, 1>(a, stream);
+        return launch_t<64, 0, false, 1>(a, stream);
     }
     if (a.variant == 2) return launch_t<64, 2>(a, stream);
-    return a.variant == 1 ? launch_t<64, 1>(a, stream) : launch_t<64, 0>(a, stream);
+    return launch_t<64, 0>(a, stream);
 }
 
 }  // namespace kdn
