@@ -143,10 +143,13 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
                      const float* p0, void* o, float* S_T, float* p_T, void* stream, int algo);
 
 /*
- * kdn_forward_gated -- kdn_forward with the gate step done inside the kernel
- * (summary page, method step 1, and its core-method paragraph: decay, process
- * noise and observation noise come from the token through sigmoid / softplus):
- * the three gate arguments hold pre-activations, and the kernel uses
+ * kdn_forward_gated -- kdn_forward with the step before the recurrence done
+ * inside the kernel (summary page, method step 1, and its core-method
+ * paragraph: decay, process noise and observation noise come from the token
+ * through sigmoid / softplus; the information scaling mu = d_k assumes
+ * unit-norm keys).  q and k are raw: each [d_k] row is divided by
+ * max(|row|, 1e-6) (queries like keys).  The three gate arguments hold
+ * pre-activations, and the kernel uses
  *
  *   alpha = sigmoid(z_alpha)          decay
  *   omega = softplus(z_omega)         process noise
@@ -155,9 +158,10 @@ int kdn_forward_algo(const void* q, const void* k, const void* v, const void* al
  * in place of alpha, omega and r, in the layouts kdn_forward gives them for
  * the variant (KDN_DIAGONAL, KDN_ISOTROPIC or KDN_ISOTROPIC_CHANNEL;
  * KDN_DIAGONAL_GROUPED returns KDN_ERR_UNSUPPORTED).  Same dtypes, alignment,
- * algorithms, aliasing rules and results as kdn_forward_algo fed with those
- * values (up to fp32 rounding of the gates: about 1 ulp each, and at most
- * about 6e-8 absolute in softplus); no extra memory is read or written.
+ * algorithms, aliasing rules and results as kdn_forward_algo fed with the
+ * normalised q, k and those values (up to fp32 rounding: about 1 ulp in each
+ * gate and norm, at most about 6e-8 absolute in softplus); no extra memory is
+ * read or written.
  */
 int kdn_forward_gated(const void* q, const void* k, const void* v, const void* z_alpha,
                       const void* z_omega, const void* z_r, const float* c0, float mu, int variant,
@@ -209,19 +213,21 @@ int kdn_validate_forward_split(const void* q, const void* k, const void* v, cons
                                int dk, int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
                                int segments, void* workspace, size_t workspace_bytes);
 
-/* kdn_forward_varlen with the gate step of kdn_forward_gated: z_alpha,
- * z_omega and z_r are pre-activations in the layouts of alpha, omega and r
- * (not KDN_DIAGONAL_GROUPED).  Same checks and results as kdn_forward_varlen
- * fed with the gated values. */
+/* kdn_forward_varlen with the step of kdn_forward_gated: raw q and k,
+ * normalised per row inside the kernel, and z_alpha, z_omega, z_r
+ * pre-activations in the layouts of alpha, omega and r (not
+ * KDN_DIAGONAL_GROUPED).  Same checks and results as kdn_forward_varlen fed
+ * with the normalised and gated values. */
 int kdn_forward_varlen_gated(const void* q, const void* k, const void* v, const void* z_alpha,
                              const void* z_omega, const void* z_r, const int* cu_seqlens, const int* order,
                              const float* c0, float mu, int variant, int dtype, int N, int total, int H, int dk,
                              int dv, const float* S0, const float* p0, void* o, float* S_T, float* p_T,
                              void* stream, int algo);
 
-/* kdn_step with the gate step of kdn_forward_gated: z_alpha, z_omega and
- * z_r are pre-activations in the layouts of alpha, omega and r (not
- * KDN_DIAGONAL_GROUPED).  S and p are updated in place as by kdn_step. */
+/* kdn_step with the step of kdn_forward_gated: raw q and k, normalised per
+ * row inside the kernel, and z_alpha, z_omega, z_r pre-activations in the
+ * layouts of alpha, omega and r (not KDN_DIAGONAL_GROUPED).  S and p are
+ * updated in place as by kdn_step. */
 int kdn_step_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
                    const void* z_r, float mu, int variant, int dtype, int N, int H, int dk, int dv,
                    float* S, float* p, void* o, void* stream);
@@ -389,9 +395,12 @@ int kdn_validate_forward_varlen(const void* q, const void* k, const void* v, con
 const char* kdn_status_string(int status);
 /*
  * kdn_backward_gated -- kdn_backward of the gated layer (kdn_forward_gated):
- * z_alpha, z_omega, z_r are the gate pre-activations (layouts of alpha, omega
- * and r; not KDN_DIAGONAL_GROUPED), and dz_alpha, dz_omega, dz_r receive the
- * gradients with respect to them (fp32, same layouts):
+ * q and k are raw, z_alpha, z_omega, z_r the gate pre-activations (layouts
+ * of alpha, omega and r; not KDN_DIAGONAL_GROUPED).  dq and dk receive the
+ * gradients with respect to the raw rows, dz_alpha, dz_omega, dz_r those
+ * with respect to the pre-activations (fp32, same layouts):
+ *   dx = (dx_hat - x_hat (x_hat . dx_hat)) / |x|   (dx_hat / 1e-6 where
+ *        |x| < 1e-6),
  *   dz_alpha = d alpha * sigmoid(z) sigmoid(-z),  dz_omega = d omega * sigmoid(z),
  *   dz_r = d r * sigmoid(z).
  * Everything else as kdn_backward, except the workspace:
@@ -406,7 +415,8 @@ int kdn_backward_gated(const void* q, const void* k, const void* v, const void* 
 
 /* Workspace bytes of kdn_backward_gated: the adjoint's workspace
  * (kdn_backward_workspace_size) rounded up to 256 bytes, then fp32 copies of
- * q, k, v, dO and the gated alpha, omega, r, each rounded up to 256 bytes.
+ * the normalised q and k, of v and dO, and the gated alpha, omega, r, each
+ * rounded up to 256 bytes.
  * 0 for negative sizes, an unknown variant or grouped noise. */
 size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv);
 

@@ -254,11 +254,13 @@ def forward_split(q, k, v, alpha, omega, r, c0, mu, S0=None, p0=None, segments=0
 
 def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, variant="diagonal", S0=None, p0=None, algo="auto",
                   out=None):
-    """KDN forward with the gate step inside the kernel: z_alpha, z_omega and
-    z_r are pre-activations in the layouts ``forward`` gives alpha, omega and
-    r for the variant ("diagonal", "isotropic" or "isochannel"), and the
-    kernel uses alpha = sigmoid(z_alpha), omega = softplus(z_omega),
-    r = 0.01 + softplus(z_r).  Other arguments and results as ``forward``."""
+    """KDN forward with the step before the recurrence inside the kernel: q
+    and k are raw (each [dk] row is divided by max(|row|, 1e-6)); z_alpha,
+    z_omega and z_r are pre-activations in the layouts ``forward`` gives
+    alpha, omega and r for the variant ("diagonal", "isotropic" or
+    "isochannel"), and the kernel uses alpha = sigmoid(z_alpha),
+    omega = softplus(z_omega), r = 0.01 + softplus(z_r).  Other arguments and
+    results as ``forward``."""
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
@@ -380,9 +382,10 @@ def step(q, k, v, alpha, omega, r, mu, S, p, variant="diagonal", o=None):
 
 
 def step_gated(q, k, v, z_alpha, z_omega, z_r, mu, S, p, variant="diagonal", o=None):
-    """One decode step from gate pre-activations z_alpha, z_omega, z_r in the
-    layouts ``step`` gives alpha, omega, r (the kernel applies sigmoid,
-    softplus and 0.01 + softplus); S and p float32 are updated in place.
+    """One decode step from raw q, k (normalised per row inside the kernel)
+    and gate pre-activations z_alpha, z_omega, z_r in the layouts ``step``
+    gives alpha, omega, r (the kernel applies sigmoid, softplus and
+    0.01 + softplus); S and p float32 are updated in place.
     Returns o [N,H,dv]."""
     torch = _torch()
     lib = load_library()
@@ -408,8 +411,9 @@ def step_gated(q, k, v, z_alpha, z_omega, z_r, mu, S, p, variant="diagonal", o=N
 
 def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, variant="diagonal", S0=None,
                          p0=None, algo="auto", order=None):
-    """``forward_varlen`` from gate pre-activations z_alpha, z_omega, z_r in
-    the layouts ``forward_varlen`` gives alpha, omega, r."""
+    """``forward_varlen`` from raw q, k (normalised per row inside the
+    kernel) and gate pre-activations z_alpha, z_omega, z_r in the layouts
+    ``forward_varlen`` gives alpha, omega, r."""
     torch = _torch()
     lib = load_library()
     var = VARIANTS[variant]
@@ -485,7 +489,7 @@ def backward_gated_workspace_size(B, T, H, dk, dv, variant="diagonal") -> int:
 def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
                    S0=None, p0=None, workspace=None):
     """Gradients of the gated forward (``forward_gated``) with respect to its
-    inputs, the gate pre-activations included.  Arguments as ``backward``
+    inputs: the raw q, k and the gate pre-activations included.  Arguments as ``backward``
     with z_alpha, z_omega, z_r in place of alpha, omega, r; the workspace is
     backward_gated_workspace_size() bytes.  Returns dq, dk, dv, dz_alpha,
     dz_omega, dz_r, dS0, dp0, dc0."""

@@ -324,7 +324,7 @@ int kdn_forward_split(const void* q, const void* k, const void* v, const void* a
                       "split forward");
 }
 
-int kdn_version(void) { return 500; }  // 0.5.0: split forward, isotropic Gram kernel
+int kdn_version(void) { return 600; }  // 0.6.0: the gated entry points normalise q and k
 
 const char* kdn_status_string(int status) {
     switch (status) {

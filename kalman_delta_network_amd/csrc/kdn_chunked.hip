@@ -108,6 +108,8 @@ struct Smem {
     alignas(16) bf16_t RW[2][L * DK];
     alignas(16) bf16_t GQ[2][L * DK];    // g_t,i (diagonal variant)  [t / 8][i][t % 8]
     alignas(16) float cr[2][64];         // mu / r_t of the chain's chunks (lane t)
+    alignas(16) float ks[2][L];          // gated: 1 / |k_t| of the chain's chunks (the prologue's normalisation)
+    alignas(16) float qs[2][L];          // gated: 1 / |q_t| (formed with the chunk, applied to its outputs)
     alignas(16) float gL[3][DK];         // gb_31, the second half's decay, fp32 (ring of three chunks)
     alignas(16) float g15[3][DK];        // g_15, the first half's decay, fp32 (ring of three chunks)
     alignas(16) float fL[3][DK];         // gb_31 of chunk c times g_15 of chunk c + 1 (slot c % 3)
@@ -225,6 +227,40 @@ __device__ __forceinline__ void chain_r_store(Smem<DK>& sm, int c, uint32_t rbit
     if (lane < L) sm.rr[c % 3][lane] = rt;
 }
 
+// Gated form, diagonal variant: 1 / |k_t| of tokens 16 hf + 4f .. + 3 of the
+// chain's chunk in buffer `buf`, from its raw k tile (16 lanes per row), by
+// formation wave f.  Rows 16..31 of the chain's current chunk are read in the
+// first half of an iteration (the chain reads their norms after the mid
+// barrier), rows 0..15 of its next chunk after that barrier (the state waves'
+// copies of them have landed by then).
+template <int DK>
+__device__ __forceinline__ void chain_knorm_store(Smem<DK>& sm, int buf, int f, int hf) {
+    const int lane = threadIdx.x & 63;
+    const int row = 16 * hf + 4 * f + (lane >> 4), part = lane & 15;
+    constexpr int PER = DK / 16;  // channels per lane: 8 or 4
+    const bf16_t* src = &sm.RK[buf][row * DK + part * PER];
+    float s = 0.f;
+    if (PER == 8) {
+        const u4 x = *reinterpret_cast<const u4*>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
+            s = fmaf(x0, x0, s);
+            s = fmaf(x1, x1, s);
+        }
+    } else {
+        const u2 x = *reinterpret_cast<const u2*>(src);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float x0 = bf_lo(x[e]), x1 = bf_hi(x[e]);
+            s = fmaf(x0, x0, s);
+            s = fmaf(x1, x1, s);
+        }
+    }
+    s = sum16(s);
+    if (part == 0) sm.ks[buf][row] = inv_norm(s);
+}
+
 // r_t of chunk c for lane t (lanes >= L repeat the chunk's last token).
 // GR: grouped observation noise, r [.., ntile] with one entry per group of
 // DVT value columns; this workgroup's columns are group `tile`
@@ -311,6 +347,14 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
     float cv[NTOK];
 #pragma unroll
     for (int j = 0; j < NTOK; ++j) cv[j] = sm.cr[buf][T0 + j];  // same address on every lane: broadcast
+    float kn[GATE ? NTOK : 1];  // gated: 1 / |k_t| (the prologue's normalisation of k)
+    if (GATE)
+#pragma unroll
+        for (int j = 0; j < NTOK; j += 4) {
+            const f4 x = *reinterpret_cast<const f4*>(&sm.ks[buf][T0 + j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kn[j + e] = x[e];
+        }
     chain_read16<DK, BUF, T0>(in, uint32_t(reinterpret_cast<uintptr_t>((lds_void_t*)&sm.RK[0][i])));
     float kk[NTOK], al[NTOK], w[NTOK], khv[NTOK], gv[NTOK];
     float ez[NTOK];                        // GATE: e^-z of the decay's pre-activation
@@ -321,6 +365,7 @@ __device__ __forceinline__ void chain_diag_run(Smem<DK>& sm, ChainIn& in, int i,
         al[j] = __uint_as_float(in.x[CHAIN_SLOTS + j]);
         w[j] = __uint_as_float(in.x[2 * CHAIN_SLOTS + j]);
         if (GATE) {
+            kk[j] *= kn[j];
             // the decay alpha = 1 / (1 + e^-z) and the process noise from
             // their pre-activations; e^-z is kept for 1 / g below
             ez[j] = __builtin_amdgcn_exp2f(-kLog2E * al[j]);
@@ -492,6 +537,13 @@ __device__ __forceinline__ void chain_iso_run(const ChainIsoRegs<VAR>& X, Smem<D
     }
     const float w = ok ? wz * (1.f / float(DK)) : 0.f;
     const float rt = ok ? rz : 1.f;
+    // gated: the prologue's normalisation of k (|k_hat|^2 = |k|^2 / |k|^2;
+    // the formation scales its k rows by the same factor)
+    const float sk = GATE ? inv_norm(n) : 1.f;
+    if (GATE) {
+        n *= sk * sk;
+        if (lane < L) sm.ks[buf][lane] = sk;
+    }
     const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
     // the uncertainty's decay: alpha^2, or with per-channel decay the trace
     // projection mean_i alpha_i^2 (padding tokens: 1)
@@ -660,7 +712,39 @@ __device__ __forceinline__ void form_load(FormRegs<DK>& X, const Args& a, size_t
     }
 }
 
-template <int DK, int VAR, bool MASK>
+// 1 / |q_t| (floored norm, the prologue's normalisation) of the formation
+// wave's 8 tokens 8f .. 8f + 7 from their bf16 rows in registers (lane l:
+// channels CPL l ..) into qs[buf].  Each of the first three exchanges halves
+// the set of tokens a lane sums: afterwards lane l holds token
+// 4 b5 + 2 b4 + b3 (its bits 5, 4, 3), summed over those three lane bits; a
+// sum over the aligned 8-lane group adds the rest.
+template <int DK>
+__device__ __forceinline__ void form_qnorm_store(Smem<DK>& sm, const uint32_t (&xp)[8], int buf, int f) {
+    const int lane = threadIdx.x & 63;
+    float v[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const float x0 = bf_lo(xp[tt]);
+        v[tt] = x0 * x0;
+        if (DK == 128) {
+            const float x1 = bf_hi(xp[tt]);
+            v[tt] = fmaf(x1, x1, v[tt]);
+        }
+    }
+    float w4[4], w2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w4[j] = halve32(v[j], v[4 + j]);  // bit 5 set: tokens 4..7
+#pragma unroll
+    for (int j = 0; j < 2; ++j) w2[j] = halve16(w4[j], w4[2 + j]);  // bit 4 set: the upper pair
+    // the row rotation by 8 brings lane i the lane whose bit 3 differs: it
+    // sends the token this lane keeps
+    const bool b3 = lane & 8;
+    float w1 = (b3 ? w2[1] : w2[0]) + dpp_mov<kDppRor8>(b3 ? w2[0] : w2[1]);
+    w1 = sum8(w1);
+    if ((lane & 7) == 0) sm.qs[buf][8 * f + 4 * (lane >> 5) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1)] = inv_norm(w1);
+}
+
+template <int DK, int VAR, bool MASK, bool GATE = false>
 __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, int nb, int kslot, int f, int nvalid) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head (Kh formed here)
     const int lane = threadIdx.x & 63;
@@ -674,6 +758,17 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
     u4 gq[CPL];     // g of channel i0 + cc, tokens 8f .. 8f + 7 (per-channel decay)
     u2 kq[CPL][2];  // kappa'/g of channel i0 + cc, tokens 8f + 4h .. 8f + 4h + 3 (diagonal variant)
     float gsv[8], bhv[8];  // isotropic scalars: g_t (scalar decay) and b_hat_t
+    // gated: the prologue's 1 / |k_t|, stored with the chain's inputs.  (q
+    // enters unnormalised: every output term is linear in q_t, so the state
+    // scales output row t by 1 / |q_t| instead; this wave forms those below.)
+    float skv[GATE ? 8 : 1];
+    if (GATE)
+#pragma unroll
+        for (int j = 0; j < 8; j += 4) {
+            const f4 x = *reinterpret_cast<const f4*>(&sm.ks[nb][8 * f + j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) skv[j + e] = x[e];
+        }
     if (ISO) {
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
@@ -712,6 +807,9 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             kk[CPL - 1] = bf_hi(kp);
             qq[CPL - 1] = bf_hi(qp);
         }
+        if (GATE)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) kk[cc] *= skv[tt];
         uint32_t khw;  // this lane's Kh entries of token t
         if (VAR == 1) {
             const float sc = bhv[tt] * __builtin_amdgcn_rcpf(gsv[tt]);
@@ -766,6 +864,7 @@ __device__ __forceinline__ void form_run(const FormRegs<DK>& X, Smem<DK>& sm, in
             }
         }
     }
+    if (GATE) form_qnorm_store<DK>(sm, X.qp, nb, f);
 }
 
 // M, tril(Qt Kh^T) and the diagonal-block inverses of chunk buffer nb; the
@@ -945,7 +1044,7 @@ __device__ __forceinline__ void state_scale(StateAcc<DK, NCT>& st, Smem<DK>& sm,
 // the next one is outside the chunked form's range), 1 fL (the next chunk's
 // Sg in one multiply), 2 gb_31 then g_15 of the next chunk (fL would leave
 // the normal fp32 range).  SC: one decay per token, factors at index 0.
-template <int DK, int NCT, bool SC>
+template <int DK, int NCT, bool SC, bool GATE>
 __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
                                            int h, int colb, int c, int mode) {
     const int gring = c % 3;
@@ -975,9 +1074,11 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
         const bool ok = full || c * L + 16 * at + n < a.T;
+        const float sq = GATE ? sm.qs[b][16 * at + n] : 1.f;  // gated: the prologue's 1 / |q_t|
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const f4 o = mfma32(Db[ct], aqk[at], st.O[at][ct]);  // (tril(Qt Kh^T) Dn)^T
+            f4 o = mfma32(Db[ct], aqk[at], st.O[at][ct]);  // (tril(Qt Kh^T) Dn)^T
+            if (GATE) o *= sq;
             if (ok) *reinterpret_cast<u2*>(orow + 16 * ct) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
         }
         orow += ostep;
@@ -1115,6 +1216,10 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     if (threadIdx.x < 6) sm.fsub[threadIdx.x >> 1][threadIdx.x & 1] = 0;
     vm_wait<0>();  // chunk 0's tiles and r have landed
     if (VAR == 0 && is_form && fwave == 3) chain_r_store<DK, GATE>(sm, 0, r0, min(L, a.T), a.mu);
+    if (GATE && VAR == 0) {
+        bar();  // every wave's copies of chunk 0's k rows have landed
+        if (is_form) chain_knorm_store<DK>(sm, 0, fwave, 0);  // rows 16..31: in the loop
+    }
     bar();
 
     // Range flags.  A chain flags chunk c (sm.bad, the smallest such c)
@@ -1337,7 +1442,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             if (run) {
                 const bool next = c + 1 < nchunks && c + 1 < bad_seen;
                 const int mode = !next ? 0 : fsub ? 2 : 1;
-                state_seg2<DK, NCT, VAR == 1>(st, sm, c & 1, ao, b, h, colo, c, mode);
+                state_seg2<DK, NCT, VAR == 1, GATE>(st, sm, c & 1, ao, b, h, colo, c, mode);
             }
             bar();
         }
@@ -1384,12 +1489,14 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     if (f == 3) rnext = chain_r_load<GR>(a, b, h, c + 2, nchunks, tile, ntile);
                 }
                 form_load<DK>(Y, a, b, h, f, c + 1, nchunks);
+                if (GATE && VAR == 0 && c + 1 < nchunks) chain_knorm_store<DK>(sm, (c + 1) & 1, f, 1);
                 if (c >= 0 && c < nchunks) {
                     const int nvalid = min(L, a.T - c * L);
-                    if (nvalid == L) form_run<DK, VAR, false>(X, sm, c & 1, c % 3, f, L);
-                    else form_run<DK, VAR, true>(X, sm, c & 1, c % 3, f, nvalid);
+                    if (nvalid == L) form_run<DK, VAR, false, GATE>(X, sm, c & 1, c % 3, f, L);
+                    else form_run<DK, VAR, true, GATE>(X, sm, c & 1, c % 3, f, nvalid);
                 }
                 bar();
+                if (GATE && VAR == 0 && c + 2 < nchunks) chain_knorm_store<DK>(sm, c & 1, f, 0);
                 if (c >= 0 && c < nchunks) mphase<DK>(sm, c & 1, c % 3, f);
                 // everything issued this iteration has landed: the chain's tiles
                 // for chunk c + 2 and q, k of chunk c + 1.  Settling the latter

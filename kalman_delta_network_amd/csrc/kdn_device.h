@@ -93,6 +93,45 @@ __device__ __forceinline__ int sw(int row, int col) {
     return row * DK + ((((col >> 3) ^ row) & (NCH - 1)) << 3) + (col & 7);
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane sums on VALU data moves, with no round trip through the LDS
+// crossbar (a ds_bpermute chain costs its latency at every step, which a role
+// run by one wave per SIMD cannot hide).  v_permlane32_swap exchanges lanes
+// 32..63 of its first operand with lanes 0..31 of its second;
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second.  DPP moves data inside a 16-lane row.  All 64
+// lanes must be active.
+// ---------------------------------------------------------------------------
+// lanes 0..31: a[i] + a[i + 32]; lanes 32..63: b[i - 32] + b[i]
+__device__ __forceinline__ float halve32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// lanes with bit 4 clear: a[i] + a[i + 16]; set: b[i - 16] + b[i]
+__device__ __forceinline__ float halve16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8-lane half row <- lane 7 - i
+constexpr int kDppRor8 = 0x128;       // lane i of each row <- lane (i + 8) mod 16, i.e. i ^ 8
+// sum over the aligned group of 8 lanes, in each of them
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    return x + dpp_mov<kDppHalfMirror>(x);
+}
+// sum over the 16-lane row, in each of its lanes
+__device__ __forceinline__ float sum16(float x) {
+    x = sum8(x);
+    return x + dpp_mov<kDppRor8>(x);
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -3,11 +3,15 @@
 // Memory", summary page, method step 1: alpha = sigmoid(z), omega =
 // softplus(z), r = r_min + softplus(z)).
 //
+// The step also normalises q and k per token-head, x_hat = x / max(|x|, eps).
+//
 // The backward of the recurrence is the fp32 one of kdn_backward.hip, run on
-// the gated values: one elementwise pass widens q, k, v and dO to fp32 and
-// evaluates the gates into the workspace (the same fp32 gate functions as the
-// gated forward), the adjoint runs on them, and a second elementwise pass
-// turns d alpha, d omega, d r into gradients of the pre-activations:
+// the prologue's values: one pass widens v and dO to fp32, normalises the q
+// and k rows and evaluates the gates into the workspace (the same fp32
+// functions as the gated forward), the adjoint runs on them, and a second
+// pass turns the gradients of those values into gradients of the raw inputs:
+//   d x = (d x_hat - x_hat (x_hat . d x_hat)) / |x|   (d x_hat / eps where
+//         |x| < eps: the map is then x / eps),
 //   d z_alpha = d alpha * sigmoid(z) sigmoid(-z),
 //   d z_omega = d omega * sigmoid(z),   d z_r = d r * sigmoid(z).
 // Both passes move a few bytes per token next to the adjoint's recomputation,
@@ -57,6 +61,55 @@ __global__ void __launch_bounds__(256) gate_grad_kernel(const Tin* __restrict__ 
     }
 }
 
+// |x|^2 of row `row` (dk channels), in every lane of the calling wave
+template <typename Tin>
+__device__ __forceinline__ float row_sumsq(const Tin* __restrict__ x, size_t row, int dk) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    for (int i = lane; i < dk; i += 64) {
+        const float v = widen(x[row * dk + i]);
+        s = fmaf(v, v, s);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    return s;
+}
+
+// y = x / max(|x|, eps) per row of dk channels (one wave per row)
+template <typename Tin>
+__global__ void __launch_bounds__(256) row_normalize_kernel(const Tin* __restrict__ x, float* __restrict__ y,
+                                                            size_t rows, int dk) {
+    const int lane = threadIdx.x & 63;
+    const size_t waves = size_t(gridDim.x) * (blockDim.x / 64);
+    for (size_t row = size_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); row < rows; row += waves) {
+        const float inv = inv_norm(row_sumsq(x, row, dk));
+        for (int i = lane; i < dk; i += 64) y[row * dk + i] = widen(x[row * dk + i]) * inv;
+    }
+}
+
+// d <- the gradient of the raw rows x given d = the gradient of their
+// normalised rows (one wave per row)
+template <typename Tin>
+__global__ void __launch_bounds__(256) row_normalize_grad_kernel(const Tin* __restrict__ x, float* __restrict__ d,
+                                                                 size_t rows, int dk) {
+    const int lane = threadIdx.x & 63;
+    const size_t waves = size_t(gridDim.x) * (blockDim.x / 64);
+    for (size_t row = size_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); row < rows; row += waves) {
+        const float nrm = sqrtf(row_sumsq(x, row, dk));
+        const bool floored = !(nrm >= kNormEps);
+        const float inv = 1.f / (floored ? kNormEps : nrm);
+        float proj = 0.f;  // x_hat . d
+        for (int i = lane; i < dk; i += 64) proj = fmaf(widen(x[row * dk + i]) * inv, d[row * dk + i], proj);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) proj += __shfl_xor(proj, off, 64);
+        if (floored) proj = 0.f;
+        for (int i = lane; i < dk; i += 64) {
+            const size_t e = row * dk + i;
+            d[e] = (d[e] - widen(x[e]) * inv * proj) * inv;
+        }
+    }
+}
+
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct GatedSizes {
@@ -91,8 +144,14 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(gate_forward_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(x), y,
                            count, op);
     };
-    fwd(a.q, fq, n.nk, kCopy);
-    fwd(a.k, fk, n.nk, kCopy);
+    const size_t rows = size_t(a.B) * size_t(a.T) * size_t(a.H);
+    const unsigned row_blocks = unsigned(rows / 4 + 1 < 8192 ? rows / 4 + 1 : 8192);  // 4 rows per block
+    if (rows) {
+        hipLaunchKernelGGL(row_normalize_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s, static_cast<const Tin*>(a.q),
+                           fq, rows, a.dk);
+        hipLaunchKernelGGL(row_normalize_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s, static_cast<const Tin*>(a.k),
+                           fk, rows, a.dk);
+    }
     fwd(a.v, fv, n.nv, kCopy);
     fwd(a.alpha, fa, n.na, kSigmoid);
     fwd(a.omega, fw, n.nw, kSoftplus);
@@ -117,6 +176,12 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(gate_grad_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(z), d,
                            count, op);
     };
+    if (rows) {
+        hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
+                           static_cast<const Tin*>(a.q), a.dq, rows, a.dk);
+        hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
+                           static_cast<const Tin*>(a.k), a.dk_, rows, a.dk);
+    }
     grad(a.alpha, a.dalpha, n.na, kSigmoid);
     grad(a.omega, a.domega, n.nw, kSoftplus);
     grad(a.r, a.dr, n.nr, kSoftplus);

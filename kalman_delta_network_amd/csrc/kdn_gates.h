@@ -22,6 +22,14 @@
 namespace kdn {
 
 constexpr float kGateRMin = 0.01f;
+// The step before the recurrence also normalises q and k per token-head:
+// x / max(|x|, kNormEps) over the d_k channels (unit-norm keys, summary page,
+// core method; queries alike).
+constexpr float kNormEps = 1e-6f;
+// 1 / max(sqrt(s), eps) = rsqrt(max(s, eps^2)) (eps^2 is a normal fp32 number)
+__device__ __forceinline__ float inv_norm(float sumsq) {
+    return __builtin_amdgcn_rsqf(fmaxf(sumsq, kNormEps * kNormEps));
+}
 constexpr float kLog2E = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

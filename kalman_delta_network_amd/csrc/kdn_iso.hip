@@ -75,7 +75,8 @@ struct IsoSmem {
     alignas(16) bf16_t Q[KR][L * DK];     // q tiles [t][sw(i)]
     alignas(16) bf16_t KT[2][L * DK];     // k^T [P / 8][i][P % 8] with P = perm32(t): the update's A operand
     alignas(16) bf16_t RV[3][L * 64];     // v tiles of the state waves ([wave][t][16 NCW columns]), ring of three
-    alignas(16) float sc[4][4][L];        // per chunk (slot c % 4): r, b_hat, G, row weight 2^G Gamma_c
+    alignas(16) float sc[4][6][L];        // per chunk (slot c % 4): r, b_hat, G, row weight of R (2^G Gamma_c;
+                                          // gated: times 1/|k_t|), 1/|k_t| (gated), row weight of O (gated)
     alignas(16) float ws[4][L];           // update column weights w_s / (the frame change), per chunk
     alignas(16) float ch[4][4];           // per chunk: the C-input factor of the update (1 = none), Gamma_c
     alignas(16) bf16_t P[3][L * PT];      // tril(P) [t][perm32(s)] (ring of three)
@@ -83,6 +84,7 @@ struct IsoSmem {
     alignas(16) bf16_t Mo[3][256];        // -M_10 [t][s]
     alignas(16) float Md[2][NT * 256];    // M's diagonal blocks, column-major [a][s][t]
     alignas(16) float Wi[NT][2][64];      // block-inverse scratch
+    alignas(16) float qn[L];              // 1/|q_t| of the Gram-P wave's chunk (gated)
 };
 
 struct IsoArgs {
@@ -203,6 +205,9 @@ __device__ __forceinline__ void scan_run(const ScanRegs& X, IsoSmem<DK>& sm, int
     const float asq = al * al;
     const float w = ok ? wz * (1.f / float(DK)) : 0.f;
     const float rt = ok ? rz : 1.f;
+    // gated: the prologue's normalisation of k (|k_hat|^2 = |k|^2 / |k|^2)
+    const float sk = GATE ? inv_norm(n) : 1.f;
+    if (GATE) n *= sk * sk;
     const float cn = ok ? (mu / (float(DK) * rt)) * n : 0.f;
     // this token's Mobius matrix [[m00, m01], [m10, m11]], composed over the
     // chunk's tokens by an inclusive scan; G by an inclusive sum
@@ -227,11 +232,16 @@ __device__ __forceinline__ void scan_run(const ScanRegs& X, IsoSmem<DK>& sm, int
     const float wcol = bh * __builtin_amdgcn_exp2f(gL - g);  // w_s
     const int slot = c & 3;
     if (lane < L) {
+        const float rw = __builtin_amdgcn_exp2f(g) * gam;  // row weight of R and O: 2^G_t Gamma_c
         sm.sc[slot][0][lane] = rt;
         sm.sc[slot][1][lane] = bh;
         sm.sc[slot][2][lane] = g;
-        sm.sc[slot][3][lane] = __builtin_amdgcn_exp2f(g) * gam;  // row weight of R and O: 2^G_t Gamma_c
-        sm.ws[slot][lane] = absorb ? wcol * __builtin_amdgcn_rcpf(gnext) : wcol;
+        sm.sc[slot][3][lane] = rw * sk;  // gated: R's rows of K S~ use k_hat = k / |k|
+        sm.ws[slot][lane] = (absorb ? wcol * __builtin_amdgcn_rcpf(gnext) : wcol) * sk;
+        if (GATE) {
+            sm.sc[slot][4][lane] = sk;
+            sm.sc[slot][5][lane] = rw;  // times 1/|q_t| by the Gram-P wave
+        }
     }
     if (lane == 0) {
         sm.ch[slot][0] = absorb ? 1.f : gnext;  // the update's C-input factor
@@ -315,8 +325,19 @@ __device__ __forceinline__ f4 pair_weights(const IsoSmem<DK>& sm, int slot, int 
     return wv;
 }
 
-// M's diagonal blocks (fp32, column-major) and -M_10 (bf16) of the chunk in slot `slot`
+// the prologue's key scales of a tile pair (gated): 1/|k_t| of rows 16 ta + g4 + e
+// times 1/|k_s| of column 16 tb + n
 template <int DK>
+__device__ __forceinline__ f4 key_scales(const IsoSmem<DK>& sm, int slot, int ta, int tb) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    const f4 st = *reinterpret_cast<const f4*>(&sm.sc[slot][4][16 * ta + g4]);
+    const float ss = sm.sc[slot][4][16 * tb + n];
+    return f4{st[0] * ss, st[1] * ss, st[2] * ss, st[3] * ss};
+}
+
+// M's diagonal blocks (fp32, column-major) and -M_10 (bf16) of the chunk in slot `slot`
+template <int DK, bool GATE>
 __device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int md, int mo) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4;
@@ -324,7 +345,8 @@ __device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
         const f4 acc = gram_tile<DK>(a ? k1 : k0, a ? k1 : k0);
-        const f4 wv = pair_weights<DK>(sm, slot, a, a);
+        f4 wv = pair_weights<DK>(sm, slot, a, a);
+        if (GATE) wv *= key_scales<DK>(sm, slot, a, a);
         const f4 rv = *reinterpret_cast<const f4*>(&sm.sc[slot][0][16 * a + g4]);
         f4 mv;
 #pragma unroll
@@ -332,21 +354,54 @@ __device__ __forceinline__ void gram_m(IsoSmem<DK>& sm, int kslot, int slot, int
         *reinterpret_cast<f4*>(&sm.Md[md][a * 256 + n * 16 + g4]) = mv;
     }
     const f4 acc = gram_tile<DK>(k1, k0);
-    const f4 wv = pair_weights<DK>(sm, slot, 1, 0);
+    f4 wv = pair_weights<DK>(sm, slot, 1, 0);
+    if (GATE) wv *= key_scales<DK>(sm, slot, 1, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.Mo[mo][(g4 + e) * 16 + n] = to_bf(-wv[e] * acc[e]);
 }
 
-// P = tril(weighted Q K^T) of the chunk, bf16 [t][perm32(s)]
+// |x|^2 of row 16 ta + n of a row tile, in every lane of column n
 template <int DK>
+__device__ __forceinline__ float row_sumsq(const RowTile<DK>& t) {
+    float s = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = static_cast<float>(t.x[kk][j]);
+            s = fmaf(x, x, s);
+        }
+    s = halve16(s, s);
+    return halve32(s, s);
+}
+
+// P = tril(weighted Q K^T) of the chunk, bf16 [t][perm32(s)].  Gated: the
+// prologue's 1/|q_t| (from the q tiles, here) and 1/|k_s| go into P's
+// weights, and 1/|q_t| into O's row weights.
+template <int DK, bool GATE>
 __device__ __forceinline__ void gram_p(IsoSmem<DK>& sm, int kslot, int slot, int pslot) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4;
     const RowTile<DK> k0 = row_tile<DK>(sm.K[kslot], 0), k1 = row_tile<DK>(sm.K[kslot], 1);
     const RowTile<DK> q0 = row_tile<DK>(sm.Q[kslot], 0), q1 = row_tile<DK>(sm.Q[kslot], 1);
     const f4 a00 = gram_tile<DK>(q0, k0), a10 = gram_tile<DK>(q1, k0), a11 = gram_tile<DK>(q1, k1);
-    const f4 w00 = pair_weights<DK>(sm, slot, 0, 0), w10 = pair_weights<DK>(sm, slot, 1, 0),
-             w11 = pair_weights<DK>(sm, slot, 1, 1);
+    f4 w00 = pair_weights<DK>(sm, slot, 0, 0), w10 = pair_weights<DK>(sm, slot, 1, 0),
+       w11 = pair_weights<DK>(sm, slot, 1, 1);
+    if (GATE) {
+        const float sq0 = inv_norm(row_sumsq<DK>(q0)), sq1 = inv_norm(row_sumsq<DK>(q1));
+        if (lane < 16) {
+            sm.qn[n] = sq0;
+            sm.qn[16 + n] = sq1;
+            sm.sc[slot][5][n] *= sq0;
+            sm.sc[slot][5][16 + n] *= sq1;
+        }
+        wave_lds_sync();
+        const f4 qa0 = *reinterpret_cast<const f4*>(&sm.qn[g4]), qa1 = *reinterpret_cast<const f4*>(&sm.qn[16 + g4]);
+        const float ks0 = sm.sc[slot][4][n], ks1 = sm.sc[slot][4][16 + n];
+        w00 *= qa0 * ks0;
+        w10 *= qa1 * ks0;
+        w11 *= qa1 * ks1;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         sm.P[pslot][(g4 + e) * PT + perm32(n)] = to_bf(w00[e] * a00[e]);
@@ -437,7 +492,7 @@ struct SegCarry {
     b8 Dw[NCW];     // diag(w) Dn for the update
 };
 
-template <int DK, int NCW>
+template <int DK, int NCW, bool GATE>
 __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& cy, IsoSmem<DK>& sm, int c,
                                          int sw_) {
     const int lane = threadIdx.x & 63;
@@ -463,7 +518,8 @@ __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& c
         }
         rw[at] = *reinterpret_cast<const f4*>(&sm.sc[slot][3][16 * at + g4]);
     }
-    const float rq0 = sm.sc[slot][3][n], rq1 = sm.sc[slot][3][16 + n];
+    // O's row weights (gated: with 1/|q_t|; otherwise R's)
+    const float rq0 = sm.sc[slot][GATE ? 5 : 3][n], rq1 = sm.sc[slot][GATE ? 5 : 3][16 + n];
     const f4 wc0 = *reinterpret_cast<const f4*>(&sm.ws[slot][g4]);
     const f4 wc1 = *reinterpret_cast<const f4*>(&sm.ws[slot][16 + g4]);
     const s4 t0 = *reinterpret_cast<const s4*>(&sm.Td[mb][n * 16 + g4]);
@@ -632,7 +688,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         // ---------------- M of chunk i - 1; k^T of chunk i - 2 ----------------
         for (int i = 0; i < nit; ++i) {
             const int c = i - 1;
-            if (c >= 0 && c < nchunks) gram_m<DK>(sm, c % KR, c & 3, c & 1, c % 3);
+            if (c >= 0 && c < nchunks) gram_m<DK, GATE>(sm, c % KR, c & 3, c & 1, c % 3);
             if (c >= 1 && c <= nchunks) transpose_k<DK>(sm.KT[(c - 1) & 1], sm.K[(c - 1) % KR]);
             bar();
         }
@@ -651,7 +707,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
             tile_issue<DK>(sm.K[(i + 2) % KR], a.k, a, h, i + 2, nchunks);
             tile_issue<DK>(sm.Q[(i + 2) % KR], a.q, a, h, i + 2, nchunks);
             const int c = i - 1;
-            if (c >= 0 && c < nchunks) gram_p<DK>(sm, c % KR, c & 3, c % 3);
+            if (c >= 0 && c < nchunks) gram_p<DK, GATE>(sm, c % KR, c & 3, c % 3);
             vm_wait<NK>();  // chunk i + 1 (copied at iteration i - 1) has landed; chunk i + 2 may not have
             bar();
         }
@@ -691,7 +747,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
                 if (i >= 5) vm_wait<2 * NS + 2 * NV>();
                 else if (i == 4) vm_wait<NS + 2 * NV>();
                 else vm_wait<2 * NV>();
-                iso_seg1<DK, NCW>(st, cy, sm, c, sw_);
+                iso_seg1<DK, NCW, GATE>(st, cy, sm, c, sw_);
                 iso_seg2<DK, NCW>(st, cy, sm, a, h, col0, c);
             }
             bar();

@@ -110,6 +110,21 @@ __device__ __forceinline__ void run_tokens(const RecIO<Tin>& a, float (&S)[DK / 
             kk[c] = to_f32(a.k[tok * DK + lane + 64 * c]);
             qq[c] = to_f32(a.q[tok * DK + lane + 64 * c]);
         }
+        if (a.gates) {
+            // the prologue's normalisation of q and k (over the d_k channels)
+            float nk = 0.f, nq = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                nk = fmaf(kk[c], kk[c], nk);
+                nq = fmaf(qq[c], qq[c], nq);
+            }
+            const float sk = inv_norm(wave_sum(nk)), sq = inv_norm(wave_sum(nq));
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                kk[c] *= sk;
+                qq[c] *= sq;
+            }
+        }
         if (ISO) {
             // trace-projected predict b_hat = a b + omega / d_k; a = alpha^2,
             // or with per-channel decay the mean of alpha_i^2 over the channels

@@ -151,16 +151,18 @@ def forward_inputs(w: Workload) -> dict:
 
 
 def gated_inputs(w: Workload) -> dict:
-    """Inputs of one gated forward: q, k, v as in ``forward_inputs`` and, in
-    place of alpha, omega and r, their gate pre-activations
-    z_alpha ~ N(alpha_loc, 0.5), z_omega ~ N(omega_loc, 1), z_r ~ N(0, 1) in
-    the variant's layouts (the distributions whose gated values
-    ``forward_inputs`` draws), all rounded to bf16 for bf16 workloads; c0 [H]."""
+    """Inputs of one gated forward, the step before the recurrence still to
+    do: raw q, k ~ N(0, 1) (the gated forward normalises them), v as in
+    ``forward_inputs`` and, in place of alpha, omega and r, their gate
+    pre-activations z_alpha ~ N(alpha_loc, 0.5), z_omega ~ N(omega_loc, 1),
+    z_r ~ N(0, 1) in the variant's layouts (the distributions whose gated
+    values ``forward_inputs`` draws), all rounded to bf16 for bf16 workloads;
+    c0 [H]."""
     rng = np.random.default_rng([w.seed, 0x6A])
     lead = (w.B, w.T, w.H)
     out = {
-        "q": _l2norm(_normal(rng, lead + (w.dk,))),
-        "k": _l2norm(_normal(rng, lead + (w.dk,))),
+        "q": _normal(rng, lead + (w.dk,)),
+        "k": _normal(rng, lead + (w.dk,)),
         "v": _normal(rng, lead + (w.dv,)),
         "z_alpha": _normal(rng, lead + (w.dk,) if w.variant in ("diagonal", "isochannel") else lead,
                            w.alpha_loc, 0.5),

@@ -328,26 +328,63 @@ def gates(z_alpha, z_omega, z_r):
     return sigmoid(_f64(z_alpha)), softplus(_f64(z_omega)), R_MIN + softplus(_f64(z_r))
 
 
-def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, variant="diagonal"):
-    """The forward fed through the gate step: ``gates`` on the
-    pre-activations, then ``forward_diag`` / ``forward_iso`` /
-    ``forward_isoc`` on the resulting alpha, omega, r (the gates are
-    elementwise, so they apply to every variant's layouts alike)."""
+NORM_EPS = 1e-6  # smallest norm l2norm divides by (a zero row stays zero)
+
+
+def l2norm(x):
+    """Each row of x (last axis: the d_k channels of one token-head) divided by
+    its Euclidean norm, in fp64: the unit-norm keys the summary page's
+    information scaling mu = d_k assumes (core method), queries alike.  Rows
+    of norm below NORM_EPS are divided by NORM_EPS."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, NORM_EPS)
+
+
+def prologue(q, k, z_alpha, z_omega, z_r):
+    """The step before the recurrence (summary page, method step 1, and the
+    unit-norm keys of the core method): q and k L2-normalised per
+    token-head, then the gates.  Returns (q_hat, k_hat, alpha, omega, r)."""
     alpha, omega, r = gates(z_alpha, z_omega, z_r)
+    return l2norm(q), l2norm(k), alpha, omega, r
+
+
+def forward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, S0=None, p0=None, variant="diagonal"):
+    """The forward fed through ``prologue``: q and k normalised, the gates on
+    the pre-activations, then ``forward_diag`` / ``forward_iso`` /
+    ``forward_isoc`` (the gates are elementwise, so they apply to every
+    variant's layouts alike)."""
+    qh, kh, alpha, omega, r = prologue(q, k, z_alpha, z_omega, z_r)
     fn = {"diagonal": forward_diag, "isotropic": forward_iso, "isochannel": forward_isoc}[variant]
-    return fn(q, k, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
+    return fn(qh, kh, v, alpha, omega, r, c0, mu, S0=S0, p0=p0)
+
+
+def l2norm_backward(x, dxh):
+    """Cotangent of the raw rows x given the cotangent dxh of l2norm(x): with
+    n = |x| (>= NORM_EPS), dx = (dxh - xh (xh . dxh)) / n; below NORM_EPS the
+    map is x / NORM_EPS and dx = dxh / NORM_EPS."""
+    x, dxh = _f64(x), _f64(dxh)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    big = n >= NORM_EPS
+    nn = np.where(big, n, NORM_EPS)
+    xh = x / nn
+    proj = np.sum(xh * dxh, axis=-1, keepdims=True)
+    return np.where(big, (dxh - xh * proj) / nn, dxh / NORM_EPS)
 
 
 def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, dp_T=None, S0=None, p0=None,
                    variant="diagonal"):
-    """Gradients of ``forward_gated``: ``backward`` on the gated values, then
-    the chain rule through the gates, d z_alpha = d alpha sigmoid'(z_alpha)
-    with sigmoid' = sigmoid (1 - sigmoid), d z_omega = d omega
-    sigmoid(z_omega) and d z_r = d r sigmoid(z_r) (softplus' = sigmoid).
+    """Gradients of ``forward_gated``: ``backward`` on the prologue's values,
+    then the chain rule through it: d q = l2norm_backward(q, d q_hat) (and k
+    alike), d z_alpha = d alpha sigmoid'(z_alpha) with sigmoid' = sigmoid
+    (1 - sigmoid), d z_omega = d omega sigmoid(z_omega) and d z_r = d r
+    sigmoid(z_r) (softplus' = sigmoid).
     Returns dq, dk, dv, dz_alpha, dz_omega, dz_r, dS0, dp0, dc0."""
-    alpha, omega, r = gates(z_alpha, z_omega, z_r)
-    g = backward(q, k, v, alpha, omega, r, c0, mu, dO=dO, dS_T=dS_T, dp_T=dp_T, S0=S0, p0=p0, variant=variant)
-    out = {n: g[n] for n in ("dq", "dk", "dv", "dS0", "dp0", "dc0")}
+    qh, kh, alpha, omega, r = prologue(q, k, z_alpha, z_omega, z_r)
+    g = backward(qh, kh, v, alpha, omega, r, c0, mu, dO=dO, dS_T=dS_T, dp_T=dp_T, S0=S0, p0=p0, variant=variant)
+    out = {n: g[n] for n in ("dv", "dS0", "dp0", "dc0")}
+    out["dq"] = l2norm_backward(q, g["dq"])
+    out["dk"] = l2norm_backward(k, g["dk"])
     out["dz_alpha"] = g["dalpha"] * alpha * (1.0 - alpha)
     out["dz_omega"] = g["domega"] * sigmoid(_f64(z_omega))
     out["dz_r"] = g["dr"] * sigmoid(_f64(z_r))

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(kdn.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kdn_version() == 500
+    assert lib.kdn_version() == 600
 
 
 def test_status_strings(lib):

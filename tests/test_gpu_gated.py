@@ -1,8 +1,9 @@
 """GPU parity of the gated forward (kdn_forward_gated and its decode and
-packed-batch forms: the gate step alpha = sigmoid(z), omega = softplus(z),
-r = 0.01 + softplus(z) done inside the kernels, for the diagonal, isotropic
-and per-channel-decay isotropic variants) against oracle.forward_gated on the
-same pre-activations, through the C ABI.  Tolerance: max relative error 1e-4
+packed-batch forms: the step before the recurrence done inside the kernels,
+q and k L2-normalised per token-head and the gates alpha = sigmoid(z),
+omega = softplus(z), r = 0.01 + softplus(z), for the diagonal, isotropic and
+per-channel-decay isotropic variants) against oracle.forward_gated /
+oracle.prologue on the same raw q, k and pre-activations, through the C ABI.  Tolerance: max relative error 1e-4
 (fp32 inputs) or 2e-2 (bf16 inputs, fp32 state), per output tensor."""
 import numpy as np
 import pytest
@@ -153,9 +154,9 @@ def test_gated_decode_steps(dev, variant):
         tok = {n: np.ascontiguousarray(x[n][:, s]) for n in GATED}
         t = {n: torch.from_numpy(tok[n]).to(torch.bfloat16).to(dev) for n in GATED}
         o = kdn.step_gated(**t, mu=w.mu, S=S, p=p, variant=variant)
-        a, om, r = oracle.gates(tok["z_alpha"], tok["z_omega"], tok["z_r"])
+        qh, kh, a, om, r = oracle.prologue(tok["q"], tok["k"], tok["z_alpha"], tok["z_omega"], tok["z_r"])
         fn = {"diagonal": oracle.step_diag, "isotropic": oracle.step_iso, "isochannel": oracle.step_isoc}[variant]
-        ref = fn(tok["q"], tok["k"], tok["v"], a, om, r, mu=w.mu, S=Sr, p=pr)
+        ref = fn(qh, kh, tok["v"], a, om, r, mu=w.mu, S=Sr, p=pr)
         Sr, pr = ref["S"], ref["p"]
         torch.cuda.synchronize()
         check(f"gated/decode/{variant}/step{s}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()),
@@ -178,7 +179,6 @@ def test_gated_packed_batch(dev, variant, algo):
                                        cu_seqlens=torch.from_numpy(cu).to(dev), mu=w.mu, variant=variant, algo=algo,
                                        order=torch.from_numpy(kdn.longest_first(cu)).to(dev))
     torch.cuda.synchronize()
-    a, om, r = oracle.gates(x["z_alpha"], x["z_omega"], x["z_r"])
-    ref = oracle.forward_varlen(x["q"], x["k"], x["v"], a, om, r, c0=x["c0"], mu=w.mu, cu_seqlens=cu,
-                                variant=variant)
+    qh, kh, a, om, r = oracle.prologue(x["q"], x["k"], x["z_alpha"], x["z_omega"], x["z_r"])
+    ref = oracle.forward_varlen(qh, kh, x["v"], a, om, r, c0=x["c0"], mu=w.mu, cu_seqlens=cu, variant=variant)
     check(f"gated/varlen/{variant}/{algo}", (o.float().cpu().numpy(), S.cpu().numpy(), p.cpu().numpy()), ref, "bf16")

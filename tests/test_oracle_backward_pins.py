@@ -139,7 +139,7 @@ def test_gated_backward_matches_finite_differences_of_the_gated_forward(variant)
 
     g = oracle.backward_gated(**{n: z[n] for n in names}, c0=z["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
                               dp_T=ct["dp_T"], variant=variant)
-    for name in ("z_alpha", "z_omega", "z_r", "k"):
+    for name in ("z_alpha", "z_omega", "z_r", "k", "q"):
         arr = z[name]
         fd = np.zeros(arr.shape)
         flat, gflat = arr.reshape(-1), fd.reshape(-1)
@@ -153,3 +153,40 @@ def test_gated_backward_matches_finite_differences_of_the_gated_forward(variant)
             flat[e] = base
             gflat[e] = (lp - lm) / (2 * h)
         _check(g["d" + name], fd, name)
+
+
+def test_l2norm_backward_matches_finite_differences():
+    # the cotangent of the raw rows through the normalisation, against
+    # central differences of <l2norm(x), c>, including a row below the floor
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((4, 3, 8))
+    x[1, 2] *= 1e-9
+    c = rng.standard_normal(x.shape)
+    g = oracle.l2norm_backward(x, c)
+    fd = np.zeros(x.shape)
+    flat, gf = x.reshape(-1), fd.reshape(-1)
+    for e in range(flat.size):
+        base = flat[e]
+        h = 1e-7 * max(1e-6, abs(base))
+        flat[e] = base + h
+        lp = np.sum(oracle.l2norm(x) * c)
+        flat[e] = base - h
+        lm = np.sum(oracle.l2norm(x) * c)
+        flat[e] = base
+        gf[e] = (lp - lm) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-6 * np.max(np.abs(fd)))
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
+def test_gated_backward_q_k_gradients_are_orthogonal_to_the_rows(variant):
+    # the loss depends on q and k only through q / |q| and k / |k|, so the
+    # gradient of each row is orthogonal to the row
+    w, x, ct, _ = _case(variant, False, seed=52)
+    z = {n: np.asarray(a, np.float64) for n, a in wl.gated_inputs(w).items()}
+    names = ("q", "k", "v", "z_alpha", "z_omega", "z_r")
+    g = oracle.backward_gated(**{n: z[n] for n in names}, c0=z["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
+                              dp_T=ct["dp_T"], variant=variant)
+    for n in ("q", "k"):
+        dot = np.sum(g["d" + n] * z[n], axis=-1)
+        scale = np.max(np.abs(g["d" + n])) * np.max(np.linalg.norm(z[n], axis=-1))
+        assert np.max(np.abs(dot)) < 1e-12 * scale, n

@@ -613,7 +613,46 @@ def test_gated_forward_inverts_through_logit_and_inverse_softplus():
     za = np.log(a) - np.log1p(-a)
     zw = np.log(np.expm1(om))
     zr = np.log(np.expm1(r - 0.01))
-    ref = oracle.forward_diag(x["q"], x["k"], x["v"], a, om, r, x["c0"], w.mu)
-    got = oracle.forward_gated(x["q"], x["k"], x["v"], za, zw, zr, x["c0"], w.mu)
+    q, k = oracle.l2norm(x["q"]), oracle.l2norm(x["k"])  # unit rows: the prologue's normalisation is exact
+    ref = oracle.forward_diag(q, k, x["v"], a, om, r, x["c0"], w.mu)
+    got = oracle.forward_gated(q, k, x["v"], za, zw, zr, x["c0"], w.mu)
     for key in ("o", "S", "p"):
         assert np.allclose(got[key], ref[key], rtol=1e-10, atol=1e-12), key
+
+
+def test_l2norm_rows():
+    # unit rows along the last axis; a row and any positive multiple of it
+    # give the same row; a zero row stays zero; a row below the floor is
+    # divided by the floor
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 5, 2, 16))
+    y = oracle.l2norm(x)
+    np.testing.assert_allclose(np.sum(y * y, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.l2norm(x * rng.uniform(0.01, 100.0, (3, 5, 2, 1))), y, rtol=1e-13)
+    assert np.all(oracle.l2norm(np.zeros((2, 8))) == 0.0)
+    tiny = np.full((1, 4), 1e-9)
+    np.testing.assert_allclose(oracle.l2norm(tiny), tiny / oracle.NORM_EPS, rtol=1e-15)
+
+
+@pytest.mark.parametrize("variant", ["diagonal", "isotropic", "isochannel"])
+def test_gated_forward_is_scale_invariant_in_q_and_k(variant):
+    # the prologue normalises q and k per token-head (over d_k): scaling each
+    # (b, t, h) row of q and of k by its own positive factor changes nothing,
+    # and a normalisation over another axis, or none, fails
+    w, x = small(variant, T=29, seed=43)
+    rng = np.random.default_rng(44)
+    z = {n: np.asarray(v, np.float64) for n, v in wl.gated_inputs(w).items()}
+    names = ("v", "z_alpha", "z_omega", "z_r")
+    ref = oracle.forward_gated(z["q"], z["k"], **{n: z[n] for n in names}, c0=z["c0"], mu=w.mu, variant=variant)
+    sq = rng.uniform(0.05, 20.0, z["q"].shape[:-1] + (1,))
+    sk = rng.uniform(0.05, 20.0, z["k"].shape[:-1] + (1,))
+    got = oracle.forward_gated(z["q"] * sq, z["k"] * sk, **{n: z[n] for n in names}, c0=z["c0"], mu=w.mu,
+                               variant=variant)
+    for key in ("o", "S", "p"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-11, atol=1e-13)
+    # the raw rows are not unit rows: the recurrence on them (no
+    # normalisation) gives another result, so the check above has teeth
+    a, om, r = oracle.gates(z["z_alpha"], z["z_omega"], z["z_r"])
+    fn = {"diagonal": oracle.forward_diag, "isotropic": oracle.forward_iso, "isochannel": oracle.forward_isoc}
+    raw = fn[variant](z["q"], z["k"], z["v"], a, om, r, z["c0"], w.mu)
+    assert np.max(np.abs(raw["o"] - ref["o"])) > 1e-2 * np.max(np.abs(ref["o"]))
