@@ -24,6 +24,7 @@
 //   post-write readout expanded), and the write S = S_hat + kappa delta^T.
 #pragma once
 
+#include "kdn_device.h"
 #include "kdn_gates.h"
 
 #include <hip/hip_runtime.h>
@@ -50,10 +51,12 @@ __device__ __forceinline__ void from_f32(bf16_t* p, float x) {
     }
 }
 
+// sum over the wave, in every lane: DPP inside 16-lane rows, then the row
+// swaps (no LDS round trip on the per-token dependency chain)
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x = dev::sum16(x);
+    x = dev::halve16(x, x);
+    return dev::halve32(x, x);
 }
 
 // LDS written by some lanes of a wave and read by other lanes of the same
