@@ -327,9 +327,14 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
  *
  * S0, dS_T, dS0 and dv must be 8-byte aligned (KDN_ERR_UNSUPPORTED
  * otherwise) and the workspace 16-byte aligned (KDN_ERR_WORKSPACE).  No output may overlap
- * an input, another output or the workspace (KDN_ERR_ALIAS).  Arithmetic is
- * fp32 throughout; calls are asynchronous on `stream` like kdn_forward, and
- * the results are bitwise repeatable.
+ * an input, another output or the workspace (KDN_ERR_ALIAS).  The diagonal
+ * variant with bf16 inputs and 16-byte aligned q, k, v, alpha, omega and dO
+ * runs its memory adjoint in chunk form on the matrix cores (bf16 operands,
+ * fp32 accumulation and state), after a checkpoint sweep of the chunked
+ * forward; (batch, head) pairs whose decays leave the chunked form's range
+ * take the token recurrence's adjoint, as do the other variants and fp32
+ * inputs (fp32 throughout).  Calls are asynchronous on `stream` like
+ * kdn_forward, and the results are bitwise repeatable.
  */
 int kdn_backward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
                  const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
@@ -347,7 +352,7 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
  * workspace), checks, kernels and results (bit for bit) as kdn_backward.
  *  - Sizes whose workspace (kdn_backward_workspace_size) exceeds the scratch
  *    return KDN_ERR_WORKSPACE and launch nothing (dk = dv = 128, H = 16, B = 1:
- *    T up to 1974; B = 2: T up to 840).
+ *    T up to 1974; B = 2: T up to 839).
  *  - Nothing is allocated: no hipMalloc, hipFree or allocating library call.
  *  - Every call on one device shares that device's scratch and leaves its
  *    contents behind (the kernels need none on entry).  Calls that overlap in
@@ -363,9 +368,9 @@ int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void
                          void* stream);
 
 /* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
- * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4
+ * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4 + B*H*4
  * (recomputation checkpoints per 64-column tile, plus per-token partial sums
- * and uncertainties per tile). */
+ * and uncertainties per tile, plus one range flag per (batch, head) pair). */
 size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv);
 int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
                           const void* omega, const void* r, const float* c0, float mu, int variant,

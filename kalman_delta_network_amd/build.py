@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkdn.so")
 SOURCES = ["kdn_api.cpp", "kdn_recurrent.hip", "kdn_chunked.hip", "kdn_backward.hip", "kdn_gate_bwd.hip",
-           "kdn_noalloc.hip", "kdn_iso.hip", "kdn_split.hip"]
+           "kdn_noalloc.hip", "kdn_iso.hip", "kdn_split.hip", "kdn_backward_chunk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -327,6 +327,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     const int nunit = A.B * A.H;
     const int tile = int(blockIdx.x) / nunit;  // the tiles of one head are nunit blocks apart
     const int unit = int(blockIdx.x) % nunit;
+    if (A.only_flagged && !A.only_flagged[unit]) return;  // the chunked adjoint took this pair
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
@@ -948,11 +949,48 @@ hipError_t launch_grouped_t(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// floats before the per-pair flags of the chunked path
+size_t flag_offset(int B, int T, int H, int dk, int dv) {
+    const size_t units = size_t(B) * size_t(H), ntile = size_t(dv) / TILE;
+    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1} (per tile)
+    return units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * ntile * 5 * dk;
+}
+
+// The chunked memory adjoint (kdn_backward_chunk.hip) for the diagonal bf16
+// form: the chunked forward's checkpoint sweep (chunk-start states and
+// uncertainties into the per-(unit, tile) checkpoint regions, one range flag
+// per (batch, head) pair), the chunked adjoint of the unflagged pairs, the
+// recurrent memory adjoint of the flagged ones, then the uncertainty adjoint
+// of all.  Both memory adjoints leave the same per-token tile sums.
+template <int DK, int DV>
+hipError_t launch_chunked_path(const BwdArgs& a, hipStream_t s) {
+    const size_t uf = unit_floats(a.T, DK, TILE);
+    int* flag = reinterpret_cast<int*>(a.work + flag_offset(a.B, a.T, a.H, DK, DV));
+    const FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, DK, DV,
+                    a.S0, a.p0, nullptr, nullptr, nullptr};
+    hipError_t e = launch_chunked_checkpoints(f, a.work, uf, flag, s);
+    if (e != hipSuccess) return e;
+    e = launch_backward_chunk(a, uf, flag, s);
+    if (e != hipSuccess) return e;
+    BwdArgs r = a;
+    r.only_flagged = flag;
+    return launch_t<DK, DV, 0, bf16_t>(r, s);
+}
+
+bool chunk_path(const BwdArgs& a) {
+    const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const bool aligned = al16(a.q) && al16(a.k) && al16(a.v) && al16(a.alpha) && al16(a.omega) && al16(a.dO);
+    FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, a.dk, a.dv,
+              a.S0, a.p0, nullptr, nullptr, nullptr};
+    return a.variant == 0 && a.dtype == 1 && a.T > 0 && aligned && chunked_supports(f);
+}
+
 template <int DK, int DV>
 hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
     if (a.variant == 3)  // diagonal with grouped observation noise
         return a.dtype == 1 ? launch_grouped_t<DK, DV, bf16_t>(a, s) : launch_grouped_t<DK, DV, float>(a, s);
     if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
+    if (chunk_path(a)) return launch_chunked_path<DK, DV>(a, s);
     return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
 }
 
@@ -960,9 +998,8 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (long(B) * H == 0 || T == 0) return 0;
-    const size_t units = size_t(B) * size_t(H), ntile = size_t(dv) / TILE;
-    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1} (per tile)
-    return (units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * ntile * 5 * dk) * sizeof(float);
+    // then one range flag per (batch, head) pair for the chunked path
+    return flag_offset(B, T, H, dk, dv) * sizeof(float) + size_t(B) * size_t(H) * sizeof(int);
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {

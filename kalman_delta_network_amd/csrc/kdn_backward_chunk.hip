@@ -1,0 +1,561 @@
+// kdn_backward_chunk.hip -- the memory adjoint of the diagonal KDN recurrence
+// in chunk form, on the matrix cores (gfx950).
+//
+// The forward token step ("Kalman Delta Networks: Uncertainty-aware
+// Associative Memory", summary page, method steps 2-5) is, per 32-token chunk
+// in the midpoint frame of the chunked forward (kdn_chunked.hip):
+//   rho_t = g_t / g_15 (t <= 15),  rho_t = prod_{16<=u<=t} alpha_u (t >= 16)
+//   Kt = k rho,  Qt = q rho,  Kh = kappa' / rho   (kappa' = p_hat k)
+//   Sg = diag(g_15) S_c,  M = diag(r) + tril(Kt Kh^T),  R = V - Kt Sg,
+//   Dn = M^-1 R,  O = Qt Sg + tril(Qt Kh^T) Dn,
+//   S_{c+1} = diag(gb_31) X,  X = Sg + Kh^T Dn.
+// Its adjoint, given dO and the cotangent dS of S_{c+1}:
+//   dX = diag(gb_31) dS,  d gb_31 = rowsum(dS . X),
+//   dDn = tril(Qt Kh^T)^T dO + Kh dX,  dR = M^-T dDn  (= dv),
+//   dSg = Qt^T dO + dX - Kt^T dR,  dS_c = diag(g_15) dSg,
+//   d g_15 = rowsum(dSg . Sg) / g_15,
+//   dM = tril(-dR Dn^T),  dQK = tril(dO Dn^T),
+//   dQt = dO Sg^T + dQK Kh,  dKt = -dR Sg^T + dM Kh,
+//   dKh = dQK^T Qt + dM^T Kt + Dn dX^T.
+// Per token and key channel that gives dq = dQt rho, the gradient of k
+// through Kt, of kappa' through Kh and of rho (w = d rho . rho), and
+// through the prefix products of alpha the gradient of alpha.  The token
+// recurrence's uncertainty adjoint (kdn_backward.hip) takes the gradient of
+// the normalised gain kappa = kappa' / d (d = r + k . kappa' = M_tt) and of k
+// with kappa held fixed; with dr_t = dM_tt those are
+//   d kappa = d (d kappa'_chunk - k dr),  dk_mem = dk_chunk - kappa' dr,
+// linear in the tile's partial sums, so every column tile converts its own.
+//
+// Work mapping: one workgroup per (batch, head, 64 value columns), 8 waves,
+// chunks in reverse order.  Each chunk runs as its two 16-token halves: the
+// first half's forward gives the state at the midpoint, then the second
+// half's adjoint and the first half's (every 16 x 16 block of M and
+// tril(Qt Kh^T) is then one tile, and the block solves are single tiles).
+// The chunk-start states (in the midpoint frame) and uncertainties come from
+// the chunked forward's checkpoint mode; the chain re-runs the chunk's
+// uncertainty recurrence from the stored p.  Waves 0 .. d_k/16 - 1 hold 16
+// key rows of the state-sized matrices (Sg, dS, X) in MFMA accumulator
+// layout.  Matrix operands whose contraction index runs along the stored
+// rows are gathered from LDS (4 or 8 two-byte reads per lane).
+#include "kdn_device.h"
+#include "kdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kdn {
+namespace {
+
+using namespace dev;
+
+constexpr int L = 32;       // chunk
+constexpr int HL = 16;      // half chunk
+constexpr int TILE = 64;    // value columns per workgroup
+constexpr int NTH = 512;    // 8 waves
+
+template <int DK>
+struct CSmem {
+    bf16_t K[L * DK];   // raw k, q, alpha, omega of the chunk, [t][i] (rows past T repeat the last token)
+    bf16_t Q[L * DK];
+    bf16_t A[L * DK];
+    bf16_t W[L * DK];
+    bf16_t V[L * TILE];   // v of the tile's columns [t][col]
+    bf16_t dO[L * TILE];  // dO, [t][col] swizzled
+    float rho[L * DK];    // rho_t,i (midpoint frame)
+    float kap[L * DK];    // kappa'_t,i; after the half's products w_t,i = d rho . rho
+    bf16_t Kt[L * DK];    // [t][i] swizzled
+    bf16_t Qt[L * DK];
+    bf16_t Kh[L * DK];
+    bf16_t S[DK * TILE];   // the half's start state, bf16 [i][col] swizzled
+    bf16_t dX[DK * TILE];  // dX of the half, bf16 [i][col] swizzled
+    bf16_t R[HL * TILE];   // [t][col] swizzled
+    bf16_t Dn[2][HL * TILE];
+    bf16_t dDn[HL * TILE];
+    bf16_t dR[HL * TILE];
+    float Md[2 * 256];     // M's diagonal blocks, column-major [a][s][t]
+    float Wi[2][2][64];    // block-inverse scratch
+    bf16_t Td[2 * 256];    // their inverses [a][t][s]
+    bf16_t QK[2 * 256];    // tril(Qt Kh^T) of each half [a][t][s]
+    bf16_t dM[256];        // tril(-dR Dn^T) of the current half [t][s]
+    bf16_t dQK[256];       // tril(dO Dn^T) [t][s]
+    float r[L];
+    float d[L];            // M_tt = r_t + k_t . kappa'_t
+    float dr[L];           // dM_tt
+    float GA[DK], GB[DK];  // g_15 and gb_31
+    float dGA[DK], dGB[DK];
+};
+
+// The lane index as a value the compiler cannot hoist out of the chunk loop:
+// otherwise it keeps every loop-invariant LDS address of the operand reads
+// below in registers across the loop (hundreds of them) and spills.
+__device__ __forceinline__ int lane_id() {
+    int l;
+    asm volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(int(threadIdx.x)));
+    return l;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operands from LDS.  Row operands: lane l reads row row0 + l % 16 of a
+// [rows][W] tile at contraction index k0 + 8 (l / 16) (16x16x32) or
+// k0 + 4 (l / 16) (16x16x16).  Gathered operands: the contraction index runs
+// along the stored rows: lane l reads rows k0 + 8 (l / 16) + j (or 4 (l / 16)
+// + j) of column c0 + l % 16.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ b8 row32(const bf16_t* A, int row0, int k0) {
+    const int lane = lane_id();
+    return *reinterpret_cast<const b8*>(A + sw<W>(row0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+template <int W>
+__device__ __forceinline__ s4 row16(const bf16_t* A, int row0, int k0) {
+    const int lane = lane_id();
+    return *reinterpret_cast<const s4*>(A + sw<W>(row0 + (lane & 15), k0 + 4 * (lane >> 4)));
+}
+template <int W>
+__device__ __forceinline__ s4 col16(const bf16_t* A, int k0, int c0) {
+    const int lane = lane_id();
+    s4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = short(A[sw<W>(k0 + 4 * (lane >> 4) + j, c0 + (lane & 15))]);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ b8 col32(const bf16_t* A, int k0, int c0) {
+    const int lane = lane_id();
+    u4 u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = A[sw<W>(k0 + 8 * (lane >> 4) + 2 * j, c0 + (lane & 15))];
+        const uint32_t hi = A[sw<W>(k0 + 8 * (lane >> 4) + 2 * j + 1, c0 + (lane & 15))];
+        u[j] = lo | (hi << 16);
+    }
+    return __builtin_bit_cast(b8, u);
+}
+// plain 16 x 16 tiles [row][col]
+__device__ __forceinline__ s4 row16p(const bf16_t* A) {
+    const int lane = lane_id();
+    return *reinterpret_cast<const s4*>(A + (lane & 15) * 16 + 4 * (lane >> 4));
+}
+__device__ __forceinline__ s4 col16p(const bf16_t* A) {
+    const int lane = lane_id();
+    s4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = short(A[(4 * (lane >> 4) + j) * 16 + (lane & 15)]);
+    return v;
+}
+// accumulator tile (rows row0 + 4 (l / 16) + e, column c0 + l % 16) to a
+// swizzled [rows][W] bf16 tile
+template <int W>
+__device__ __forceinline__ void put(bf16_t* D, int row0, int c0, f4 c) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) D[sw<W>(row0 + 4 * (lane >> 4) + e, c0 + (lane & 15))] = to_bf(c[e]);
+}
+
+constexpr f4 kZero = {0.f, 0.f, 0.f, 0.f};
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int DK>
+__global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
+    constexpr int NT = DK / 16;     // 16-row tiles of the key dimension (state waves)
+    constexpr int NCW = DK / 64;    // chain waves
+    __shared__ CSmem<DK> sm;
+    const int nunit = A.B * A.H;
+    const int ntile = A.dv / TILE;
+    const int tile = int(blockIdx.x) / nunit;
+    const int unit = int(blockIdx.x) % nunit;
+    if (flag[unit]) return;  // the recurrent memory adjoint takes this pair
+    const int h = unit % A.H;
+    const size_t b = size_t(unit / A.H);
+    const int T = A.T;
+    const int DV = A.dv;
+    const int nchunks = (T + L - 1) / L;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = 4 * (lane >> 4);
+    const float mu = A.mu;
+    const bf16_t* qin = static_cast<const bf16_t*>(A.q);
+    const bf16_t* kin = static_cast<const bf16_t*>(A.k);
+    const bf16_t* vin = static_cast<const bf16_t*>(A.v);
+    const bf16_t* ain = static_cast<const bf16_t*>(A.alpha);
+    const bf16_t* win = static_cast<const bf16_t*>(A.omega);
+    const bf16_t* rin = static_cast<const bf16_t*>(A.r);
+    const bf16_t* doin = static_cast<const bf16_t*>(A.dO);
+    const float* ck = A.work + (size_t(unit) * ntile + tile) * ck_floats;                // [chunk][DK][64]
+    const float* ckp = A.work + size_t(unit) * ntile * ck_floats + size_t(nchunks) * DK * TILE;  // [chunk][DK]
+    float* partial = A.work + size_t(nunit) * ntile * ck_floats;  // [unit][T][ntile][4][DK]
+    float* pbuf = partial + size_t(nunit) * T * ntile * 4 * DK;   // [unit][T][ntile][DK]
+    const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
+
+    // the upper 8 x 8 corner of each inverse block is zero (block_inverse
+    // writes the rest)
+    for (int e = threadIdx.x; e < 2 * 64; e += NTH) sm.Td[(e >> 6) * 256 + ((e >> 3) & 7) * 16 + 8 + (e & 7)] = 0;
+
+    // the cotangent of the state, key rows 16 wave + 4 (l / 16) + e, columns 16 ct + l % 16
+    const bool stw = wave < NT;
+    f4 dS[4], Sg[4], Sm[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        dS[ct] = kZero;
+        if (stw && A.dS_T)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dS[ct][e] = A.dS_T[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n];
+    }
+
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const int lane = lane_id();  // (see lane_id)
+        const int n = lane & 15, g4 = 4 * (lane >> 4);
+        const int t0 = c * L;
+        const int nvalid = min(L, T - t0);
+        // ---- loads: raw k, q, alpha, omega, v and dO tiles, r, Sg ----
+        {
+            const int last = nvalid - 1;
+            constexpr int PR = DK / 8;  // 16-byte pieces per row
+            for (int pc = threadIdx.x; pc < L * PR; pc += NTH) {
+                const int t = pc / PR, cc = pc % PR;
+                const size_t src = tokidx(t0 + min(t, last)) * DK + 8 * cc;
+                *reinterpret_cast<u4*>(&sm.K[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(kin + src);
+                *reinterpret_cast<u4*>(&sm.Q[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(qin + src);
+                *reinterpret_cast<u4*>(&sm.A[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(ain + src);
+                *reinterpret_cast<u4*>(&sm.W[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(win + src);
+            }
+            for (int pc = threadIdx.x; pc < L * 8; pc += NTH) {
+                const int t = pc / 8, cc = pc % 8;
+                const bool ok = t < nvalid;
+                const size_t src = tokidx(t0 + min(t, last)) * DV + tile * TILE + 8 * cc;
+                const u4 zero = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u4*>(&sm.V[t * TILE + 8 * cc]) = ok ? *reinterpret_cast<const u4*>(vin + src) : zero;
+                const u4 dov = (ok && doin) ? *reinterpret_cast<const u4*>(doin + src) : zero;
+                *reinterpret_cast<u4*>(&sm.dO[sw<TILE>(t, 8 * cc)]) = dov;
+            }
+            if (threadIdx.x < L) {
+                const int t = threadIdx.x;
+                sm.r[t] = t < nvalid ? bf1(rin[tokidx(t0 + t)]) : 1.f;
+            }
+            if (stw) {
+                const float* ckc = ck + size_t(c) * DK * TILE;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Sg[ct][e] = ckc[(16 * wave + g4 + e) * TILE + 16 * ct + n];
+            }
+        }
+        bar();
+        // ---- chain: uncertainty recurrence, decays, the chunk's operands ----
+        if (wave < NCW) {
+            const int i = 64 * wave + lane;
+            // first half: rho_t = 1 / prod_{t<u<=15} alpha_u, from the
+            // midpoint backwards
+            float hr = 1.f;
+#pragma unroll 1
+            for (int t = HL - 1; t >= 0; --t) {
+                sm.rho[t * DK + i] = hr;  // 1 / rho for now
+                hr *= t < nvalid ? bf1(sm.A[t * DK + i]) : 1.f;
+            }
+            const float ga = hr;  // g_15
+            float p = ckp[size_t(c) * DK + i];
+            float gb = 1.f;
+#pragma unroll 2
+            for (int t = 0; t < L; ++t) {
+                const bool ok = t < nvalid;
+                const float al = ok ? bf1(sm.A[t * DK + i]) : 1.f;
+                const float kk = ok ? bf1(sm.K[t * DK + i]) : 0.f;
+                const float qq = ok ? bf1(sm.Q[t * DK + i]) : 0.f;
+                const float w = ok ? bf1(sm.W[t * DK + i]) : 0.f;
+                const float rt = sm.r[t];
+                if (ok && tile == 0) pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i] = p;
+                const float ph = fmaf(al * al, p, w);
+                const float kap = ph * kk;
+                p = ph / fmaf((mu / rt) * kk * kk, ph, 1.f);
+                float rh, rinv;  // rho and 1 / rho
+                if (t < HL) {
+                    rinv = sm.rho[t * DK + i];
+                    rh = 1.f / rinv;
+                } else {
+                    gb *= al;
+                    rh = gb;
+                    rinv = 1.f / gb;
+                }
+                sm.rho[t * DK + i] = rh;
+                sm.kap[t * DK + i] = kap;
+                sm.Kt[sw<DK>(t, i)] = to_bf(kk * rh);
+                sm.Qt[sw<DK>(t, i)] = to_bf(qq * rh);
+                sm.Kh[sw<DK>(t, i)] = to_bf(kap * rinv);
+            }
+            sm.GA[i] = ga;
+            sm.GB[i] = gb;
+        }
+        if (stw) {
+            // the first half's start state as bf16
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) put<TILE>(sm.S, 16 * wave, 16 * ct, Sg[ct]);
+        }
+        bar();
+        // ---- M's diagonal blocks and tril(Qt Kh^T) of both halves ----
+        if (wave < 4) {
+            const int a = wave & 1;
+            const bf16_t* X = wave < 2 ? sm.Kt : sm.Qt;
+            f4 acc = kZero;
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(X, HL * a, k0), row32<DK>(sm.Kh, HL * a, k0), acc);
+            // acc[e] = row t = g4 + e, column s = n
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = g4 + e;
+                if (wave < 2) {
+                    const float m = t > n ? acc[e] : t == n ? acc[e] + sm.r[HL * a + t] : 0.f;
+                    sm.Md[a * 256 + n * 16 + t] = m;
+                    if (t == n) sm.d[HL * a + t] = m;
+                } else {
+                    sm.QK[a * 256 + t * 16 + n] = to_bf(t >= n ? acc[e] : 0.f);
+                }
+            }
+        }
+        bar();
+        if (wave == 0) block_inverse(sm.Md, sm.Wi, sm.Td, lane);
+        // R of the first half: V - Kt Sg (waves 4..7, one 16-column tile each)
+        if (wave >= 4) {
+            const int ct = wave - 4;
+            f4 acc = kZero;
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(sm.Kt, 0, k0), col32<TILE>(sm.S, k0, 16 * ct), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = bf1(sm.V[(g4 + e) * TILE + 16 * ct + n]) - acc[e];
+            put<TILE>(sm.R, 0, 16 * ct, acc);
+        }
+        bar();
+        // Dn of the first half: T_A R
+        if (wave < 4) {
+            const int ct = wave;
+            const f4 acc = mfma16(row16p(sm.Td), col16<TILE>(sm.R, 0, 16 * ct), kZero);
+            put<TILE>(sm.Dn[0], 0, 16 * ct, acc);
+        }
+        bar();
+        // the midpoint state Sm = Sg + Kh_A^T Dn_A (state waves), as bf16 for
+        // the second half
+        if (stw) {
+            const s4 ak = col16<DK>(sm.Kh, 0, 16 * wave);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                Sm[ct] = mfma16(ak, col16<TILE>(sm.Dn[0], 0, 16 * ct), Sg[ct]);
+                put<TILE>(sm.S, 16 * wave, 16 * ct, Sm[ct]);
+            }
+        }
+        bar();
+        // R of the second half: V - Kt Sm
+        if (wave >= 4) {
+            const int ct = wave - 4;
+            f4 acc = kZero;
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(sm.Kt, HL, k0), col32<TILE>(sm.S, k0, 16 * ct), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = bf1(sm.V[(HL + g4 + e) * TILE + 16 * ct + n]) - acc[e];
+            put<TILE>(sm.R, 0, 16 * ct, acc);
+        }
+        bar();
+        if (wave < 4) {
+            const int ct = wave;
+            const f4 acc = mfma16(row16p(sm.Td + 256), col16<TILE>(sm.R, 0, 16 * ct), kZero);
+            put<TILE>(sm.Dn[1], 0, 16 * ct, acc);
+        }
+        bar();
+        // X = Sm + Kh_B^T Dn_B, d gb_31 = rowsum(dS . X), dX = diag(gb_31) dS
+        if (stw) {
+            const s4 ak = col16<DK>(sm.Kh, HL, 16 * wave);
+            f4 part = kZero;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const f4 x = mfma16(ak, col16<TILE>(sm.Dn[1], 0, 16 * ct), Sm[ct]);
+                part += dS[ct] * x;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s = sum16(part[e]);
+                const int i = 16 * wave + g4 + e;
+                if (n == 0) sm.dGB[i] = s;
+                const float gbi = sm.GB[i];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) dS[ct][e] *= gbi;  // dS now holds dX
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) put<TILE>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
+        }
+        bar();
+
+        // ---- the adjoint of each half, the second first ----
+#pragma unroll 1
+        for (int half = 1; half >= 0; --half) {
+            const int th = HL * half;
+            const bf16_t* Tinv = sm.Td + 256 * half;
+            const bf16_t* QKh = sm.QK + 256 * half;
+            const bf16_t* Dnh = sm.Dn[half];
+            // dDn = QK^T dO + Kh dX
+            if (wave < 4) {
+                const int ct = wave;
+                f4 acc = mfma16(col16p(QKh), col16<TILE>(sm.dO, th, 16 * ct), kZero);
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(sm.Kh, th, k0), col32<TILE>(sm.dX, k0, 16 * ct), acc);
+                put<TILE>(sm.dDn, 0, 16 * ct, acc);
+            }
+            bar();
+            // dR = T^T dDn (= dv)
+            if (wave < 4) {
+                const int ct = wave;
+                const f4 acc = mfma16(col16p(Tinv), col16<TILE>(sm.dDn, 0, 16 * ct), kZero);
+                put<TILE>(sm.dR, 0, 16 * ct, acc);
+                if (A.dv_)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = th + g4 + e;
+                        if (t < nvalid) A.dv_[tokidx(t0 + t) * DV + tile * TILE + 16 * ct + n] = acc[e];
+                    }
+            }
+            bar();
+            if (stw) {
+                // dS_start = dX + Qt^T dO - Kt^T dR
+                const s4 aq = col16<DK>(sm.Qt, th, 16 * wave), akt = col16<DK>(sm.Kt, th, 16 * wave);
+                f4 part = kZero;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const f4 pos = mfma16(aq, col16<TILE>(sm.dO, th, 16 * ct), dS[ct]);
+                    const f4 neg = mfma16(akt, col16<TILE>(sm.dR, 0, 16 * ct), kZero);
+                    dS[ct] = pos - neg;
+                    if (half == 0) part += dS[ct] * Sg[ct];
+                }
+                if (half == 0) {
+                    // d g_15 = rowsum(dSg . Sg) / g_15; the previous chunk's dS = diag(g_15) dSg
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float s = sum16(part[e]);
+                        const int i = 16 * wave + g4 + e;
+                        const float ga = sm.GA[i];
+                        if (n == 0) sm.dGA[i] = s / ga;
+#pragma unroll
+                        for (int ct = 0; ct < 4; ++ct) dS[ct][e] *= ga;
+                    }
+                }
+            }
+            // dM = tril(-dR Dn^T) and dQK = tril(dO Dn^T) on two waves (after
+            // their state work at d_k = 128, where every wave is a state wave)
+            constexpr int WM = NT < 6 ? NT : 6;
+            if (wave == WM || wave == WM + 1) {
+                const bool isM = wave == WM;
+                f4 acc = kZero;
+#pragma unroll
+                for (int k0 = 0; k0 < TILE; k0 += 32)
+                    acc = mfma32(isM ? row32<TILE>(sm.dR, 0, k0) : row32<TILE>(sm.dO, th, k0), row32<TILE>(Dnh, 0, k0), acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = g4 + e;
+                    if (isM) {
+                        sm.dM[t * 16 + n] = to_bf(t >= n ? -acc[e] : 0.f);
+                        if (t == n) sm.dr[th + t] = -acc[e];
+                    } else {
+                        sm.dQK[t * 16 + n] = to_bf(t >= n ? acc[e] : 0.f);
+                    }
+                }
+            }
+            bar();
+            // per token and key channel: dQt, dKt, dKh of key tile wave
+            if (wave < NT) {
+                const int i0 = 16 * wave;
+                const bf16_t* Sh = sm.S;  // this half's start state (bf16 [i][col])
+                f4 dqt = mfma16(row16p(sm.dQK), col16<DK>(sm.Kh, th, i0), kZero);
+                f4 dkt = mfma16(row16p(sm.dM), col16<DK>(sm.Kh, th, i0), kZero);
+                f4 dkh = mfma16(col16p(sm.dQK), col16<DK>(sm.Qt, th, i0), kZero);
+                dkh = mfma16(col16p(sm.dM), col16<DK>(sm.Kt, th, i0), dkh);
+                f4 neg = kZero;
+#pragma unroll
+                for (int k0 = 0; k0 < TILE; k0 += 32) {
+                    const b8 sv = row32<TILE>(Sh, i0, k0);
+                    dqt = mfma32(row32<TILE>(sm.dO, th, k0), sv, dqt);
+                    neg = mfma32(row32<TILE>(sm.dR, 0, k0), sv, neg);
+                    dkh = mfma32(row32<TILE>(Dnh, 0, k0), row32<TILE>(sm.dX, i0, k0), dkh);
+                }
+                dkt -= neg;
+                // acc[e]: token th + g4 + e, channel i0 + n
+                const int i = i0 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tl = th + g4 + e;
+                    const float rh = sm.rho[tl * DK + i], kp = sm.kap[tl * DK + i];
+                    const float kk = bf1(sm.K[tl * DK + i]), qq = bf1(sm.Q[tl * DK + i]);
+                    const float dq = dqt[e] * rh, dkc = dkt[e] * rh, dkapc = dkh[e] / rh;
+                    const float drt = sm.dr[tl], dt = sm.d[tl];
+                    sm.kap[tl * DK + i] = fmaf(dkc, kk, fmaf(dq, qq, -dkapc * kp));  // w = d rho . rho
+                    if (tl < nvalid) {
+                        float* dst = partial + ((size_t(unit) * T + t0 + tl) * ntile + tile) * 4 * DK + i;
+                        dst[0] = dq;
+                        dst[DK] = dt * fmaf(-kk, drt, dkapc);
+                        dst[2 * DK] = fmaf(-kp, drt, dkc);
+                    }
+                }
+            }
+            bar();
+            if (half == 1) {
+                // the first half: its start state and dX = dS (the state waves
+                // hold the cotangent of the midpoint state)
+                if (stw)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        put<TILE>(sm.S, 16 * wave, 16 * ct, Sg[ct]);
+                        put<TILE>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
+                    }
+                bar();
+            }
+        }
+        // ---- d alpha of the memory part, per channel over the chunk ----
+        if (wave < NCW) {
+            const int i = 64 * wave + lane;
+            const float fa = sm.dGA[i] * sm.GA[i], fb = sm.dGB[i] * sm.GB[i];
+            // u <= 15: -sum_{t<u} w_t + fa;  u >= 16: sum_{t>=u} w_t + fb
+            float pre = 0.f;
+#pragma unroll
+            for (int u = 0; u < HL; ++u) {
+                if (u < nvalid) {
+                    const float al = bf1(sm.A[u * DK + i]);
+                    partial[((size_t(unit) * T + t0 + u) * ntile + tile) * 4 * DK + 3 * DK + i] = (fa - pre) / al;
+                }
+                pre += sm.kap[u * DK + i];
+            }
+            float suf = 0.f;
+#pragma unroll
+            for (int u = L - 1; u >= HL; --u) {
+                suf += sm.kap[u * DK + i];
+                if (u < nvalid) {
+                    const float al = bf1(sm.A[u * DK + i]);
+                    partial[((size_t(unit) * T + t0 + u) * ntile + tile) * 4 * DK + 3 * DK + i] = (suf + fb) / al;
+                }
+            }
+        }
+        bar();
+    }
+    // dS0
+    if (stw && A.dS0)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                A.dS0[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n] = dS[ct][e];
+}
+
+}  // namespace
+
+hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+    const unsigned units = unsigned(long(a.B) * a.H);
+    const unsigned grid = units * unsigned(a.dv / TILE);
+    if (a.dk == 128)
+        hipLaunchKernelGGL(kdn_backward_chunk_kernel<128>, dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+    else if (a.dk == 64)
+        hipLaunchKernelGGL(kdn_backward_chunk_kernel<64>, dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+    else
+        return hipErrorNotSupported;
+    return hipGetLastError();
+}
+
+}  // namespace kdn

@@ -174,6 +174,15 @@ struct Args {
     const float* mob = nullptr;  // [B*H][nseg][DK][4] Mobius products of the segments
     bf16_t* ophi = nullptr;      // o of the identity columns, [tokens][H][DK]
     float* sseg = nullptr;       // segment end states [B*H][nseg][DK][DV + DK]
+    // checkpoint mode (the chunked backward's forward sweep; diagonal,
+    // ungated, 64-column tiles): per (unit, tile) region of ck_floats floats
+    // from ck: the memory in the midpoint frame, diag(g_15) S, at every chunk
+    // start ([chunk][DK][64]), then (tile 0) p at every chunk start
+    // ([chunk][DK]); ck_flag[unit] = 1 where a chunk leaves the chunked
+    // form's range (its checkpoints stop there), else 0.  No o, S_T or p_T.
+    float* ck = nullptr;
+    size_t ck_floats = 0;
+    int* ck_flag = nullptr;
 };
 
 // position of token t of the workgroup's sequence (of head h) in the token
@@ -1044,7 +1053,7 @@ __device__ __forceinline__ void state_scale(StateAcc<DK, NCT>& st, Smem<DK>& sm,
 // the next one is outside the chunked form's range), 1 fL (the next chunk's
 // Sg in one multiply), 2 gb_31 then g_15 of the next chunk (fL would leave
 // the normal fp32 range).  SC: one decay per token, factors at index 0.
-template <int DK, int NCT, bool SC, bool GATE>
+template <int DK, int NCT, bool SC, bool GATE, bool STORE = false>
 __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, int b, const Args& a, size_t bb,
                                            int h, int colb, int c, int mode) {
     const int gring = c % 3;
@@ -1079,7 +1088,7 @@ __device__ __forceinline__ void state_seg2(StateAcc<DK, NCT>& st, Smem<DK>& sm, 
         for (int ct = 0; ct < NCT; ++ct) {
             f4 o = mfma32(Db[ct], aqk[at], st.O[at][ct]);  // (tril(Qt Kh^T) Dn)^T
             if (GATE) o *= sq;
-            if (ok) *reinterpret_cast<u2*>(orow + 16 * ct) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+            if (ok && !STORE) *reinterpret_cast<u2*>(orow + 16 * ct) = u2{pack2(o[0], o[1]), pack2(o[2], o[3])};
         }
         orow += ostep;
     }
@@ -1119,10 +1128,11 @@ __device__ __forceinline__ int form_index(int w) {
 // GR (diagonal only): grouped observation noise, one r and one uncertainty
 // state p per group of DVT value columns, i.e. per column tile; the tiles of
 // a head are then independent diagonal recurrences sharing q, k, alpha, omega.
-template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false>
+template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false, bool STORE = false>
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
     static_assert(!GATE || !GR, "no gate step with grouped observation noise");
+    static_assert(!STORE || (VAR == 0 && !GR && NCT == 2 && !GATE), "checkpoints: diagonal, 64-column tiles");
     static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
     static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
     constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
@@ -1265,6 +1275,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 bad_seen = sm.bad;  // flags of chunks before c
                 if (bad_seen == c - 1) psave = pst[BUF ^ 1];
                 pst[BUF] = p;
+                if (STORE && tile == 0 && active && c < nchunks)
+                    a.ck[size_t(unit) * ntile * a.ck_floats + size_t(nchunks) * DK * DVTN + size_t(c) * DK + i] = p;
                 float g = 1.f, gi = 1.f;
                 if (active && c < nchunks) {
                     if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
@@ -1288,7 +1300,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 step(IntC<1>{}, c + 1);
             }
             bad_seen = sm.bad;
-            if (bad_seen >= nchunks && active && (GR || tile == 0) && seg_g == a.nseg - 1) a.p_T[pidx] = p;
+            if (!STORE && bad_seen >= nchunks && active && (GR || tile == 0) && seg_g == a.nseg - 1) a.p_T[pidx] = p;
         } else if (wave == 1) {
             // the per-channel decays (isotropic variant with per-channel
             // decay; otherwise this wave only keeps the barrier count)
@@ -1431,6 +1443,17 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const int fsub = sm.fsub[c % 3][0] | sm.fsub[c % 3][1];  // read early: its use is a segment away
             const bool run = c < nchunks && c < bad_seen;
             if (!phi) state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (STORE && run) {
+                // chunk c's start state, diag(g_15) S (fp32)
+                float* ck = a.ck + (size_t(unit) * ntile + tile) * a.ck_floats + size_t(c) * DK * DVTN;
+#pragma unroll
+                for (int r4 = 0; r4 < DK / 16; ++r4)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ck[(16 * r4 + g4 + e) * DVTN + cw * (16 * NCT) + 16 * ct + n] = st.S[r4][ct][e];
+            }
             if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
             // everything but the NCT loads just issued has landed: the v of
             // chunk it - 1, the previous iteration's stores and chain rows
@@ -1442,12 +1465,14 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             if (run) {
                 const bool next = c + 1 < nchunks && c + 1 < bad_seen;
                 const int mode = !next ? 0 : fsub ? 2 : 1;
-                state_seg2<DK, NCT, VAR == 1, GATE>(st, sm, c & 1, ao, b, h, colo, c, mode);
+                state_seg2<DK, NCT, VAR == 1, GATE, STORE>(st, sm, c & 1, ao, b, h, colo, c, mode);
             }
             bar();
         }
         bad_seen = sm.bad;
-        if (bad_seen >= nchunks) {
+        if (STORE) {
+            // no final state in checkpoint mode
+        } else if (bad_seen >= nchunks) {
             // segment mode: the segment's end state, [v | identity] columns
             float* sout = a.seg ? a.sseg + (size_t(unit) * a.nseg + seg_g) * DK * (a.DV + DK) : a.S_T + sbase;
             const int sstride = a.seg ? a.DV + DK : a.DV;
@@ -1517,7 +1542,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
         }
         bad_seen = sm.bad;
     }
-    if (bad_seen >= nchunks) {
+    if (STORE && tile == 0 && threadIdx.x == 0) a.ck_flag[unit] = bad_seen < nchunks ? 1 : 0;
+    if (STORE || bad_seen >= nchunks) {
         vm_wait<0>();  // no direct copy may land after the workgroup's LDS is released
         return;
     }
@@ -1652,7 +1678,50 @@ hipError_t launch_segments_t(const FwdArgs& f, int seg, int nseg, const float* m
     return hipGetLastError();
 }
 
+// Checkpoint sweep of the chunked backward (diagonal, bf16, 64-column tiles).
+template <int DK>
+hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, int* ck_flag, hipStream_t stream) {
+    const int units = f.B * f.H;
+    if (units == 0 || f.T == 0) return hipSuccess;
+    Args a;
+    a.q = static_cast<const bf16_t*>(f.q);
+    a.k = static_cast<const bf16_t*>(f.k);
+    a.v = static_cast<const bf16_t*>(f.v);
+    a.alpha = static_cast<const bf16_t*>(f.alpha);
+    a.omega = static_cast<const bf16_t*>(f.omega);
+    a.r = static_cast<const bf16_t*>(f.r);
+    a.c0 = f.c0;
+    a.mu = f.mu;
+    a.T = f.T;
+    a.H = f.H;
+    a.DV = f.dv;
+    a.units = units;
+    a.S0 = f.S0;
+    a.p0 = f.p0;
+    a.o = nullptr;
+    a.S_T = nullptr;
+    a.p_T = nullptr;
+    a.cu = nullptr;
+    a.ord = nullptr;
+    a.tok0 = 0;
+    a.ck = ck;
+    a.ck_floats = ck_floats;
+    a.ck_flag = ck_flag;
+    const int ntile = f.dv / DVT;
+    const int groups = (units + 7) / 8;
+    const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, 0, false, 2, false, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,
+                                      hipStream_t stream) {
+    if (!chunked_supports(a) || a.variant != 0 || a.gates || a.cu_seqlens) return hipErrorNotSupported;
+    return a.dk == 128 ? launch_checkpoints_t<128>(a, ck, ck_floats, ck_flag, stream)
+                       : launch_checkpoints_t<64>(a, ck, ck_floats, ck_flag, stream);
+}
 
 // Compute units of the current device (read once per device and cached; 256
 // on MI355X).  A failed query gives 256.

@@ -71,6 +71,10 @@ struct BwdArgs {
     float* dp0;
     float* dc0;   // may be NULL
     float* work;  // backward_workspace_bytes() bytes
+    // set by the chunked backward: flag[unit] = 1 for the (batch, head) pairs
+    // the recurrent memory adjoint must take (their decays leave the chunked
+    // form's range); the recurrent memory kernel then skips every other pair
+    const int* only_flagged = nullptr;
 };
 
 // Bytes of device workspace one backward call needs (0 for an empty call).
@@ -117,6 +121,20 @@ hipError_t launch_split(const FwdArgs& a, int nseg, void* workspace, size_t work
 // sseg: [B*H][nseg][dk][dv + dk] segment end states.
 hipError_t launch_chunked_segments(const FwdArgs& a, int seg, int nseg, const float* mob, void* ophi, float* sseg,
                                    hipStream_t stream);
+// The chunked memory adjoint of the diagonal bf16 form (kdn_backward_chunk.hip):
+// one workgroup per (batch, head, 64 value columns) whose flag is 0, reading
+// the checkpoints launch_chunked_checkpoints wrote (region ck_floats floats per
+// (unit, tile) at a.work) and writing the per-token tile sums, p_{t-1}, dv and
+// dS0 in the recurrent memory adjoint's workspace layout.
+hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream);
+// Checkpoint sweep of the chunked backward (kdn_chunked.hip, diagonal bf16,
+// d_v a multiple of 64): per (unit, 64-column tile) region of ck_floats
+// floats from ck, the memory in the midpoint frame diag(g_15) S at every
+// 32-token chunk start ([chunk][dk][64]) and, in tile 0's region after those,
+// p at every chunk start ([chunk][dk]); ck_flag[unit] = 1 where a chunk
+// leaves the chunked form's range (checkpoints stop there), else 0.
+hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,
+                                      hipStream_t stream);
 // Chunkwise forward of the isotropic variant (variant 1) on Gram matrices of
 // the raw keys (kdn_iso.hip); narrow = 32 value columns per workgroup, else 64.
 // Same preconditions as launch_chunked, and T > 0.

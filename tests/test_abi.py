@@ -293,10 +293,11 @@ def call_validate_bwd(lib, a):
 
 def test_backward_workspace_size_formula(lib):
     # per 64-column tile: ceil(T/32) checkpoints of S and of p (one copy per 8 value columns), a
-    # 32-token stash, and per token the tile's four row sums and p_{t-1}
+    # 32-token stash, and per token the tile's four row sums and p_{t-1}; then one int per
+    # (batch, head) pair (the chunked path's range flags)
     for B, T, H, dk, dv in ((2, 40, 3, 64, 128), (8, 4096, 16, 128, 128), (1, 1, 1, 128, 64)):
         nseg, nt = -(-T // 32), dv // 64
-        want = B * H * nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk + 5 * T * dk) * 4
+        want = B * H * nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk + 5 * T * dk) * 4 + B * H * 4
         assert lib.kdn_backward_workspace_size(B, T, H, dk, dv) == want
     assert lib.kdn_backward_workspace_size(0, 10, 2, 64, 64) == 0
     assert lib.kdn_backward_workspace_size(2, 0, 2, 64, 64) == 0
