@@ -613,6 +613,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
     constexpr bool ISO = VAR != 0;
     const int nunit = A.B * A.H;
     const int unit = int(blockIdx.x);
+    if (A.only_flagged && !A.only_flagged[unit]) return;  // the chunked path's adjoint took this pair
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
@@ -971,6 +972,8 @@ hipError_t launch_chunked_path(const BwdArgs& a, hipStream_t s) {
     hipError_t e = launch_chunked_checkpoints(f, a.work, uf, flag, s);
     if (e != hipSuccess) return e;
     e = launch_backward_chunk(a, uf, flag, s);
+    if (e != hipSuccess) return e;
+    e = launch_backward_unc_chunk(a, uf, flag, s);
     if (e != hipSuccess) return e;
     BwdArgs r = a;
     r.only_flagged = flag;

@@ -44,6 +44,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 namespace kdn {
 namespace {
@@ -81,10 +82,13 @@ struct CSmem {
     bf16_t dM[256];        // tril(-dR Dn^T) of the current half [t][s]
     bf16_t dQK[256];       // tril(dO Dn^T) [t][s]
     float r[L];
+    float cr[L];           // mu / r_t
     float d[L];            // M_tt = r_t + k_t . kappa'_t
     float dr[L];           // dM_tt
     float GA[DK], GB[DK];  // g_15 and gb_31
     float dGA[DK], dGB[DK];
+    float spart[L][DK / 64];  // sum_i p_hat k^2 over each wave's 64 channels (fp32)
+    float uacc[DK / 16][L];   // sum_i d kappa kappa' over each key tile's 16 channels
 };
 
 // The lane index as a value the compiler cannot hoist out of the chunk loop:
@@ -156,6 +160,16 @@ __device__ __forceinline__ void put(bf16_t* D, int row0, int c0, f4 c) {
 
 constexpr f4 kZero = {0.f, 0.f, 0.f, 0.f};
 
+// One chunk's inputs as each thread loads them, one chunk ahead: its 16-byte
+// piece of the raw k, q, alpha, omega tiles and of the v and dO tiles, r
+// (threads < 32) and (state waves) its 16 entries of the checkpoint Sg.
+struct Pre {
+    u4 kqaw[4];
+    u4 v, d;
+    bf16_t r;
+    f4 sg[4];
+};
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -185,7 +199,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
     const bf16_t* win = static_cast<const bf16_t*>(A.omega);
     const bf16_t* rin = static_cast<const bf16_t*>(A.r);
     const bf16_t* doin = static_cast<const bf16_t*>(A.dO);
-    const float* ck = A.work + (size_t(unit) * ntile + tile) * ck_floats;                // [chunk][DK][64]
+    float* ckw = A.work + (size_t(unit) * ntile + tile) * ck_floats;  // [chunk][DK / 4][64][4]
+    const float* ck = ckw;
     const float* ckp = A.work + size_t(unit) * ntile * ck_floats + size_t(nchunks) * DK * TILE;  // [chunk][DK]
     float* partial = A.work + size_t(nunit) * ntile * ck_floats;  // [unit][T][ntile][4][DK]
     float* pbuf = partial + size_t(nunit) * T * ntile * 4 * DK;   // [unit][T][ntile][DK]
@@ -207,88 +222,165 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 dS[ct][e] = A.dS_T[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n];
     }
 
+    Pre pre;
+    // chunk c's inputs into pre (rows past T repeat the last token; v and dO
+    // rows past T read as zero)
+    const auto load = [&](int c) {
+        const int tid = threadIdx.x;
+        const int t0 = c * L, nvalid = min(L, T - t0), last = nvalid - 1;
+        constexpr int PR = DK / 8;
+        if (tid < L * PR) {
+            const int t = tid / PR, cc = tid % PR;
+            const size_t src = tokidx(t0 + min(t, last)) * DK + 8 * cc;
+            pre.kqaw[0] = *reinterpret_cast<const u4*>(kin + src);
+            pre.kqaw[1] = *reinterpret_cast<const u4*>(qin + src);
+            pre.kqaw[2] = *reinterpret_cast<const u4*>(ain + src);
+            pre.kqaw[3] = *reinterpret_cast<const u4*>(win + src);
+        }
+        if (tid < L * 8) {
+            const int t = tid / 8, cc = tid % 8;
+            const bool ok = t < nvalid;
+            const size_t src = tokidx(t0 + min(t, last)) * DV + tile * TILE + 8 * cc;
+            const u4 zero = {0u, 0u, 0u, 0u};
+            pre.v = ok ? *reinterpret_cast<const u4*>(vin + src) : zero;
+            pre.d = (ok && doin) ? *reinterpret_cast<const u4*>(doin + src) : zero;
+        }
+        if (tid < L) pre.r = rin[tokidx(t0 + min(tid, last))];
+        if (stw) {
+            // [DK / 4][64][4]: rows 4 (l / 16) .. + 3 of the wave's 16 in one load
+            const f4* ckc = reinterpret_cast<const f4*>(ck + size_t(c) * DK * TILE);
+            const int ln = threadIdx.x & 63;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) pre.sg[ct] = ckc[(4 * wave + (ln >> 4)) * TILE + 16 * ct + (ln & 15)];
+        }
+    };
+    load(nchunks - 1);
     for (int c = nchunks - 1; c >= 0; --c) {
         const int lane = lane_id();  // (see lane_id)
         const int n = lane & 15, g4 = 4 * (lane >> 4);
         const int t0 = c * L;
         const int nvalid = min(L, T - t0);
-        // ---- loads: raw k, q, alpha, omega, v and dO tiles, r, Sg ----
+        // ---- this chunk's inputs (loaded one chunk ahead) into LDS ----
         {
-            const int last = nvalid - 1;
+            const int tid = threadIdx.x;
             constexpr int PR = DK / 8;  // 16-byte pieces per row
-            for (int pc = threadIdx.x; pc < L * PR; pc += NTH) {
-                const int t = pc / PR, cc = pc % PR;
-                const size_t src = tokidx(t0 + min(t, last)) * DK + 8 * cc;
-                *reinterpret_cast<u4*>(&sm.K[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(kin + src);
-                *reinterpret_cast<u4*>(&sm.Q[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(qin + src);
-                *reinterpret_cast<u4*>(&sm.A[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(ain + src);
-                *reinterpret_cast<u4*>(&sm.W[t * DK + 8 * cc]) = *reinterpret_cast<const u4*>(win + src);
+            if (tid < L * PR) {
+                const int t = tid / PR, cc = tid % PR;
+                *reinterpret_cast<u4*>(&sm.K[t * DK + 8 * cc]) = pre.kqaw[0];
+                *reinterpret_cast<u4*>(&sm.Q[t * DK + 8 * cc]) = pre.kqaw[1];
+                *reinterpret_cast<u4*>(&sm.A[t * DK + 8 * cc]) = pre.kqaw[2];
+                *reinterpret_cast<u4*>(&sm.W[t * DK + 8 * cc]) = pre.kqaw[3];
             }
-            for (int pc = threadIdx.x; pc < L * 8; pc += NTH) {
-                const int t = pc / 8, cc = pc % 8;
-                const bool ok = t < nvalid;
-                const size_t src = tokidx(t0 + min(t, last)) * DV + tile * TILE + 8 * cc;
-                const u4 zero = {0u, 0u, 0u, 0u};
-                *reinterpret_cast<u4*>(&sm.V[t * TILE + 8 * cc]) = ok ? *reinterpret_cast<const u4*>(vin + src) : zero;
-                const u4 dov = (ok && doin) ? *reinterpret_cast<const u4*>(doin + src) : zero;
-                *reinterpret_cast<u4*>(&sm.dO[sw<TILE>(t, 8 * cc)]) = dov;
+            if (tid < L * 8) {
+                const int t = tid / 8, cc = tid % 8;
+                *reinterpret_cast<u4*>(&sm.V[t * TILE + 8 * cc]) = pre.v;
+                *reinterpret_cast<u4*>(&sm.dO[sw<TILE>(t, 8 * cc)]) = pre.d;
             }
-            if (threadIdx.x < L) {
-                const int t = threadIdx.x;
-                sm.r[t] = t < nvalid ? bf1(rin[tokidx(t0 + t)]) : 1.f;
+            if (tid < L) {
+                const float rt = tid < nvalid ? bf1(pre.r) : 1.f;
+                sm.r[tid] = rt;
+                sm.cr[tid] = mu / rt;
             }
-            if (stw) {
-                const float* ckc = ck + size_t(c) * DK * TILE;
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Sg[ct][e] = ckc[(16 * wave + g4 + e) * TILE + 16 * ct + n];
-            }
+            for (int ct = 0; ct < 4; ++ct) Sg[ct] = pre.sg[ct];
         }
         bar();
+        if (c > 0) load(c - 1);  // the next chunk's inputs, in flight during this one
         // ---- chain: uncertainty recurrence, decays, the chunk's operands ----
-        if (wave < NCW) {
+        // (MASK: a tail chunk; padding tokens take alpha = 1, k = q = omega = 0)
+        const auto chain = [&](auto maskc) {
+            constexpr bool MASK = decltype(maskc)::value;
             const int i = 64 * wave + lane;
-            // first half: rho_t = 1 / prod_{t<u<=15} alpha_u, from the
-            // midpoint backwards
-            float hr = 1.f;
-#pragma unroll 1
-            for (int t = HL - 1; t >= 0; --t) {
-                sm.rho[t * DK + i] = hr;  // 1 / rho for now
-                hr *= t < nvalid ? bf1(sm.A[t * DK + i]) : 1.f;
+            // the first half's 1 / rho_t = prod_{t<u<=15} alpha_u, from the
+            // midpoint backwards (registers)
+            float hr[HL], a0;
+            {
+                float a16[HL];
+#pragma unroll
+                for (int t = 0; t < HL; ++t) {
+                    const float x = bf1(sm.A[t * DK + i]);
+                    a16[t] = (!MASK || t < nvalid) ? x : 1.f;
+                }
+                hr[HL - 1] = 1.f;
+#pragma unroll
+                for (int t = HL - 2; t >= 0; --t) hr[t] = hr[t + 1] * a16[t + 1];
+                a0 = a16[0];
             }
-            const float ga = hr;  // g_15
+            const float ga = hr[0] * a0;  // g_15
             float p = ckp[size_t(c) * DK + i];
             float gb = 1.f;
-#pragma unroll 2
-            for (int t = 0; t < L; ++t) {
-                const bool ok = t < nvalid;
-                const float al = ok ? bf1(sm.A[t * DK + i]) : 1.f;
-                const float kk = ok ? bf1(sm.K[t * DK + i]) : 0.f;
-                const float qq = ok ? bf1(sm.Q[t * DK + i]) : 0.f;
-                const float w = ok ? bf1(sm.W[t * DK + i]) : 0.f;
-                const float rt = sm.r[t];
-                if (ok && tile == 0) pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i] = p;
-                const float ph = fmaf(al * al, p, w);
-                const float kap = ph * kk;
-                p = ph / fmaf((mu / rt) * kk * kk, ph, 1.f);
-                float rh, rinv;  // rho and 1 / rho
-                if (t < HL) {
-                    rinv = sm.rho[t * DK + i];
-                    rh = 1.f / rinv;
-                } else {
-                    gb *= al;
-                    rh = gb;
-                    rinv = 1.f / gb;
+            // eight tokens at a time: every LDS read of a group is issued
+            // before its recurrence starts.  The chain keeps to the
+            // sequential part (p_hat and rho per token); every wave forms the
+            // operands from them below.
+#pragma unroll
+            for (int b8i = 0; b8i < L / 8; ++b8i) {
+                float al[8], kk[8], w[8], cv[8], pv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 8 * b8i + j;
+                    const bool ok = !MASK || t < nvalid;
+                    const float xa = bf1(sm.A[t * DK + i]), xk = bf1(sm.K[t * DK + i]);
+                    const float xw = bf1(sm.W[t * DK + i]);
+                    al[j] = ok ? xa : 1.f;
+                    kk[j] = ok ? xk : 0.f;
+                    w[j] = ok ? xw : 0.f;
+                    cv[j] = sm.cr[t];
                 }
-                sm.rho[t * DK + i] = rh;
-                sm.kap[t * DK + i] = kap;
-                sm.Kt[sw<DK>(t, i)] = to_bf(kk * rh);
-                sm.Qt[sw<DK>(t, i)] = to_bf(qq * rh);
-                sm.Kh[sw<DK>(t, i)] = to_bf(kap * rinv);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 8 * b8i + j;
+                    pv[j] = p;
+                    const float ph = fmaf(al[j] * al[j], p, w[j]);
+                    // the forward chain's arithmetic: p' = p_hat / (1 + (mu / r) k^2 p_hat)
+                    p = ph * __builtin_amdgcn_rcpf(fmaf(cv[j] * kk[j], ph * kk[j], 1.f));
+                    float rh;
+                    if (t < HL) {
+                        rh = __builtin_amdgcn_rcpf(hr[t]);
+                    } else {
+                        gb *= al[j];
+                        rh = gb;
+                    }
+                    sm.rho[t * DK + i] = rh;
+                    sm.kap[t * DK + i] = ph;  // p_hat until the operands are formed
+                }
+                if (tile == 0)  // p_{t-1} of the group's tokens
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int t = 8 * b8i + j;
+                        if (!MASK || t < nvalid) pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i] = pv[j];
+                    }
+                asm volatile("" ::: "memory");  // one group at a time
             }
             sm.GA[i] = ga;
             sm.GB[i] = gb;
+        };
+        if (wave < NCW) {
+            if (nvalid == L) chain(std::false_type{});
+            else chain(std::true_type{});
+        }
+        bar();
+        // the chunk's operands from p_hat and rho (every wave): kappa' =
+        // p_hat k, Kt = k rho, Qt = q rho, Kh = kappa' / rho; and the gain
+        // denominators' sums p_hat k^2 in fp32 (a wave covers 64 channels of
+        // one token per step)
+#pragma unroll
+        for (int j = 0; j < L * DK / NTH; ++j) {
+            const int e = threadIdx.x + NTH * j;
+            const int t = e / DK, i = e % DK;
+            const bool ok = t < nvalid;
+            const float xk = bf1(sm.K[e]), xq = bf1(sm.Q[e]);
+            const float kk = ok ? xk : 0.f, qq = ok ? xq : 0.f;
+            const float rh = sm.rho[e];
+            const float kap = sm.kap[e] * kk;
+            sm.kap[e] = kap;
+            sm.Kt[sw<DK>(t, i)] = to_bf(kk * rh);
+            sm.Qt[sw<DK>(t, i)] = to_bf(qq * rh);
+            sm.Kh[sw<DK>(t, i)] = to_bf(kap * __builtin_amdgcn_rcpf(rh));
+            float sk = sum16(kap * kk);
+            sk = halve16(sk, sk);
+            sk = halve32(sk, sk);
+            if (lane == 0) sm.spart[t][i / 64] = sk;
         }
         if (stw) {
             // the first half's start state as bf16
@@ -480,23 +572,48 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 dkt -= neg;
                 // acc[e]: token th + g4 + e, channel i0 + n
                 const int i = i0 + n;
+                float uv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tl = th + g4 + e;
                     const float rh = sm.rho[tl * DK + i], kp = sm.kap[tl * DK + i];
                     const float kk = bf1(sm.K[tl * DK + i]), qq = bf1(sm.Q[tl * DK + i]);
-                    const float dq = dqt[e] * rh, dkc = dkt[e] * rh, dkapc = dkh[e] / rh;
+                    const float dq = dqt[e] * rh, dkc = dkt[e] * rh, dkapc = dkh[e] * __builtin_amdgcn_rcpf(rh);
                     const float drt = sm.dr[tl], dt = sm.d[tl];
+                    const float dkap = dt * fmaf(-kk, drt, dkapc);
+                    uv[e] = dkap * kp;
                     sm.kap[tl * DK + i] = fmaf(dkc, kk, fmaf(dq, qq, -dkapc * kp));  // w = d rho . rho
                     if (tl < nvalid) {
                         float* dst = partial + ((size_t(unit) * T + t0 + tl) * ntile + tile) * 4 * DK + i;
                         dst[0] = dq;
-                        dst[DK] = dt * fmaf(-kk, drt, dkapc);
+                        dst[DK] = dkap;
                         dst[2 * DK] = fmaf(-kp, drt, dkc);
                     }
                 }
+                // u_t = sum_i d kappa kappa' over the key tile's 16 channels
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float su = sum16(uv[e]);
+                    if (n == 0) sm.uacc[wave][th + g4 + e] = su;
+                }
             }
             bar();
+            if (wave == NT - 1 && lane < HL) {
+                // the uncertainty adjoint's per-token sums go into this
+                // chunk's checkpoint slot (read already): u_t of this tile at
+                // [t]; tile 0 also d_t = r_t + sum_i p_hat k^2 at [L + t]
+                float u = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < NT; ++w2) u += sm.uacc[w2][th + lane];
+                float* slot = ckw + size_t(c) * DK * TILE;
+                slot[th + lane] = u;
+                if (tile == 0) {
+                    float sk = sm.r[th + lane];
+#pragma unroll
+                    for (int w2 = 0; w2 < DK / 64; ++w2) sk += sm.spart[th + lane][w2];
+                    slot[L + th + lane] = sk;
+                }
+            }
             if (half == 1) {
                 // the first half: its start state and dX = dS (the state waves
                 // hold the cotangent of the midpoint state)
@@ -510,28 +627,43 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
             }
         }
         // ---- d alpha of the memory part, per channel over the chunk ----
-        if (wave < NCW) {
+        const auto scan = [&](auto maskc) {
+            constexpr bool MASK = decltype(maskc)::value;
             const int i = 64 * wave + lane;
             const float fa = sm.dGA[i] * sm.GA[i], fb = sm.dGB[i] * sm.GB[i];
+            float* dst = partial + ((size_t(unit) * T + t0) * ntile + tile) * 4 * DK + 3 * DK + i;
+            const size_t tstep = size_t(ntile) * 4 * DK;
             // u <= 15: -sum_{t<u} w_t + fa;  u >= 16: sum_{t>=u} w_t + fb
-            float pre = 0.f;
 #pragma unroll
-            for (int u = 0; u < HL; ++u) {
-                if (u < nvalid) {
-                    const float al = bf1(sm.A[u * DK + i]);
-                    partial[((size_t(unit) * T + t0 + u) * ntile + tile) * 4 * DK + 3 * DK + i] = (fa - pre) / al;
-                }
-                pre += sm.kap[u * DK + i];
-            }
-            float suf = 0.f;
+            for (int hf = 0; hf < 2; ++hf) {
+                float wv[HL], av[HL];
 #pragma unroll
-            for (int u = L - 1; u >= HL; --u) {
-                suf += sm.kap[u * DK + i];
-                if (u < nvalid) {
-                    const float al = bf1(sm.A[u * DK + i]);
-                    partial[((size_t(unit) * T + t0 + u) * ntile + tile) * 4 * DK + 3 * DK + i] = (suf + fb) / al;
+                for (int j = 0; j < HL; ++j) {
+                    const int u = HL * hf + j;
+                    wv[j] = sm.kap[u * DK + i];
+                    const float x = bf1(sm.A[u * DK + i]);
+                    av[j] = (!MASK || u < nvalid) ? x : 1.f;
                 }
+                float acc = 0.f;
+                if (hf == 0) {
+#pragma unroll
+                    for (int j = 0; j < HL; ++j) {
+                        if (!MASK || j < nvalid) dst[j * tstep] = (fa - acc) * __builtin_amdgcn_rcpf(av[j]);
+                        acc += wv[j];
+                    }
+                } else {
+#pragma unroll
+                    for (int j = HL - 1; j >= 0; --j) {
+                        acc += wv[j];
+                        if (!MASK || HL + j < nvalid) dst[(HL + j) * tstep] = (acc + fb) * __builtin_amdgcn_rcpf(av[j]);
+                    }
+                }
+                asm volatile("" ::: "memory");
             }
+        };
+        if (wave < NCW) {
+            if (nvalid == L) scan(std::false_type{});
+            else scan(std::true_type{});
         }
         bar();
     }
@@ -544,7 +676,199 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 A.dS0[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n] = dS[ct][e];
 }
 
+// ---------------------------------------------------------------------------
+// The uncertainty adjoint after the chunked memory adjoint: one wave per
+// (batch, head, 64 key channels), lane = channel, backwards over the tokens.
+// The step is the token recurrence's (kdn_backward.hip): with
+// p_hat = alpha^2 p_{t-1} + omega, d = r + sum_i p_hat k^2 and
+// u = sum_i d kappa p_hat k, the gain's derivatives d kappa / d p_hat = k / d
+// and d kappa / dk = p_hat / d and the denominator's dd = -u / d^2, the
+// posterior p' = p_hat / (1 + (mu / r) k^2 p_hat); the carried dp and the
+// gradients of k, alpha, omega follow per channel.  d and u are sums over
+// every channel (and u over the column tiles) that do not depend on dp: the
+// chunked kernel leaves them per token in each chunk's checkpoint slot, so
+// the channels split over waves with no exchange per token.  dr, a channel
+// sum that does depend on dp, is left per wave in the slot and added by
+// kdn_backward_dr_kernel.
+// The carried dp is affine in itself per token, dp_{t-1} = f_t dp_t + g_t
+// with f_t = alpha^2 / den^2 and g_t = alpha^2 (gk k / d + dd k^2), so the
+// sequence is cut into segments of SEGU tokens run in parallel: a first
+// launch (MAPS) composes each segment's affine map, a second runs every
+// segment from its exact entering dp (the later segments' maps applied to
+// dp_T in order) and writes the gradients.
+// Slot of chunk c (tile 0 unless noted): [t] u of each tile (its own slot),
+// [L + t] d, [2L + t] dd, [3L + 32 w + t] wave w's share of dr, and in the
+// slot of a segment's first chunk [MAPOFF + 2 i], [MAPOFF + 2 i + 1] the
+// segment's map of channel i.
+// ---------------------------------------------------------------------------
+constexpr int PFU = 8;  // prefetch ring: token inputs are loaded 7 tokens ahead
+constexpr int SEGU = 512;  // tokens per segment of the uncertainty adjoint
+constexpr int MAPOFF = 256;
+
+struct UncTok {
+    float q[2], k[2], ks[2], a[2];  // the tiles' (at most 2) partial sums
+    float u[2];
+    float d, pp;
+    bf16_t al, kk, w, r;
+};
+
+template <int DK, bool MAPS>
+__global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
+    constexpr int NWV = DK / 64;
+    const int nunit = A.B * A.H;
+    const int ntile = A.dv / TILE;  // 1 or 2
+    const int unit = int(blockIdx.x) % nunit;
+    const int wv = (int(blockIdx.x) / nunit) % NWV;  // 64-channel group
+    const int sg = int(blockIdx.x) / (nunit * NWV);  // segment
+    if (flag[unit]) return;
+    const int h = unit % A.H;
+    const size_t b = size_t(unit / A.H);
+    const int T = A.T;
+    const int lane = threadIdx.x & 63;
+    const int i = 64 * wv + lane;
+    const float mu = A.mu;
+    const bf16_t* kin = static_cast<const bf16_t*>(A.k);
+    const bf16_t* ain = static_cast<const bf16_t*>(A.alpha);
+    const bf16_t* win = static_cast<const bf16_t*>(A.omega);
+    const bf16_t* rin = static_cast<const bf16_t*>(A.r);
+    const float* partial = A.work + size_t(nunit) * ntile * ck_floats;
+    const float* pbuf = partial + size_t(nunit) * T * ntile * 4 * DK;
+    float* slot0 = A.work + size_t(unit) * ntile * ck_floats;  // tile 0's region
+    const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
+    const auto slot = [&](int tile, int t) {
+        return A.work + (size_t(unit) * ntile + tile) * ck_floats + size_t(t / L) * DK * TILE;
+    };
+    const auto load = [&](UncTok& x, int t) {
+        t = max(t, 0);
+        const size_t tok = tokidx(t);
+        const int tl = t % L;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const int tc = min(tile, ntile - 1);
+            const float* src = partial + ((size_t(unit) * T + t) * ntile + tc) * 4 * DK + i;
+            x.k[tile] = src[DK];
+            if (!MAPS) {
+                x.q[tile] = src[0];
+                x.ks[tile] = src[2 * DK];
+                x.a[tile] = src[3 * DK];
+            }
+            x.u[tile] = slot(tc, t)[tl];
+        }
+        x.d = slot(0, t)[L + tl];
+        x.pp = pbuf[(size_t(unit) * T + t) * ntile * DK + i];
+        x.al = ain[tok * DK + i];
+        x.kk = kin[tok * DK + i];
+        x.w = win[tok * DK + i];
+        x.r = rin[tok];
+    };
+    const int nseg = (T + SEGU - 1) / SEGU;
+    const int s0 = sg * SEGU, s1 = min(T, s0 + SEGU);
+    const auto mapslot = [&](int s) { return slot0 + size_t(s * SEGU / L) * DK * TILE + MAPOFF + 2 * i; };
+    float dp = 0.f, fa = 1.f, fb = 0.f;  // OUTPUTS: the carried dp; MAPS: dp_t = fa dp_in + fb
+    if (!MAPS) {
+        dp = A.dp_T ? A.dp_T[size_t(unit) * DK + i] : 0.f;
+        for (int s = nseg - 1; s > sg; --s) {
+            const float* m = mapslot(s);
+            dp = fmaf(m[0], dp, m[1]);
+        }
+    }
+    const auto step = [&](int t, const UncTok& x) {
+        const bool two = ntile > 1;
+        const float gk = x.k[0] + (two ? x.k[1] : 0.f);
+        const float u = x.u[0] + (two ? x.u[1] : 0.f);
+        const float al = bf1(x.al), kk = bf1(x.kk), w = bf1(x.w), rt = bf1(x.r);
+        const size_t tok = tokidx(t);
+        const float ph = al * al * x.pp + w;
+        const float inv = 1.0f / x.d;
+        const float dd = -u * inv * inv;
+        const float mr = mu / rt;
+        const float k2 = kk * kk;
+        const float den = 1.0f + mr * k2 * ph;
+        if (MAPS) {
+            const float f = al * al / (den * den);
+            fa *= f;
+            fb = fmaf(f, fb, al * al * (gk * kk * inv + dd * k2));
+            return;
+        }
+        const float gq = x.q[0] + (two ? x.q[1] : 0.f);
+        const float gks = x.ks[0] + (two ? x.ks[1] : 0.f), ga = x.a[0] + (two ? x.a[1] : 0.f);
+        const float pn = ph / den;
+        const float du = -dp * pn * pn;
+        const float dph = dp / (den * den) + gk * kk * inv + dd * k2;
+        A.dq[tok * DK + i] = gq;
+        A.dk_[tok * DK + i] = gks + gk * ph * inv + 2.0f * dd * ph * kk + 2.0f * du * mr * kk;
+        A.dalpha[tok * DK + i] = ga + 2.0f * dph * al * x.pp;
+        A.domega[tok * DK + i] = dph;
+        dp = dph * al * al;
+        float dr = -du * mr * k2 / rt;
+        dr = sum16(dr);
+        dr = halve16(dr, dr);
+        dr = halve32(dr, dr);
+        float* sl = slot0 + size_t(t / L) * DK * TILE;
+        if (lane == 0) {
+            sl[3 * L + 32 * wv + t % L] = dr;
+            if (wv == 0) sl[2 * L + t % L] = dd;
+        }
+    };
+    UncTok ring[PFU];
+#pragma unroll
+    for (int s = 0; s < PFU - 1; ++s) load(ring[s], max(s1 - 1 - s, s0));
+    for (int t = s1 - 1; t >= s0; t -= PFU) {
+#pragma unroll
+        for (int s = 0; s < PFU; ++s) {
+            load(ring[(s + PFU - 1) % PFU], max(t - s - (PFU - 1), s0));  // PFU - 1 tokens ahead
+            if (t - s >= s0) step(t - s, ring[s]);
+        }
+    }
+    if (MAPS) {
+        float* m = mapslot(sg);
+        m[0] = fa;
+        m[1] = fb;
+    } else if (sg == 0) {
+        A.dp0[size_t(unit) * DK + i] = dp;
+    }
+}
+
+// dr = dd + the waves' shares (one thread per token of a (batch, head) pair)
+template <int DK>
+__global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
+    const int nunit = A.B * A.H;
+    const int ntile = A.dv / TILE;
+    const int unit = int(blockIdx.y);
+    const int t = int(blockIdx.x) * 256 + int(threadIdx.x);
+    if (flag[unit] || t >= A.T) return;
+    const float* sl = A.work + size_t(unit) * ntile * ck_floats + size_t(t / L) * DK * TILE;
+    float dr = sl[2 * L + t % L];
+#pragma unroll
+    for (int w = 0; w < DK / 64; ++w) dr += sl[3 * L + 32 * w + t % L];
+    const size_t b = size_t(unit / A.H);
+    A.dr[(b * size_t(A.T) + size_t(t)) * size_t(A.H) + size_t(unit % A.H)] = dr;
+    (void)nunit;
+}
+
 }  // namespace
+
+hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+    const unsigned units = unsigned(long(a.B) * a.H);
+    const unsigned nseg = unsigned((a.T + SEGU - 1) / SEGU);
+    const dim3 dgrid(unsigned((a.T + 255) / 256), units);
+    if (a.dk == 128) {
+        const dim3 grid(units * 2 * nseg);
+        if (nseg > 1)
+            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, true>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, false>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL(kdn_backward_dr_kernel<128>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
+    } else if (a.dk == 64) {
+        const dim3 grid(units * nseg);
+        if (nseg > 1)
+            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, true>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, false>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL(kdn_backward_dr_kernel<64>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
+    } else {
+        return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
     const unsigned units = unsigned(long(a.B) * a.H);

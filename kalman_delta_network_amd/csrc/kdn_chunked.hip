@@ -177,7 +177,7 @@ struct Args {
     // checkpoint mode (the chunked backward's forward sweep; diagonal,
     // ungated, 64-column tiles): per (unit, tile) region of ck_floats floats
     // from ck: the memory in the midpoint frame, diag(g_15) S, at every chunk
-    // start ([chunk][DK][64]), then (tile 0) p at every chunk start
+    // start ([chunk][DK / 4][64][4]), then (tile 0) p at every chunk start
     // ([chunk][DK]); ck_flag[unit] = 1 where a chunk leaves the chunked
     // form's range (its checkpoints stop there), else 0.  No o, S_T or p_T.
     float* ck = nullptr;
@@ -1444,15 +1444,15 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const bool run = c < nchunks && c < bad_seen;
             if (!phi) state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
             if (STORE && run) {
-                // chunk c's start state, diag(g_15) S (fp32)
-                float* ck = a.ck + (size_t(unit) * ntile + tile) * a.ck_floats + size_t(c) * DK * DVTN;
+                // chunk c's start state, diag(g_15) S (fp32), as [DK / 4][64][4]:
+                // rows 4j .. 4j + 3 of a column in one 16-byte store
+                f4* ck = reinterpret_cast<f4*>(a.ck + (size_t(unit) * ntile + tile) * a.ck_floats +
+                                               size_t(c) * DK * DVTN);
 #pragma unroll
                 for (int r4 = 0; r4 < DK / 16; ++r4)
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            ck[(16 * r4 + g4 + e) * DVTN + cw * (16 * NCT) + 16 * ct + n] = st.S[r4][ct][e];
+                        ck[((16 * r4 + g4) / 4) * DVTN + cw * (16 * NCT) + 16 * ct + n] = st.S[r4][ct];
             }
             if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
             // everything but the NCT loads just issued has landed: the v of

@@ -127,10 +127,14 @@ hipError_t launch_chunked_segments(const FwdArgs& a, int seg, int nseg, const fl
 // (unit, tile) at a.work) and writing the per-token tile sums, p_{t-1}, dv and
 // dS0 in the recurrent memory adjoint's workspace layout.
 hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream);
+// The uncertainty adjoint after launch_backward_chunk (same pairs, same
+// workspace): per-channel waves, with the per-token channel sums the chunked
+// kernel left in the checkpoint slots; then dr.
+hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream);
 // Checkpoint sweep of the chunked backward (kdn_chunked.hip, diagonal bf16,
 // d_v a multiple of 64): per (unit, 64-column tile) region of ck_floats
 // floats from ck, the memory in the midpoint frame diag(g_15) S at every
-// 32-token chunk start ([chunk][dk][64]) and, in tile 0's region after those,
+// 32-token chunk start ([chunk][dk / 4][64][4]) and, in tile 0's region after those,
 // p at every chunk start ([chunk][dk]); ck_flag[unit] = 1 where a chunk
 // leaves the chunked form's range (checkpoints stop there), else 0.
 hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,

@@ -113,12 +113,15 @@ def test_backward_empty_sequence_passes_state_cotangents_through(dev):
     w = wl.Workload("bwd_empty", "diagonal", "bf16", 2, 0, 3, 128, 128, 128.0, "uniform", 9)
     x = wl.forward_inputs(w)
     t = to_dev(x, "bf16", dev)
-    dS_T = torch.randn(2, 3, 128, 128, device=dev)
-    dp_T = torch.randn(2, 3, 128, device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    dS_T = torch.randn(2, 3, 128, 128, generator=gen).to(dev)
+    dp_T = torch.randn(2, 3, 128, generator=gen).to(dev)
     g = kdn.backward(**t, mu=w.mu, dS_T=dS_T, dp_T=dp_T)
     torch.cuda.synchronize()
     assert torch.equal(g["dS0"], dS_T) and torch.equal(g["dp0"], dp_T)
-    assert torch.allclose(g["dc0"], dp_T.sum(dim=(0, 2)))
+    # dc0 sums 256 fp32 values per head in the kernel's order, the reference
+    # in torch's: the orders differ by a few ulps of the partial sums (|x| <~ 4)
+    assert torch.allclose(g["dc0"], dp_T.sum(dim=(0, 2)), rtol=1e-5, atol=1e-4)
 
 
 def test_backward_deterministic(dev):
