@@ -70,11 +70,13 @@ struct CSmem {
     bf16_t Qt[L * DK];
     bf16_t Kh[L * DK];
     bf16_t S[DK * TILE];   // the half's start state, bf16 [i][col] swizzled
-    bf16_t dX[DK * TILE];  // dX of the half, bf16 [i][col] swizzled
+    bf16_t dX[TILE * DK];  // dX of the half, bf16 [col][i] swizzled
     bf16_t R[HL * TILE];   // [t][col] swizzled
     bf16_t Dn[2][HL * TILE];
     bf16_t dDn[HL * TILE];
     bf16_t dR[HL * TILE];
+    bf16_t dOT[TILE * L];  // dO transposed, [col][t] swizzled
+    bf16_t dRT[TILE * HL]; // dR transposed, [col][t] swizzled
     float Md[2 * 256];     // M's diagonal blocks, column-major [a][s][t]
     float Wi[2][2][64];    // block-inverse scratch
     bf16_t Td[2 * 256];    // their inverses [a][t][s]
@@ -156,6 +158,15 @@ __device__ __forceinline__ void put(bf16_t* D, int row0, int c0, f4 c) {
     const int lane = lane_id();
 #pragma unroll
     for (int e = 0; e < 4; ++e) D[sw<W>(row0 + 4 * (lane >> 4) + e, c0 + (lane & 15))] = to_bf(c[e]);
+}
+
+// accumulator tile (rows row0 + 4 (l / 16) + e, column c0 + l % 16) to the
+// transposed swizzled [cols][W] tile: the lane's four rows are consecutive
+// there (one 8-byte store)
+template <int W>
+__device__ __forceinline__ void putT(bf16_t* D, int row0, int c0, f4 c) {
+    const int lane = lane_id();
+    *reinterpret_cast<s4*>(D + sw<W>(c0 + (lane & 15), row0 + 4 * (lane >> 4))) = __builtin_bit_cast(s4, u2{pack2(c[0], c[1]), pack2(c[2], c[3])});
 }
 
 constexpr f4 kZero = {0.f, 0.f, 0.f, 0.f};
@@ -275,6 +286,11 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 const int t = tid / 8, cc = tid % 8;
                 *reinterpret_cast<u4*>(&sm.V[t * TILE + 8 * cc]) = pre.v;
                 *reinterpret_cast<u4*>(&sm.dO[sw<TILE>(t, 8 * cc)]) = pre.d;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sm.dOT[sw<L>(8 * cc + 2 * j, t)] = bf16_t(pre.d[j] & 0xffffu);
+                    sm.dOT[sw<L>(8 * cc + 2 * j + 1, t)] = bf16_t(pre.d[j] >> 16);
+                }
             }
             if (tid < L) {
                 const float rt = tid < nvalid ? bf1(pre.r) : 1.f;
@@ -475,7 +491,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 for (int ct = 0; ct < 4; ++ct) dS[ct][e] *= gbi;  // dS now holds dX
             }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) put<TILE>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
+            for (int ct = 0; ct < 4; ++ct) putT<DK>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
         }
         bar();
 
@@ -489,9 +505,9 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
             // dDn = QK^T dO + Kh dX
             if (wave < 4) {
                 const int ct = wave;
-                f4 acc = mfma16(col16p(QKh), col16<TILE>(sm.dO, th, 16 * ct), kZero);
+                f4 acc = mfma16(col16p(QKh), row16<L>(sm.dOT, 16 * ct, th), kZero);
 #pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(sm.Kh, th, k0), col32<TILE>(sm.dX, k0, 16 * ct), acc);
+                for (int k0 = 0; k0 < DK; k0 += 32) acc = mfma32(row32<DK>(sm.Kh, th, k0), row32<DK>(sm.dX, 16 * ct, k0), acc);
                 put<TILE>(sm.dDn, 0, 16 * ct, acc);
             }
             bar();
@@ -500,6 +516,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 const int ct = wave;
                 const f4 acc = mfma16(col16p(Tinv), col16<TILE>(sm.dDn, 0, 16 * ct), kZero);
                 put<TILE>(sm.dR, 0, 16 * ct, acc);
+                putT<HL>(sm.dRT, 0, 16 * ct, acc);
                 if (A.dv_)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -514,8 +531,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 f4 part = kZero;
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const f4 pos = mfma16(aq, col16<TILE>(sm.dO, th, 16 * ct), dS[ct]);
-                    const f4 neg = mfma16(akt, col16<TILE>(sm.dR, 0, 16 * ct), kZero);
+                    const f4 pos = mfma16(aq, row16<L>(sm.dOT, 16 * ct, th), dS[ct]);
+                    const f4 neg = mfma16(akt, row16<HL>(sm.dRT, 16 * ct, 0), kZero);
                     dS[ct] = pos - neg;
                     if (half == 0) part += dS[ct] * Sg[ct];
                 }
@@ -567,7 +584,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                     const b8 sv = row32<TILE>(Sh, i0, k0);
                     dqt = mfma32(row32<TILE>(sm.dO, th, k0), sv, dqt);
                     neg = mfma32(row32<TILE>(sm.dR, 0, k0), sv, neg);
-                    dkh = mfma32(row32<TILE>(Dnh, 0, k0), row32<TILE>(sm.dX, i0, k0), dkh);
+                    dkh = mfma32(row32<TILE>(Dnh, 0, k0), col32<DK>(sm.dX, k0, i0), dkh);
                 }
                 dkt -= neg;
                 // acc[e]: token th + g4 + e, channel i0 + n
@@ -621,7 +638,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         put<TILE>(sm.S, 16 * wave, 16 * ct, Sg[ct]);
-                        put<TILE>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
+                        putT<DK>(sm.dX, 16 * wave, 16 * ct, dS[ct]);
                     }
                 bar();
             }
