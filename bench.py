@@ -115,7 +115,8 @@ COUNTED = {
                          ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
     # the backward's kernels (uncertainty adjoint, memory adjoint, d c0): the
     # counters pass runs no other library kernel
-    "backward": ("diag_bf16_b8_t4096_h16_d128", "kdn_", ("kdn_backward.hip",)),
+    "backward": ("diag_bf16_b8_t4096_h16_d128", "kdn_", ("kdn_backward.hip", "kdn_backward_chunk.hip",
+                                                          "kdn_chunked.hip", "kdn_device.h")),
 }
 
 

@@ -139,6 +139,37 @@ def test_backward_deterministic(dev):
         assert torch.equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_backward_chunked_segments(dev, dk, dv):
+    # the diagonal bf16 backward runs in chunk form: T = 1100 is 34 full
+    # chunks and a 12-token tail, and three segments (512, 512, 76 tokens)
+    # of the uncertainty adjoint, whose maps carry dp across them
+    w = wl.Workload("bwd_seg", "diagonal", "bf16", 1, 1100, 2, dk, dv, float(dk), "uniform", 120 + dk + dv,
+                    omega_loc=-1.0)
+    x = wl.forward_inputs(w)
+    ct = wl.backward_cotangents(w, with_state=True)
+    rng = np.random.default_rng(121)
+    st = {"S0": wl.round_bf16(rng.standard_normal((1, 2, dk, dv)).astype(np.float32) * 0.2),
+          "p0": rng.uniform(0.5, 2.0, (1, 2, dk)).astype(np.float32)}
+    got = run_backward(dev, w, x, ct, st)
+    ref = oracle_backward(w, x, ct, st)
+    check(f"chunked/segments/dk{dk}/dv{dv}", got, ref, "bf16")
+
+
+def test_backward_chunked_with_a_pair_out_of_range(dev):
+    # one (batch, head) pair has a chunk of alpha = 1e-6, outside the chunked
+    # form's range: that pair takes the token recurrence's adjoint, the
+    # others the chunked one, in the same call
+    w = wl.Workload("bwd_mix", "diagonal", "bf16", 2, 300, 2, 128, 128, 128.0, "uniform", 130, omega_loc=-1.0)
+    x = wl.forward_inputs(w)
+    x["alpha"][1, 96:128, 0] = wl.round_bf16(np.full((32, 128), 1e-6, np.float32))
+    ct = wl.backward_cotangents(w, with_state=True)
+    st = {"S0": None, "p0": None}
+    got = run_backward(dev, w, x, ct, st)
+    ref = oracle_backward(w, x, ct, st)
+    check("chunked/mixed range", got, ref, "bf16")
+
+
 @pytest.mark.parametrize("name", ["diag_bf16_b8_t4096_h16_d128", "iso_bf16_b8_t4096_h16_d128"])
 def test_backward_full_size_sampled_heads(dev, name):
     """The B=8, T=4096, H=16, d=128 workloads (the diagonal one in the launch
