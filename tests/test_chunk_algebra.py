@@ -20,7 +20,9 @@ recurrence from that chunk on.  These tests model exactly that, in fp64 (the
 algebra is an identity) and in fp32 with bf16 matrix operands (the ranges),
 and compare with the fp64 oracle.  They also show that the chunk-start
 reference (Kh = p_hat k / g_t over all 32 tokens) overflows fp32 where the
-midpoint reference does not.
+midpoint reference does not.  The last tests model the chunked backward: the
+transpose of the same chunk form, converted to the token recurrence's gain
+gradient and fed to its uncertainty adjoint, against oracle.backward.
 """
 from __future__ import annotations
 
@@ -272,3 +274,144 @@ def test_iso_gram_form_in_fp32_with_bf16_operands(alpha_loc):
     assert np.isfinite(big) and big < 2.0 ** 100
     ro, rS, rp = _iso_ref(x, mu)
     assert _rel(o, ro) < 2e-2 and _rel(S, rS) < 2e-2 and abs(p - rp) < 1e-6 * abs(rp)
+
+
+# ---------------------------------------------------------------------------
+# The chunked backward (kdn_backward_chunk.hip): the transpose of the
+# midpoint-frame chunk form above, per chunk in reverse, then the token
+# recurrence's uncertainty adjoint fed with the gradient of the normalised
+# gain.  fp64, against oracle.backward (which is pinned by finite differences).
+# ---------------------------------------------------------------------------
+
+
+def chunk_backward_model(q, k, v, alpha, omega, r, mu, dO, dS_T, S0, p0):
+    """One (batch, head) pair.  Returns the memory part's per-token sums in the
+    token form (dq, dkap = gradient of kappa = kappa' / d, dk_mem, dalpha_mem),
+    p_{t-1}, dv and dS0."""
+    T, dk = k.shape
+    dv = v.shape[1]
+    nch = (T + L - 1) // L
+
+    def chunk(c, S, p):
+        t0, t1 = c * L, min(T, (c + 1) * L)
+        n = t1 - t0
+        pad = lambda x, fill, w: np.concatenate([x[t0:t1], np.full((L - n, w), fill)]) if n < L else x[t0:t1]
+        a, kk, qq = pad(alpha, 1.0, dk), pad(k, 0.0, dk), pad(q, 0.0, dk)
+        ww, vv = pad(omega, 0.0, dk), pad(v, 0.0, dv)
+        rr = np.concatenate([r[t0:t1], np.ones(L - n)])
+        ph, pprev = np.zeros((L, dk)), np.zeros((L, dk))
+        for j in range(L):
+            pprev[j] = p
+            ph[j] = a[j] ** 2 * p + ww[j]
+            p = ph[j] / (1.0 + (mu / rr[j]) * kk[j] ** 2 * ph[j])
+        g, gb = np.cumprod(a[:16], axis=0), np.cumprod(a[16:], axis=0)
+        g15, gb31 = g[15], gb[-1]
+        rho = np.concatenate([g / g15, gb])
+        kap = ph * kk
+        Kt, Qt, Kh = kk * rho, qq * rho, kap / rho
+        Sg = g15[:, None] * S
+        M = np.diag(rr) + np.tril(Kt @ Kh.T)
+        Dn = np.linalg.solve(M, vv - Kt @ Sg)
+        X = Sg + Kh.T @ Dn
+        f = dict(n=n, t0=t0, a=a, kk=kk, qq=qq, pprev=pprev, g15=g15, gb31=gb31, rho=rho, kap=kap, Kt=Kt, Qt=Qt,
+                 Kh=Kh, Sg=Sg, M=M, Dn=Dn, QK=np.tril(Qt @ Kh.T), X=X, S=S)
+        return f, gb31[:, None] * X, p
+
+    Sc, pc = [], []
+    S, p = S0.copy(), p0.copy()
+    for c in range(nch):
+        Sc.append(S)
+        pc.append(p)
+        _, S, p = chunk(c, S, p)
+    out = {n: np.zeros((T, dk)) for n in ("dq", "dkap", "dkm", "dam", "pp")}
+    out["dv"] = np.zeros((T, dv))
+    dS = dS_T.copy()
+    for c in reversed(range(nch)):
+        f, _, _ = chunk(c, Sc[c], pc[c])
+        n, t0 = f["n"], f["t0"]
+        dOc = np.zeros((L, dv))
+        dOc[:n] = dO[t0:t0 + n]
+        dX = f["gb31"][:, None] * dS
+        dgb31 = np.sum(dS * f["X"], axis=1)
+        dDn = f["QK"].T @ dOc + f["Kh"] @ dX
+        dR = np.linalg.solve(f["M"].T, dDn)
+        dSg = f["Qt"].T @ dOc + dX - f["Kt"].T @ dR
+        dM = np.tril(-dR @ f["Dn"].T)
+        dQK = np.tril(dOc @ f["Dn"].T)
+        dQt = dOc @ f["Sg"].T + dQK @ f["Kh"]
+        dKt = -dR @ f["Sg"].T + dM @ f["Kh"]
+        dKh = dQK.T @ f["Qt"] + dM.T @ f["Kt"] + f["Dn"] @ dX.T
+        dg15 = np.sum(dSg * f["S"], axis=1)
+        dS = f["g15"][:, None] * dSg
+        rho, kap = f["rho"], f["kap"]
+        dq, dkc, dkapc = dQt * rho, dKt * rho, dKh / rho
+        w = dkc * f["kk"] + dq * f["qq"] - dkapc * kap  # d rho . rho
+        ad = np.zeros((L, dk))
+        for u in range(16):
+            ad[u] = -np.sum(w[:u], axis=0) + dg15 * f["g15"]
+        for u in range(16, L):
+            ad[u] = np.sum(w[u:], axis=0) + dgb31 * f["gb31"]
+        d, dr = np.diag(f["M"]), np.diag(dM)
+        sl = slice(t0, t0 + n)
+        out["dq"][sl] = dq[:n]
+        out["dkap"][sl] = (d[:, None] * (dkapc - f["kk"] * dr[:, None]))[:n]
+        out["dkm"][sl] = (dkc - kap * dr[:, None])[:n]
+        out["dam"][sl] = (ad / f["a"])[:n]
+        out["pp"][sl] = f["pprev"][:n]
+        out["dv"][sl] = dR[:n]
+    out["dS0"] = dS
+    return out
+
+
+def uncertainty_backward_model(k, alpha, omega, r, mu, m, dp_T):
+    """The token recurrence's uncertainty adjoint, backwards over the tokens,
+    given the memory part's sums m.  Returns dk, dalpha, domega, dr, dp0."""
+    T, dk = k.shape
+    dp = dp_T.copy()
+    dk_o, da_o, dw_o, dr_o = np.zeros((T, dk)), np.zeros((T, dk)), np.zeros((T, dk)), np.zeros(T)
+    for t in reversed(range(T)):
+        pp, a, kk = m["pp"][t], alpha[t], k[t]
+        ph = a * a * pp + omega[t]
+        d = r[t] + np.sum(ph * kk * kk)
+        dkap = m["dkap"][t]
+        dd = -np.sum(dkap * ph * kk) / d ** 2  # gain denominator
+        c = mu / r[t]
+        den = 1 + c * kk * kk * ph
+        dph = dkap * kk / d + dd * kk * kk + dp / den ** 2
+        dkk = dkap * ph / d + dd * 2 * ph * kk + dp * (-2 * c * kk * ph ** 2 / den ** 2)
+        dr_o[t] = dd + np.sum(dp * (-kk * kk * ph ** 2 / den ** 2)) * (-mu / r[t] ** 2)
+        da_o[t] = m["dam"][t] + dph * 2 * a * pp
+        dw_o[t] = dph
+        dk_o[t] = m["dkm"][t] + dkk
+        dp = dph * a * a
+    return dk_o, da_o, dw_o, dr_o, dp
+
+
+@pytest.mark.parametrize("T,alpha_loc", [(1, 2.0), (31, 2.0), (32, 2.0), (45, 2.0), (100, 2.0), (77, 0.0),
+                                         (77, -3.0)])
+def test_chunk_backward_is_the_adjoint(T, alpha_loc):
+    # fp64: the chunk form's transpose, converted to the token form's gain
+    # gradient (d kappa = d (d kappa' - k dr), dk_mem = dk - kappa' dr) and
+    # fed to the uncertainty adjoint, gives the oracle's gradients
+    dk, dv = 16, 8
+    w = wl.Workload("bwd_model", "diagonal", "bf16", 1, T, 1, dk, dv, float(dk), "one", 300 + T,
+                    alpha_loc=alpha_loc, omega_loc=-2.0)
+    x = wl.forward_inputs(w)
+    rng = np.random.default_rng(301 + T)
+    dO = rng.standard_normal((1, T, 1, dv))
+    dS_T = rng.standard_normal((1, 1, dk, dv))
+    dp_T = rng.standard_normal((1, 1, dk))
+    S0 = rng.standard_normal((1, 1, dk, dv)) * 0.3
+    p0 = rng.uniform(0.5, 2.0, (1, 1, dk))
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], x["c0"], w.mu, dO=dO, dS_T=dS_T,
+                          dp_T=dp_T, S0=S0, p0=p0)
+    g = {n: x[n][0, :, 0].astype(np.float64) for n in ("q", "k", "v", "alpha", "omega")}
+    rr = x["r"][0, :, 0].astype(np.float64)
+    m = chunk_backward_model(g["q"], g["k"], g["v"], g["alpha"], g["omega"], rr, w.mu, dO[0, :, 0], dS_T[0, 0],
+                             S0[0, 0], p0[0, 0])
+    dkk, da, dw, dr, dp0 = uncertainty_backward_model(g["k"], g["alpha"], g["omega"], rr, w.mu, m, dp_T[0, 0])
+    got = {"dq": m["dq"], "dk": dkk, "dv": m["dv"], "dalpha": da, "domega": dw, "dr": dr, "dS0": m["dS0"],
+           "dp0": dp0}
+    for name, val in got.items():
+        want = ref[name][0, :, 0] if name not in ("dS0", "dp0") else ref[name][0, 0]
+        assert _rel(val, want) < 1e-11, name
