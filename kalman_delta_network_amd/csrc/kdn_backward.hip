@@ -963,21 +963,25 @@ size_t flag_offset(int B, int T, int H, int dk, int dv) {
 // per (batch, head) pair), the chunked adjoint of the unflagged pairs, the
 // recurrent memory adjoint of the flagged ones, then the uncertainty adjoint
 // of all.  Both memory adjoints leave the same per-token tile sums.
+// fb: the arguments the token path takes for flagged pairs (a itself, or
+// for the gated layer its fp32 copies of the gated values)
 template <int DK, int DV>
-hipError_t launch_chunked_path(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_chunked_path(const BwdArgs& a, const BwdArgs& fb, hipStream_t s) {
     const size_t uf = unit_floats(a.T, DK, TILE);
     int* flag = reinterpret_cast<int*>(a.work + flag_offset(a.B, a.T, a.H, DK, DV));
-    const FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, DK, DV,
-                    a.S0, a.p0, nullptr, nullptr, nullptr};
+    FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, DK, DV,
+              a.S0, a.p0, nullptr, nullptr, nullptr};
+    f.gates = a.gates;
     hipError_t e = launch_chunked_checkpoints(f, a.work, uf, flag, s);
     if (e != hipSuccess) return e;
     e = launch_backward_chunk(a, uf, flag, s);
     if (e != hipSuccess) return e;
     e = launch_backward_unc_chunk(a, uf, flag, s);
     if (e != hipSuccess) return e;
-    BwdArgs r = a;
+    BwdArgs r = fb;
     r.only_flagged = flag;
-    return launch_t<DK, DV, 0, bf16_t>(r, s);
+    r.gates = false;
+    return fb.dtype == 1 ? launch_t<DK, DV, 0, bf16_t>(r, s) : launch_t<DK, DV, 0, float>(r, s);
 }
 
 bool chunk_path(const BwdArgs& a) {
@@ -993,7 +997,7 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
     if (a.variant == 3)  // diagonal with grouped observation noise
         return a.dtype == 1 ? launch_grouped_t<DK, DV, bf16_t>(a, s) : launch_grouped_t<DK, DV, float>(a, s);
     if (a.variant == 2) return launch_dtype<DK, DV, 2>(a, s);
-    if (chunk_path(a)) return launch_chunked_path<DK, DV>(a, s);
+    if (chunk_path(a)) return launch_chunked_path<DK, DV>(a, a, s);
     return a.variant == 1 ? launch_dtype<DK, DV, 1>(a, s) : launch_dtype<DK, DV, 0>(a, s);
 }
 
@@ -1003,6 +1007,22 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (long(B) * H == 0 || T == 0) return 0;
     // then one range flag per (batch, head) pair for the chunked path
     return flag_offset(B, T, H, dk, dv) * sizeof(float) + size_t(B) * size_t(H) * sizeof(int);
+}
+
+bool backward_chunked_eligible(const BwdArgs& a) {
+    return (a.dk == 128 || a.dk == 64) && (a.dv == 128 || a.dv == 64) && chunk_path(a);
+}
+
+hipError_t launch_backward_chunked(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream) {
+    hipError_t e;
+    if (a.dk == 128 && a.dv == 128) e = launch_chunked_path<128, 128>(a, fallback, stream);
+    else if (a.dk == 128 && a.dv == 64) e = launch_chunked_path<128, 64>(a, fallback, stream);
+    else if (a.dk == 64 && a.dv == 128) e = launch_chunked_path<64, 128>(a, fallback, stream);
+    else if (a.dk == 64 && a.dv == 64) e = launch_chunked_path<64, 64>(a, fallback, stream);
+    else return hipErrorNotSupported;
+    if (e != hipSuccess || !a.dc0) return e;
+    hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned(a.H)), dim3(64), 0, stream, a.dp0, a.dc0, a.B, a.H, a.dk);
+    return hipGetLastError();
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {

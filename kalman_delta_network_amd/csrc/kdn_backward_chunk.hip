@@ -38,6 +38,7 @@
 // layout.  Matrix operands whose contraction index runs along the stored
 // rows are gathered from LDS (4 or 8 two-byte reads per lane).
 #include "kdn_device.h"
+#include "kdn_gates.h"
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -90,6 +91,9 @@ struct CSmem {
     float GA[DK], GB[DK];  // g_15 and gb_31
     float dGA[DK], dGB[DK];
     float spart[L][DK / 64];  // sum_i p_hat k^2 over each wave's 64 channels (fp32)
+    float nk[L][DK / 64];     // gated: |k_t|^2 and |q_t|^2 over each wave's 64 channels
+    float nq[L][DK / 64];
+    float skv[L], sqv[L];     // gated: 1 / |k_t| and 1 / |q_t|
     float uacc[DK / 16][L];   // sum_i d kappa kappa' over each key tile's 16 channels
 };
 
@@ -184,7 +188,10 @@ struct Pre {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int DK>
+// GATE: the gated layer's values from raw inputs, as the gated forward forms
+// them (alpha = sigmoid(z), omega = softplus(z), r = r_min + softplus(z), q
+// and k divided by their norms over the d_k channels)
+template <int DK, bool GATE>
 __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
     constexpr int NT = DK / 16;     // 16-row tiles of the key dimension (state waves)
     constexpr int NCW = DK / 64;    // chain waves
@@ -293,7 +300,9 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 }
             }
             if (tid < L) {
-                const float rt = tid < nvalid ? bf1(pre.r) : 1.f;
+                float rz = bf1(pre.r);
+                if (GATE) rz = kGateRMin + gate_softplus(rz);
+                const float rt = tid < nvalid ? rz : 1.f;
                 sm.r[tid] = rt;
                 sm.cr[tid] = mu / rt;
             }
@@ -302,6 +311,42 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
         }
         bar();
         if (c > 0) load(c - 1);  // the next chunk's inputs, in flight during this one
+        if constexpr (GATE) {
+            // |k_t|^2 and |q_t|^2, a wave covering 64 channels of one token per step
+#pragma unroll 1
+            for (int j = 0; j < L * DK / NTH; ++j) {
+                const int e = threadIdx.x + NTH * j;
+                const int t = e / DK, i = e % DK;
+                const float xk = bf1(sm.K[e]), xq = bf1(sm.Q[e]);
+                float a = xk * xk, b2 = xq * xq;
+                a = sum16(a);
+                a = halve16(a, a);
+                a = halve32(a, a);
+                b2 = sum16(b2);
+                b2 = halve16(b2, b2);
+                b2 = halve32(b2, b2);
+                if (lane == 0) {
+                    sm.nk[t][i / 64] = a;
+                    sm.nq[t][i / 64] = b2;
+                }
+            }
+            bar();
+        }
+        // gated: the prologue's 1 / |k_t| and 1 / |q_t|; otherwise 1
+        const auto kscale = [&](int t) {
+            if constexpr (!GATE) return 1.f;
+            float a = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < DK / 64; ++w2) a += sm.nk[t][w2];
+            return inv_norm(a);
+        };
+        const auto qscale = [&](int t) {
+            if constexpr (!GATE) return 1.f;
+            float a = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < DK / 64; ++w2) a += sm.nq[t][w2];
+            return inv_norm(a);
+        };
         // ---- chain: uncertainty recurrence, decays, the chunk's operands ----
         // (MASK: a tail chunk; padding tokens take alpha = 1, k = q = omega = 0)
         const auto chain = [&](auto maskc) {
@@ -314,7 +359,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 float a16[HL];
 #pragma unroll
                 for (int t = 0; t < HL; ++t) {
-                    const float x = bf1(sm.A[t * DK + i]);
+                    float x = bf1(sm.A[t * DK + i]);
+                    if (GATE) x = gate_sigmoid(x);
                     a16[t] = (!MASK || t < nvalid) ? x : 1.f;
                 }
                 hr[HL - 1] = 1.f;
@@ -336,8 +382,13 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 for (int j = 0; j < 8; ++j) {
                     const int t = 8 * b8i + j;
                     const bool ok = !MASK || t < nvalid;
-                    const float xa = bf1(sm.A[t * DK + i]), xk = bf1(sm.K[t * DK + i]);
-                    const float xw = bf1(sm.W[t * DK + i]);
+                    float xa = bf1(sm.A[t * DK + i]), xk = bf1(sm.K[t * DK + i]);
+                    float xw = bf1(sm.W[t * DK + i]);
+                    if (GATE) {
+                        xa = gate_sigmoid(xa);
+                        xw = gate_softplus(xw);
+                        xk *= kscale(t);
+                    }
                     al[j] = ok ? xa : 1.f;
                     kk[j] = ok ? xk : 0.f;
                     w[j] = ok ? xw : 0.f;
@@ -374,6 +425,9 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
         if (wave < NCW) {
             if (nvalid == L) chain(std::false_type{});
             else chain(std::true_type{});
+        } else if (GATE && wave == NCW && lane < L) {
+            sm.skv[lane] = kscale(lane);
+            sm.sqv[lane] = qscale(lane);
         }
         bar();
         // the chunk's operands from p_hat and rho (every wave): kappa' =
@@ -385,7 +439,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
             const int e = threadIdx.x + NTH * j;
             const int t = e / DK, i = e % DK;
             const bool ok = t < nvalid;
-            const float xk = bf1(sm.K[e]), xq = bf1(sm.Q[e]);
+            const float xk = bf1(sm.K[e]) * (GATE ? sm.skv[t] : 1.f), xq = bf1(sm.Q[e]) * (GATE ? sm.sqv[t] : 1.f);
             const float kk = ok ? xk : 0.f, qq = ok ? xq : 0.f;
             const float rh = sm.rho[e];
             const float kap = sm.kap[e] * kk;
@@ -594,7 +648,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 for (int e = 0; e < 4; ++e) {
                     const int tl = th + g4 + e;
                     const float rh = sm.rho[tl * DK + i], kp = sm.kap[tl * DK + i];
-                    const float kk = bf1(sm.K[tl * DK + i]), qq = bf1(sm.Q[tl * DK + i]);
+                    const float kk = bf1(sm.K[tl * DK + i]) * (GATE ? sm.skv[tl] : 1.f);
+                    const float qq = bf1(sm.Q[tl * DK + i]) * (GATE ? sm.sqv[tl] : 1.f);
                     const float dq = dqt[e] * rh, dkc = dkt[e] * rh, dkapc = dkh[e] * __builtin_amdgcn_rcpf(rh);
                     const float drt = sm.dr[tl], dt = sm.d[tl];
                     const float dkap = dt * fmaf(-kk, drt, dkapc);
@@ -629,6 +684,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 #pragma unroll
                     for (int w2 = 0; w2 < DK / 64; ++w2) sk += sm.spart[th + lane][w2];
                     slot[L + th + lane] = sk;
+                    if (GATE) slot[5 * L + th + lane] = sm.skv[th + lane];  // 1 / |k_t|
                 }
             }
             if (half == 1) {
@@ -658,7 +714,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 for (int j = 0; j < HL; ++j) {
                     const int u = HL * hf + j;
                     wv[j] = sm.kap[u * DK + i];
-                    const float x = bf1(sm.A[u * DK + i]);
+                    float x = bf1(sm.A[u * DK + i]);
+                    if (GATE) x = gate_sigmoid(x);
                     av[j] = (!MASK || u < nvalid) ? x : 1.f;
                 }
                 float acc = 0.f;
@@ -714,7 +771,8 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 // segment from its exact entering dp (the later segments' maps applied to
 // dp_T in order) and writes the gradients.
 // Slot of chunk c (tile 0 unless noted): [t] u of each tile (its own slot),
-// [L + t] d, [2L + t] dd, [3L + 32 w + t] wave w's share of dr, and in the
+// [L + t] d, [2L + t] dd, [3L + 32 w + t] wave w's share of dr, (gated)
+// [5L + t] 1 / |k_t|, and in the
 // slot of a segment's first chunk [MAPOFF + 2 i], [MAPOFF + 2 i + 1] the
 // segment's map of channel i.
 // ---------------------------------------------------------------------------
@@ -725,11 +783,11 @@ constexpr int MAPOFF = 256;
 struct UncTok {
     float q[2], k[2], ks[2], a[2];  // the tiles' (at most 2) partial sums
     float u[2];
-    float d, pp;
+    float d, pp, sk;  // sk (gated): 1 / |k_t|
     bf16_t al, kk, w, r;
 };
 
-template <int DK, bool MAPS>
+template <int DK, bool MAPS, bool GATE>
 __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
     constexpr int NWV = DK / 64;
     const int nunit = A.B * A.H;
@@ -772,6 +830,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
             x.u[tile] = slot(tc, t)[tl];
         }
         x.d = slot(0, t)[L + tl];
+        if (GATE) x.sk = slot(0, t)[5 * L + tl];
         x.pp = pbuf[(size_t(unit) * T + t) * ntile * DK + i];
         x.al = ain[tok * DK + i];
         x.kk = kin[tok * DK + i];
@@ -793,7 +852,14 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         const bool two = ntile > 1;
         const float gk = x.k[0] + (two ? x.k[1] : 0.f);
         const float u = x.u[0] + (two ? x.u[1] : 0.f);
-        const float al = bf1(x.al), kk = bf1(x.kk), w = bf1(x.w), rt = bf1(x.r);
+        float al = bf1(x.al), kk = bf1(x.kk), w = bf1(x.w), rt = bf1(x.r);
+        if (GATE) {
+            // the gated layer's values (as the gated forward forms them)
+            al = gate_sigmoid(al);
+            w = gate_softplus(w);
+            rt = kGateRMin + gate_softplus(rt);
+            kk *= x.sk;
+        }
         const size_t tok = tokidx(t);
         const float ph = al * al * x.pp + w;
         const float inv = 1.0f / x.d;
@@ -863,23 +929,22 @@ __global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, size_t 
     (void)nunit;
 }
 
-}  // namespace
-
-hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+template <bool GATE>
+hipError_t launch_unc_chunk_t(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
     const unsigned units = unsigned(long(a.B) * a.H);
     const unsigned nseg = unsigned((a.T + SEGU - 1) / SEGU);
     const dim3 dgrid(unsigned((a.T + 255) / 256), units);
     if (a.dk == 128) {
         const dim3 grid(units * 2 * nseg);
         if (nseg > 1)
-            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, true>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, false>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
         hipLaunchKernelGGL(kdn_backward_dr_kernel<128>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
     } else if (a.dk == 64) {
         const dim3 grid(units * nseg);
         if (nseg > 1)
-            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, true>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, false>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
         hipLaunchKernelGGL(kdn_backward_dr_kernel<64>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
     } else {
         return hipErrorNotSupported;
@@ -887,16 +952,28 @@ hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const i
     return hipGetLastError();
 }
 
-hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+template <bool GATE>
+hipError_t launch_chunk_t(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
     const unsigned units = unsigned(long(a.B) * a.H);
     const unsigned grid = units * unsigned(a.dv / TILE);
     if (a.dk == 128)
-        hipLaunchKernelGGL(kdn_backward_chunk_kernel<128>, dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_chunk_kernel<128, GATE>), dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
     else if (a.dk == 64)
-        hipLaunchKernelGGL(kdn_backward_chunk_kernel<64>, dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_chunk_kernel<64, GATE>), dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
     else
         return hipErrorNotSupported;
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+    return a.gates ? launch_unc_chunk_t<true>(a, ck_floats, flag, stream)
+                   : launch_unc_chunk_t<false>(a, ck_floats, flag, stream);
+}
+
+hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+    return a.gates ? launch_chunk_t<true>(a, ck_floats, flag, stream) : launch_chunk_t<false>(a, ck_floats, flag, stream);
 }
 
 }  // namespace kdn

@@ -1132,7 +1132,7 @@ template <int DK, int VAR, bool GR = false, int NCT = 2, bool GATE = false, bool
 __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
     constexpr bool ISO = VAR != 0;  // one uncertainty scalar per head
     static_assert(!GATE || !GR, "no gate step with grouped observation noise");
-    static_assert(!STORE || (VAR == 0 && !GR && NCT == 2 && !GATE), "checkpoints: diagonal, 64-column tiles");
+    static_assert(!STORE || (VAR == 0 && !GR && NCT == 2), "checkpoints: diagonal, 64-column tiles");
     static_assert(!GR || VAR == 0, "grouped noise is a diagonal form");
     static_assert(!GR || NCT == 2, "a noise group is one 64-column tile");
     constexpr int DVTN = dvt_of<NCT>();  // value columns of this workgroup
@@ -1678,8 +1678,9 @@ hipError_t launch_segments_t(const FwdArgs& f, int seg, int nseg, const float* m
     return hipGetLastError();
 }
 
-// Checkpoint sweep of the chunked backward (diagonal, bf16, 64-column tiles).
-template <int DK>
+// Checkpoint sweep of the chunked backward (diagonal, bf16, 64-column tiles;
+// GATE: the gated forward's values).
+template <int DK, bool GATE>
 hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, int* ck_flag, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0 || f.T == 0) return hipSuccess;
@@ -1710,7 +1711,7 @@ hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, i
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
     const unsigned grid = unsigned(groups) * 8u * unsigned(ntile);
-    hipLaunchKernelGGL((kdn_chunk_kernel<DK, 0, false, 2, false, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((kdn_chunk_kernel<DK, 0, false, 2, GATE, true>), dim3(grid), dim3(NTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1718,9 +1719,12 @@ hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, i
 
 hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,
                                       hipStream_t stream) {
-    if (!chunked_supports(a) || a.variant != 0 || a.gates || a.cu_seqlens) return hipErrorNotSupported;
-    return a.dk == 128 ? launch_checkpoints_t<128>(a, ck, ck_floats, ck_flag, stream)
-                       : launch_checkpoints_t<64>(a, ck, ck_floats, ck_flag, stream);
+    if (!chunked_supports(a) || a.variant != 0 || a.cu_seqlens) return hipErrorNotSupported;
+    if (a.gates)
+        return a.dk == 128 ? launch_checkpoints_t<128, true>(a, ck, ck_floats, ck_flag, stream)
+                           : launch_checkpoints_t<64, true>(a, ck, ck_floats, ck_flag, stream);
+    return a.dk == 128 ? launch_checkpoints_t<128, false>(a, ck, ck_floats, ck_flag, stream)
+                       : launch_checkpoints_t<64, false>(a, ck, ck_floats, ck_flag, stream);
 }
 
 // Compute units of the current device (read once per device and cached; 256

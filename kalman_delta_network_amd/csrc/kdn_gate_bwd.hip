@@ -167,8 +167,14 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     f.omega = fw;
     f.r = fr;
     f.dO = a.dO ? fdo : nullptr;
-    f.dtype = 0;  // the adjoint runs on the fp32 copies
-    e = launch_backward(f, s);
+    f.dtype = 0;  // the token path runs on the fp32 copies
+    // The diagonal bf16 form takes the chunked path on the raw inputs (its
+    // kernels form the gated values as the gated forward does); the copies
+    // serve the pairs outside its range.
+    BwdArgs c = a;
+    c.gates = true;
+    if (backward_chunked_eligible(c)) e = launch_backward_chunked(c, f, s);
+    else e = launch_backward(f, s);
     if (e != hipSuccess) return e;
     const auto grad = [&](const void* z, float* d, size_t count, int op) {
         if (count == 0) return;

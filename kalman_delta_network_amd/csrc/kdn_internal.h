@@ -75,11 +75,19 @@ struct BwdArgs {
     // the recurrent memory adjoint must take (their decays leave the chunked
     // form's range); the recurrent memory kernel then skips every other pair
     const int* only_flagged = nullptr;
+    // chunked path only: alpha, omega, r hold the gate pre-activations and q,
+    // k are raw (the kernels form the gated layer's values themselves)
+    bool gates = false;
 };
 
 // Bytes of device workspace one backward call needs (0 for an empty call).
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// The chunked path on its own (diagonal bf16 form; with a.gates the gated
+// layer on raw q, k and pre-activations): the chunked adjoint for every pair
+// in range, the token path with `fallback`'s arguments for the others, dc0.
+bool backward_chunked_eligible(const BwdArgs& a);
+hipError_t launch_backward_chunked(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream);
 // Backward of the gated layer: a.alpha, a.omega, a.r hold the gate
 // pre-activations and d alpha, d omega, d r come out as their gradients.
 // a.work holds backward_gated_workspace_bytes() bytes (the adjoint's

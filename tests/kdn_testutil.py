@@ -85,3 +85,17 @@ def sample_pairs(B: int, H: int, n: int, seed: int = 0):
     idx = rng.choice(len(allp), size=min(n, len(allp)), replace=False)
     picked = {allp[i] for i in idx} | {(0, 0), (B - 1, H - 1)}
     return sorted(picked)
+
+
+def check_dc0(dc0, dp0):
+    """dc0 is the sum of dp0 over the batch and every axis after the head
+    axis (the c0 gradient when p0 is not given): compare the kernel's dc0 with
+    the kernel's own dp0 summed in fp64, relative to the sum of magnitudes (a
+    sum's rounding and inherited errors scale with sum |terms|, not with
+    |sum|).  dp0 itself is compared with the oracle elsewhere."""
+    dp0 = np.asarray(dp0, np.float64)
+    axes = (0,) + tuple(range(2, dp0.ndim))
+    want = dp0.sum(axis=axes)
+    scale = np.abs(dp0).sum(axis=axes)
+    err = np.abs(np.asarray(dc0, np.float64) - want)
+    assert np.all(err <= 1e-5 * np.maximum(scale, 1e-30)), (err, scale)
