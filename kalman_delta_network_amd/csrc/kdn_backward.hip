@@ -963,25 +963,37 @@ size_t flag_offset(int B, int T, int H, int dk, int dv) {
 // per (batch, head) pair), the chunked adjoint of the unflagged pairs, the
 // recurrent memory adjoint of the flagged ones, then the uncertainty adjoint
 // of all.  Both memory adjoints leave the same per-token tile sums.
-// fb: the arguments the token path takes for flagged pairs (a itself, or
-// for the gated layer its fp32 copies of the gated values)
-template <int DK, int DV>
-hipError_t launch_chunked_path(const BwdArgs& a, const BwdArgs& fb, hipStream_t s) {
-    const size_t uf = unit_floats(a.T, DK, TILE);
-    int* flag = reinterpret_cast<int*>(a.work + flag_offset(a.B, a.T, a.H, DK, DV));
-    FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, DK, DV,
+// The chunked path in two parts.  main: the checkpoint sweep (which flags the
+// pairs outside the chunked range) and the chunked adjoints of the others.
+// fallback: the token path with fb's arguments for the flagged pairs (fb is a
+// itself, or for the gated layer its fp32 copies of the gated values).
+int* chunk_flags(const BwdArgs& a) { return reinterpret_cast<int*>(a.work + flag_offset(a.B, a.T, a.H, a.dk, a.dv)); }
+
+hipError_t chunked_main(const BwdArgs& a, hipStream_t s) {
+    const size_t uf = unit_floats(a.T, a.dk, TILE);
+    int* flag = chunk_flags(a);
+    FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, a.dk, a.dv,
               a.S0, a.p0, nullptr, nullptr, nullptr};
     f.gates = a.gates;
     hipError_t e = launch_chunked_checkpoints(f, a.work, uf, flag, s);
     if (e != hipSuccess) return e;
     e = launch_backward_chunk(a, uf, flag, s);
     if (e != hipSuccess) return e;
-    e = launch_backward_unc_chunk(a, uf, flag, s);
-    if (e != hipSuccess) return e;
+    return launch_backward_unc_chunk(a, uf, flag, s);
+}
+
+template <int DK, int DV>
+hipError_t chunked_fallback(const BwdArgs& a, const BwdArgs& fb, hipStream_t s) {
     BwdArgs r = fb;
-    r.only_flagged = flag;
+    r.only_flagged = chunk_flags(a);
     r.gates = false;
     return fb.dtype == 1 ? launch_t<DK, DV, 0, bf16_t>(r, s) : launch_t<DK, DV, 0, float>(r, s);
+}
+
+template <int DK, int DV>
+hipError_t launch_chunked_path(const BwdArgs& a, const BwdArgs& fb, hipStream_t s) {
+    const hipError_t e = chunked_main(a, s);
+    return e != hipSuccess ? e : chunked_fallback<DK, DV>(a, fb, s);
 }
 
 bool chunk_path(const BwdArgs& a) {
@@ -1013,12 +1025,16 @@ bool backward_chunked_eligible(const BwdArgs& a) {
     return (a.dk == 128 || a.dk == 64) && (a.dv == 128 || a.dv == 64) && chunk_path(a);
 }
 
-hipError_t launch_backward_chunked(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream) {
+int* backward_chunk_flags(const BwdArgs& a) { return chunk_flags(a); }
+
+hipError_t launch_backward_chunked_main(const BwdArgs& a, hipStream_t stream) { return chunked_main(a, stream); }
+
+hipError_t launch_backward_chunked_fallback(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream) {
     hipError_t e;
-    if (a.dk == 128 && a.dv == 128) e = launch_chunked_path<128, 128>(a, fallback, stream);
-    else if (a.dk == 128 && a.dv == 64) e = launch_chunked_path<128, 64>(a, fallback, stream);
-    else if (a.dk == 64 && a.dv == 128) e = launch_chunked_path<64, 128>(a, fallback, stream);
-    else if (a.dk == 64 && a.dv == 64) e = launch_chunked_path<64, 64>(a, fallback, stream);
+    if (a.dk == 128 && a.dv == 128) e = chunked_fallback<128, 128>(a, fallback, stream);
+    else if (a.dk == 128 && a.dv == 64) e = chunked_fallback<128, 64>(a, fallback, stream);
+    else if (a.dk == 64 && a.dv == 128) e = chunked_fallback<64, 128>(a, fallback, stream);
+    else if (a.dk == 64 && a.dv == 64) e = chunked_fallback<64, 64>(a, fallback, stream);
     else return hipErrorNotSupported;
     if (e != hipSuccess || !a.dc0) return e;
     hipLaunchKernelGGL(kdn_dc0_kernel, dim3(unsigned(a.H)), dim3(64), 0, stream, a.dp0, a.dc0, a.B, a.H, a.dk);

@@ -32,12 +32,39 @@ enum GateOp { kCopy = 0, kSigmoid = 1, kSoftplus = 2, kRSoftplus = 3 };
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
+// Only the (batch, head) pairs flagged in `only` (when given) need the fp32
+// copies: element i of a [B, T, H, width] array belongs to pair
+// (i / width / (T H)) H + (i / width) % H.
+struct PairFilter {
+    const int* only;
+    size_t TH;
+    int H, width, units;
+    __device__ __forceinline__ bool skip(size_t i) const {
+        if (!only) return false;
+        const size_t row = i / size_t(width);
+        return !only[(row / TH) * size_t(H) + row % size_t(H)];
+    }
+    // no pair flagged (the usual case): the whole workgroup has nothing to do
+    __device__ __forceinline__ bool none() const {
+        if (!only) return false;
+        __shared__ int any;
+        if (threadIdx.x == 0) any = 0;
+        __syncthreads();
+        for (int u = threadIdx.x; u < units; u += blockDim.x)
+            if (only[u]) any = 1;
+        __syncthreads();
+        return any == 0;
+    }
+};
+
 // y[i] = op(x[i]) in fp32
 template <typename Tin>
 __global__ void __launch_bounds__(256) gate_forward_kernel(const Tin* __restrict__ x, float* __restrict__ y,
-                                                           size_t n, int op) {
+                                                           size_t n, int op, PairFilter pf) {
+    if (pf.none()) return;
     const size_t stride = size_t(gridDim.x) * blockDim.x;
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        if (pf.skip(i)) continue;
         const float z = widen(x[i]);
         float out = z;
         if (op == kSigmoid) out = gate_sigmoid(z);
@@ -78,10 +105,12 @@ __device__ __forceinline__ float row_sumsq(const Tin* __restrict__ x, size_t row
 // y = x / max(|x|, eps) per row of dk channels (one wave per row)
 template <typename Tin>
 __global__ void __launch_bounds__(256) row_normalize_kernel(const Tin* __restrict__ x, float* __restrict__ y,
-                                                            size_t rows, int dk) {
+                                                            size_t rows, int dk, PairFilter pf) {
+    if (pf.none()) return;
     const int lane = threadIdx.x & 63;
     const size_t waves = size_t(gridDim.x) * (blockDim.x / 64);
     for (size_t row = size_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); row < rows; row += waves) {
+        if (pf.skip(row)) continue;  // (width 1: one row per token-head)
         const float inv = inv_norm(row_sumsq(x, row, dk));
         for (int i = lane; i < dk; i += 64) y[row * dk + i] = widen(x[row * dk + i]) * inv;
     }
@@ -138,26 +167,43 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     float* fw = take(n.nw);
     float* fr = take(n.nr);
     float* fdo = take(n.nv);
-    const auto fwd = [&](const void* x, float* y, size_t count, int op) {
+    // The diagonal bf16 form takes the chunked path on the raw inputs (its
+    // kernels form the gated values as the gated forward does); the fp32
+    // copies then serve only the pairs outside its range, which its
+    // checkpoint sweep flags.
+    BwdArgs c = a;
+    c.gates = true;
+    const bool chunked = backward_chunked_eligible(c);
+    hipError_t e = hipSuccess;
+    PairFilter pf{nullptr, size_t(a.T) * size_t(a.H), a.H, 1, a.B * a.H};
+    if (chunked) {
+        e = launch_backward_chunked_main(c, s);
+        if (e != hipSuccess) return e;
+        pf.only = backward_chunk_flags(c);
+    }
+    const auto fwd = [&](const void* x, float* y, size_t count, int op, int width) {
         if (count == 0) return;
         const unsigned blocks = unsigned(count / 256 + 1 < 8192 ? count / 256 + 1 : 8192);
+        PairFilter f = pf;
+        f.width = width;
         hipLaunchKernelGGL(gate_forward_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(x), y,
-                           count, op);
+                           count, op, f);
     };
     const size_t rows = size_t(a.B) * size_t(a.T) * size_t(a.H);
     const unsigned row_blocks = unsigned(rows / 4 + 1 < 8192 ? rows / 4 + 1 : 8192);  // 4 rows per block
     if (rows) {
         hipLaunchKernelGGL(row_normalize_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s, static_cast<const Tin*>(a.q),
-                           fq, rows, a.dk);
+                           fq, rows, a.dk, pf);
         hipLaunchKernelGGL(row_normalize_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s, static_cast<const Tin*>(a.k),
-                           fk, rows, a.dk);
+                           fk, rows, a.dk, pf);
     }
-    fwd(a.v, fv, n.nv, kCopy);
-    fwd(a.alpha, fa, n.na, kSigmoid);
-    fwd(a.omega, fw, n.nw, kSoftplus);
-    fwd(a.r, fr, n.nr, kRSoftplus);
-    if (a.dO) fwd(a.dO, fdo, n.nv, kCopy);
-    hipError_t e = hipGetLastError();
+    const int wa = int(n.na / (rows ? rows : 1)), ww = int(n.nw / (rows ? rows : 1));  // per-token widths
+    fwd(a.v, fv, n.nv, kCopy, a.dv);
+    fwd(a.alpha, fa, n.na, kSigmoid, wa);
+    fwd(a.omega, fw, n.nw, kSoftplus, ww);
+    fwd(a.r, fr, n.nr, kRSoftplus, 1);
+    if (a.dO) fwd(a.dO, fdo, n.nv, kCopy, a.dv);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     BwdArgs f = a;
     f.q = fq;
@@ -168,12 +214,7 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     f.r = fr;
     f.dO = a.dO ? fdo : nullptr;
     f.dtype = 0;  // the token path runs on the fp32 copies
-    // The diagonal bf16 form takes the chunked path on the raw inputs (its
-    // kernels form the gated values as the gated forward does); the copies
-    // serve the pairs outside its range.
-    BwdArgs c = a;
-    c.gates = true;
-    if (backward_chunked_eligible(c)) e = launch_backward_chunked(c, f, s);
+    if (chunked) e = launch_backward_chunked_fallback(c, f, s);
     else e = launch_backward(f, s);
     if (e != hipSuccess) return e;
     const auto grad = [&](const void* z, float* d, size_t count, int op) {

@@ -86,8 +86,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // The chunked path on its own (diagonal bf16 form; with a.gates the gated
 // layer on raw q, k and pre-activations): the chunked adjoint for every pair
 // in range, the token path with `fallback`'s arguments for the others, dc0.
+// In two parts: main (checkpoints and the chunked adjoints; the flags of the
+// pairs outside the chunked range are then at backward_chunk_flags) and
+// fallback (the token path with `fallback`'s arguments for the flagged
+// pairs, then dc0).
 bool backward_chunked_eligible(const BwdArgs& a);
-hipError_t launch_backward_chunked(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream);
+int* backward_chunk_flags(const BwdArgs& a);
+hipError_t launch_backward_chunked_main(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_chunked_fallback(const BwdArgs& a, const BwdArgs& fallback, hipStream_t stream);
 // Backward of the gated layer: a.alpha, a.omega, a.r hold the gate
 // pre-activations and d alpha, d omega, d r come out as their gradients.
 // a.work holds backward_gated_workspace_bytes() bytes (the adjoint's

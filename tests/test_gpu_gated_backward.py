@@ -59,3 +59,28 @@ def test_gated_backward(dev, variant, dtype, dk, dv, T, with_state):
             assert e <= tol(dtype), (k, e)
     check_dc0(g["dc0"].cpu().numpy(), g["dp0"].cpu().numpy())
 
+
+
+def test_gated_backward_with_a_pair_out_of_range(dev):
+    # one (batch, head) pair has a chunk of z_alpha = -14 (alpha ~ 8e-7),
+    # outside the chunked form's range: that pair takes the token path on the
+    # fp32 copies of its gated values, the others the chunked path on the raw
+    # inputs, in the same call
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("gbwd_mix", "diagonal", "bf16", 2, 300, 2, 128, 128, 128.0, "uniform", 1790, omega_loc=-1.0)
+    x = wl.gated_inputs(w)
+    x["z_alpha"][1, 96:128, 0] = wl.round_bf16(np.full((32, 128), -14.0, np.float32))
+    ct = wl.backward_cotangents(w, with_state=True)
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev) for n in GATED}
+    g = kdn.backward_gated(**t, c0=_f32(x["c0"], dev), mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev),
+                           dS_T=_f32(ct["dS_T"], dev), dp_T=_f32(ct["dp_T"], dev))
+    torch.cuda.synchronize()
+    ref = oracle.backward_gated(**{n: x[n] for n in GATED}, c0=x["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
+                                dp_T=ct["dp_T"])
+    errs = {k: rel_err(g[k].cpu().numpy(), ref[k]) for k in GRADS}
+    print("gated bwd mixed range: " + " ".join(f"{k}={e:.1e}" for k, e in errs.items()), flush=True)
+    for k, e in errs.items():
+        if k != "dc0":
+            assert e <= tol("bf16"), (k, e)
+    check_dc0(g["dc0"].cpu().numpy(), g["dp0"].cpu().numpy())
