@@ -104,19 +104,22 @@ def chunked_workgroups(w, cus: int = 256) -> int:
 # substring of the kernel's name, the sources it is built from (counters
 # taken on other source are not reported), and how one call is run
 COUNTED = {
-    "main": ("diag_bf16_b8_t4096_h16_d128", "kdn_chunk_kernel", ("kdn_chunked.hip", "kdn_device.h")),
+    "main": ("diag_bf16_b8_t4096_h16_d128", "kdn_chunk_kernel",
+             ("kdn_chunked.hip", "kdn_device.h", "kdn_recurrent_core.h", "kdn_gates.h")),
     "isotropic": ("iso_bf16_b8_t4096_h16_d128", "kdn_iso_kernel", ("kdn_iso.hip", "kdn_device.h", "kdn_gates.h")),
     # the split forward's kernels (Mobius pre-pass, chunked segments, state
     # chaining, output correction): bytes per call
-    "long_context": ("diag_bf16_b1_t65536_h16_d128", "kdn_", ("kdn_chunked.hip", "kdn_split.hip", "kdn_device.h")),
+    "long_context": ("diag_bf16_b1_t65536_h16_d128", "kdn_",
+                     ("kdn_chunked.hip", "kdn_split.hip", "kdn_device.h", "kdn_recurrent_core.h", "kdn_gates.h")),
     "decode": ("decode_diag_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
-               ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
+               ("kdn_recurrent.hip", "kdn_recurrent_core.h", "kdn_device.h", "kdn_gates.h")),
     "decode_isotropic": ("decode_iso_bf16_n256_h16_d128_s1024", "kdn_recurrent_kernel",
-                         ("kdn_recurrent.hip", "kdn_recurrent_core.h")),
+                         ("kdn_recurrent.hip", "kdn_recurrent_core.h", "kdn_device.h", "kdn_gates.h")),
     # the backward's kernels (uncertainty adjoint, memory adjoint, d c0): the
     # counters pass runs no other library kernel
     "backward": ("diag_bf16_b8_t4096_h16_d128", "kdn_", ("kdn_backward.hip", "kdn_backward_chunk.hip",
-                                                          "kdn_chunked.hip", "kdn_device.h")),
+                                                          "kdn_chunked.hip", "kdn_device.h",
+                                                          "kdn_recurrent_core.h", "kdn_gates.h")),
 }
 
 
