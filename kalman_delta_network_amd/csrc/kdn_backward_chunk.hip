@@ -853,12 +853,20 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         const float gk = x.k[0] + (two ? x.k[1] : 0.f);
         const float u = x.u[0] + (two ? x.u[1] : 0.f);
         float al = bf1(x.al), kk = bf1(x.kk), w = bf1(x.w), rt = bf1(x.r);
+        float ga_z = 1.f, gw_z = 1.f;  // (gated) the gates' derivatives at z
         if (GATE) {
-            // the gated layer's values (as the gated forward forms them)
-            al = gate_sigmoid(al);
-            w = gate_softplus(w);
+            // the gated layer's values (as the gated forward forms them);
+            // sigmoid' = sigmoid(z) sigmoid(-z) (no cancellation in
+            // 1 - sigmoid), softplus' = sigmoid
+            const float za = al, zw = w;
+            al = gate_sigmoid(za);
+            w = gate_softplus(zw);
             rt = kGateRMin + gate_softplus(rt);
             kk *= x.sk;
+            if (!MAPS) {
+                ga_z = al * gate_sigmoid(-za);
+                gw_z = gate_sigmoid(zw);
+            }
         }
         const size_t tok = tokidx(t);
         const float ph = al * al * x.pp + w;
@@ -880,8 +888,9 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         const float dph = dp / (den * den) + gk * kk * inv + dd * k2;
         A.dq[tok * DK + i] = gq;
         A.dk_[tok * DK + i] = gks + gk * ph * inv + 2.0f * dd * ph * kk + 2.0f * du * mr * kk;
-        A.dalpha[tok * DK + i] = ga + 2.0f * dph * al * x.pp;
-        A.domega[tok * DK + i] = dph;
+        // (gated: the gradients of the pre-activations)
+        A.dalpha[tok * DK + i] = GATE ? (ga + 2.0f * dph * al * x.pp) * ga_z : ga + 2.0f * dph * al * x.pp;
+        A.domega[tok * DK + i] = GATE ? dph * gw_z : dph;
         dp = dph * al * al;
         float dr = -du * mr * k2 / rt;
         dr = sum16(dr);
@@ -912,8 +921,9 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
     }
 }
 
-// dr = dd + the waves' shares (one thread per token of a (batch, head) pair)
-template <int DK>
+// dr = dd + the waves' shares (one thread per token of a (batch, head) pair);
+// GATE: times softplus' = sigmoid at the pre-activation
+template <int DK, bool GATE>
 __global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
     const int nunit = A.B * A.H;
     const int ntile = A.dv / TILE;
@@ -925,7 +935,9 @@ __global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, size_t 
 #pragma unroll
     for (int w = 0; w < DK / 64; ++w) dr += sl[3 * L + 32 * w + t % L];
     const size_t b = size_t(unit / A.H);
-    A.dr[(b * size_t(A.T) + size_t(t)) * size_t(A.H) + size_t(unit % A.H)] = dr;
+    const size_t tok = (b * size_t(A.T) + size_t(t)) * size_t(A.H) + size_t(unit % A.H);
+    if (GATE) dr *= gate_sigmoid(bf1(static_cast<const bf16_t*>(A.r)[tok]));
+    A.dr[tok] = dr;
     (void)nunit;
 }
 
@@ -939,13 +951,13 @@ hipError_t launch_unc_chunk_t(const BwdArgs& a, size_t ck_floats, const int* fla
         if (nseg > 1)
             hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
         hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL(kdn_backward_dr_kernel<128>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_dr_kernel<128, GATE>), dgrid, dim3(256), 0, stream, a, ck_floats, flag);
     } else if (a.dk == 64) {
         const dim3 grid(units * nseg);
         if (nseg > 1)
             hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
         hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL(kdn_backward_dr_kernel<64>, dgrid, dim3(256), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_dr_kernel<64, GATE>), dgrid, dim3(256), 0, stream, a, ck_floats, flag);
     } else {
         return hipErrorNotSupported;
     }

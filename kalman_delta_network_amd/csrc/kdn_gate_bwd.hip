@@ -5,22 +5,25 @@
 //
 // The step also normalises q and k per token-head, x_hat = x / max(|x|, eps).
 //
-// The backward of the recurrence is the fp32 one of kdn_backward.hip, run on
-// the prologue's values: one pass widens v and dO to fp32, normalises the q
-// and k rows and evaluates the gates into the workspace (the same fp32
-// functions as the gated forward), the adjoint runs on them, and a second
-// pass turns the gradients of those values into gradients of the raw inputs:
+// The diagonal bf16 form runs the chunked adjoint on the raw inputs: its
+// kernels form the gates and the normalised rows as the gated forward does,
+// and take the gates' derivatives where they write the gradients.  Other
+// forms, and pairs outside the chunked range, run the fp32 adjoint of
+// kdn_backward.hip on the prologue's values: one pass widens v and dO to
+// fp32, normalises the q and k rows and evaluates the gates into the
+// workspace (the same fp32 functions as the gated forward), the adjoint runs
+// on them, and a pass takes the gates' derivatives.  Last, one pass over the
+// q and k rows applies the normalisation's Jacobian.  The chain rule:
 //   d x = (d x_hat - x_hat (x_hat . d x_hat)) / |x|   (d x_hat / eps where
 //         |x| < eps: the map is then x / eps),
 //   d z_alpha = d alpha * sigmoid(z) sigmoid(-z),
 //   d z_omega = d omega * sigmoid(z),   d z_r = d r * sigmoid(z).
-// Both passes move a few bytes per token next to the adjoint's recomputation,
-// which bounds this path.
 #include "kdn_gates.h"
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -77,9 +80,11 @@ __global__ void __launch_bounds__(256) gate_forward_kernel(const Tin* __restrict
 // d[i] *= the derivative of the gate at z[i]
 template <typename Tin>
 __global__ void __launch_bounds__(256) gate_grad_kernel(const Tin* __restrict__ z, float* __restrict__ d, size_t n,
-                                                        int op) {
+                                                        int op, PairFilter pf) {
+    if (pf.none()) return;
     const size_t stride = size_t(gridDim.x) * blockDim.x;
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        if (pf.skip(i)) continue;
         const float x = widen(z[i]);
         // sigmoid' = sigmoid(z) sigmoid(-z) (no cancellation in 1 - sigmoid);
         // softplus' = sigmoid
@@ -139,7 +144,64 @@ __global__ void __launch_bounds__(256) row_normalize_grad_kernel(const Tin* __re
     }
 }
 
+// Four consecutive channels as fp32 (8-byte bf16 or 16-byte fp32 load)
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// sum over the LPR lanes of a row (aligned groups of LPR lanes)
+template <int LPR>
+__device__ __forceinline__ float group_sum(float s) {
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    return s;
+}
+
+// The same map as row_normalize_grad_kernel for the q rows (blockIdx.y 0)
+// and the k rows (blockIdx.y 1) in one launch: LPR = dk / 4 lanes per row,
+// four channels per lane, each element read and written once.
+template <typename Tin, int LPR>
+__global__ void __launch_bounds__(256) row_normalize_grad4_kernel(const Tin* __restrict__ xq,
+                                                                  const Tin* __restrict__ xk, float* __restrict__ dq,
+                                                                  float* __restrict__ dk, size_t rows) {
+    constexpr int DK = 4 * LPR;
+    constexpr int RPB = 256 / LPR;  // rows per workgroup and iteration
+    const Tin* __restrict__ x = blockIdx.y ? xk : xq;
+    float* __restrict__ d = blockIdx.y ? dk : dq;
+    const int sub = int(threadIdx.x) % LPR;
+    const size_t stride = size_t(gridDim.x) * RPB;
+    // the LPR lanes of a row share it, so they take the loop together
+    for (size_t row = size_t(blockIdx.x) * RPB + threadIdx.x / LPR; row < rows; row += stride) {
+        const size_t e = row * DK + 4 * sub;
+        const float4 v = load4(x + e);
+        float4 g = *reinterpret_cast<const float4*>(d + e);
+        float s = v.x * v.x;
+        s = fmaf(v.y, v.y, s);
+        s = fmaf(v.z, v.z, s);
+        s = fmaf(v.w, v.w, s);
+        const float nrm = sqrtf(group_sum<LPR>(s));
+        const bool floored = !(nrm >= kNormEps);
+        const float inv = 1.f / (floored ? kNormEps : nrm);
+        float proj = (v.x * inv) * g.x;  // x_hat . d
+        proj = fmaf(v.y * inv, g.y, proj);
+        proj = fmaf(v.z * inv, g.z, proj);
+        proj = fmaf(v.w * inv, g.w, proj);
+        proj = group_sum<LPR>(proj);
+        if (floored) proj = 0.f;
+        g.x = (g.x - v.x * inv * proj) * inv;
+        g.y = (g.y - v.y * inv * proj) * inv;
+        g.z = (g.z - v.z * inv * proj) * inv;
+        g.w = (g.w - v.w * inv * proj) * inv;
+        *reinterpret_cast<float4*>(d + e) = g;
+    }
+}
+
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 struct GatedSizes {
     size_t nk, nv, na, nw, nr;
@@ -217,21 +279,39 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     if (chunked) e = launch_backward_chunked_fallback(c, f, s);
     else e = launch_backward(f, s);
     if (e != hipSuccess) return e;
-    const auto grad = [&](const void* z, float* d, size_t count, int op) {
+    // The chunked kernels leave the gradients of the gate pre-activations
+    // themselves; the token path's (all pairs, or only the flagged ones)
+    // still take the gates' derivatives here.
+    const auto grad = [&](const void* z, float* d, size_t count, int op, int width) {
         if (count == 0) return;
         const unsigned blocks = unsigned(count / 256 + 1 < 8192 ? count / 256 + 1 : 8192);
+        PairFilter f = pf;
+        f.width = width;
         hipLaunchKernelGGL(gate_grad_kernel<Tin>, dim3(blocks), dim3(256), 0, s, static_cast<const Tin*>(z), d,
-                           count, op);
+                           count, op, f);
     };
     if (rows) {
-        hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
-                           static_cast<const Tin*>(a.q), a.dq, rows, a.dk);
-        hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
-                           static_cast<const Tin*>(a.k), a.dk_, rows, a.dk);
+        const bool vec = (a.dk == 64 || a.dk == 128) && aligned16(a.q) && aligned16(a.k) && aligned16(a.dq) &&
+                         aligned16(a.dk_);
+        if (vec) {
+            const size_t rpb = size_t(256 / (a.dk / 4));
+            const unsigned blocks = unsigned(std::min<size_t>((rows + rpb - 1) / rpb, 4096));
+            if (a.dk == 128)
+                hipLaunchKernelGGL((row_normalize_grad4_kernel<Tin, 32>), dim3(blocks, 2), dim3(256), 0, s,
+                                   static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.dq, a.dk_, rows);
+            else
+                hipLaunchKernelGGL((row_normalize_grad4_kernel<Tin, 16>), dim3(blocks, 2), dim3(256), 0, s,
+                                   static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.dq, a.dk_, rows);
+        } else {
+            hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
+                               static_cast<const Tin*>(a.q), a.dq, rows, a.dk);
+            hipLaunchKernelGGL(row_normalize_grad_kernel<Tin>, dim3(row_blocks), dim3(256), 0, s,
+                               static_cast<const Tin*>(a.k), a.dk_, rows, a.dk);
+        }
     }
-    grad(a.alpha, a.dalpha, n.na, kSigmoid);
-    grad(a.omega, a.domega, n.nw, kSoftplus);
-    grad(a.r, a.dr, n.nr, kSoftplus);
+    grad(a.alpha, a.dalpha, n.na, kSigmoid, wa);
+    grad(a.omega, a.domega, n.nw, kSoftplus, ww);
+    grad(a.r, a.dr, n.nr, kSoftplus, 1);
     return hipGetLastError();
 }
 
