@@ -31,15 +31,17 @@
 // Workgroup = one (batch, head) pair and 64 value columns (32 when the
 // 64-column tiling would leave more than half of the CUs idle), 8 waves, in a
 // software pipeline with one workgroup barrier per iteration: at iteration i
-//   wave 0  scan of chunk i: |k_t|^2 from its k tile, then the uncertainty
-//           scalar's Mobius maps over the chunk's 32 tokens (lane = token),
-//           composed as 2 x 2 matrix products by an inclusive cross-lane scan
-//           on DPP row shifts and a row broadcast; the log-decay prefix sums
-//           the same way; per-token weights to LDS
+//   wave 0  scan of chunk i: the uncertainty scalar's Mobius maps over the
+//           chunk's 32 tokens (lane = token) from |k_t|^2 (gated: computed
+//           here from the chunk's k tile), composed as 2 x 2 matrix products
+//           by an inclusive cross-lane scan on DPP row shifts and a row
+//           broadcast; the log-decay prefix sums the same way; per-token
+//           weights to LDS
 //   wave 1  Gram K K^T of chunk i - 1 (matrix cores), weighted into M's
 //           diagonal blocks and -M_10; k^T of chunk i - 2 for the update
 //   wave 2  inverses of M's diagonal blocks of chunk i - 2
-//   wave 3  direct copies of the k and q tiles of chunk i + 2; Gram Q K^T of
+//   wave 3  direct copies of the k and q tiles of chunk i + 2; |k_t|^2 of
+//           chunk i + 1 once its tile has landed (not gated); Gram Q K^T of
 //           chunk i - 1, weighted into P = tril(...)
 //   waves 4..7  state update of chunk i - 3: 16 value columns each, S~ in
 //           registers (fp32)
@@ -85,6 +87,7 @@ struct IsoSmem {
     alignas(16) float Md[2][NT * 256];    // M's diagonal blocks, column-major [a][s][t]
     alignas(16) float Wi[NT][2][64];      // block-inverse scratch
     alignas(16) float qn[L];              // 1/|q_t| of the Gram-P wave's chunk (gated)
+    alignas(16) float kn[2][L];           // |k_t|^2 of the next chunk (slot c & 1), for the scan
 };
 
 struct IsoArgs {
@@ -666,6 +669,10 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         tile_issue<DK>(sm.K[1], a.k, a, h, 1, nchunks);
         tile_issue<DK>(sm.Q[1], a.q, a, h, 1, nchunks);
         vm_wait<NK>();  // chunk 0 has landed
+        if (!GATE) {
+            const float nrm = tile_norm<DK>(sm.K[0]);
+            if (lane < L) sm.kn[0][lane] = nrm;
+        }
     }
     bar();
 
@@ -677,7 +684,8 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         scan_load(X, a, h, 0, nchunks);
         for (int i = 0; i < nit; ++i) {
             if (i < nchunks) {
-                const float nrm = tile_norm<DK>(sm.K[i % KR]);
+                // gated: the q norms load the copy wave, so the scan takes the k norms itself
+                const float nrm = GATE ? tile_norm<DK>(sm.K[i % KR]) : sm.kn[i & 1][lane & 31];
                 scan_run<DK, GATE>(X, sm, i, nrm, a.mu, bprev, gam, min(L, a.T - i * L));
             }
             scan_load(X, a, h, i + 1, nchunks);  // used at the next iteration
@@ -700,15 +708,21 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
             bar();
         }
     } else if (wave == 3) {
-        // ---------------- tile copies; P of chunk i - 1 ----------------
+        // ---------------- tile copies; |k|^2 of chunk i + 1; P of chunk i - 1 ----------------
         for (int i = 0; i < nit; ++i) {
             // chunk i + 2 into slot (i + 2) % KR: its previous occupant, chunk
             // i + 2 - KR, was last read at iteration i - 1
             tile_issue<DK>(sm.K[(i + 2) % KR], a.k, a, h, i + 2, nchunks);
             tile_issue<DK>(sm.Q[(i + 2) % KR], a.q, a, h, i + 2, nchunks);
+            vm_wait<NK>();  // chunk i + 1 (copied at iteration i - 1) has landed; chunk i + 2 may not have
+            if (!GATE && i + 1 < nchunks) {
+                // the row norms the scan takes at iteration i + 1 (its slot was
+                // last read at iteration i - 1)
+                const float nrm = tile_norm<DK>(sm.K[(i + 1) % KR]);
+                if (lane < L) sm.kn[(i + 1) & 1][lane] = nrm;
+            }
             const int c = i - 1;
             if (c >= 0 && c < nchunks) gram_p<DK, GATE>(sm, c % KR, c & 3, c % 3);
-            vm_wait<NK>();  // chunk i + 1 (copied at iteration i - 1) has landed; chunk i + 2 may not have
             bar();
         }
         vm_wait<0>();
