@@ -73,27 +73,33 @@ __global__ void __launch_bounds__(64) kdn_split_mob_sub_kernel(const bf16_t* __r
     float4 P[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) P[c] = make_float4(1.f, 0.f, 0.f, 1.f);
-    // 8 tokens' inputs are loaded before their maps are applied, so one
-    // memory round trip serves 8 tokens
+    // Batches of U tokens in two register sets: the next batch's loads are
+    // issued before this batch's maps are applied, so the composition runs
+    // while they are in flight.  Loads past the sub-segment read its last
+    // token (clamped) and are not applied.
     constexpr int U = 8;
-    for (int tb = t0; tb < t1; tb += U) {
+    struct Batch {
         u2 al[U], w[U], kk[U];
         float rr[U];
+    };
+    const auto load = [&](Batch& B, int tb) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const size_t tok = (size_t(b) * T + min(tb + j, t1 - 1)) * H + h;
-            al[j] = *reinterpret_cast<const u2*>(alpha + tok * DK + 4 * cq);
-            w[j] = *reinterpret_cast<const u2*>(omega + tok * DK + 4 * cq);
-            kk[j] = *reinterpret_cast<const u2*>(k + tok * DK + 4 * cq);
-            rr[j] = bf1(r[tok]);
+            B.al[j] = *reinterpret_cast<const u2*>(alpha + tok * DK + 4 * cq);
+            B.w[j] = *reinterpret_cast<const u2*>(omega + tok * DK + 4 * cq);
+            B.kk[j] = *reinterpret_cast<const u2*>(k + tok * DK + 4 * cq);
+            B.rr[j] = bf1(r[tok]);
         }
+    };
+    const auto apply = [&](const Batch& B, int tb) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             if (tb + j < t1) {
-                const float mr = mu / rr[j];
+                const float mr = mu / B.rr[j];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint32_t wa = al[j][c >> 1], ww = w[j][c >> 1], wk = kk[j][c >> 1];
+                    const uint32_t wa = B.al[j][c >> 1], ww = B.w[j][c >> 1], wk = B.kk[j][c >> 1];
                     const float a = (c & 1) ? bf_hi(wa) : bf_lo(wa), om = (c & 1) ? bf_hi(ww) : bf_lo(ww);
                     const float kv = (c & 1) ? bf_hi(wk) : bf_lo(wk);
                     const float u = mr * kv * kv, a2 = a * a;
@@ -101,6 +107,14 @@ __global__ void __launch_bounds__(64) kdn_split_mob_sub_kernel(const bf16_t* __r
                 }
             }
         }
+    };
+    Batch A, B;
+    load(A, t0);
+    for (int tb = t0; tb < t1; tb += 2 * U) {
+        load(B, tb + U);
+        apply(A, tb);
+        load(A, tb + 2 * U);
+        apply(B, tb + U);
     }
     float4* dst = out + ((size_t(unit) * nseg + g) * nsub + sub) * DK + 4 * cq;
 #pragma unroll
@@ -199,34 +213,50 @@ __global__ void __launch_bounds__(256) kdn_split_correct_kernel(const bf16_t* __
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
-    for (int rt = wave; rt < TB / 16; rt += 4) {
-        const int tn = tb + 16 * rt + n;  // this lane's token (B operand column, output row)
-        if (tb + 16 * rt >= tend) break;
-        const bool ok = tn < tend;
-        const size_t tok = (size_t(b) * T + min(tn, tend - 1)) * H + h;
+    constexpr int NTW = TB / 64;  // 16-token row tiles per wave: w, w + 4, ...
+    // One row tile's operands: the tokens' o^Phi rows and their current
+    // outputs, loaded a tile ahead of its products (tokens past the segment
+    // read its last token and are not written).
+    struct Tile {
         b8 bo[KS];
+        u2 cur[DV / 16];
+    };
+    const auto load = [&](Tile& X, int rt) {
+        const int tn = min(tb + 16 * rt + n, tend - 1);
+        const size_t tok = (size_t(b) * T + tn) * H + h;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            bo[kk] = *reinterpret_cast<const b8*>(ophi + tok * DK + 32 * kk + kg8);
-            if (!ok) bo[kk] = b8{};
-        }
-        bf16_t* orow = o + tok * DV;
+        for (int kk = 0; kk < KS; ++kk) X.bo[kk] = *reinterpret_cast<const b8*>(ophi + tok * DK + 32 * kk + kg8);
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) X.cur[ct] = *reinterpret_cast<const u2*>(o + tok * DV + 16 * ct + g4);
+    };
+    const auto apply = [&](const Tile& X, int rt) {
+        // every lane takes part in the products (the matrix cores read the
+        // operands of the whole wave); only tokens inside the segment store
+        const int tn = tb + 16 * rt + n;  // this lane's token (B operand column, output row)
+        const bool ok = tn < tend;
+        bf16_t* orow = o + ((size_t(b) * T + min(tn, tend - 1)) * H + h) * DV;
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const b8 as = *reinterpret_cast<const b8*>(&St[(16 * ct + n) * P + 32 * kk + kg8]);
-                acc = mfma32(as, bo[kk], acc);
+                acc = mfma32(as, X.bo[kk], acc);
             }
             // acc[e]: value column 16 ct + g4 + e of token tn
-            if (ok) {
-                const u2 cur = *reinterpret_cast<const u2*>(orow + 16 * ct + g4);
-                const float o0 = bf_lo(cur[0]) + acc[0], o1 = bf_hi(cur[0]) + acc[1];
-                const float o2 = bf_lo(cur[1]) + acc[2], o3 = bf_hi(cur[1]) + acc[3];
-                *reinterpret_cast<u2*>(orow + 16 * ct + g4) = u2{pack2(o0, o1), pack2(o2, o3)};
-            }
+            const float o0 = bf_lo(X.cur[ct][0]) + acc[0], o1 = bf_hi(X.cur[ct][0]) + acc[1];
+            const float o2 = bf_lo(X.cur[ct][1]) + acc[2], o3 = bf_hi(X.cur[ct][1]) + acc[3];
+            if (ok) *reinterpret_cast<u2*>(orow + 16 * ct + g4) = u2{pack2(o0, o1), pack2(o2, o3)};
         }
+    };
+    Tile X0, X1;
+    load(X0, wave);
+#pragma unroll
+    for (int i = 0; i < NTW; i += 2) {
+        if (i + 1 < NTW) load(X1, wave + 4 * (i + 1));
+        apply(X0, wave + 4 * i);
+        if (i + 2 < NTW) load(X0, wave + 4 * (i + 2));
+        if (i + 1 < NTW) apply(X1, wave + 4 * (i + 1));
     }
 }
 
