@@ -84,3 +84,35 @@ def test_gated_backward_with_a_pair_out_of_range(dev):
         if k != "dc0":
             assert e <= tol("bf16"), (k, e)
     check_dc0(g["dc0"].cpu().numpy(), g["dp0"].cpu().numpy())
+
+
+def test_gated_backward_full_size_sampled_heads(dev):
+    """kdn_backward_gated at B=8, T=4096, H=16, d=128 (diagonal, bf16, the
+    chunked path with the gates and the q/k normalisation inside its
+    kernels); the oracle runs on sampled (batch, head) pairs."""
+    import torch
+    import kalman_delta_network_amd as kdn
+    from kdn_testutil import sample_pairs
+    w = wl.WORKLOADS["diag_bf16_b8_t4096_h16_d128"]
+    x = wl.gated_inputs(w)
+    ct = wl.backward_cotangents(w, with_state=False)
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev) for n in GATED}
+    g = kdn.backward_gated(**t, c0=_f32(x["c0"], dev), mu=w.mu,
+                           dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev), variant=w.variant)
+    torch.cuda.synchronize()
+    got = {n: v.cpu().numpy() for n, v in g.items()}
+    pairs = sample_pairs(w.B, w.H, 2, seed=w.seed + 1)
+    worst = {k: 0.0 for k in GRADS if k != "dc0"}
+    for b, h in pairs:
+        sub = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in GATED}
+        ref = oracle.backward_gated(**sub, c0=x["c0"][h:h + 1], mu=w.mu,
+                                    dO=np.ascontiguousarray(ct["dO"][b:b + 1, :, h:h + 1]), variant=w.variant)
+        for k in worst:
+            gk = got[k][b:b + 1, :, h:h + 1] if k not in ("dS0", "dp0") else got[k][b:b + 1, h:h + 1]
+            worst[k] = max(worst[k], rel_err(gk, ref[k]))
+    print(f"gated full size pairs={pairs}: " + " ".join(f"{k}={v:.1e}" for k, v in worst.items()), flush=True)
+    for k, e in worst.items():
+        assert e <= tol("bf16"), (k, e)
+    for k in GRADS:
+        assert np.all(np.isfinite(got[k])), k
+    check_dc0(got["dc0"], got["dp0"])
