@@ -116,3 +116,36 @@ def test_gated_backward_full_size_sampled_heads(dev):
     for k in GRADS:
         assert np.all(np.isfinite(got[k])), k
     check_dc0(got["dc0"], got["dp0"])
+
+
+def test_gated_backward_misaligned_q_k(dev):
+    """q and k two bytes off 16-byte alignment: the chunked path does not
+    apply (it loads 16-byte pieces), so every pair takes the token path on
+    the fp32 copies (read element by element), and the normalisation's
+    Jacobian takes its element-wise pass instead of the 16-byte one."""
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("gbwd_mis", "diagonal", "bf16", 2, 100, 2, 128, 128, 128.0, "uniform", 1811, omega_loc=-1.0)
+    x = wl.gated_inputs(w)
+    ct = wl.backward_cotangents(w, with_state=True)
+
+    def misaligned(a):
+        buf = torch.empty(a.size + 1, dtype=torch.bfloat16, device=dev)
+        view = buf[1:].view(a.shape)
+        view.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16))
+        assert view.data_ptr() % 16 != 0
+        return view
+
+    t = {n: (misaligned(x[n]) if n in ("q", "k") else
+             torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev)) for n in GATED}
+    g = kdn.backward_gated(**t, c0=_f32(x["c0"], dev), mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev),
+                           dS_T=_f32(ct["dS_T"], dev), dp_T=_f32(ct["dp_T"], dev))
+    torch.cuda.synchronize()
+    ref = oracle.backward_gated(**{n: x[n] for n in GATED}, c0=x["c0"], mu=w.mu, dO=ct["dO"], dS_T=ct["dS_T"],
+                                dp_T=ct["dp_T"])
+    errs = {k: rel_err(g[k].cpu().numpy(), ref[k]) for k in GRADS}
+    print("gated bwd misaligned q, k: " + " ".join(f"{k}={e:.1e}" for k, e in errs.items()), flush=True)
+    for k, e in errs.items():
+        if k != "dc0":
+            assert e <= tol("bf16"), (k, e)
+    check_dc0(g["dc0"].cpu().numpy(), g["dp0"].cpu().numpy())
