@@ -50,19 +50,21 @@ def _ft(x, emulate):
         return np.asarray(x, np.float32).astype(np.float64)
 
 
-def chunk_model(q, k, v, alpha, omega, r, c0, mu, emulate=False):
+def chunk_model(q, k, v, alpha, omega, r, c0, mu, emulate=False, lc=L):
     """One (batch, head) pair: q, k, alpha, omega [T, dk]; v [T, dv]; r [T].
     Returns o, S_T, p_T, the first chunk outside the fast form's range (or
-    None) and the largest |operand| the fast form produced."""
+    None) and the largest |operand| the fast form produced.  lc: the chunk
+    length (even; the kernel's is 32), referenced to its midpoint lc / 2."""
     T, dk = k.shape
     dv = v.shape[1]
+    hl = lc // 2
     S = np.zeros((dk, dv))
     p = np.full(dk, float(c0))
     o = np.zeros((T, dv))
     big = 0.0
-    nch = (T + L - 1) // L
+    nch = (T + lc - 1) // lc
     for c in range(nch):
-        t0, t1 = c * L, min(T, (c + 1) * L)
+        t0, t1 = c * lc, min(T, (c + 1) * lc)
         n = t1 - t0
         # chain: uncertainty recurrence (sequential per channel) and decays
         ph = np.zeros((n, dk))
@@ -70,11 +72,11 @@ def chunk_model(q, k, v, alpha, omega, r, c0, mu, emulate=False):
         for j in range(n):
             ph[j] = alpha[t0 + j] ** 2 * pe + omega[t0 + j]
             pe = ph[j] / (1.0 + (mu / r[t0 + j]) * k[t0 + j] ** 2 * ph[j])
-        a = np.ones((L, dk))
+        a = np.ones((lc, dk))
         a[:n] = alpha[t0:t1]
-        g = np.cumprod(a[:16], axis=0)              # g_t, t <= 15
-        gb = np.cumprod(a[16:], axis=0)             # prod over 16..t, t >= 16
-        g15, gb31 = g[15], gb[-1]
+        g = np.cumprod(a[:hl], axis=0)              # g_t, t < hl (hl = 16 in the kernel)
+        gb = np.cumprod(a[hl:], axis=0)             # prod over hl..t, t >= hl
+        g15, gb31 = g[-1], gb[-1]
         if np.min(g15) < 2.0 ** -THETA or np.min(gb31) < 2.0 ** -THETA:
             # outside the fast form: token recurrence from this chunk on
             rest = {nm: x[None, t0:, None] for nm, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha),
@@ -129,6 +131,22 @@ def test_midpoint_form_is_the_recurrence(alpha_loc):
     assert bad is None
     ro, rS, rp = _ref(x, mu)
     assert _rel(o, ro) < 1e-10 and _rel(S, rS) < 1e-10 and _rel(p, rp) < 1e-12
+
+
+@pytest.mark.parametrize("lc", [2, 8, 16, 64, 128])
+def test_chunk_form_does_not_depend_on_the_chunk_length(lc):
+    # The chunk length is a blocking choice, not part of the method (the
+    # configs name 64, the kernel uses 32): in fp64 the midpoint form with
+    # any even length equals the token recurrence and the 32-token form,
+    # ragged last chunk included
+    x, mu = _inputs(301, 32, 16, 2.0, 37)
+    args = (x["q"], x["k"], x["v"], x["alpha"], x["omega"], x["r"], 1.0, mu)
+    o, S, p, bad, _ = chunk_model(*args, lc=lc)
+    o32, S32, p32, _, _ = chunk_model(*args)
+    assert bad is None
+    ro, rS, rp = _ref(x, mu)
+    assert _rel(o, ro) < 1e-10 and _rel(S, rS) < 1e-10 and _rel(p, rp) < 1e-12
+    assert _rel(o, o32) < 1e-10 and _rel(S, S32) < 1e-10 and _rel(p, p32) < 1e-12
 
 
 @pytest.mark.parametrize("alpha_const", [1e-3, 1e-6])
