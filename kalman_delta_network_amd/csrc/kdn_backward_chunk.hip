@@ -769,7 +769,10 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 // sequence is cut into segments of SEGU tokens run in parallel: a first
 // launch (MAPS) composes each segment's affine map, a second runs every
 // segment from its exact entering dp (the later segments' maps applied to
-// dp_T in order) and writes the gradients.
+// dp_T in order) and writes the gradients.  GATE: alpha, omega and r are
+// formed from the pre-activations as the gated forward forms them, and the
+// written d alpha, d omega (and dr, in kdn_backward_dr_kernel) are already
+// the gradients of the pre-activations.
 // Slot of chunk c (tile 0 unless noted): [t] u of each tile (its own slot),
 // [L + t] d, [2L + t] dd, [3L + 32 w + t] wave w's share of dr, (gated)
 // [5L + t] 1 / |k_t|, and in the
