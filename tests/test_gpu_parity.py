@@ -232,6 +232,41 @@ def test_decode_full_size(dev, name):
     assert max(worst, eS, ep) <= tol("bf16")
 
 
+@pytest.mark.parametrize("name", ["decode_diag_bf16_n256_h16_d128_s1024", "decode_iso_bf16_n256_h16_d128_s1024"])
+def test_decode_streamed_state(dev, name):
+    # N=512 sequences x 16 heads: a 537 MB state, above the size from which
+    # the step streams S with nontemporal hints; 16 steps, sampled pairs
+    # stepped by the oracle alongside
+    import torch
+    import kalman_delta_network_amd as kdn
+    import oracle
+    w = wl.WORKLOADS[name].with_(name=name.replace("n256", "n512"), B=512, decode_steps=16)
+    ostep = oracle.step_diag if w.variant == "diagonal" else oracle.step_iso
+    st = wl.decode_state(w)
+    S = torch.from_numpy(st["S0"]).to(dev)
+    p = torch.from_numpy(st["p0"]).to(dev)
+    pairs = sample_pairs(w.B, w.H, 6, seed=w.seed + 3)
+    Sr = {pr: st["S0"][pr[0]:pr[0] + 1, pr[1]:pr[1] + 1].astype(np.float64) for pr in pairs}
+    prr = {pr: st["p0"][pr[0]:pr[0] + 1, pr[1]:pr[1] + 1].astype(np.float64) for pr in pairs}
+    worst = 0.0
+    for s in range(w.decode_steps):
+        x = wl.decode_tokens(w, s)
+        o = kdn.step(**to_dev(x, "bf16", dev), mu=w.mu, S=S, p=p, variant=w.variant)
+        o_h = o.float().cpu().numpy()
+        for pr in pairs:
+            n, h = pr
+            sub = {k: np.ascontiguousarray(x[k][n:n + 1, h:h + 1]) for k in TOKEN_INPUTS}
+            res = ostep(**sub, mu=w.mu, S=Sr[pr], p=prr[pr])
+            Sr[pr], prr[pr] = res["S"], res["p"]
+            worst = max(worst, rel_err(o_h[n:n + 1, h:h + 1], res["o"]))
+    torch.cuda.synchronize()
+    S_h, p_h = S.cpu().numpy(), p.cpu().numpy()
+    eS = max(rel_err(S_h[n:n + 1, h:h + 1], Sr[(n, h)]) for n, h in pairs)
+    ep = max(rel_err(p_h[n:n + 1, h:h + 1], prr[(n, h)]) for n, h in pairs)
+    print(f"decode streamed {w.variant}: o={worst:.2e} S={eS:.2e} p={ep:.2e}", flush=True)
+    assert max(worst, eS, ep) <= tol("bf16")
+
+
 @pytest.mark.parametrize("variant", ["diagonal", "isotropic"])
 def test_decode_steps_all_heads(dev, variant):
     # eight plain kdn_step calls from a carried state (N=5, H=3, d_k=d_v=128),
