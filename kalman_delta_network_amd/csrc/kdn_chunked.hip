@@ -1443,9 +1443,15 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             const int fsub = sm.fsub[c % 3][0] | sm.fsub[c % 3][1];  // read early: its use is a segment away
             const bool run = c < nchunks && c < bad_seen;
             if (!phi) state_issue_t<DK, NCT>(sm, a, b, h, colb, cw, it, nchunks);
+            if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
+            // everything but the NCT loads just issued has landed: the v of
+            // chunk it - 1, the previous iteration's stores and chain rows
+            vm_wait<NCT>();
             if (STORE && run) {
-                // chunk c's start state, diag(g_15) S (fp32), as [DK / 4][64][4]:
-                // rows 4j .. 4j + 3 of a column in one 16-byte store
+                // chunk c's start state, diag(g_15) S (fp32; the first segment
+                // leaves it unchanged), as [DK / 4][64][4]: rows 4j .. 4j + 3 of
+                // a column in one 16-byte store.  Issued after the wait, so
+                // that they complete during the next iteration, not this one.
                 f4* ck = reinterpret_cast<f4*>(a.ck + (size_t(unit) * ntile + tile) * a.ck_floats +
                                                size_t(c) * DK * DVTN);
 #pragma unroll
@@ -1454,10 +1460,6 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                     for (int ct = 0; ct < NCT; ++ct)
                         ck[((16 * r4 + g4) / 4) * DVTN + cw * (16 * NCT) + 16 * ct + n] = st.S[r4][ct];
             }
-            if (run) state_seg1<DK, NCT>(st, sm, c & 1, cw, c % 3);
-            // everything but the NCT loads just issued has landed: the v of
-            // chunk it - 1, the previous iteration's stores and chain rows
-            vm_wait<NCT>();
             bar();
             // rows 0..15 of the chain's chunk it + 2: the chain has read those
             // rows of chunk it (same buffer) before the barrier above
