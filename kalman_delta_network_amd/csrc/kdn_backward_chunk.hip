@@ -415,7 +415,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int t = 8 * b8i + j;
-                        if (!MASK || t < nvalid) pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i] = pv[j];
+                        if (!MASK || t < nvalid) __builtin_nontemporal_store(pv[j], &pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i]);
                     }
                 asm volatile("" ::: "memory");  // one group at a time
             }
@@ -657,9 +657,9 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                     sm.kap[tl * DK + i] = fmaf(dkc, kk, fmaf(dq, qq, -dkapc * kp));  // w = d rho . rho
                     if (tl < nvalid) {
                         float* dst = partial + ((size_t(unit) * T + t0 + tl) * ntile + tile) * 4 * DK + i;
-                        dst[0] = dq;
-                        dst[DK] = dkap;
-                        dst[2 * DK] = fmaf(-kp, drt, dkc);
+                        __builtin_nontemporal_store(dq, &dst[0]);
+                        __builtin_nontemporal_store(dkap, &dst[DK]);
+                        __builtin_nontemporal_store(fmaf(-kp, drt, dkc), &dst[2 * DK]);
                     }
                 }
                 // u_t = sum_i d kappa kappa' over the key tile's 16 channels
@@ -722,14 +722,14 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 if (hf == 0) {
 #pragma unroll
                     for (int j = 0; j < HL; ++j) {
-                        if (!MASK || j < nvalid) dst[j * tstep] = (fa - acc) * __builtin_amdgcn_rcpf(av[j]);
+                        if (!MASK || j < nvalid) __builtin_nontemporal_store((fa - acc) * __builtin_amdgcn_rcpf(av[j]), &dst[j * tstep]);
                         acc += wv[j];
                     }
                 } else {
 #pragma unroll
                     for (int j = HL - 1; j >= 0; --j) {
                         acc += wv[j];
-                        if (!MASK || HL + j < nvalid) dst[(HL + j) * tstep] = (acc + fb) * __builtin_amdgcn_rcpf(av[j]);
+                        if (!MASK || HL + j < nvalid) __builtin_nontemporal_store((acc + fb) * __builtin_amdgcn_rcpf(av[j]), &dst[(HL + j) * tstep]);
                     }
                 }
                 asm volatile("" ::: "memory");
@@ -778,6 +778,9 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 // [5L + t] 1 / |k_t|, and in the
 // slot of a segment's first chunk [MAPOFF + 2 i], [MAPOFF + 2 i + 1] the
 // segment's map of channel i.
+// The per-token tile sums and p_{t-1} (GBs at B=8, T=4096, H=16, d=128, far
+// beyond any cache) are written by the memory adjoint and read here with
+// nontemporal hints, as are the gradients written here.
 // ---------------------------------------------------------------------------
 constexpr int PFU = 8;  // prefetch ring: token inputs are loaded 7 tokens ahead
 constexpr int SEGU = 512;  // tokens per segment of the uncertainty adjoint
@@ -824,17 +827,17 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         for (int tile = 0; tile < 2; ++tile) {
             const int tc = min(tile, ntile - 1);
             const float* src = partial + ((size_t(unit) * T + t) * ntile + tc) * 4 * DK + i;
-            x.k[tile] = src[DK];
+            x.k[tile] = __builtin_nontemporal_load(&src[DK]);
             if (!MAPS) {
-                x.q[tile] = src[0];
-                x.ks[tile] = src[2 * DK];
-                x.a[tile] = src[3 * DK];
+                x.q[tile] = __builtin_nontemporal_load(&src[0]);
+                x.ks[tile] = __builtin_nontemporal_load(&src[2 * DK]);
+                x.a[tile] = __builtin_nontemporal_load(&src[3 * DK]);
             }
             x.u[tile] = slot(tc, t)[tl];
         }
         x.d = slot(0, t)[L + tl];
         if (GATE) x.sk = slot(0, t)[5 * L + tl];
-        x.pp = pbuf[(size_t(unit) * T + t) * ntile * DK + i];
+        x.pp = __builtin_nontemporal_load(&pbuf[(size_t(unit) * T + t) * ntile * DK + i]);
         x.al = ain[tok * DK + i];
         x.kk = kin[tok * DK + i];
         x.w = win[tok * DK + i];
@@ -889,11 +892,11 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         const float pn = ph / den;
         const float du = -dp * pn * pn;
         const float dph = dp / (den * den) + gk * kk * inv + dd * k2;
-        A.dq[tok * DK + i] = gq;
-        A.dk_[tok * DK + i] = gks + gk * ph * inv + 2.0f * dd * ph * kk + 2.0f * du * mr * kk;
+        __builtin_nontemporal_store(gq, &A.dq[tok * DK + i]);
+        __builtin_nontemporal_store(gks + gk * ph * inv + 2.0f * dd * ph * kk + 2.0f * du * mr * kk, &A.dk_[tok * DK + i]);
         // (gated: the gradients of the pre-activations)
-        A.dalpha[tok * DK + i] = GATE ? (ga + 2.0f * dph * al * x.pp) * ga_z : ga + 2.0f * dph * al * x.pp;
-        A.domega[tok * DK + i] = GATE ? dph * gw_z : dph;
+        __builtin_nontemporal_store(GATE ? (ga + 2.0f * dph * al * x.pp) * ga_z : ga + 2.0f * dph * al * x.pp, &A.dalpha[tok * DK + i]);
+        __builtin_nontemporal_store(GATE ? dph * gw_z : dph, &A.domega[tok * DK + i]);
         dp = dph * al * al;
         float dr = -du * mr * k2 / rt;
         dr = sum16(dr);
