@@ -488,6 +488,28 @@ __device__ __forceinline__ void v_issue(IsoSmem<DK>& sm, const IsoArgs& a, int h
     }
 }
 
+// The k and q rows of a state chunk as matrix-core operands (lane (n, kg8):
+// row 16 at + n, channels 32 kk + kg8 .. + 7).  A state wave loads the next
+// chunk's during the S update of the current one, so the reads overlap
+// those products instead of opening the next chunk.
+template <int DK>
+struct StateOps {
+    b8 ak[NT][DK / 32], aq[NT][DK / 32];
+};
+template <int DK>
+__device__ __forceinline__ void iso_ops_load(StateOps<DK>& op, const IsoSmem<DK>& sm, int c) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, kg8 = (lane >> 4) * 8;
+    const int kslot = c % KR;
+#pragma unroll
+    for (int at = 0; at < NT; ++at)
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            op.ak[at][kk] = *reinterpret_cast<const b8*>(sm.K[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
+            op.aq[at][kk] = *reinterpret_cast<const b8*>(sm.Q[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
+        }
+}
+
 template <int NCW>
 struct SegCarry {
     f4 O[NCW][NT];  // (Q S)^T of the chunk, scaled: value column x token
@@ -497,16 +519,17 @@ struct SegCarry {
 
 template <int DK, int NCW, bool GATE>
 __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& cy, IsoSmem<DK>& sm, int c,
-                                         int sw_) {
+                                         int sw_, const StateOps<DK>& op) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     constexpr int KS = DK / 32;
     constexpr int VP = 16 * NCW;  // v row pitch
-    const int kslot = c % KR, slot = c & 3, vslot = c % 3, mb = c & 1, m3 = c % 3;
+    const int slot = c & 3, vslot = c % 3, mb = c & 1, m3 = c % 3;
     const bf16_t* rv = &sm.RV[vslot][sw_ * NCW * 512];
-    // read phase
+    // read phase (the k and q operands came with op)
+    const auto& ak = op.ak;
+    const auto& aq = op.aq;
     uint32_t vr[NCW][NT][4];
-    b8 ak[NT][KS], aq[NT][KS];
     f4 rw[NT];
 #pragma unroll
     for (int at = 0; at < NT; ++at) {
@@ -514,11 +537,6 @@ __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& c
         for (int j = 0; j < NCW; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) vr[j][at][e] = rv[(16 * at + g4 + e) * VP + 16 * j + n];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            ak[at][kk] = *reinterpret_cast<const b8*>(sm.K[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
-            aq[at][kk] = *reinterpret_cast<const b8*>(sm.Q[kslot] + sw<DK>(16 * at + n, 32 * kk + kg8));
-        }
         rw[at] = *reinterpret_cast<const f4*>(&sm.sc[slot][3][16 * at + g4]);
     }
     // O's row weights (gated: with 1/|q_t|; otherwise R's)
@@ -565,7 +583,8 @@ __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& c
 
 template <int DK, int NCW>
 __device__ __forceinline__ void iso_seg2(IsoState<DK, NCW>& st, const SegCarry<NCW>& cy, IsoSmem<DK>& sm,
-                                         const IsoArgs& a, int h, int col0, int c) {
+                                         const IsoArgs& a, int h, int col0, int c, int nchunks,
+                                         StateOps<DK>& op) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
     const int slot = c & 3;
@@ -590,6 +609,9 @@ __device__ __forceinline__ void iso_seg2(IsoState<DK, NCW>& st, const SegCarry<N
         }
         orow += ostep;
     }
+    // the next chunk's k and q operands (its tiles landed iterations ago;
+    // their ring slot is not reused before the next chunk is done)
+    if (c + 1 < nchunks) iso_ops_load<DK>(op, sm, c + 1);
     // S~ <- cin S~ + K^T diag(w') Dn  (cin = 1 unless the frame is renormalised)
     if (cin != 1.f) {
 #pragma unroll
@@ -733,6 +755,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         const int n = lane & 15, g4 = (lane >> 4) * 4;
         IsoState<DK, NCW> st;
         SegCarry<NCW> cy;
+        StateOps<DK> op;  // k and q operands of the next state chunk
         const size_t sbase = size_t(unit) * DK * a.DV;
 #pragma unroll
         for (int j = 0; j < NCW; ++j)
@@ -761,8 +784,9 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
                 if (i >= 5) vm_wait<2 * NS + 2 * NV>();
                 else if (i == 4) vm_wait<NS + 2 * NV>();
                 else vm_wait<2 * NV>();
-                iso_seg1<DK, NCW, GATE>(st, cy, sm, c, sw_);
-                iso_seg2<DK, NCW>(st, cy, sm, a, h, col0, c);
+                if (c == 0) iso_ops_load<DK>(op, sm, 0);
+                iso_seg1<DK, NCW, GATE>(st, cy, sm, c, sw_, op);
+                iso_seg2<DK, NCW>(st, cy, sm, a, h, col0, c, nchunks, op);
             }
             bar();
         }
