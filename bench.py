@@ -302,7 +302,9 @@ def backward_call(kdn, w, dev, gated=False):
                          dtype=torch.uint8, device=dev)
         call = lambda: kdn.backward_gated(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
     else:
-        ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+        # the smallest workspace kdn_backward accepts for this variant and dtype
+        ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.variant, t["q"].dtype),
+                         dtype=torch.uint8, device=dev)
         call = lambda: kdn.backward(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
     return call, ws
 

@@ -321,9 +321,14 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
  *   dc0   [H]          float output, may be NULL: the sum of dp0 over the
  *                      batch and the channels, which is the gradient with
  *                      respect to c0 when p0 is NULL
- *   workspace          device memory of at least kdn_backward_workspace_size()
- *                      bytes, 16-byte aligned (the recomputation checkpoints);
- *                      its contents on entry do not matter
+ *   workspace          device memory of at least
+ *                      kdn_backward_workspace_size_for(variant, dtype, ...)
+ *                      bytes, 16-byte aligned (the recomputation checkpoints
+ *                      and per-token sums); its contents on entry do not
+ *                      matter.  A larger workspace lets the chunked path take
+ *                      longer slabs of tokens (fewer launches) and the token
+ *                      path more pairs at once; the results do not depend on
+ *                      its size
  *
  * S0, dS_T, dS0 and dv must be 8-byte aligned (KDN_ERR_UNSUPPORTED
  * otherwise) and the workspace 16-byte aligned (KDN_ERR_WORKSPACE).  No output may overlap
@@ -331,10 +336,14 @@ int kdn_step(const void* q, const void* k, const void* v, const void* alpha, con
  * variant with bf16 inputs and 16-byte aligned q, k, v, alpha, omega and dO
  * runs its memory adjoint in chunk form on the matrix cores (bf16 operands,
  * fp32 accumulation and state), after a checkpoint sweep of the chunked
- * forward; (batch, head) pairs whose decays leave the chunked form's range
- * take the token recurrence's adjoint, as do the other variants and fp32
- * inputs (fp32 throughout).  Calls are asynchronous on `stream` like
- * kdn_forward, and the results are bitwise repeatable.
+ * forward.  That sweep keeps the chunk-start states in bf16 (the precision in
+ * which the adjoint's products take them), and the adjoint runs over slabs of
+ * tokens from the last, so that its per-token buffers hold one slab.
+ * (Batch, head) pairs whose decays leave the chunked form's range take the
+ * token recurrence's adjoint, as do the other variants and fp32 inputs (fp32
+ * throughout); on the chunked path's workspace it takes the pairs in rounds
+ * of as many as fit.  Calls are asynchronous on `stream` like kdn_forward,
+ * and the results are bitwise repeatable.
  */
 int kdn_backward(const void* q, const void* k, const void* v, const void* alpha, const void* omega,
                  const void* r, const float* c0, float mu, int variant, int dtype, int B, int T,
@@ -350,9 +359,8 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
  * place.  Each device holds its own copy of the scratch from the library's
  * loading on that device until the process ends.  Same arguments (minus the
  * workspace), checks, kernels and results (bit for bit) as kdn_backward.
- *  - Sizes whose workspace (kdn_backward_workspace_size) exceeds the scratch
- *    return KDN_ERR_WORKSPACE and launch nothing (dk = dv = 128, H = 16, B = 1:
- *    T up to 1974; B = 2: T up to 839).
+ *  - Sizes whose workspace (kdn_backward_workspace_size_for) exceeds the
+ *    scratch return KDN_ERR_WORKSPACE and launch nothing.
  *  - Nothing is allocated: no hipMalloc, hipFree or allocating library call.
  *  - Every call on one device shares that device's scratch and leaves its
  *    contents behind (the kernels need none on entry).  Calls that overlap in
@@ -367,11 +375,24 @@ int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void
                          float* dalpha, float* domega, float* dr, float* dS0, float* dp0, float* dc0,
                          void* stream);
 
-/* Workspace bytes kdn_backward needs for these sizes (0 when B*H*T == 0):
- * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4 + B*H*4
- * (recomputation checkpoints per 64-column tile, plus per-token partial sums
- * and uncertainties per tile, plus one range flag per (batch, head) pair). */
+/* Workspace bytes with which kdn_backward runs every variant and dtype at
+ * these sizes with all (batch, head) pairs at once (0 when B*H*T == 0):
+ * B*H*(dv/64)*(ceil(T/32)*(64*dk + 8*dk) + 32*64*dk + 5*T*dk)*4 plus B*H*4
+ * rounded up to 256 (the token path's checkpoints and stash per 64-column
+ * tile, its per-token partial sums and uncertainties per tile, and one range
+ * flag per (batch, head) pair). */
 size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv);
+/* The smallest workspace kdn_backward accepts for this variant and dtype
+ * (0 when B*H*T == 0).  For KDN_DIAGONAL with bf16 inputs and dk, dv in
+ * {64, 128}, the chunked path's: with U = B*H pairs, n = ceil(T/32) chunks
+ * and a slab of S = min(32*n, max(512, 65536/U rounded up to 512)) tokens,
+ * about U*(dv/64)*n*dk*128 (bf16 chunk-start states) + U*n*dk*4 (chunk-start
+ * uncertainties) + U*T*32 (per-token sums) + U*dk*dv*4 (the state's
+ * cotangent between slabs) + U*S*dk*(dv/4 + 4) (one slab's tile sums and
+ * uncertainties) bytes, each region rounded up to 256, and never less than
+ * the flags plus one pair's token-path workspace (0.874 GB at B=8, T=4096,
+ * H=16, dk=dv=128).  Otherwise kdn_backward_workspace_size(). */
+size_t kdn_backward_workspace_size_for(int variant, int dtype, int B, int T, int H, int dk, int dv);
 int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
                           const void* omega, const void* r, const float* c0, float mu, int variant,
                           int dtype, int B, int T, int H, int dk, int dv, const float* S0,

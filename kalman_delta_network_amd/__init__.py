@@ -53,7 +53,7 @@ SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward
            "kdn_backward_gated_workspace_size", "kdn_backward_noalloc", "kdn_forward_split",
            "kdn_forward_split_segments", "kdn_forward_split_workspace_size", "kdn_validate_forward_split",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated",
-           "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size",
+           "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size", "kdn_backward_workspace_size_for",
            "kdn_validate_backward", "kdn_status_string", "kdn_last_error", "kdn_version")
 
 _lib = None
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_validate_backward.argtypes = bwd + [P, ctypes.c_size_t]
     lib.kdn_backward_workspace_size.argtypes = [I, I, I, I, I]
     lib.kdn_backward_workspace_size.restype = ctypes.c_size_t
+    lib.kdn_backward_workspace_size_for.argtypes = [I, I, I, I, I, I, I]
+    lib.kdn_backward_workspace_size_for.restype = ctypes.c_size_t
     lib.kdn_backward_gated.argtypes = bwd + [P, ctypes.c_size_t, P]
     lib.kdn_backward_noalloc.argtypes = bwd + [P]
     lib.kdn_backward_gated_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -446,9 +448,17 @@ def forward_varlen_gated(q, k, v, z_alpha, z_omega, z_r, c0, cu_seqlens, mu, var
     return o, S_T, p_T
 
 
-def backward_workspace_size(B, T, H, dk, dv) -> int:
-    """Bytes of device workspace kdn_backward needs for these sizes."""
-    return int(load_library().kdn_backward_workspace_size(B, T, H, dk, dv))
+def backward_workspace_size(B, T, H, dk, dv, variant=None, dtype=None) -> int:
+    """Bytes of device workspace for kdn_backward at these sizes: with
+    ``variant`` and ``dtype`` (a torch dtype), the smallest it accepts for
+    them (kdn_backward_workspace_size_for); without, the size that serves
+    every variant and dtype with all pairs at once."""
+    lib = load_library()
+    if variant is None:
+        return int(lib.kdn_backward_workspace_size(B, T, H, dk, dv))
+    torch = _torch()
+    code = {torch.bfloat16: KDN_BF16, torch.float32: KDN_F32}[dtype]
+    return int(lib.kdn_backward_workspace_size_for(VARIANTS[variant], code, B, T, H, dk, dv))
 
 
 def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
@@ -459,7 +469,8 @@ def backward(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=None, va
     Inputs as ``forward``; dO [B,T,H,dv] in the input dtype, dS_T
     [B,H,dk,dv] and dp_T [B,H,dk] (isotropic forms [B,H]) float32; any of the
     three may be None (zero).  ``workspace``: a uint8 device tensor of at
-    least backward_workspace_size() bytes, or None to allocate one.
+    least backward_workspace_size(..., variant, q.dtype) bytes, or None to
+    allocate that many.
     Returns a dict of float32 tensors dq, dk, dv, dalpha, domega, dr (input
     layouts), dS0, dp0 and dc0 [H] (sum of dp0 over batch and channels).
     """
@@ -536,7 +547,8 @@ def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0,
             *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dp0", "dc0")), _stream(dev))
         _check(st, "kdn_backward_noalloc")
         return g
-    need = backward_gated_workspace_size(B, T, H, dk, dv, variant) if gated else backward_workspace_size(B, T, H, dk, dv)
+    need = (backward_gated_workspace_size(B, T, H, dk, dv, variant) if gated
+            else backward_workspace_size(B, T, H, dk, dv, variant, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fn = lib.kdn_backward_gated if gated else lib.kdn_backward

@@ -199,7 +199,7 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     if (gated && variant == KDN_DIAGONAL_GROUPED)
         return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
     const size_t need = gated ? kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv)
-                              : kdn::backward_workspace_bytes(B, T, H, dk, dv);
+                              : kdn::backward_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
     if (need > 0 && (!work || work_bytes < need))
         return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, work_bytes);
     const auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
@@ -485,6 +485,11 @@ size_t kdn_backward_workspace_size(int B, int T, int H, int dk, int dv) {
     return kdn::backward_workspace_bytes(B, T, H, dk, dv);
 }
 
+size_t kdn_backward_workspace_size_for(int variant, int dtype, int B, int T, int H, int dk, int dv) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
+    return kdn::backward_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
+}
+
 int kdn_validate_backward(const void* q, const void* k, const void* v, const void* alpha,
                           const void* omega, const void* r, const float* c0, float mu, int variant,
                           int dtype, int B, int T, int H, int dk, int dv, const float* S0,
@@ -512,7 +517,7 @@ int kdn_backward(const void* q, const void* k, const void* v, const void* alpha,
     if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
     const kdn::BwdArgs a{q, k, v, alpha, omega, r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, dO, dS_T,
                          dp_T, dq, dk_out, dv_out, dalpha, domega, dr, dS0, dp0, dc0,
-                         static_cast<float*>(workspace)};
+                         static_cast<float*>(workspace), workspace_bytes};
     return hip_status(kdn::launch_backward(a, static_cast<hipStream_t>(stream)), "backward");
 }
 
@@ -526,7 +531,7 @@ int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void
     int st = validate_common(variant, dtype, mu, dk, dv);
     if (st != KDN_OK) return st;
     if (B < 0 || T < 0 || H < 0) return fail(KDN_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
-    const size_t need = kdn::backward_workspace_bytes(B, T, H, dk, dv);
+    const size_t need = kdn::backward_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
     if (need > kdn::kNoallocScratchBytes)
         return fail(KDN_ERR_WORKSPACE,
                     "kdn_backward_noalloc: these sizes need %zu bytes of workspace, more than the %zu-byte static "
@@ -560,7 +565,7 @@ int kdn_backward_gated(const void* q, const void* k, const void* v, const void* 
     if (fault_launch()) return fail(KDN_ERR_HIP, "launch suppressed by KDN_FAULT=launch");
     const kdn::BwdArgs a{q, k, v, z_alpha, z_omega, z_r, c0, mu, variant, dtype, B, T, H, dk, dv, S0, p0, dO, dS_T,
                          dp_T, dq, dk_out, dv_out, dz_alpha, dz_omega, dz_r, dS0, dp0, dc0,
-                         static_cast<float*>(workspace)};
+                         static_cast<float*>(workspace), workspace_bytes};
     return hip_status(kdn::launch_backward_gated(a, static_cast<hipStream_t>(stream)), "gated backward");
 }
 

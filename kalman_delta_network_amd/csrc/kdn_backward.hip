@@ -39,6 +39,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstddef>
 #include <cstdint>
 
 namespace kdn {
@@ -325,8 +327,13 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     __shared__ BwdSmem<DK, TILE> sm;
 
     const int nunit = A.B * A.H;
-    const int tile = int(blockIdx.x) / nunit;  // the tiles of one head are nunit blocks apart
-    const int unit = int(blockIdx.x) % nunit;
+    // this round's pairs slot0 .. slot0 + nslot - 1, pair slot0 + s in workspace slot s
+    // (wslot; not the LDS ring's slot of the reverse walk below)
+    const int nslot = A.nslot ? A.nslot : nunit;
+    const int tile = int(blockIdx.x) / nslot;  // the tiles of one head are nslot blocks apart
+    const int wslot = int(blockIdx.x) % nslot;
+    const int unit = A.slot0 + wslot;
+    if (unit >= nunit) return;
     if (A.only_flagged && !A.only_flagged[unit]) return;  // the chunked adjoint took this pair
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
@@ -340,14 +347,14 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
     const int nseg = (T + SEG - 1) / SEG;
     const float mu = A.mu;
 
-    float* ckS = A.work + (size_t(unit) * NTILE + tile) * unit_floats(T, DK, TILE);
+    float* ckS = A.work + (size_t(wslot) * NTILE + tile) * unit_floats(T, DK, TILE);
     float* ckP = ckS + size_t(nseg) * DK * TILE;
     // memory snapshots as float4 (m, m + 1) row pairs, see snap_idx
     float4* stash = reinterpret_cast<float4*>(ckP + size_t(nseg) * NW * DK);
     float4* ckS4 = reinterpret_cast<float4*>(ckS);
     constexpr int SNAP = NT * (RPT / SG);  // float4 per snapshot
-    float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);  // [unit][T][NTILE][4][DK]
-    float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;                    // [unit][T][NTILE][DK]
+    float* partial = A.work + size_t(nslot) * NTILE * unit_floats(T, DK, TILE);  // [wslot][T][NTILE][4][DK]
+    float* pbuf = partial + size_t(nslot) * T * NTILE * 4 * DK;                    // [wslot][T][NTILE][DK]
     const size_t sbase = size_t(unit) * DK * DV;
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
 
@@ -439,7 +446,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
             const bool rec_p = rec && (GR || tile == 0);  // p_{t-1} of each group
             const auto run = [&](const TokIn<DK, VAR, Tin>& x, int tt) {
                 fwd_token<DK, TILE, VAR, Tin>(x, S, p, pb, mu, sm.chan[wave], rec ? sm.seg_chan[tt] : nullptr,
-                                              rec_p ? pbuf + ((size_t(unit) * T + t0 + tt) * NTILE + tile) * DK : nullptr,
+                                              rec_p ? pbuf + ((size_t(wslot) * T + t0 + tt) * NTILE + tile) * DK : nullptr,
                                               stash + size_t(tt) * SNAP, lane, rg, tid);
             };
             const auto ld = [&](TokIn<DK, VAR, Tin>& x, int tt) {
@@ -486,7 +493,7 @@ __global__ void __launch_bounds__(TILE / WCOLS * 64) kdn_backward_mem_kernel(Bwd
         const auto iter = [&](int it, const RevIn& cur, RevIn& ahead) {
             if (it >= 1 && wave < 4) {
                 const int slot = (it - 1) & 1;
-                float* dst = partial + ((size_t(unit) * T + t0 + n - it) * NTILE + tile) * 4 * DK + size_t(wave) * DK;
+                float* dst = partial + ((size_t(wslot) * T + t0 + n - it) * NTILE + tile) * 4 * DK + size_t(wave) * DK;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const int i = lane + 64 * c;
@@ -612,15 +619,18 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
     constexpr int CPL = DK / 64;
     constexpr bool ISO = VAR != 0;
     const int nunit = A.B * A.H;
-    const int unit = int(blockIdx.x);
+    const int nslot = A.nslot ? A.nslot : nunit;
+    const int wslot = int(blockIdx.x);
+    const int unit = A.slot0 + wslot;
+    if (unit >= nunit) return;
     if (A.only_flagged && !A.only_flagged[unit]) return;  // the chunked path's adjoint took this pair
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
     const int lane = threadIdx.x;
     const float mu = A.mu;
-    const float* partial = A.work + size_t(nunit) * NTILE * unit_floats(T, DK, TILE);
-    const float* pbuf = partial + size_t(nunit) * T * NTILE * 4 * DK;
+    const float* partial = A.work + size_t(nslot) * NTILE * unit_floats(T, DK, TILE);
+    const float* pbuf = partial + size_t(nslot) * T * NTILE * 4 * DK;
     const Tin* kin = static_cast<const Tin*>(A.k);
     const Tin* ain = static_cast<const Tin*>(A.alpha);
     const Tin* omg = static_cast<const Tin*>(A.omega);
@@ -644,7 +654,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
     };
     const auto load = [&](UncIn& u, int t) {
         const size_t tok = tokidx(t);
-        const float* src = partial + (size_t(unit) * T + t) * NTILE * 4 * DK;
+        const float* src = partial + (size_t(wslot) * T + t) * NTILE * 4 * DK;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int i = lane + 64 * c;
@@ -658,7 +668,7 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_kernel(BwdArgs A) {
             }
             u.al[c] = VAR == 1 ? ain[tok] : ain[tok * DK + i];
             u.kk[c] = kin[tok * DK + i];
-            u.pp[c] = ISO ? pbuf[(size_t(unit) * T + t) * NTILE * DK] : pbuf[(size_t(unit) * T + t) * NTILE * DK + i];
+            u.pp[c] = ISO ? pbuf[(size_t(wslot) * T + t) * NTILE * DK] : pbuf[(size_t(wslot) * T + t) * NTILE * DK + i];
             u.w[c] = VAR == 0 ? omg[tok * DK + i] : omg[tok];
         }
         u.r = rr[tok];
@@ -786,14 +796,17 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_grouped_kernel(BwdArgs A)
     constexpr int G = DV / TILE;
     constexpr int CPL = DK / 64;
     const int nunit = A.B * A.H;
-    const int unit = int(blockIdx.x);
+    const int nslot = A.nslot ? A.nslot : nunit;
+    const int wslot = int(blockIdx.x);
+    const int unit = A.slot0 + wslot;
+    if (unit >= nunit) return;
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
     const int lane = threadIdx.x;
     const float mu = A.mu;
-    const float* partial = A.work + size_t(nunit) * G * unit_floats(T, DK, TILE);
-    const float* pbuf = partial + size_t(nunit) * T * G * 4 * DK;
+    const float* partial = A.work + size_t(nslot) * G * unit_floats(T, DK, TILE);
+    const float* pbuf = partial + size_t(nslot) * T * G * 4 * DK;
     const Tin* kin = static_cast<const Tin*>(A.k);
     const Tin* ain = static_cast<const Tin*>(A.alpha);
     const Tin* omg = static_cast<const Tin*>(A.omega);
@@ -813,8 +826,8 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_grouped_kernel(BwdArgs A)
     };
     const auto load = [&](UncG& u, int t) {
         const size_t tok = tokidx(t);
-        const float* src = partial + (size_t(unit) * T + t) * G * 4 * DK;
-        const float* ps = pbuf + (size_t(unit) * T + t) * G * DK;
+        const float* src = partial + (size_t(wslot) * T + t) * G * 4 * DK;
+        const float* ps = pbuf + (size_t(wslot) * T + t) * G * DK;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int i = lane + 64 * c;
@@ -923,15 +936,36 @@ __global__ void __launch_bounds__(64) kdn_dc0_kernel(const float* __restrict__ d
     if (lane == 0) dc0[h] = acc;
 }
 
+// The token path in rounds of as many pairs as the workspace from a.work
+// holds (every pair at once with backward_workspace_bytes()).
+template <typename F>
+hipError_t in_rounds(const BwdArgs& a, F&& launch) {
+    const int units = a.B * a.H;
+    const size_t per = token_pair_bytes(a.T, a.dk, a.dv);
+    // (T = 0 touches no workspace: the cotangents pass straight through)
+    const int k = a.T == 0 ? units : int(std::min<size_t>(size_t(units), a.work_bytes / per));
+    if (k < 1) return hipErrorInvalidValue;
+    BwdArgs r = a;
+    r.nslot = k;
+    for (int s0 = 0; s0 < units; s0 += k) {
+        r.slot0 = s0;
+        const hipError_t e = launch(r);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int DK, int DV, int VAR, typename Tin>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const unsigned units = unsigned(long(a.B) * a.H);
-    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, VAR, Tin>), dim3(units * (DV / TILE)), dim3(TILE / WCOLS * 64), 0,
-                       stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kdn_backward_unc_kernel<DK, DV, VAR, Tin>), dim3(units), dim3(64), 0, stream, a);
-    return hipGetLastError();
+    return in_rounds(a, [&](const BwdArgs& r) {
+        const unsigned n = unsigned(r.nslot);
+        hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, VAR, Tin>), dim3(n * (DV / TILE)), dim3(TILE / WCOLS * 64), 0,
+                           stream, r);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kdn_backward_unc_kernel<DK, DV, VAR, Tin>), dim3(n), dim3(64), 0, stream, r);
+        return hipGetLastError();
+    });
 }
 
 template <int DK, int DV, int VAR>
@@ -941,51 +975,53 @@ hipError_t launch_dtype(const BwdArgs& a, hipStream_t s) {
 
 template <int DK, int DV, typename Tin>
 hipError_t launch_grouped_t(const BwdArgs& a, hipStream_t stream) {
-    const unsigned units = unsigned(long(a.B) * a.H);
-    hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, 0, Tin, true>), dim3(units * (DV / TILE)),
-                       dim3(TILE / WCOLS * 64), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kdn_backward_unc_grouped_kernel<DK, DV, Tin>), dim3(units), dim3(64), 0, stream, a);
-    return hipGetLastError();
+    return in_rounds(a, [&](const BwdArgs& r) {
+        const unsigned n = unsigned(r.nslot);
+        hipLaunchKernelGGL((kdn_backward_mem_kernel<DK, DV, 0, Tin, true>), dim3(n * (DV / TILE)),
+                           dim3(TILE / WCOLS * 64), 0, stream, r);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kdn_backward_unc_grouped_kernel<DK, DV, Tin>), dim3(n), dim3(64), 0, stream, r);
+        return hipGetLastError();
+    });
 }
 
-// floats before the per-pair flags of the chunked path
-size_t flag_offset(int B, int T, int H, int dk, int dv) {
-    const size_t units = size_t(B) * size_t(H), ntile = size_t(dv) / TILE;
-    // per (unit, tile) checkpoints and stash; per token the tile sums and p_{t-1} (per tile)
-    return units * ntile * unit_floats(T, dk, TILE) + units * size_t(T) * ntile * 5 * dk;
+// The chunked path for the diagonal bf16 form, in two parts, on the
+// workspace layout of ChunkWs.  main: the chunked forward's checkpoint sweep
+// (chunk-start states in bf16 and uncertainties, one range flag per (batch,
+// head) pair), then per slab of tokens, from the last, the chunked memory
+// adjoint (kdn_backward_chunk.hip) and the uncertainty adjoint of the
+// unflagged pairs, carrying dS and dp from slab to slab; then dr.
+// fallback: the token path with fb's arguments (a itself, or for the gated
+// layer its fp32 copies of the gated values) for the flagged pairs, in
+// rounds over the workspace after the flags.
+ChunkWs chunk_layout(const BwdArgs& a) {
+    ChunkWs w{};
+    chunk_workspace(a.B, a.T, a.H, a.dk, a.dv, a.work, a.work_bytes, &w);
+    return w;
 }
-
-// The chunked memory adjoint (kdn_backward_chunk.hip) for the diagonal bf16
-// form: the chunked forward's checkpoint sweep (chunk-start states and
-// uncertainties into the per-(unit, tile) checkpoint regions, one range flag
-// per (batch, head) pair), the chunked adjoint of the unflagged pairs, the
-// recurrent memory adjoint of the flagged ones, then the uncertainty adjoint
-// of all.  Both memory adjoints leave the same per-token tile sums.
-// The chunked path in two parts.  main: the checkpoint sweep (which flags the
-// pairs outside the chunked range) and the chunked adjoints of the others.
-// fallback: the token path with fb's arguments for the flagged pairs (fb is a
-// itself, or for the gated layer its fp32 copies of the gated values).
-int* chunk_flags(const BwdArgs& a) { return reinterpret_cast<int*>(a.work + flag_offset(a.B, a.T, a.H, a.dk, a.dv)); }
 
 hipError_t chunked_main(const BwdArgs& a, hipStream_t s) {
-    const size_t uf = unit_floats(a.T, a.dk, TILE);
-    int* flag = chunk_flags(a);
+    ChunkWs w{};
+    if (!chunk_workspace(a.B, a.T, a.H, a.dk, a.dv, a.work, a.work_bytes, &w)) return hipErrorInvalidValue;
     FwdArgs f{a.q, a.k, a.v, a.alpha, a.omega, a.r, a.c0, a.mu, 0, 1, a.B, a.T, a.H, a.dk, a.dv,
               a.S0, a.p0, nullptr, nullptr, nullptr};
     f.gates = a.gates;
-    hipError_t e = launch_chunked_checkpoints(f, a.work, uf, flag, s);
-    if (e != hipSuccess) return e;
-    e = launch_backward_chunk(a, uf, flag, s);
-    if (e != hipSuccess) return e;
-    return launch_backward_unc_chunk(a, uf, flag, s);
+    hipError_t e = launch_chunked_checkpoints(f, w.cks, w.ckp, w.flag, s);
+    for (int j = w.nslab - 1; j >= 0 && e == hipSuccess; --j) {
+        e = launch_backward_chunk(a, w, j, s);
+        if (e == hipSuccess) e = launch_backward_unc_chunk(a, w, j, s);
+    }
+    return e != hipSuccess ? e : launch_backward_dr(a, w, s);
 }
 
 template <int DK, int DV>
 hipError_t chunked_fallback(const BwdArgs& a, const BwdArgs& fb, hipStream_t s) {
+    const ChunkWs w = chunk_layout(a);
     BwdArgs r = fb;
-    r.only_flagged = chunk_flags(a);
+    r.only_flagged = w.flag;
+    r.work = reinterpret_cast<float*>(w.rest);
+    r.work_bytes = w.rest_bytes;
     r.gates = false;
     return fb.dtype == 1 ? launch_t<DK, DV, 0, bf16_t>(r, s) : launch_t<DK, DV, 0, float>(r, s);
 }
@@ -1015,17 +1051,35 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t token_pair_bytes(int T, int dk, int dv) {
+    const size_t ntile = size_t(dv) / TILE;
+    // per tile checkpoints and stash; per token the tile sums and p_{t-1} (per tile)
+    return (ntile * unit_floats(T, dk, TILE) + size_t(T) * ntile * 5 * dk) * sizeof(float);
+}
+
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (long(B) * H == 0 || T == 0) return 0;
-    // then one range flag per (batch, head) pair for the chunked path
-    return flag_offset(B, T, H, dk, dv) * sizeof(float) + size_t(B) * size_t(H) * sizeof(int);
+    // every pair on the token path at once, plus the chunked path's range
+    // flags (its layout fits in this size: bf16 checkpoints, longer slabs)
+    const size_t units = size_t(B) * size_t(H);
+    return units * token_pair_bytes(T, dk, dv) + ((units * sizeof(int) + 255) & ~size_t(255));
+}
+
+size_t backward_workspace_bytes_for(int variant, int dtype, int B, int T, int H, int dk, int dv) {
+    if (long(B) * H == 0 || T == 0) return 0;
+    const bool chunked = variant == 0 && dtype == 1 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    if (!chunked) return backward_workspace_bytes(B, T, H, dk, dv);
+    // the chunked layout, and room after the flags for one pair on the token
+    // path (pairs outside the chunked range, or inputs it cannot take)
+    const size_t flags = ((size_t(B) * size_t(H) * sizeof(int)) + 255) & ~size_t(255);
+    return std::max(chunk_workspace_min_bytes(B, T, H, dk, dv), flags + token_pair_bytes(T, dk, dv));
 }
 
 bool backward_chunked_eligible(const BwdArgs& a) {
     return (a.dk == 128 || a.dk == 64) && (a.dv == 128 || a.dv == 64) && chunk_path(a);
 }
 
-int* backward_chunk_flags(const BwdArgs& a) { return chunk_flags(a); }
+int* backward_chunk_flags(const BwdArgs& a) { return chunk_layout(a).flag; }
 
 hipError_t launch_backward_chunked_main(const BwdArgs& a, hipStream_t stream) { return chunked_main(a, stream); }
 

@@ -43,6 +43,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <type_traits>
@@ -177,13 +178,19 @@ constexpr f4 kZero = {0.f, 0.f, 0.f, 0.f};
 
 // One chunk's inputs as each thread loads them, one chunk ahead: its 16-byte
 // piece of the raw k, q, alpha, omega tiles and of the v and dO tiles, r
-// (threads < 32) and (state waves) its 16 entries of the checkpoint Sg.
+// (threads < 32) and (state waves) its 16 entries of the checkpoint Sg
+// (bf16, four rows of a column in each u2).
 struct Pre {
     u4 kqaw[4];
     u4 v, d;
     bf16_t r;
-    f4 sg[4];
+    u2 sg[4];
 };
+
+__device__ __forceinline__ f4 unpack4(u2 x) {
+    return f4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u), __uint_as_float(x[1] << 16),
+              __uint_as_float(x[1] & 0xffff0000u)};
+}
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -192,7 +199,7 @@ struct Pre {
 // them (alpha = sigmoid(z), omega = softplus(z), r = r_min + softplus(z), q
 // and k divided by their norms over the d_k channels)
 template <int DK, bool GATE>
-__global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
+__global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, ChunkWs W, int c_lo, int c_hi) {
     constexpr int NT = DK / 16;     // 16-row tiles of the key dimension (state waves)
     constexpr int NCW = DK / 64;    // chain waves
     __shared__ CSmem<DK> sm;
@@ -200,7 +207,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
     const int ntile = A.dv / TILE;
     const int tile = int(blockIdx.x) / nunit;
     const int unit = int(blockIdx.x) % nunit;
-    if (flag[unit]) return;  // the recurrent memory adjoint takes this pair
+    if (W.flag[unit]) return;  // the recurrent memory adjoint takes this pair
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
@@ -217,27 +224,31 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
     const bf16_t* win = static_cast<const bf16_t*>(A.omega);
     const bf16_t* rin = static_cast<const bf16_t*>(A.r);
     const bf16_t* doin = static_cast<const bf16_t*>(A.dO);
-    float* ckw = A.work + (size_t(unit) * ntile + tile) * ck_floats;  // [chunk][DK / 4][64][4]
-    const float* ck = ckw;
-    const float* ckp = A.work + size_t(unit) * ntile * ck_floats + size_t(nchunks) * DK * TILE;  // [chunk][DK]
-    float* partial = A.work + size_t(nunit) * ntile * ck_floats;  // [unit][T][ntile][4][DK]
-    float* pbuf = partial + size_t(nunit) * T * ntile * 4 * DK;   // [unit][T][ntile][DK]
+    const bf16_t* ck = W.cks + (size_t(unit) * ntile + tile) * nchunks * DK * TILE;  // [chunk][DK / 4][64][4]
+    const float* ckp = W.ckp + size_t(unit) * nchunks * DK;                          // [chunk][DK]
+    const int tb = c_lo * L;  // the slab's first token
+    // the slab's per-token buffers, token t at row t - tb: [unit][slab][ntile][4][DK], [unit][slab][DK]
+    float* partial = W.partial + size_t(unit) * W.slab * ntile * 4 * DK;
+    float* pbuf = W.pbuf + size_t(unit) * W.slab * DK;
+    float* tsc = W.tsc + size_t(unit) * T * 8;  // [T][8] per-token sums
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
 
     // the upper 8 x 8 corner of each inverse block is zero (block_inverse
     // writes the rest)
     for (int e = threadIdx.x; e < 2 * 64; e += NTH) sm.Td[(e >> 6) * 256 + ((e >> 3) & 7) * 16 + 8 + (e & 7)] = 0;
 
-    // the cotangent of the state, key rows 16 wave + 4 (l / 16) + e, columns 16 ct + l % 16
+    // the cotangent of the state, key rows 16 wave + 4 (l / 16) + e, columns 16
+    // ct + l % 16: dS_T at the last slab, else what the later slab left
     const bool stw = wave < NT;
+    const float* dsi = c_hi == nchunks ? A.dS_T : W.dsc;
     f4 dS[4], Sg[4], Sm[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         dS[ct] = kZero;
-        if (stw && A.dS_T)
+        if (stw && dsi)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                dS[ct][e] = A.dS_T[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n];
+                dS[ct][e] = dsi[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n];
     }
 
     Pre pre;
@@ -266,14 +277,14 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
         if (tid < L) pre.r = rin[tokidx(t0 + min(tid, last))];
         if (stw) {
             // [DK / 4][64][4]: rows 4 (l / 16) .. + 3 of the wave's 16 in one load
-            const f4* ckc = reinterpret_cast<const f4*>(ck + size_t(c) * DK * TILE);
+            const u2* ckc = reinterpret_cast<const u2*>(ck + size_t(c) * DK * TILE);
             const int ln = threadIdx.x & 63;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) pre.sg[ct] = ckc[(4 * wave + (ln >> 4)) * TILE + 16 * ct + (ln & 15)];
         }
     };
-    load(nchunks - 1);
-    for (int c = nchunks - 1; c >= 0; --c) {
+    load(c_hi - 1);
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int lane = lane_id();  // (see lane_id)
         const int n = lane & 15, g4 = 4 * (lane >> 4);
         const int t0 = c * L;
@@ -307,10 +318,10 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 sm.cr[tid] = mu / rt;
             }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) Sg[ct] = pre.sg[ct];
+            for (int ct = 0; ct < 4; ++ct) Sg[ct] = unpack4(pre.sg[ct]);
         }
         bar();
-        if (c > 0) load(c - 1);  // the next chunk's inputs, in flight during this one
+        if (c > c_lo) load(c - 1);  // the next chunk's inputs, in flight during this one
         if constexpr (GATE) {
             // |k_t|^2 and |q_t|^2, a wave covering 64 channels of one token per step
 #pragma unroll 1
@@ -415,7 +426,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int t = 8 * b8i + j;
-                        if (!MASK || t < nvalid) __builtin_nontemporal_store(pv[j], &pbuf[((size_t(unit) * T + t0 + t) * ntile) * DK + i]);
+                        if (!MASK || t < nvalid) __builtin_nontemporal_store(pv[j], &pbuf[size_t(t0 - tb + t) * DK + i]);
                     }
                 asm volatile("" ::: "memory");  // one group at a time
             }
@@ -656,7 +667,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                     uv[e] = dkap * kp;
                     sm.kap[tl * DK + i] = fmaf(dkc, kk, fmaf(dq, qq, -dkapc * kp));  // w = d rho . rho
                     if (tl < nvalid) {
-                        float* dst = partial + ((size_t(unit) * T + t0 + tl) * ntile + tile) * 4 * DK + i;
+                        float* dst = partial + (size_t(t0 - tb + tl) * ntile + tile) * 4 * DK + i;
                         __builtin_nontemporal_store(dq, &dst[0]);
                         __builtin_nontemporal_store(dkap, &dst[DK]);
                         __builtin_nontemporal_store(fmaf(-kp, drt, dkc), &dst[2 * DK]);
@@ -670,21 +681,21 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
                 }
             }
             bar();
-            if (wave == NT - 1 && lane < HL) {
-                // the uncertainty adjoint's per-token sums go into this
-                // chunk's checkpoint slot (read already): u_t of this tile at
-                // [t]; tile 0 also d_t = r_t + sum_i p_hat k^2 at [L + t]
+            if (wave == NT - 1 && lane < HL && th + lane < nvalid) {
+                // the uncertainty adjoint's per-token sums: u_t of this tile
+                // at [tile]; tile 0 also d_t = r_t + sum_i p_hat k^2 at [2]
+                // and (gated) 1 / |k_t| at [6]
                 float u = 0.f;
 #pragma unroll
                 for (int w2 = 0; w2 < NT; ++w2) u += sm.uacc[w2][th + lane];
-                float* slot = ckw + size_t(c) * DK * TILE;
-                slot[th + lane] = u;
+                float* ts = tsc + size_t(t0 + th + lane) * 8;
+                ts[tile] = u;
                 if (tile == 0) {
                     float sk = sm.r[th + lane];
 #pragma unroll
                     for (int w2 = 0; w2 < DK / 64; ++w2) sk += sm.spart[th + lane][w2];
-                    slot[L + th + lane] = sk;
-                    if (GATE) slot[5 * L + th + lane] = sm.skv[th + lane];  // 1 / |k_t|
+                    ts[2] = sk;
+                    if (GATE) ts[6] = sm.skv[th + lane];
                 }
             }
             if (half == 1) {
@@ -704,7 +715,7 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
             constexpr bool MASK = decltype(maskc)::value;
             const int i = 64 * wave + lane;
             const float fa = sm.dGA[i] * sm.GA[i], fb = sm.dGB[i] * sm.GB[i];
-            float* dst = partial + ((size_t(unit) * T + t0) * ntile + tile) * 4 * DK + 3 * DK + i;
+            float* dst = partial + (size_t(t0 - tb) * ntile + tile) * 4 * DK + 3 * DK + i;
             const size_t tstep = size_t(ntile) * 4 * DK;
             // u <= 15: -sum_{t<u} w_t + fa;  u >= 16: sum_{t>=u} w_t + fb
 #pragma unroll
@@ -741,13 +752,15 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
         }
         bar();
     }
-    // dS0
-    if (stw && A.dS0)
+    // dS0 after the first slab, else the cotangent the earlier slab starts from
+    // (each workgroup reads its own part of it at its start, then writes it)
+    float* dso = c_lo == 0 ? A.dS0 : W.dsc;
+    if (stw && dso)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                A.dS0[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n] = dS[ct][e];
+                dso[(size_t(unit) * DK + 16 * wave + g4 + e) * DV + tile * TILE + 16 * ct + n] = dS[ct][e];
 }
 
 // ---------------------------------------------------------------------------
@@ -760,31 +773,30 @@ __global__ void __launch_bounds__(NTH) kdn_backward_chunk_kernel(BwdArgs A, size
 // posterior p' = p_hat / (1 + (mu / r) k^2 p_hat); the carried dp and the
 // gradients of k, alpha, omega follow per channel.  d and u are sums over
 // every channel (and u over the column tiles) that do not depend on dp: the
-// chunked kernel leaves them per token in each chunk's checkpoint slot, so
-// the channels split over waves with no exchange per token.  dr, a channel
-// sum that does depend on dp, is left per wave in the slot and added by
+// chunked kernel leaves them per token in the per-token sums, so the
+// channels split over waves with no exchange per token.  dr, a channel sum
+// that does depend on dp, is left there per wave and added by
 // kdn_backward_dr_kernel.
 // The carried dp is affine in itself per token, dp_{t-1} = f_t dp_t + g_t
 // with f_t = alpha^2 / den^2 and g_t = alpha^2 (gk k / d + dd k^2), so the
 // sequence is cut into segments of SEGU tokens run in parallel: a first
 // launch (MAPS) composes each segment's affine map, a second runs every
-// segment from its exact entering dp (the later segments' maps applied to
-// dp_T in order) and writes the gradients.  GATE: alpha, omega and r are
-// formed from the pre-activations as the gated forward forms them, and the
-// written d alpha, d omega (and dr, in kdn_backward_dr_kernel) are already
-// the gradients of the pre-activations.
-// Slot of chunk c (tile 0 unless noted): [t] u of each tile (its own slot),
-// [L + t] d, [2L + t] dd, [3L + 32 w + t] wave w's share of dr, (gated)
-// [5L + t] 1 / |k_t|, and in the
-// slot of a segment's first chunk [MAPOFF + 2 i], [MAPOFF + 2 i + 1] the
-// segment's map of channel i.
-// The per-token tile sums and p_{t-1} (GBs at B=8, T=4096, H=16, d=128, far
-// beyond any cache) are written by the memory adjoint and read here with
+// segment from its entering dp (the later segments' maps applied in order to
+// dp_T) and writes the gradients.  A slab's launches cover its segments; the
+// dp a slab leaves for the next is its first segment's map applied to that
+// segment's entering dp, so every segment's entering dp is the same chain of
+// operations whatever the slab length.  GATE:
+// alpha, omega and r are formed from the pre-activations as the gated
+// forward forms them, and the written d alpha, d omega (and dr, in
+// kdn_backward_dr_kernel) are already the gradients of the pre-activations.
+// Per-token sums [t][8]: u of tiles 0 and 1, d, dd, dr of channel halves 0
+// and 1, (gated) 1 / |k_t|.
+// The per-token tile sums and p_{t-1} (hundreds of MB per slab at B=8,
+// H=16, d=128) are written by the memory adjoint and read here with
 // nontemporal hints, as are the gradients written here.
 // ---------------------------------------------------------------------------
-constexpr int PFU = 8;  // prefetch ring: token inputs are loaded 7 tokens ahead
-constexpr int SEGU = 512;  // tokens per segment of the uncertainty adjoint
-constexpr int MAPOFF = 256;
+constexpr int PFU = 8;    // prefetch ring: token inputs are loaded 7 tokens ahead
+constexpr int SEGU = 64;  // tokens per segment of the uncertainty adjoint (slabs are multiples of it)
 
 struct UncTok {
     float q[2], k[2], ks[2], a[2];  // the tiles' (at most 2) partial sums
@@ -794,14 +806,15 @@ struct UncTok {
 };
 
 template <int DK, bool MAPS, bool GATE>
-__global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
+__global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, ChunkWs W, int slab, int tb, int te,
+                                                                   int nseg) {
     constexpr int NWV = DK / 64;
     const int nunit = A.B * A.H;
     const int ntile = A.dv / TILE;  // 1 or 2
     const int unit = int(blockIdx.x) % nunit;
     const int wv = (int(blockIdx.x) / nunit) % NWV;  // 64-channel group
-    const int sg = int(blockIdx.x) / (nunit * NWV);  // segment
-    if (flag[unit]) return;
+    const int sg = int(blockIdx.x) / (nunit * NWV);  // segment of the slab
+    if (W.flag[unit]) return;
     const int h = unit % A.H;
     const size_t b = size_t(unit / A.H);
     const int T = A.T;
@@ -812,48 +825,49 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
     const bf16_t* ain = static_cast<const bf16_t*>(A.alpha);
     const bf16_t* win = static_cast<const bf16_t*>(A.omega);
     const bf16_t* rin = static_cast<const bf16_t*>(A.r);
-    const float* partial = A.work + size_t(nunit) * ntile * ck_floats;
-    const float* pbuf = partial + size_t(nunit) * T * ntile * 4 * DK;
-    float* slot0 = A.work + size_t(unit) * ntile * ck_floats;  // tile 0's region
+    // the slab's buffers (token t at row t - tb) and the per-token sums
+    const float* partial = W.partial + size_t(unit) * W.slab * ntile * 4 * DK;
+    const float* pbuf = W.pbuf + size_t(unit) * W.slab * DK;
+    float* tsc = W.tsc + size_t(unit) * T * 8;
     const auto tokidx = [&](int t) { return (b * size_t(T) + size_t(t)) * size_t(A.H) + size_t(h); };
-    const auto slot = [&](int tile, int t) {
-        return A.work + (size_t(unit) * ntile + tile) * ck_floats + size_t(t / L) * DK * TILE;
-    };
+    const int s0 = tb + sg * SEGU, s1 = min(te, s0 + SEGU);
     const auto load = [&](UncTok& x, int t) {
-        t = max(t, 0);
+        t = max(t, s0);
         const size_t tok = tokidx(t);
-        const int tl = t % L;
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
             const int tc = min(tile, ntile - 1);
-            const float* src = partial + ((size_t(unit) * T + t) * ntile + tc) * 4 * DK + i;
+            const float* src = partial + (size_t(t - tb) * ntile + tc) * 4 * DK + i;
             x.k[tile] = __builtin_nontemporal_load(&src[DK]);
             if (!MAPS) {
                 x.q[tile] = __builtin_nontemporal_load(&src[0]);
                 x.ks[tile] = __builtin_nontemporal_load(&src[2 * DK]);
                 x.a[tile] = __builtin_nontemporal_load(&src[3 * DK]);
             }
-            x.u[tile] = slot(tc, t)[tl];
+            x.u[tile] = tsc[size_t(t) * 8 + tc];
         }
-        x.d = slot(0, t)[L + tl];
-        if (GATE) x.sk = slot(0, t)[5 * L + tl];
-        x.pp = __builtin_nontemporal_load(&pbuf[(size_t(unit) * T + t) * ntile * DK + i]);
+        x.d = tsc[size_t(t) * 8 + 2];
+        if (GATE) x.sk = tsc[size_t(t) * 8 + 6];
+        x.pp = __builtin_nontemporal_load(&pbuf[size_t(t - tb) * DK + i]);
         x.al = ain[tok * DK + i];
         x.kk = kin[tok * DK + i];
         x.w = win[tok * DK + i];
         x.r = rin[tok];
     };
-    const int nseg = (T + SEGU - 1) / SEGU;
-    const int s0 = sg * SEGU, s1 = min(T, s0 + SEGU);
-    const auto mapslot = [&](int s) { return slot0 + size_t(s * SEGU / L) * DK * TILE + MAPOFF + 2 * i; };
+    const auto mapslot = [&](int s) { return W.maps + ((size_t(unit) * W.maxseg + s) * DK + i) * 2; };
+    // dp carried between slabs: slab j reads what slab j + 1 left in buffer
+    // (j + 1) & 1 and leaves its own in buffer j & 1
+    const size_t cstride = size_t(nunit) * DK;
     float dp = 0.f, fa = 1.f, fb = 0.f;  // OUTPUTS: the carried dp; MAPS: dp_t = fa dp_in + fb
     if (!MAPS) {
-        dp = A.dp_T ? A.dp_T[size_t(unit) * DK + i] : 0.f;
+        if (te == T) dp = A.dp_T ? A.dp_T[size_t(unit) * DK + i] : 0.f;
+        else dp = W.dpc[size_t((slab + 1) & 1) * cstride + size_t(unit) * DK + i];
         for (int s = nseg - 1; s > sg; --s) {
             const float* m = mapslot(s);
             dp = fmaf(m[0], dp, m[1]);
         }
     }
+    const float dpin = dp;
     const auto step = [&](int t, const UncTok& x) {
         const bool two = ntile > 1;
         const float gk = x.k[0] + (two ? x.k[1] : 0.f);
@@ -902,10 +916,9 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         dr = sum16(dr);
         dr = halve16(dr, dr);
         dr = halve32(dr, dr);
-        float* sl = slot0 + size_t(t / L) * DK * TILE;
         if (lane == 0) {
-            sl[3 * L + 32 * wv + t % L] = dr;
-            if (wv == 0) sl[2 * L + t % L] = dd;
+            tsc[size_t(t) * 8 + 4 + wv] = dr;
+            if (wv == 0) tsc[size_t(t) * 8 + 3] = dd;
         }
     };
     UncTok ring[PFU];
@@ -923,75 +936,157 @@ __global__ void __launch_bounds__(64) kdn_backward_unc_chunk_kernel(BwdArgs A, s
         m[0] = fa;
         m[1] = fb;
     } else if (sg == 0) {
-        A.dp0[size_t(unit) * DK + i] = dp;
+        if (tb == 0) {
+            A.dp0[size_t(unit) * DK + i] = dp;
+        } else {
+            const float* m = mapslot(0);
+            W.dpc[size_t(slab & 1) * cstride + size_t(unit) * DK + i] = fmaf(m[0], dpin, m[1]);
+        }
     }
 }
 
 // dr = dd + the waves' shares (one thread per token of a (batch, head) pair);
 // GATE: times softplus' = sigmoid at the pre-activation
 template <int DK, bool GATE>
-__global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, size_t ck_floats, const int* flag) {
-    const int nunit = A.B * A.H;
-    const int ntile = A.dv / TILE;
+__global__ void __launch_bounds__(256) kdn_backward_dr_kernel(BwdArgs A, ChunkWs W) {
     const int unit = int(blockIdx.y);
     const int t = int(blockIdx.x) * 256 + int(threadIdx.x);
-    if (flag[unit] || t >= A.T) return;
-    const float* sl = A.work + size_t(unit) * ntile * ck_floats + size_t(t / L) * DK * TILE;
-    float dr = sl[2 * L + t % L];
+    if (W.flag[unit] || t >= A.T) return;
+    const float* ts = W.tsc + (size_t(unit) * A.T + t) * 8;
+    float dr = ts[3];
 #pragma unroll
-    for (int w = 0; w < DK / 64; ++w) dr += sl[3 * L + 32 * w + t % L];
+    for (int w = 0; w < DK / 64; ++w) dr += ts[4 + w];
     const size_t b = size_t(unit / A.H);
     const size_t tok = (b * size_t(A.T) + size_t(t)) * size_t(A.H) + size_t(unit % A.H);
     if (GATE) dr *= gate_sigmoid(bf1(static_cast<const bf16_t*>(A.r)[tok]));
     A.dr[tok] = dr;
-    (void)nunit;
 }
 
-template <bool GATE>
-hipError_t launch_unc_chunk_t(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
-    const unsigned units = unsigned(long(a.B) * a.H);
-    const unsigned nseg = unsigned((a.T + SEGU - 1) / SEGU);
-    const dim3 dgrid(unsigned((a.T + 255) / 256), units);
-    if (a.dk == 128) {
-        const dim3 grid(units * 2 * nseg);
-        if (nseg > 1)
-            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<128, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_dr_kernel<128, GATE>), dgrid, dim3(256), 0, stream, a, ck_floats, flag);
-    } else if (a.dk == 64) {
-        const dim3 grid(units * nseg);
-        if (nseg > 1)
-            hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, true, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<64, false, GATE>), grid, dim3(64), 0, stream, a, ck_floats, flag);
-        hipLaunchKernelGGL((kdn_backward_dr_kernel<64, GATE>), dgrid, dim3(256), 0, stream, a, ck_floats, flag);
-    } else {
-        return hipErrorNotSupported;
-    }
+template <int DK, bool GATE>
+hipError_t launch_unc_chunk_t(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream) {
+    const int units = a.B * a.H;
+    const int tb = slab * w.slab, te = std::min(a.T, tb + w.slab);
+    const int nseg = (te - tb + SEGU - 1) / SEGU;
+    const dim3 grid(unsigned(units * (DK / 64) * nseg));
+    if (nseg > 1 || tb > 0)
+        hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<DK, true, GATE>), grid, dim3(64), 0, stream, a, w, slab, tb,
+                           te, nseg);
+    hipLaunchKernelGGL((kdn_backward_unc_chunk_kernel<DK, false, GATE>), grid, dim3(64), 0, stream, a, w, slab, tb, te,
+                       nseg);
     return hipGetLastError();
 }
 
 template <bool GATE>
-hipError_t launch_chunk_t(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
+hipError_t launch_chunk_t(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream) {
     const unsigned units = unsigned(long(a.B) * a.H);
     const unsigned grid = units * unsigned(a.dv / TILE);
+    const int nchunks = (a.T + L - 1) / L;
+    const int c_lo = slab * (w.slab / L), c_hi = std::min(nchunks, c_lo + w.slab / L);
     if (a.dk == 128)
-        hipLaunchKernelGGL((kdn_backward_chunk_kernel<128, GATE>), dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_chunk_kernel<128, GATE>), dim3(grid), dim3(NTH), 0, stream, a, w, c_lo, c_hi);
     else if (a.dk == 64)
-        hipLaunchKernelGGL((kdn_backward_chunk_kernel<64, GATE>), dim3(grid), dim3(NTH), 0, stream, a, ck_floats, flag);
+        hipLaunchKernelGGL((kdn_backward_chunk_kernel<64, GATE>), dim3(grid), dim3(NTH), 0, stream, a, w, c_lo, c_hi);
     else
         return hipErrorNotSupported;
     return hipGetLastError();
 }
 
-}  // namespace
+// region sizes of the chunked backward's workspace (ChunkWs order)
+struct ChunkSizes {
+    size_t b[9];
+    size_t total() const {
+        size_t t = 0;
+        for (size_t x : b) t += (x + 255) & ~size_t(255);
+        return t;
+    }
+};
 
-hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
-    return a.gates ? launch_unc_chunk_t<true>(a, ck_floats, flag, stream)
-                   : launch_unc_chunk_t<false>(a, ck_floats, flag, stream);
+ChunkSizes chunk_sizes(int B, int T, int H, int dk, int dv, int slab) {
+    const size_t U = size_t(B) * size_t(H), nt = size_t(dv) / TILE, nch = (size_t(T) + L - 1) / L;
+    const size_t S = size_t(slab), maxseg = size_t((slab + SEGU - 1) / SEGU), f = sizeof(float);
+    return {{U * sizeof(int), U * nt * nch * dk * TILE * sizeof(uint16_t), U * nch * dk * f, U * size_t(T) * 8 * f,
+             U * maxseg * dk * 2 * f, 2 * U * dk * f, U * size_t(dk) * dv * f, U * S * nt * 4 * dk * f,
+             U * S * dk * f}};
 }
 
-hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream) {
-    return a.gates ? launch_chunk_t<true>(a, ck_floats, flag, stream) : launch_chunk_t<false>(a, ck_floats, flag, stream);
+// the shortest slab: about 64k token-heads of per-token buffers (512 tokens
+// at B = 8, H = 16), at most the sequence
+int chunk_min_slab(int B, int T, int H) {
+    const long units = std::max(1L, long(B) * H);
+    long s = (65536 + units - 1) / units;
+    s = std::max(512L, (s + 511) / 512 * 512);
+    const long tr = (long(T) + L - 1) / L * L;
+    return int(std::min(s, tr));
+}
+
+}  // namespace
+
+bool chunk_workspace(int B, int T, int H, int dk, int dv, void* work, size_t bytes, ChunkWs* out) {
+    if (T <= 0) return false;
+    const int tr = (T + L - 1) / L * L;
+    int slab = chunk_min_slab(B, T, H);
+    if (chunk_sizes(B, T, H, dk, dv, slab).total() > bytes) return false;
+    // the longest slab that fits (fewer launches): the whole sequence, else a
+    // multiple of SEGU
+    for (int s2 = tr; s2 > slab; s2 = (s2 / 2 + SEGU - 1) / SEGU * SEGU)
+        if (chunk_sizes(B, T, H, dk, dv, s2).total() <= bytes) {
+            slab = s2;
+            break;
+        }
+    const ChunkSizes z = chunk_sizes(B, T, H, dk, dv, slab);
+    char* p = static_cast<char*>(work);
+    char* reg[9];
+    for (int j = 0; j < 9; ++j) {
+        reg[j] = p;
+        p += (z.b[j] + 255) & ~size_t(255);
+    }
+    out->flag = reinterpret_cast<int*>(reg[0]);
+    out->cks = reinterpret_cast<uint16_t*>(reg[1]);
+    out->ckp = reinterpret_cast<float*>(reg[2]);
+    out->tsc = reinterpret_cast<float*>(reg[3]);
+    out->maps = reinterpret_cast<float*>(reg[4]);
+    out->dpc = reinterpret_cast<float*>(reg[5]);
+    out->dsc = reinterpret_cast<float*>(reg[6]);
+    out->partial = reinterpret_cast<float*>(reg[7]);
+    out->pbuf = reinterpret_cast<float*>(reg[8]);
+    out->slab = slab;
+    out->nslab = (T + slab - 1) / slab;
+    out->maxseg = (slab + SEGU - 1) / SEGU;
+    out->rest = reg[1];
+    out->rest_bytes = bytes - size_t(reg[1] - reg[0]);
+    return true;
+}
+
+size_t chunk_workspace_min_bytes(int B, int T, int H, int dk, int dv) {
+    return chunk_sizes(B, T, H, dk, dv, chunk_min_slab(B, T, H)).total();
+}
+
+hipError_t launch_backward_unc_chunk(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream) {
+    if (a.dk == 128)
+        return a.gates ? launch_unc_chunk_t<128, true>(a, w, slab, stream)
+                       : launch_unc_chunk_t<128, false>(a, w, slab, stream);
+    if (a.dk == 64)
+        return a.gates ? launch_unc_chunk_t<64, true>(a, w, slab, stream)
+                       : launch_unc_chunk_t<64, false>(a, w, slab, stream);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_backward_chunk(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream) {
+    return a.gates ? launch_chunk_t<true>(a, w, slab, stream) : launch_chunk_t<false>(a, w, slab, stream);
+}
+
+hipError_t launch_backward_dr(const BwdArgs& a, const ChunkWs& w, hipStream_t stream) {
+    const dim3 grid(unsigned((a.T + 255) / 256), unsigned(a.B * a.H));
+    if (a.dk == 128) {
+        if (a.gates) hipLaunchKernelGGL((kdn_backward_dr_kernel<128, true>), grid, dim3(256), 0, stream, a, w);
+        else hipLaunchKernelGGL((kdn_backward_dr_kernel<128, false>), grid, dim3(256), 0, stream, a, w);
+    } else if (a.dk == 64) {
+        if (a.gates) hipLaunchKernelGGL((kdn_backward_dr_kernel<64, true>), grid, dim3(256), 0, stream, a, w);
+        else hipLaunchKernelGGL((kdn_backward_dr_kernel<64, false>), grid, dim3(256), 0, stream, a, w);
+    } else {
+        return hipErrorNotSupported;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace kdn

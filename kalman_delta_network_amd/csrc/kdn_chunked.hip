@@ -174,14 +174,14 @@ struct Args {
     const float* mob = nullptr;  // [B*H][nseg][DK][4] Mobius products of the segments
     bf16_t* ophi = nullptr;      // o of the identity columns, [tokens][H][DK]
     float* sseg = nullptr;       // segment end states [B*H][nseg][DK][DV + DK]
-    // checkpoint mode (the chunked backward's forward sweep; diagonal,
-    // ungated, 64-column tiles): per (unit, tile) region of ck_floats floats
-    // from ck: the memory in the midpoint frame, diag(g_15) S, at every chunk
-    // start ([chunk][DK / 4][64][4]), then (tile 0) p at every chunk start
-    // ([chunk][DK]); ck_flag[unit] = 1 where a chunk leaves the chunked
-    // form's range (its checkpoints stop there), else 0.  No o, S_T or p_T.
-    float* ck = nullptr;
-    size_t ck_floats = 0;
+    // checkpoint mode (the chunked backward's forward sweep; diagonal, 64-column
+    // tiles): the memory in the midpoint frame, diag(g_15) S, in bf16 at every
+    // chunk start ([unit][tile][chunk][DK / 4][64][4] at cks), and p at every
+    // chunk start ([unit][chunk][DK] at ckp); ck_flag[unit] = 1 where a chunk
+    // leaves the chunked form's range (its checkpoints stop there), else 0.
+    // No o, S_T or p_T.
+    bf16_t* cks = nullptr;
+    float* ckp = nullptr;
     int* ck_flag = nullptr;
 };
 
@@ -1275,8 +1275,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
                 bad_seen = sm.bad;  // flags of chunks before c
                 if (bad_seen == c - 1) psave = pst[BUF ^ 1];
                 pst[BUF] = p;
-                if (STORE && tile == 0 && active && c < nchunks)
-                    a.ck[size_t(unit) * ntile * a.ck_floats + size_t(nchunks) * DK * DVTN + size_t(c) * DK + i] = p;
+                if (STORE && tile == 0 && active && c < nchunks) a.ckp[(size_t(unit) * nchunks + c) * DK + i] = p;
                 float g = 1.f, gi = 1.f;
                 if (active && c < nchunks) {
                     if (nvalid == L) chain_diag_run<DK, BUF, 0, CHAIN_SPLIT, false, GATE>(sm, in, i, p, g, gi, L, c % 3);
@@ -1448,17 +1447,18 @@ __global__ void __launch_bounds__(NTHREADS) kdn_chunk_kernel(Args a) {
             // chunk it - 1, the previous iteration's stores and chain rows
             vm_wait<NCT>();
             if (STORE && run) {
-                // chunk c's start state, diag(g_15) S (fp32; the first segment
-                // leaves it unchanged), as [DK / 4][64][4]: rows 4j .. 4j + 3 of
-                // a column in one 16-byte store.  Issued after the wait, so
-                // that they complete during the next iteration, not this one.
-                f4* ck = reinterpret_cast<f4*>(a.ck + (size_t(unit) * ntile + tile) * a.ck_floats +
-                                               size_t(c) * DK * DVTN);
+                // chunk c's start state, diag(g_15) S (the first segment leaves
+                // it unchanged), rounded to bf16 as [DK / 4][64][4]: rows 4j ..
+                // 4j + 3 of a column in one 8-byte store.  Issued after the
+                // wait, so that they complete during the next iteration.
+                u2* ck = reinterpret_cast<u2*>(a.cks + ((size_t(unit) * ntile + tile) * nchunks + c) * DK * DVTN);
 #pragma unroll
                 for (int r4 = 0; r4 < DK / 16; ++r4)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        ck[((16 * r4 + g4) / 4) * DVTN + cw * (16 * NCT) + 16 * ct + n] = st.S[r4][ct];
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const f4 x = st.S[r4][ct];
+                        ck[((16 * r4 + g4) / 4) * DVTN + cw * (16 * NCT) + 16 * ct + n] = u2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+                    }
             }
             bar();
             // rows 0..15 of the chain's chunk it + 2: the chain has read those
@@ -1683,7 +1683,7 @@ hipError_t launch_segments_t(const FwdArgs& f, int seg, int nseg, const float* m
 // Checkpoint sweep of the chunked backward (diagonal, bf16, 64-column tiles;
 // GATE: the gated forward's values).
 template <int DK, bool GATE>
-hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, int* ck_flag, hipStream_t stream) {
+hipError_t launch_checkpoints_t(const FwdArgs& f, bf16_t* cks, float* ckp, int* ck_flag, hipStream_t stream) {
     const int units = f.B * f.H;
     if (units == 0 || f.T == 0) return hipSuccess;
     Args a;
@@ -1707,8 +1707,8 @@ hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, i
     a.cu = nullptr;
     a.ord = nullptr;
     a.tok0 = 0;
-    a.ck = ck;
-    a.ck_floats = ck_floats;
+    a.cks = cks;
+    a.ckp = ckp;
     a.ck_flag = ck_flag;
     const int ntile = f.dv / DVT;
     const int groups = (units + 7) / 8;
@@ -1719,14 +1719,14 @@ hipError_t launch_checkpoints_t(const FwdArgs& f, float* ck, size_t ck_floats, i
 
 }  // namespace
 
-hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,
+hipError_t launch_chunked_checkpoints(const FwdArgs& a, uint16_t* cks, float* ckp, int* ck_flag,
                                       hipStream_t stream) {
     if (!chunked_supports(a) || a.variant != 0 || a.cu_seqlens) return hipErrorNotSupported;
     if (a.gates)
-        return a.dk == 128 ? launch_checkpoints_t<128, true>(a, ck, ck_floats, ck_flag, stream)
-                           : launch_checkpoints_t<64, true>(a, ck, ck_floats, ck_flag, stream);
-    return a.dk == 128 ? launch_checkpoints_t<128, false>(a, ck, ck_floats, ck_flag, stream)
-                       : launch_checkpoints_t<64, false>(a, ck, ck_floats, ck_flag, stream);
+        return a.dk == 128 ? launch_checkpoints_t<128, true>(a, cks, ckp, ck_flag, stream)
+                           : launch_checkpoints_t<64, true>(a, cks, ckp, ck_flag, stream);
+    return a.dk == 128 ? launch_checkpoints_t<128, false>(a, cks, ckp, ck_flag, stream)
+                       : launch_checkpoints_t<64, false>(a, cks, ckp, ck_flag, stream);
 }
 
 // Compute units of the current device (read once per device and cached; 256

@@ -216,7 +216,9 @@ GatedSizes gated_sizes(int variant, int B, int T, int H, int dk, int dv) {
 template <typename Tin>
 hipError_t run(const BwdArgs& a, hipStream_t s) {
     const GatedSizes n = gated_sizes(a.variant, a.B, a.T, a.H, a.dk, a.dv);
-    char* w = reinterpret_cast<char*>(a.work) + round256(backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv));
+    // the adjoint's workspace, then the fp32 copies
+    const size_t base = backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv);
+    char* w = reinterpret_cast<char*>(a.work) + round256(base);
     auto take = [&](size_t count) {
         float* p = reinterpret_cast<float*>(w);
         w += round256(count * sizeof(float));
@@ -235,6 +237,7 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     // checkpoint sweep flags.
     BwdArgs c = a;
     c.gates = true;
+    c.work_bytes = base;
     const bool chunked = backward_chunked_eligible(c);
     hipError_t e = hipSuccess;
     PairFilter pf{nullptr, size_t(a.T) * size_t(a.H), a.H, 1, a.B * a.H};
@@ -268,6 +271,7 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     BwdArgs f = a;
+    f.work_bytes = base;
     f.q = fq;
     f.k = fk;
     f.v = fv;

@@ -70,7 +70,8 @@ struct BwdArgs {
     float* dS0;
     float* dp0;
     float* dc0;   // may be NULL
-    float* work;  // backward_workspace_bytes() bytes
+    float* work;  // the workspace: work_bytes bytes, at least backward_workspace_bytes_for()
+    size_t work_bytes = 0;
     // set by the chunked backward: flag[unit] = 1 for the (batch, head) pairs
     // the recurrent memory adjoint must take (their decays leave the chunked
     // form's range); the recurrent memory kernel then skips every other pair
@@ -78,10 +79,50 @@ struct BwdArgs {
     // chunked path only: alpha, omega, r hold the gate pre-activations and q,
     // k are raw (the kernels form the gated layer's values themselves)
     bool gates = false;
+    // the token path's pairs in rounds: this call takes pairs slot0 ..
+    // slot0 + nslot - 1, each in workspace slot (pair - slot0); nslot = 0
+    // takes every pair at once (slot = pair)
+    int slot0 = 0;
+    int nslot = 0;
 };
 
-// Bytes of device workspace one backward call needs (0 for an empty call).
+// Bytes of device workspace with which every variant and dtype runs with all
+// its pairs at once (0 for an empty call).
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+// The smallest workspace a backward call of this variant and dtype accepts:
+// the chunked path's layout (ChunkWs) where the diagonal bf16 form can take
+// it, else backward_workspace_bytes.
+size_t backward_workspace_bytes_for(int variant, int dtype, int B, int T, int H, int dk, int dv);
+// Workspace of one (batch, head) pair on the token path (its rounds take as
+// many pairs as the workspace holds).
+size_t token_pair_bytes(int T, int dk, int dv);
+
+// The chunked backward's workspace (diagonal bf16 form), carved from the
+// caller's by chunk_workspace(); every region starts on 256 bytes, in this
+// order.  The big per-token buffers hold one slab of tokens: the backward
+// runs the slabs from the last, carrying dS and dp from one to the next.
+struct ChunkWs {
+    int* flag;          // [units] 1 where a chunk leaves the chunked form's range
+    uint16_t* cks;      // [units][ntile][nchunks][dk / 4][64][4] bf16: diag(g_15) S at each chunk start
+    float* ckp;         // [units][nchunks][dk]: p at each chunk start
+    float* tsc;         // [units][T][8] per-token sums: u of tiles 0 and 1, d, dd, dr of the
+                        // channel halves (2), 1 / |k| (gated), unused
+    float* maps;        // [units][maxseg][dk][2]: the uncertainty adjoint's segment maps in one slab
+    float* dpc;         // [2][units][dk]: dp carried between slabs (by slab parity)
+    float* dsc;         // [units][dk][dv]: dS carried between slabs
+    float* partial;     // [units][slab][ntile][4][dk]: per-token tile sums of one slab
+    float* pbuf;        // [units][slab][dk]: p_{t-1} of one slab
+    int slab;           // tokens per slab (a multiple of 32)
+    int nslab;
+    int maxseg;         // uncertainty segments per slab at most
+    char* rest;         // everything after the flags (the token path's rounds reuse it)
+    size_t rest_bytes;
+};
+// Layout in `bytes` bytes at `work`: the slab as long as fits (at least the
+// minimum); false if even the minimum does not fit.
+bool chunk_workspace(int B, int T, int H, int dk, int dv, void* work, size_t bytes, ChunkWs* out);
+// Bytes of the chunked layout at its shortest slab.
+size_t chunk_workspace_min_bytes(int B, int T, int H, int dk, int dv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // The chunked path on its own (diagonal bf16 form; with a.gates the gated
 // layer on raw q, k and pre-activations): the chunked adjoint for every pair
@@ -135,23 +176,23 @@ hipError_t launch_split(const FwdArgs& a, int nseg, void* workspace, size_t work
 // sseg: [B*H][nseg][dk][dv + dk] segment end states.
 hipError_t launch_chunked_segments(const FwdArgs& a, int seg, int nseg, const float* mob, void* ophi, float* sseg,
                                    hipStream_t stream);
-// The chunked memory adjoint of the diagonal bf16 form (kdn_backward_chunk.hip):
-// one workgroup per (batch, head, 64 value columns) whose flag is 0, reading
-// the checkpoints launch_chunked_checkpoints wrote (region ck_floats floats per
-// (unit, tile) at a.work) and writing the per-token tile sums, p_{t-1}, dv and
-// dS0 in the recurrent memory adjoint's workspace layout.
-hipError_t launch_backward_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream);
-// The uncertainty adjoint after launch_backward_chunk (same pairs, same
-// workspace): per-channel waves, with the per-token channel sums the chunked
-// kernel left in the checkpoint slots; then dr.
-hipError_t launch_backward_unc_chunk(const BwdArgs& a, size_t ck_floats, const int* flag, hipStream_t stream);
+// The chunked memory adjoint of the diagonal bf16 form (kdn_backward_chunk.hip)
+// over chunks [c_lo, c_hi) of slab `slab`: one workgroup per (batch, head, 64
+// value columns) whose flag is 0, reading the checkpoints
+// launch_chunked_checkpoints wrote, writing the slab's per-token tile sums
+// and p_{t-1}, the per-token sums, dv and (first slab) dS0.
+hipError_t launch_backward_chunk(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream);
+// The uncertainty adjoint of the same slab after launch_backward_chunk
+// (per-channel waves); then, after the first slab, launch_backward_dr.
+hipError_t launch_backward_unc_chunk(const BwdArgs& a, const ChunkWs& w, int slab, hipStream_t stream);
+hipError_t launch_backward_dr(const BwdArgs& a, const ChunkWs& w, hipStream_t stream);
 // Checkpoint sweep of the chunked backward (kdn_chunked.hip, diagonal bf16,
-// d_v a multiple of 64): per (unit, 64-column tile) region of ck_floats
-// floats from ck, the memory in the midpoint frame diag(g_15) S at every
-// 32-token chunk start ([chunk][dk / 4][64][4]) and, in tile 0's region after those,
-// p at every chunk start ([chunk][dk]); ck_flag[unit] = 1 where a chunk
-// leaves the chunked form's range (checkpoints stop there), else 0.
-hipError_t launch_chunked_checkpoints(const FwdArgs& a, float* ck, size_t ck_floats, int* ck_flag,
+// d_v a multiple of 64): the memory in the midpoint frame, diag(g_15) S, in
+// bf16 at every 32-token chunk start ([unit][tile][chunk][dk / 4][64][4] at
+// cks) and p at every chunk start ([unit][chunk][dk] at ckp); ck_flag[unit] =
+// 1 where a chunk leaves the chunked form's range (checkpoints stop there),
+// else 0.
+hipError_t launch_chunked_checkpoints(const FwdArgs& a, uint16_t* cks, float* ckp, int* ck_flag,
                                       hipStream_t stream);
 // Chunkwise forward of the isotropic variant (variant 1) on Gram matrices of
 // the raw keys (kdn_iso.hip); narrow = 32 value columns per workgroup, else 64.

@@ -99,3 +99,30 @@ def check_dc0(dc0, dp0):
     scale = np.abs(dp0).sum(axis=axes)
     err = np.abs(np.asarray(dc0, np.float64) - want)
     assert np.all(err <= 1e-5 * np.maximum(scale, 1e-30)), (err, scale)
+
+
+# Workspace sizes of the backward, restated from include/kdn.h
+
+def r256(n):
+    return (n + 255) // 256 * 256
+
+
+def token_pair_bytes(T, dk, dv):
+    # one (batch, head) pair on the token path, per 64-column tile: ceil(T/32) checkpoints of S
+    # and of p (one copy per 8 value columns), a 32-token stash, and per token the tile's four
+    # row sums and p_{t-1}
+    nseg, nt = -(-T // 32), dv // 64
+    return nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk + 5 * T * dk) * 4
+
+
+def chunk_min_bytes(B, T, H, dk, dv):
+    # the chunked backward's regions (include/kdn.h, kdn_backward_workspace_size_for): flags,
+    # bf16 chunk-start states, chunk-start p, 8 per-token sums, the uncertainty segments' maps
+    # (64 tokens each) of one slab, dp and dS carried between slabs, one slab's tile sums and
+    # p_{t-1}; the slab is about 64k token-heads, a multiple of 512, at most the sequence
+    U, nt, nch = B * H, dv // 64, -(-T // 32)
+    per = -(-65536 // U)  # token-heads per pair, rounded up
+    slab = min(nch * 32, max(512, -(-per // 512) * 512))
+    regions = (U * 4, U * nt * nch * dk * 64 * 2, U * nch * dk * 4, U * T * 32, U * -(-slab // 64) * dk * 8,
+               2 * U * dk * 4, U * dk * dv * 4, U * slab * nt * 4 * dk * 4, U * slab * dk * 4)
+    return max(sum(r256(x) for x in regions), r256(U * 4) + token_pair_bytes(T, dk, dv))

@@ -8,6 +8,7 @@ import re
 import pytest
 
 import kalman_delta_network_amd as kdn
+from kdn_testutil import chunk_min_bytes, r256, token_pair_bytes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kdn.h")
@@ -292,15 +293,42 @@ def call_validate_bwd(lib, a):
 
 
 def test_backward_workspace_size_formula(lib):
-    # per 64-column tile: ceil(T/32) checkpoints of S and of p (one copy per 8 value columns), a
-    # 32-token stash, and per token the tile's four row sums and p_{t-1}; then one int per
-    # (batch, head) pair (the chunked path's range flags)
+    # every pair on the token path at once, then one int per (batch, head) pair (the chunked
+    # path's range flags) rounded up to 256 bytes
     for B, T, H, dk, dv in ((2, 40, 3, 64, 128), (8, 4096, 16, 128, 128), (1, 1, 1, 128, 64)):
-        nseg, nt = -(-T // 32), dv // 64
-        want = B * H * nt * (nseg * (64 * dk + 8 * dk) + 32 * 64 * dk + 5 * T * dk) * 4 + B * H * 4
+        want = B * H * token_pair_bytes(T, dk, dv) + r256(B * H * 4)
         assert lib.kdn_backward_workspace_size(B, T, H, dk, dv) == want
     assert lib.kdn_backward_workspace_size(0, 10, 2, 64, 64) == 0
     assert lib.kdn_backward_workspace_size(2, 0, 2, 64, 64) == 0
+
+
+def test_backward_workspace_size_for(lib):
+    # the diagonal bf16 form at dk, dv in {64, 128}: the chunked path's layout (with room for
+    # one pair on the token path); everything else: the all-pairs size
+    for B, T, H, dk, dv in ((2, 40, 3, 64, 128), (8, 4096, 16, 128, 128), (1, 1, 1, 128, 64),
+                            (1, 65536, 16, 128, 128), (4, 1000, 2, 128, 64), (1, 4096, 1, 128, 128)):
+        full = lib.kdn_backward_workspace_size(B, T, H, dk, dv)
+        assert lib.kdn_backward_workspace_size_for(0, 1, B, T, H, dk, dv) == chunk_min_bytes(B, T, H, dk, dv)
+        assert lib.kdn_backward_workspace_size_for(0, 1, B, T, H, dk, dv) <= full
+        for variant, dtype in ((0, 0), (1, 1), (2, 1), (3, 1), (1, 0)):
+            assert lib.kdn_backward_workspace_size_for(variant, dtype, B, T, H, dk, dv) == full
+    # the diagonal bf16 backward at B=8, T=4096, H=16, d=128 within 1 GB (the all-pairs size is 4.2 GB)
+    assert lib.kdn_backward_workspace_size_for(0, 1, 8, 4096, 16, 128, 128) == 873595392
+    assert lib.kdn_backward_workspace_size_for(0, 1, 8, 4096, 16, 128, 128) < 10**9
+    assert lib.kdn_backward_workspace_size_for(0, 1, 0, 10, 2, 64, 64) == 0
+    assert lib.kdn_backward_workspace_size_for(0, 1, 2, 0, 2, 64, 64) == 0
+    assert lib.kdn_backward_workspace_size_for(0, 1, 2, 10, 2, 96, 64) == lib.kdn_backward_workspace_size(
+        2, 10, 2, 96, 64)
+
+
+def test_validate_backward_workspace_for_variant(lib):
+    # the smallest workspace each variant and dtype accepts, and one byte less
+    f = Fake()
+    for variant, dtype in ((0, 1), (0, 0), (1, 1)):
+        need = lib.kdn_backward_workspace_size_for(variant, dtype, 2, 40, 2, 64, 64)
+        assert call_validate_bwd(lib, bwd_args(f, lib, variant=variant, dtype=dtype, work_bytes=need)) == kdn.KDN_OK
+        assert call_validate_bwd(lib, bwd_args(f, lib, variant=variant, dtype=dtype,
+                                               work_bytes=need - 1)) == kdn.KDN_ERR_WORKSPACE
 
 
 def test_validate_backward_accepts_good_arguments(lib):
@@ -422,8 +450,8 @@ def test_noalloc_backward_host_checks_without_gpu(lib, monkeypatch):
     # refused before any device access; with the launch fault hook the call
     # reports the launch error (its remaining checks and the scratch need a GPU)
     f = Fake()
-    big = bwd_args(f, lib, B=1, T=2048, H=16, dk=128, dv=128)
-    assert lib.kdn_backward_workspace_size(1, 2048, 16, 128, 128) > kdn.NOALLOC_SCRATCH_BYTES
+    big = bwd_args(f, lib, B=1, T=8192, H=16, dk=128, dv=128)
+    assert lib.kdn_backward_workspace_size_for(0, 1, 1, 8192, 16, 128, 128) > kdn.NOALLOC_SCRATCH_BYTES
     noalloc = lambda a: lib.kdn_backward_noalloc(*_bwd_list(a)[:-2], None)
     assert noalloc(big) == kdn.KDN_ERR_WORKSPACE
     assert b"static scratch" in lib.kdn_last_error()

@@ -74,8 +74,9 @@ def test_noalloc_refuses_sizes_beyond_the_scratch(dev):
     import torch
     import kalman_delta_network_amd as kdn
     lib = kdn.load_library()
-    w = wl.Workload("noalloc_big", "diagonal", "bf16", 1, 2048, 16, 128, 128, 128.0, "uniform", 3103)
-    assert kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv) > kdn.NOALLOC_SCRATCH_BYTES
+    w = wl.Workload("noalloc_big", "diagonal", "bf16", 1, 8192, 16, 128, 128, 128.0, "uniform", 3103)
+    assert kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv, "diagonal", torch.bfloat16) > \
+        kdn.NOALLOC_SCRATCH_BYTES
     t, cot = _case(w, dev)
     g = _outputs(w, dev, 7.0)
     st = _call_noalloc(lib, w, t, cot, g, torch.cuda.current_stream(dev).cuda_stream)
