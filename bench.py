@@ -298,7 +298,7 @@ def backward_call(kdn, w, dev, gated=False):
     t = upload(wl.gated_inputs(w) if gated else wl.forward_inputs(w), w.dtype, dev)
     dO = torch.from_numpy(wl.backward_cotangents(w, with_state=False)["dO"]).to(t["q"].dtype).to(dev)
     if gated:
-        ws = torch.empty(kdn.backward_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.variant),
+        ws = torch.empty(kdn.backward_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.variant, t["q"].dtype),
                          dtype=torch.uint8, device=dev)
         call = lambda: kdn.backward_gated(**t, mu=w.mu, dO=dO, variant=w.variant, workspace=ws)
     else:

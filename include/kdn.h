@@ -429,8 +429,10 @@ const char* kdn_status_string(int status);
  *        |x| < 1e-6),
  *   dz_alpha = d alpha * sigmoid(z) sigmoid(-z),  dz_omega = d omega * sigmoid(z),
  *   dz_r = d r * sigmoid(z).
- * Everything else as kdn_backward, except the workspace:
- * kdn_backward_gated_workspace_size() bytes, 16-byte aligned.
+ * Everything else as kdn_backward, except the workspace: at least
+ * kdn_backward_gated_workspace_size_for(variant, dtype, ...) bytes, 16-byte
+ * aligned; the fp32 copies take its last bytes and the adjoint everything
+ * before them.
  */
 int kdn_backward_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,
                        const void* z_r, const float* c0, float mu, int variant, int dtype, int B, int T,
@@ -445,6 +447,11 @@ int kdn_backward_gated(const void* q, const void* k, const void* v, const void* 
  * rounded up to 256 bytes.
  * 0 for negative sizes, an unknown variant or grouped noise. */
 size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv);
+/* The smallest workspace kdn_backward_gated accepts for this variant and
+ * dtype: kdn_backward_workspace_size_for(variant, dtype, ...) rounded up to
+ * 256 bytes, then the same fp32 copies (2.49 GB for the diagonal bf16 form at
+ * B=8, T=4096, H=16, dk=dv=128).  0 as kdn_backward_gated_workspace_size. */
+size_t kdn_backward_gated_workspace_size_for(int variant, int dtype, int B, int T, int H, int dk, int dv);
 
 /* Detail of the last error on the calling thread ("" if none). */
 const char* kdn_last_error(void);

@@ -50,7 +50,8 @@ def _p_shape(var, lead, dk, dv):
 # exported symbols of include/kdn.h
 SYMBOLS = ("kdn_forward", "kdn_forward_algo", "kdn_forward_varlen", "kdn_forward_gated",
            "kdn_forward_varlen_gated", "kdn_step", "kdn_step_gated", "kdn_backward_gated",
-           "kdn_backward_gated_workspace_size", "kdn_backward_noalloc", "kdn_forward_split",
+           "kdn_backward_gated_workspace_size", "kdn_backward_gated_workspace_size_for", "kdn_backward_noalloc",
+           "kdn_forward_split",
            "kdn_forward_split_segments", "kdn_forward_split_workspace_size", "kdn_validate_forward_split",
            "kdn_validate_forward", "kdn_validate_forward_varlen", "kdn_validate_forward_gated",
            "kdn_validate_step", "kdn_backward", "kdn_backward_workspace_size", "kdn_backward_workspace_size_for",
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH):
     lib.kdn_backward_noalloc.argtypes = bwd + [P]
     lib.kdn_backward_gated_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kdn_backward_gated_workspace_size.restype = ctypes.c_size_t
+    lib.kdn_backward_gated_workspace_size_for.argtypes = [I, I, I, I, I, I, I]
+    lib.kdn_backward_gated_workspace_size_for.restype = ctypes.c_size_t
     for fn in (lib.kdn_forward, lib.kdn_forward_algo, lib.kdn_validate_forward, lib.kdn_step,
                lib.kdn_validate_step, lib.kdn_forward_varlen, lib.kdn_validate_forward_varlen,
                lib.kdn_backward, lib.kdn_validate_backward, lib.kdn_version, lib.kdn_forward_gated,
@@ -492,9 +495,16 @@ def backward_noalloc(q, k, v, alpha, omega, r, c0, mu, dO=None, dS_T=None, dp_T=
 NOALLOC_SCRATCH_BYTES = 256 << 20  # KDN_NOALLOC_SCRATCH_BYTES of kdn.h
 
 
-def backward_gated_workspace_size(B, T, H, dk, dv, variant="diagonal") -> int:
-    """Bytes of device workspace kdn_backward_gated needs for these sizes."""
-    return int(load_library().kdn_backward_gated_workspace_size(VARIANTS[variant], B, T, H, dk, dv))
+def backward_gated_workspace_size(B, T, H, dk, dv, variant="diagonal", dtype=None) -> int:
+    """Bytes of device workspace for kdn_backward_gated at these sizes: with
+    ``dtype`` (a torch dtype), the smallest it accepts for the variant and
+    dtype; without, the size that serves every dtype with all pairs at once."""
+    lib = load_library()
+    if dtype is None:
+        return int(lib.kdn_backward_gated_workspace_size(VARIANTS[variant], B, T, H, dk, dv))
+    torch = _torch()
+    code = {torch.bfloat16: KDN_BF16, torch.float32: KDN_F32}[dtype]
+    return int(lib.kdn_backward_gated_workspace_size_for(VARIANTS[variant], code, B, T, H, dk, dv))
 
 
 def backward_gated(q, k, v, z_alpha, z_omega, z_r, c0, mu, dO=None, dS_T=None, dp_T=None, variant="diagonal",
@@ -547,7 +557,7 @@ def _backward(q, k, v, alpha, omega, r, c0, mu, dO, dS_T, dp_T, variant, S0, p0,
             *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dalpha", "domega", "dr", "dS0", "dp0", "dc0")), _stream(dev))
         _check(st, "kdn_backward_noalloc")
         return g
-    need = (backward_gated_workspace_size(B, T, H, dk, dv, variant) if gated
+    need = (backward_gated_workspace_size(B, T, H, dk, dv, variant, dt) if gated
             else backward_workspace_size(B, T, H, dk, dv, variant, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

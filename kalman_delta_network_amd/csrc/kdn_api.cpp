@@ -198,7 +198,7 @@ int validate_backward(const void* q, const void* k, const void* v, const void* a
     if (!c0 && !p0) return fail(KDN_ERR_NULL, "c0 may be NULL only when p0 is given");
     if (gated && variant == KDN_DIAGONAL_GROUPED)
         return fail(KDN_ERR_UNSUPPORTED, "no gate step with grouped observation noise (variant %d)", variant);
-    const size_t need = gated ? kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv)
+    const size_t need = gated ? kdn::backward_gated_workspace_bytes_for(variant, dtype, B, T, H, dk, dv)
                               : kdn::backward_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
     if (need > 0 && (!work || work_bytes < need))
         return fail(KDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, work_bytes);
@@ -549,6 +549,11 @@ int kdn_backward_noalloc(const void* q, const void* k, const void* v, const void
 size_t kdn_backward_gated_workspace_size(int variant, int B, int T, int H, int dk, int dv) {
     if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || variant < 0 || variant > 2) return 0;
     return kdn::backward_gated_workspace_bytes(variant, B, T, H, dk, dv);
+}
+
+size_t kdn_backward_gated_workspace_size_for(int variant, int dtype, int B, int T, int H, int dk, int dv) {
+    if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0 || variant < 0 || variant > 2) return 0;
+    return kdn::backward_gated_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
 }
 
 int kdn_backward_gated(const void* q, const void* k, const void* v, const void* z_alpha, const void* z_omega,

@@ -35,6 +35,10 @@
 // LDS one token behind, and store the tile's sums per token in the
 // workspace; the uncertainty kernel adds the tiles and runs its part
 // backwards over the tokens.
+//
+// Each pair needs token_pair_bytes() of workspace.  The kernels take the
+// pairs in rounds of as many as the workspace holds (all of them with
+// backward_workspace_bytes()); pair slot0 + s of a round uses slot s.
 #include "kdn_internal.h"
 
 #include <hip/hip_runtime.h>

@@ -31,9 +31,13 @@
 // first half's forward gives the state at the midpoint, then the second
 // half's adjoint and the first half's (every 16 x 16 block of M and
 // tril(Qt Kh^T) is then one tile, and the block solves are single tiles).
-// The chunk-start states (in the midpoint frame) and uncertainties come from
+// The chunk-start states (in the midpoint frame, rounded to bf16: the
+// adjoint's products take them as bf16 operands) and uncertainties come from
 // the chunked forward's checkpoint mode; the chain re-runs the chunk's
-// uncertainty recurrence from the stored p.  Waves 0 .. d_k/16 - 1 hold 16
+// uncertainty recurrence from the stored p.  One launch covers a slab of
+// chunks (ChunkWs): its per-token sums go to buffers of one slab, and the
+// state's cotangent passes to the next launch (the earlier slab) through
+// the workspace.  Waves 0 .. d_k/16 - 1 hold 16
 // key rows of the state-sized matrices (Sg, dS, X) in MFMA accumulator
 // layout.  Matrix operands whose contraction index runs along the stored
 // rows are gathered from LDS (4 or 8 two-byte reads per lane).

@@ -213,12 +213,21 @@ GatedSizes gated_sizes(int variant, int B, int T, int H, int dk, int dv) {
     return {toks * dk, toks * dv, chan ? toks * dk : toks, iso ? toks : toks * dk, toks};
 }
 
+// bytes of the fp32 copies (each rounded up to 256)
+size_t copies_bytes(const GatedSizes& n) {
+    const size_t f = sizeof(float);
+    return 2 * round256(n.nk * f) + 2 * round256(n.nv * f) + round256(n.na * f) + round256(n.nw * f) +
+           round256(n.nr * f);
+}
+
 template <typename Tin>
 hipError_t run(const BwdArgs& a, hipStream_t s) {
     const GatedSizes n = gated_sizes(a.variant, a.B, a.T, a.H, a.dk, a.dv);
-    // the adjoint's workspace, then the fp32 copies
-    const size_t base = backward_workspace_bytes(a.B, a.T, a.H, a.dk, a.dv);
-    char* w = reinterpret_cast<char*>(a.work) + round256(base);
+    // the adjoint's workspace, then the fp32 copies at the workspace's end
+    // (16-byte aligned): the adjoint takes everything before them
+    const uintptr_t end = reinterpret_cast<uintptr_t>(a.work) + a.work_bytes;
+    char* w = reinterpret_cast<char*>((end - copies_bytes(n)) & ~uintptr_t(15));
+    const size_t base = size_t(w - reinterpret_cast<char*>(a.work));
     auto take = [&](size_t count) {
         float* p = reinterpret_cast<float*>(w);
         w += round256(count * sizeof(float));
@@ -324,10 +333,13 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
 size_t backward_gated_workspace_bytes(int variant, int B, int T, int H, int dk, int dv) {
     const size_t base = backward_workspace_bytes(B, T, H, dk, dv);
     if (base == 0) return 0;
-    const GatedSizes n = gated_sizes(variant, B, T, H, dk, dv);
-    const size_t f = sizeof(float);
-    return round256(base) + 2 * round256(n.nk * f) + 2 * round256(n.nv * f) + round256(n.na * f) +
-           round256(n.nw * f) + round256(n.nr * f);
+    return round256(base) + copies_bytes(gated_sizes(variant, B, T, H, dk, dv));
+}
+
+size_t backward_gated_workspace_bytes_for(int variant, int dtype, int B, int T, int H, int dk, int dv) {
+    const size_t base = backward_workspace_bytes_for(variant, dtype, B, T, H, dk, dv);
+    if (base == 0) return 0;
+    return round256(base) + copies_bytes(gated_sizes(variant, B, T, H, dk, dv));
 }
 
 hipError_t launch_backward_gated(const BwdArgs& a, hipStream_t stream) {

@@ -140,6 +140,9 @@ hipError_t launch_backward_chunked_fallback(const BwdArgs& a, const BwdArgs& fal
 // a.work holds backward_gated_workspace_bytes() bytes (the adjoint's
 // workspace, then fp32 copies of the token inputs, the gated values and dO).
 size_t backward_gated_workspace_bytes(int variant, int B, int T, int H, int dk, int dv);
+// The smallest gated workspace for this variant and dtype: the adjoint's
+// (backward_workspace_bytes_for) and the copies.
+size_t backward_gated_workspace_bytes_for(int variant, int dtype, int B, int T, int H, int dk, int dv);
 hipError_t launch_backward_gated(const BwdArgs& a, hipStream_t stream);
 
 // kdn_backward_noalloc: the workspace is a static device array of this many

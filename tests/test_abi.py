@@ -442,6 +442,14 @@ def test_gated_backward_workspace_size_formula(lib):
     assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64, "isotropic") == (
         r256(base) + 2 * r256(toks * 128 * 4) + 2 * r256(toks * 64 * 4) + 3 * r256(toks * 4))
     assert kdn.backward_gated_workspace_size(2, 33, 2, 128, 64, "grouped") == 0
+    # the smallest: the adjoint's smallest workspace for the variant and dtype, the same copies
+    copies = 2 * r256(toks * 128 * 4) + 2 * r256(toks * 64 * 4) + 2 * r256(toks * 128 * 4) + r256(toks * 4)
+    for dtype in (0, 1):
+        assert lib.kdn_backward_gated_workspace_size_for(0, dtype, 2, 33, 2, 128, 64) == (
+            r256(lib.kdn_backward_workspace_size_for(0, dtype, 2, 33, 2, 128, 64)) + copies)
+    big = lib.kdn_backward_gated_workspace_size_for(0, 1, 8, 4096, 16, 128, 128)
+    assert big == r256(chunk_min_bytes(8, 4096, 16, 128, 128)) + 8 * 4096 * 16 * 4 * (6 * 128 + 1)
+    assert lib.kdn_backward_gated_workspace_size_for(3, 1, 2, 33, 2, 128, 64) == 0
     assert kdn.backward_gated_workspace_size(0, 33, 2, 128, 64) == 0
 
 

@@ -150,3 +150,34 @@ def test_backward_misaligned_inputs_on_the_chunked_workspace(dev):
     b = _run(dev, w, x, ct, st, full, misalign=True)
     _equal(a, b, "misaligned")
     _check_pairs("misaligned", a, w, x, ct, st, [(1, 1), (5, 12)])
+
+
+def test_gated_backward_smallest_workspace_equals_all_pairs(dev):
+    # kdn_backward_gated on kdn_backward_gated_workspace_size_for (the fp32
+    # copies at its end, the chunked adjoint in slabs before them) and on the
+    # all-pairs size, with two pairs on the token path (a chunk of z_alpha =
+    # -14, alpha ~ 8e-7); the gated parity tests cover the smallest size
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.Workload("gbwd_ws", "diagonal", "bf16", B, T, H, D, D, float(D), "uniform", 5104, omega_loc=-1.0)
+    x = wl.gated_inputs(w)
+    for b, h, c in ((1, 3, 2), (7, 11, 33)):
+        x["z_alpha"][b, 32 * c:32 * c + 32, h] = wl.round_bf16(np.full((32, D), -14.0, np.float32))
+    ct = wl.backward_cotangents(w, with_state=True)
+    t = {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16).to(dev)
+         for n in ("q", "k", "v", "z_alpha", "z_omega", "z_r")}
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    small = kdn.backward_gated_workspace_size(B, T, H, D, D, "diagonal", torch.bfloat16)
+    full = kdn.backward_gated_workspace_size(B, T, H, D, D, "diagonal")
+    assert small < full
+    out = []
+    for nb in (small, full):
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        g = kdn.backward_gated(**t, c0=f32(x["c0"]), mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev),
+                               dS_T=f32(ct["dS_T"]), dp_T=f32(ct["dp_T"]), workspace=ws)
+        torch.cuda.synchronize()
+        out.append({n: v.cpu().numpy() for n, v in g.items()})
+        del ws
+    _equal(out[0], out[1], "gated")
+    for n, v in out[0].items():
+        assert np.all(np.isfinite(v)), n
