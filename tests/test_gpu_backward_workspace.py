@@ -28,15 +28,16 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _case(seed, out_of_range=()):
-    w = wl.Workload("bwd_ws", "diagonal", "bf16", B, T, H, D, D, float(D), "uniform", seed, omega_loc=-1.0)
+def _case(seed, out_of_range=(), shape=(B, T, H, D, D)):
+    b_, t_, h_, dk, dv = shape
+    w = wl.Workload("bwd_ws", "diagonal", "bf16", b_, t_, h_, dk, dv, float(dk), "uniform", seed, omega_loc=-1.0)
     x = wl.forward_inputs(w)
     for b, h, c in out_of_range:  # a chunk of alpha = 1e-6: the pair leaves the chunked form's range
-        x["alpha"][b, 32 * c:32 * c + 32, h] = wl.round_bf16(np.full((32, D), 1e-6, np.float32))
+        x["alpha"][b, 32 * c:32 * c + 32, h] = wl.round_bf16(np.full((32, dk), 1e-6, np.float32))
     ct = wl.backward_cotangents(w, with_state=True)
     rng = np.random.default_rng(seed + 1)
-    st = {"S0": wl.round_bf16(rng.standard_normal((B, H, D, D)).astype(np.float32) * 0.2),
-          "p0": rng.uniform(0.5, 2.0, (B, H, D)).astype(np.float32)}
+    st = {"S0": wl.round_bf16(rng.standard_normal((b_, h_, dk, dv)).astype(np.float32) * 0.2),
+          "p0": rng.uniform(0.5, 2.0, (b_, h_, dk)).astype(np.float32)}
     return w, x, ct, st
 
 
@@ -58,16 +59,18 @@ def _run(dev, w, x, ct, st, ws_bytes, misalign=False):
     return {n: v.cpu().numpy() for n, v in g.items()}
 
 
-def _sizes():
+def _sizes(w=None):
     import torch
     import kalman_delta_network_amd as kdn
-    small = kdn.backward_workspace_size(B, T, H, D, D, "diagonal", torch.bfloat16)
-    full = kdn.backward_workspace_size(B, T, H, D, D)
+    b_, t_, h_, dk, dv = (B, T, H, D, D) if w is None else (w.B, w.T, w.H, w.dk, w.dv)
+    small = kdn.backward_workspace_size(b_, t_, h_, dk, dv, "diagonal", torch.bfloat16)
+    full = kdn.backward_workspace_size(b_, t_, h_, dk, dv)
     assert small < full
     return small, full
 
 
 def _check_pairs(name, got, w, x, ct, st, pairs):
+    """Sampled pairs against oracle.backward (bf16 tolerance), every gradient finite."""
     worst = {k: 0.0 for k in GRADS}
     for b, h in pairs:
         sub = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in TOKEN_INPUTS}
@@ -111,14 +114,26 @@ def _equal(a, b, name):
         assert np.array_equal(a[n], b[n]), (name, n, float(np.max(np.abs(a[n] - b[n]))))
 
 
-def test_backward_slabs_equal_one_slab(dev):
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_backward_slabs_equal_one_slab(dev, dk, dv):
     # three slabs with dS and dp carried between them, against one slab
-    w, x, ct, st = _case(5101)
-    small, full = _sizes()
+    w, x, ct, st = _case(5101 + dk + dv, shape=(B, T, H, dk, dv))
+    small, full = _sizes(w)
     a = _run(dev, w, x, ct, st, small)
     b = _run(dev, w, x, ct, st, full)
-    _equal(a, b, "slabs")
-    _check_pairs("slabs", a, w, x, ct, st, [(0, 0), (3, 9), (7, 15)])
+    _equal(a, b, f"slabs/dk{dk}/dv{dv}")
+    _check_pairs(f"slabs/dk{dk}/dv{dv}", a, w, x, ct, st, [(0, 0), (3, 9), (7, 15)])
+
+
+def test_backward_long_sequence_slabs(dev):
+    # B*H = 16 pairs: 4096-token slabs (64k token-heads), T = 10000 gives
+    # three (4096, 4096, 1808), each with 64 uncertainty segments
+    w, x, ct, st = _case(5105, shape=(1, 10000, 16, D, D))
+    small, full = _sizes(w)
+    a = _run(dev, w, x, ct, st, small)
+    b = _run(dev, w, x, ct, st, full)
+    _equal(a, b, "long")
+    _check_pairs("long", a, w, x, ct, st, [(0, 7)])
 
 
 def test_backward_token_path_rounds_for_pairs_out_of_range(dev):
