@@ -521,7 +521,7 @@ template <int DK, int NCW, bool GATE>
 __device__ __forceinline__ void iso_seg1(IsoState<DK, NCW>& st, SegCarry<NCW>& cy, IsoSmem<DK>& sm, int c,
                                          int sw_, const StateOps<DK>& op) {
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15, g4 = (lane >> 4) * 4, kg8 = (lane >> 4) * 8;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
     constexpr int KS = DK / 32;
     constexpr int VP = 16 * NCW;  // v row pitch
     const int slot = c & 3, vslot = c % 3, mb = c & 1, m3 = c % 3;
