@@ -200,3 +200,37 @@ def test_backward_full_size_sampled_heads(dev, name):
         assert e <= tol("bf16"), (k, e)
     for k in GRADS:
         assert np.all(np.isfinite(got[k])), k
+
+
+def test_backward_full_size_every_pair(dev):
+    """The diagonal bf16 backward at B=8, T=4096, H=16, d=128 on its smallest
+    workspace (the benchmark's configuration: eight 512-token slabs), every
+    (batch, head) pair against oracle.backward; reports the worst pair."""
+    import torch
+    import kalman_delta_network_amd as kdn
+    w = wl.WORKLOADS["diag_bf16_b8_t4096_h16_d128"]
+    x = wl.forward_inputs(w)
+    ct = wl.backward_cotangents(w, with_state=False)
+    t = to_dev(x, "bf16", dev)
+    ws = torch.empty(kdn.backward_workspace_size(w.B, w.T, w.H, w.dk, w.dv, w.variant, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    g = kdn.backward(**t, mu=w.mu, dO=torch.from_numpy(ct["dO"]).to(torch.bfloat16).to(dev), variant=w.variant,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    got = {n: v.cpu().numpy() for n, v in g.items()}
+    del g, ws, t
+    ref = oracle.backward(**{n: x[n] for n in TOKEN_INPUTS}, c0=x["c0"], mu=w.mu, dO=ct["dO"], variant=w.variant)
+    errs = {k: rel_err(got[k], ref[k]) for k in GRADS}
+    worst = {}
+    for k in GRADS:
+        per = [rel_err(got[k][b, :, h] if k not in ("dS0", "dp0") else got[k][b, h],
+                       ref[k][b, :, h] if k not in ("dS0", "dp0") else ref[k][b, h])
+               for b in range(w.B) for h in range(w.H)]
+        j = int(np.argmax(per))
+        worst[k] = (per[j], divmod(j, w.H))
+    print("backward full size, every pair: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    print("worst pair: " + " ".join(f"{k}={v[0]:.2e}{v[1]}" for k, v in worst.items()), flush=True)
+    for k in GRADS:
+        assert np.all(np.isfinite(got[k])), k
+        assert errs[k] <= tol("bf16"), (k, errs[k])
+        assert worst[k][0] <= tol("bf16"), (k, worst[k])
