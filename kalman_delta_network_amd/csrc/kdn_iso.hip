@@ -426,6 +426,11 @@ __device__ __forceinline__ int chan_of(int p) {
     const int q = p & 31;
     return (p & ~31) + (q < 16 ? 8 * (q >> 2) + (q & 3) : 8 * ((q - 16) >> 2) + 4 + (q & 3));
 }
+// 16-byte unit of k^T: the low two bits XOR bits 5..6.  The transpose's
+// lanes (cg) write units 32 (cg >> 2) + 4 (cg & 3) + j, which would share
+// four bank groups; the state waves read 16 consecutive units, for which the
+// XOR is one constant.
+__device__ __forceinline__ int kt_unit(int u) { return u ^ ((u >> 5) & 3); }
 __device__ __forceinline__ int pos_of(int ch) {
     const int j = ch & 7, g = (ch >> 3) & 3;
     return (ch & ~31) + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
@@ -451,7 +456,7 @@ __device__ __forceinline__ void transpose_k(bf16_t* KT, const bf16_t* K) {
         u4 outv;
 #pragma unroll
         for (int m = 0; m < 4; ++m) outv[m] = __builtin_amdgcn_perm(rw[2 * m + 1][cc >> 1], rw[2 * m][cc >> 1], sel);
-        *reinterpret_cast<u4*>(KT + (qg * DK + pos_of(8 * cg + cc)) * 8) = outv;
+        *reinterpret_cast<u4*>(KT + kt_unit(qg * DK + pos_of(8 * cg + cc)) * 8) = outv;
     }
 }
 
@@ -594,7 +599,7 @@ __device__ __forceinline__ void iso_seg2(IsoState<DK, NCW>& st, const SegCarry<N
     for (int at = 0; at < NT; ++at) ap[at] = *reinterpret_cast<const b8*>(&sm.P[c % 3][(16 * at + n) * PT + kg8]);
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it)
-        akt[it] = *reinterpret_cast<const b8*>(&sm.KT[c & 1][((lane >> 4) * DK + 16 * it + n) * 8]);
+        akt[it] = *reinterpret_cast<const b8*>(&sm.KT[c & 1][kt_unit((lane >> 4) * DK + 16 * it + n) * 8]);
     const float cin = sm.ch[slot][0];
     // outputs, transposed: lane (n, g4) holds value columns 16 j + g4 .. + 3 of token 16 at + n
     bf16_t* orow = a.o + tokidx(a, h, c * L + n) * a.DV + col0 + g4;
