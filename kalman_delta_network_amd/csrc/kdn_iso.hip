@@ -728,10 +728,11 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
             bar();
         }
     } else if (wave == 2) {
-        // ---------------- inverses of chunk i - 2 ----------------
+        // ---------------- inverses of chunk i - 2; (not gated) P of chunk i - 1 ----------------
         for (int i = 0; i < nit; ++i) {
             const int c = i - 2;
             if (c >= 0 && c < nchunks) block_inverse(sm.Md[c & 1], sm.Wi, sm.Td[c & 1], lane);
+            if (!GATE && c + 1 >= 0 && c + 1 < nchunks) gram_p<DK, GATE>(sm, (c + 1) % KR, (c + 1) & 3, (c + 1) % 3);
             bar();
         }
     } else if (wave == 3) {
@@ -749,7 +750,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
                 if (lane < L) sm.kn[(i + 1) & 1][lane] = nrm;
             }
             const int c = i - 1;
-            if (c >= 0 && c < nchunks) gram_p<DK, GATE>(sm, c % KR, c & 3, c % 3);
+            if (GATE && c >= 0 && c < nchunks) gram_p<DK, GATE>(sm, c % KR, c & 3, c % 3);
             bar();
         }
         vm_wait<0>();
