@@ -39,10 +39,13 @@
 //           weights to LDS
 //   wave 1  Gram K K^T of chunk i - 1 (matrix cores), weighted into M's
 //           diagonal blocks and -M_10; k^T of chunk i - 2 for the update
-//   wave 2  inverses of M's diagonal blocks of chunk i - 2
+//   wave 2  inverses of M's diagonal blocks of chunk i - 2; not gated, Gram
+//           Q K^T of chunk i - 1, weighted into P = tril(...)
 //   wave 3  direct copies of the k and q tiles of chunk i + 2; |k_t|^2 of
-//           chunk i + 1 once its tile has landed (not gated); Gram Q K^T of
-//           chunk i - 1, weighted into P = tril(...)
+//           chunk i + 1 once its tile has landed (not gated); gated, the
+//           query norms and P of chunk i - 1 (each SIMD runs one state wave
+//           and one of waves 0..3, so the other roles' work is spread so that
+//           no SIMD pair carries much more than the others)
 //   waves 4..7  state update of chunk i - 3: 16 value columns each, S~ in
 //           registers (fp32)
 // Everything a wave reads at iteration i was written before the barrier that
