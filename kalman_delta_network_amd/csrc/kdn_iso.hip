@@ -38,9 +38,11 @@
 //           broadcast; the log-decay prefix sums the same way; per-token
 //           weights to LDS
 //   wave 1  Gram K K^T of chunk i - 1 (matrix cores), weighted into M's
-//           diagonal blocks and -M_10; k^T of chunk i - 2 for the update
-//   wave 2  inverses of M's diagonal blocks of chunk i - 2; not gated, Gram
-//           Q K^T of chunk i - 1, weighted into P = tril(...)
+//           diagonal blocks and -M_10; not gated, tile (1,1) of P of chunk
+//           i - 1; k^T of chunk i - 2 for the update
+//   wave 2  inverses of M's diagonal blocks of chunk i - 2; not gated, tiles
+//           (0,0) and (1,0) of the Gram Q K^T of chunk i - 1, weighted into
+//           P = tril(...)
 //   wave 3  direct copies of the k and q tiles of chunk i + 2; |k_t|^2 of
 //           chunk i + 1 once its tile has landed (not gated); gated, the
 //           query norms and P of chunk i - 1 (each SIMD runs one state wave
@@ -415,6 +417,31 @@ __device__ __forceinline__ void gram_p(IsoSmem<DK>& sm, int kslot, int slot, int
         sm.P[pslot][(16 + g4 + e) * PT + perm32(16 + n)] = to_bf(w11[e] * a11[e]);
     }
 }
+// Not gated, in two parts on two waves: tiles (0,0) and (1,0) of P, then
+// tile (1,1), each reading only the row tiles it needs.
+template <int DK>
+__device__ __forceinline__ void gram_p_part(IsoSmem<DK>& sm, int kslot, int slot, int pslot, int part) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = (lane >> 4) * 4;
+    if (part == 0) {
+        const RowTile<DK> k0 = row_tile<DK>(sm.K[kslot], 0);
+        const RowTile<DK> q0 = row_tile<DK>(sm.Q[kslot], 0), q1 = row_tile<DK>(sm.Q[kslot], 1);
+        const f4 a00 = gram_tile<DK>(q0, k0), a10 = gram_tile<DK>(q1, k0);
+        const f4 w00 = pair_weights<DK>(sm, slot, 0, 0), w10 = pair_weights<DK>(sm, slot, 1, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sm.P[pslot][(g4 + e) * PT + perm32(n)] = to_bf(w00[e] * a00[e]);
+            sm.P[pslot][(16 + g4 + e) * PT + perm32(n)] = to_bf(w10[e] * a10[e]);
+        }
+    } else {
+        const RowTile<DK> k1 = row_tile<DK>(sm.K[kslot], 1), q1 = row_tile<DK>(sm.Q[kslot], 1);
+        const f4 a11 = gram_tile<DK>(q1, k1);
+        const f4 w11 = pair_weights<DK>(sm, slot, 1, 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.P[pslot][(16 + g4 + e) * PT + perm32(16 + n)] = to_bf(w11[e] * a11[e]);
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // state: one wave = 16 value columns, S~ (d_k x 16 fp32) in registers
@@ -727,6 +754,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         for (int i = 0; i < nit; ++i) {
             const int c = i - 1;
             if (c >= 0 && c < nchunks) gram_m<DK, GATE>(sm, c % KR, c & 3, c & 1, c % 3);
+            if (!GATE && c >= 0 && c < nchunks) gram_p_part<DK>(sm, c % KR, c & 3, c % 3, 1);
             if (c >= 1 && c <= nchunks) transpose_k<DK>(sm.KT[(c - 1) & 1], sm.K[(c - 1) % KR]);
             bar();
         }
@@ -735,7 +763,7 @@ __global__ void __launch_bounds__(NTHREADS) kdn_iso_kernel(IsoArgs a) {
         for (int i = 0; i < nit; ++i) {
             const int c = i - 2;
             if (c >= 0 && c < nchunks) block_inverse(sm.Md[c & 1], sm.Wi, sm.Td[c & 1], lane);
-            if (!GATE && c + 1 >= 0 && c + 1 < nchunks) gram_p<DK, GATE>(sm, (c + 1) % KR, (c + 1) & 3, (c + 1) % 3);
+            if (!GATE && c + 1 >= 0 && c + 1 < nchunks) gram_p_part<DK>(sm, (c + 1) % KR, (c + 1) & 3, (c + 1) % 3, 0);
             bar();
         }
     } else if (wave == 3) {
