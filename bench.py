@@ -208,8 +208,13 @@ def time_forward(kdn, w, t, steps, warmup, algo):
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
-    # per-launch durations (events on the same stream the kernel runs on)
+    # per-launch durations (events on the same stream the kernel runs on).
+    # One untimed call first keeps the device busy while the host enqueues
+    # the first timed launch; after the synchronisation above the device
+    # would otherwise sit idle inside that interval for the host's launch
+    # latency.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    call()
     for a, b in evs:
         a.record()
         call()
